@@ -1,0 +1,168 @@
+"""ctypes wrapper around the C oracle (test infrastructure only).
+
+Every function takes plain numpy arrays (host memory) and returns numpy arrays.
+bf16 tensors are passed as their uint16 bit patterns.  Nothing here imports or
+calls the GPU library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def load(path: str):
+    """Load an oracle build from ``path`` (the tests also load mutated builds)."""
+    h = ctypes.CDLL(path)
+    h.specref_verify_attn.restype = ctypes.c_int
+    h.specref_accept.restype = ctypes.c_int
+    h.specref_compact_kv.restype = ctypes.c_int
+    return h
+
+
+def lib(override=None):
+    global _lib
+    if override is not None:
+        return override
+    if _lib is None:
+        _lib = load(_build.build(force=False))
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _kv_dtype(a) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError(f"KV arrays must be bf16 bits (uint16) or float32, got {a.dtype}")
+
+
+def verify_attn(q, k_cache, v_cache, kv_start, kv_len, k_new, v_new, B, K, Hq, Hkv, D,
+                k_prefix=None, v_prefix=None, scale=0.0, sel_rows=None, sel_heads=None,
+                lib_=None):
+    """fp64 attention of the K+1 verify queries.
+
+    Returns [B*(K+1), Hq, D] float64, or [n_sel, D] for the listed (row, head) pairs.
+    """
+    dt = _kv_dtype(q)
+    store = np.uint16 if dt == BF16 else np.float32
+    arrs = [_c(x, store) for x in (q, k_cache, v_cache, k_new, v_new)]
+    kp = None if k_prefix is None else _c(k_prefix, store)
+    vp = None if v_prefix is None else _c(v_prefix, store)
+    P = 0 if kp is None else int(kp.shape[0])
+    ks, kl = _c(kv_start, np.int64), _c(kv_len, np.int32)
+    if sel_rows is None:
+        out = np.zeros((B * (K + 1), Hq, D), dtype=np.float64)
+        sr = sh = None
+        n_sel = -1
+    else:
+        sr, sh = _c(sel_rows, np.int32), _c(sel_heads, np.int32)
+        n_sel = int(sr.shape[0])
+        out = np.zeros((n_sel, D), dtype=np.float64)
+    rc = lib(lib_).specref_verify_attn(
+        _p(arrs[0]), _p(arrs[1]), _p(arrs[2]), _p(ks), _p(kl), _p(arrs[3]), _p(arrs[4]),
+        _p(kp), _p(vp), ctypes.c_int(P), B, K, Hq, Hkv, D, dt, ctypes.c_double(scale),
+        _p(sr), _p(sh), ctypes.c_int(n_sel), _p(out))
+    if rc:
+        raise ValueError(f"specref_verify_attn failed: {rc}")
+    return out
+
+
+def accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature,
+           top_p, greedy=False, lib_=None):
+    """One verify round of modified rejection sampling per sequence.
+
+    Returns a dict with n_accepted [B], out_tokens [B, K+1], q_tok/p_tok [B, K],
+    flag_pos [B], n_decisions, n_flagged.  ``temperature`` and ``top_p`` are
+    rounded to float32 first, as the GPU library receives them.
+    """
+    tl = _c(target_logits, np.float32)
+    B, K1, V = tl.shape
+    K = K1 - 1
+    dl = None if draft_logits is None else _c(draft_logits, np.float32)
+    if dl is None and not greedy:
+        raise ValueError("draft logits are required unless greedy")
+    dtok = _c(draft_tokens, np.int32).reshape(B, K)
+    ua = _c(u_accept, np.float32).reshape(B, K)
+    us = _c(u_sample, np.float32).reshape(B)
+    n = np.zeros(B, np.int32)
+    out = np.zeros((B, K + 1), np.int32)
+    qt = np.zeros((B, K), np.float64)
+    pt = np.zeros((B, K), np.float64)
+    fp = np.zeros(B, np.int32)
+    nd = ctypes.c_int64(0)
+    nf = ctypes.c_int64(0)
+    rc = lib(lib_).specref_accept(
+        _p(tl), _p(dl), _p(dtok), _p(ua), _p(us), B, K, V,
+        ctypes.c_double(float(np.float32(temperature))),
+        ctypes.c_double(float(np.float32(top_p))), int(bool(greedy)),
+        _p(n), _p(out), _p(qt), _p(pt), _p(fp), ctypes.byref(nd), ctypes.byref(nf))
+    if rc:
+        raise ValueError(f"specref_accept failed: {rc}")
+    return {"n_accepted": n, "out_tokens": out, "q_tok": qt, "p_tok": pt, "flag_pos": fp,
+            "n_decisions": int(nd.value), "n_flagged": int(nf.value)}
+
+
+def compact_kv(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, k_new, v_new,
+               K, Hkv, D, lib_=None):
+    """Padding-free compaction.  Returns (tokens_packed, cu_tokens, kv_len, k_cache,
+    v_cache) as new arrays; the inputs are not modified."""
+    n = _c(n_accepted, np.int32)
+    B = int(n.shape[0])
+    ot = _c(out_tokens, np.int32)
+    kl = _c(kv_len, np.int32).copy()
+    ks = _c(kv_start, np.int64)
+    kc = np.array(k_cache, copy=True, order="C")
+    vc = np.array(v_cache, copy=True, order="C")
+    kn = np.ascontiguousarray(k_new)
+    vn = np.ascontiguousarray(v_new)
+    es = kc.dtype.itemsize
+    packed = np.full(B * (K + 1), -1, np.int32)
+    cu = np.zeros(B + 1, np.int32)
+    rc = lib(lib_).specref_compact_kv(_p(n), _p(ot), _p(kl), _p(ks), _p(kc), _p(vc), _p(kn),
+                                  _p(vn), _p(packed), _p(cu), B, K, Hkv, D, es)
+    if rc:
+        raise ValueError(f"specref_compact_kv failed: {rc}")
+    return packed, cu, kl, kc, vc
+
+
+def workload_attn(w, sel_rows=None, sel_heads=None):
+    """Oracle attention on a workload object from the shared input generator."""
+    c = w.cfg
+    return verify_attn(w.q, w.k_cache, w.v_cache, w.kv_start, w.kv_len, w.k_new, w.v_new,
+                       c.B, c.K, c.Hq, c.Hkv, c.D, k_prefix=w.k_prefix,
+                       v_prefix=w.v_prefix, sel_rows=sel_rows, sel_heads=sel_heads)
+
+
+def workload_accept(w):
+    c = w.cfg
+    return accept(w.target_logits, None if c.greedy else w.draft_logits, w.draft_tokens,
+                  w.u_accept, w.u_sample, c.temperature, c.top_p, c.greedy)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact conversion of bf16 bit patterns to float64."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def kv_to_f64(a: np.ndarray) -> np.ndarray:
+    return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecref.so")

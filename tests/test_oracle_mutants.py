@@ -1,0 +1,173 @@
+"""Negative controls: plausible mistakes planted in copies of the CPU oracle.
+
+Each mutant is the oracle's C source with one textual change (a dropped term,
+a wrong sign, index or operand), compiled into a temporary library.  The pin
+named next to it must reject the mutant; if a mutant slipped through, the pins
+would not be able to tell that mistake from the method.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import specref as R
+from speculative_decoding_verify_04_amd import workloads as W
+
+import pins
+from test_oracle_pins import ATTN_SHAPES, numpy_attention, oracle_sampler
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "specref.c")
+CASES = {c.name: c for c in pins.make_cases()}
+N = 200_000
+
+
+def _theorem1(case_names):
+    def check(lib_):
+        for name in case_names:
+            case = CASES[name]
+            pv, res, tok = pins.theorem1_pvalues(oracle_sampler(lib_), case, n=N, seed=5)
+            if min(pv) <= pins.ALPHA:
+                return False
+            if any(abs(z) >= 5 for z in pins.accept_rate_z(res, case)):
+                return False
+        return True
+    return check
+
+
+def _nucleus_closed_forms(lib_):
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "nucleus_cases.json")) as f:
+        gold = json.load(f)
+    for c in gold["cases"]:
+        z = np.log(np.array(c["probs"], np.float64)).astype(np.float32)
+        zt, zd = np.stack([z, z])[None], z[None, None]
+        for t in range(z.shape[0]):
+            res = R.accept(zt, zd, np.array([[t]], np.int32), np.zeros((1, 1), np.float32),
+                           np.zeros(1, np.float32), c.get("temperature", 1.0), c["top_p"],
+                           lib_=lib_)
+            if abs(res["q_tok"][0, 0] - c["expected"][t]) > 1e-6:
+                return False
+    return True
+
+
+def _attention(shape_names):
+    def check(lib_):
+        for name in shape_names:
+            w = W.make_workload(ATTN_SHAPES[name], sub_seed=4)
+            c = w.cfg
+            o = R.verify_attn(w.q, w.k_cache, w.v_cache, w.kv_start, w.kv_len, w.k_new,
+                              w.v_new, c.B, c.K, c.Hq, c.Hkv, c.D, k_prefix=w.k_prefix,
+                              v_prefix=w.v_prefix, lib_=lib_)
+            if not np.allclose(o, numpy_attention(w), rtol=1e-12, atol=1e-12):
+                return False
+        return True
+    return check
+
+
+def _compaction(lib_):
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], Hq=2, Hkv=2, D=16, V=256, len_lo=3,
+                          len_hi=20)
+    w = W.make_workload(cfg, sub_seed=2)
+    res = R.workload_accept(w)
+    packed, cu, kl, kc, _ = R.compact_kv(res["n_accepted"], res["out_tokens"], w.kv_len,
+                                         w.kv_start, w.k_cache, w.v_cache, w.k_new, w.v_new,
+                                         cfg.K, cfg.Hkv, cfg.D, lib_=lib_)
+    e = res["n_accepted"] + 1
+    if not (np.array_equal(np.diff(cu), e) and np.array_equal(kl - w.kv_len, e)):
+        return False
+    for b in range(cfg.B):
+        if not np.array_equal(packed[cu[b]:cu[b + 1]], res["out_tokens"][b, :e[b]]):
+            return False
+        s, L = int(w.kv_start[b]), int(w.kv_len[b])
+        r0 = b * (cfg.K + 1)
+        if not np.array_equal(kc[s + L:s + L + e[b]], w.k_new[r0:r0 + e[b]]):
+            return False
+    return True
+
+
+MUTANTS = {
+    "resample_from_q": (
+        "tok = draw(mass > 0.0 ? w : q, V, (double)u_sample[b], &amb);",
+        "tok = draw(q, V, (double)u_sample[b], &amb);",
+        _theorem1(["dirichlet_v4", "dirichlet_v8"])),
+    "accept_min_p_over_q": (
+        "int accept = px > 0.0 ? (u * px < qx) : (qx > 0.0);",
+        "int accept = qx > 0.0 ? (u * qx < px) : (px > 0.0);",
+        _theorem1(["v2", "dirichlet_v4"])),
+    "residual_sign": (
+        "w[t] = q[t] - p[t] > 0.0 ? q[t] - p[t] : 0.0;",
+        "w[t] = p[t] - q[t] > 0.0 ? p[t] - q[t] : 0.0;",
+        _theorem1(["v2", "dirichlet_v4"])),
+    "bonus_from_draft_row": (
+        "                    tok = draw(q, V, (double)u_sample[b], &amb);",
+        "                    tok = draw(p, V, (double)u_sample[b], &amb);",
+        _theorem1(["dirichlet_v4", "dirichlet_v8"])),
+    "temperature_multiplied": (
+        "pi[t] = exp(((double)z[t] - m) / T);",
+        "pi[t] = exp(((double)z[t] - m) * T);",
+        _theorem1(["temp_half"])),
+    "nucleus_drops_boundary_group": (
+        "        if (pi[t] >= tau) kept += pi[t];\n"
+        "    for (int t = 0; t < V; ++t) pi[t] = pi[t] >= tau ? pi[t] / kept : 0.0;",
+        "        if (pi[t] > tau) kept += pi[t];\n"
+        "    for (int t = 0; t < V; ++t) pi[t] = pi[t] > tau ? pi[t] / kept : 0.0;",
+        _nucleus_closed_forms),
+    "nucleus_not_renormalised": (
+        "pi[t] = pi[t] >= tau ? pi[t] / kept : 0.0;",
+        "pi[t] = pi[t] >= tau ? pi[t] : 0.0;",
+        _nucleus_closed_forms),
+    "nucleus_strict_mass": (
+        "if (above + group >= top_p || e == V) {",
+        "if (above + group > top_p + 0.05 || e == V) {",
+        _nucleus_closed_forms),
+    "causal_window_short": (
+        "int n_keys = a->prefix_len + a->kv_len[b] + j + 1;",
+        "int n_keys = a->prefix_len + a->kv_len[b] + (j > 0 ? j : 1);",
+        _attention(["tiny_fp32"])),
+    "gqa_interleaved_heads": (
+        "    int g = h / G;\n    int n_keys",
+        "    int g = h % a->Hkv; (void)G;\n    int n_keys",
+        _attention(["bf16_gqa"])),
+    "missing_scale": (
+        "s[t] = a->scale * dot;",
+        "s[t] = dot;",
+        _attention(["tiny_fp32"])),
+    "prefix_dropped": (
+        "int n_keys = a->prefix_len + a->kv_len[b] + j + 1;",
+        "int n_keys = a->kv_len[b] + j + 1;",
+        _attention(["bf16_prefix"])),
+    "compaction_drops_drawn_token": (
+        "cu_tokens[b + 1] = cu_tokens[b] + n_accepted[b] + 1;",
+        "cu_tokens[b + 1] = cu_tokens[b] + n_accepted[b];",
+        _compaction),
+}
+
+
+def _build_mutant(tmp_path, name, find, repl):
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation site for {name} not unique/present"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(find, repl))
+    lib = tmp_path / f"lib{name}.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-w", "-shared", "-fPIC", str(path),
+                           "-o", str(lib), "-lm"])
+    return R.load(str(lib))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    find, repl, check = MUTANTS[name]
+    lib_ = _build_mutant(tmp_path, name, find, repl)
+    try:
+        passed = check(lib_)
+    except (ValueError, FloatingPointError):
+        passed = False
+    assert not passed, f"pin did not catch mutant {name}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_unmutated_oracle_passes_same_check(name):
+    _, _, check = MUTANTS[name]
+    assert check(R.lib())

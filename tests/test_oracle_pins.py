@@ -1,0 +1,316 @@
+"""The CPU oracle, pinned to what the pages and the mathematics fix (no GPU).
+
+Sampler pins (Theorem 1 and "Modified rejection sampling" of "Accelerating
+Large Language Model Decoding with Speculative Sampling"):
+  (1) chi-square over 10^6 trials: the emitted token is distributed as q'
+  (2) acceptance rate = sum_x min(p', q')
+  (3) p = q accepts every draft
+  (4) 1 <= emitted tokens <= K+1
+  plus: scan-length law, disjoint supports, greedy as the T -> 0 limit,
+  nucleus / temperature closed forms, compaction structure.
+Attention pins: (5) brute force vs a float64 numpy softmax(QK^T)V, and
+invariants (single key, equal keys, permutation, causality, GQA = repeated
+MHA, bifurcated prefix = concatenated KV).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import special
+
+from oracle import specref as R
+from speculative_decoding_verify_04_amd import workloads as W
+
+import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def oracle_sampler(lib_=None):
+    def f(zt, zd, tok, ua, us, T, top_p, greedy):
+        return R.accept(zt, zd, tok, ua, us, T, top_p, greedy, lib_=lib_)
+    return f
+
+
+CASES = {c.name: c for c in pins.make_cases()}
+
+
+# ---------------------------------------------------------------- sampler pins
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_theorem1_distribution_and_accept_rate(name):
+    case = CASES[name]
+    pv, res, tok = pins.theorem1_pvalues(oracle_sampler(), case, seed=11)
+    assert len(pv) >= 1
+    assert min(pv) > pins.ALPHA, (name, pv)
+    zs = pins.accept_rate_z(res, case)
+    assert all(abs(z) < 5 for z in zs), (name, zs)
+    assert pins.scan_length_pvalue(res, case) > pins.ALPHA
+    pins.check_counts(res, tok, case.K, case.V)
+
+
+def test_disjoint_supports_never_accept():
+    case = CASES["disjoint"]
+    _, res, _ = pins.theorem1_pvalues(oracle_sampler(), case, n=20000, seed=3)
+    assert np.all(res["n_accepted"] == 0)
+    assert set(np.unique(res["out_tokens"][:, 0])) <= {0, 1}
+
+
+def test_p_equals_q_accepts_all_small_configs():
+    for name in ("tiny_fp32", "bass_b8k5", "chinchilla_b1k4", "prefix_b32k4"):
+        cfg = W.CONFIGS[name]
+        w = W.make_workload(cfg if name == "tiny_fp32" else W.small_variant(cfg, V=4096),
+                            sub_seed=5)
+        c = w.cfg
+        zd = np.ascontiguousarray(w.target_logits[:, : c.K, :])
+        # drafts must lie in the draft nucleus: use the target argmax, which every
+        # nucleus contains
+        tok = np.argmax(zd, axis=-1).astype(np.int32)
+        res = R.accept(w.target_logits, zd, tok, w.u_accept, w.u_sample, c.temperature,
+                       c.top_p)
+        assert np.all(res["n_accepted"] == c.K), name
+        np.testing.assert_array_equal(res["q_tok"], res["p_tok"])
+
+
+def test_counts_on_every_config_shape():
+    for name, cfg in W.CONFIGS.items():
+        small = cfg if name == "tiny_fp32" else W.small_variant(cfg, V=2048, B=min(cfg.B, 8))
+        w = W.make_workload(small, sub_seed=1)
+        res = R.workload_accept(w)
+        pins.check_counts(res, w.draft_tokens, small.K, small.V)
+
+
+def test_greedy_is_low_temperature_limit():
+    rng = np.random.default_rng(7)
+    B, K, V = 64, 4, 257
+    zt = rng.standard_normal((B, K + 1, V)).astype(np.float32) * 3
+    zd = (zt[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32)).astype(np.float32)
+    tok = np.argmax(zd, axis=-1).astype(np.int32)
+    ua = (rng.integers(1, 2 ** 24, size=(B, K)) * 2.0 ** -24).astype(np.float32)
+    us = (rng.integers(0, 2 ** 24, size=B) * 2.0 ** -24).astype(np.float32)
+    srt = np.sort(zt, axis=-1)
+    gap_t = srt[..., -1] - srt[..., -2]
+    gap_d = np.sort(zd, axis=-1)
+    gap_d = gap_d[..., -1] - gap_d[..., -2]
+    ok = np.all(gap_t > 0.01, axis=1) & np.all(gap_d > 0.01, axis=1)
+    g = R.accept(zt, None, tok, ua, us, 1.0, 1.0, greedy=True)
+    s = R.accept(zt, zd, tok, ua, us, 1e-4, 1.0, greedy=False)
+    assert ok.sum() > 40
+    np.testing.assert_array_equal(g["n_accepted"][ok], s["n_accepted"][ok])
+    np.testing.assert_array_equal(g["out_tokens"][ok], s["out_tokens"][ok])
+    # greedy closed form: accept while the draft equals the target argmax
+    am = np.argmax(zt, axis=-1)
+    for b in range(B):
+        n = 0
+        while n < K and tok[b, n] == am[b, n]:
+            n += 1
+        assert g["n_accepted"][b] == n
+        assert g["out_tokens"][b, n] == am[b, n]
+
+
+def test_softmax_matches_library_at_unit_temperature():
+    rng = np.random.default_rng(3)
+    B, K, V = 16, 3, 1000
+    zt = (rng.standard_normal((B, K + 1, V)) * 3).astype(np.float32)
+    zd = (rng.standard_normal((B, K, V)) * 3).astype(np.float32)
+    tok = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    ua = np.zeros((B, K), np.float32)   # u = 0 accepts every draft with q > 0
+    us = np.zeros(B, np.float32)
+    res = R.accept(zt, zd, tok, ua, us, 1.0, 1.0)
+    qs = special.softmax(zt.astype(np.float64), axis=-1)
+    ps = special.softmax(zd.astype(np.float64), axis=-1)
+    bi, ji = np.meshgrid(np.arange(B), np.arange(K), indexing="ij")
+    np.testing.assert_allclose(res["q_tok"], qs[bi, ji, tok], rtol=1e-13)
+    np.testing.assert_allclose(res["p_tok"], ps[bi, ji, tok], rtol=1e-13)
+    assert np.all(res["n_accepted"] == K)
+    # u_sample = 0 draws the smallest id with nonzero bonus weight: token 0
+    assert np.all(res["out_tokens"][:, K] == 0)
+
+
+def test_nucleus_closed_forms():
+    with open(os.path.join(GOLDEN, "nucleus_cases.json")) as f:
+        gold = json.load(f)
+    for c in gold["cases"]:
+        z = np.log(np.array(c["probs"], np.float64)).astype(np.float32)
+        V = z.shape[0]
+        zt = np.stack([z, z])[None]          # [1, 2, V]
+        zd = z[None, None]                    # [1, 1, V]
+        for t in range(V):
+            res = R.accept(zt, zd, np.array([[t]], np.int32), np.zeros((1, 1), np.float32),
+                           np.zeros(1, np.float32), c.get("temperature", 1.0), c["top_p"])
+            assert res["q_tok"][0, 0] == pytest.approx(c["expected"][t], abs=1e-6), (c, t)
+            assert res["p_tok"][0, 0] == pytest.approx(c["expected"][t], abs=1e-6), (c, t)
+
+
+def test_residual_closed_form_v2():
+    """V=2: after a rejection of token x, (q-p)_+ puts all mass on the other token."""
+    with open(os.path.join(GOLDEN, "theorem1_v2.json")) as f:
+        gold = json.load(f)
+    q = np.array(gold["q"]); p = np.array(gold["p"])
+    zt = np.log(np.stack([q, q]))[None].astype(np.float32)
+    zd = np.log(p)[None, None].astype(np.float32)
+    # token 0 has p > q: rejected when u*p >= q
+    u = np.float32(0.99)
+    res = R.accept(zt, zd, np.array([[0]], np.int32), np.array([[u]]), np.array([0.5], np.float32),
+                   1.0, 1.0)
+    assert res["n_accepted"][0] == 0
+    assert res["out_tokens"][0, 0] == gold["residual_support"]
+    assert abs(np.minimum(p, q).sum() - gold["accept_rate"]) < 1e-12
+
+
+def test_ambiguity_accounting():
+    """A uniform exactly at q/p is flagged; a clear one is not."""
+    z = np.log(np.array([0.5, 0.5]))[None, None].astype(np.float32)            # [1, 1, 2]
+    zt = np.log(np.array([[0.25, 0.75], [0.5, 0.5]]))[None].astype(np.float32)  # [1, 2, 2]
+    qx = float(special.softmax(zt[0, 0].astype(np.float64))[0])
+    px = float(special.softmax(z[0, 0].astype(np.float64))[0])
+    u_edge = np.float32(qx / px)
+    res = R.accept(zt, z, np.array([[0]], np.int32), np.array([[u_edge]]),
+                   np.array([0.3], np.float32), 1.0, 1.0)
+    assert res["flag_pos"][0] == 0 and res["n_flagged"] >= 1
+    res = R.accept(zt, z, np.array([[0]], np.int32), np.array([[0.1]], np.float32),
+                   np.array([0.3], np.float32), 1.0, 1.0)
+    assert res["flag_pos"][0] == -1 and res["n_flagged"] == 0
+
+
+# ---------------------------------------------------------------- compaction
+
+def test_compaction_structure():
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], Hq=4, Hkv=2, D=64, V=512,
+                          len_lo=3, len_hi=40)
+    w = W.make_workload(cfg, sub_seed=2)
+    res = R.workload_accept(w)
+    packed, cu, kl, kc, vc = R.compact_kv(res["n_accepted"], res["out_tokens"], w.kv_len,
+                                          w.kv_start, w.k_cache, w.v_cache, w.k_new,
+                                          w.v_new, cfg.K, cfg.Hkv, cfg.D)
+    e = res["n_accepted"] + 1
+    assert cu[0] == 0 and np.array_equal(np.diff(cu), e) and cu[-1] == e.sum()
+    assert np.all(packed[: cu[-1]] >= 0) and np.all(packed[cu[-1]:] == -1)
+    assert np.array_equal(kl - w.kv_len, e)
+    for b in range(cfg.B):
+        assert np.array_equal(packed[cu[b]:cu[b + 1]], res["out_tokens"][b, : e[b]])
+        s, L = int(w.kv_start[b]), int(w.kv_len[b])
+        r0 = b * (cfg.K + 1)
+        assert np.array_equal(kc[s + L: s + L + e[b]], w.k_new[r0: r0 + e[b]])
+        assert np.array_equal(vc[s + L: s + L + e[b]], w.v_new[r0: r0 + e[b]])
+        # rows before L_b and after L_b + e_b are untouched
+        assert np.array_equal(kc[s: s + L], w.k_cache[s: s + L])
+        rest = slice(s + L + e[b], s + int(w.kv_cap[b]))
+        assert np.array_equal(kc[rest].view(np.uint16), w.k_cache[rest].view(np.uint16))
+
+
+# ---------------------------------------------------------------- attention pins
+
+def numpy_attention(w):
+    """Textbook float64 softmax(Q K^T / sqrt(D)) V over each query's key list."""
+    c = w.cfg
+    f = R.kv_to_f64
+    q, kc, vc, kn, vn = f(w.q), f(w.k_cache), f(w.v_cache), f(w.k_new), f(w.v_new)
+    G = c.Hq // c.Hkv
+    out = np.zeros((c.rows, c.Hq, c.D))
+    for b in range(c.B):
+        s, L = int(w.kv_start[b]), int(w.kv_len[b])
+        for j in range(c.K + 1):
+            r = b * (c.K + 1) + j
+            ks = [kc[s:s + L], kn[b * (c.K + 1): r + 1]]
+            vs = [vc[s:s + L], vn[b * (c.K + 1): r + 1]]
+            if w.k_prefix is not None:
+                ks.insert(0, f(w.k_prefix))
+                vs.insert(0, f(w.v_prefix))
+            Kt, Vt = np.concatenate(ks), np.concatenate(vs)
+            for h in range(c.Hq):
+                sc = Kt[:, h // G, :] @ q[r, h] / np.sqrt(c.D)
+                out[r, h] = special.softmax(sc) @ Vt[:, h // G, :]
+    return out
+
+
+ATTN_SHAPES = {
+    "tiny_fp32": W.CONFIGS["tiny_fp32"],
+    "bf16_mha": W.small_variant(W.CONFIGS["bass_b8k5"], B=3, Hq=4, Hkv=4, D=32,
+                                len_lo=0, len_hi=70, V=64),
+    "bf16_gqa": W.small_variant(W.CONFIGS["gqa_b64k8"], B=3, Hq=8, Hkv=2, D=32,
+                                len_lo=20, len_hi=90, V=64),
+    "bf16_prefix": W.small_variant(W.CONFIGS["prefix_b32k4"], B=4, Hq=4, Hkv=4, D=32,
+                                   prefix_len=50, len_lo=0, len_hi=6, V=64),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_SHAPES))
+def test_attention_brute_force(name):
+    w = W.make_workload(ATTN_SHAPES[name], sub_seed=4)
+    np.testing.assert_allclose(R.workload_attn(w), numpy_attention(w), rtol=1e-12,
+                               atol=1e-12)
+
+
+def _tiny(B=1, K=0, H=1, Hkv=1, D=8, lens=(0,), prefix=0, dtype=W.F32):
+    cfg = W.Config(name="t", B=B, K=K, Hq=H, Hkv=Hkv, D=D, V=8, kv_dtype=dtype,
+                   len_kind="fixed", len_lo=0, len_hi=0, fixed_lens=tuple(lens),
+                   prefix_len=prefix)
+    return W.make_workload(cfg, sub_seed=9)
+
+
+def test_single_key_returns_its_value():
+    w = _tiny()   # L=0, K=0: query 0 sees only new row 0
+    o = R.workload_attn(w)
+    np.testing.assert_allclose(o[0, 0], w.v_new[0, 0].astype(np.float64), rtol=0, atol=0)
+
+
+def test_equal_keys_average_values():
+    w = _tiny(lens=(6,))
+    s = int(w.kv_start[0])
+    w.k_cache[s:s + 6] = w.k_new[0]
+    o = R.workload_attn(w)
+    vals = np.concatenate([w.v_cache[s:s + 6], w.v_new[:1]]).astype(np.float64)
+    np.testing.assert_allclose(o[0, 0], vals[:, 0].mean(axis=0), rtol=1e-14, atol=1e-14)
+
+
+def test_cache_permutation_invariance():
+    w = _tiny(B=2, K=3, H=2, Hkv=2, lens=(9, 4))
+    o1 = R.workload_attn(w)
+    s, L = int(w.kv_start[0]), int(w.kv_len[0])
+    perm = np.random.default_rng(0).permutation(L)
+    w.k_cache[s:s + L] = w.k_cache[s:s + L][perm]
+    w.v_cache[s:s + L] = w.v_cache[s:s + L][perm]
+    np.testing.assert_allclose(R.workload_attn(w), o1, rtol=1e-13, atol=1e-13)
+
+
+def test_causal_among_new_rows():
+    w = _tiny(B=2, K=4, H=2, Hkv=2, lens=(5, 3))
+    o1 = R.workload_attn(w)
+    j = 2
+    for b in range(2):
+        for r in range(b * 5 + j + 1, b * 5 + 5):
+            w.k_new[r] += 10.0
+            w.v_new[r] -= 7.0
+    o2 = R.workload_attn(w)
+    for b in range(2):
+        np.testing.assert_array_equal(o2[b * 5: b * 5 + j + 1], o1[b * 5: b * 5 + j + 1])
+        assert not np.allclose(o2[b * 5 + j + 1: b * 5 + 5], o1[b * 5 + j + 1: b * 5 + 5])
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    w = _tiny(B=2, K=2, H=6, Hkv=2, lens=(7, 2))
+    o = R.workload_attn(w)
+    G = 3
+    c = w.cfg
+    rep = lambda a: np.repeat(a, G, axis=1)
+    o_mha = R.verify_attn(w.q, rep(w.k_cache), rep(w.v_cache), w.kv_start, w.kv_len,
+                          rep(w.k_new), rep(w.v_new), c.B, c.K, 6, 6, c.D)
+    np.testing.assert_array_equal(o, o_mha)
+
+
+def test_bifurcated_prefix_equals_concatenated():
+    w = _tiny(B=3, K=2, H=2, Hkv=2, lens=(0, 4, 2), prefix=11)
+    o_bif = R.workload_attn(w)
+    c = w.cfg
+    P = 11
+    caps = w.kv_len.astype(np.int64) + P
+    starts = np.concatenate([[0], np.cumsum(caps)[:-1]])
+    kc = np.concatenate([np.concatenate([w.k_prefix, w.k_cache[s:s + L]])
+                         for s, L in zip(w.kv_start, w.kv_len)])
+    vc = np.concatenate([np.concatenate([w.v_prefix, w.v_cache[s:s + L]])
+                         for s, L in zip(w.kv_start, w.kv_len)])
+    o_cat = R.verify_attn(w.q, kc, vc, starts, caps.astype(np.int32), w.k_new, w.v_new,
+                          c.B, c.K, c.Hq, c.Hkv, c.D)
+    np.testing.assert_allclose(o_bif, o_cat, rtol=1e-13, atol=1e-13)
