@@ -1,0 +1,197 @@
+/*
+ * libspecverify -- the verify step of batched speculative sampling on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The step scores K draft tokens per sequence with the target model and keeps
+ * the longest prefix that the modified rejection scheme accepts:
+ *
+ *   spec_verify_attn  target attention for the K+1 verify queries of every
+ *                     sequence over its own ragged, unpadded KV cache, with an
+ *                     optional shared prompt prefix read once (bifurcated).
+ *   spec_accept       softmax with temperature and nucleus on target and draft
+ *                     logits, left-to-right accept test min(1, q/p), residual
+ *                     resample from (q - p)_+, bonus token when all K pass.
+ *   spec_compact_kv   padding-free compaction of the accepted tokens and KV rows.
+ *
+ * Sources, cited by page title and section:
+ *   [SpS] "Accelerating Large Language Model Decoding with Speculative
+ *         Sampling" (Chen et al.): "Conditional scoring", "Modified rejection
+ *         sampling", Theorem 1.
+ *   [BASS] "BASS: Batched Attention-optimized Speculative Sampling": abstract
+ *         (batched speculative decoding, each sequence its own accepted length).
+ *   [EMS] "EMS-SD: Efficient Multi-sample Speculative Decoding": abstract
+ *         (different accepted counts per sample, no padding tokens).
+ *   [BIF] bifurcated-attention abstract (Athiwaratkun et al.): attention split
+ *         into a GEMM over the shared prefill KV and one over per-sample KV;
+ *         same FLOPs, exact result, less memory IO.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is DEVICE memory, allocated and owned by the caller,
+ *     row-major and contiguous, unless its comment says "host".
+ *   - The library never allocates, never synchronizes the device, and enqueues
+ *     its kernels only on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Return value: SV_OK (0) or a negative sv_status.  On error nothing has
+ *     been enqueued and sv_last_error() (thread-local) describes the problem.
+ *   - `status`, where present, is a device int32 the caller zeroes; kernels
+ *     store the first data error they meet there (SV_DEV_*), never abort.
+ *   - `workspace` is caller-owned device memory of at least the size the
+ *     matching *_workspace_size call reports.  It must be zero-filled once
+ *     before its first use; every call leaves it ready for the next call.
+ *     One workspace serves one call at a time (calls on different streams
+ *     need different workspaces).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* sv_stream_t; /* = hipStream_t */
+
+typedef enum {
+    SV_OK = 0,
+    SV_ERR_INVALID_ARG = -1, /* null pointer, bad size or bad parameter value */
+    SV_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim)     */
+    SV_ERR_WORKSPACE = -3,   /* workspace smaller than required               */
+    SV_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed    */
+} sv_status;
+
+/* Element types of tensors. */
+enum { SV_F32 = 0, SV_BF16 = 1 };
+
+/* Device-side data errors written to `status` (first one wins). */
+enum {
+    SV_DEV_OK = 0,
+    SV_DEV_BAD_TOKEN = 1,   /* a draft or output token id outside [0, V)          */
+    SV_DEV_BAD_UNIFORM = 2, /* a uniform outside [0, 1)                           */
+    SV_DEV_BAD_LENGTH = 3,  /* kv_len[b] < 0 or above the host bound kv_len_host  */
+    SV_DEV_BAD_COUNT = 4    /* n_accepted[b] outside [0, K]                       */
+};
+
+/* Last error message of the calling thread ("" if none). */
+const char* sv_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int sv_version(void);
+
+/* ------------------------------------------------------------------------
+ * spec_verify_attn -- target attention of the K+1 verify queries.
+ *
+ * [SpS] "Conditional scoring": one target call scores all K drafted positions
+ * plus the next one; attention reads the KV cache of all previous tokens and
+ * its cost does not grow with K.  [BASS], [EMS]: sequences keep their own
+ * lengths, with no padding.  [BIF]: a prompt prefix shared by all sequences is
+ * read once for all of them, with the exact result.
+ *
+ * For sequence b (0 <= b < B), query j (0 <= j <= K) and query head h, with
+ * kv head g = h / (Hq / Hkv) (contiguous grouping; Hq == Hkv is MHA):
+ *   keys/values = prefix rows [0, prefix_len)            (if prefix_len > 0)
+ *              ++ cache rows kv_start[b] + [0, kv_len[b])
+ *              ++ new rows b*(K+1) + [0, j]               (causal among new rows)
+ *   out[b*(K+1)+j, h, :] = softmax(scale * K q) V,  scale = softmax_scale, or
+ *                          1/sqrt(D) when softmax_scale <= 0.
+ * No position term is added: q and k arrive position-encoded.
+ *
+ * q, out        [B*(K+1), Hq, D]   dtype; row b*(K+1)+j is query j of sequence b
+ * k_cache,
+ * v_cache       [rows, Hkv, D]     dtype; sequence b owns rows kv_start[b]..
+ * kv_start      [B] int64          first cache row of sequence b
+ * kv_len        [B] int32          rows cached BEFORE this step (L_b >= 0)
+ * kv_len_host   [B] int32, HOST    an upper bound of kv_len (e.g. a copy); it
+ *                                  sizes the grid and the workspace only
+ * k_new, v_new  [B*(K+1), Hkv, D]  K/V of the K+1 verify tokens
+ * k_prefix,
+ * v_prefix      [prefix_len, Hkv, D] shared prefix, or NULL with prefix_len 0
+ * dtype         SV_BF16 (MFMA path, D in {64, 128}) or SV_F32 (D <= 256)
+ * status        device int32 or NULL: SV_DEV_BAD_LENGTH if kv_len > bound
+ * Accumulation is fp32; bf16 outputs are rounded to nearest even.
+ * ------------------------------------------------------------------------ */
+int spec_verify_attn_workspace_size(int B, int K, int Hq, int Hkv, int D, int dtype,
+                                    const int32_t* kv_len_host, int prefix_len,
+                                    size_t* bytes);
+
+int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                     const int64_t* kv_start, const int32_t* kv_len,
+                     const int32_t* kv_len_host, const void* k_new, const void* v_new,
+                     const void* k_prefix, const void* v_prefix, int prefix_len,
+                     void* out, int B, int K, int Hq, int Hkv, int D, int dtype,
+                     float softmax_scale, int32_t* status, void* workspace,
+                     size_t workspace_bytes, sv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * spec_accept -- modified rejection sampling, one verify round per sequence.
+ *
+ * [SpS] "Modified rejection sampling": with q the target and p the draft
+ * distribution, draft x_j is accepted with probability min(1, q(x_j)/p(x_j)),
+ * left to right; at the first rejection the position is resampled from
+ * (q - p)_+ = max(0, q - p) / sum max(0, q - p); if all K are accepted a bonus
+ * token is sampled from the last target row.  Temperature and nucleus modify
+ * both distributions first.  Theorem 1: the emitted tokens follow q.
+ *
+ * Given the uniforms, the result is deterministic:
+ *   q'_j, p'_j : softmax((z - max z) / temperature), then, if top_p < 1, the
+ *                smallest tie-closed set of top tokens whose mass is >= top_p,
+ *                renormalised.
+ *   accept x_j iff u_accept[b, j] * p'_j(x_j) < q'_j(x_j)  (p' = 0: iff q' > 0)
+ *   draw       : the smallest token id i with u_sample[b] * S < C_i, C the
+ *                running sum of the weights in ascending id order, S = C_{V-1};
+ *                weights (q'_j - p'_j)_+ after a rejection at j (q'_j if that
+ *                has zero mass), q'_K for the bonus.
+ *   greedy != 0: accept while x_j == argmax target row j (lowest id on ties);
+ *                emit argmax of the stopping row; uniforms are not read.
+ * Precision: row normalisers, masses and the draw are computed in fp64.
+ *
+ * target_logits [B, K+1, V]  logits_dtype (SV_F32 or SV_BF16)
+ * draft_logits  [B, K, V]    logits_dtype; may be NULL iff greedy
+ * draft_tokens  [B, K] int32 ids in [0, V)
+ * u_accept      [B, K] float in [0, 1);  u_sample [B] float in [0, 1)
+ * temperature > 0;  0 < top_p <= 1 (1 disables the nucleus)
+ * n_accepted    [B] int32 out: n_b in [0, K]
+ * out_tokens    [B, K+1] int32 out: drafts 0..n_b-1, the drawn token at n_b,
+ *               -1 after it
+ * status        device int32 or NULL: SV_DEV_BAD_TOKEN / SV_DEV_BAD_UNIFORM
+ * ------------------------------------------------------------------------ */
+int spec_accept_workspace_size(int B, int K, int V, size_t* bytes);
+
+int spec_accept(const void* target_logits, const void* draft_logits, int logits_dtype,
+                const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                int B, int K, int V, float temperature, float top_p, int greedy,
+                int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
+                void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * spec_compact_kv -- padding-free compaction after a verify round.
+ *
+ * [EMS]: samples accept different numbers of tokens; they are packed without
+ * padding tokens.  With e_b = n_accepted[b] + 1:
+ *   cu_tokens[0] = 0, cu_tokens[b+1] = cu_tokens[b] + e_b
+ *   tokens_packed[cu_tokens[b] + i] = out_tokens[b, i]          (i < e_b)
+ *   cache rows kv_start[b] + kv_len[b] + i <- new rows b*(K+1) + i   (K and V)
+ *   kv_len[b] += e_b
+ * The KV of the inputs 0..n_b of the round becomes valid; the KV of the token
+ * drawn at n_b is produced by the next round.  The caller guarantees capacity
+ * for kv_len[b] + K + 1 rows at kv_start[b].
+ *
+ * n_accepted [B] int32, out_tokens [B, K+1] int32 (from spec_accept)
+ * kv_len     [B] int32 in/out;  kv_start [B] int64
+ * k_cache, v_cache [rows, Hkv, D] dtype, in/out;  k_new, v_new [B*(K+1), Hkv, D]
+ * tokens_packed [B*(K+1)] int32 out (first cu_tokens[B] valid; rest untouched)
+ * cu_tokens  [B+1] int32 out
+ * status     device int32 or NULL: SV_DEV_BAD_COUNT if n_accepted[b] not in [0, K]
+ *            (that sequence is then left unchanged)
+ * ------------------------------------------------------------------------ */
+int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
+                    const int64_t* kv_start, void* k_cache, void* v_cache,
+                    const void* k_new, const void* v_new, int32_t* tokens_packed,
+                    int32_t* cu_tokens, int B, int K, int Hkv, int D, int dtype,
+                    int32_t* status, sv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,227 @@
+// C ABI of libspecverify: argument validation, workspace sizing and kernel
+// launch.  Declarations and the meaning of every argument are in
+// include/specverify.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/specverify.h"
+#include "sv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return SV_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipStream_t as_stream(sv_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_attn_shape(int B, int K, int Hq, int Hkv, int D, int dtype, const int32_t* kv_len_host,
+                     int prefix_len) {
+    if (B < 1) return fail(SV_ERR_INVALID_ARG, "B must be >= 1 (got %d)", B);
+    if (B > 65536) return fail(SV_ERR_UNSUPPORTED, "B must be <= 65536 (got %d)", B);
+    if (K < 0) return fail(SV_ERR_INVALID_ARG, "K must be >= 0 (got %d)", K);
+    if (Hq < 1 || Hkv < 1) return fail(SV_ERR_INVALID_ARG, "head counts must be >= 1");
+    if (Hq % Hkv != 0)
+        return fail(SV_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (dtype != SV_F32 && dtype != SV_BF16)
+        return fail(SV_ERR_INVALID_ARG, "dtype must be SV_F32 or SV_BF16 (got %d)", dtype);
+    if (D < 1) return fail(SV_ERR_INVALID_ARG, "head_dim must be >= 1 (got %d)", D);
+    if (dtype == SV_BF16) {
+        if (D != 64 && D != 128)
+            return fail(SV_ERR_UNSUPPORTED, "bf16 attention supports head_dim 64 or 128 (got %d)", D);
+        if ((Hq / Hkv) * (K + 1) > 64)
+            return fail(SV_ERR_UNSUPPORTED,
+                        "bf16 attention supports (Hq/Hkv)*(K+1) <= 64 query columns per kv head "
+                        "(got %d)", (Hq / Hkv) * (K + 1));
+    } else if (D > 256 || D % 4 != 0) {
+        return fail(SV_ERR_UNSUPPORTED, "fp32 attention supports head_dim <= 256, multiple of 4 (got %d)", D);
+    }
+    if (prefix_len < 0) return fail(SV_ERR_INVALID_ARG, "prefix_len must be >= 0");
+    if (!kv_len_host) return fail(SV_ERR_INVALID_ARG, "kv_len_host is NULL");
+    for (int b = 0; b < B; ++b)
+        if (kv_len_host[b] < 0)
+            return fail(SV_ERR_INVALID_ARG, "kv_len_host[%d] = %d is negative", b, kv_len_host[b]);
+    return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sv_last_error(void) { return g_err; }
+
+int sv_version(void) { return 100; }
+
+int spec_verify_attn_workspace_size(int B, int K, int Hq, int Hkv, int D, int dtype,
+                                    const int32_t* kv_len_host, int prefix_len, size_t* bytes) {
+    int rc = check_attn_shape(B, K, Hq, Hkv, D, dtype, kv_len_host, prefix_len);
+    if (rc) return rc;
+    if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, prefix_len).bytes;
+    return ok();
+}
+
+int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                     const int64_t* kv_start, const int32_t* kv_len,
+                     const int32_t* kv_len_host, const void* k_new, const void* v_new,
+                     const void* k_prefix, const void* v_prefix, int prefix_len,
+                     void* out, int B, int K, int Hq, int Hkv, int D, int dtype,
+                     float softmax_scale, int32_t* status, void* workspace,
+                     size_t workspace_bytes, sv_stream_t stream) {
+    int rc = check_attn_shape(B, K, Hq, Hkv, D, dtype, kv_len_host, prefix_len);
+    if (rc) return rc;
+    if (!q || !k_cache || !v_cache || !kv_start || !kv_len || !k_new || !v_new || !out)
+        return fail(SV_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    if (prefix_len > 0 && (!k_prefix || !v_prefix))
+        return fail(SV_ERR_INVALID_ARG, "prefix_len > 0 needs k_prefix and v_prefix");
+    const size_t al = dtype == SV_BF16 ? 16 : 4;
+    if (!aligned(q, al) || !aligned(k_cache, al) || !aligned(v_cache, al) || !aligned(k_new, al) ||
+        !aligned(v_new, al) || !aligned(out, al) || (prefix_len > 0 && (!aligned(k_prefix, al) ||
+                                                                       !aligned(v_prefix, al))))
+        return fail(SV_ERR_INVALID_ARG, "tensors must be %zu-byte aligned", al);
+    if (!isfinite(softmax_scale)) return fail(SV_ERR_INVALID_ARG, "softmax_scale is not finite");
+    const sv::AttnPlan plan =
+        sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, prefix_len);
+    if (!workspace || workspace_bytes < plan.bytes)
+        return fail(SV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.bytes,
+                    workspace ? workspace_bytes : static_cast<size_t>(0));
+    sv::AttnArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.kv_start = kv_start;
+    a.kv_len = kv_len;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_prefix = prefix_len > 0 ? k_prefix : nullptr;
+    a.v_prefix = prefix_len > 0 ? v_prefix : nullptr;
+    a.out = out;
+    a.status = status;
+    a.B = B;
+    a.K = K;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.bf16 = dtype == SV_BF16;
+    a.prefix_len = prefix_len;
+    a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
+    a.workspace = workspace;
+    hipError_t e = sv::attn_launch(a, plan, as_stream(stream));
+    if (e != hipSuccess) return fail(SV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int spec_accept_workspace_size(int B, int K, int V, size_t* bytes) {
+    if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
+    if (V > sv::accept_max_vocab())
+        return fail(SV_ERR_UNSUPPORTED, "vocabulary above %d", sv::accept_max_vocab());
+    if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = sv::accept_workspace_bytes(B, K, V);
+    return ok();
+}
+
+int spec_accept(const void* target_logits, const void* draft_logits, int logits_dtype,
+                const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                int B, int K, int V, float temperature, float top_p, int greedy,
+                int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
+                void* workspace, size_t workspace_bytes, sv_stream_t stream) {
+    if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
+    if (V > sv::accept_max_vocab())
+        return fail(SV_ERR_UNSUPPORTED, "vocabulary above %d", sv::accept_max_vocab());
+    if (logits_dtype != SV_F32 && logits_dtype != SV_BF16)
+        return fail(SV_ERR_INVALID_ARG, "logits_dtype must be SV_F32 or SV_BF16");
+    if (!(temperature > 0.0f) || !isfinite(temperature))
+        return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0");
+    if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(SV_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+    if (B == 0) return ok();
+    if (!target_logits || !n_accepted || !out_tokens)
+        return fail(SV_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    if (K > 0 && !draft_tokens) return fail(SV_ERR_INVALID_ARG, "draft_tokens is NULL");
+    if (!greedy) {
+        if (!u_sample || (K > 0 && (!u_accept || !draft_logits)))
+            return fail(SV_ERR_INVALID_ARG, "draft_logits, u_accept and u_sample are required unless greedy");
+    }
+    const size_t need = sv::accept_workspace_bytes(B, K, V);
+    if (!workspace || workspace_bytes < need)
+        return fail(SV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : static_cast<size_t>(0));
+    const size_t al = logits_dtype == SV_BF16 ? 8 : 16;
+    if (V % 4 == 0 && (!aligned(target_logits, al) || (draft_logits && !aligned(draft_logits, al))))
+        return fail(SV_ERR_INVALID_ARG, "logits must be %zu-byte aligned", al);
+    sv::AcceptArgs a{};
+    a.target_logits = target_logits;
+    a.draft_logits = draft_logits;
+    a.draft_tokens = draft_tokens;
+    a.u_accept = u_accept;
+    a.u_sample = u_sample;
+    a.n_accepted = n_accepted;
+    a.out_tokens = out_tokens;
+    a.status = status;
+    a.workspace = workspace;
+    a.B = B;
+    a.K = K;
+    a.V = V;
+    a.bf16 = logits_dtype == SV_BF16;
+    a.greedy = greedy ? 1 : 0;
+    a.temperature = temperature;
+    a.top_p = top_p;
+    hipError_t e = sv::accept_launch(a, as_stream(stream));
+    if (e != hipSuccess) return fail(SV_ERR_HIP, "sampler launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
+                    const int64_t* kv_start, void* k_cache, void* v_cache,
+                    const void* k_new, const void* v_new, int32_t* tokens_packed,
+                    int32_t* cu_tokens, int B, int K, int Hkv, int D, int dtype,
+                    int32_t* status, sv_stream_t stream) {
+    if (B < 0 || K < 0 || Hkv < 1 || D < 1)
+        return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, Hkv >= 1, D >= 1");
+    if (dtype != SV_F32 && dtype != SV_BF16)
+        return fail(SV_ERR_INVALID_ARG, "dtype must be SV_F32 or SV_BF16");
+    const int es = dtype == SV_BF16 ? 2 : 4;
+    if ((static_cast<size_t>(Hkv) * D * es) % 4 != 0)
+        return fail(SV_ERR_UNSUPPORTED, "a KV row must be a multiple of 4 bytes");
+    if (B == 0) return ok();
+    if (!n_accepted || !out_tokens || !kv_len || !kv_start || !k_cache || !v_cache || !k_new ||
+        !v_new || !tokens_packed || !cu_tokens)
+        return fail(SV_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    sv::CompactArgs a{};
+    a.n_accepted = n_accepted;
+    a.out_tokens = out_tokens;
+    a.kv_len = kv_len;
+    a.kv_start = kv_start;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.tokens_packed = tokens_packed;
+    a.cu_tokens = cu_tokens;
+    a.status = status;
+    a.B = B;
+    a.K = K;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.elem_bytes = es;
+    hipError_t e = sv::compact_launch(a, as_stream(stream));
+    if (e != hipSuccess) return fail(SV_ERR_HIP, "compaction launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,723 @@
+// Target attention for the K+1 verify queries of every sequence, on gfx950.
+//
+// Method: "Accelerating Large Language Model Decoding with Speculative
+// Sampling", section "Conditional scoring" (one target call scores all drafted
+// positions; attention reads the whole KV cache and its cost does not grow with
+// K); sequences keep ragged, unpadded lengths (BASS and EMS-SD abstracts); a
+// prompt prefix shared by all sequences is read once (bifurcated-attention
+// abstract: a GEMM over the shared prefill KV plus one over per-sample KV,
+// exact result).
+//
+// Work decomposition (split-K over keys, flash-decoding style):
+//   decode_bf16_kernel  one workgroup per (sequence chunk, kv head).  The keys
+//       of sequence b are its L_b cached rows followed by its K+1 new rows; a
+//       chunk is `chunk` consecutive keys.  Each of the 4 waves takes 16-key
+//       slices; S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K rows go straight
+//       from HBM into A-operand registers), an fp32 online softmax per query
+//       column, and O^T += V^T P^T with v_mfma_f32_16x16x16_bf16 (V is
+//       transposed through LDS).  The query columns of a kv head are its
+//       G = Hq/Hkv heads times the K+1 queries, in 16-wide tiles.
+//   prefix_bf16_kernel  one workgroup per (prefix chunk, kv head, column
+//       group): every query column of every sequence against one 64-key LDS
+//       tile at a time, so the shared prefix is read from HBM once.
+//   attn_f32_kernel  fp32 VALU path (small head dims, fp32 inputs).
+//   merge_kernel  log-sum-exp merge of the partial (m, l, o) of all chunks.
+// Scores are kept in the log2 domain (scale * log2(e) folded into S).
+#include <stdlib.h>
+
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 256;
+
+struct AttnParams {
+    const uint16_t* q;
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const uint16_t* k_prefix;
+    const uint16_t* v_prefix;
+    const float* qf;
+    const float* kcf;
+    const float* vcf;
+    const float* knf;
+    const float* vnf;
+    const float* kpf;
+    const float* vpf;
+    const int64_t* kv_start;
+    const int32_t* kv_len;
+    void* out;
+    int32_t* status;
+    float* part_o;     // [slots][Hkv][CPG][D]
+    float2* part_ml;   // [slots][Hkv][CPG]  (m in log2 units, l)
+    int* seq_base;     // [B] first slot of sequence b
+    float* pre_o;      // [prefix_slots][Hkv][NC][D]
+    float2* pre_ml;    // [prefix_slots][Hkv][NC]
+    int B, K, Hq, Hkv, G, CPG, NC, D, chunk, prefix_chunk, prefix_len, prefix_slots, slots;
+    int bf16;
+    float scale_log2;
+};
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Work item x (a global chunk index) -> (sequence, chunk within it), computed by
+// wave 0 from the device lengths; writes s_b = -1 when x is past the last chunk.
+__device__ void find_sequence(const AttnParams& p, int x, int g, int* s_b, int* s_c) {
+    const int lane = threadIdx.x & 63;
+    int run = 0, fb = -1, fc = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+        const int b = b0 + lane;
+        int n = 0;
+        if (b < p.B) {
+            int L = p.kv_len[b];
+            if (L < 0) {
+                if (x == 0 && g == 0) set_status(p.status, 3);
+                L = 0;
+            }
+            n = ceil_div(L + p.K + 1, p.chunk);
+        }
+        const int inc = wave_incl_scan(n, lane) + run;
+        const int excl = inc - n;
+        if (b < p.B && x >= excl && x < inc) { fb = b; fc = x - excl; }
+        run = __shfl(inc, 63, 64);
+    }
+    // fold the owning lane's answer into lane 0
+    unsigned long long own = __ballot(fb >= 0);
+    int src = own ? __ffsll(own) - 1 : 0;
+    fb = __shfl(fb, src, 64);
+    fc = __shfl(fc, src, 64);
+    if (lane == 0) {
+        *s_b = own ? fb : -1;
+        *s_c = fc;
+        if (x == 0 && g == 0 && run > p.slots) set_status(p.status, 3);
+    }
+}
+
+
+// ---------------------------------------------------------------- decode (bf16)
+
+template <int D>
+struct DecodeLds {
+    static constexpr int VP = D + 4;  // V slice pitch (bf16): conflict-free transposed reads
+    union {
+        uint16_t vs[4][16][VP];
+        struct {
+            float o[4][16][D];
+            float m[4][16];
+            float l[4][16];
+        } red;
+    };
+    int sb, sc;
+};
+
+template <int D, int NCT>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(AttnParams p) {
+    constexpr int KK = D / 32;   // 16x16x32 steps over the head dim
+    constexpr int DT = D / 16;   // 16-wide head-dim tiles of the PV product
+    constexpr int VCH = D / 8;   // 16-byte chunks per K/V row
+    constexpr int VLD = 16 * VCH / 64;  // 16-byte V loads per lane per slice
+    __shared__ DecodeLds<D> S;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = blockIdx.y;
+    if (w == 0) find_sequence(p, blockIdx.x, g, &S.sb, &S.sc);
+    __syncthreads();
+    const int b = S.sb, c = S.sc;
+    if (b < 0) return;
+    if (c == 0 && g == 0 && tid == 0) p.seq_base[b] = blockIdx.x;
+
+    const int K1 = p.K + 1;
+    const int L = max(p.kv_len[b], 0);
+    const int T = L + K1;
+    const int t_begin = c * p.chunk;
+    const int t_end = min(T, t_begin + p.chunk);
+    const int64_t kv0 = p.kv_start[b];
+    const int col16 = lane & 15, kg = lane >> 4;
+
+    // Q^T operands and causal limits of this lane's columns
+    bf16x8 qv[NCT][KK];
+    int lim[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int col = ct * 16 + col16;
+        if (col < p.CPG) {
+            const int hh = col / K1, j = col % K1;
+            const int h = g * p.G + hh;
+            const uint16_t* qp = p.q + ((static_cast<size_t>(b) * K1 + j) * p.Hq + h) * D + kg * 8;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                qv[ct][kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
+            lim[ct] = L + j + 1;
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qv[ct][kk][e] = static_cast<__bf16>(0.0f);
+            lim[ct] = 0;
+        }
+    }
+
+    floatx4 o[NCT][DT];
+    float mrun[NCT], lrun[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        mrun[ct] = -INFINITY;
+        lrun[ct] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[ct][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const size_t head_off = static_cast<size_t>(g) * D;
+    const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
+    // K/V row of key t of sequence b (keys past T clamp to the last new row)
+    auto krow = [&](int t, const uint16_t* cache, const uint16_t* fresh) -> const uint16_t* {
+        t = min(t, T - 1);
+        return (t < L) ? cache + static_cast<size_t>(kv0 + t) * row_stride + head_off
+                       : fresh + static_cast<size_t>(b * K1 + (t - L)) * row_stride + head_off;
+    };
+
+    uint16_t(*vs)[DecodeLds<D>::VP] = S.vs[w];
+    for (int t0 = t_begin + 16 * w; t0 < t_end; t0 += 64) {
+        // K slice: lane holds key t0 + col16, head-dim chunks kg*8 + 32*kk
+        bf16x8 kr[KK];
+        const uint16_t* kp = krow(t0 + col16, p.k_cache, p.k_new) + kg * 8;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kr[kk] = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
+        // V slice in natural layout -> LDS
+        uint4 vr[VLD];
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+            const int qi = i * 64 + lane;
+            const int kl = qi / VCH, dc = qi % VCH;
+            vr[i] = *reinterpret_cast<const uint4*>(krow(t0 + kl, p.v_cache, p.v_new) + dc * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < VLD; ++i) {
+            const int qi = i * 64 + lane;
+            const int kl = qi / VCH, dc = qi % VCH;
+            uint2* dst = reinterpret_cast<uint2*>(&vs[kl][dc * 8]);
+            dst[0] = make_uint2(vr[i].x, vr[i].y);
+            dst[1] = make_uint2(vr[i].z, vr[i].w);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // V^T operands: lane (d = dt*16 + col16) holds keys kg*4 .. kg*4+3
+        shortx4 va[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                va[dt][e] = static_cast<short>(vs[kg * 4 + e][dt * 16 + col16]);
+        }
+
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qv[ct][kk], acc, 0, 0, 0);
+            float s[4];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = t0 + kg * 4 + e;
+                s[e] = (t < lim[ct]) ? acc[e] * p.scale_log2 : -INFINITY;
+                mt = fmaxf(mt, s[e]);
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float mnew = fmaxf(mrun[ct], mt);
+            float alpha = 1.0f;
+            shortx4 pb;
+            if (mnew == -INFINITY) {
+                pb = shortx4{0, 0, 0, 0};
+            } else {
+                alpha = exp2f(mrun[ct] - mnew);
+                float ps = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pe = exp2f(s[e] - mnew);
+                    ps += pe;
+                    pb[e] = static_cast<short>(f32_to_bf16(pe));
+                }
+                lrun[ct] = lrun[ct] * alpha + ps;
+                mrun[ct] = mnew;
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                o[ct][dt] *= alpha;
+                o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, o[ct][dt], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        lrun[ct] += __shfl_xor(lrun[ct], 16, 64);
+        lrun[ct] += __shfl_xor(lrun[ct], 32, 64);
+    }
+
+    // combine the 4 waves (fixed order) and write this chunk's partials
+    const size_t slot_col0 = (static_cast<size_t>(blockIdx.x) * p.Hkv + g) * p.CPG;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        __syncthreads();
+        if (kg == 0) {
+            S.red.m[w][col16] = mrun[ct];
+            S.red.l[w][col16] = lrun[ct];
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S.red.o[w][col16][dt * 16 + kg * 4 + e] = o[ct][dt][e];
+        __syncthreads();
+        for (int idx = tid; idx < 16 * D; idx += kThreads) {
+            const int cl = idx / D, d = idx % D;
+            const int col = ct * 16 + cl;
+            if (col >= p.CPG) continue;
+            float ms = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ms = fmaxf(ms, S.red.m[u][cl]);
+            float acc = 0.0f, l = 0.0f;
+            if (ms != -INFINITY) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float mu = S.red.m[u][cl];
+                    const float f = (mu == -INFINITY) ? 0.0f : exp2f(mu - ms);
+                    acc += S.red.o[u][cl][d] * f;
+                    l += S.red.l[u][cl] * f;
+                }
+            }
+            p.part_o[(slot_col0 + col) * D + d] = acc;
+            if (d == 0) p.part_ml[slot_col0 + col] = make_float2(ms, l);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- prefix (bf16)
+
+template <int D>
+struct PrefixLds {
+    static constexpr int KP = D + 8;  // K tile pitch (bf16)
+    static constexpr int VP = D + 4;  // V tile pitch (bf16)
+    uint16_t ks[64][KP];
+    uint16_t vs[64][VP];
+};
+
+// grid: x = prefix chunk, y = kv head, z = column group (16 tiles of 16 columns);
+// block: one wave per column tile of the group.
+template <int D>
+__global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
+    constexpr int KK = D / 32, DT = D / 16, VCH = D / 8;
+    __shared__ PrefixLds<D> S;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nthreads = blockDim.x;
+    const int x = blockIdx.x, g = blockIdx.y;
+    const int K1 = p.K + 1;
+    const int t_begin = x * p.prefix_chunk;
+    const int t_end = min(p.prefix_len, t_begin + p.prefix_chunk);
+    const int col16 = lane & 15, kg = lane >> 4;
+    const int tile = blockIdx.z * 16 + w;
+    const int cg = tile * 16 + col16;           // global column: b*CPG + hh*(K+1) + j
+    const bool active = tile * 16 < p.NC;
+
+    bf16x8 qv[KK];
+    if (cg < p.NC) {
+        const int bb = cg / p.CPG, cl = cg % p.CPG;
+        const int hh = cl / K1, j = cl % K1;
+        const uint16_t* qp =
+            p.q + ((static_cast<size_t>(bb) * K1 + j) * p.Hq + g * p.G + hh) * D + kg * 8;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qv[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[kk][e] = static_cast<__bf16>(0.0f);
+    }
+
+    floatx4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.0f;
+    const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
+
+    for (int tb = t_begin; tb < t_end; tb += 64) {
+        // cooperative load of the 64-key K and V tiles
+        for (int qi = tid; qi < 2 * 64 * VCH; qi += nthreads) {
+            const int isv = qi >= 64 * VCH;
+            const int r = (qi % (64 * VCH)) / VCH, dc = qi % VCH;
+            const int t = min(tb + r, p.prefix_len - 1);
+            const uint16_t* src = (isv ? p.v_prefix : p.k_prefix) +
+                                  static_cast<size_t>(t) * row_stride + static_cast<size_t>(g) * D +
+                                  dc * 8;
+            uint4 v = *reinterpret_cast<const uint4*>(src);
+            uint16_t* dst = isv ? &S.vs[r][dc * 8] : &S.ks[r][dc * 8];
+            reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+            reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+        }
+        __syncthreads();
+        if (active) {
+            floatx4 acc[4];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                acc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    const uint2* src =
+                        reinterpret_cast<const uint2*>(&S.ks[kt * 16 + col16][kg * 8 + 32 * kk]);
+                    uint2 lo = src[0], hi = src[1];
+                    uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    bf16x8 ka = *reinterpret_cast<bf16x8*>(&u);
+                    acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv[kk], acc[kt], 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = tb + kt * 16 + kg * 4 + e;
+                    acc[kt][e] = (t < t_end) ? acc[kt][e] * p.scale_log2 : -INFINITY;
+                    mt = fmaxf(mt, acc[kt][e]);
+                }
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float mnew = fmaxf(mrun, mt);   // finite: every tile has a valid key
+            const float alpha = exp2f(mrun - mnew);
+            float ps = 0.0f;
+            shortx4 pb[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pe = exp2f(acc[kt][e] - mnew);
+                    ps += pe;
+                    pb[kt][e] = static_cast<short>(f32_to_bf16(pe));
+                }
+            lrun = lrun * alpha + ps;
+            mrun = mnew;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    shortx4 va;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        va[e] = static_cast<short>(S.vs[kt * 16 + kg * 4 + e][dt * 16 + col16]);
+                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kt], o[dt], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    lrun += __shfl_xor(lrun, 16, 64);
+    lrun += __shfl_xor(lrun, 32, 64);
+    if (cg < p.NC) {
+        const size_t base = (static_cast<size_t>(x) * p.Hkv + g) * p.NC + cg;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.pre_o[base * D + dt * 16 + kg * 4 + e] = o[dt][e];
+        if (kg == 0) p.pre_ml[base] = make_float2(mrun, lrun);
+    }
+}
+
+// ---------------------------------------------------------------- fp32 path
+
+// mode 0: per-sequence chunks (grid.x = slot); mode 1: prefix chunks (grid.x = chunk).
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p, int mode) {
+    __shared__ float sc[1024];
+    __shared__ float red[kThreads / 64];
+    __shared__ double redd[kThreads / 64];
+    __shared__ int sb, scc;
+    const int tid = threadIdx.x;
+    const int g = blockIdx.y, x = blockIdx.x;
+    const int K1 = p.K + 1, D = p.D;
+    const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
+    int b = 0, t_begin, t_end, ncols, L = 0;
+    int64_t kv0 = 0;
+    if (mode == 0) {
+        if (tid < 64) find_sequence(p, x, g, &sb, &scc);
+        __syncthreads();
+        b = sb;
+        if (b < 0) return;
+        if (scc == 0 && g == 0 && tid == 0) p.seq_base[b] = x;
+        L = max(p.kv_len[b], 0);
+        kv0 = p.kv_start[b];
+        t_begin = scc * p.chunk;
+        t_end = min(L + K1, t_begin + p.chunk);
+        ncols = p.CPG;
+    } else {
+        t_begin = x * p.prefix_chunk;
+        t_end = min(p.prefix_len, t_begin + p.prefix_chunk);
+        ncols = p.NC;
+    }
+    const int nk = t_end - t_begin;
+    auto key_ptr = [&](int t, bool v) -> const float* {
+        if (mode == 1)
+            return (v ? p.vpf : p.kpf) + static_cast<size_t>(t) * row_stride + static_cast<size_t>(g) * D;
+        return (t < L) ? (v ? p.vcf : p.kcf) + static_cast<size_t>(kv0 + t) * row_stride + static_cast<size_t>(g) * D
+                       : (v ? p.vnf : p.knf) + static_cast<size_t>(b * K1 + t - L) * row_stride + static_cast<size_t>(g) * D;
+    };
+    for (int col = 0; col < ncols; ++col) {
+        int bb = b, cl = col;
+        if (mode == 1) { bb = col / p.CPG; cl = col % p.CPG; }
+        const int hh = cl / K1, j = cl % K1;
+        const float* qp = p.qf + ((static_cast<size_t>(bb) * K1 + j) * p.Hq + g * p.G + hh) * D;
+        const int lim = (mode == 1) ? t_end : min(t_end, L + j + 1);
+        float lm = -INFINITY;
+        for (int i = tid; i < nk; i += kThreads) {
+            const int t = t_begin + i;
+            float s = -INFINITY;
+            if (t < lim) {
+                const float* kp = key_ptr(t, false);
+                float dot = 0.0f;
+                for (int d = 0; d < D; ++d) dot = fmaf(qp[d], kp[d], dot);
+                s = dot * p.scale_log2;
+            }
+            sc[i] = s;
+            lm = fmaxf(lm, s);
+        }
+        const float m = block_max<kThreads>(lm, red);
+        double ls = 0.0;
+        for (int i = tid; i < nk; i += kThreads) {
+            const float pe = (m == -INFINITY) ? 0.0f : exp2f(sc[i] - m);
+            sc[i] = pe;
+            ls += pe;
+        }
+        const double l = block_sum<kThreads>(ls, redd);
+        __syncthreads();
+        size_t base;
+        float* po;
+        float2* pml;
+        if (mode == 0) {
+            base = (static_cast<size_t>(x) * p.Hkv + g) * p.CPG + col;
+            po = p.part_o; pml = p.part_ml;
+        } else {
+            base = (static_cast<size_t>(x) * p.Hkv + g) * p.NC + col;
+            po = p.pre_o; pml = p.pre_ml;
+        }
+        for (int d = tid; d < D; d += kThreads) {
+            float acc = 0.0f;
+            for (int i = 0; i < nk; ++i)
+                if (sc[i] != 0.0f) acc = fmaf(sc[i], key_ptr(t_begin + i, true)[d], acc);
+            po[base * D + d] = acc;
+        }
+        if (tid == 0) pml[base] = make_float2(m, static_cast<float>(l));
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- merge
+
+// grid: one block per (row, head); threads over the head dim.
+__global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
+    const int r = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+    const int K1 = p.K + 1;
+    const int b = r / K1, j = r % K1;
+    const int g = h / p.G, hh = h % p.G;
+    const int col = hh * K1 + j;
+    const int L = max(p.kv_len[b], 0);
+    int n = ceil_div(L + K1, p.chunk);
+    int base = p.seq_base[b];
+    // A device length above the host bound has no work items (status 3 is set
+    // by the chunk kernel); keep every read inside the partial buffers.
+    base = min(max(base, 0), p.slots - 1);
+    n = min(n, p.slots - base);
+    const size_t pcol = static_cast<size_t>(b) * p.CPG + col;
+
+    float ms = -INFINITY;
+    for (int i = 0; i < p.prefix_slots; ++i)
+        ms = fmaxf(ms, p.pre_ml[(static_cast<size_t>(i) * p.Hkv + g) * p.NC + pcol].x);
+    for (int i = 0; i < n; ++i)
+        ms = fmaxf(ms, p.part_ml[(static_cast<size_t>(base + i) * p.Hkv + g) * p.CPG + col].x);
+
+    for (int d = threadIdx.x; d < p.D; d += blockDim.x) {
+        float acc = 0.0f, l = 0.0f;
+        for (int i = 0; i < p.prefix_slots; ++i) {
+            const size_t idx = (static_cast<size_t>(i) * p.Hkv + g) * p.NC + pcol;
+            const float2 ml = p.pre_ml[idx];
+            const float f = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - ms);
+            acc += p.pre_o[idx * p.D + d] * f;
+            l += ml.y * f;
+        }
+        for (int i = 0; i < n; ++i) {
+            const size_t idx = (static_cast<size_t>(base + i) * p.Hkv + g) * p.CPG + col;
+            const float2 ml = p.part_ml[idx];
+            const float f = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - ms);
+            acc += p.part_o[idx * p.D + d] * f;
+            l += ml.y * f;
+        }
+        const float val = acc / l;
+        const size_t oi = (static_cast<size_t>(r) * p.Hq + h) * p.D + d;
+        if (p.bf16)
+            static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(val);
+        else
+            static_cast<float*>(p.out)[oi] = val;
+    }
+}
+
+int env_int(const char* name, int dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    int v = atoi(s);
+    return v > 0 ? v : dflt;
+}
+
+}  // namespace
+
+AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
+                   const int32_t* kv_len_host, int prefix_len) {
+    AttnPlan pl{};
+    const int K1 = K + 1;
+    long long keys = 0;
+    for (int b = 0; b < B; ++b) keys += (kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1;
+    int chunk = env_int("SPECVERIFY_ATTN_CHUNK", 0);
+    if (chunk <= 0) {
+        // largest power-of-two chunk (64..1024) that still gives >= 4 work items per CU
+        chunk = 64;
+        for (int c = 1024; c >= 64; c >>= 1) {
+            long long items = 0;
+            for (int b = 0; b < B; ++b)
+                items += ((kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1 + c - 1) / c;
+            if (items * Hkv >= 1024) { chunk = c; break; }
+        }
+    }
+    chunk = (chunk + 63) / 64 * 64;
+    if (chunk > 1024) chunk = 1024;
+    (void)keys;
+    int slots = 0;
+    for (int b = 0; b < B; ++b)
+        slots += ((kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1 + chunk - 1) / chunk;
+    int pchunk = env_int("SPECVERIFY_PREFIX_CHUNK", 1024);
+    pchunk = (pchunk + 63) / 64 * 64;
+    if (!bf16 && pchunk > 1024) pchunk = 1024;
+    const int pslots = prefix_len > 0 ? (prefix_len + pchunk - 1) / pchunk : 0;
+    const size_t CPG = static_cast<size_t>(Hq / Hkv) * K1;
+    const size_t NC = CPG * B;
+    size_t off = 0;
+    auto take = [&](size_t n) { off = (off + 255) & ~static_cast<size_t>(255); off += n; };
+    take(static_cast<size_t>(slots) * Hkv * CPG * D * 4);
+    take(static_cast<size_t>(slots) * Hkv * CPG * 8);
+    take(static_cast<size_t>(B) * 4);
+    take(static_cast<size_t>(pslots) * Hkv * NC * D * 4);
+    take(static_cast<size_t>(pslots) * Hkv * NC * 8);
+    pl.chunk = chunk;
+    pl.prefix_chunk = pchunk;
+    pl.slots = slots;
+    pl.prefix_slots = pslots;
+    pl.bytes = (off + 255) & ~static_cast<size_t>(255);
+    return pl;
+}
+
+hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
+    AttnParams p{};
+    p.q = static_cast<const uint16_t*>(a.q);
+    p.k_cache = static_cast<const uint16_t*>(a.k_cache);
+    p.v_cache = static_cast<const uint16_t*>(a.v_cache);
+    p.k_new = static_cast<const uint16_t*>(a.k_new);
+    p.v_new = static_cast<const uint16_t*>(a.v_new);
+    p.k_prefix = static_cast<const uint16_t*>(a.k_prefix);
+    p.v_prefix = static_cast<const uint16_t*>(a.v_prefix);
+    p.qf = static_cast<const float*>(a.q);
+    p.kcf = static_cast<const float*>(a.k_cache);
+    p.vcf = static_cast<const float*>(a.v_cache);
+    p.knf = static_cast<const float*>(a.k_new);
+    p.vnf = static_cast<const float*>(a.v_new);
+    p.kpf = static_cast<const float*>(a.k_prefix);
+    p.vpf = static_cast<const float*>(a.v_prefix);
+    p.kv_start = a.kv_start;
+    p.kv_len = a.kv_len;
+    p.out = a.out;
+    p.status = a.status;
+    p.B = a.B;
+    p.K = a.K;
+    p.Hq = a.Hq;
+    p.Hkv = a.Hkv;
+    p.G = a.Hq / a.Hkv;
+    p.CPG = p.G * (a.K + 1);
+    p.NC = p.CPG * a.B;
+    p.D = a.D;
+    p.chunk = pl.chunk;
+    p.prefix_chunk = pl.prefix_chunk;
+    p.prefix_len = a.prefix_len;
+    p.prefix_slots = pl.prefix_slots;
+    p.slots = pl.slots;
+    p.bf16 = a.bf16;
+    p.scale_log2 = a.scale * kLog2e;
+
+    char* base = static_cast<char*>(a.workspace);
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        off = (off + 255) & ~static_cast<size_t>(255);
+        char* r = base + off;
+        off += n;
+        return r;
+    };
+    const size_t CPG = p.CPG, NC = p.NC;
+    p.part_o = reinterpret_cast<float*>(take(static_cast<size_t>(pl.slots) * a.Hkv * CPG * a.D * 4));
+    p.part_ml = reinterpret_cast<float2*>(take(static_cast<size_t>(pl.slots) * a.Hkv * CPG * 8));
+    p.seq_base = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * 4));
+    p.pre_o = reinterpret_cast<float*>(take(static_cast<size_t>(pl.prefix_slots) * a.Hkv * NC * a.D * 4));
+    p.pre_ml = reinterpret_cast<float2*>(take(static_cast<size_t>(pl.prefix_slots) * a.Hkv * NC * 8));
+
+    if (a.bf16) {
+        if (pl.prefix_slots > 0) {
+            const int tiles = (p.NC + 15) / 16;
+            const int groups = (tiles + 15) / 16;
+            const int waves = tiles < 16 ? tiles : 16;
+            dim3 grid(pl.prefix_slots, a.Hkv, groups);
+            if (a.D == 128)
+                hipLaunchKernelGGL(prefix_bf16_kernel<128>, grid, dim3(waves * 64), 0, stream, p);
+            else
+                hipLaunchKernelGGL(prefix_bf16_kernel<64>, grid, dim3(waves * 64), 0, stream, p);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        const int nct = (p.CPG + 15) / 16;
+        dim3 grid(pl.slots, a.Hkv);
+#define SV_DECODE(DD, NN) hipLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream, p)
+        if (a.D == 128) {
+            switch (nct) {
+                case 1: SV_DECODE(128, 1); break;
+                case 2: SV_DECODE(128, 2); break;
+                case 3: SV_DECODE(128, 3); break;
+                default: SV_DECODE(128, 4); break;
+            }
+        } else {
+            switch (nct) {
+                case 1: SV_DECODE(64, 1); break;
+                case 2: SV_DECODE(64, 2); break;
+                case 3: SV_DECODE(64, 3); break;
+                default: SV_DECODE(64, 4); break;
+            }
+        }
+#undef SV_DECODE
+    } else {
+        if (pl.prefix_slots > 0) {
+            hipLaunchKernelGGL(attn_f32_kernel, dim3(pl.prefix_slots, a.Hkv), dim3(kThreads), 0,
+                               stream, p, 1);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(attn_f32_kernel, dim3(pl.slots, a.Hkv), dim3(kThreads), 0, stream, p, 0);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int mthreads = a.D <= 64 ? 64 : (a.D <= 128 ? 128 : 256);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.B * (a.K + 1) * a.Hq), dim3(mthreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,80 @@
+// Padding-free compaction after a verify round, on gfx950.
+//
+// Method: "EMS-SD: Efficient Multi-sample Speculative Decoding" (abstract):
+// samples accept different numbers of tokens in the verification phase; they
+// are handled without padding tokens, so no extra memory or compute is spent.
+// With e_b = n_b + 1 tokens emitted by sequence b ("Accelerating Large Language
+// Model Decoding with Speculative Sampling", "Modified rejection sampling": at
+// least one and at most K+1 tokens per round):
+//   cu = exclusive scan of e;  packed[cu_b + i] = out_tokens[b, i];
+//   cache rows L_b .. L_b + n_b of b <- new rows 0 .. n_b;  L_b += e_b.
+// One workgroup per sequence; it computes its own scan offset, so the kernel
+// needs no cross-workgroup synchronisation.
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int emitted(int n, int K) { return (n >= 0 && n <= K) ? n + 1 : 0; }
+
+__global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
+    __shared__ int red[kThreads / 64];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int K1 = a.K + 1;
+    const int nb = a.n_accepted[b];
+    const int e = emitted(nb, a.K);
+    if (tid == 0 && e == 0) set_status(a.status, 4);
+
+    int part = 0;
+    for (int i = tid; i < b; i += kThreads) part += emitted(a.n_accepted[i], a.K);
+    const int cu = block_sum<kThreads>(part, red);
+    if (tid == 0) {
+        a.cu_tokens[b] = cu;
+        if (b == a.B - 1) a.cu_tokens[a.B] = cu + e;
+    }
+    for (int i = tid; i < e; i += kThreads)
+        a.tokens_packed[cu + i] = a.out_tokens[static_cast<size_t>(b) * K1 + i];
+
+    const int L = a.kv_len[b];
+    const size_t row_bytes = static_cast<size_t>(a.Hkv) * a.D * a.elem_bytes;
+    const size_t dst0 = static_cast<size_t>(a.kv_start[b] + L) * row_bytes;
+    const size_t src0 = static_cast<size_t>(b) * K1 * row_bytes;
+    const size_t nbytes = static_cast<size_t>(e) * row_bytes;
+    if (row_bytes % 16 == 0) {
+        const size_t n16 = nbytes / 16;
+        for (size_t i = tid; i < 2 * n16; i += kThreads) {
+            const bool v = i >= n16;
+            const size_t k = v ? i - n16 : i;
+            const uint4* src = reinterpret_cast<const uint4*>(
+                static_cast<const char*>(v ? a.v_new : a.k_new) + src0) + k;
+            uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(v ? a.v_cache : a.k_cache) + dst0) + k;
+            *dst = *src;
+        }
+    } else {
+        const size_t n4 = nbytes / 4;
+        for (size_t i = tid; i < 2 * n4; i += kThreads) {
+            const bool v = i >= n4;
+            const size_t k = v ? i - n4 : i;
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                static_cast<const char*>(v ? a.v_new : a.k_new) + src0) + k;
+            uint32_t* dst =
+                reinterpret_cast<uint32_t*>(static_cast<char*>(v ? a.v_cache : a.k_cache) + dst0) + k;
+            *dst = *src;
+        }
+    }
+    __syncthreads();  // every thread has read kv_len[b]
+    if (tid == 0) a.kv_len[b] = L + e;
+}
+
+}  // namespace
+
+hipError_t compact_launch(const CompactArgs& a, hipStream_t stream) {
+    if (a.B == 0) return hipSuccess;
+    hipLaunchKernelGGL(compact_kernel, dim3(a.B), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,124 @@
+// Device-side helpers shared by the gfx950 kernels of libspecverify.
+// Wave64 reductions, bf16 packing, and the MFMA operand vector types.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Inclusive prefix sum across the wave in lane order (Hillis-Steele).
+__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        double t = __shfl_up(v, o, kWave);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int t = __shfl_up(v, o, kWave);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Block-wide reductions for blockDim.x == NT (multiple of 64).  `red` is LDS
+// scratch of at least NT/64 elements.  Every thread gets the result.  The
+// combination order is fixed, so results are bit-reproducible.
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_max(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) r = fmaxf(r, red[i]);
+    return r;
+}
+
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    double r = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) r += red[i];
+    return r;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_sum(int v, int* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    int r = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / 64; ++i) r += red[i];
+    return r;
+}
+
+// Workgroups are handed to the 8 XCDs of an MI355X round-robin by linear id.
+// xcd_remap(L, n) returns a logical index such that logical indices
+// [k*(n/8), (k+1)*(n/8)) all run on XCD k: consecutive logical blocks share an
+// L2.  n must be a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int L, int n) {
+    return (L & 7) * (n >> 3) + (L >> 3);
+}
+
+// Record the first device-side data error (0 = none).
+__device__ __forceinline__ void set_status(int32_t* status, int code) {
+    if (status) atomicCAS(status, 0, code);
+}
+
+}  // namespace sv

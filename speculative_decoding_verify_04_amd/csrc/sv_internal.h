@@ -1,0 +1,77 @@
+// Host-side interface between the C ABI layer (api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int64_t* kv_start;
+    const int32_t* kv_len;
+    const void* k_new;
+    const void* v_new;
+    const void* k_prefix;
+    const void* v_prefix;
+    void* out;
+    int32_t* status;
+    int B, K, Hq, Hkv, D, bf16, prefix_len;
+    float scale;
+    int chunk;          // keys per split-K work item of the per-sequence part
+    int prefix_chunk;   // keys per work item of the shared prefix
+    int slots;          // split-K work items per kv head (host upper bound)
+    void* workspace;
+};
+
+// Chunking decisions made on the host from the host length bound.
+struct AttnPlan {
+    int chunk, prefix_chunk, slots, prefix_slots;
+    size_t bytes;
+};
+
+AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
+                   const int32_t* kv_len_host, int prefix_len);
+hipError_t attn_launch(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
+
+// ---------------------------------------------------------------- sampler
+struct AcceptArgs {
+    const void* target_logits;
+    const void* draft_logits;
+    const int32_t* draft_tokens;
+    const float* u_accept;
+    const float* u_sample;
+    int32_t* n_accepted;
+    int32_t* out_tokens;
+    int32_t* status;
+    void* workspace;
+    int B, K, V, bf16, greedy;
+    float temperature, top_p;
+};
+
+size_t accept_workspace_bytes(int B, int K, int V);
+int accept_max_vocab();
+hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- compaction
+struct CompactArgs {
+    const int32_t* n_accepted;
+    const int32_t* out_tokens;
+    int32_t* kv_len;
+    const int64_t* kv_start;
+    void* k_cache;
+    void* v_cache;
+    const void* k_new;
+    const void* v_new;
+    int32_t* tokens_packed;
+    int32_t* cu_tokens;
+    int32_t* status;
+    int B, K, Hkv, D, elem_bytes;
+};
+
+hipError_t compact_launch(const CompactArgs& a, hipStream_t stream);
+
+}  // namespace sv

@@ -211,12 +211,14 @@ def _draft_sample(z: np.ndarray, temperature: float, top_p: float, greedy: bool,
 
 
 def make_workload(cfg: Config, sub_seed: int = 0, growth_rows: int = 0,
-                  lens: Optional[np.ndarray] = None) -> Workload:
+                  lens: Optional[np.ndarray] = None, with_kv: bool = True) -> Workload:
     """Build the inputs of one verify step for ``cfg``.
 
     ``growth_rows`` reserves that many extra cache rows per sequence beyond
     L_b + K + 1, so that repeated compaction (which appends accepted rows) stays
     inside each sequence's region.  ``lens`` overrides the sampled KV lengths.
+    ``with_kv=False`` skips the attention tensors (they become 1-row
+    placeholders) for sampler-only use; the sampler inputs are unchanged.
     """
     ss = np.random.SeedSequence([cfg.seed, sub_seed])
     (s_len, s_q, s_kc, s_vc, s_kn, s_vn, s_pre, s_tl, s_dn, s_dt,
@@ -231,13 +233,17 @@ def make_workload(cfg: Config, sub_seed: int = 0, growth_rows: int = 0,
     kv_start = np.concatenate([[0], np.cumsum(cap)[:-1]]).astype(np.int64)
     rows = int(cap.sum())
 
+    if not with_kv:
+        R, Hq, Hkv, D, rows = 1, 1, 1, 8, 1
+        kv_len = np.zeros(B, np.int32)
+        kv_start = np.zeros(B, np.int64)
     q = _normal_kv(np.random.default_rng(s_q), (R, Hq, D), cfg.kv_dtype)
     fill = _NAN_BF16 if cfg.kv_dtype == BF16 else np.float32(np.nan)
     kdt = np.uint16 if cfg.kv_dtype == BF16 else np.float32
     k_cache = np.full((rows, Hkv, D), fill, dtype=kdt)
     v_cache = np.full((rows, Hkv, D), fill, dtype=kdt)
     rk, rv = np.random.default_rng(s_kc), np.random.default_rng(s_vc)
-    for b in range(B):
+    for b in range(B if with_kv else 0):
         n = int(kv_len[b])
         s0 = int(kv_start[b])
         if n:
@@ -246,7 +252,7 @@ def make_workload(cfg: Config, sub_seed: int = 0, growth_rows: int = 0,
     k_new = _normal_kv(np.random.default_rng(s_kn), (R, Hkv, D), cfg.kv_dtype)
     v_new = _normal_kv(np.random.default_rng(s_vn), (R, Hkv, D), cfg.kv_dtype)
     k_prefix = v_prefix = None
-    if cfg.prefix_len:
+    if cfg.prefix_len and with_kv:
         rp = np.random.default_rng(s_pre)
         k_prefix = _normal_kv(rp, (cfg.prefix_len, Hkv, D), cfg.kv_dtype)
         v_prefix = _normal_kv(rp, (cfg.prefix_len, Hkv, D), cfg.kv_dtype)

@@ -103,11 +103,9 @@ def make_cases():
     return cases
 
 
-def run_case(sampler, case: Case, n=N_TRIALS, seed=0):
-    """Run ``n`` independent verify rounds on the fixed rows of ``case``.
-
-    Each trial draws its own draft tokens x_j ~ p'_j and its own uniforms.
-    """
+def make_trials(case: Case, n=N_TRIALS, seed=0):
+    """Inputs of ``n`` independent verify rounds on the fixed rows of ``case``:
+    each trial draws its own draft tokens x_j ~ p'_j and its own uniforms."""
     rng = np.random.default_rng(seed)
     K, V = case.K, case.V
     zt = np.ascontiguousarray(np.broadcast_to(case.zt, (n, K + 1, V)))
@@ -117,6 +115,12 @@ def run_case(sampler, case: Case, n=N_TRIALS, seed=0):
         tok[:, j] = rng.choice(V, size=n, p=case.p_mod[j] / case.p_mod[j].sum())
     ua = (rng.integers(0, 2 ** 24, size=(n, K)) * 2.0 ** -24).astype(np.float32)
     us = (rng.integers(0, 2 ** 24, size=n) * 2.0 ** -24).astype(np.float32)
+    return zt, zd, tok, ua, us
+
+
+def run_case(sampler, case: Case, n=N_TRIALS, seed=0):
+    """Run ``n`` independent verify rounds of ``case`` through ``sampler``."""
+    zt, zd, tok, ua, us = make_trials(case, n, seed)
     res = sampler(zt, zd, tok, ua, us, case.temperature, case.top_p, False)
     return tok, res
 

@@ -1,0 +1,378 @@
+"""GPU path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Bars:
+  * attention: per output row, max_d |o - o_ref| <= tol * max_d |o_ref|, with
+    tol = 1e-2 for bf16 inputs (fp32 accumulation) and 1e-5 for fp32.
+  * sampler: n_accepted and out_tokens bit-exact, except that a decision the
+    oracle flags as ambiguous (|u p - q| < 1e-6 p, a draw or nucleus boundary
+    within 1e-12 of its edge) releases that sequence from that position on;
+    flagged decisions must stay below 0.01% of all decisions.
+  * compaction: bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import specref as R
+from speculative_decoding_verify_04_amd import api
+from speculative_decoding_verify_04_amd import workloads as W
+from speculative_decoding_verify_04_amd.devio import kv_tensor, to_device
+
+import pins
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- helpers
+
+def run_attn(w, t, scale=0.0):
+    c = w.cfg
+    t.status.zero_()
+    api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, w.kv_len, t.k_new,
+                         t.v_new, t.out, c.K, k_prefix=t.k_prefix, v_prefix=t.v_prefix,
+                         softmax_scale=scale, status=t.status, check_rows=True)
+    torch.cuda.synchronize()
+    assert int(t.status.item()) == 0
+    return t.out.float().cpu().numpy().astype(np.float64)
+
+
+def attn_errors(o, ref):
+    """Row-relative infinity-norm error per output row."""
+    num = np.abs(o - ref).max(axis=-1)
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    return num / den
+
+
+def attn_tol(cfg):
+    return 1e-5 if cfg.kv_dtype == W.F32 else 1e-2
+
+
+def run_accept(w, t, greedy=None):
+    c = w.cfg
+    g = c.greedy if greedy is None else greedy
+    t.status.zero_()
+    api.spec_accept(t.target_logits, None if g else t.draft_logits, t.draft_tokens, t.u_accept,
+                    t.u_sample, c.temperature, c.top_p, g, t.n_accepted, t.out_tokens,
+                    status=t.status)
+    torch.cuda.synchronize()
+    assert int(t.status.item()) == 0, api.device_error_name(int(t.status.item()))
+    return t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy()
+
+
+def compare_accept(n, toks, ref, K):
+    """Bit-exact outside flagged decisions.  Returns (#sequences compared fully)."""
+    full = 0
+    for b in range(n.shape[0]):
+        f, nr = int(ref["flag_pos"][b]), int(ref["n_accepted"][b])
+        if f < 0 or f > nr:
+            assert n[b] == nr, (b, n[b], nr)
+            assert np.array_equal(toks[b], ref["out_tokens"][b]), (b, toks[b], ref["out_tokens"][b])
+            full += 1
+        else:
+            assert n[b] >= f, (b, n[b], f)
+            assert np.array_equal(toks[b, :f], ref["out_tokens"][b, :f])
+    return full
+
+
+class FlagBudget:
+    def __init__(self):
+        self.decisions = 0
+        self.flagged = 0
+
+    def add(self, ref):
+        self.decisions += ref["n_decisions"]
+        self.flagged += ref["n_flagged"]
+
+    def check(self):
+        assert self.decisions > 0
+        assert self.flagged <= 1e-4 * self.decisions, (self.flagged, self.decisions)
+
+
+def gpu_sampler(zt, zd, tok, ua, us, T, top_p, greedy):
+    B, K1, V = zt.shape
+    K = K1 - 1
+    dev = DEV
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    out = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    api.spec_accept(torch.from_numpy(np.ascontiguousarray(zt)).to(dev),
+                    None if greedy else torch.from_numpy(np.ascontiguousarray(zd)).to(dev),
+                    torch.from_numpy(np.ascontiguousarray(tok, np.int32)).to(dev),
+                    torch.from_numpy(np.ascontiguousarray(ua, np.float32)).to(dev),
+                    torch.from_numpy(np.ascontiguousarray(us, np.float32)).to(dev),
+                    T, top_p, greedy, n, out, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    return {"n_accepted": n.cpu().numpy(), "out_tokens": out.cpu().numpy()}
+
+
+# ---------------------------------------------------------------- attention: small shapes
+
+SMALL_ATTN = {
+    "tiny_fp32": W.CONFIGS["tiny_fp32"],
+    "fp32_d64_prefix": W.small_variant(W.CONFIGS["prefix_b32k4"], kv_dtype=W.F32, B=3, Hq=4,
+                                       Hkv=2, D=64, prefix_len=300, len_lo=0, len_hi=90, V=64),
+    "bf16_mha_d128": W.small_variant(W.CONFIGS["bass_b8k5"], B=4, Hq=4, Hkv=4, len_lo=0,
+                                     len_hi=700, V=64),
+    "bf16_mha_d64": W.small_variant(W.CONFIGS["bass_b8k5"], B=3, Hq=3, Hkv=3, D=64, len_lo=1,
+                                    len_hi=300, V=64),
+    "bf16_gqa_k8": W.small_variant(W.CONFIGS["gqa_b64k8"], B=5, Hq=8, Hkv=2, len_lo=100,
+                                   len_hi=900, V=64),
+    "bf16_gqa_g8_k7": W.small_variant(W.CONFIGS["gqa_b64k8"], B=2, K=7, Hq=16, Hkv=2, D=64,
+                                      len_lo=10, len_hi=200, V=64),
+    "bf16_prefix": W.small_variant(W.CONFIGS["prefix_b32k4"], B=6, Hq=4, Hkv=4, prefix_len=700,
+                                   len_lo=0, len_hi=40, V=64),
+    "bf16_prefix_gqa_many_cols": W.small_variant(W.CONFIGS["prefix_b32k4"], B=60, K=4, Hq=8,
+                                                 Hkv=2, prefix_len=1100, len_lo=0, len_hi=20,
+                                                 V=64),
+    "bf16_k0_single_query": W.small_variant(W.CONFIGS["bass_b8k5"], K=0, B=3, Hq=2, Hkv=2,
+                                            len_lo=0, len_hi=200, V=64),
+    "bf16_all_empty_cache": W.small_variant(W.CONFIGS["bass_b8k5"], B=4, Hq=2, Hkv=2, len_lo=0,
+                                            len_hi=0, V=64),
+    "chinchilla_heads8": W.small_variant(W.CONFIGS["chinchilla_b1k4"], Hq=8, Hkv=8, V=64),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_ATTN))
+def test_attention_small(name):
+    cfg = SMALL_ATTN[name]
+    say(f"[attn small] {name}")
+    w = W.make_workload(cfg, sub_seed=21)
+    t = to_device(w, DEV)
+    o = run_attn(w, t)
+    ref = R.workload_attn(w)
+    err = attn_errors(o, ref)
+    assert np.isfinite(o).all()
+    assert err.max() <= attn_tol(cfg), (name, float(err.max()))
+
+
+def test_attention_custom_scale_and_determinism():
+    cfg = SMALL_ATTN["bf16_gqa_k8"]
+    w = W.make_workload(cfg, sub_seed=3)
+    t = to_device(w, DEV)
+    o1 = run_attn(w, t, scale=0.05)
+    o2 = run_attn(w, t, scale=0.05)
+    assert np.array_equal(o1, o2)
+    ref = R.verify_attn(w.q, w.k_cache, w.v_cache, w.kv_start, w.kv_len, w.k_new, w.v_new,
+                        cfg.B, cfg.K, cfg.Hq, cfg.Hkv, cfg.D, scale=0.05)
+    assert attn_errors(o1, ref).max() <= 1e-2
+
+
+def test_attention_bifurcated_equals_concatenated_gpu():
+    """Prefix read once == the same prefix copied into every sequence's cache."""
+    cfg = SMALL_ATTN["bf16_prefix"]
+    w = W.make_workload(cfg, sub_seed=8)
+    t = to_device(w, DEV)
+    o_bif = run_attn(w, t)
+    P = w.prefix_len
+    lens = w.kv_len.astype(np.int64) + P
+    caps = lens + cfg.K + 1
+    starts = np.concatenate([[0], np.cumsum(caps)[:-1]])
+    kc = np.zeros((int(caps.sum()), cfg.Hkv, cfg.D), np.uint16)
+    vc = np.zeros_like(kc)
+    for b in range(cfg.B):
+        s, L = int(w.kv_start[b]), int(w.kv_len[b])
+        kc[starts[b]:starts[b] + P] = w.k_prefix
+        vc[starts[b]:starts[b] + P] = w.v_prefix
+        kc[starts[b] + P:starts[b] + P + L] = w.k_cache[s:s + L]
+        vc[starts[b] + P:starts[b] + P + L] = w.v_cache[s:s + L]
+    out = torch.empty_like(t.q)
+    api.spec_verify_attn(t.q, kv_tensor(kc, DEV), kv_tensor(vc, DEV),
+                         torch.from_numpy(starts.astype(np.int64)).to(DEV),
+                         torch.from_numpy(lens.astype(np.int32)).to(DEV), lens, t.k_new,
+                         t.v_new, out, cfg.K)
+    torch.cuda.synchronize()
+    o_cat = out.float().cpu().numpy().astype(np.float64)
+    ref = R.workload_attn(w)
+    assert attn_errors(o_bif, ref).max() <= 1e-2
+    assert attn_errors(o_cat, ref).max() <= 1e-2
+    assert attn_errors(o_bif, o_cat).max() <= 1e-2
+
+
+# ---------------------------------------------------------------- attention: full sizes
+
+FULL = ["bass_b8k5", "chinchilla_b1k4", "gqa_b64k8", "prefix_b32k4"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_attention_full_size_sampled(name):
+    cfg = W.CONFIGS[name]
+    say(f"[attn full] {name}: generating")
+    w = W.make_workload(cfg, sub_seed=0)
+    t = to_device(w, DEV)
+    say(f"[attn full] {name}: running B={cfg.B} K={cfg.K} Hq={cfg.Hq} Hkv={cfg.Hkv}")
+    o = run_attn(w, t)
+    assert np.isfinite(o).all()
+    rng = np.random.default_rng(5)
+    R_ = cfg.rows
+    # the longest sequence's rows, the first and last rows, and random rows
+    bmax = int(np.argmax(w.kv_len))
+    rows = [0, R_ - 1, bmax * (cfg.K + 1), bmax * (cfg.K + 1) + cfg.K]
+    rows += list(rng.integers(0, R_, size=28))
+    heads = [0, cfg.Hq - 1] + list(rng.integers(0, cfg.Hq, size=len(rows) - 2))
+    ref = R.workload_attn(w, sel_rows=rows, sel_heads=heads)
+    got = o[rows, heads]
+    err = attn_errors(got, ref)
+    assert err.max() <= 1e-2, (name, float(err.max()))
+
+
+# ---------------------------------------------------------------- sampler
+
+ACCEPT_CFGS = ["tiny_fp32", "bass_b8k5", "chinchilla_b1k4", "chinchilla_b1k4_greedy",
+               "gqa_b64k8", "prefix_b32k4"]
+
+
+@pytest.mark.parametrize("name", ACCEPT_CFGS)
+def test_accept_full_size(name):
+    cfg = W.CONFIGS[name]
+    budget = FlagBudget()
+    seeds = range(6) if cfg.B * cfg.V < 2_000_000 else range(2)
+    for sub in seeds:
+        say(f"[accept] {name} seed {sub}")
+        w = W.make_workload(cfg, sub_seed=sub, with_kv=False)
+        t = to_device(w, DEV)
+        n, toks = run_accept(w, t)
+        ref = R.workload_accept(w)
+        budget.add(ref)
+        compare_accept(n, toks, ref, cfg.K)
+        pins.check_counts({"n_accepted": n, "out_tokens": toks}, w.draft_tokens, cfg.K, cfg.V)
+    budget.check()
+
+
+@pytest.mark.parametrize("logits", ["f32", "bf16"])
+def test_accept_many_sequences_small_vocab(logits):
+    """Ragged vocab (not a multiple of 4), many sequences, K=3, nucleus."""
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=512, K=3, V=1001, top_p=0.9, temperature=0.7)
+    w = W.make_workload(cfg, sub_seed=4, with_kv=False)
+    if logits == "bf16":
+        # bf16 logits: the oracle sees the same (exactly upcast) values
+        w.target_logits = W.bf16_bits_to_f32(W.f32_to_bf16_bits(w.target_logits))
+        w.draft_logits = W.bf16_bits_to_f32(W.f32_to_bf16_bits(w.draft_logits))
+    t = to_device(w, DEV, logits_dtype=torch.bfloat16 if logits == "bf16" else torch.float32)
+    n, toks = run_accept(w, t)
+    ref = R.workload_accept(w)
+    compare_accept(n, toks, ref, cfg.K)
+
+
+def test_accept_k0_bonus_only():
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=64, K=0, V=5000)
+    w = W.make_workload(cfg, sub_seed=2, with_kv=False)
+    t = to_device(w, DEV)
+    n, toks = run_accept(w, t)
+    ref = R.workload_accept(w)
+    compare_accept(n, toks, ref, 0)
+    assert np.all(n == 0)
+
+
+def test_accept_p_equals_q_accepts_all():
+    cfg = W.CONFIGS["bass_b8k5"]
+    w = W.make_workload(cfg, sub_seed=9, with_kv=False)
+    w.draft_logits = np.ascontiguousarray(w.target_logits[:, : cfg.K])
+    w.draft_tokens = np.argmax(w.draft_logits, axis=-1).astype(np.int32)
+    t = to_device(w, DEV)
+    n, toks = run_accept(w, t)
+    assert np.all(n == cfg.K)
+    compare_accept(n, toks, R.workload_accept(w), cfg.K)
+
+
+def test_accept_flat_rows_use_exact_fallback():
+    """All-equal logits: the nucleus boundary bin holds the whole row (radix path)."""
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=4, K=2, V=8192, top_p=0.5)
+    w = W.make_workload(cfg, sub_seed=1, with_kv=False)
+    w.target_logits[:] = 0.25
+    w.target_logits[1, 0, 17] = 3.0       # one peaked row mixed in
+    w.draft_logits[:] = 0.25
+    w.draft_tokens[:] = np.arange(cfg.B * cfg.K, dtype=np.int32).reshape(cfg.B, cfg.K) * 7
+    t = to_device(w, DEV)
+    n, toks = run_accept(w, t)
+    compare_accept(n, toks, R.workload_accept(w), cfg.K)
+
+
+def test_accept_wide_rows_deep_threshold():
+    """Low temperature and top_p close to 1: the nucleus boundary lies far below the max."""
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=16, K=3, V=20000, top_p=0.9999,
+                          temperature=0.05, target_sigma=1.0)
+    w = W.make_workload(cfg, sub_seed=6, with_kv=False)
+    t = to_device(w, DEV)
+    n, toks = run_accept(w, t)
+    compare_accept(n, toks, R.workload_accept(w), cfg.K)
+
+
+def test_accept_bad_token_sets_status():
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=4, K=2, V=3000)
+    w = W.make_workload(cfg, sub_seed=1, with_kv=False)
+    t = to_device(w, DEV)
+    t.draft_tokens[2, 1] = cfg.V + 5
+    api.spec_accept(t.target_logits, t.draft_logits, t.draft_tokens, t.u_accept, t.u_sample,
+                    cfg.temperature, cfg.top_p, False, t.n_accepted, t.out_tokens,
+                    status=t.status)
+    torch.cuda.synchronize()
+    assert int(t.status.item()) == 1
+
+
+@pytest.mark.parametrize("case", ["dirichlet_v8", "nucleus", "temp_half", "disjoint"])
+def test_theorem1_on_gpu(case):
+    """The GPU sampler passes the same Theorem-1 pins as the oracle (10^6 trials)."""
+    c = {x.name: x for x in pins.make_cases()}[case]
+    pv, res, tok = pins.theorem1_pvalues(gpu_sampler, c, seed=17)
+    assert min(pv) > pins.ALPHA, pv
+    assert all(abs(z) < 5 for z in pins.accept_rate_z(res, c))
+    assert pins.scan_length_pvalue(res, c) > pins.ALPHA
+
+
+@pytest.mark.parametrize("case", ["dirichlet_v8", "nucleus", "disjoint"])
+def test_accept_gpu_matches_oracle_many_trials(case):
+    """Same 200k trials through both: bit-exact outside flagged decisions."""
+    c = {x.name: x for x in pins.make_cases()}[case]
+    zt, zd, tok, ua, us = pins.make_trials(c, n=200_000, seed=3)
+    res = gpu_sampler(zt, zd, tok, ua, us, c.temperature, c.top_p, False)
+    ref = R.accept(zt, zd, tok, ua, us, c.temperature, c.top_p)
+    compare_accept(res["n_accepted"], res["out_tokens"], ref, c.K)
+
+
+# ---------------------------------------------------------------- compaction
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "bass_b8k5"])
+def test_compaction_matches_oracle(name):
+    cfg = W.CONFIGS[name]
+    if name != "tiny_fp32":
+        cfg = W.small_variant(cfg, B=8, Hq=4, Hkv=4, len_lo=5, len_hi=300, V=4096)
+    w = W.make_workload(cfg, sub_seed=12)
+    t = to_device(w, DEV)
+    n, toks = run_accept(w, t)
+    t.status.zero_()
+    api.spec_compact_kv(t.n_accepted, t.out_tokens, t.kv_len, t.kv_start, t.k_cache, t.v_cache,
+                        t.k_new, t.v_new, t.tokens_packed, t.cu_tokens, status=t.status)
+    torch.cuda.synchronize()
+    assert int(t.status.item()) == 0
+    packed, cu, kl, kc, vc = R.compact_kv(n, toks, w.kv_len, w.kv_start, w.k_cache, w.v_cache,
+                                          w.k_new, w.v_new, cfg.K, cfg.Hkv, cfg.D)
+    assert np.array_equal(t.cu_tokens.cpu().numpy(), cu)
+    assert np.array_equal(t.kv_len.cpu().numpy(), kl)
+    assert np.array_equal(t.tokens_packed.cpu().numpy()[: cu[-1]], packed[: cu[-1]])
+    view = np.uint16 if cfg.kv_dtype == W.BF16 else np.uint32
+    got_k = t.k_cache.view(torch.int16 if view == np.uint16 else torch.int32).cpu().numpy()
+    got_v = t.v_cache.view(torch.int16 if view == np.uint16 else torch.int32).cpu().numpy()
+    assert np.array_equal(got_k.view(view), kc.view(view))
+    assert np.array_equal(got_v.view(view), vc.view(view))
+
+
+def test_compaction_rejects_bad_count():
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=3, Hq=2, Hkv=2, len_lo=5, len_hi=30, V=512)
+    w = W.make_workload(cfg, sub_seed=1)
+    t = to_device(w, DEV)
+    t.n_accepted.copy_(torch.tensor([1, cfg.K + 3, 0], dtype=torch.int32))
+    t.out_tokens.fill_(3)
+    api.spec_compact_kv(t.n_accepted, t.out_tokens, t.kv_len, t.kv_start, t.k_cache, t.v_cache,
+                        t.k_new, t.v_new, t.tokens_packed, t.cu_tokens, status=t.status)
+    torch.cuda.synchronize()
+    assert int(t.status.item()) == 4
+    kl = t.kv_len.cpu().numpy()
+    assert kl[1] == w.kv_len[1] and kl[0] == w.kv_len[0] + 2 and kl[2] == w.kv_len[2] + 1
+    assert t.cu_tokens.cpu().numpy().tolist() == [0, 2, 2, 3]
