@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Throughput of the batched speculative-sampling verify step on one MI355X.
+
+One step = spec_verify_attn + spec_accept + spec_compact_kv over one batch of
+the workload (default: B=8 sequences, K=5 drafts, 32 heads x D128, ragged KV
+lengths U{512..2048}, V=49152, bf16 KV, fp32 logits, T=0.8, nucleus 0.95).
+
+Inputs are synthetic and seeded; `--sets` input sets (default 6, ~1.1 GB) are
+resident in HBM before timing and the steps rotate through them, so the 256 MB
+Infinity Cache cannot serve a step from the previous use of its inputs.  The
+timed steps are captured into one HIP graph (the per-step host work of the
+ctypes binding would otherwise exceed the GPU time); the timed region is one
+replay between two device synchronisations.  The dominant kernel's duration is
+then measured with HIP events around it over the same rotation of sets.
+
+Compaction appends each set's accepted KV rows, so a set's KV grows by its
+emitted tokens on every use, as in real decoding; the byte counts follow the
+realised lengths.  Printed: one JSON line (metric, value = verified tokens/s,
+roofline of the dominant kernel timed live with HIP events, the CPU oracle
+baseline).
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verified tokens/sec per verify step (B=8,K=5 ragged); % of HBM peak GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=12)
+    ap.add_argument("--config", default="bass_b8k5")
+    ap.add_argument("--sets", type=int, default=6, help="rotating input sets resident in HBM")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample (0: skip)")
+    ap.add_argument("--traffic-json", default=None,
+                    help="HBM counter summary of the dominant kernel (default: profiles/)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent helpers over libamdhip64 (torch events do not expose their handle)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.h.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        return ms.value if rc == 0 else None
+
+
+def kernel_source_hash():
+    with open(os.path.join(ROOT, "speculative_decoding_verify_04_amd", "csrc", "attn.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verify step is "
+              "built and measured on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib_mib:
+        copy_calibration(args.copy_calib_mib)
+        return
+
+    import numpy as np
+    import torch
+
+    from speculative_decoding_verify_04_amd import api
+    from speculative_decoding_verify_04_amd import workloads as W
+    from speculative_decoding_verify_04_amd.devio import to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[args.config]
+    B, K = cfg.B, cfg.K
+    S = args.sets
+    steps, warmup = args.steps, args.warmup
+    uses_max = math.ceil((steps + warmup) / S) + 1
+    growth = (K + 1) * (uses_max + 1)
+
+    t_gen = time.perf_counter()
+    sets = [W.make_workload(cfg, sub_seed=s, growth_rows=growth) for s in range(S)]
+    dsets = [to_device(w, dev) for w in sets]
+    bounds = [[int(x) + growth for x in w.kv_len] for w in sets]
+    print(f"# generated and uploaded {S} input sets in {time.perf_counter() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+
+    P = cfg.prefix_len
+    ws_attn = max(api.spec_verify_attn_workspace_size(B, K, cfg.Hq, cfg.Hkv, cfg.D,
+                                                      api.SV_BF16 if cfg.kv_dtype == W.BF16
+                                                      else api.SV_F32, bnd, P)
+                  for bnd in bounds)
+    ws_acc = api.spec_accept_workspace_size(B, K, cfg.V)
+    wa = torch.zeros(ws_attn, dtype=torch.uint8, device=dev)
+    wacc = torch.zeros(ws_acc, dtype=torch.uint8, device=dev)
+
+    def step(s):
+        t = dsets[s]
+        api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, bounds[s], t.k_new,
+                             t.v_new, t.out, K, k_prefix=t.k_prefix, v_prefix=t.v_prefix,
+                             status=t.status, workspace=wa)
+        api.spec_accept(t.target_logits, None if cfg.greedy else t.draft_logits, t.draft_tokens,
+                        t.u_accept, t.u_sample, cfg.temperature, cfg.top_p, cfg.greedy,
+                        t.n_accepted, t.out_tokens, status=t.status, workspace=wacc)
+        api.spec_compact_kv(t.n_accepted, t.out_tokens, t.kv_len, t.kv_start, t.k_cache,
+                            t.v_cache, t.k_new, t.v_new, t.tokens_packed, t.cu_tokens,
+                            status=t.status)
+
+    # Reference tokens of every set (the sampler does not depend on the KV state).
+    ref_n, ref_tok = [], []
+    for s in range(S):
+        t = dsets[s]
+        api.spec_accept(t.target_logits, None if cfg.greedy else t.draft_logits, t.draft_tokens,
+                        t.u_accept, t.u_sample, cfg.temperature, cfg.top_p, cfg.greedy,
+                        t.n_accepted, t.out_tokens, status=t.status, workspace=wacc)
+        torch.cuda.synchronize()
+        ref_n.append(t.n_accepted.cpu().numpy().copy())
+        ref_tok.append(t.out_tokens.cpu().numpy().copy())
+    emitted = [int((n + 1).sum()) for n in ref_n]
+
+    # The warm-up steps and the timed steps are each captured into one HIP graph
+    # (step i uses input set i % S); one replay runs them back to back.
+    cap_stream = torch.cuda.Stream()
+
+    def capture(n, first):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for i in range(first, first + n):
+                step(i % S)
+        return g
+
+    g_warm = capture(warmup, 0) if warmup else None
+    g_timed = capture(steps, warmup)
+    torch.cuda.synchronize()
+    uses = [0] * S
+    if g_warm is not None:
+        g_warm.replay()
+        for i in range(warmup):
+            uses[i % S] += 1
+    torch.cuda.synchronize()
+    use_at_start = list(uses)
+
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    g_timed.replay()
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_stop)
+    timed_sets = [(warmup + i) % S for i in range(steps)]
+
+    # Dominant kernel: the split-K chunk kernel of spec_verify_attn, bracketed by
+    # HIP events recorded on its stream by the library (events cannot be graph
+    # nodes here, so this loop launches eagerly, over the same rotation of sets
+    # and the KV lengths the timed steps left behind).
+    hip = Hip()
+    evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    kern_bytes = []
+    for i in range(steps):
+        s = timed_sets[i]
+        t = dsets[s]
+        api.sv_set_kernel_events(*evs[i])
+        api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, bounds[s], t.k_new,
+                             t.v_new, t.out, K, k_prefix=t.k_prefix, v_prefix=t.v_prefix,
+                             status=t.status, workspace=wa)
+    api.sv_set_kernel_events(None, None)
+    torch.cuda.synchronize()
+
+    # Check every set's last outputs against its reference (graph replays vs eager).
+    for s in range(S):
+        t = dsets[s]
+        st = int(t.status.item())
+        assert st == 0, f"set {s}: device status {st} ({api.device_error_name(st)})"
+        assert np.array_equal(t.n_accepted.cpu().numpy(), ref_n[s]), f"set {s}: n_accepted"
+        assert np.array_equal(t.out_tokens.cpu().numpy(), ref_tok[s]), f"set {s}: out_tokens"
+
+    # Bytes and tokens of every timed step from the realised lengths.
+    es = 2 if cfg.kv_dtype == W.BF16 else 4
+    row_kv = cfg.Hkv * cfg.D * es * 2
+    R = cfg.rows
+    tokens = 0
+    step_bytes = 0
+    uses = list(use_at_start)
+    for i in range(steps):
+        s = timed_sets[i]
+        L = sets[s].kv_len.astype(np.int64) + uses[s] * (ref_n[s].astype(np.int64) + 1)
+        uses[s] += 1
+        b = W.algorithmic_bytes(cfg, L, P)
+        step_bytes += b["attn"] + b["accept"]
+        tokens += emitted[s]
+    for i in range(steps):  # the kernel-timing loop ran on the lengths after the timed steps
+        s = timed_sets[i]
+        L = sets[s].kv_len.astype(np.int64) + uses[s] * (ref_n[s].astype(np.int64) + 1)
+        kern_bytes.append(int(L.sum()) * row_kv + R * row_kv + R * cfg.Hq * cfg.D * es)
+    kern_ms = [hip.elapsed_ms(*evs[i]) for i in range(steps)]
+    kern_ok = all(m is not None and m > 0 for m in kern_ms)
+    kern_avg_us = 1e3 * sum(kern_ms) / steps if kern_ok else None
+    achieved = (sum(kern_bytes) / (1e-3 * sum(kern_ms))) / 1e9 if kern_ok else None
+
+    # HBM counter summary (if one was taken for the current kernel source)
+    traffic = None
+    tj = args.traffic_json or os.path.join(ROOT, "profiles", f"traffic_{args.config}.json")
+    if os.path.exists(tj):
+        with open(tj) as f:
+            tr = json.load(f)
+        if tr.get("attn_source_sha256_16") == kernel_source_hash():
+            traffic = tr.get("traffic_bytes_per_launch")
+
+    ms_step = ms_total / steps
+    value = tokens / (ms_total * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: B={B}, K={K}, {cfg.Hq}/{cfg.Hkv} heads x D{cfg.D}, "
+                         f"ragged KV {cfg.len_kind} [{cfg.len_lo},{cfg.len_hi}]"
+                         + (f" + shared prefix {P}" if P else "")
+                         + f", V={cfg.V}, T={cfg.temperature}, top_p={cfg.top_p}"
+                         + (", greedy" if cfg.greedy else "")),
+            "B": B, "K": K, "rotating_input_sets": S,
+        },
+        "hbm_frac_step": round(step_bytes / (ms_total * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes_avg": int(step_bytes / steps),
+        "verified_tokens_per_step_avg": round(tokens / steps, 3),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "kernel": "decode_bf16_kernel (split-K verify attention)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1) if achieved else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch_avg": int(sum(kern_bytes) / steps),
+            "avg_launch_us": round(kern_avg_us, 3) if kern_avg_us else None,
+        },
+    }
+
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(sets, cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(sets, cfg, budget_s):
+    """The CPU oracle as it stands (single-threaded fp64 C) on whole verify steps."""
+    import numpy as np
+
+    from oracle import specref as Ref
+
+    tokens, spent, n = 0, 0.0, 0
+    for w in sets:
+        t0 = time.perf_counter()
+        Ref.workload_attn(w)
+        a = Ref.workload_accept(w)
+        Ref.compact_kv(a["n_accepted"], a["out_tokens"], w.kv_len, w.kv_start, w.k_cache,
+                       w.v_cache, w.k_new, w.v_new, cfg.K, cfg.Hkv, cfg.D)
+        spent += time.perf_counter() - t0
+        tokens += int((a["n_accepted"] + 1).sum())
+        n += 1
+        if spent >= budget_s:
+            break
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for l in f:
+                if l.startswith("model name"):
+                    cpu = l.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(tokens / spent, 3), "unit": "verified tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"{n} whole verify steps of {cfg.name} (input sets 0..{n - 1}): fp64 "
+                       f"attention of all {cfg.rows}x{cfg.Hq} query rows, sampler on all rows, "
+                       f"compaction; {spent:.1f}s on 1 thread of {cpu}")}
+
+
+if __name__ == "__main__":
+    main()

@@ -190,6 +190,19 @@ int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_
                     int32_t* cu_tokens, int B, int K, int Hkv, int D, int dtype,
                     int32_t* status, sv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * sv_set_kernel_events -- timing instrumentation for the dominant kernel.
+ *
+ * When `start` and `stop` (hipEvent_t handles created by the caller) are both
+ * non-NULL, every later spec_verify_attn call on the calling thread records
+ * `start` on its stream immediately before its per-sequence split-K chunk
+ * kernel and `stop` immediately after it (also while the stream is being
+ * captured into a graph, where the records become graph nodes).  Passing NULL
+ * for either turns the recording off.  The events stay owned by the caller.
+ * Returns SV_OK.
+ * ------------------------------------------------------------------------ */
+int sv_set_kernel_events(void* start, void* stop);
+
 #ifdef __cplusplus
 }
 #endif

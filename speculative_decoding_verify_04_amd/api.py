@@ -50,7 +50,8 @@ def lib():
                                   ctypes.c_float, i32, vp, vp, vp, vp, sz, vp]
         h.spec_compact_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                       i32, vp, vp]
-        for f in ("spec_verify_attn_workspace_size", "spec_verify_attn",
+        h.sv_set_kernel_events.argtypes = [vp, vp]
+        for f in ("sv_set_kernel_events", "spec_verify_attn_workspace_size", "spec_verify_attn",
                   "spec_accept_workspace_size", "spec_accept", "spec_compact_kv"):
             getattr(h, f).restype = i32
         _lib = h
@@ -199,6 +200,13 @@ def spec_compact_kv(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, 
         _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(tokens_packed), _ptr(cu_tokens), B, K,
         Hkv, D, _kv_dtype(k_cache), _ptr(status), _stream(k_cache)))
     return tokens_packed, cu_tokens
+
+
+def sv_set_kernel_events(start: Optional[int], stop: Optional[int]) -> None:
+    """Record hipEvent handles ``start``/``stop`` around the split-K chunk kernel of
+    later spec_verify_attn calls on this thread (None turns it off)."""
+    _check(lib().sv_set_kernel_events(ctypes.c_void_p(start) if start else None,
+                                      ctypes.c_void_p(stop) if stop else None))
 
 
 def device_error_name(code: int) -> str:

@@ -13,6 +13,8 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
 
 int fail(int code, const char* fmt, ...) {
     va_list ap;
@@ -45,6 +47,8 @@ int check_attn_shape(int B, int K, int Hq, int Hkv, int D, int dtype, const int3
     if (dtype == SV_BF16) {
         if (D != 64 && D != 128)
             return fail(SV_ERR_UNSUPPORTED, "bf16 attention supports head_dim 64 or 128 (got %d)", D);
+        if (B > 2048)
+            return fail(SV_ERR_UNSUPPORTED, "bf16 attention supports B <= 2048 sequences per call (got %d)", B);
         if ((Hq / Hkv) * (K + 1) > 64)
             return fail(SV_ERR_UNSUPPORTED,
                         "bf16 attention supports (Hq/Hkv)*(K+1) <= 64 query columns per kv head "
@@ -68,12 +72,24 @@ const char* sv_last_error(void) { return g_err; }
 
 int sv_version(void) { return 100; }
 
+int sv_set_kernel_events(void* start, void* stop) {
+    if (start && stop) {
+        g_ev_start = static_cast<hipEvent_t>(start);
+        g_ev_stop = static_cast<hipEvent_t>(stop);
+    } else {
+        g_ev_start = g_ev_stop = nullptr;
+    }
+    return ok();
+}
+
 int spec_verify_attn_workspace_size(int B, int K, int Hq, int Hkv, int D, int dtype,
                                     const int32_t* kv_len_host, int prefix_len, size_t* bytes) {
     int rc = check_attn_shape(B, K, Hq, Hkv, D, dtype, kv_len_host, prefix_len);
     if (rc) return rc;
     if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, prefix_len).bytes;
+    const sv::AttnPlan plan = sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, prefix_len);
+    if (!plan.ok) return fail(SV_ERR_UNSUPPORTED, "KV length bound too long (bf16: at most 2^25 keys per sequence, 2^30 64-key tiles in all)");
+    *bytes = plan.bytes;
     return ok();
 }
 
@@ -98,6 +114,7 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
     if (!isfinite(softmax_scale)) return fail(SV_ERR_INVALID_ARG, "softmax_scale is not finite");
     const sv::AttnPlan plan =
         sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, prefix_len);
+    if (!plan.ok) return fail(SV_ERR_UNSUPPORTED, "KV length bound too long (bf16: at most 2^25 keys per sequence, 2^30 64-key tiles in all)");
     if (!workspace || workspace_bytes < plan.bytes)
         return fail(SV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.bytes,
                     workspace ? workspace_bytes : static_cast<size_t>(0));
@@ -122,6 +139,8 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
     a.prefix_len = prefix_len;
     a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
     a.workspace = workspace;
+    a.ev_start = g_ev_start;
+    a.ev_stop = g_ev_stop;
     hipError_t e = sv::attn_launch(a, plan, as_stream(stream));
     if (e != hipSuccess) return fail(SV_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -149,6 +168,8 @@ int spec_accept(const void* target_logits, const void* draft_logits, int logits_
     if (!(temperature > 0.0f) || !isfinite(temperature))
         return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0");
     if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(SV_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+    if (K > sv::accept_max_drafts())
+        return fail(SV_ERR_UNSUPPORTED, "K above %d", sv::accept_max_drafts());
     if (B == 0) return ok();
     if (!target_logits || !n_accepted || !out_tokens)
         return fail(SV_ERR_INVALID_ARG, "a required tensor pointer is NULL");

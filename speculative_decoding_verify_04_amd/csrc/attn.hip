@@ -20,8 +20,12 @@
 //   prefix_bf16_kernel  one workgroup per (prefix chunk, kv head, column
 //       group): every query column of every sequence against one 64-key LDS
 //       tile at a time, so the shared prefix is read from HBM once.
+//       The last chunk workgroup of each (sequence, kv head) to finish merges
+//       all partials (log-sum-exp) and writes the output rows; the hand-off
+//       uses coherent stores/loads and an arrival counter, no cache flush.
+//       Each wave keeps its next 16-key slice in flight while computing one.
 //   attn_f32_kernel  fp32 VALU path (small head dims, fp32 inputs).
-//   merge_kernel  log-sum-exp merge of the partial (m, l, o) of all chunks.
+//   merge_kernel  log-sum-exp merge of the fp32 path's partials.
 // Scores are kept in the log2 domain (scale * log2(e) folded into S).
 #include <stdlib.h>
 
@@ -33,6 +37,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
+constexpr int kMergeMax = 1024;  // (part, column) entries merged per LDS pass
 
 struct AttnParams {
     const uint16_t* q;
@@ -53,12 +58,14 @@ struct AttnParams {
     const int32_t* kv_len;
     void* out;
     int32_t* status;
-    float* part_o;     // [slots][Hkv][CPG][D]
-    float2* part_ml;   // [slots][Hkv][CPG]  (m in log2 units, l)
-    int* seq_base;     // [B] first slot of sequence b
+    float* part_o;     // bf16 path [slots][D][CPG]; fp32 path [slots][Hkv][CPG][D]
+    float2* part_ml;   // bf16 path [slots][CPG]; fp32 path [slots][Hkv][CPG]  (m in log2 units, l)
+    int* seq_base;     // [B] first slot of sequence b (fp32 path)
+    int* merge_cnt;    // [B][Hkv] arrival counters of the fused merge (bf16 path)
     float* pre_o;      // [prefix_slots][Hkv][NC][D]
     float2* pre_ml;    // [prefix_slots][Hkv][NC]
     int B, K, Hq, Hkv, G, CPG, NC, D, chunk, prefix_chunk, prefix_len, prefix_slots, slots;
+    int tiles;         // bf16 path: Hkv * sum_b ceil((L_b + K + 1) / 64) for the host bound
     int bf16;
     float scale_log2;
 };
@@ -100,211 +107,422 @@ __device__ void find_sequence(const AttnParams& p, int x, int g, int* s_b, int* 
 
 
 // ---------------------------------------------------------------- decode (bf16)
+//
+// Balanced persistent split-K ("stream-K").  The keys of sequence b (its L_b
+// cached rows, then its K+1 new rows) form, for each kv head g, a segment of
+// n_b = ceil((L_b + K + 1) / 64) tiles of 64 keys.  Segments are ordered
+// (b, g) and their tiles concatenated; the launch has as many workgroups as
+// the GPU holds at once, and workgroup w takes the tiles [w*per, (w+1)*per),
+// per = ceil(N / workgroups).  Every workgroup therefore streams the same
+// number of keys, whatever the ragged lengths.  Inside a tile, each of the 4
+// waves takes 16 keys.  When a workgroup leaves a segment it combines its 4
+// waves and writes one partial (m, l, o) for that segment; the last part of a
+// segment to arrive merges all of them (and the shared-prefix partials of the
+// prefix kernel) and writes the output rows.
 
-template <int D>
-struct DecodeLds {
-    static constexpr int VP = D + 4;  // V slice pitch (bf16): conflict-free transposed reads
+constexpr int kTile = 64;       // keys per workgroup step (4 waves x 16)
+constexpr int kSkMaxB = 2048;   // sequences per call on the bf16 path
+constexpr int kSkMaxKeys = 1 << 25;  // keys per sequence on the bf16 path
+
+typedef short v4s_t __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i supplies the address of 4 consecutive b16 values that form
+// row i/4, columns 4*(i%4) .. 4*(i%4)+3 of a 4 x 16 tile; lane n receives
+// column n of that tile (rows 0..3).
+__device__ __forceinline__ shortx4 lds_read_tr16(const uint16_t* p) {
+    v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(const_cast<uint16_t*>(p)));
+    return shortx4{r[0], r[1], r[2], r[3]};
+}
+
+template <int D, int NCT>
+struct SkLds {
+    static constexpr int VP = D + 4;   // V slice pitch (bf16)
+    static constexpr int OP = 20;      // column pitch of the wave-combine buffer (floats)
     union {
         uint16_t vs[4][16][VP];
         struct {
-            float o[4][16][D];
+            float o[4][D / 2][OP];     // [wave][d within the half][column]
             float m[4][16];
             float l[4][16];
         } red;
+        struct {
+            float2 ml[kMergeMax];      // (m, l) of every (part, column) of a column group
+            float w[kMergeMax];        // merge weight of every (part, column)
+            int slot[kMergeMax];       // partial slot of every part (-1 - i: prefix chunk i)
+        } mrg;
     };
-    int sb, sc;
+    uint16_t qs[NCT * 16][D + 8];      // the segment's query columns (B operand source)
+    int P[kSkMaxB + 1];                // P[b] = sum of n_b' over b' < b
+    int flag;
 };
 
+// Segment of tile t (b, g, tile index i within the segment, n_b).
+__device__ __forceinline__ void sk_locate(const int* P, int B, int Hkv, int t, int* b, int* g,
+                                          int* i, int* nb) {
+    int lo = 0, hi = B - 1;  // largest b with Hkv * P[b] <= t
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (Hkv * P[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    *b = lo;
+    *nb = P[lo + 1] - P[lo];
+    const int r = t - Hkv * P[lo];
+    *g = r / *nb;
+    *i = r % *nb;
+}
+
+// Merge every part of segment (b, g) -- the prefix chunks first, then the
+// stream-K parts in workgroup order -- and write the output rows
+// b*(K+1)+j of heads g*G + hh.  Fixed order: bit-reproducible.
 template <int D, int NCT>
-__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(AttnParams p) {
-    constexpr int KK = D / 32;   // 16x16x32 steps over the head dim
-    constexpr int DT = D / 16;   // 16-wide head-dim tiles of the PV product
-    constexpr int VCH = D / 8;   // 16-byte chunks per K/V row
-    constexpr int VLD = 16 * VCH / 64;  // 16-byte V loads per lane per slice
-    __shared__ DecodeLds<D> S;
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int g = blockIdx.y;
-    if (w == 0) find_sequence(p, blockIdx.x, g, &S.sb, &S.sc);
+__device__ void sk_merge(const AttnParams& p, SkLds<D, NCT>& S, int b, int g, int s0, int s1,
+                         int per) {
+    const int tid = threadIdx.x;
+    const int np = p.prefix_slots;
+    const int w0 = s0 / per, w1 = (s1 - 1) / per;
+    const int nparts = np + (w1 - w0 + 1);
+    const int CPG = p.CPG, K1 = p.K + 1;
+    const int seg = b * p.Hkv + g;
     __syncthreads();
-    const int b = S.sb, c = S.sc;
-    if (b < 0) return;
-    if (c == 0 && g == 0 && tid == 0) p.seq_base[b] = blockIdx.x;
-
-    const int K1 = p.K + 1;
-    const int L = max(p.kv_len[b], 0);
-    const int T = L + K1;
-    const int t_begin = c * p.chunk;
-    const int t_end = min(T, t_begin + p.chunk);
-    const int64_t kv0 = p.kv_start[b];
-    const int col16 = lane & 15, kg = lane >> 4;
-
-    // Q^T operands and causal limits of this lane's columns
-    bf16x8 qv[NCT][KK];
-    int lim[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int col = ct * 16 + col16;
-        if (col < p.CPG) {
-            const int hh = col / K1, j = col % K1;
-            const int h = g * p.G + hh;
-            const uint16_t* qp = p.q + ((static_cast<size_t>(b) * K1 + j) * p.Hq + h) * D + kg * 8;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                qv[ct][kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
-            lim[ct] = L + j + 1;
+    for (int j = tid; j < nparts; j += kThreads) {
+        if (j < np) {
+            S.mrg.slot[j] = -1 - j;
         } else {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qv[ct][kk][e] = static_cast<__bf16>(0.0f);
-            lim[ct] = 0;
+            const int wp = w0 + (j - np);
+            int bb, gg, ii, nn;
+            sk_locate(S.P, p.B, p.Hkv, wp * per, &bb, &gg, &ii, &nn);
+            S.mrg.slot[j] = wp * per + (seg - (bb * p.Hkv + gg));
         }
     }
-
-    floatx4 o[NCT][DT];
-    float mrun[NCT], lrun[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        mrun[ct] = -INFINITY;
-        lrun[ct] = 0.0f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[ct][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const size_t head_off = static_cast<size_t>(g) * D;
-    const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
-    // K/V row of key t of sequence b (keys past T clamp to the last new row)
-    auto krow = [&](int t, const uint16_t* cache, const uint16_t* fresh) -> const uint16_t* {
-        t = min(t, T - 1);
-        return (t < L) ? cache + static_cast<size_t>(kv0 + t) * row_stride + head_off
-                       : fresh + static_cast<size_t>(b * K1 + (t - L)) * row_stride + head_off;
-    };
-
-    uint16_t(*vs)[DecodeLds<D>::VP] = S.vs[w];
-    for (int t0 = t_begin + 16 * w; t0 < t_end; t0 += 64) {
-        // K slice: lane holds key t0 + col16, head-dim chunks kg*8 + 32*kk
-        bf16x8 kr[KK];
-        const uint16_t* kp = krow(t0 + col16, p.k_cache, p.k_new) + kg * 8;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kr[kk] = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
-        // V slice in natural layout -> LDS
-        uint4 vr[VLD];
-#pragma unroll
-        for (int i = 0; i < VLD; ++i) {
-            const int qi = i * 64 + lane;
-            const int kl = qi / VCH, dc = qi % VCH;
-            vr[i] = *reinterpret_cast<const uint4*>(krow(t0 + kl, p.v_cache, p.v_new) + dc * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < VLD; ++i) {
-            const int qi = i * 64 + lane;
-            const int kl = qi / VCH, dc = qi % VCH;
-            uint2* dst = reinterpret_cast<uint2*>(&vs[kl][dc * 8]);
-            dst[0] = make_uint2(vr[i].x, vr[i].y);
-            dst[1] = make_uint2(vr[i].z, vr[i].w);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // V^T operands: lane (d = dt*16 + col16) holds keys kg*4 .. kg*4+3
-        shortx4 va[DT];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                va[dt][e] = static_cast<short>(vs[kg * 4 + e][dt * 16 + col16]);
-        }
-
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk], qv[ct][kk], acc, 0, 0, 0);
-            float s[4];
-            float mt = -INFINITY;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = t0 + kg * 4 + e;
-                s[e] = (t < lim[ct]) ? acc[e] * p.scale_log2 : -INFINITY;
-                mt = fmaxf(mt, s[e]);
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float mnew = fmaxf(mrun[ct], mt);
-            float alpha = 1.0f;
-            shortx4 pb;
-            if (mnew == -INFINITY) {
-                pb = shortx4{0, 0, 0, 0};
+    const int group = max(1, min(CPG, kMergeMax / nparts));
+    for (int c0 = 0; c0 < CPG; c0 += group) {
+        const int nc = min(group, CPG - c0);
+        __syncthreads();
+        for (int idx = tid; idx < nparts * nc; idx += kThreads) {
+            const int j = idx / nc, col = c0 + idx % nc;
+            const int sl = S.mrg.slot[j];
+            float2 v;
+            if (sl < 0) {
+                v = p.pre_ml[(static_cast<size_t>(-1 - sl) * p.Hkv + g) * p.NC +
+                             static_cast<size_t>(b) * CPG + col];
             } else {
-                alpha = exp2f(mrun[ct] - mnew);
-                float ps = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float pe = exp2f(s[e] - mnew);
-                    ps += pe;
-                    pb[e] = static_cast<short>(f32_to_bf16(pe));
-                }
-                lrun[ct] = lrun[ct] * alpha + ps;
-                mrun[ct] = mnew;
+                const size_t s = static_cast<size_t>(sl) * CPG + col;
+                v.x = ld_coh(&p.part_ml[s].x);
+                v.y = ld_coh(&p.part_ml[s].y);
             }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                o[ct][dt] *= alpha;
-                o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, o[ct][dt], 0, 0, 0);
-            }
+            S.mrg.ml[idx] = v;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        lrun[ct] += __shfl_xor(lrun[ct], 16, 64);
-        lrun[ct] += __shfl_xor(lrun[ct], 32, 64);
-    }
-
-    // combine the 4 waves (fixed order) and write this chunk's partials
-    const size_t slot_col0 = (static_cast<size_t>(blockIdx.x) * p.Hkv + g) * p.CPG;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
         __syncthreads();
-        if (kg == 0) {
-            S.red.m[w][col16] = mrun[ct];
-            S.red.l[w][col16] = lrun[ct];
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) S.red.o[w][col16][dt * 16 + kg * 4 + e] = o[ct][dt][e];
-        __syncthreads();
-        for (int idx = tid; idx < 16 * D; idx += kThreads) {
-            const int cl = idx / D, d = idx % D;
-            const int col = ct * 16 + cl;
-            if (col >= p.CPG) continue;
+        for (int cl = tid; cl < nc; cl += kThreads) {
             float ms = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) ms = fmaxf(ms, S.red.m[u][cl]);
-            float acc = 0.0f, l = 0.0f;
-            if (ms != -INFINITY) {
+            for (int j = 0; j < nparts; ++j) ms = fmaxf(ms, S.mrg.ml[j * nc + cl].x);
+            float l = 0.0f;
+            for (int j = 0; j < nparts; ++j) {
+                const float2 v = S.mrg.ml[j * nc + cl];
+                const float f = (v.x == -INFINITY) ? 0.0f : exp2f(v.x - ms);
+                S.mrg.w[j * nc + cl] = f;
+                l += v.y * f;
+            }
+            const float inv = 1.0f / l;
+            for (int j = 0; j < nparts; ++j) S.mrg.w[j * nc + cl] *= inv;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nc * D; idx += kThreads) {
+            const int cl = idx % nc, d = idx / nc, col = c0 + cl;
+            float acc = 0.0f;
+            for (int j0 = 0; j0 < nparts; j0 += 4) {
+                float v[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float mu = S.red.m[u][cl];
-                    const float f = (mu == -INFINITY) ? 0.0f : exp2f(mu - ms);
-                    acc += S.red.o[u][cl][d] * f;
-                    l += S.red.l[u][cl] * f;
+                    const int j = j0 + u;
+                    v[u] = 0.0f;
+                    if (j < nparts) {
+                        const int sl = S.mrg.slot[j];
+                        v[u] = (sl < 0)
+                                   ? p.pre_o[((static_cast<size_t>(-1 - sl) * p.Hkv + g) * p.NC +
+                                              static_cast<size_t>(b) * CPG + col) * D + d]
+                                   : ld_coh(p.part_o + (static_cast<size_t>(sl) * D + d) * CPG + col);
+                    }
                 }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (j0 + u < nparts) acc += v[u] * S.mrg.w[(j0 + u) * nc + cl];
             }
-            p.part_o[(slot_col0 + col) * D + d] = acc;
-            if (d == 0) p.part_ml[slot_col0 + col] = make_float2(ms, l);
+            const int hh = col / K1, j = col % K1;
+            const size_t oi = ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + d;
+            static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(acc);
         }
     }
 }
 
-// ---------------------------------------------------------------- prefix (bf16)
+// K and V of one 16-key slice held in registers.
+template <int D>
+struct Slice {
+    bf16x8 k[D / 32];
+    uint4 v[16 * (D / 8) / 64];
+};
+
+template <int D, int NCT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? 4 : 1)))
+void decode_bf16_kernel(AttnParams p) {
+    constexpr int KK = D / 32;   // 16x16x32 steps over the head dim
+    constexpr int DT = D / 16;   // 16-wide head-dim tiles of the PV product
+    constexpr int VCH = D / 8;   // 16-byte chunks per K/V row
+    constexpr int VLD = 16 * VCH / 64;  // 16-byte V loads per lane per slice
+    constexpr int VP = SkLds<D, NCT>::VP;
+    __shared__ SkLds<D, NCT> S;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col16 = lane & 15, kg = lane >> 4;
+    const int K1 = p.K + 1;
+
+    // tiles per sequence and their prefix (one round trip for all lengths)
+    for (int bb = tid; bb < p.B; bb += kThreads) {
+        int L = p.kv_len[bb];
+        if (L < 0) {
+            if (blockIdx.x == 0) set_status(p.status, 3);
+            L = 0;
+        }
+        S.P[bb + 1] = min(ceil_div(min(L, kSkMaxKeys) + K1, kTile), kSkMaxKeys / kTile);
+    }
+    __syncthreads();
+    if (w == 0) {
+        int run = 0;
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            const int v = (b0 + lane < p.B) ? S.P[b0 + lane + 1] : 0;
+            const int inc = wave_incl_scan(v, lane) + run;
+            if (b0 + lane < p.B) S.P[b0 + lane + 1] = inc;
+            run = __shfl(inc, 63, 64);
+        }
+        if (lane == 0) S.P[0] = 0;
+    }
+    __syncthreads();
+    // A device length above the host bound would overrun the partial slots:
+    // every workgroup sees the same total and leaves.
+    const long long Nl = static_cast<long long>(p.Hkv) * S.P[p.B];
+    if (Nl > p.tiles) {
+        if (blockIdx.x == 0 && tid == 0) set_status(p.status, 3);
+        return;
+    }
+    const int N = static_cast<int>(Nl);
+    const int per = ceil_div(N, gridDim.x);
+    const int t_lo = blockIdx.x * per;
+    const int t_hi = min(N, t_lo + per);
+    const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
+
+    int v_key[VLD], v_chunk[VLD];
+#pragma unroll
+    for (int i = 0; i < VLD; ++i) {
+        v_key[i] = (i * 64 + lane) / VCH;
+        v_chunk[i] = (i * 64 + lane) % VCH;
+    }
+    uint16_t(*vs)[VP] = S.vs[w];
+    // transposed-read address of this lane: row kg*4 + col16/4, column 4*(col16%4)
+    const uint16_t* vt_base = &vs[kg * 4 + (col16 >> 2)][(col16 & 3) * 4];
+
+    int k_local = 0;
+    for (int t = t_lo; t < t_hi; ++k_local) {
+        int b, g, i, nb;
+        sk_locate(S.P, p.B, p.Hkv, t, &b, &g, &i, &nb);
+        const int s0 = t - i, s1 = s0 + nb;
+        const int e = min(t_hi, s1);
+        const int L = max(p.kv_len[b], 0);
+        const int T = L + K1;
+        const int64_t kv0 = p.kv_start[b];
+        const size_t head_off = static_cast<size_t>(g) * D;
+        const int k_lo = i * kTile;
+        const int k_hi = min(T, (i + (e - t)) * kTile);
+
+        // K/V row of key tt (keys past T clamp to the last new row)
+        auto krow = [&](int tt, const uint16_t* cache, const uint16_t* fresh) -> const uint16_t* {
+            tt = min(tt, T - 1);
+            return (tt < L) ? cache + static_cast<size_t>(kv0 + tt) * row_stride + head_off
+                            : fresh + static_cast<size_t>(b * K1 + (tt - L)) * row_stride + head_off;
+        };
+        auto load_slice = [&](Slice<D>& sl, int t0) {
+            if (t0 + 15 < L) {  // whole slice in the cache: plain strided rows
+                const uint16_t* kb = p.k_cache + static_cast<size_t>(kv0 + t0) * row_stride + head_off;
+                const uint16_t* kp = kb + col16 * row_stride + kg * 8;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) sl.k[kk] = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
+                const uint16_t* vb = p.v_cache + static_cast<size_t>(kv0 + t0) * row_stride + head_off;
+#pragma unroll
+                for (int q = 0; q < VLD; ++q)
+                    sl.v[q] = *reinterpret_cast<const uint4*>(vb + v_key[q] * row_stride + v_chunk[q] * 8);
+            } else {
+                const uint16_t* kp = krow(t0 + col16, p.k_cache, p.k_new) + kg * 8;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) sl.k[kk] = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
+#pragma unroll
+                for (int q = 0; q < VLD; ++q)
+                    sl.v[q] = *reinterpret_cast<const uint4*>(krow(t0 + v_key[q], p.v_cache, p.v_new) +
+                                                              v_chunk[q] * 8);
+            }
+        };
+
+        const int t_first = k_lo + 16 * w;
+        Slice<D> sl;
+        if (t_first < k_hi) load_slice(sl, t_first);
+
+        // the segment's query columns -> LDS (zero rows for padding columns)
+        __syncthreads();
+        for (int idx = tid; idx < NCT * 16 * VCH; idx += kThreads) {
+            const int col = idx / VCH, ch = idx % VCH;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (col < p.CPG) {
+                const int hh = col / K1, j = col % K1;
+                v = *reinterpret_cast<const uint4*>(
+                    p.q + ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + ch * 8);
+            }
+            uint2* dst = reinterpret_cast<uint2*>(&S.qs[col][ch * 8]);
+            dst[0] = make_uint2(v.x, v.y);
+            dst[1] = make_uint2(v.z, v.w);
+        }
+        int lim[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int col = ct * 16 + col16;
+            lim[ct] = (col < p.CPG) ? L + col % K1 + 1 : 0;
+        }
+        __syncthreads();
+
+        floatx4 o[NCT][DT];
+        float mrun[NCT], lrun[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            mrun[ct] = -INFINITY;
+            lrun[ct] = 0.0f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[ct][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+
+        // Per slice: stage V in LDS, S^T = K Q^T, then reissue the slice
+        // registers for the wave's next slice (in flight during the softmax
+        // and the PV product).
+        for (int t0 = t_first; t0 < k_hi; t0 += 64) {
+#pragma unroll
+            for (int q = 0; q < VLD; ++q) {
+                uint2* dst = reinterpret_cast<uint2*>(&vs[v_key[q]][v_chunk[q] * 8]);
+                dst[0] = make_uint2(sl.v[q].x, sl.v[q].y);
+                dst[1] = make_uint2(sl.v[q].z, sl.v[q].w);
+            }
+            floatx4 acc[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    const bf16x8 qb =
+                        *reinterpret_cast<const bf16x8*>(&S.qs[ct * 16 + col16][kg * 8 + 32 * kk]);
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl.k[kk], qb, acc[ct], 0, 0, 0);
+                }
+            }
+            if (t0 + 64 < k_hi) load_slice(sl, t0 + 64);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // V^T operands: lane (d = dt*16 + col16) gets keys kg*4 .. kg*4+3
+            shortx4 va[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) va[dt] = lds_read_tr16(vt_base + dt * 16);
+            const bool full = t0 + 15 < L;  // no key of the slice is masked for any column
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                float s[4];
+                float mt = -INFINITY;
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee) {
+                    const int tt = t0 + kg * 4 + ee;
+                    s[ee] = (full || tt < lim[ct]) ? acc[ct][ee] * p.scale_log2 : -INFINITY;
+                    mt = fmaxf(mt, s[ee]);
+                }
+                mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+                mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                const float mnew = fmaxf(mrun[ct], mt);
+                float alpha = 1.0f;
+                shortx4 pb;
+                if (mnew == -INFINITY) {
+                    pb = shortx4{0, 0, 0, 0};
+                } else {
+                    alpha = exp2f(mrun[ct] - mnew);
+                    float pe[4];
+#pragma unroll
+                    for (int ee = 0; ee < 4; ++ee) pe[ee] = exp2f(s[ee] - mnew);
+                    lrun[ct] = lrun[ct] * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
+                    mrun[ct] = mnew;
+#pragma unroll
+                    for (int ee = 0; ee < 4; ++ee) pb[ee] = static_cast<short>(f32_to_bf16(pe[ee]));
+                }
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    o[ct][dt] *= alpha;
+                    o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, o[ct][dt], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            lrun[ct] += __shfl_xor(lrun[ct], 16, 64);
+            lrun[ct] += __shfl_xor(lrun[ct], 32, 64);
+        }
+
+        // combine the 4 waves (fixed order) in two halves of the head dim; the
+        // part is stored at slot blockIdx.x*per + k_local, laid out [d][column]
+        const size_t slot = static_cast<size_t>(blockIdx.x) * per + k_local;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                __syncthreads();
+                if (kg == 0 && half == 0) {
+                    S.red.m[w][col16] = mrun[ct];
+                    S.red.l[w][col16] = lrun[ct];
+                }
+#pragma unroll
+                for (int dt = half * (DT / 2); dt < (half + 1) * (DT / 2); ++dt)
+#pragma unroll
+                    for (int ee = 0; ee < 4; ++ee)
+                        S.red.o[w][(dt - half * (DT / 2)) * 16 + kg * 4 + ee][col16] = o[ct][dt][ee];
+                __syncthreads();
+                const int ncol = min(16, p.CPG - ct * 16);
+                for (int idx = tid; idx < 16 * (D / 2); idx += kThreads) {
+                    const int cl = idx & 15, dh = idx >> 4;
+                    if (cl >= ncol) continue;
+                    const int col = ct * 16 + cl, d = half * (D / 2) + dh;
+                    float ms = -INFINITY;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) ms = fmaxf(ms, S.red.m[u][cl]);
+                    float accv = 0.0f, l = 0.0f;
+                    if (ms != -INFINITY) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const float mu = S.red.m[u][cl];
+                            const float f = (mu == -INFINITY) ? 0.0f : exp2f(mu - ms);
+                            accv += S.red.o[u][dh][cl] * f;
+                            l += S.red.l[u][cl] * f;
+                        }
+                    }
+                    st_coh(p.part_o + (slot * D + d) * p.CPG + col, accv);
+                    if (d == 0) {
+                        st_coh(&p.part_ml[slot * p.CPG + col].x, ms);
+                        st_coh(&p.part_ml[slot * p.CPG + col].y, l);
+                    }
+                }
+            }
+        }
+
+        const int nparts = (s1 - 1) / per - s0 / per + 1;
+        if (arrive_last(p.merge_cnt + static_cast<size_t>(b) * p.Hkv + g, nparts, &S.flag))
+            sk_merge<D, NCT>(p, S, b, g, s0, s1, per);
+        t = e;
+    }
+}
 
 template <int D>
 struct PrefixLds {
@@ -575,47 +793,102 @@ int env_int(const char* name, int dflt) {
     return v > 0 ? v : dflt;
 }
 
+// Workgroups of the stream-K decode kernel that the GPU holds at once (CUs x
+// resident workgroups per CU), cached per device and kernel variant.
+int sk_resident_grid(int D, int nct) {
+    static int cache[16][2][4];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) {
+        (void)hipGetLastError();
+        return 1024;  // no device: any value sizes a workspace that is never launched
+    }
+    int& c = cache[dev][D == 128 ? 1 : 0][nct - 1];
+    if (c > 0) return c;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    const void* fn = nullptr;
+#define SV_FN(DD, NN) fn = reinterpret_cast<const void*>(&decode_bf16_kernel<DD, NN>)
+    if (D == 128) {
+        switch (nct) { case 1: SV_FN(128, 1); break; case 2: SV_FN(128, 2); break;
+                       case 3: SV_FN(128, 3); break; default: SV_FN(128, 4); break; }
+    } else {
+        switch (nct) { case 1: SV_FN(64, 1); break; case 2: SV_FN(64, 2); break;
+                       case 3: SV_FN(64, 3); break; default: SV_FN(64, 4); break; }
+    }
+#undef SV_FN
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess) per_cu = 0;
+    (void)hipGetLastError();
+    if (cus <= 0 || per_cu <= 0) return 1024;
+    const int wpc = env_int("SPECVERIFY_SK_WGS_PER_CU", 0);
+    if (wpc > 0 && wpc < per_cu) per_cu = wpc;
+    c = cus * per_cu;
+    return c;
+}
+
 }  // namespace
 
 AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
                    const int32_t* kv_len_host, int prefix_len) {
     AttnPlan pl{};
     const int K1 = K + 1;
-    long long keys = 0;
-    for (int b = 0; b < B; ++b) keys += (kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1;
-    int chunk = env_int("SPECVERIFY_ATTN_CHUNK", 0);
-    if (chunk <= 0) {
-        // largest power-of-two chunk (64..1024) that still gives >= 4 work items per CU
-        chunk = 64;
-        for (int c = 1024; c >= 64; c >>= 1) {
-            long long items = 0;
-            for (int b = 0; b < B; ++b)
-                items += ((kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1 + c - 1) / c;
-            if (items * Hkv >= 1024) { chunk = c; break; }
-        }
-    }
-    chunk = (chunk + 63) / 64 * 64;
-    if (chunk > 1024) chunk = 1024;
-    (void)keys;
-    int slots = 0;
-    for (int b = 0; b < B; ++b)
-        slots += ((kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1 + chunk - 1) / chunk;
+    const size_t CPG = static_cast<size_t>(Hq / Hkv) * K1;
+    const size_t NC = CPG * B;
     int pchunk = env_int("SPECVERIFY_PREFIX_CHUNK", 1024);
     pchunk = (pchunk + 63) / 64 * 64;
     if (!bf16 && pchunk > 1024) pchunk = 1024;
+    // the fused merge takes at most kMergeMax parts: keep half for the prefix
+    while (bf16 && prefix_len > 0 && (prefix_len + pchunk - 1) / pchunk > kMergeMax / 2)
+        pchunk *= 2;
     const int pslots = prefix_len > 0 ? (prefix_len + pchunk - 1) / pchunk : 0;
-    const size_t CPG = static_cast<size_t>(Hq / Hkv) * K1;
-    const size_t NC = CPG * B;
+    pl.ok = true;
+    long long slots = 0;
+    int chunk = 64;
+    if (bf16) {
+        long long tiles = 0;
+        for (int b = 0; b < B; ++b) {
+            const long long L = kv_len_host[b] > 0 ? kv_len_host[b] : 0;
+            if (L + K1 > kSkMaxKeys) pl.ok = false;
+            tiles += (L + K1 + kTile - 1) / kTile;
+        }
+        tiles *= Hkv;
+        if (B > kSkMaxB || tiles > (1LL << 30)) pl.ok = false;
+        const int nct = static_cast<int>((CPG + 15) / 16);
+        int grid = sk_resident_grid(D, nct < 4 ? nct : 4);
+        if (grid > kMergeMax - pslots) grid = kMergeMax - pslots;
+        if (grid < 1) grid = 1;
+        pl.grid = grid;
+        pl.tiles = pl.ok ? static_cast<int>(tiles) : 0;
+        slots = pl.ok ? tiles + grid : 0;
+    } else {
+        chunk = env_int("SPECVERIFY_ATTN_CHUNK", 0);
+        if (chunk <= 0) {
+            // largest power-of-two chunk (64..1024) that still gives >= 4 work items per CU
+            chunk = 64;
+            for (int c = 1024; c >= 64; c >>= 1) {
+                long long items = 0;
+                for (int b = 0; b < B; ++b)
+                    items += ((kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1 + c - 1) / c;
+                if (items * Hkv >= 1024) { chunk = c; break; }
+            }
+        }
+        chunk = (chunk + 63) / 64 * 64;
+        if (chunk > 1024) chunk = 1024;
+        for (int b = 0; b < B; ++b)
+            slots += ((kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1 + chunk - 1) / chunk;
+        if (slots > (1LL << 30)) pl.ok = false;
+        slots *= Hkv;  // the fp32 partials are per (slot, kv head)
+    }
     size_t off = 0;
     auto take = [&](size_t n) { off = (off + 255) & ~static_cast<size_t>(255); off += n; };
-    take(static_cast<size_t>(slots) * Hkv * CPG * D * 4);
-    take(static_cast<size_t>(slots) * Hkv * CPG * 8);
+    take(static_cast<size_t>(slots) * CPG * D * 4);
+    take(static_cast<size_t>(slots) * CPG * 8);
     take(static_cast<size_t>(B) * 4);
+    take(static_cast<size_t>(B) * Hkv * 4);
     take(static_cast<size_t>(pslots) * Hkv * NC * D * 4);
     take(static_cast<size_t>(pslots) * Hkv * NC * 8);
     pl.chunk = chunk;
     pl.prefix_chunk = pchunk;
-    pl.slots = slots;
+    pl.slots = bf16 ? static_cast<int>(slots) : static_cast<int>(slots / (Hkv > 0 ? Hkv : 1));
     pl.prefix_slots = pslots;
     pl.bytes = (off + 255) & ~static_cast<size_t>(255);
     return pl;
@@ -654,6 +927,7 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
     p.prefix_len = a.prefix_len;
     p.prefix_slots = pl.prefix_slots;
     p.slots = pl.slots;
+    p.tiles = pl.tiles;
     p.bf16 = a.bf16;
     p.scale_log2 = a.scale * kLog2e;
 
@@ -666,9 +940,11 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
         return r;
     };
     const size_t CPG = p.CPG, NC = p.NC;
-    p.part_o = reinterpret_cast<float*>(take(static_cast<size_t>(pl.slots) * a.Hkv * CPG * a.D * 4));
-    p.part_ml = reinterpret_cast<float2*>(take(static_cast<size_t>(pl.slots) * a.Hkv * CPG * 8));
+    const size_t pslots_all = a.bf16 ? static_cast<size_t>(pl.slots) : static_cast<size_t>(pl.slots) * a.Hkv;
+    p.part_o = reinterpret_cast<float*>(take(pslots_all * CPG * a.D * 4));
+    p.part_ml = reinterpret_cast<float2*>(take(pslots_all * CPG * 8));
     p.seq_base = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * 4));
+    p.merge_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * a.Hkv * 4));
     p.pre_o = reinterpret_cast<float*>(take(static_cast<size_t>(pl.prefix_slots) * a.Hkv * NC * a.D * 4));
     p.pre_ml = reinterpret_cast<float2*>(take(static_cast<size_t>(pl.prefix_slots) * a.Hkv * NC * 8));
 
@@ -686,7 +962,11 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
             if (e != hipSuccess) return e;
         }
         const int nct = (p.CPG + 15) / 16;
-        dim3 grid(pl.slots, a.Hkv);
+        dim3 grid(pl.grid);
+        if (a.ev_start) {
+            hipError_t e = hipEventRecord(a.ev_start, stream);
+            if (e != hipSuccess) return e;
+        }
 #define SV_DECODE(DD, NN) hipLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream, p)
         if (a.D == 128) {
             switch (nct) {
@@ -711,10 +991,19 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
+        if (a.ev_start) {
+            hipError_t e = hipEventRecord(a.ev_start, stream);
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(attn_f32_kernel, dim3(pl.slots, a.Hkv), dim3(kThreads), 0, stream, p, 0);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.ev_stop) {
+        e = hipEventRecord(a.ev_stop, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (a.bf16) return hipSuccess;  // the chunk kernel merges in its last workgroup
     const int mthreads = a.D <= 64 ? 64 : (a.D <= 128 ? 128 : 256);
     hipLaunchKernelGGL(merge_kernel, dim3(a.B * (a.K + 1) * a.Hq), dim3(mthreads), 0, stream, p);
     return hipGetLastError();

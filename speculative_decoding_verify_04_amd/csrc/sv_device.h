@@ -116,6 +116,40 @@ __device__ __forceinline__ int xcd_remap(int L, int n) {
     return (L & 7) * (n >> 3) + (L >> 3);
 }
 
+// ---- Hand-off of data between workgroups of one kernel.
+// Data that another workgroup of the same launch reads is written with st_coh
+// and read with ld_coh: relaxed atomics at agent scope, which the compiler
+// emits as coherent (sc1) stores and loads.  The hand-off itself is an arrival
+// counter (arrive_last).  No agent-scope fence is used: on gfx950 such a fence
+// writes back and invalidates the whole L2 of the XCD, which costs far more
+// than the few coherent accesses here.
+template <typename T>
+__device__ __forceinline__ void st_coh(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_coh(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by all threads of a workgroup after its st_coh stores.  Waits until
+// those stores have completed, counts the workgroup in *cnt, and returns true
+// in the workgroup that arrives n-th (which also resets *cnt to 0 for the next
+// launch).  That workgroup then sees every other workgroup's st_coh data
+// through ld_coh.
+__device__ __forceinline__ bool arrive_last(int* cnt, int n, int* flag_lds) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = (old == n - 1) ? 1 : 0;
+        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag_lds = last;
+    }
+    __syncthreads();
+    return *flag_lds != 0;
+}
+
 // Record the first device-side data error (0 = none).
 __device__ __forceinline__ void set_status(int32_t* status, int code) {
     if (status) atomicCAS(status, 0, code);

@@ -25,12 +25,16 @@ struct AttnArgs {
     int prefix_chunk;   // keys per work item of the shared prefix
     int slots;          // split-K work items per kv head (host upper bound)
     void* workspace;
+    hipEvent_t ev_start, ev_stop;  // optional records around the chunk kernel
 };
 
 // Chunking decisions made on the host from the host length bound.
 struct AttnPlan {
     int chunk, prefix_chunk, slots, prefix_slots;
+    int grid;    // bf16 path: workgroups of the stream-K decode kernel
+    int tiles;   // bf16 path: 64-key work tiles over all (sequence, kv head) for the host bound
     size_t bytes;
+    bool ok;  // false: the sequences are too long for the merge (unsupported)
 };
 
 AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
@@ -54,6 +58,7 @@ struct AcceptArgs {
 
 size_t accept_workspace_bytes(int B, int K, int V);
 int accept_max_vocab();
+int accept_max_drafts();
 hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- compaction

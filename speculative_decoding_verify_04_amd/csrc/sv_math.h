@@ -1,0 +1,48 @@
+// fp64 exp for the sampler's weights exp((z - max z) / T), arguments <= 0.
+//
+// Table-driven method of P. T. P. Tang, "Table-driven implementation of the
+// exponential function in IEEE floating-point arithmetic", ACM TOMS 15(2),
+// 1989: write x = (64 k + j) ln2/64 + r with |r| <= ln2/128, then
+//   exp(x) = 2^k * 2^(j/64) * exp(r),
+// with exp(r) from its degree-5 Taylor polynomial (truncation below 4e-17 for
+// |r| <= ln2/128) and the 64 values 2^(j/64) from a table the caller fills
+// with exp2(j/64).  The reduction uses ln2/64 split into a 32-bit head (exact
+// products for |k| < 2^20) and a tail.  Relative error stays below ~1e-15,
+// far inside the 1e-12 decision margins of the sampler; about 14 vector
+// instructions instead of ~40 for the library's general exp.
+//
+// The header compiles for the device (hipcc) and for host-side accuracy tests.
+#pragma once
+#include <math.h>
+
+#if defined(__HIPCC__)
+#define SV_HD __host__ __device__ __forceinline__
+#else
+#define SV_HD static inline
+#endif
+
+namespace sv {
+
+constexpr double kInvLn2x64 = 92.33248261689366;        // 64 / ln 2
+constexpr double kLn2d64Hi = 0.01083042469326756;       // ln2/64, 32 significant bits
+constexpr double kLn2d64Lo = 2.9815858269852933e-12;    // ln2/64 - kLn2d64Hi
+
+// exp(x) for x <= 0 (including -inf); `tab[j]` = 2^(j/64), j = 0..63.
+SV_HD double exp_nonpos(double x, const double* tab) {
+    if (!(x > -745.0)) return 0.0;  // underflow, -inf (NaN also maps to 0)
+    const double kd = rint(x * kInvLn2x64);
+    double r = fma(-kd, kLn2d64Hi, x);
+    r = fma(-kd, kLn2d64Lo, r);
+    const int k = static_cast<int>(kd);
+    const int j = k & 63;
+    const int e = k >> 6;  // arithmetic shift: floor(k / 64)
+    double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+    p = fma(r, p, 1.0 / 6.0);
+    p = fma(r, p, 0.5);
+    p = fma(r, p, 1.0);
+    p = p * r;  // exp(r) - 1
+    const double t = tab[j];
+    return ldexp(fma(t, p, t), e);
+}
+
+}  // namespace sv
