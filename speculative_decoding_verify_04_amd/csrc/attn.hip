@@ -9,25 +9,29 @@
 // exact result).
 //
 // Work decomposition (split-K over keys, flash-decoding style):
-//   decode_bf16_kernel  one workgroup per (sequence chunk, kv head).  The keys
-//       of sequence b are its L_b cached rows followed by its K+1 new rows; a
-//       chunk is `chunk` consecutive keys.  Each of the 4 waves takes 16-key
-//       slices; S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K rows go straight
+//   decode_bf16_kernel  one workgroup per work item (sequence b, chunk c, kv
+//       head g).  The keys of sequence b are its L_b cached rows followed by
+//       its K+1 new rows; each sequence is cut into chunks of at most
+//       `lambda` 16-key slices, lambda chosen so that all work items fit in
+//       one resident wave of workgroups.  Each of the 4 waves takes every 4th
+//       slice; S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K rows go straight
 //       from HBM into A-operand registers), an fp32 online softmax per query
 //       column, and O^T += V^T P^T with v_mfma_f32_16x16x16_bf16 (V is
-//       transposed through LDS).  The query columns of a kv head are its
-//       G = Hq/Hkv heads times the K+1 queries, in 16-wide tiles.
+//       transposed through LDS with ds_read_b64_tr_b16).  The query columns
+//       of a kv head are its G = Hq/Hkv heads times the K+1 queries, in
+//       16-wide tiles.  The last chunk of each (sequence, kv head) to finish
+//       merges all partials (log-sum-exp) and writes the output rows; the
+//       hand-off uses coherent stores/loads and an arrival counter, no cache
+//       flush.
 //   prefix_bf16_kernel  one workgroup per (prefix chunk, kv head, column
 //       group): every query column of every sequence against one 64-key LDS
 //       tile at a time, so the shared prefix is read from HBM once.
-//       The last chunk workgroup of each (sequence, kv head) to finish merges
-//       all partials (log-sum-exp) and writes the output rows; the hand-off
-//       uses coherent stores/loads and an arrival counter, no cache flush.
-//       Each wave keeps its next 16-key slice in flight while computing one.
 //   attn_f32_kernel  fp32 VALU path (small head dims, fp32 inputs).
 //   merge_kernel  log-sum-exp merge of the fp32 path's partials.
 // Scores are kept in the log2 domain (scale * log2(e) folded into S).
 #include <stdlib.h>
+
+#include <algorithm>
 
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -37,7 +41,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
-constexpr int kMergeMax = 1024;  // (part, column) entries merged per LDS pass
+constexpr int kMergeMax = 1024;  // parts (prefix chunks + workgroups) merged per segment
 
 struct AttnParams {
     const uint16_t* q;
@@ -65,7 +69,7 @@ struct AttnParams {
     float* pre_o;      // [prefix_slots][Hkv][NC][D]
     float2* pre_ml;    // [prefix_slots][Hkv][NC]
     int B, K, Hq, Hkv, G, CPG, NC, D, chunk, prefix_chunk, prefix_len, prefix_slots, slots;
-    int tiles;         // bf16 path: Hkv * sum_b ceil((L_b + K + 1) / 64) for the host bound
+    int lambda;        // bf16 path: 16-key slices per work item at most
     int bf16;
     float scale_log2;
 };
@@ -106,22 +110,27 @@ __device__ void find_sequence(const AttnParams& p, int x, int g, int* s_b, int* 
 }
 
 
+#ifndef SV_NCT1_WAVES
+#define SV_NCT1_WAVES 3
+#endif
+
 // ---------------------------------------------------------------- decode (bf16)
 //
-// Balanced persistent split-K ("stream-K").  The keys of sequence b (its L_b
-// cached rows, then its K+1 new rows) form, for each kv head g, a segment of
-// n_b = ceil((L_b + K + 1) / 64) tiles of 64 keys.  Segments are ordered
-// (b, g) and their tiles concatenated; the launch has as many workgroups as
-// the GPU holds at once, and workgroup w takes the tiles [w*per, (w+1)*per),
-// per = ceil(N / workgroups).  Every workgroup therefore streams the same
-// number of keys, whatever the ragged lengths.  Inside a tile, each of the 4
-// waves takes 16 keys.  When a workgroup leaves a segment it combines its 4
-// waves and writes one partial (m, l, o) for that segment; the last part of a
-// segment to arrive merges all of them (and the shared-prefix partials of the
-// prefix kernel) and writes the output rows.
+// Split-K over keys with one work item per workgroup.  The keys of sequence b
+// are its L_b cached rows followed by its K+1 new rows: S_b = ceil((L_b+K+1)/16)
+// slices of 16 keys.  With a slice budget `lambda` chosen on the host (the
+// smallest one for which the work items fit in one resident wave of
+// workgroups), sequence b is cut into q_b = ceil(S_b / lambda) chunks of
+// equal size (+-1 slice), and work item (b, chunk c, kv head g) is workgroup
+// Hkv * (q_0 + .. + q_{b-1}) + c * Hkv + g.  The kv head varies fastest, so
+// workgroups running side by side read the same cache rows for all heads
+// (whole DRAM rows instead of scattered 256-byte pieces).  Each of the 4
+// waves takes every 4th slice of the chunk and keeps the next one in flight.
+// At the end the workgroup combines its waves and writes one partial (m, l, o);
+// the last chunk of a (sequence, head) to arrive merges all of them and the
+// shared-prefix partials of the prefix kernel, and writes the output rows.
 
-constexpr int kTile = 64;       // keys per workgroup step (4 waves x 16)
-constexpr int kSkMaxB = 2048;   // sequences per call on the bf16 path
+constexpr int kSkMaxB = 2048;        // sequences per call on the bf16 path
 constexpr int kSkMaxKeys = 1 << 25;  // keys per sequence on the bf16 path
 
 typedef short v4s_t __attribute__((__vector_size__(8)));
@@ -137,7 +146,7 @@ __device__ __forceinline__ shortx4 lds_read_tr16(const uint16_t* p) {
 }
 
 template <int D, int NCT>
-struct SkLds {
+struct DecLds {
     static constexpr int VP = D + 4;   // V slice pitch (bf16)
     static constexpr int OP = 20;      // column pitch of the wave-combine buffer (floats)
     union {
@@ -147,113 +156,70 @@ struct SkLds {
             float m[4][16];
             float l[4][16];
         } red;
-        struct {
-            float2 ml[kMergeMax];      // (m, l) of every (part, column) of a column group
-            float w[kMergeMax];        // merge weight of every (part, column)
-            int slot[kMergeMax];       // partial slot of every part (-1 - i: prefix chunk i)
-        } mrg;
     };
-    uint16_t qs[NCT * 16][D + 8];      // the segment's query columns (B operand source)
-    int P[kSkMaxB + 1];                // P[b] = sum of n_b' over b' < b
+    uint16_t qs[NCT * 16][D + 8];      // the work item's query columns (B operand source)
+    int Q[kSkMaxB + 1];                // Q[b] = q_0 + .. + q_{b-1}
+    int L;                             // kv_len of this workgroup's sequence
+    long long kv0;                     // kv_start of this workgroup's sequence
     int flag;
 };
 
-// Segment of tile t (b, g, tile index i within the segment, n_b).
-__device__ __forceinline__ void sk_locate(const int* P, int B, int Hkv, int t, int* b, int* g,
-                                          int* i, int* nb) {
-    int lo = 0, hi = B - 1;  // largest b with Hkv * P[b] <= t
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (Hkv * P[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    *b = lo;
-    *nb = P[lo + 1] - P[lo];
-    const int r = t - Hkv * P[lo];
-    *g = r / *nb;
-    *i = r % *nb;
-}
-
-// Merge every part of segment (b, g) -- the prefix chunks first, then the
-// stream-K parts in workgroup order -- and write the output rows
-// b*(K+1)+j of heads g*G + hh.  Fixed order: bit-reproducible.
-template <int D, int NCT>
-__device__ void sk_merge(const AttnParams& p, SkLds<D, NCT>& S, int b, int g, int s0, int s1,
-                         int per) {
+// Merge every part of (sequence b, kv head g) -- the prefix chunks first, then
+// its q_b chunks in order -- and write the output rows b*(K+1)+j of heads
+// g*G + hh.  One pass with a running maximum; the loads of 4 parts are issued
+// together.  Fixed order: bit-reproducible.
+template <int D>
+__device__ void dec_merge(const AttnParams& p, int b, int g, int first_slot, int qb) {
     const int tid = threadIdx.x;
     const int np = p.prefix_slots;
-    const int w0 = s0 / per, w1 = (s1 - 1) / per;
-    const int nparts = np + (w1 - w0 + 1);
+    const int nparts = np + qb;
     const int CPG = p.CPG, K1 = p.K + 1;
-    const int seg = b * p.Hkv + g;
-    __syncthreads();
-    for (int j = tid; j < nparts; j += kThreads) {
-        if (j < np) {
-            S.mrg.slot[j] = -1 - j;
-        } else {
-            const int wp = w0 + (j - np);
-            int bb, gg, ii, nn;
-            sk_locate(S.P, p.B, p.Hkv, wp * per, &bb, &gg, &ii, &nn);
-            S.mrg.slot[j] = wp * per + (seg - (bb * p.Hkv + gg));
-        }
-    }
-    const int group = max(1, min(CPG, kMergeMax / nparts));
-    for (int c0 = 0; c0 < CPG; c0 += group) {
-        const int nc = min(group, CPG - c0);
-        __syncthreads();
-        for (int idx = tid; idx < nparts * nc; idx += kThreads) {
-            const int j = idx / nc, col = c0 + idx % nc;
-            const int sl = S.mrg.slot[j];
-            float2 v;
-            if (sl < 0) {
-                v = p.pre_ml[(static_cast<size_t>(-1 - sl) * p.Hkv + g) * p.NC +
-                             static_cast<size_t>(b) * CPG + col];
-            } else {
-                const size_t s = static_cast<size_t>(sl) * CPG + col;
-                v.x = ld_coh(&p.part_ml[s].x);
-                v.y = ld_coh(&p.part_ml[s].y);
-            }
-            S.mrg.ml[idx] = v;
-        }
-        __syncthreads();
-        for (int cl = tid; cl < nc; cl += kThreads) {
-            float ms = -INFINITY;
-            for (int j = 0; j < nparts; ++j) ms = fmaxf(ms, S.mrg.ml[j * nc + cl].x);
-            float l = 0.0f;
-            for (int j = 0; j < nparts; ++j) {
-                const float2 v = S.mrg.ml[j * nc + cl];
-                const float f = (v.x == -INFINITY) ? 0.0f : exp2f(v.x - ms);
-                S.mrg.w[j * nc + cl] = f;
-                l += v.y * f;
-            }
-            const float inv = 1.0f / l;
-            for (int j = 0; j < nparts; ++j) S.mrg.w[j * nc + cl] *= inv;
-        }
-        __syncthreads();
-        for (int idx = tid; idx < nc * D; idx += kThreads) {
-            const int cl = idx % nc, d = idx / nc, col = c0 + cl;
-            float acc = 0.0f;
-            for (int j0 = 0; j0 < nparts; j0 += 4) {
-                float v[4];
+    const size_t pre_col0 = static_cast<size_t>(g) * p.NC + static_cast<size_t>(b) * CPG;
+    for (int idx = tid; idx < CPG * D; idx += kThreads) {
+        const int col = idx % CPG, d = idx / CPG;
+        float M = -INFINITY, A = 0.0f, Ls = 0.0f;
+        for (int j0 = 0; j0 < nparts; j0 += 4) {
+            float mj[4], lj[4], oj[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int j = j0 + u;
-                    v[u] = 0.0f;
-                    if (j < nparts) {
-                        const int sl = S.mrg.slot[j];
-                        v[u] = (sl < 0)
-                                   ? p.pre_o[((static_cast<size_t>(-1 - sl) * p.Hkv + g) * p.NC +
-                                              static_cast<size_t>(b) * CPG + col) * D + d]
-                                   : ld_coh(p.part_o + (static_cast<size_t>(sl) * D + d) * CPG + col);
-                    }
+            for (int u = 0; u < 4; ++u) {
+                mj[u] = -INFINITY;
+                lj[u] = 0.0f;
+                oj[u] = 0.0f;
+                const int j = j0 + u;
+                if (j < np) {
+                    const size_t e = static_cast<size_t>(j) * p.Hkv * p.NC + pre_col0 + col;
+                    const float2 v = p.pre_ml[e];
+                    mj[u] = v.x;
+                    lj[u] = v.y;
+                    oj[u] = p.pre_o[e * D + d];
+                } else if (j < nparts) {
+                    const size_t sl = static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * p.Hkv;
+                    const size_t e = sl * CPG + col;
+                    const unsigned long long v =
+                        ld_coh(reinterpret_cast<const unsigned long long*>(p.part_ml + e));
+                    mj[u] = __uint_as_float(static_cast<unsigned>(v));
+                    lj[u] = __uint_as_float(static_cast<unsigned>(v >> 32));
+                    oj[u] = ld_coh(p.part_o + (sl * D + d) * CPG + col);
                 }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (j0 + u < nparts) acc += v[u] * S.mrg.w[(j0 + u) * nc + cl];
             }
-            const int hh = col / K1, j = col % K1;
-            const size_t oi = ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + d;
-            static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(acc);
+            float Mn = M;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, mj[u]);
+            if (Mn == -INFINITY) continue;
+            const float sc = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
+            A *= sc;
+            Ls *= sc;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float f = (mj[u] == -INFINITY) ? 0.0f : exp2f(mj[u] - Mn);
+                A += oj[u] * f;
+                Ls += lj[u] * f;
+            }
+            M = Mn;
         }
+        const int hh = col / K1, j = col % K1;
+        const size_t oi = ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + d;
+        static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(A / Ls);
     }
 }
 
@@ -265,263 +231,275 @@ struct Slice {
 };
 
 template <int D, int NCT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? 4 : 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? SV_NCT1_WAVES : 1)))
 void decode_bf16_kernel(AttnParams p) {
     constexpr int KK = D / 32;   // 16x16x32 steps over the head dim
     constexpr int DT = D / 16;   // 16-wide head-dim tiles of the PV product
     constexpr int VCH = D / 8;   // 16-byte chunks per K/V row
     constexpr int VLD = 16 * VCH / 64;  // 16-byte V loads per lane per slice
-    constexpr int VP = SkLds<D, NCT>::VP;
-    __shared__ SkLds<D, NCT> S;
+    constexpr int VP = DecLds<D, NCT>::VP;
+    constexpr int NPRO = kSkMaxB / kThreads;
+    __shared__ DecLds<D, NCT> S;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col16 = lane & 15, kg = lane >> 4;
     const int K1 = p.K + 1;
+    const int lambda = p.lambda;
+    const int id = blockIdx.x;
 
-    // tiles per sequence and their prefix (one round trip for all lengths)
-    for (int bb = tid; bb < p.B; bb += kThreads) {
-        int L = p.kv_len[bb];
-        if (L < 0) {
-            if (blockIdx.x == 0) set_status(p.status, 3);
-            L = 0;
+    // ---- chunks per sequence and their prefix sum (one round trip)
+    int Lr[NPRO];
+    long long Sr[NPRO];
+#pragma unroll
+    for (int u = 0; u < NPRO; ++u) {
+        const int bb = tid + u * kThreads;
+        Lr[u] = 0;
+        Sr[u] = 0;
+        if (bb < p.B) {
+            Lr[u] = p.kv_len[bb];
+            Sr[u] = p.kv_start[bb];
         }
-        S.P[bb + 1] = min(ceil_div(min(L, kSkMaxKeys) + K1, kTile), kSkMaxKeys / kTile);
+    }
+#pragma unroll
+    for (int u = 0; u < NPRO; ++u) {
+        const int bb = tid + u * kThreads;
+        if (bb < p.B) {
+            if (Lr[u] < 0) {
+                if (id == 0) set_status(p.status, 3);
+                Lr[u] = 0;
+            }
+            Lr[u] = min(Lr[u], kSkMaxKeys);
+            S.Q[bb + 1] = ceil_div(ceil_div(Lr[u] + K1, 16), lambda);
+        }
     }
     __syncthreads();
     if (w == 0) {
         int run = 0;
         for (int b0 = 0; b0 < p.B; b0 += 64) {
-            const int v = (b0 + lane < p.B) ? S.P[b0 + lane + 1] : 0;
+            const int v = (b0 + lane < p.B) ? S.Q[b0 + lane + 1] : 0;
             const int inc = wave_incl_scan(v, lane) + run;
-            if (b0 + lane < p.B) S.P[b0 + lane + 1] = inc;
+            if (b0 + lane < p.B) S.Q[b0 + lane + 1] = inc;
             run = __shfl(inc, 63, 64);
         }
-        if (lane == 0) S.P[0] = 0;
+        if (lane == 0) S.Q[0] = 0;
     }
     __syncthreads();
-    // A device length above the host bound would overrun the partial slots:
-    // every workgroup sees the same total and leaves.
-    const long long Nl = static_cast<long long>(p.Hkv) * S.P[p.B];
-    if (Nl > p.tiles) {
-        if (blockIdx.x == 0 && tid == 0) set_status(p.status, 3);
+    // Device lengths above the host bound would need more work items than the
+    // launch has: every workgroup sees the same total and leaves.
+    const long long items = static_cast<long long>(p.Hkv) * S.Q[p.B];
+    if (items > static_cast<long long>(gridDim.x)) {
+        if (id == 0 && tid == 0) set_status(p.status, 3);
         return;
     }
-    const int N = static_cast<int>(Nl);
-    const int per = ceil_div(N, gridDim.x);
-    const int t_lo = blockIdx.x * per;
-    const int t_hi = min(N, t_lo + per);
-    const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
-
-    int v_key[VLD], v_chunk[VLD];
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-        v_key[i] = (i * 64 + lane) / VCH;
-        v_chunk[i] = (i * 64 + lane) % VCH;
+    if (id >= items) return;
+    int b;
+    {
+        int lo = 0, hi = p.B - 1;  // largest b with Hkv * Q[b] <= id
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.Hkv * S.Q[mid] <= id) lo = mid; else hi = mid - 1;
+        }
+        b = __builtin_amdgcn_readfirstlane(lo);
     }
+    const int first_slot = p.Hkv * S.Q[b];
+    const int qb = S.Q[b + 1] - S.Q[b];
+    const int c = (id - first_slot) / p.Hkv;
+    const int g = (id - first_slot) % p.Hkv;
+#pragma unroll
+    for (int u = 0; u < NPRO; ++u) {
+        if (tid + u * kThreads == b) {
+            S.L = Lr[u];
+            S.kv0 = Sr[u];
+        }
+    }
+    __syncthreads();
+    const int L = __builtin_amdgcn_readfirstlane(S.L);
+    const long long kv0 = S.kv0;
+    const int T = L + K1;
+    const int Sb = ceil_div(T, 16);
+    const int sl_lo = static_cast<int>(static_cast<long long>(c) * Sb / qb);
+    const int sl_hi = static_cast<int>(static_cast<long long>(c + 1) * Sb / qb);
+
+    const int rs = p.Hkv * D;  // elements per cache row
+    const size_t head = static_cast<size_t>(g) * D;
     uint16_t(*vs)[VP] = S.vs[w];
     // transposed-read address of this lane: row kg*4 + col16/4, column 4*(col16%4)
     const uint16_t* vt_base = &vs[kg * 4 + (col16 >> 2)][(col16 & 3) * 4];
 
-    int k_local = 0;
-    for (int t = t_lo; t < t_hi; ++k_local) {
-        int b, g, i, nb;
-        sk_locate(S.P, p.B, p.Hkv, t, &b, &g, &i, &nb);
-        const int s0 = t - i, s1 = s0 + nb;
-        const int e = min(t_hi, s1);
-        const int L = max(p.kv_len[b], 0);
-        const int T = L + K1;
-        const int64_t kv0 = p.kv_start[b];
-        const size_t head_off = static_cast<size_t>(g) * D;
-        const int k_lo = i * kTile;
-        const int k_hi = min(T, (i + (e - t)) * kTile);
+    // Slice of keys [k0, k0+16) into registers.  Every lane addresses its own
+    // row: cache rows for keys < L, new rows after them; keys past the last
+    // one are clamped to it (and masked).
+    auto row = [&](int tt, const uint16_t* cache, const uint16_t* fresh) -> const uint16_t* {
+        tt = min(tt, T - 1);
+        return (tt < L) ? cache + static_cast<size_t>(kv0 + tt) * rs + head
+                        : fresh + static_cast<size_t>(b * K1 + (tt - L)) * rs + head;
+    };
+    auto load_slice = [&](Slice<D>& sl, int k0) {
+        const uint16_t* kp = row(k0 + col16, p.k_cache, p.k_new) + kg * 8;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sl.k[kk] = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
+#pragma unroll
+        for (int q = 0; q < VLD; ++q)
+            sl.v[q] = *reinterpret_cast<const uint4*>(row(k0 + (q * 64 + lane) / VCH, p.v_cache, p.v_new) +
+                                                      ((q * 64 + lane) % VCH) * 8);
+    };
 
-        // K/V row of key tt (keys past T clamp to the last new row)
-        auto krow = [&](int tt, const uint16_t* cache, const uint16_t* fresh) -> const uint16_t* {
-            tt = min(tt, T - 1);
-            return (tt < L) ? cache + static_cast<size_t>(kv0 + tt) * row_stride + head_off
-                            : fresh + static_cast<size_t>(b * K1 + (tt - L)) * row_stride + head_off;
-        };
-        auto load_slice = [&](Slice<D>& sl, int t0) {
-            if (t0 + 15 < L) {  // whole slice in the cache: plain strided rows
-                const uint16_t* kb = p.k_cache + static_cast<size_t>(kv0 + t0) * row_stride + head_off;
-                const uint16_t* kp = kb + col16 * row_stride + kg * 8;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) sl.k[kk] = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
-                const uint16_t* vb = p.v_cache + static_cast<size_t>(kv0 + t0) * row_stride + head_off;
-#pragma unroll
-                for (int q = 0; q < VLD; ++q)
-                    sl.v[q] = *reinterpret_cast<const uint4*>(vb + v_key[q] * row_stride + v_chunk[q] * 8);
-            } else {
-                const uint16_t* kp = krow(t0 + col16, p.k_cache, p.k_new) + kg * 8;
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) sl.k[kk] = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
-#pragma unroll
-                for (int q = 0; q < VLD; ++q)
-                    sl.v[q] = *reinterpret_cast<const uint4*>(krow(t0 + v_key[q], p.v_cache, p.v_new) +
-                                                              v_chunk[q] * 8);
-            }
-        };
+    Slice<D> sl;
+    if (sl_lo + w < sl_hi) load_slice(sl, (sl_lo + w) * 16);
 
-        const int t_first = k_lo + 16 * w;
-        Slice<D> sl;
-        if (t_first < k_hi) load_slice(sl, t_first);
-
-        // the segment's query columns -> LDS (zero rows for padding columns)
-        __syncthreads();
-        for (int idx = tid; idx < NCT * 16 * VCH; idx += kThreads) {
-            const int col = idx / VCH, ch = idx % VCH;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (col < p.CPG) {
-                const int hh = col / K1, j = col % K1;
-                v = *reinterpret_cast<const uint4*>(
-                    p.q + ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + ch * 8);
-            }
-            uint2* dst = reinterpret_cast<uint2*>(&S.qs[col][ch * 8]);
-            dst[0] = make_uint2(v.x, v.y);
-            dst[1] = make_uint2(v.z, v.w);
+    // the work item's query columns -> LDS (zero rows for padding columns)
+    for (int idx = tid; idx < NCT * 16 * VCH; idx += kThreads) {
+        const int col = idx / VCH, ch = idx % VCH;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (col < p.CPG) {
+            const int hh = col / K1, j = col % K1;
+            v = *reinterpret_cast<const uint4*>(
+                p.q + ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + ch * 8);
         }
-        int lim[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int col = ct * 16 + col16;
-            lim[ct] = (col < p.CPG) ? L + col % K1 + 1 : 0;
-        }
-        __syncthreads();
-
-        floatx4 o[NCT][DT];
-        float mrun[NCT], lrun[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            mrun[ct] = -INFINITY;
-            lrun[ct] = 0.0f;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[ct][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-
-        // Per slice: stage V in LDS, S^T = K Q^T, then reissue the slice
-        // registers for the wave's next slice (in flight during the softmax
-        // and the PV product).
-        for (int t0 = t_first; t0 < k_hi; t0 += 64) {
-#pragma unroll
-            for (int q = 0; q < VLD; ++q) {
-                uint2* dst = reinterpret_cast<uint2*>(&vs[v_key[q]][v_chunk[q] * 8]);
-                dst[0] = make_uint2(sl.v[q].x, sl.v[q].y);
-                dst[1] = make_uint2(sl.v[q].z, sl.v[q].w);
-            }
-            floatx4 acc[NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const bf16x8 qb =
-                        *reinterpret_cast<const bf16x8*>(&S.qs[ct * 16 + col16][kg * 8 + 32 * kk]);
-                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl.k[kk], qb, acc[ct], 0, 0, 0);
-                }
-            }
-            if (t0 + 64 < k_hi) load_slice(sl, t0 + 64);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // V^T operands: lane (d = dt*16 + col16) gets keys kg*4 .. kg*4+3
-            shortx4 va[DT];
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) va[dt] = lds_read_tr16(vt_base + dt * 16);
-            const bool full = t0 + 15 < L;  // no key of the slice is masked for any column
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                float s[4];
-                float mt = -INFINITY;
-#pragma unroll
-                for (int ee = 0; ee < 4; ++ee) {
-                    const int tt = t0 + kg * 4 + ee;
-                    s[ee] = (full || tt < lim[ct]) ? acc[ct][ee] * p.scale_log2 : -INFINITY;
-                    mt = fmaxf(mt, s[ee]);
-                }
-                mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-                mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-                const float mnew = fmaxf(mrun[ct], mt);
-                float alpha = 1.0f;
-                shortx4 pb;
-                if (mnew == -INFINITY) {
-                    pb = shortx4{0, 0, 0, 0};
-                } else {
-                    alpha = exp2f(mrun[ct] - mnew);
-                    float pe[4];
-#pragma unroll
-                    for (int ee = 0; ee < 4; ++ee) pe[ee] = exp2f(s[ee] - mnew);
-                    lrun[ct] = lrun[ct] * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-                    mrun[ct] = mnew;
-#pragma unroll
-                    for (int ee = 0; ee < 4; ++ee) pb[ee] = static_cast<short>(f32_to_bf16(pe[ee]));
-                }
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    o[ct][dt] *= alpha;
-                    o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, o[ct][dt], 0, 0, 0);
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            lrun[ct] += __shfl_xor(lrun[ct], 16, 64);
-            lrun[ct] += __shfl_xor(lrun[ct], 32, 64);
-        }
-
-        // combine the 4 waves (fixed order) in two halves of the head dim; the
-        // part is stored at slot blockIdx.x*per + k_local, laid out [d][column]
-        const size_t slot = static_cast<size_t>(blockIdx.x) * per + k_local;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                __syncthreads();
-                if (kg == 0 && half == 0) {
-                    S.red.m[w][col16] = mrun[ct];
-                    S.red.l[w][col16] = lrun[ct];
-                }
-#pragma unroll
-                for (int dt = half * (DT / 2); dt < (half + 1) * (DT / 2); ++dt)
-#pragma unroll
-                    for (int ee = 0; ee < 4; ++ee)
-                        S.red.o[w][(dt - half * (DT / 2)) * 16 + kg * 4 + ee][col16] = o[ct][dt][ee];
-                __syncthreads();
-                const int ncol = min(16, p.CPG - ct * 16);
-                for (int idx = tid; idx < 16 * (D / 2); idx += kThreads) {
-                    const int cl = idx & 15, dh = idx >> 4;
-                    if (cl >= ncol) continue;
-                    const int col = ct * 16 + cl, d = half * (D / 2) + dh;
-                    float ms = -INFINITY;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) ms = fmaxf(ms, S.red.m[u][cl]);
-                    float accv = 0.0f, l = 0.0f;
-                    if (ms != -INFINITY) {
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const float mu = S.red.m[u][cl];
-                            const float f = (mu == -INFINITY) ? 0.0f : exp2f(mu - ms);
-                            accv += S.red.o[u][dh][cl] * f;
-                            l += S.red.l[u][cl] * f;
-                        }
-                    }
-                    st_coh(p.part_o + (slot * D + d) * p.CPG + col, accv);
-                    if (d == 0) {
-                        st_coh(&p.part_ml[slot * p.CPG + col].x, ms);
-                        st_coh(&p.part_ml[slot * p.CPG + col].y, l);
-                    }
-                }
-            }
-        }
-
-        const int nparts = (s1 - 1) / per - s0 / per + 1;
-        if (arrive_last(p.merge_cnt + static_cast<size_t>(b) * p.Hkv + g, nparts, &S.flag))
-            sk_merge<D, NCT>(p, S, b, g, s0, s1, per);
-        t = e;
+        uint2* dst = reinterpret_cast<uint2*>(&S.qs[col][ch * 8]);
+        dst[0] = make_uint2(v.x, v.y);
+        dst[1] = make_uint2(v.z, v.w);
     }
+    int lim[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int col = ct * 16 + col16;
+        lim[ct] = (col < p.CPG) ? L + col % K1 + 1 : 0;
+    }
+    __syncthreads();
+
+    floatx4 o[NCT][DT];
+    float mrun[NCT], lrun[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        mrun[ct] = -INFINITY;
+        lrun[ct] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[ct][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Per slice: stage V in LDS, S^T = K Q^T, then reissue the slice
+    // registers for the wave's next slice (in flight during the softmax and
+    // the PV product).
+    for (int si = sl_lo + w; si < sl_hi; si += 4) {
+        const int k0 = si * 16;
+#pragma unroll
+        for (int q = 0; q < VLD; ++q) {
+            uint2* dst = reinterpret_cast<uint2*>(&vs[(q * 64 + lane) / VCH][((q * 64 + lane) % VCH) * 8]);
+            dst[0] = make_uint2(sl.v[q].x, sl.v[q].y);
+            dst[1] = make_uint2(sl.v[q].z, sl.v[q].w);
+        }
+        floatx4 acc[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const bf16x8 qb =
+                    *reinterpret_cast<const bf16x8*>(&S.qs[ct * 16 + col16][kg * 8 + 32 * kk]);
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl.k[kk], qb, acc[ct], 0, 0, 0);
+            }
+        }
+        if (si + 4 < sl_hi) load_slice(sl, k0 + 64);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // V^T operands: lane (d = dt*16 + col16) gets keys kg*4 .. kg*4+3
+        shortx4 va[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) va[dt] = lds_read_tr16(vt_base + dt * 16);
+        const bool full = k0 + 15 < L;  // no key of the slice is masked for any column
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            float s[4];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int ee = 0; ee < 4; ++ee) {
+                const int tt = k0 + kg * 4 + ee;
+                s[ee] = (full || tt < lim[ct]) ? acc[ct][ee] * p.scale_log2 : -INFINITY;
+                mt = fmaxf(mt, s[ee]);
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float mnew = fmaxf(mrun[ct], mt);
+            float alpha = 1.0f;
+            shortx4 pb;
+            if (mnew == -INFINITY) {
+                pb = shortx4{0, 0, 0, 0};
+            } else {
+                alpha = exp2f(mrun[ct] - mnew);
+                float pe[4];
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee) pe[ee] = exp2f(s[ee] - mnew);
+                lrun[ct] = lrun[ct] * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
+                mrun[ct] = mnew;
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee) pb[ee] = static_cast<short>(f32_to_bf16(pe[ee]));
+            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                o[ct][dt] *= alpha;
+                o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, o[ct][dt], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        lrun[ct] += __shfl_xor(lrun[ct], 16, 64);
+        lrun[ct] += __shfl_xor(lrun[ct], 32, 64);
+    }
+
+    // combine the 4 waves (fixed order) in two halves of the head dim; the
+    // partial of work item `id` is stored at slot id, laid out [d][column]
+    const size_t slot = static_cast<size_t>(id);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            __syncthreads();
+            if (kg == 0 && half == 0) {
+                S.red.m[w][col16] = mrun[ct];
+                S.red.l[w][col16] = lrun[ct];
+            }
+#pragma unroll
+            for (int dt = half * (DT / 2); dt < (half + 1) * (DT / 2); ++dt)
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee)
+                    S.red.o[w][(dt - half * (DT / 2)) * 16 + kg * 4 + ee][col16] = o[ct][dt][ee];
+            __syncthreads();
+            const int ncol = min(16, p.CPG - ct * 16);
+            for (int idx = tid; idx < 16 * (D / 2); idx += kThreads) {
+                const int cl = idx & 15, dh = idx >> 4;
+                if (cl >= ncol) continue;
+                const int col = ct * 16 + cl, d = half * (D / 2) + dh;
+                float ms = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) ms = fmaxf(ms, S.red.m[u][cl]);
+                float accv = 0.0f, l = 0.0f;
+                if (ms != -INFINITY) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float mu = S.red.m[u][cl];
+                        const float f = (mu == -INFINITY) ? 0.0f : exp2f(mu - ms);
+                        accv += S.red.o[u][dh][cl] * f;
+                        l += S.red.l[u][cl] * f;
+                    }
+                }
+                st_coh(p.part_o + (slot * D + d) * p.CPG + col, accv);
+                if (d == 0) {
+                    const unsigned long long v =
+                        (static_cast<unsigned long long>(__float_as_uint(l)) << 32) | __float_as_uint(ms);
+                    st_coh(reinterpret_cast<unsigned long long*>(p.part_ml + slot * p.CPG + col), v);
+                }
+            }
+        }
+    }
+    if (arrive_last(p.merge_cnt + static_cast<size_t>(b) * p.Hkv + g, qb, &S.flag))
+        dec_merge<D>(p, b, g, first_slot + g, qb);
 }
 
 template <int D>
@@ -793,7 +771,7 @@ int env_int(const char* name, int dflt) {
     return v > 0 ? v : dflt;
 }
 
-// Workgroups of the stream-K decode kernel that the GPU holds at once (CUs x
+// Workgroups of the decode kernel that the GPU holds at once (CUs x
 // resident workgroups per CU), cached per device and kernel variant.
 int sk_resident_grid(int D, int nct) {
     static int cache[16][2][4];
@@ -844,21 +822,43 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
     long long slots = 0;
     int chunk = 64;
     if (bf16) {
-        long long tiles = 0;
+        // slices per sequence for the host bound
+        int smax = 1;
         for (int b = 0; b < B; ++b) {
             const long long L = kv_len_host[b] > 0 ? kv_len_host[b] : 0;
             if (L + K1 > kSkMaxKeys) pl.ok = false;
-            tiles += (L + K1 + kTile - 1) / kTile;
+            const int sb = static_cast<int>((std::min<long long>(L, kSkMaxKeys) + K1 + 15) / 16);
+            smax = sb > smax ? sb : smax;
         }
-        tiles *= Hkv;
-        if (B > kSkMaxB || tiles > (1LL << 30)) pl.ok = false;
+        if (B > kSkMaxB) pl.ok = false;
+        auto items_for = [&](int lam) {
+            long long n = 0;
+            for (int b = 0; b < B; ++b) {
+                const long long L = kv_len_host[b] > 0 ? std::min<long long>(kv_len_host[b], kSkMaxKeys) : 0;
+                n += ((L + K1 + 15) / 16 + lam - 1) / lam;
+            }
+            return n * Hkv;
+        };
         const int nct = static_cast<int>((CPG + 15) / 16);
-        int grid = sk_resident_grid(D, nct < 4 ? nct : 4);
-        if (grid > kMergeMax - pslots) grid = kMergeMax - pslots;
-        if (grid < 1) grid = 1;
-        pl.grid = grid;
-        pl.tiles = pl.ok ? static_cast<int>(tiles) : 0;
-        slots = pl.ok ? tiles + grid : 0;
+        const long long cap = static_cast<long long>(sk_resident_grid(D, nct < 4 ? nct : 4)) *
+                              env_int("SPECVERIFY_SK_ROUNDS", 1);
+        // smallest slice budget whose work items fit in `cap` workgroups, and
+        // whose chunks per sequence fit in the merge
+        int lo = 1, hi = smax;
+        const int lam_merge = (smax + (kMergeMax - pslots) - 1) / (kMergeMax - pslots);
+        if (lo < lam_merge) lo = lam_merge;
+        if (hi < lo) hi = lo;
+        while (lo < hi) {
+            const int mid = lo + (hi - lo) / 2;
+            if (items_for(mid) <= cap) hi = mid; else lo = mid + 1;
+        }
+        const int lam_env = env_int("SPECVERIFY_SK_LAMBDA", 0);
+        if (lam_env >= lo) lo = lam_env;
+        const long long items = items_for(lo);
+        if (items > (1LL << 30)) pl.ok = false;
+        pl.lambda = lo;
+        pl.grid = pl.ok ? static_cast<int>(items) : 0;
+        slots = pl.ok ? items : 0;
     } else {
         chunk = env_int("SPECVERIFY_ATTN_CHUNK", 0);
         if (chunk <= 0) {
@@ -927,7 +927,7 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
     p.prefix_len = a.prefix_len;
     p.prefix_slots = pl.prefix_slots;
     p.slots = pl.slots;
-    p.tiles = pl.tiles;
+    p.lambda = pl.lambda;
     p.bf16 = a.bf16;
     p.scale_log2 = a.scale * kLog2e;
 

@@ -31,8 +31,8 @@ struct AttnArgs {
 // Chunking decisions made on the host from the host length bound.
 struct AttnPlan {
     int chunk, prefix_chunk, slots, prefix_slots;
-    int grid;    // bf16 path: workgroups of the stream-K decode kernel
-    int tiles;   // bf16 path: 64-key work tiles over all (sequence, kv head) for the host bound
+    int grid;    // bf16 path: workgroups (work items) of the decode kernel for the host bound
+    int lambda;  // bf16 path: 16-key slices per work item at most
     size_t bytes;
     bool ok;  // false: the sequences are too long for the merge (unsupported)
 };

@@ -136,16 +136,18 @@ SMALL_ATTN = {
     "bf16_all_empty_cache": W.small_variant(W.CONFIGS["bass_b8k5"], B=4, Hq=2, Hkv=2, len_lo=0,
                                             len_hi=0, V=64),
     "chinchilla_heads8": W.small_variant(W.CONFIGS["chinchilla_b1k4"], Hq=8, Hkv=8, V=64),
-    # more 64-key tiles than resident workgroups: each workgroup crosses
-    # several (sequence, head) segments
-    "bf16_streamk_many_segments": W.small_variant(W.CONFIGS["bass_b8k5"], B=16, Hq=8, Hkv=8,
-                                                  len_lo=1, len_hi=2500, V=64),
-    "bf16_streamk_gqa_many_segments": W.small_variant(W.CONFIGS["gqa_b64k8"], B=24, K=5, Hq=8,
-                                                      Hkv=2, len_lo=700, len_hi=3000, V=64),
-    # one long sequence: each segment is split over hundreds of workgroups
-    "bf16_streamk_long_single": W.small_variant(W.CONFIGS["chinchilla_b1k4"], Hq=2, Hkv=2,
-                                                fixed_lens=(120000,), len_lo=120000,
-                                                len_hi=120000, V=64),
+    # many (sequence, chunk, head) work items of unequal chunk counts
+    "bf16_many_items": W.small_variant(W.CONFIGS["bass_b8k5"], B=16, Hq=8, Hkv=8, len_lo=1,
+                                       len_hi=2500, V=64),
+    "bf16_gqa_many_items": W.small_variant(W.CONFIGS["gqa_b64k8"], B=24, K=5, Hq=8, Hkv=2,
+                                           len_lo=700, len_hi=3000, V=64),
+    # more work items than workgroups resident at once (one chunk each)
+    "bf16_more_items_than_resident": W.small_variant(W.CONFIGS["bass_b8k5"], B=600, K=3, Hq=2,
+                                                     Hkv=2, len_lo=0, len_hi=80, V=64),
+    # one long sequence: each (sequence, head) is cut into hundreds of chunks
+    "bf16_long_single": W.small_variant(W.CONFIGS["chinchilla_b1k4"], Hq=2, Hkv=2,
+                                        fixed_lens=(120000,), len_lo=120000, len_hi=120000,
+                                        V=64),
 }
 
 
