@@ -6,25 +6,31 @@
 // rejected position from (q - p)_+, draw a bonus token from the last target
 // row when all K drafts pass; temperature and nucleus modify q and p first.
 //
-// Kernels (one launch each, chained inside a launch by last-arriver counters):
-//   rows_kernel  grid = rows x segments.  Each workgroup reads one 4096-logit
-//                segment once, computes its max, its fp64 mass relative to
-//                that max, and (nucleus) an fp64 mass histogram over absolute
-//                quarter-unit bins of z/T.  The last segment of a row to finish
-//                merges the row: max, normaliser S, nucleus threshold (exact:
-//                the boundary bin is re-read and its few candidates sorted;
-//                a radix select over the row handles every other case), and
-//                the fp64 weight of the drafted token.  The last row of a
-//                sequence to finish runs the accept scan.
-//                Every merge first fetches all it needs with independent
-//                loads issued together (one memory round trip), then works
-//                from LDS: a chain of dependent global loads costs ~0.3 us
-//                per link on MI355X.
-//   draw_kernel  grid = sequences x segments.  fp64 residual (q'-p')_+ or
-//                bonus q' weights of the stopping row, per-segment sums; the
-//                last segment picks the crossing segment and scans it exactly.
+// rows_kernel  grid = rows x segments of 4096 logits; one kernel for the whole
+//   round when the nucleus is on (or greedy), chained by last-arriver counters:
+//   segment  read the segment once: max, fp64 mass relative to it, and
+//            (nucleus) the segment's candidate list: every element of the
+//            highest quarter-unit bins of z/T, as many bins as fit in 256
+//            entries, stored in id order.  Near-threshold tokens of a nucleus
+//            are few per segment, so the lists hold the whole nucleus.
+//   row      the last segment of a row merges it: max, normaliser, and the
+//            exact tie-closed nucleus threshold from the lists alone (bin
+//            masses, then the boundary bin's few entries ranked exactly);
+//            for target rows it also fetches the draft logits at the list
+//            ids (the residual of that position only needs those).  When a
+//            list misses part of the nucleus the row falls back to a radix
+//            select over the whole row.
+//   sequence the last row of a sequence runs the accept scan and draws the
+//            emitted token from the stopping row's list: the residual
+//            (q' - p')_+ and q' vanish outside the target nucleus.  A row
+//            without a complete list is drawn by a pass over the whole row.
+// draw_kernel  (no nucleus) grid = sequences x segments: fp64 residual or
+//   bonus weights of the stopping row, per-segment sums; the last segment
+//   picks the crossing segment and scans it exactly.
 // Every quantity that decides a token is fp64; the exp of the logits is the
 // table-driven fp64 exp of sv_math.h (table of 2^(j/64) built per workgroup).
+// A chain of dependent global accesses costs about a microsecond per link
+// under load, so every merge issues its loads together.
 #include "sv_device.h"
 #include "sv_internal.h"
 #include "sv_math.h"
@@ -35,14 +41,18 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerThread = 16;
 constexpr int kSeg = kThreads * kPerThread;  // 4096 logits per segment
-constexpr int kBins = 128;                   // nucleus histogram bins (width 0.25 in z/T)
-constexpr int kCap = 1024;                   // boundary-bin candidates sorted in LDS
+constexpr int kBins = 128;                   // quarter-unit bins of z/T below the segment max
+constexpr int kList = kThreads;              // candidate list capacity per segment
+constexpr int kCap = 1024;                   // boundary-bin entries ranked in LDS
 constexpr int kMaxSeg = 64;                  // V <= 64 * 4096
+constexpr int kChunk = 16;                   // list segments a thread loads per round trip
 constexpr int kMaxRowsPerSeq = 2 * 64 + 1;   // K <= 64
 
 struct SegHead {
     float m;      // segment max (greedy: max value)
     int kb_top;   // bin of the max (greedy: index of the max)
+    int kb_cut;   // nucleus: every element with bin >= kb_cut is in the list
+    int n;        // nucleus: list length
     double S;     // sum of exp((z - m)/T) over the segment
 };
 
@@ -53,7 +63,8 @@ struct RowRec {
     double wx;    // exp((z[x] - m)/T) for the drafted token x of this row
     int kept;     // drafted token inside the nucleus
     int argmax;   // lowest id of the row maximum (greedy)
-    int pad0, pad1;
+    int fast;     // the row's lists hold its whole nucleus
+    int pad;
 };
 
 struct SeqRec {
@@ -71,8 +82,8 @@ struct AcceptParams {
     int32_t* out_tokens;
     int32_t* status;
     SegHead* seg;
-    double* hmass;
-    int* hcnt;
+    double* hmass;             // [nrows][nseg][kBins]: fp64 mass of bin kb_top - o
+    unsigned long long* list;  // [nrows][nseg][kList]: (id << 32) | bits of z, ids ascending
     RowRec* rows;
     SeqRec* seqs;
     double* dsum;
@@ -162,51 +173,73 @@ __device__ __forceinline__ float fkey_inv(uint32_t k) {
 
 struct RowsLds {
     double tab[64];           // 2^(j/64) for exp_nonpos
-    double hm[kBins];
-    int hc[kBins];
     double red_d[kThreads / 64];
+    double red_d2[kThreads / 64];
     float red_f[kThreads / 64];
     int flag;
+    union {
+        struct {              // segment: per-wave histograms of bins kb_top - o
+            int hc[4][kBins];
+            double hm[4][kBins];
+            int cum[kBins];
+            int fit[2];
+            unsigned long long wtot[kThreads / 64];
+        } seg;
+        struct {              // row merge: boundary-bin entries
+            unsigned long long ck[kCap];  // order key: (z desc, id asc) <-> key desc
+            float rz[kCap];   // z in rank order
+            double rw[kCap];  // weight in rank order
+        } cand;
+        struct {              // radix select fallback
+            double rh_m[256];
+            int rh_c[256];
+        } rad;
+        struct {              // sequence
+            RowRec rr[kMaxRowsPerSeq];
+            float ua[64];
+            int x[64];
+            double scan[kThreads];
+            double scan2[kThreads];
+            unsigned long long run_e[kChunk];
+            float run_zp[kChunk];
+            double run0;
+        } sq;
+    };
     // row merge
     float seg_m[kMaxSeg];
     int seg_kb[kMaxSeg];
+    int seg_cut[kMaxSeg];
+    int seg_n[kMaxSeg];
     double seg_S[kMaxSeg];
     double sc[kMaxSeg];       // per-segment rescale exp((m_s - m)/T)
     float m;
     int argmax;
     double S;
     float zx;                 // logit of the drafted token of the row
-    // nucleus threshold
-    double rh_m[256];         // radix-select digit masses
-    int rh_c[256];
-    float cz[kCap];
-    int cidx[kCap];
-    double cw[kCap];
+    int kb_top, kb_lo;
+    double hm[kBins];         // row mass per bin kb_top - og
+    int og;
     int ccount;
-    int bsel;
+    int fast;
     double above;
     float tau;
     double kept;
-    int mode;                 // 0: candidate path, 1: radix fallback
     uint32_t prefix, mask;
     int chosen;
-    // sequence scan
-    RowRec rr[kMaxRowsPerSeq];
-    float ua[64];
-    int x[64];
+    int n, tok, lastpos;
 };
 
 // Exact tie-closed nucleus threshold by radix select over the whole row
 // (4 passes of 8 bits over order-preserving keys, fp64 digit masses).  Used
-// only when the boundary bin is unusable (deep threshold or flat rows).
-__device__ void radix_threshold(const AcceptParams& p, const void* row, float m, double target,
+// when a row's candidate lists do not hold its whole nucleus.
+__device__ __forceinline__ void radix_threshold(const AcceptParams& p, const void* row, float m, double target,
                                 RowsLds& L) {
     const int tid = threadIdx.x;
     if (tid == 0) { L.prefix = 0; L.mask = 0; L.above = 0.0; }
     __syncthreads();
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        for (int d = tid; d < 256; d += kThreads) { L.rh_m[d] = 0.0; L.rh_c[d] = 0; }
+        for (int d = tid; d < 256; d += kThreads) { L.rad.rh_m[d] = 0.0; L.rad.rh_c[d] = 0; }
         __syncthreads();
         const uint32_t prefix = L.prefix, mask = L.mask;
         for (int base = 0; base < p.V; base += kThreads * 16) {
@@ -219,8 +252,8 @@ __device__ void radix_threshold(const AcceptParams& p, const void* row, float m,
                 const uint32_t key = fkey(z[k]);
                 if (e < p.V && (key & mask) == prefix) {
                     const int d = (key >> shift) & 0xFF;
-                    atomicAdd(&L.rh_m[d], weight(z[k], m, p.invT, L.tab));
-                    atomicAdd(&L.rh_c[d], 1);
+                    atomicAdd(&L.rad.rh_m[d], weight(z[k], m, p.invT, L.tab));
+                    atomicAdd(&L.rad.rh_c[d], 1);
                 }
             }
         }
@@ -229,14 +262,14 @@ __device__ void radix_threshold(const AcceptParams& p, const void* row, float m,
             double cum = L.above;
             int chosen = -1, lowest = -1;
             for (int d = 255; d >= 0; --d) {
-                if (L.rh_c[d] == 0) continue;
+                if (L.rad.rh_c[d] == 0) continue;
                 lowest = d;
-                if (cum + L.rh_m[d] >= target) { chosen = d; break; }
-                cum += L.rh_m[d];
+                if (cum + L.rad.rh_m[d] >= target) { chosen = d; break; }
+                cum += L.rad.rh_m[d];
             }
             if (chosen < 0) {  // rounding left the target unreached: keep everything
                 chosen = lowest;
-                cum -= L.rh_m[lowest];
+                cum -= L.rad.rh_m[lowest];
             }
             L.above = cum;
             L.prefix |= static_cast<uint32_t>(chosen) << shift;
@@ -247,150 +280,261 @@ __device__ void radix_threshold(const AcceptParams& p, const void* row, float m,
     }
     if (tid == 0) {
         L.tau = fkey_inv(L.prefix);
-        L.kept = L.above + L.rh_m[L.chosen];
+        L.kept = L.above + L.rad.rh_m[L.chosen];
     }
     __syncthreads();
 }
 
-// Bitonic sort of L.cz/L.cidx[0, n2) by (z descending, id ascending).
-__device__ void sort_candidates(RowsLds& L, int n2) {
-    const int tid = threadIdx.x;
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < n2 / 2; i += kThreads) {
-                int a = 2 * i - (i & (stride - 1));
-                int b = a + stride;
-                bool desc_block = ((a & size) == 0);
-                float za = L.cz[a], zb = L.cz[b];
-                int ia = L.cidx[a], ib = L.cidx[b];
-                bool a_first = (za > zb) || (za == zb && ia < ib);
-                if (a_first != desc_block) {
-                    L.cz[a] = zb; L.cz[b] = za;
-                    L.cidx[a] = ib; L.cidx[b] = ia;
-                }
-            }
-            __syncthreads();
-        }
+// Inclusive wave scan of 64-bit words holding four 16-bit counters (no carry
+// crosses a field: every field total stays below 2^16).
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
     }
+    return v;
 }
 
-// Exact nucleus threshold of one row from its merged histogram: the boundary
-// bin's elements are gathered by one pass over the row (batched loads), sorted
-// by (z desc, id asc) and scanned until the kept mass reaches the target.
-__device__ void nucleus_threshold(const AcceptParams& p, int r, const void* row, float m,
-                                  double S, RowsLds& L) {
-    const int tid = threadIdx.x;
-    const double target = p.top_p * S;
-    const int kb_top = bin_of(m, p.bscale);
-    // merged histogram over bins kb_top - og, og in [0, kBins): thread og sums
-    // the segments in fixed order, four independent loads at a time
+// Block-wide exclusive scan of one double per thread in thread order; returns
+// the exclusive prefix and writes the total to *total.  Fixed order.
+__device__ __forceinline__ double block_excl_scan(double v, double* scan, double* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const double inc = wave_incl_scan(v, lane);
+    __syncthreads();
+    scan[tid] = inc;
+    __syncthreads();
+    double off = 0.0, tot = 0.0;
+#pragma unroll
+    for (int u = 0; u < kThreads / 64; ++u) {
+        const double t = scan[u * 64 + 63];
+        if (u < wv) off += t;
+        tot += t;
+    }
+    *total = tot;
+    return off + inc - v;
+}
+
+// Two block-wide exclusive scans at once (thread order, fixed order).
+__device__ __forceinline__ void block_excl_scan2(double a, double b, double* sa, double* sb,
+                                                 double* ea, double* eb, double* ta, double* tb) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const double ia = wave_incl_scan(a, lane);
+    const double ib = wave_incl_scan(b, lane);
+    __syncthreads();
+    sa[tid] = ia;
+    sb[tid] = ib;
+    __syncthreads();
+    double oa = 0.0, ob = 0.0, xa = 0.0, xb = 0.0;
+#pragma unroll
+    for (int u = 0; u < kThreads / 64; ++u) {
+        const double va = sa[u * 64 + 63], vb = sb[u * 64 + 63];
+        if (u < wv) { oa += va; ob += vb; }
+        xa += va;
+        xb += vb;
+    }
+    *ta = xa;
+    *tb = xb;
+    *ea = oa + ia - a;
+    *eb = ob + ib - b;
+}
+
+// ---------------------------------------------------------------- segment
+
+// Histograms (count, fp64 mass) over bins kb_top - o, o in [0, kBins), and
+// the candidate list: all elements of the highest bins that fit in kList
+// entries, in id order; then the segment head.
+__device__ __forceinline__ void segment_list(const AcceptParams& p, int r, int s, const float* z,
+                                             const double* w, float ms, double Ss, RowsLds& L) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int kb_top = bin_of(ms, p.bscale);
+    for (int i = tid; i < 4 * kBins; i += kThreads) {
+        (&L.seg.hc[0][0])[i] = 0;
+        (&L.seg.hm[0][0])[i] = 0.0;
+    }
+    __syncthreads();
+    int o[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        o[k] = (z[k] == -INFINITY) ? kBins : kb_top - bin_of(z[k], p.bscale);
+        if (o[k] < kBins) {
+            atomicAdd(&L.seg.hc[wv][o[k]], 1);
+            atomicAdd(&L.seg.hm[wv][o[k]], w[k]);
+        }
+    }
+    __syncthreads();
     if (tid < kBins) {
-        double hm = 0.0;
-        int hc = 0;
-        for (int s0 = 0; s0 < p.nseg; s0 += 4) {
-            double vm[4];
-            int vc[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int s = s0 + u;
-                const int o = (s < p.nseg) ? tid - (kb_top - L.seg_kb[s]) : -1;
-                const bool ok = (s < p.nseg) && o >= 0 && o < kBins && L.sc[s] != 0.0;
-                const size_t h = (static_cast<size_t>(r) * p.nseg + (ok ? s : 0)) * kBins + (ok ? o : 0);
-                vm[u] = ok ? ld_coh(p.hmass + h) : 0.0;
-                vc[u] = ok ? ld_coh(p.hcnt + h) : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (s0 + u < p.nseg) {
-                    hm += vm[u] * L.sc[s0 + u];
-                    hc += vc[u];
-                }
-            }
-        }
-        L.hm[tid] = hm;
-        L.hc[tid] = hc;
+        const int c = (L.seg.hc[0][tid] + L.seg.hc[1][tid]) + (L.seg.hc[2][tid] + L.seg.hc[3][tid]);
+        const double hmv = (L.seg.hm[0][tid] + L.seg.hm[1][tid]) + (L.seg.hm[2][tid] + L.seg.hm[3][tid]);
+        st_coh(p.hmass + (static_cast<size_t>(r) * p.nseg + s) * kBins + tid, hmv);
+        // cumulative counts from the top bin down (waves 0 and 1: bins 0..127)
+        L.seg.cum[tid] = wave_incl_scan(c, lane);
     }
     __syncthreads();
+    if (tid < kBins) {
+        const int cum = L.seg.cum[tid] + (wv == 1 ? L.seg.cum[63] : 0);
+        const unsigned long long bal = __ballot(cum <= kList);
+        if (lane == 0) L.seg.fit[wv] = __popcll(bal);
+    }
+    __syncthreads();
+    // bins 0 .. ocut fit (cum is nondecreasing); -1: the top bin alone overflows
+    const int ocut = L.seg.fit[0] + L.seg.fit[1] - 1;
+    // positions in id order: group g = k/4 holds ids s*4096 + g*1024 + 4*tid + k%4
+    unsigned long long packed = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+        if (o[k] <= ocut) packed += 1ull << (16 * (k >> 2));
+    const unsigned long long inc = wave_incl_scan_u64(packed, lane);
+    if (lane == 63) L.seg.wtot[wv] = inc;
+    __syncthreads();
+    unsigned long long off = 0, tot = 0;
+#pragma unroll
+    for (int u = 0; u < kThreads / 64; ++u) {
+        if (u < wv) off += L.seg.wtot[u];
+        tot += L.seg.wtot[u];
+    }
+    const unsigned long long excl = off + inc - packed;
+    int gofs[4];
+    int run = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        gofs[g] = run + static_cast<int>((excl >> (16 * g)) & 0xFFFF);
+        run += static_cast<int>((tot >> (16 * g)) & 0xFFFF);
+    }
+    unsigned long long* dst = p.list + (static_cast<size_t>(r) * p.nseg + s) * kList;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        if (o[k] <= ocut) {
+            const int g = k >> 2;
+            const unsigned id = static_cast<unsigned>(seg_index(s, tid, k));
+            st_coh(dst + gofs[g], (static_cast<unsigned long long>(id) << 32) | __float_as_uint(z[k]));
+            ++gofs[g];
+        }
+    }
     if (tid == 0) {
+        SegHead* h = p.seg + static_cast<size_t>(r) * p.nseg + s;
+        st_coh(&h->m, ms);
+        st_coh(&h->kb_top, kb_top);
+        st_coh(&h->kb_cut, kb_top - ocut);
+        st_coh(&h->n, run);
+        st_coh(&h->S, Ss);
+    }
+}
+
+// ---------------------------------------------------------------- row merge
+
+__device__ __forceinline__ float entry_z(unsigned long long e) {
+    return __uint_as_float(static_cast<unsigned>(e));
+}
+__device__ __forceinline__ int entry_id(unsigned long long e) { return static_cast<int>(e >> 32); }
+
+// Exact tie-closed nucleus threshold of a row from its merged histogram
+// (L.hm, fp64) and the boundary bin's entries of its candidate lists, held
+// in registers (slot tid of segments 0..kChunk-1).  Sets L.fast = 0 when the
+// lists cannot decide it.
+__device__ __forceinline__ void list_threshold(const AcceptParams& p, double target,
+                                               const unsigned long long* e, RowsLds& L) {
+    const int tid = threadIdx.x;
+    const float m = L.m;
+    const int kb_top = L.kb_top;
+    if (tid < 64) {
+        // first bin whose cumulative mass from the top reaches the target
+        // (lane l: bins 2l and 2l+1)
+        const int lane = tid;
+        const double v0 = L.hm[2 * lane], v1 = L.hm[2 * lane + 1];
+        const double inc = wave_incl_scan(v0 + v1, lane);
+        const double before = inc - (v0 + v1);
+        const unsigned long long hit = __ballot(inc >= target);
+        int og = -1;
         double cum = 0.0;
-        int bsel = -1;
-        for (int og = 0; og < kBins; ++og) {
-            if (cum + L.hm[og] >= target) { bsel = og; break; }
-            cum += L.hm[og];
+        if (hit) {
+            const int l = __ffsll(hit) - 1;
+            const double b_l = __shfl(before, l, 64), v0_l = __shfl(v0, l, 64);
+            og = (b_l + v0_l >= target) ? 2 * l : 2 * l + 1;
+            cum = (og == 2 * l) ? b_l : b_l + v0_l;
         }
-        L.bsel = bsel;
-        L.above = cum;
-        L.mode = (bsel < 0 || L.hc[bsel] > kCap) ? 1 : 0;
-        L.ccount = 0;
+        if (lane == 0) {
+            // the boundary bin must be complete in every segment's list
+            const bool ok = og >= 0 && kb_top - og >= L.kb_lo && p.nseg <= kChunk;
+            L.og = og;
+            L.above = cum;
+            L.fast = ok ? 1 : 0;
+            L.ccount = 0;
+        }
     }
     __syncthreads();
-    if (L.mode == 0) {
-        const int kb_sel = kb_top - L.bsel;
-        // one pass over the row, 8 independent 16-byte loads per thread in flight
-        for (int base = 0; base < p.V; base += kThreads * 32) {
-            float z[32];
+    if (!L.fast) return;
+    const int kb_sel = kb_top - L.og;
+    const int lane = tid & 63;
+    // boundary-bin entries -> LDS keys, one counter update per wave and chunk
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                load4(row, p.bf16, p.vec, p.V, base + (i * kThreads + tid) * 4, z + 4 * i);
-#pragma unroll
-            for (int k = 0; k < 32; ++k) {
-                const int e = base + ((k >> 2) * kThreads + tid) * 4 + (k & 3);
-                if (e < p.V && bin_of(z[k], p.bscale) == kb_sel) {
-                    const int slot = atomicAdd(&L.ccount, 1);
-                    if (slot < kCap) { L.cz[slot] = z[k]; L.cidx[slot] = e; }
-                }
-            }
+    for (int c = 0; c < kChunk; ++c) {
+        const bool in = (c < p.nseg) & (tid < L.seg_n[min(c, p.nseg - 1)]) &
+                        (bin_of(entry_z(e[c]), p.bscale) == kb_sel);
+        const unsigned long long bal = __ballot(in);
+        if (bal == 0) continue;
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&L.ccount, __popcll(bal));
+        base = __shfl(base, 0, 64);
+        const int slot = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bal >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bal), 0));
+        if (in && slot < kCap) {
+            const uint32_t id = static_cast<uint32_t>(entry_id(e[c]));
+            L.cand.ck[slot] = (static_cast<unsigned long long>(fkey(entry_z(e[c]))) << 32) | (0xFFFFFFFFu - id);
         }
+    }
+    __syncthreads();
+    const int n = L.ccount;
+    if (n > kCap || n == 0) {
+        if (tid == 0) L.fast = 0;
         __syncthreads();
-        const int n = L.ccount;
-        if (n > kCap || n == 0) {
-            if (tid == 0) L.mode = 1;
-        } else {
-            int n2 = 1;
-            while (n2 < n) n2 <<= 1;
-            for (int i = n + tid; i < n2; i += kThreads) {
-                L.cz[i] = -INFINITY;
-                L.cidx[i] = 0x7FFFFFFF;
-            }
-            __syncthreads();
-            sort_candidates(L, n2);
-            for (int i = tid; i < n; i += kThreads) L.cw[i] = weight(L.cz[i], m, p.invT, L.tab);
-            __syncthreads();
-            // first sorted candidate whose running mass reaches the target
-            if (tid < 64) {
-                const int lane = tid;
-                double run = L.above;
-                int istar = -1;
-                for (int c0 = 0; c0 < n && istar < 0; c0 += 64) {
-                    const double v = (c0 + lane < n) ? L.cw[c0 + lane] : 0.0;
-                    const double inc = run + wave_incl_scan(v, lane);
-                    const unsigned long long hit = __ballot(c0 + lane < n && inc >= target);
-                    if (hit) istar = c0 + __ffsll(hit) - 1;
-                    run = __shfl(inc, 63, 64);
-                }
-                if (istar < 0) istar = n - 1;
-                const float tau = L.cz[istar];
-                // kept mass: everything above the bin plus candidates >= tau
-                double part = 0.0;
-                for (int c0 = 0; c0 < n; c0 += 64) {
-                    const int i = c0 + lane;
-                    part += (i < n && L.cz[i] >= tau) ? L.cw[i] : 0.0;
-                }
-                part = wave_sum(part);
-                if (lane == 0) {
-                    L.tau = tau;
-                    L.kept = L.above + part;
-                }
-            }
-            __syncthreads();
+        return;
+    }
+    // rank = number of larger keys (keys are distinct); every lane of a wave
+    // reads the same key (LDS broadcast)
+    for (int i = tid; i < n; i += kThreads) {
+        const unsigned long long ki = L.cand.ck[i];
+        int rank = 0;
+        int j = 0;
+        for (; j + 4 <= n; j += 4) {
+            rank += static_cast<int>(L.cand.ck[j] > ki) + static_cast<int>(L.cand.ck[j + 1] > ki) +
+                    static_cast<int>(L.cand.ck[j + 2] > ki) + static_cast<int>(L.cand.ck[j + 3] > ki);
+        }
+        for (; j < n; ++j) rank += static_cast<int>(L.cand.ck[j] > ki);
+        const float zi = fkey_inv(static_cast<uint32_t>(ki >> 32));
+        L.cand.rz[rank] = zi;
+        L.cand.rw[rank] = weight(zi, m, p.invT, L.tab);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        double run = L.above;
+        int istar = -1;
+        for (int c0 = 0; c0 < n && istar < 0; c0 += 64) {
+            const double v = (c0 + lane < n) ? L.cand.rw[c0 + lane] : 0.0;
+            const double inc = run + wave_incl_scan(v, lane);
+            const unsigned long long hit = __ballot(c0 + lane < n && inc >= target);
+            if (hit) istar = c0 + __ffsll(hit) - 1;
+            run = __shfl(inc, 63, 64);
+        }
+        if (istar < 0) istar = n - 1;
+        const float tau = L.cand.rz[istar];
+        // kept mass: everything above the bin plus the entries >= tau (ties kept)
+        double part = 0.0;
+        for (int c0 = 0; c0 < n; c0 += 64) {
+            const int i = c0 + lane;
+            part += (i < n && L.cand.rz[i] >= tau) ? L.cand.rw[i] : 0.0;
+        }
+        part = wave_sum(part);
+        if (lane == 0) {
+            L.tau = tau;
+            L.kept = L.above + part;
         }
     }
     __syncthreads();
-    if (L.mode == 1) radix_threshold(p, row, m, target, L);
 }
 
 // Merge the segments of row r and write its RowRec.
-__device__ void finalize_row(const AcceptParams& p, int r, RowsLds& L) {
+__device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, RowsLds& L) {
     const int tid = threadIdx.x;
     const int nt = p.B * (p.K + 1);
     const void* row = row_ptr(p, r);
@@ -398,7 +542,8 @@ __device__ void finalize_row(const AcceptParams& p, int r, RowsLds& L) {
 
     // drafted token of this row: target row j < K, or draft row j
     int j = -1, b = 0;
-    if (r < nt) {
+    const bool is_target = r < nt;
+    if (is_target) {
         b = r / (p.K + 1);
         j = r % (p.K + 1);
         if (j == p.K) j = -1;
@@ -406,28 +551,64 @@ __device__ void finalize_row(const AcceptParams& p, int r, RowsLds& L) {
         b = (r - nt) / p.K;
         j = (r - nt) % p.K;
     }
-    int x = -1;
-    if (j >= 0) x = p.draft_tokens[b * p.K + j];
-    const bool x_ok = (x >= 0 && x < p.V);
 
-    // one round trip: segment heads (one per thread) and the drafted logit
+    // one round trip: segment heads, histograms (thread t: bins 8*(t%16) .. +7
+    // of segment t/16), the first kChunk segments' list slot tid, and the
+    // drafted logit
     if (tid < p.nseg) {
         L.seg_m[tid] = ld_coh(&sr[tid].m);
         L.seg_kb[tid] = ld_coh(&sr[tid].kb_top);
+        L.seg_cut[tid] = ld_coh(&sr[tid].kb_cut);
+        L.seg_n[tid] = ld_coh(&sr[tid].n);
         L.seg_S[tid] = ld_coh(&sr[tid].S);
     }
-    if (tid == kThreads - 1) L.zx = (j >= 0 && x_ok && !p.greedy) ? load1(row, p.bf16, x) : 0.0f;
-    __syncthreads();
-    if (tid == 0) {
-        float m = -INFINITY;
-        int arg = 0;
-        for (int s = 0; s < p.nseg; ++s)
-            if (L.seg_m[s] > m) { m = L.seg_m[s]; arg = L.seg_kb[s]; }
-        L.m = m;
-        L.argmax = arg;
+    const bool nuc = p.nucleus != 0;
+    double hv[8];
+    const int hs = tid >> 4, ho = (tid & 15) * 8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        hv[u] = (nuc && hs < p.nseg)
+                    ? ld_coh(p.hmass + (static_cast<size_t>(r) * p.nseg + hs) * kBins + ho + u)
+                    : 0.0;
+    unsigned long long e[kChunk];
+    const unsigned long long* lb = p.list + static_cast<size_t>(r) * p.nseg * kList;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c)
+        e[c] = (nuc && c < p.nseg) ? ld_coh(lb + static_cast<size_t>(c) * kList + tid) : 0ull;
+    if (tid == kThreads - 1) {
+        int x = -1;
+        if (j >= 0) x = p.draft_tokens[b * p.K + j];
+        L.n = x;
+        L.zx = (j >= 0 && x >= 0 && x < p.V && !p.greedy) ? load1(row, p.bf16, x) : 0.0f;
     }
     __syncthreads();
+    if (tid < 64) {
+        // row max (first segment holding it: lowest ids), deepest complete bin
+        const int lane = tid;
+        float bv = (lane < p.nseg) ? L.seg_m[lane] : -INFINITY;
+        int bs = (lane < p.nseg) ? lane : 0x7FFFFFFF;
+        int lo = (lane < p.nseg) ? L.seg_cut[lane] : -0x40000000;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int os = __shfl_xor(bs, o, 64);
+            const bool take = (ov > bv) | ((ov == bv) & (os < bs));
+            bv = take ? ov : bv;
+            bs = take ? os : bs;
+            lo = max(lo, __shfl_xor(lo, o, 64));
+        }
+        if (lane == 0) {
+            L.m = bv;
+            L.argmax = (bs < p.nseg) ? L.seg_kb[bs] : 0;
+            L.kb_top = bin_of(bv, p.bscale);
+            L.kb_lo = lo;
+        }
+    }
+    if (tid < kBins) L.hm[tid] = 0.0;
+    __syncthreads();
     const float m = L.m;
+    const int x = L.n;
+    const bool x_ok = (x >= 0 && x < p.V);
 
     RowRec rec;
     rec.m = m;
@@ -436,25 +617,37 @@ __device__ void finalize_row(const AcceptParams& p, int r, RowsLds& L) {
     rec.kept = 1;
     rec.wx = 0.0;
     rec.S = 0.0;
-    rec.pad0 = rec.pad1 = 0;
+    rec.fast = 0;
+    rec.pad = 0;
 
     if (!p.greedy) {
-        if (tid < p.nseg) {
-            const float ms = L.seg_m[tid];
-            L.sc[tid] = (ms == -INFINITY) ? 0.0 : weight(ms, m, p.invT, L.tab);
+        if (tid < 64) {
+            const float ms = (tid < p.nseg) ? L.seg_m[tid] : -INFINITY;
+            const double sc = (ms == -INFINITY) ? 0.0 : weight(ms, m, p.invT, L.tab);
+            if (tid < p.nseg) L.sc[tid] = sc;
+            const double S = wave_sum((tid < p.nseg) ? L.seg_S[tid] * sc : 0.0);
+            if (tid == 0) L.S = S;
         }
         __syncthreads();
-        if (tid == 0) {
-            double S = 0.0;
-            for (int s = 0; s < p.nseg; ++s) S += L.seg_S[s] * L.sc[s];
-            L.S = S;
+        if (nuc && hs < p.nseg) {
+            // segment bin o is row bin og = o + (kb_top - kb_top_s)
+            const int sh = L.kb_top - L.seg_kb[hs];
+            const double scs = L.sc[hs];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int og = ho + u + sh;
+                if (og < kBins && hv[u] != 0.0) atomicAdd(&L.hm[og], hv[u] * scs);
+            }
         }
         __syncthreads();
         rec.S = L.S;
-        if (p.nucleus) {
-            nucleus_threshold(p, r, row, m, L.S, L);
+        if (nuc) {
+            const double target = p.top_p * L.S;
+            list_threshold(p, target, e, L);
+            if (!L.fast) radix_threshold(p, row, m, target, L);
             rec.tau = L.tau;
             rec.S = L.kept;
+            rec.fast = L.fast;
         }
     }
     if (tid == 0) {
@@ -474,56 +667,270 @@ __device__ void finalize_row(const AcceptParams& p, int r, RowsLds& L) {
         st_coh(&dst->wx, rec.wx);
         st_coh(&dst->kept, rec.kept);
         st_coh(&dst->argmax, rec.argmax);
+        st_coh(&dst->fast, rec.fast);
     }
 }
 
-// Accept scan of sequence b once all of its rows are final.
-__device__ void finalize_sequence(const AcceptParams& p, int b, RowsLds& L) {
+// ---------------------------------------------------------------- sequence
+
+// The stopping row's parameters a draw needs (target q', draft p').
+struct DrawRows {
+    float mq, tq, mp, tp;  // row maxima and nucleus thresholds
+    double Sq, Sp;         // kept masses
+};
+
+__device__ __forceinline__ DrawRows draw_rows(const RowRec& rq, const RowRec& rp) {
+    return DrawRows{rq.m, rq.tau, rp.m, rp.tau, rq.S, rp.S};
+}
+
+// Draw weights of one element of the stopping row: residual (q'-p')_+ and q'.
+// Branch-free: the weights are computed unconditionally and selected.
+__device__ __forceinline__ void pair_weights(const DrawRows& R, bool residual, float zq, float zpv,
+                                             bool valid, double invT, const double* tab, double* d,
+                                             double* q) {
+    const double wq = weight(zq, R.mq, invT, tab) / R.Sq;  // as the oracle: w / S
+    const double qv = (valid & (zq >= R.tq)) ? wq : 0.0;
+    *q = qv;
+    if (residual) {
+        const double wp = weight(zpv, R.mp, invT, tab) / R.Sp;
+        const double pv = (valid & (zpv >= R.tp)) ? wp : 0.0;
+        const double dd = qv - pv;
+        *d = dd > 0.0 ? dd : 0.0;
+    } else {
+        *d = qv;
+    }
+}
+
+// The draw over per-thread runs of elements in id order (thread t's run
+// precedes thread t+1's).  Given this thread's sums `ds` (residual) and `qs`
+// (q'), finds the crossing run with two block scans and returns, in every
+// thread, the drawn id; `rescan(run, target, useq, &hit, &last)` walks this
+// thread's run from the prefix `run`.  The residual falls back to q' when it
+// has no mass.
+template <typename RS>
+__device__ __forceinline__ int draw_runs(const AcceptParams& p, int b, bool residual, double ds,
+                                         double qs, RS rescan, RowsLds& L) {
+    const int tid = threadIdx.x;
+    double dt, qt;
+    const double dx = block_excl_scan(ds, L.sq.scan, &dt);
+    const double qx = block_excl_scan(qs, L.sq.scan, &qt);
+    const bool useq = residual && !(dt > 0.0);
+    const double tot = useq ? qt : dt;
+    const float u = p.u_sample[b];
+    if (tid == 0 && !(u >= 0.0f && u < 1.0f)) set_status(p.status, 2);
+    const double target = static_cast<double>(u) * tot;
+    const double run0 = useq ? qx : dx;
+    const double mine = useq ? qs : ds;
+    if (tid == 0) { L.tok = 0x7FFFFFFF; L.lastpos = -1; }
+    __syncthreads();
+    if (mine > 0.0) {
+        atomicMax(&L.lastpos, tid);
+        if (run0 <= target && target < run0 + mine) {
+            int hit = 0x7FFFFFFF, last = -1;
+            rescan(run0, target, useq, &hit, &last);
+            if (hit != 0x7FFFFFFF) atomicMin(&L.tok, hit);
+        }
+    }
+    __syncthreads();
+    if (L.tok == 0x7FFFFFFF) {
+        // rounding left the target past every prefix: the last positive id
+        if (tid == L.lastpos) {
+            int hit = 0x7FFFFFFF, last = -1;
+            rescan(run0, INFINITY, useq, &hit, &last);
+            L.tok = last >= 0 ? last : 0;
+        }
+        __syncthreads();
+        if (L.tok == 0x7FFFFFFF) return 0;
+    }
+    return L.tok;
+}
+
+// Token drawn at position n of sequence b from the stopping row's lists:
+// list slots in (segment, slot) order are in id order; thread t takes the
+// contiguous run of slots [t*E, (t+1)*E), E = nseg <= kChunk.  Per-thread
+// sums, one block scan of the (residual, q') pairs, then the run that holds
+// the crossing is scanned by E lanes of wave 0 at once.
+__device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int n, RowsLds& L) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int K = p.K;
+    const int rq = b * (K + 1) + n;
+    const bool residual = n < K;
+    const DrawRows R = draw_rows(L.sq.rr[n], residual ? L.sq.rr[K + 1 + n] : L.sq.rr[n]);
+    const int E = p.nseg;
+    const unsigned long long* lb = p.list + static_cast<size_t>(rq) * p.nseg * kList;
+    // one round trip: list lengths and every slot of this thread's run
+    if (tid < p.nseg) L.seg_n[tid] = ld_coh(&p.seg[static_cast<size_t>(rq) * p.nseg + tid].n);
+    unsigned long long e[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) e[i] = (i < E) ? ld_coh(lb + tid * E + i) : 0ull;
+    __syncthreads();
+    auto is_valid = [&](int i) {
+        const int lin = tid * E + i;
+        return (i < E) & ((lin % kList) < L.seg_n[min(lin / kList, kMaxSeg - 1)]);
+    };
+    // second round trip: the residual needs the draft logits at those ids
+    const void* drow = row_ptr(p, p.B * (K + 1) + b * K + (residual ? n : 0));
+    float zpv[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+        zpv[i] = (is_valid(i) & residual) ? load1(drow, p.bf16, entry_id(e[i])) : 0.0f;
+    double ds = 0.0, qs = 0.0;
+#pragma unroll 1
+    for (int i = 0; i < E; ++i) {
+        double d, q;
+        pair_weights(R, residual, entry_z(e[i]), zpv[i], is_valid(i), p.invT, L.tab, &d, &q);
+        ds += d;
+        qs += q;
+    }
+    double dt, qt;
+    double dx, qx;
+    block_excl_scan2(ds, qs, L.sq.scan, L.sq.scan2, &dx, &qx, &dt, &qt);
+    const bool useq = residual && !(dt > 0.0);  // zero residual mass: fall back to q'
+    const double tot = useq ? qt : dt;
+    const float u = p.u_sample[b];
+    if (tid == 0 && !(u >= 0.0f && u < 1.0f)) set_status(p.status, 2);
+    const double target = static_cast<double>(u) * tot;
+    const double run0 = useq ? qx : dx;
+    const double mine = useq ? qs : ds;
+    if (tid == 0) { L.tok = 0x7FFFFFFF; L.lastpos = -1; }
+    __syncthreads();
+    if (mine > 0.0) {
+        atomicMax(&L.lastpos, tid);
+        if ((run0 <= target) & (target < run0 + mine)) L.tok = tid;  // one run holds it
+    }
+    __syncthreads();
+    const int owner = (L.tok != 0x7FFFFFFF) ? L.tok : L.lastpos;  // rounding: last positive run
+    if (owner < 0) return 0;
+    if (tid == owner) {
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            L.sq.run_e[i] = is_valid(i) ? e[i] : 0ull;
+            L.sq.run_zp[i] = zpv[i];
+        }
+        L.sq.run0 = run0;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        double d = 0.0, q = 0.0;
+        const unsigned long long ei = (lane < E) ? L.sq.run_e[lane] : 0ull;
+        pair_weights(R, residual, entry_z(ei), (lane < E) ? L.sq.run_zp[lane] : 0.0f,
+                     (lane < E) & (ei != 0ull), p.invT, L.tab, &d, &q);
+        const double w = useq ? q : d;
+        const double run = L.sq.run0 + wave_incl_scan(w, lane);
+        const bool tgt = (L.tok != 0x7FFFFFFF);
+        const unsigned long long hit = __ballot((w > 0.0) & (target < run) & tgt);
+        const unsigned long long pos = __ballot(w > 0.0);
+        int src = -1;
+        if (hit) src = __ffsll(hit) - 1;
+        else if (pos) src = 63 - __clzll(pos);
+        const int id = entry_id(ei);
+        const int tok = (src >= 0) ? __shfl(id, src, 64) : 0;
+        if (lane == 0) L.n = tok;
+    }
+    __syncthreads();
+    return L.n;
+}
+
+// Token drawn at position n of sequence b by one pass over the whole stopping
+// row (rows whose lists do not hold the nucleus): thread t owns the
+// contiguous ids [t*per, (t+1)*per).
+__device__ __forceinline__ int draw_full_row(const AcceptParams& p, int b, int n, RowsLds& L) {
+    const int tid = threadIdx.x;
+    const int K = p.K, nt = p.B * (K + 1);
+    const bool residual = n < K;
+    const DrawRows R = draw_rows(L.sq.rr[n], residual ? L.sq.rr[K + 1 + n] : L.sq.rr[n]);
+    const void* qrow = row_ptr(p, b * (K + 1) + n);
+    const void* prow = residual ? row_ptr(p, nt + b * K + n) : qrow;
+    const int per = (p.V + kThreads - 1) / kThreads;
+    const int e0 = min(p.V, tid * per), e1 = min(p.V, e0 + per);
+    const int bf16 = p.bf16;
+    const double invT = p.invT;
+    double ds = 0.0, qs = 0.0;
+    for (int e = e0; e < e1; ++e) {
+        double d, q;
+        pair_weights(R, residual, load1(qrow, bf16, e), residual ? load1(prow, bf16, e) : 0.0f,
+                     true, invT, L.tab, &d, &q);
+        ds += d;
+        qs += q;
+    }
+    auto rescan = [&](double run, double target, bool useq, int* hit, int* last) {
+        for (int e = e0; e < e1; ++e) {
+            double d, q;
+            pair_weights(R, residual, load1(qrow, bf16, e), residual ? load1(prow, bf16, e) : 0.0f,
+                         true, invT, L.tab, &d, &q);
+            const double w = useq ? q : d;
+            if (w > 0.0) {
+                *last = e;
+                run += w;
+                if (*hit == 0x7FFFFFFF && target < run) *hit = e;
+            }
+        }
+    };
+    return draw_runs(p, b, residual, ds, qs, rescan, L);
+}
+
+// Accept scan of sequence b once all of its rows are final; with the nucleus
+// on (or greedy) also the emitted token.
+__device__ __forceinline__ void finalize_sequence(const AcceptParams& p, int b, RowsLds& L) {
     const int tid = threadIdx.x;
     const int K = p.K, nt = p.B * (K + 1);
     const int nr = p.greedy ? K + 1 : 2 * K + 1;
+    __syncthreads();  // the row merge's LDS use ends
     // one round trip: the sequence's row records, drafts and uniforms
     if (tid < nr) {
         const int r = (tid <= K) ? b * (K + 1) + tid : nt + b * K + (tid - K - 1);
         const RowRec* src = p.rows + r;
-        L.rr[tid].m = ld_coh(&src->m);
-        L.rr[tid].tau = ld_coh(&src->tau);
-        L.rr[tid].S = ld_coh(&src->S);
-        L.rr[tid].wx = ld_coh(&src->wx);
-        L.rr[tid].kept = ld_coh(&src->kept);
-        L.rr[tid].argmax = ld_coh(&src->argmax);
+        L.sq.rr[tid].m = ld_coh(&src->m);
+        L.sq.rr[tid].tau = ld_coh(&src->tau);
+        L.sq.rr[tid].S = ld_coh(&src->S);
+        L.sq.rr[tid].wx = ld_coh(&src->wx);
+        L.sq.rr[tid].kept = ld_coh(&src->kept);
+        L.sq.rr[tid].argmax = ld_coh(&src->argmax);
+        L.sq.rr[tid].fast = ld_coh(&src->fast);
     }
     if (tid >= 128 && tid - 128 < K) {
-        L.x[tid - 128] = p.draft_tokens[b * K + tid - 128];
-        L.ua[tid - 128] = p.greedy ? 0.0f : p.u_accept[b * K + tid - 128];
+        L.sq.x[tid - 128] = p.draft_tokens[b * K + tid - 128];
+        L.sq.ua[tid - 128] = p.greedy ? 0.0f : p.u_accept[b * K + tid - 128];
     }
     __syncthreads();
-    if (tid != 0) return;
-    int n = K;
-    for (int jj = 0; jj < K; ++jj) {
-        bool acc;
-        const RowRec& tr = L.rr[jj];
-        if (p.greedy) {
-            acc = (L.x[jj] == tr.argmax);
-        } else {
-            const RowRec& dr = L.rr[K + 1 + jj];
-            const double q = tr.kept ? tr.wx / tr.S : 0.0;
-            const double pp = dr.kept ? dr.wx / dr.S : 0.0;
-            const float u = L.ua[jj];
-            if (!(u >= 0.0f && u < 1.0f)) set_status(p.status, 2);
-            acc = (pp > 0.0) ? (static_cast<double>(u) * pp < q) : (q > 0.0);
+    if (tid < 64) {
+        // every position's test at once (lane jj); n = first rejection
+        const int jj = tid;
+        bool acc = true;
+        if (jj < K) {
+            const RowRec& tr = L.sq.rr[jj];
+            if (p.greedy) {
+                acc = (L.sq.x[jj] == tr.argmax);
+            } else {
+                const RowRec& dr = L.sq.rr[K + 1 + jj];
+                const double q = tr.kept ? tr.wx / tr.S : 0.0;
+                const double pp = dr.kept ? dr.wx / dr.S : 0.0;
+                const float u = L.sq.ua[jj];
+                if (!(u >= 0.0f && u < 1.0f)) set_status(p.status, 2);
+                acc = (pp > 0.0) ? (static_cast<double>(u) * pp < q) : (q > 0.0);
+            }
         }
-        if (!acc) { n = jj; break; }
+        const unsigned long long rej = __ballot(jj < K && !acc);
+        if (jj == 0) L.n = rej ? __ffsll(rej) - 1 : K;
     }
-    int32_t* out = p.out_tokens + static_cast<size_t>(b) * (K + 1);
-    for (int i = 0; i < n; ++i) out[i] = L.x[i];
-    for (int i = n + 1; i <= K; ++i) out[i] = -1;
-    if (p.greedy) out[n] = L.rr[n].argmax;
-    p.n_accepted[b] = n;
-    p.seqs[b].n = n;
+    __syncthreads();
+    if (tid == 0) {
+        const int n = L.n;
+        int32_t* out = p.out_tokens + static_cast<size_t>(b) * (K + 1);
+        for (int i = 0; i < n; ++i) out[i] = L.sq.x[i];
+        for (int i = n + 1; i <= K; ++i) out[i] = -1;
+        if (p.greedy) out[n] = L.sq.rr[n].argmax;
+        p.n_accepted[b] = n;
+        p.seqs[b].n = n;
+    }
+    __syncthreads();
+    if (p.greedy || !p.nucleus) return;  // no nucleus: draw_kernel draws
+    const int n = L.n;
+    const int tok = L.sq.rr[n].fast ? draw_from_lists(p, b, n, L) : draw_full_row(p, b, n, L);
+    if (tid == 0) p.out_tokens[static_cast<size_t>(b) * (K + 1) + n] = tok;
 }
 
-__global__ __launch_bounds__(kThreads) void rows_kernel(AcceptParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void rows_kernel(AcceptParams p) {
     __shared__ RowsLds L;
     const int tid = threadIdx.x;
     const int total = p.grid_rows * p.nseg;
@@ -543,14 +950,18 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(AcceptParams p) {
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) {
             int e = seg_index(s, tid, k);
-            if (e < p.V && (z[k] > bv || (z[k] == bv && e < bi))) { bv = z[k]; bi = e; }
+            const bool take = (e < p.V) & ((z[k] > bv) | ((z[k] == bv) & (e < bi)));
+            bv = take ? z[k] : bv;
+            bi = take ? e : bi;
         }
         // (value desc, index asc) reduction
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
             float ov = __shfl_xor(bv, o, 64);
             int oi = __shfl_xor(bi, o, 64);
-            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+            const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
+            bv = take ? ov : bv;
+            bi = take ? oi : bi;
         }
         __shared__ float gv[kThreads / 64];
         __shared__ int gi[kThreads / 64];
@@ -576,29 +987,12 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(AcceptParams p) {
             acc += w[k];
         }
         const double Ss = block_sum<kThreads>(acc, L.red_d);
-        const int kb_top = bin_of(ms, p.bscale);
         if (p.nucleus) {
-            if (tid < kBins) { L.hm[tid] = 0.0; L.hc[tid] = 0; }
-            __syncthreads();
-#pragma unroll
-            for (int k = 0; k < kPerThread; ++k) {
-                const int o = kb_top - bin_of(z[k], p.bscale);
-                if (w[k] > 0.0 && o < kBins) {
-                    atomicAdd(&L.hm[o], w[k]);
-                    atomicAdd(&L.hc[o], 1);
-                }
-            }
-            __syncthreads();
-            if (tid < kBins) {
-                const size_t h = (static_cast<size_t>(r) * p.nseg + s) * kBins + tid;
-                st_coh(p.hmass + h, L.hm[tid]);
-                st_coh(p.hcnt + h, L.hc[tid]);
-            }
-        }
-        if (tid == 0) {
+            segment_list(p, r, s, z, w, ms, Ss, L);
+        } else if (tid == 0) {
             SegHead* dst = p.seg + static_cast<size_t>(r) * p.nseg + s;
             st_coh(&dst->m, ms);
-            st_coh(&dst->kb_top, kb_top);
+            st_coh(&dst->kb_top, bin_of(ms, p.bscale));
             st_coh(&dst->S, Ss);
         }
     }
@@ -645,10 +1039,12 @@ struct DrawCtx {
 
 __device__ __forceinline__ void draw_weights(const DrawCtx& c, const AcceptParams& p, float zq,
                                              float zp, bool valid, double* w, double* qv) {
-    const double q = (valid && zq >= c.rq.tau) ? weight(zq, c.rq.m, p.invT, c.tab) * c.invSq : 0.0;
+    const double wq = weight(zq, c.rq.m, p.invT, c.tab) * c.invSq;
+    const double q = (valid & (zq >= c.rq.tau)) ? wq : 0.0;
     *qv = q;
     if (c.residual) {
-        const double pv = (valid && zp >= c.rp.tau) ? weight(zp, c.rp.m, p.invT, c.tab) * c.invSp : 0.0;
+        const double wp = weight(zp, c.rp.m, p.invT, c.tab) * c.invSp;
+        const double pv = (valid & (zp >= c.rp.tau)) ? wp : 0.0;
         const double d = q - pv;
         *w = d > 0.0 ? d : 0.0;
     } else {
@@ -777,7 +1173,7 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
     for (int k = 0; k < kPerThread; ++k) {
         if (w[k] > 0.0) lastpos = e0 + k;
         run += w[k];
-        if (mine == 0x7FFFFFFF && w[k] > 0.0 && target < run) mine = e0 + k;
+        mine = ((mine == 0x7FFFFFFF) & (w[k] > 0.0) & (target < run)) ? e0 + k : mine;
     }
     if (mine != 0x7FFFFFFF) atomicMin(&L.tok, mine);
     if (lastpos >= 0) atomicMax(&L.last_pos, lastpos);
@@ -798,7 +1194,7 @@ size_t accept_workspace_bytes(int B, int K, int V) {
     auto take = [&](size_t bytes) { off = (off + 255) & ~static_cast<size_t>(255); off += bytes; };
     take(nrows * nseg * sizeof(SegHead));
     take(nrows * nseg * kBins * sizeof(double));
-    take(nrows * nseg * kBins * sizeof(int));
+    take(nrows * nseg * kList * sizeof(unsigned long long));
     take(nrows * sizeof(RowRec));
     take(static_cast<size_t>(B) * sizeof(SeqRec));
     take(static_cast<size_t>(B) * nseg * sizeof(double));
@@ -848,7 +1244,7 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     };
     p.seg = reinterpret_cast<SegHead*>(take(nrows_max * nseg * sizeof(SegHead)));
     p.hmass = reinterpret_cast<double*>(take(nrows_max * nseg * kBins * sizeof(double)));
-    p.hcnt = reinterpret_cast<int*>(take(nrows_max * nseg * kBins * sizeof(int)));
+    p.list = reinterpret_cast<unsigned long long*>(take(nrows_max * nseg * kList * sizeof(unsigned long long)));
     p.rows = reinterpret_cast<RowRec*>(take(nrows_max * sizeof(RowRec)));
     p.seqs = reinterpret_cast<SeqRec*>(take(static_cast<size_t>(a.B) * sizeof(SeqRec)));
     p.dsum = reinterpret_cast<double*>(take(static_cast<size_t>(a.B) * nseg * sizeof(double)));
@@ -859,7 +1255,7 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
 
     hipLaunchKernelGGL(rows_kernel, dim3(p.grid_rows * p.nseg), dim3(kThreads), 0, stream, p);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.greedy) return err;
+    if (err != hipSuccess || a.greedy || p.nucleus) return err;
     const int grid_seqs = (a.B + 7) / 8 * 8;
     hipLaunchKernelGGL(draw_kernel, dim3(grid_seqs * p.nseg), dim3(kThreads), 0, stream, p,
                        grid_seqs);

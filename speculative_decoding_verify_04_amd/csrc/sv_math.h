@@ -28,8 +28,11 @@ constexpr double kLn2d64Hi = 0.01083042469326756;       // ln2/64, 32 significan
 constexpr double kLn2d64Lo = 2.9815858269852933e-12;    // ln2/64 - kLn2d64Hi
 
 // exp(x) for x <= 0 (including -inf); `tab[j]` = 2^(j/64), j = 0..63.
-SV_HD double exp_nonpos(double x, const double* tab) {
-    if (!(x > -745.0)) return 0.0;  // underflow, -inf (NaN also maps to 0)
+// Branch-free: arguments at or below -745 (exp underflows), -inf and NaN give 0
+// through a final select, so vector code runs it without divergent branches.
+SV_HD double exp_nonpos(double x_in, const double* tab) {
+    const bool live = x_in > -745.0;
+    const double x = live ? x_in : -745.0;
     const double kd = rint(x * kInvLn2x64);
     double r = fma(-kd, kLn2d64Hi, x);
     r = fma(-kd, kLn2d64Lo, r);
@@ -42,7 +45,8 @@ SV_HD double exp_nonpos(double x, const double* tab) {
     p = fma(r, p, 1.0);
     p = p * r;  // exp(r) - 1
     const double t = tab[j];
-    return ldexp(fma(t, p, t), e);
+    const double r_ = ldexp(fma(t, p, t), e);
+    return live ? r_ : 0.0;
 }
 
 }  // namespace sv
