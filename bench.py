@@ -297,8 +297,11 @@ def cpu_baseline(sets, cfg, budget_s):
 
     from oracle import specref as Ref
 
+    # whole steps over the input sets in turn until the time budget is spent
+    # (at most 64 steps); the oracle does not modify its inputs
     tokens, spent, n = 0, 0.0, 0
-    for w in sets:
+    while spent < budget_s and n < 64:
+        w = sets[n % len(sets)]
         t0 = time.perf_counter()
         Ref.workload_attn(w)
         a = Ref.workload_accept(w)
@@ -307,8 +310,6 @@ def cpu_baseline(sets, cfg, budget_s):
         spent += time.perf_counter() - t0
         tokens += int((a["n_accepted"] + 1).sum())
         n += 1
-        if spent >= budget_s:
-            break
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -320,7 +321,7 @@ def cpu_baseline(sets, cfg, budget_s):
         pass
     return {"value": round(tokens / spent, 3), "unit": "verified tokens/s", "cores": 1,
             "kind": "oracle",
-            "sample": (f"{n} whole verify steps of {cfg.name} (input sets 0..{n - 1}): fp64 "
+            "sample": (f"{n} whole verify steps of {cfg.name} (input sets taken in turn): fp64 "
                        f"attention of all {cfg.rows}x{cfg.Hq} query rows, sampler on all rows, "
                        f"compaction; {spent:.1f}s on 1 thread of {cpu}")}
 
