@@ -8,51 +8,58 @@
 // least one and at most K+1 tokens per round):
 //   cu = exclusive scan of e;  packed[cu_b + i] = out_tokens[b, i];
 //   cache rows L_b .. L_b + n_b of b <- new rows 0 .. n_b;  L_b += e_b.
-// One workgroup per sequence; it computes its own scan offset, so the kernel
-// needs no cross-workgroup synchronisation.
+// One workgroup of 1024 threads per sequence; it computes its own scan offset,
+// so the kernel needs no cross-workgroup synchronisation.
 #include "sv_device.h"
 #include "sv_internal.h"
 
 namespace sv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 
 __device__ __forceinline__ int emitted(int n, int K) { return (n >= 0 && n <= K) ? n + 1 : 0; }
+
+// Copy `n16` 16-byte words of K and of V with every load of a batch issued
+// before its stores: the copy takes one memory round trip per batch.  Indices
+// past the end are clamped to the last word (re-read and re-written with its
+// own value), so the batch needs no branches.
+__device__ __forceinline__ void copy_rows16(const uint4* ks, const uint4* vs, uint4* kd, uint4* vd,
+                                            size_t n16) {
+    if (n16 == 0) return;
+    const size_t last = n16 - 1;
+    for (size_t base = threadIdx.x; base < n16; base += static_cast<size_t>(kThreads) * 4) {
+        const size_t i0 = min(base, last), i1 = min(base + kThreads, last);
+        const size_t i2 = min(base + 2 * kThreads, last), i3 = min(base + 3 * kThreads, last);
+        const uint4 k0 = ks[i0], k1 = ks[i1], k2 = ks[i2], k3 = ks[i3];
+        const uint4 v0 = vs[i0], v1 = vs[i1], v2 = vs[i2], v3 = vs[i3];
+        kd[i0] = k0; kd[i1] = k1; kd[i2] = k2; kd[i3] = k3;
+        vd[i0] = v0; vd[i1] = v1; vd[i2] = v2; vd[i3] = v3;
+    }
+}
 
 __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     __shared__ int red[kThreads / 64];
     const int b = blockIdx.x, tid = threadIdx.x;
     const int K1 = a.K + 1;
+    // independent loads, issued together
     const int nb = a.n_accepted[b];
+    const int L = a.kv_len[b];
+    const int64_t start = a.kv_start[b];
+    int part = 0;
+    for (int i = tid; i < b; i += kThreads) part += emitted(a.n_accepted[i], a.K);
     const int e = emitted(nb, a.K);
     if (tid == 0 && e == 0) set_status(a.status, 4);
 
-    int part = 0;
-    for (int i = tid; i < b; i += kThreads) part += emitted(a.n_accepted[i], a.K);
-    const int cu = block_sum<kThreads>(part, red);
-    if (tid == 0) {
-        a.cu_tokens[b] = cu;
-        if (b == a.B - 1) a.cu_tokens[a.B] = cu + e;
-    }
-    for (int i = tid; i < e; i += kThreads)
-        a.tokens_packed[cu + i] = a.out_tokens[static_cast<size_t>(b) * K1 + i];
-
-    const int L = a.kv_len[b];
     const size_t row_bytes = static_cast<size_t>(a.Hkv) * a.D * a.elem_bytes;
-    const size_t dst0 = static_cast<size_t>(a.kv_start[b] + L) * row_bytes;
+    const size_t dst0 = static_cast<size_t>(start + L) * row_bytes;
     const size_t src0 = static_cast<size_t>(b) * K1 * row_bytes;
     const size_t nbytes = static_cast<size_t>(e) * row_bytes;
     if (row_bytes % 16 == 0) {
-        const size_t n16 = nbytes / 16;
-        for (size_t i = tid; i < 2 * n16; i += kThreads) {
-            const bool v = i >= n16;
-            const size_t k = v ? i - n16 : i;
-            const uint4* src = reinterpret_cast<const uint4*>(
-                static_cast<const char*>(v ? a.v_new : a.k_new) + src0) + k;
-            uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(v ? a.v_cache : a.k_cache) + dst0) + k;
-            *dst = *src;
-        }
+        copy_rows16(reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src0),
+                    reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_new) + src0),
+                    reinterpret_cast<uint4*>(static_cast<char*>(a.k_cache) + dst0),
+                    reinterpret_cast<uint4*>(static_cast<char*>(a.v_cache) + dst0), nbytes / 16);
     } else {
         const size_t n4 = nbytes / 4;
         for (size_t i = tid; i < 2 * n4; i += kThreads) {
@@ -65,8 +72,14 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
             *dst = *src;
         }
     }
-    __syncthreads();  // every thread has read kv_len[b]
-    if (tid == 0) a.kv_len[b] = L + e;
+    const int cu = block_sum<kThreads>(part, red);  // also: every thread has read kv_len[b]
+    if (tid == 0) {
+        a.cu_tokens[b] = cu;
+        if (b == a.B - 1) a.cu_tokens[a.B] = cu + e;
+        a.kv_len[b] = L + e;
+    }
+    for (int i = tid; i < e; i += kThreads)
+        a.tokens_packed[cu + i] = a.out_tokens[static_cast<size_t>(b) * K1 + i];
 }
 
 }  // namespace
