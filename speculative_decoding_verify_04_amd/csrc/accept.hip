@@ -285,17 +285,6 @@ __device__ __forceinline__ void radix_threshold(const AcceptParams& p, const voi
     __syncthreads();
 }
 
-// Inclusive wave scan of 64-bit words holding four 16-bit counters (no carry
-// crosses a field: every field total stays below 2^16).
-__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long v, int lane) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long t = __shfl_up(v, o, 64);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
 // Block-wide exclusive scan of one double per thread in thread order; returns
 // the exclusive prefix and writes the total to *total.  Fixed order.
 __device__ __forceinline__ double block_excl_scan(double v, double* scan, double* total) {
@@ -384,7 +373,8 @@ __device__ __forceinline__ void segment_list(const AcceptParams& p, int r, int s
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k)
         if (o[k] <= ocut) packed += 1ull << (16 * (k >> 2));
-    const unsigned long long inc = wave_incl_scan_u64(packed, lane);
+    // 64-bit words holding four 16-bit counters: no carry crosses a field
+    const unsigned long long inc = wave_incl_scan(packed, lane);
     if (lane == 63) L.seg.wtot[wv] = inc;
     __syncthreads();
     unsigned long long off = 0, tot = 0;
@@ -469,8 +459,8 @@ __device__ __forceinline__ void list_threshold(const AcceptParams& p, double tar
     // boundary-bin entries -> LDS keys, one counter update per wave and chunk
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
-        const bool in = (c < p.nseg) & (tid < L.seg_n[min(c, p.nseg - 1)]) &
-                        (bin_of(entry_z(e[c]), p.bscale) == kb_sel);
+        const bool in = static_cast<int>(c < p.nseg) & static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
+                        static_cast<int>(bin_of(entry_z(e[c]), p.bscale) == kb_sel);
         const unsigned long long bal = __ballot(in);
         if (bal == 0) continue;
         int base = 0;

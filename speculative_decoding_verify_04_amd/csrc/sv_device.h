@@ -23,47 +23,101 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return static_cast<uint16_t>(u >> 16);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+// ---- Wave-wide scans and reductions with DPP (data-parallel primitives).
+// An inclusive scan over the 64 lanes takes seven DPP steps: row_shr 1, 2, 3
+// (within rows of 16 lanes), row_shr 4 and 8 on the upper banks, then
+// row_bcast 15 and 31 to carry between rows.  Lanes a step does not update
+// receive the identity.  This runs at VALU speed; a scan built from
+// ds_bpermute shuffles costs about three times as long on gfx950.  The order
+// of the combinations is fixed, so results are bit-reproducible.
+template <int CTRL, int ROW, int BANK>
+__device__ __forceinline__ int dpp_i(int v, int identity) {
+    return __builtin_amdgcn_update_dpp(identity, v, CTRL, ROW, BANK, true);
+}
+template <int CTRL, int ROW, int BANK>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long bits = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits), CTRL, ROW, BANK, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(bits >> 32), CTRL, ROW, BANK, true);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+template <int CTRL, int ROW, int BANK>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW, BANK, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(v >> 32), CTRL, ROW, BANK, true);
+    return (static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) | static_cast<unsigned>(lo);
+}
+
+// Inclusive prefix sum across the wave in lane order (`lane` is unused; kept
+// for call-site symmetry).
+__device__ __forceinline__ double wave_incl_scan(double v, int /*lane*/) {
+    double r = v + dpp_d<0x111, 0xF, 0xF>(v);
+    r += dpp_d<0x112, 0xF, 0xF>(v);
+    r += dpp_d<0x113, 0xF, 0xF>(v);
+    r += dpp_d<0x114, 0xF, 0xE>(r);
+    r += dpp_d<0x118, 0xF, 0xC>(r);
+    r += dpp_d<0x142, 0xA, 0xF>(r);
+    r += dpp_d<0x143, 0xC, 0xF>(r);
+    return r;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+    int r = v + dpp_i<0x111, 0xF, 0xF>(v, 0);
+    r += dpp_i<0x112, 0xF, 0xF>(v, 0);
+    r += dpp_i<0x113, 0xF, 0xF>(v, 0);
+    r += dpp_i<0x114, 0xF, 0xE>(r, 0);
+    r += dpp_i<0x118, 0xF, 0xC>(r, 0);
+    r += dpp_i<0x142, 0xA, 0xF>(r, 0);
+    r += dpp_i<0x143, 0xC, 0xF>(r, 0);
+    return r;
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_scan(unsigned long long v, int /*lane*/) {
+    unsigned long long r = v + dpp_u64<0x111, 0xF, 0xF>(v);
+    r += dpp_u64<0x112, 0xF, 0xF>(v);
+    r += dpp_u64<0x113, 0xF, 0xF>(v);
+    r += dpp_u64<0x114, 0xF, 0xE>(r);
+    r += dpp_u64<0x118, 0xF, 0xC>(r);
+    r += dpp_u64<0x142, 0xA, 0xF>(r);
+    r += dpp_u64<0x143, 0xC, 0xF>(r);
+    return r;
+}
+
+// Value of lane 63 in every lane (a uniform result).
+__device__ __forceinline__ double lane63(double v) {
+    const long long bits = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(bits), 63);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), 63);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+__device__ __forceinline__ double wave_sum(double v) { return lane63(wave_incl_scan(v, 0)); }
+
+__device__ __forceinline__ int wave_sum(int v) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(v, 0), 63);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    float r = v + __int_as_float(dpp_i<0x111, 0xF, 0xF>(__float_as_int(v), 0));
+    r += __int_as_float(dpp_i<0x112, 0xF, 0xF>(__float_as_int(v), 0));
+    r += __int_as_float(dpp_i<0x113, 0xF, 0xF>(__float_as_int(v), 0));
+    r += __int_as_float(dpp_i<0x114, 0xF, 0xE>(__float_as_int(r), 0));
+    r += __int_as_float(dpp_i<0x118, 0xF, 0xC>(__float_as_int(r), 0));
+    r += __int_as_float(dpp_i<0x142, 0xA, 0xF>(__float_as_int(r), 0));
+    r += __int_as_float(dpp_i<0x143, 0xC, 0xF>(__float_as_int(r), 0));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 63));
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-
-// Inclusive prefix sum across the wave in lane order (Hillis-Steele).
-__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        double t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
-    return v;
+__device__ __forceinline__ float wave_max(float v) {
+    const int ninf = __float_as_int(-INFINITY);
+    float r = fmaxf(v, __int_as_float(dpp_i<0x111, 0xF, 0xF>(__float_as_int(v), ninf)));
+    r = fmaxf(r, __int_as_float(dpp_i<0x112, 0xF, 0xF>(__float_as_int(v), ninf)));
+    r = fmaxf(r, __int_as_float(dpp_i<0x113, 0xF, 0xF>(__float_as_int(v), ninf)));
+    r = fmaxf(r, __int_as_float(dpp_i<0x114, 0xF, 0xE>(__float_as_int(r), ninf)));
+    r = fmaxf(r, __int_as_float(dpp_i<0x118, 0xF, 0xC>(__float_as_int(r), ninf)));
+    r = fmaxf(r, __int_as_float(dpp_i<0x142, 0xA, 0xF>(__float_as_int(r), ninf)));
+    r = fmaxf(r, __int_as_float(dpp_i<0x143, 0xC, 0xF>(__float_as_int(r), ninf)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), 63));
 }
 
 // Block-wide reductions for blockDim.x == NT (multiple of 64).  `red` is LDS
