@@ -46,6 +46,7 @@ constexpr int kList = kThreads;              // candidate list capacity per segm
 constexpr int kCap = 1024;                   // boundary-bin entries ranked in LDS
 constexpr int kMaxSeg = 64;                  // V <= 64 * 4096
 constexpr int kChunk = 16;                   // list segments a thread loads per round trip
+constexpr int kNuc = 2048;                   // nucleus members a list draw handles
 constexpr int kMaxRowsPerSeq = 2 * 64 + 1;   // K <= 64
 
 struct SegHead {
@@ -200,8 +201,9 @@ struct RowsLds {
             int x[64];
             double scan[kThreads];
             double scan2[kThreads];
-            unsigned long long run_e[kChunk];
-            float run_zp[kChunk];
+            float mz[kNuc];   // nucleus members of the stopping row, in id order
+            int mid[kNuc];
+            float run_zp[kNuc / kThreads];
             double run0;
         } sq;
     };
@@ -735,40 +737,66 @@ __device__ __forceinline__ int draw_runs(const AcceptParams& p, int b, bool resi
     return L.tok;
 }
 
-// Token drawn at position n of sequence b from the stopping row's lists:
-// list slots in (segment, slot) order are in id order; thread t takes the
-// contiguous run of slots [t*E, (t+1)*E), E = nseg <= kChunk.  Per-thread
-// sums, one block scan of the (residual, q') pairs, then the run that holds
-// the crossing is scanned by E lanes of wave 0 at once.
+// Token drawn at position n of sequence b from the stopping row's lists.  The
+// residual (q'-p')_+ and q' vanish outside the target nucleus, so only list
+// entries with z >= tau_q take part: they are compacted in id order into LDS
+// (list slots in (segment, slot) order are in id order), the draft logits are
+// fetched at their ids, thread t takes the contiguous run [t*E, (t+1)*E) of
+// members, and one block scan of the (residual, q') pairs finds the run that
+// holds the crossing, which E lanes of wave 0 then scan at once.  Returns -1
+// when the nucleus has more than kNuc members (the caller then draws from the
+// whole row).
 __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int n, RowsLds& L) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int K = p.K;
     const int rq = b * (K + 1) + n;
     const bool residual = n < K;
     const DrawRows R = draw_rows(L.sq.rr[n], residual ? L.sq.rr[K + 1 + n] : L.sq.rr[n]);
-    const int E = p.nseg;
+    const int E0 = p.nseg;
     const unsigned long long* lb = p.list + static_cast<size_t>(rq) * p.nseg * kList;
     // one round trip: list lengths and every slot of this thread's run
     if (tid < p.nseg) L.seg_n[tid] = ld_coh(&p.seg[static_cast<size_t>(rq) * p.nseg + tid].n);
     unsigned long long e[kChunk];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) e[i] = (i < E) ? ld_coh(lb + tid * E + i) : 0ull;
+    for (int i = 0; i < kChunk; ++i) e[i] = (i < E0) ? ld_coh(lb + tid * E0 + i) : 0ull;
     __syncthreads();
-    auto is_valid = [&](int i) {
-        const int lin = tid * E + i;
-        return (i < E) & ((lin % kList) < L.seg_n[min(lin / kList, kMaxSeg - 1)]);
-    };
+    // nucleus members in id order -> LDS
+    int cnt = 0;
+    bool mem[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        const int lin = tid * E0 + i;
+        mem[i] = static_cast<int>(i < E0) & static_cast<int>((lin % kList) < L.seg_n[min(lin / kList, kMaxSeg - 1)]) &
+                 static_cast<int>(entry_z(e[i]) >= R.tq);
+        cnt += mem[i] ? 1 : 0;
+    }
+    double unused;
+    int pos = static_cast<int>(block_excl_scan(static_cast<double>(cnt), L.sq.scan, &unused));
+    const int M = static_cast<int>(unused);
+    if (M > kNuc) return -1;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        if (mem[i]) {
+            L.sq.mz[pos] = entry_z(e[i]);
+            L.sq.mid[pos] = entry_id(e[i]);
+            ++pos;
+        }
+    }
+    __syncthreads();
+    const int E = (M + kThreads - 1) / kThreads;  // <= kNuc / kThreads
+    const int m0 = tid * E;
     // second round trip: the residual needs the draft logits at those ids
     const void* drow = row_ptr(p, p.B * (K + 1) + b * K + (residual ? n : 0));
-    float zpv[kChunk];
+    float zpv[kNuc / kThreads];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i)
-        zpv[i] = (is_valid(i) & residual) ? load1(drow, p.bf16, entry_id(e[i])) : 0.0f;
+    for (int i = 0; i < kNuc / kThreads; ++i)
+        zpv[i] = (residual & (i < E) & (m0 + i < M)) ? load1(drow, p.bf16, L.sq.mid[m0 + i]) : 0.0f;
     double ds = 0.0, qs = 0.0;
-#pragma unroll 1
-    for (int i = 0; i < E; ++i) {
-        double d, q;
-        pair_weights(R, residual, entry_z(e[i]), zpv[i], is_valid(i), p.invT, L.tab, &d, &q);
+#pragma unroll
+    for (int i = 0; i < kNuc / kThreads; ++i) {
+        double d = 0.0, q = 0.0;
+        if ((i < E) & (m0 + i < M))
+            pair_weights(R, residual, L.sq.mz[m0 + i], zpv[i], true, p.invT, L.tab, &d, &q);
         ds += d;
         qs += q;
     }
@@ -793,27 +821,26 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
     if (owner < 0) return 0;
     if (tid == owner) {
 #pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            L.sq.run_e[i] = is_valid(i) ? e[i] : 0ull;
-            L.sq.run_zp[i] = zpv[i];
-        }
+        for (int i = 0; i < kNuc / kThreads; ++i) L.sq.run_zp[i] = zpv[i];
         L.sq.run0 = run0;
     }
     __syncthreads();
     if (tid < 64) {
+        const int mi = owner * E + lane;
+        const bool ok = (lane < E) & (mi < M);
         double d = 0.0, q = 0.0;
-        const unsigned long long ei = (lane < E) ? L.sq.run_e[lane] : 0ull;
-        pair_weights(R, residual, entry_z(ei), (lane < E) ? L.sq.run_zp[lane] : 0.0f,
-                     (lane < E) & (ei != 0ull), p.invT, L.tab, &d, &q);
+        if (ok)
+            pair_weights(R, residual, L.sq.mz[mi], L.sq.run_zp[min(lane, kNuc / kThreads - 1)], true,
+                         p.invT, L.tab, &d, &q);
         const double w = useq ? q : d;
         const double run = L.sq.run0 + wave_incl_scan(w, lane);
         const bool tgt = (L.tok != 0x7FFFFFFF);
         const unsigned long long hit = __ballot((w > 0.0) & (target < run) & tgt);
-        const unsigned long long pos = __ballot(w > 0.0);
+        const unsigned long long posb = __ballot(w > 0.0);
         int src = -1;
         if (hit) src = __ffsll(hit) - 1;
-        else if (pos) src = 63 - __clzll(pos);
-        const int id = entry_id(ei);
+        else if (posb) src = 63 - __clzll(posb);
+        const int id = ok ? L.sq.mid[mi] : 0;
         const int tok = (src >= 0) ? __shfl(id, src, 64) : 0;
         if (lane == 0) L.n = tok;
     }
@@ -916,7 +943,8 @@ __device__ __forceinline__ void finalize_sequence(const AcceptParams& p, int b, 
     __syncthreads();
     if (p.greedy || !p.nucleus) return;  // no nucleus: draw_kernel draws
     const int n = L.n;
-    const int tok = L.sq.rr[n].fast ? draw_from_lists(p, b, n, L) : draw_full_row(p, b, n, L);
+    int tok = L.sq.rr[n].fast ? draw_from_lists(p, b, n, L) : -1;
+    if (tok < 0) tok = draw_full_row(p, b, n, L);
     if (tid == 0) p.out_tokens[static_cast<size_t>(b) * (K + 1) + n] = tok;
 }
 
