@@ -178,7 +178,7 @@ struct RowsLds {
     double red_d2[kThreads / 64];
     float red_f[kThreads / 64];
     int flag;
-    union {
+    union alignas(16) {
         struct {              // segment: per-wave histograms of bins kb_top - o
             int hc[4][kBins];
             double hm[4][kBins];
@@ -187,7 +187,8 @@ struct RowsLds {
             unsigned long long wtot[kThreads / 64];
         } seg;
         struct {              // row merge: boundary-bin entries
-            unsigned long long ck[kCap];  // order key: (z desc, id asc) <-> key desc
+            unsigned long long ck[kCap + 8];  // order key: (z desc, id asc) <-> key desc
+            int wcnt[kThreads / 64];
             float rz[kCap];   // z in rank order
             double rw[kCap];  // weight in rank order
         } cand;
@@ -458,22 +459,34 @@ __device__ __forceinline__ void list_threshold(const AcceptParams& p, double tar
     if (!L.fast) return;
     const int kb_sel = kb_top - L.og;
     const int lane = tid & 63;
-    // boundary-bin entries -> LDS keys, one counter update per wave and chunk
+    // boundary-bin entries -> LDS keys: per-wave counts, one barrier for the
+    // wave offsets, then positions from the ballots (no contended counter)
+    const int wv = tid >> 6;
+    unsigned long long bal[kChunk];
+    int wcount = 0;
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
         const bool in = static_cast<int>(c < p.nseg) & static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
                         static_cast<int>(bin_of(entry_z(e[c]), p.bscale) == kb_sel);
-        const unsigned long long bal = __ballot(in);
-        if (bal == 0) continue;
-        int base = 0;
-        if (lane == 0) base = atomicAdd(&L.ccount, __popcll(bal));
-        base = __shfl(base, 0, 64);
-        const int slot = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bal >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bal), 0));
-        if (in && slot < kCap) {
+        bal[c] = __ballot(in);
+        wcount += __popcll(bal[c]);
+    }
+    if (lane == 0) L.cand.wcnt[wv] = wcount;
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int u = 0; u < kThreads / 64; ++u) base += (u < wv) ? L.cand.wcnt[u] : 0;
+    if (tid == 0) L.ccount = L.cand.wcnt[0] + L.cand.wcnt[1] + L.cand.wcnt[2] + L.cand.wcnt[3];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+        const unsigned long long bc = bal[c];
+        const int slot = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
+        if (((bc >> lane) & 1ull) && slot < kCap) {
             const uint32_t id = static_cast<uint32_t>(entry_id(e[c]));
             L.cand.ck[slot] = (static_cast<unsigned long long>(fkey(entry_z(e[c]))) << 32) | (0xFFFFFFFFu - id);
         }
+        base += __popcll(bc);
     }
     __syncthreads();
     const int n = L.ccount;
@@ -483,16 +496,20 @@ __device__ __forceinline__ void list_threshold(const AcceptParams& p, double tar
         return;
     }
     // rank = number of larger keys (keys are distinct); every lane of a wave
-    // reads the same key (LDS broadcast)
+    // reads the same keys (LDS broadcast), 8 per batch
+    for (int i = n + tid; i < ((n + 7) & ~7); i += kThreads) L.cand.ck[i] = 0ull;  // pad: never larger
+    __syncthreads();
     for (int i = tid; i < n; i += kThreads) {
         const unsigned long long ki = L.cand.ck[i];
         int rank = 0;
-        int j = 0;
-        for (; j + 4 <= n; j += 4) {
-            rank += static_cast<int>(L.cand.ck[j] > ki) + static_cast<int>(L.cand.ck[j + 1] > ki) +
-                    static_cast<int>(L.cand.ck[j + 2] > ki) + static_cast<int>(L.cand.ck[j + 3] > ki);
+        const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(L.cand.ck);
+#pragma unroll 2
+        for (int j = 0; j < n; j += 8) {
+            const ulonglong2 a0 = k2[j / 2], a1 = k2[j / 2 + 1], a2 = k2[j / 2 + 2], a3 = k2[j / 2 + 3];
+            rank += static_cast<int>(a0.x > ki) + static_cast<int>(a0.y > ki) + static_cast<int>(a1.x > ki) +
+                    static_cast<int>(a1.y > ki) + static_cast<int>(a2.x > ki) + static_cast<int>(a2.y > ki) +
+                    static_cast<int>(a3.x > ki) + static_cast<int>(a3.y > ki);
         }
-        for (; j < n; ++j) rank += static_cast<int>(L.cand.ck[j] > ki);
         const float zi = fkey_inv(static_cast<uint32_t>(ki >> 32));
         L.cand.rz[rank] = zi;
         L.cand.rw[rank] = weight(zi, m, p.invT, L.tab);
