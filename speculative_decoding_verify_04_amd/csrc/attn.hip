@@ -42,6 +42,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;
 constexpr int kMergeMax = 1024;  // parts (prefix chunks + workgroups) merged per segment
+constexpr int kMergeLds = 1536;  // (part, column) weights of a merge staged in LDS at a time
 
 struct AttnParams {
     const uint16_t* q;
@@ -156,6 +157,10 @@ struct DecLds {
             float m[4][16];
             float l[4][16];
         } red;
+        struct {
+            float2 ml[kMergeLds];      // (m, l) of (part, column) pairs of a column group
+            float w[kMergeLds];        // their merge weights
+        } mrg;
     };
     uint16_t qs[NCT * 16][D + 8];      // the work item's query columns (B operand source)
     int Q[kSkMaxB + 1];                // Q[b] = q_0 + .. + q_{b-1}
@@ -166,60 +171,96 @@ struct DecLds {
 
 // Merge every part of (sequence b, kv head g) -- the prefix chunks first, then
 // its q_b chunks in order -- and write the output rows b*(K+1)+j of heads
-// g*G + hh.  One pass with a running maximum; the loads of 4 parts are issued
-// together.  Fixed order: bit-reproducible.
-template <int D>
-__device__ void dec_merge(const AttnParams& p, int b, int g, int first_slot, int qb) {
+// g*G + hh.  Two round trips: the (m, l) of every (part, column) into LDS and
+// the per-column weights, then every o value weighted, with the loads of up
+// to 4 columns x 8 parts in flight per thread.  Fixed order: bit-reproducible.
+template <int D, typename MRG>
+__device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_slot, int qb) {
     const int tid = threadIdx.x;
     const int np = p.prefix_slots;
     const int nparts = np + qb;
     const int CPG = p.CPG, K1 = p.K + 1;
     const size_t pre_col0 = static_cast<size_t>(g) * p.NC + static_cast<size_t>(b) * CPG;
-    for (int idx = tid; idx < CPG * D; idx += kThreads) {
-        const int col = idx % CPG, d = idx / CPG;
-        float M = -INFINITY, A = 0.0f, Ls = 0.0f;
-        for (int j0 = 0; j0 < nparts; j0 += 4) {
-            float mj[4], lj[4], oj[4];
+    auto slot_of = [&](int j) {  // partial slot of stream part j >= np
+        return static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * p.Hkv;
+    };
+    const int group = max(1, min(CPG, kMergeLds / nparts));
+    for (int c0 = 0; c0 < CPG; c0 += group) {
+        const int nc = min(group, CPG - c0);
+        __syncthreads();
+        for (int idx = tid; idx < nparts * nc; idx += kThreads) {
+            const int j = idx / nc, col = c0 + idx % nc;
+            float2 v;
+            if (j < np) {
+                v = p.pre_ml[static_cast<size_t>(j) * p.Hkv * p.NC + pre_col0 + col];
+            } else {
+                const unsigned long long u =
+                    ld_coh(reinterpret_cast<const unsigned long long*>(p.part_ml + slot_of(j) * CPG + col));
+                v = make_float2(__uint_as_float(static_cast<unsigned>(u)),
+                                __uint_as_float(static_cast<unsigned>(u >> 32)));
+            }
+            M.ml[idx] = v;
+        }
+        __syncthreads();
+        for (int cl = tid; cl < nc; cl += kThreads) {
+            float ms = -INFINITY;
+            for (int j = 0; j < nparts; ++j) ms = fmaxf(ms, M.ml[j * nc + cl].x);
+            float l = 0.0f;
+            for (int j = 0; j < nparts; ++j) {
+                const float2 v = M.ml[j * nc + cl];
+                const float f = (v.x == -INFINITY) ? 0.0f : exp2f(v.x - ms);
+                M.w[j * nc + cl] = f;
+                l += v.y * f;
+            }
+            const float inv = 1.0f / l;
+            for (int j = 0; j < nparts; ++j) M.w[j * nc + cl] *= inv;
+        }
+        __syncthreads();
+        const int npairs = nc * D;
+        for (int q0 = tid; q0 < npairs; q0 += 4 * kThreads) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            int off[4];  // element offset of pair u inside one part ([d][column] layout)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                mj[u] = -INFINITY;
-                lj[u] = 0.0f;
-                oj[u] = 0.0f;
-                const int j = j0 + u;
-                if (j < np) {
-                    const size_t e = static_cast<size_t>(j) * p.Hkv * p.NC + pre_col0 + col;
-                    const float2 v = p.pre_ml[e];
-                    mj[u] = v.x;
-                    lj[u] = v.y;
-                    oj[u] = p.pre_o[e * D + d];
-                } else if (j < nparts) {
-                    const size_t sl = static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * p.Hkv;
-                    const size_t e = sl * CPG + col;
-                    const unsigned long long v =
-                        ld_coh(reinterpret_cast<const unsigned long long*>(p.part_ml + e));
-                    mj[u] = __uint_as_float(static_cast<unsigned>(v));
-                    lj[u] = __uint_as_float(static_cast<unsigned>(v >> 32));
-                    oj[u] = ld_coh(p.part_o + (sl * D + d) * CPG + col);
+                const int pq = min(q0 + u * kThreads, npairs - 1);
+                off[u] = (pq / nc) * CPG + c0 + pq % nc;
+            }
+            for (int j0 = 0; j0 < nparts; j0 += 8) {
+                float ov[8][4];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int j = min(j0 + jj, nparts - 1);  // past the end: re-read the last part
+                    // the part's base is uniform over the workgroup
+                    const float* pb = (j < np) ? nullptr : p.part_o + slot_of(j) * D * CPG;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (j < np) {
+                            const int pq = min(q0 + u * kThreads, npairs - 1);
+                            ov[jj][u] = p.pre_o[(static_cast<size_t>(j) * p.Hkv * p.NC + pre_col0 + c0 +
+                                                 pq % nc) * D + pq / nc];
+                        } else {
+                            ov[jj][u] = ld_coh(pb + off[u]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int cl = min(q0 + u * kThreads, npairs - 1) % nc;
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj)
+                        if (j0 + jj < nparts) acc[u] += ov[jj][u] * M.w[(j0 + jj) * nc + cl];
                 }
             }
-            float Mn = M;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, mj[u]);
-            if (Mn == -INFINITY) continue;
-            const float sc = (M == -INFINITY) ? 0.0f : exp2f(M - Mn);
-            A *= sc;
-            Ls *= sc;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float f = (mj[u] == -INFINITY) ? 0.0f : exp2f(mj[u] - Mn);
-                A += oj[u] * f;
-                Ls += lj[u] * f;
+                const int pq = q0 + u * kThreads;
+                if (pq >= npairs) continue;
+                const int cl = pq % nc, d = pq / nc, col = c0 + cl;
+                const int hh = col / K1, j = col % K1;
+                const size_t oi = ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + d;
+                static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(acc[u]);
             }
-            M = Mn;
         }
-        const int hh = col / K1, j = col % K1;
-        const size_t oi = ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + d;
-        static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(A / Ls);
     }
 }
 
@@ -499,7 +540,7 @@ void decode_bf16_kernel(AttnParams p) {
         }
     }
     if (arrive_last(p.merge_cnt + static_cast<size_t>(b) * p.Hkv + g, qb, &S.flag))
-        dec_merge<D>(p, b, g, first_slot + g, qb);
+        dec_merge<D>(p, S.mrg, b, g, first_slot + g, qb);
 }
 
 template <int D>
