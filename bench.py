@@ -11,7 +11,8 @@ Infinity Cache cannot serve a step from the previous use of its inputs.  The
 timed steps are captured into one HIP graph (the per-step host work of the
 ctypes binding would otherwise exceed the GPU time); the timed region is one
 replay between two device synchronisations.  The dominant kernel's duration is
-then measured with HIP events around it over the same rotation of sets.
+then measured with HIP events stamped by its own dispatch, over the same
+rotation of sets.
 
 Compaction appends each set's accepted KV rows, so a set's KV grows by its
 emitted tokens on every use, as in real decoding; the byte counts follow the
@@ -48,6 +49,9 @@ def parse():
                     help="HBM counter summary of the dominant kernel (default: profiles/)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--traffic-from", default=None,
+                    help="only summarise counter passes under this directory (fetch/, write/, "
+                         "calib_fetch/, calib_write/) into profiles/traffic_<config>.json")
     return ap.parse_args()
 
 
@@ -80,14 +84,56 @@ def kernel_source_hash():
 
 
 def copy_calibration(mib):
+    """A plain elementwise copy kernel of `mib` MiB (reads and writes n bytes once)."""
     import torch
     n = mib * (1 << 20)
     src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(5):
-        dst.copy_(src)
+        torch.add(src, 0, out=dst)  # a kernel, unlike copy_, which may become a DMA copy
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def _counter_rows(d, counter):
+    """(kernel name, dispatch id, value) summed over counter instances, from the
+    rocprofv3 csv files under directory d."""
+    import csv
+    import glob
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return [(k[0], k[1], v) for k, v in per.items()]
+
+
+def traffic_summary(d, config, mib):
+    """HBM bytes per launch of the verify-attention kernel from two counter
+    passes (FETCH_SIZE and WRITE_SIZE, KiB per dispatch) over this script, each
+    scaled by what the same counter reads for the plain copy of `mib` MiB."""
+    n = mib * (1 << 20)
+    out = {"config": config, "attn_source_sha256_16": kernel_source_hash(), "copy_bytes": n}
+    total = 0.0
+    for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        calib = [v for k, _, v in _counter_rows(os.path.join(d, "calib_" + sub), counter)
+                 if "add" in k.lower() and "random" not in k.lower()]
+        kern = [v for k, _, v in _counter_rows(os.path.join(d, sub), counter)
+                if "decode_bf16_kernel" in k]
+        if not calib or not kern:
+            raise SystemExit(f"no {counter} rows for the copy or the attention kernel under {d}")
+        c_kib = sum(calib) / len(calib)
+        factor = n / (c_kib * 1024.0)
+        k_kib = sum(kern) / len(kern)
+        out[counter] = {"copy_kib_per_dispatch": round(c_kib, 1), "scale": round(factor, 5),
+                        "attn_kib_per_dispatch": round(k_kib, 1), "attn_dispatches": len(kern),
+                        "attn_bytes_per_launch": int(k_kib * 1024.0 * factor)}
+        total += k_kib * 1024.0 * factor
+    out["traffic_bytes_per_launch"] = int(total)
+    return out
 
 
 def main():
@@ -96,6 +142,13 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the verify step is "
               "built and measured on a single MI355X.", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        tr = traffic_summary(args.traffic_from, args.config, args.copy_calib_mib or 1024)
+        with open(os.path.join(ROOT, "profiles", f"traffic_{args.config}.json"), "w") as f:
+            json.dump(tr, f, indent=1)
+            f.write("\n")
+        print(json.dumps(tr), flush=True)
+        return
     if args.copy_calib_mib:
         copy_calibration(args.copy_calib_mib)
         return
@@ -189,10 +242,10 @@ def main():
     ms_total = t_start.elapsed_time(t_stop)
     timed_sets = [(warmup + i) % S for i in range(steps)]
 
-    # Dominant kernel: the split-K chunk kernel of spec_verify_attn, bracketed by
-    # HIP events recorded on its stream by the library (events cannot be graph
-    # nodes here, so this loop launches eagerly, over the same rotation of sets
-    # and the KV lengths the timed steps left behind).
+    # Dominant kernel: the split-K chunk kernel of spec_verify_attn, timed with
+    # HIP events that its own dispatch stamps at kernel start and end (eager
+    # launches, over the same rotation of sets and the KV lengths the timed
+    # steps left behind).
     hip = Hip()
     evs = [(hip.event(), hip.event()) for _ in range(steps)]
     kern_bytes = []

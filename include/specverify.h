@@ -193,13 +193,14 @@ int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_
 /* ------------------------------------------------------------------------
  * sv_set_kernel_events -- timing instrumentation for the dominant kernel.
  *
- * When `start` and `stop` (hipEvent_t handles created by the caller) are both
- * non-NULL, every later spec_verify_attn call on the calling thread records
- * `start` on its stream immediately before its per-sequence split-K chunk
- * kernel and `stop` immediately after it (also while the stream is being
- * captured into a graph, where the records become graph nodes).  Passing NULL
- * for either turns the recording off.  The events stay owned by the caller.
- * Returns SV_OK.
+ * When `start` and `stop` (hipEvent_t handles created by the caller, with
+ * timing enabled) are both non-NULL, every later spec_verify_attn call on the
+ * calling thread launches its per-sequence split-K chunk kernel (bf16 KV; the
+ * fp32 path's partial kernel) so that the dispatch itself stamps `start` when
+ * the kernel begins and `stop` when it ends: hipEventElapsedTime of the pair is
+ * that one kernel's duration.  Meant for eager launches; do not leave it on
+ * while a stream is captured into a graph.  Passing NULL for either turns it
+ * off.  The events stay owned by the caller.  Returns SV_OK.
  * ------------------------------------------------------------------------ */
 int sv_set_kernel_events(void* start, void* stop);
 

@@ -33,6 +33,8 @@
 
 #include <algorithm>
 
+#include <hip/hip_ext.h>
+
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -838,7 +840,10 @@ int sk_resident_grid(int D, int nct) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess) per_cu = 0;
     (void)hipGetLastError();
     if (cus <= 0 || per_cu <= 0) return 1024;
-    const int wpc = env_int("SPECVERIFY_SK_WGS_PER_CU", 0);
+    // Three resident workgroups per CU keep enough loads in flight to saturate
+    // HBM; more of them only lengthen the queue that the first slice of each
+    // workgroup waits in, and the last of them finish later.
+    const int wpc = env_int("SPECVERIFY_SK_WGS_PER_CU", 3);
     if (wpc > 0 && wpc < per_cu) per_cu = wpc;
     c = cus * per_cu;
     return c;
@@ -1004,11 +1009,16 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
         }
         const int nct = (p.CPG + 15) / 16;
         dim3 grid(pl.grid);
-        if (a.ev_start) {
-            hipError_t e = hipEventRecord(a.ev_start, stream);
-            if (e != hipSuccess) return e;
-        }
-#define SV_DECODE(DD, NN) hipLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream, p)
+        // With timing events, the dispatch itself stamps them at the kernel's
+        // start and end (the same timestamps a kernel trace reports).
+#define SV_DECODE(DD, NN)                                                                          \
+    do {                                                                                           \
+        if (a.ev_start && a.ev_stop)                                                               \
+            hipExtLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream,  \
+                                  a.ev_start, a.ev_stop, 0, p);                                    \
+        else                                                                                       \
+            hipLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream, p);  \
+    } while (0)
         if (a.D == 128) {
             switch (nct) {
                 case 1: SV_DECODE(128, 1); break;
@@ -1032,18 +1042,15 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        if (a.ev_start) {
-            hipError_t e = hipEventRecord(a.ev_start, stream);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(attn_f32_kernel, dim3(pl.slots, a.Hkv), dim3(kThreads), 0, stream, p, 0);
+        if (a.ev_start && a.ev_stop)
+            hipExtLaunchKernelGGL(attn_f32_kernel, dim3(pl.slots, a.Hkv), dim3(kThreads), 0, stream,
+                                  a.ev_start, a.ev_stop, 0, p, 0);
+        else
+            hipLaunchKernelGGL(attn_f32_kernel, dim3(pl.slots, a.Hkv), dim3(kThreads), 0, stream, p,
+                               0);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.ev_stop) {
-        e = hipEventRecord(a.ev_stop, stream);
-        if (e != hipSuccess) return e;
-    }
     if (a.bf16) return hipSuccess;  // the chunk kernel merges in its last workgroup
     const int mthreads = a.D <= 64 ? 64 : (a.D <= 128 ? 128 : 256);
     hipLaunchKernelGGL(merge_kernel, dim3(a.B * (a.K + 1) * a.Hq), dim3(mthreads), 0, stream, p);

@@ -176,6 +176,38 @@ def test_attention_custom_scale_and_determinism():
     assert attn_errors(o1, ref).max() <= 1e-2
 
 
+@pytest.mark.parametrize("name", ["bf16_gqa_k8", "fp32_d64_prefix"])
+def test_attention_timing_events(name):
+    """With dispatch-stamped timing events on, the result is unchanged and the
+    events measure a positive duration."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    cfg = SMALL_ATTN[name]
+    w = W.make_workload(cfg, sub_seed=5)
+    t = to_device(w, DEV)
+    o1 = run_attn(w, t)
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    try:
+        api.sv_set_kernel_events(ev[0].value, ev[1].value)
+        try:
+            o2 = run_attn(w, t)
+        finally:
+            api.sv_set_kernel_events(None, None)
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+        assert 0.0 < ms.value < 1000.0
+    finally:
+        for e in ev:
+            hip.hipEventDestroy(e)
+    assert np.array_equal(o1, o2)
+
+
 def test_attention_bifurcated_equals_concatenated_gpu():
     """Prefix read once == the same prefix copied into every sequence's cache."""
     cfg = SMALL_ATTN["bf16_prefix"]
