@@ -41,7 +41,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerThread = 16;
 constexpr int kSeg = kThreads * kPerThread;  // 4096 logits per segment
-constexpr int kBins = 128;                   // quarter-unit bins of z/T below the segment max
+constexpr int kBins = 128;                   // quarter-unit bins of z/T below the row max
+constexpr int kCutBins = 64;                 // bins below the segment max a list may span
 constexpr int kList = kThreads;              // candidate list capacity per segment
 constexpr int kCap = 1024;                   // boundary-bin entries ranked in LDS
 constexpr int kMaxSeg = 64;                  // V <= 64 * 4096
@@ -83,9 +84,9 @@ struct AcceptParams {
     int32_t* out_tokens;
     int32_t* status;
     SegHead* seg;
-    double* hmass;             // [nrows][nseg][kBins]: fp64 mass of bin kb_top - o
     unsigned long long* list;  // [nrows][nseg][kList]: (id << 32) | bits of z, ids ascending
     RowRec* rows;
+    float* zx;                 // [nrows]: logit of the row's drafted token (segment that holds it)
     SeqRec* seqs;
     double* dsum;
     double* qsum;
@@ -179,11 +180,9 @@ struct RowsLds {
     float red_f[kThreads / 64];
     int flag;
     union alignas(16) {
-        struct {              // segment: per-wave histograms of bins kb_top - o
-            int hc[4][kBins];
-            double hm[4][kBins];
-            int cum[kBins];
-            int fit[2];
+        struct {              // segment: per-wave counts of bins kb_top - o
+            int hc[4][kCutBins];
+            int fit;
             unsigned long long wtot[kThreads / 64];
         } seg;
         struct {              // row merge: boundary-bin entries
@@ -230,6 +229,7 @@ struct RowsLds {
     uint32_t prefix, mask;
     int chosen;
     int n, tok, lastpos;
+    float us;                 // u_sample of the sequence
 };
 
 // Exact tie-closed nucleus threshold by radix select over the whole row
@@ -333,44 +333,33 @@ __device__ __forceinline__ void block_excl_scan2(double a, double b, double* sa,
 
 // ---------------------------------------------------------------- segment
 
-// Histograms (count, fp64 mass) over bins kb_top - o, o in [0, kBins), and
-// the candidate list: all elements of the highest bins that fit in kList
-// entries, in id order; then the segment head.
+// Counts of bins kb_top - o, o in [0, kCutBins), and the candidate list: all
+// elements of the highest bins that fit in kList entries, in id order; then
+// the segment head.  The row merge takes bin masses from the lists.
 __device__ __forceinline__ void segment_list(const AcceptParams& p, int r, int s, const float* z,
-                                             const double* w, float ms, double Ss, RowsLds& L) {
+                                             float ms, double Ss, RowsLds& L) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int kb_top = bin_of(ms, p.bscale);
-    for (int i = tid; i < 4 * kBins; i += kThreads) {
-        (&L.seg.hc[0][0])[i] = 0;
-        (&L.seg.hm[0][0])[i] = 0.0;
-    }
+    static_assert(4 * kCutBins == kThreads, "one counter per thread");
+    (&L.seg.hc[0][0])[tid] = 0;
     __syncthreads();
     int o[kPerThread];
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
-        o[k] = (z[k] == -INFINITY) ? kBins : kb_top - bin_of(z[k], p.bscale);
-        if (o[k] < kBins) {
-            atomicAdd(&L.seg.hc[wv][o[k]], 1);
-            atomicAdd(&L.seg.hm[wv][o[k]], w[k]);
-        }
+        o[k] = (z[k] == -INFINITY) ? kCutBins : kb_top - bin_of(z[k], p.bscale);
+        if (o[k] < kCutBins) atomicAdd(&L.seg.hc[wv][o[k]], 1);
     }
     __syncthreads();
-    if (tid < kBins) {
+    if (tid < kCutBins) {
+        // cumulative counts from the top bin down; bins 0 .. fit-1 fit in the list
         const int c = (L.seg.hc[0][tid] + L.seg.hc[1][tid]) + (L.seg.hc[2][tid] + L.seg.hc[3][tid]);
-        const double hmv = (L.seg.hm[0][tid] + L.seg.hm[1][tid]) + (L.seg.hm[2][tid] + L.seg.hm[3][tid]);
-        st_coh(p.hmass + (static_cast<size_t>(r) * p.nseg + s) * kBins + tid, hmv);
-        // cumulative counts from the top bin down (waves 0 and 1: bins 0..127)
-        L.seg.cum[tid] = wave_incl_scan(c, lane);
-    }
-    __syncthreads();
-    if (tid < kBins) {
-        const int cum = L.seg.cum[tid] + (wv == 1 ? L.seg.cum[63] : 0);
+        const int cum = wave_incl_scan(c, lane);
         const unsigned long long bal = __ballot(cum <= kList);
-        if (lane == 0) L.seg.fit[wv] = __popcll(bal);
+        if (lane == 0) L.seg.fit = __popcll(bal);
     }
     __syncthreads();
     // bins 0 .. ocut fit (cum is nondecreasing); -1: the top bin alone overflows
-    const int ocut = L.seg.fit[0] + L.seg.fit[1] - 1;
+    const int ocut = L.seg.fit - 1;
     // positions in id order: group g = k/4 holds ids s*4096 + g*1024 + 4*tid + k%4
     unsigned long long packed = 0;
 #pragma unroll
@@ -561,9 +550,8 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, RowsL
         j = (r - nt) % p.K;
     }
 
-    // one round trip: segment heads, histograms (thread t: bins 8*(t%16) .. +7
-    // of segment t/16), the first kChunk segments' list slot tid, and the
-    // drafted logit
+    // one round trip: segment heads, the first kChunk segments' list slot
+    // tid, and the drafted logit
     if (tid < p.nseg) {
         L.seg_m[tid] = ld_coh(&sr[tid].m);
         L.seg_kb[tid] = ld_coh(&sr[tid].kb_top);
@@ -572,23 +560,18 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, RowsL
         L.seg_S[tid] = ld_coh(&sr[tid].S);
     }
     const bool nuc = p.nucleus != 0;
-    double hv[8];
-    const int hs = tid >> 4, ho = (tid & 15) * 8;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-        hv[u] = (nuc && hs < p.nseg)
-                    ? ld_coh(p.hmass + (static_cast<size_t>(r) * p.nseg + hs) * kBins + ho + u)
-                    : 0.0;
     unsigned long long e[kChunk];
     const unsigned long long* lb = p.list + static_cast<size_t>(r) * p.nseg * kList;
 #pragma unroll
     for (int c = 0; c < kChunk; ++c)
         e[c] = (nuc && c < p.nseg) ? ld_coh(lb + static_cast<size_t>(c) * kList + tid) : 0ull;
     if (tid == kThreads - 1) {
-        int x = -1;
-        if (j >= 0) x = p.draft_tokens[b * p.K + j];
+        // independent loads: the drafted token, and its logit as stored by the
+        // segment holding it (meaningful only for a valid token)
+        const int x = (j >= 0) ? p.draft_tokens[b * p.K + j] : -1;
+        const float zv = ld_coh(p.zx + r);
         L.n = x;
-        L.zx = (j >= 0 && x >= 0 && x < p.V && !p.greedy) ? load1(row, p.bf16, x) : 0.0f;
+        L.zx = (j >= 0 && x >= 0 && x < p.V && !p.greedy) ? zv : 0.0f;
     }
     __syncthreads();
     if (tid < 64) {
@@ -638,14 +621,18 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, RowsL
             if (tid == 0) L.S = S;
         }
         __syncthreads();
-        if (nuc && hs < p.nseg) {
-            // segment bin o is row bin og = o + (kb_top - kb_top_s)
-            const int sh = L.kb_top - L.seg_kb[hs];
-            const double scs = L.sc[hs];
+        if (nuc && p.nseg <= kChunk) {
+            // bin masses of the listed entries, relative to the row max: exact
+            // for every bin at or above kb_lo, which all lists hold in full
+            const int kb_top = L.kb_top;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int og = ho + u + sh;
-                if (og < kBins && hv[u] != 0.0) atomicAdd(&L.hm[og], hv[u] * scs);
+            for (int c = 0; c < kChunk; ++c) {
+                const float zc = entry_z(e[c]);
+                const int o = kb_top - bin_of(zc, p.bscale);
+                const bool in = static_cast<int>(c < p.nseg) &
+                                static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
+                                static_cast<int>(o < kBins);
+                if (in) atomicAdd(&L.hm[o], weight(zc, m, p.invT, L.tab));
             }
         }
         __syncthreads();
@@ -725,7 +712,7 @@ __device__ __forceinline__ int draw_runs(const AcceptParams& p, int b, bool resi
     const double qx = block_excl_scan(qs, L.sq.scan, &qt);
     const bool useq = residual && !(dt > 0.0);
     const double tot = useq ? qt : dt;
-    const float u = p.u_sample[b];
+    const float u = L.us;
     if (tid == 0 && !(u >= 0.0f && u < 1.0f)) set_status(p.status, 2);
     const double target = static_cast<double>(u) * tot;
     const double run0 = useq ? qx : dx;
@@ -822,7 +809,7 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
     block_excl_scan2(ds, qs, L.sq.scan, L.sq.scan2, &dx, &qx, &dt, &qt);
     const bool useq = residual && !(dt > 0.0);  // zero residual mass: fall back to q'
     const double tot = useq ? qt : dt;
-    const float u = p.u_sample[b];
+    const float u = L.us;
     if (tid == 0 && !(u >= 0.0f && u < 1.0f)) set_status(p.status, 2);
     const double target = static_cast<double>(u) * tot;
     const double run0 = useq ? qx : dx;
@@ -926,6 +913,7 @@ __device__ __forceinline__ void finalize_sequence(const AcceptParams& p, int b, 
         L.sq.x[tid - 128] = p.draft_tokens[b * K + tid - 128];
         L.sq.ua[tid - 128] = p.greedy ? 0.0f : p.u_accept[b * K + tid - 128];
     }
+    if (tid == kThreads - 1) L.us = p.greedy ? 0.0f : p.u_sample[b];
     __syncthreads();
     if (tid < 64) {
         // every position's test at once (lane jj); n = first rejection
@@ -974,9 +962,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (r >= p.nrows) return;
     const void* row = row_ptr(p, r);
 
+    // drafted token of this row (target row j < K, or draft row j): loaded
+    // with the logits; the segment holding it stores its logit for the merge
+    const int nt = p.B * (p.K + 1);
+    const int jr = (r < nt) ? r % (p.K + 1) : (r - nt) % p.K;
+    const bool has_x = (!p.greedy) & ((r >= nt) | (jr < p.K));
+    const int br = (r < nt) ? r / (p.K + 1) : (r - nt) / p.K;
+    const int xr = has_x ? p.draft_tokens[br * p.K + jr] : -1;
+
     float z[kPerThread];
     load_segment(row, p.bf16, p.vec, p.V, s, tid, z);
     fill_exp_table(L.tab);
+    if ((xr >= s * kSeg) & (xr < (s + 1) * kSeg) & (xr < p.V)) {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k)
+            if (seg_index(s, tid, k) == xr) st_coh(p.zx + r, z[k]);
+    }
     __syncthreads();
 
     if (p.greedy) {
@@ -1014,16 +1015,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k) lm = fmaxf(lm, z[k]);
         const float ms = block_max<kThreads>(lm, L.red_f);
-        double w[kPerThread];
         double acc = 0.0;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
-            w[k] = (ms == -INFINITY) ? 0.0 : weight(z[k], ms, p.invT, L.tab);
-            acc += w[k];
-        }
+        for (int k = 0; k < kPerThread; ++k)
+            acc += (ms == -INFINITY) ? 0.0 : weight(z[k], ms, p.invT, L.tab);
         const double Ss = block_sum<kThreads>(acc, L.red_d);
         if (p.nucleus) {
-            segment_list(p, r, s, z, w, ms, Ss, L);
+            segment_list(p, r, s, z, ms, Ss, L);
         } else if (tid == 0) {
             SegHead* dst = p.seg + static_cast<size_t>(r) * p.nseg + s;
             st_coh(&dst->m, ms);
@@ -1035,8 +1033,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (!arrive_last(p.row_cnt + r, p.nseg, &L.flag)) return;
     finalize_row(p, r, L);
 
-    const int nt = p.B * (p.K + 1);
-    const int b = (r < nt) ? r / (p.K + 1) : (r - nt) / p.K;
+    const int b = br;
     const int rows_per_seq = p.greedy ? p.K + 1 : 2 * p.K + 1;
     if (!arrive_last(p.seq_cnt + b, rows_per_seq, &L.flag)) return;
     finalize_sequence(p, b, L);
@@ -1228,9 +1225,9 @@ size_t accept_workspace_bytes(int B, int K, int V) {
     size_t off = 0;
     auto take = [&](size_t bytes) { off = (off + 255) & ~static_cast<size_t>(255); off += bytes; };
     take(nrows * nseg * sizeof(SegHead));
-    take(nrows * nseg * kBins * sizeof(double));
     take(nrows * nseg * kList * sizeof(unsigned long long));
     take(nrows * sizeof(RowRec));
+    take(nrows * sizeof(float));
     take(static_cast<size_t>(B) * sizeof(SeqRec));
     take(static_cast<size_t>(B) * nseg * sizeof(double));
     take(static_cast<size_t>(B) * nseg * sizeof(double));
@@ -1278,9 +1275,9 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
         return ptr;
     };
     p.seg = reinterpret_cast<SegHead*>(take(nrows_max * nseg * sizeof(SegHead)));
-    p.hmass = reinterpret_cast<double*>(take(nrows_max * nseg * kBins * sizeof(double)));
     p.list = reinterpret_cast<unsigned long long*>(take(nrows_max * nseg * kList * sizeof(unsigned long long)));
     p.rows = reinterpret_cast<RowRec*>(take(nrows_max * sizeof(RowRec)));
+    p.zx = reinterpret_cast<float*>(take(nrows_max * sizeof(float)));
     p.seqs = reinterpret_cast<SeqRec*>(take(static_cast<size_t>(a.B) * sizeof(SeqRec)));
     p.dsum = reinterpret_cast<double*>(take(static_cast<size_t>(a.B) * nseg * sizeof(double)));
     p.qsum = reinterpret_cast<double*>(take(static_cast<size_t>(a.B) * nseg * sizeof(double)));
