@@ -623,16 +623,28 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, RowsL
         __syncthreads();
         if (nuc && p.nseg <= kChunk) {
             // bin masses of the listed entries, relative to the row max: exact
-            // for every bin at or above kb_lo, which all lists hold in full
+            // for every bin at or above kb_lo, which all lists hold in full.
+            // Weights of a batch are computed unconditionally (independent
+            // chains; unused slots are masked), then added.
             const int kb_top = L.kb_top;
 #pragma unroll
-            for (int c = 0; c < kChunk; ++c) {
-                const float zc = entry_z(e[c]);
-                const int o = kb_top - bin_of(zc, p.bscale);
-                const bool in = static_cast<int>(c < p.nseg) &
-                                static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
-                                static_cast<int>(o < kBins);
-                if (in) atomicAdd(&L.hm[o], weight(zc, m, p.invT, L.tab));
+            for (int c0 = 0; c0 < kChunk; c0 += 8) {
+                double wv[8];
+                int ov[8];
+                bool in[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int c = c0 + u;
+                    const float zc = entry_z(e[c]);
+                    ov[u] = kb_top - bin_of(zc, p.bscale);
+                    in[u] = static_cast<int>(c < p.nseg) &
+                            static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
+                            static_cast<int>(ov[u] < kBins);
+                    wv[u] = weight(zc, m, p.invT, L.tab);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (in[u]) atomicAdd(&L.hm[ov[u]], wv[u]);
             }
         }
         __syncthreads();
@@ -681,20 +693,21 @@ __device__ __forceinline__ DrawRows draw_rows(const RowRec& rq, const RowRec& rp
 
 // Draw weights of one element of the stopping row: residual (q'-p')_+ and q'.
 // Branch-free: the weights are computed unconditionally and selected.
+// Draw weights of one element, each up to a positive factor common to the
+// whole row (the inverse-CDF draw is invariant to it): q' ~ w_q, and the
+// residual (q' - p')_+ = (w_q/S_q - w_p/S_p)_+ ~ (w_q*S_p - w_p*S_q)_+.
+// Both exps are computed unconditionally, so the calls of an unrolled loop
+// are independent chains.
 __device__ __forceinline__ void pair_weights(const DrawRows& R, bool residual, float zq, float zpv,
                                              bool valid, double invT, const double* tab, double* d,
                                              double* q) {
-    const double wq = weight(zq, R.mq, invT, tab) / R.Sq;  // as the oracle: w / S
+    const double wq = weight(zq, R.mq, invT, tab);
+    const double wp = weight(zpv, R.mp, invT, tab);
     const double qv = (valid & (zq >= R.tq)) ? wq : 0.0;
+    const double pv = (valid & residual & (zpv >= R.tp)) ? wp : 0.0;
     *q = qv;
-    if (residual) {
-        const double wp = weight(zpv, R.mp, invT, tab) / R.Sp;
-        const double pv = (valid & (zpv >= R.tp)) ? wp : 0.0;
-        const double dd = qv - pv;
-        *d = dd > 0.0 ? dd : 0.0;
-    } else {
-        *d = qv;
-    }
+    const double dd = fma(qv, R.Sp, -(pv * R.Sq));
+    *d = residual ? (dd > 0.0 ? dd : 0.0) : qv;
 }
 
 // The draw over per-thread runs of elements in id order (thread t's run
@@ -798,9 +811,10 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
     double ds = 0.0, qs = 0.0;
 #pragma unroll
     for (int i = 0; i < kNuc / kThreads; ++i) {
-        double d = 0.0, q = 0.0;
-        if ((i < E) & (m0 + i < M))
-            pair_weights(R, residual, L.sq.mz[m0 + i], zpv[i], true, p.invT, L.tab, &d, &q);
+        const bool ok = (i < E) & (m0 + i < M);
+        const float zq = L.sq.mz[min(m0 + i, kNuc - 1)];
+        double d, q;
+        pair_weights(R, residual, zq, zpv[i], ok, p.invT, L.tab, &d, &q);
         ds += d;
         qs += q;
     }
