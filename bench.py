@@ -49,6 +49,9 @@ def parse():
                     help="HBM counter summary of the dominant kernel (default: profiles/)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--k-sweep", default=None,
+                    help="comma-separated draft lengths: time the step and each entry point "
+                         "per K on the workload's shape (one JSON line per K)")
     ap.add_argument("--traffic-from", default=None,
                     help="only summarise counter passes under this directory (fetch/, write/, "
                          "calib_fetch/, calib_write/) into profiles/traffic_<config>.json")
@@ -151,6 +154,9 @@ def main():
         return
     if args.copy_calib_mib:
         copy_calibration(args.copy_calib_mib)
+        return
+    if args.k_sweep:
+        k_sweep(args, [int(k) for k in args.k_sweep.split(",")])
         return
 
     import numpy as np
@@ -342,6 +348,101 @@ def main():
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(sets, cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def k_sweep(args, ks):
+    """Verify cost against the draft length K on one workload shape (K = 0 is
+    plain decode: one query per sequence, the bonus draw only).  Per K: the
+    whole step (graph of `steps` steps), each entry point alone (graph of
+    `steps` calls), and the emitted tokens."""
+    import numpy as np
+    import torch
+
+    from speculative_decoding_verify_04_amd import api
+    from speculative_decoding_verify_04_amd import workloads as W
+    from speculative_decoding_verify_04_amd.devio import to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    base = W.CONFIGS[args.config]
+    steps, S = args.steps, min(args.sets, 4)
+    cap_stream = torch.cuda.Stream()
+
+    def timed(fns):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / len(fns)  # us per call
+
+    for K in ks:
+        cfg = W.small_variant(base, K=K)
+        B = cfg.B
+        # every set is used 4 * ceil(steps / S) times by the two graphs that compact
+        growth = (K + 1) * (4 * math.ceil(steps / S) + 2)
+        sets = [W.make_workload(cfg, sub_seed=s, growth_rows=growth) for s in range(S)]
+        dsets = [to_device(w, dev) for w in sets]
+        bounds = [[int(x) + growth for x in w.kv_len] for w in sets]
+        dt = api.SV_BF16 if cfg.kv_dtype == W.BF16 else api.SV_F32
+        wa = torch.zeros(max(api.spec_verify_attn_workspace_size(B, K, cfg.Hq, cfg.Hkv, cfg.D, dt,
+                                                                 bnd, cfg.prefix_len)
+                             for bnd in bounds), dtype=torch.uint8, device=dev)
+        wacc = torch.zeros(api.spec_accept_workspace_size(B, K, cfg.V), dtype=torch.uint8,
+                           device=dev)
+
+        def attn(s):
+            t = dsets[s]
+            api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, bounds[s],
+                                 t.k_new, t.v_new, t.out, K, k_prefix=t.k_prefix,
+                                 v_prefix=t.v_prefix, status=t.status, workspace=wa)
+
+        def accept(s):
+            t = dsets[s]
+            api.spec_accept(t.target_logits, None if cfg.greedy else t.draft_logits,
+                            t.draft_tokens, t.u_accept, t.u_sample, cfg.temperature, cfg.top_p,
+                            cfg.greedy, t.n_accepted, t.out_tokens, status=t.status,
+                            workspace=wacc)
+
+        def compact(s):
+            t = dsets[s]
+            api.spec_compact_kv(t.n_accepted, t.out_tokens, t.kv_len, t.kv_start, t.k_cache,
+                                t.v_cache, t.k_new, t.v_new, t.tokens_packed, t.cu_tokens,
+                                status=t.status)
+
+        emitted = []
+        for s in range(S):
+            accept(s)
+            torch.cuda.synchronize()
+            emitted.append(int((dsets[s].n_accepted.cpu().numpy() + 1).sum()))
+        step_us = timed([lambda s=i % S: (attn(s), accept(s), compact(s)) for i in range(steps)])
+        attn_us = timed([lambda s=i % S: attn(s) for i in range(steps)])
+        acc_us = timed([lambda s=i % S: accept(s) for i in range(steps)])
+        comp_us = timed([lambda s=i % S: compact(s) for i in range(steps)])
+        for s in range(S):
+            st = int(dsets[s].status.item())
+            assert st == 0, f"K={K} set {s}: device status {st} ({api.device_error_name(st)})"
+        tok = sum(emitted[i % S] for i in range(steps)) / steps
+        L = np.concatenate([w.kv_len for w in sets]).astype(np.int64)
+        attn_bytes = W.algorithmic_bytes(cfg, L, cfg.prefix_len)["attn"] / S
+        print(json.dumps({
+            "k_sweep": K, "config": cfg.name, "B": B, "steps": steps,
+            "us_per_step": round(step_us, 2), "attn_us": round(attn_us, 2),
+            "accept_us": round(acc_us, 2), "compact_us": round(comp_us, 2),
+            "emitted_per_step": round(tok, 3),
+            "emitted_per_scored_position": round(tok / (B * (K + 1)), 4),
+            "verified_tokens_per_s": round(tok / (step_us * 1e-6), 1),
+            "attn_GBs_at_start_lengths": round(attn_bytes / (attn_us * 1e-6) / 1e9, 1),
+        }), flush=True)
+        del dsets, wa, wacc
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(sets, cfg, budget_s):

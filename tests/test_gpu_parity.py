@@ -382,11 +382,15 @@ def test_accept_gpu_matches_oracle_many_trials(case):
 
 # ---------------------------------------------------------------- compaction
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "bass_b8k5"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "bass_b8k5", "bass_k0"])
 def test_compaction_matches_oracle(name):
-    cfg = W.CONFIGS[name]
-    if name != "tiny_fp32":
-        cfg = W.small_variant(cfg, B=8, Hq=4, Hkv=4, len_lo=5, len_hi=300, V=4096)
+    """Sampler then compaction against the oracle; bass_k0 is plain decode
+    (K = 0: the bonus token only, one appended row per sequence)."""
+    if name == "tiny_fp32":
+        cfg = W.CONFIGS[name]
+    else:
+        cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=8, Hq=4, Hkv=4, len_lo=5, len_hi=300,
+                              V=4096, K=0 if name == "bass_k0" else 5)
     w = W.make_workload(cfg, sub_seed=12)
     t = to_device(w, DEV)
     n, toks = run_accept(w, t)
