@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--k-sweep", default=None,
                     help="comma-separated draft lengths: time the step and each entry point "
                          "per K on the workload's shape (one JSON line per K)")
+    ap.add_argument("--ragged", action="store_true",
+                    help="time the step with ragged draft lengths K_b ~ U{0..K} (one JSON line)")
     ap.add_argument("--traffic-from", default=None,
                     help="only summarise counter passes under this directory (fetch/, write/, "
                          "calib_fetch/, calib_write/) into profiles/traffic_<config>.json")
@@ -157,6 +159,9 @@ def main():
         return
     if args.k_sweep:
         k_sweep(args, [int(k) for k in args.k_sweep.split(",")])
+        return
+    if args.ragged:
+        ragged_bench(args)
         return
 
     import numpy as np
@@ -264,6 +269,19 @@ def main():
                              status=t.status, workspace=wa)
     api.sv_set_kernel_events(None, None)
     torch.cuda.synchronize()
+
+    # The shared workspace served every set: each set's last attention output must
+    # equal a run on a fresh workspace (same inputs: bit-identical).
+    for s in range(S):
+        t = dsets[s]
+        prev = t.out.clone()
+        fresh = torch.zeros_like(wa)
+        api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, bounds[s], t.k_new,
+                             t.v_new, t.out, K, k_prefix=t.k_prefix, v_prefix=t.v_prefix,
+                             status=t.status, workspace=fresh)
+        torch.cuda.synchronize()
+        assert torch.equal(prev, t.out), f"set {s}: attention output differs on a fresh workspace"
+        del fresh
 
     # Check every set's last outputs against its reference (graph replays vs eager).
     for s in range(S):
@@ -443,6 +461,102 @@ def k_sweep(args, ks):
         }), flush=True)
         del dsets, wa, wacc
         torch.cuda.empty_cache()
+
+
+def ragged_bench(args):
+    """The step with ragged draft lengths (each sequence its own K_b ~ U{0..K},
+    rows packed without padding): whole step and each entry point, graph-timed
+    over rotating input sets; bytes from the realised lengths and row counts."""
+    import numpy as np
+    import torch
+
+    from speculative_decoding_verify_04_amd import api
+    from speculative_decoding_verify_04_amd import workloads as W
+    from speculative_decoding_verify_04_amd.devio import ragged_to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[args.config]
+    B, K = cfg.B, cfg.K
+    steps, S = args.steps, args.sets
+    growth = (K + 1) * (4 * math.ceil(steps / S) + 2)
+    rws = [W.make_ragged(W.make_workload(cfg, sub_seed=s, growth_rows=growth),
+                         W.ragged_draft_lengths(cfg, s)) for s in range(S)]
+    ts = [ragged_to_device(rw, dev) for rw in rws]
+    bounds = [[int(x) + growth for x in rw.base.kv_len] for rw in rws]
+    dt = api.SV_BF16 if cfg.kv_dtype == W.BF16 else api.SV_F32
+    wa = torch.zeros(max(api.spec_verify_attn_ragged_workspace_size(
+        B, cfg.Hq, cfg.Hkv, cfg.D, dt, bnd, rw.cu_q, cfg.prefix_len)
+        for bnd, rw in zip(bounds, rws)), dtype=torch.uint8, device=dev)
+    wacc = torch.zeros(max(api.spec_accept_ragged_workspace_size(B, rw.cu_q, cfg.V) for rw in rws),
+                       dtype=torch.uint8, device=dev)
+    cap_stream = torch.cuda.Stream()
+
+    def attn(s):
+        t = ts[s]
+        api.spec_verify_attn_ragged(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, bounds[s],
+                                    t.k_new, t.v_new, t.out, t.cu_q, t.cu_q_host,
+                                    k_prefix=t.k_prefix, v_prefix=t.v_prefix, status=t.status,
+                                    workspace=wa)
+
+    def accept(s):
+        t = ts[s]
+        api.spec_accept_ragged(t.target_logits, None if cfg.greedy else t.draft_logits,
+                               t.draft_tokens, t.u_accept, t.u_sample, t.cu_q, t.cu_q_host,
+                               cfg.temperature, cfg.top_p, cfg.greedy, t.n_accepted, t.out_tokens,
+                               status=t.status, workspace=wacc)
+
+    def compact(s):
+        t = ts[s]
+        api.spec_compact_kv_ragged(t.n_accepted, t.out_tokens, t.kv_len, t.kv_start, t.k_cache,
+                                   t.v_cache, t.k_new, t.v_new, t.tokens_packed, t.cu_tokens,
+                                   t.cu_q, status=t.status)
+
+    def timed(fns):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for fn in fns:
+                fn()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / len(fns)
+
+    emitted = []
+    for s in range(S):
+        accept(s)
+        torch.cuda.synchronize()
+        emitted.append(int((ts[s].n_accepted.cpu().numpy() + 1).sum()))
+    step_us = timed([lambda s=i % S: (attn(s), accept(s), compact(s)) for i in range(steps)])
+    attn_us = timed([lambda s=i % S: attn(s) for i in range(steps)])
+    acc_us = timed([lambda s=i % S: accept(s) for i in range(steps)])
+    comp_us = timed([lambda s=i % S: compact(s) for i in range(steps)])
+    for s in range(S):
+        st = int(ts[s].status.item())
+        assert st == 0, f"set {s}: device status {st} ({api.device_error_name(st)})"
+    es = 2 if cfg.kv_dtype == W.BF16 else 4
+    row_kv = cfg.Hkv * cfg.D * es * 2
+    tok = sum(emitted[i % S] for i in range(steps)) / steps
+    nt = np.mean([int(rw.cu_q[-1]) for rw in rws])
+    attn_b = np.mean([int(rw.base.kv_len.sum()) * row_kv + int(rw.cu_q[-1]) * row_kv
+                      + 2 * int(rw.cu_q[-1]) * cfg.Hq * cfg.D * es for rw in rws])
+    acc_b = np.mean([(2 * int(rw.cu_q[-1]) - B) * cfg.V * 4 for rw in rws])
+    print(json.dumps({
+        "ragged": True, "config": cfg.name, "B": B, "K_max": K, "steps": steps,
+        "K_b": [int(x) for x in rws[0].kb], "query_rows_avg": round(float(nt), 2),
+        "us_per_step": round(step_us, 2), "attn_us": round(attn_us, 2),
+        "accept_us": round(acc_us, 2), "compact_us": round(comp_us, 2),
+        "emitted_per_step": round(tok, 3),
+        "verified_tokens_per_s": round(tok / (step_us * 1e-6), 1),
+        "attn_GBs_at_start_lengths": round(attn_b / (attn_us * 1e-6) / 1e9, 1),
+        "step_hbm_frac_at_start_lengths": round((attn_b + acc_b) / (step_us * 1e-6) / 1e9
+                                                / HBM_PEAK_GBS, 4),
+    }), flush=True)
 
 
 def cpu_baseline(sets, cfg, budget_s):

@@ -36,9 +36,12 @@
  *     store the first data error they meet there (SV_DEV_*), never abort.
  *   - `workspace` is caller-owned device memory of at least the size the
  *     matching *_workspace_size call reports.  It must be zero-filled once
- *     before its first use; every call leaves it ready for the next call.
- *     One workspace serves one call at a time (calls on different streams
- *     need different workspaces).
+ *     before its first use; every call leaves it ready for the next call
+ *     with the same B (and, for attention, the same Hkv) -- other lengths,
+ *     draft counts and vocabularies may change from call to call if the
+ *     workspace is large enough for each.  Zero it again before a call with
+ *     another B or Hkv.  One workspace serves one call at a time (calls on
+ *     different streams need different workspaces).
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -189,6 +192,59 @@ int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_
                     const void* k_new, const void* v_new, int32_t* tokens_packed,
                     int32_t* cu_tokens, int B, int K, int Hkv, int D, int dtype,
                     int32_t* status, sv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Ragged draft lengths -- every sequence with its own K_b.
+ *
+ * [EMS]: samples may carry different numbers of prediction tokens, handled
+ * without padding.  The same three operations, with the K_b + 1 query rows of
+ * sequence b packed back to back:
+ *   cu_q       [B+1] int32 device: cu_q[0] = 0, sequence b owns query rows
+ *              cu_q[b] .. cu_q[b+1]-1, so K_b = cu_q[b+1] - cu_q[b] - 1 >= 0
+ *   cu_q_host  [B+1] int32, HOST: the same offsets (they size the grid and the
+ *              workspace and bound K_b); the device copy must hold equal values
+ * and every "b*(K+1) + j" row of the uniform calls above becomes cu_q[b] + j:
+ *   attention  q, out, k_new, v_new [cu_q[B], ...]; query j <= K_b of sequence
+ *              b sees its cache and new rows cu_q[b] .. cu_q[b]+j.  The limits
+ *              of spec_verify_attn hold with K = max K_b.
+ *   sampler    target_logits [cu_q[B], V] (row cu_q[b] + j is target row j of
+ *              b), draft_logits [cu_q[B] - B, V], draft_tokens and u_accept
+ *              [cu_q[B] - B] (sequence b's K_b entries start at cu_q[b] - b),
+ *              u_sample [B], n_accepted [B] (n_b in [0, K_b]), out_tokens
+ *              [cu_q[B]] (sequence b's K_b + 1 entries start at cu_q[b]).
+ *              K_b <= 64.
+ *   compaction new rows cu_q[b] .. cu_q[b] + n_b are appended; out_tokens as
+ *              from spec_accept_ragged; tokens_packed [cu_q[B]];
+ *              SV_DEV_BAD_COUNT if n_accepted[b] is not in [0, K_b].
+ * With cu_q[b] = b*(K+1) every result equals that of the uniform call.
+ * ------------------------------------------------------------------------ */
+int spec_verify_attn_ragged_workspace_size(int B, int Hq, int Hkv, int D, int dtype,
+                                           const int32_t* kv_len_host, const int32_t* cu_q_host,
+                                           int prefix_len, size_t* bytes);
+
+int spec_verify_attn_ragged(const void* q, const void* k_cache, const void* v_cache,
+                            const int64_t* kv_start, const int32_t* kv_len,
+                            const int32_t* kv_len_host, const void* k_new, const void* v_new,
+                            const void* k_prefix, const void* v_prefix, int prefix_len,
+                            void* out, const int32_t* cu_q, const int32_t* cu_q_host, int B,
+                            int Hq, int Hkv, int D, int dtype, float softmax_scale,
+                            int32_t* status, void* workspace, size_t workspace_bytes,
+                            sv_stream_t stream);
+
+int spec_accept_ragged_workspace_size(int B, const int32_t* cu_q_host, int V, size_t* bytes);
+
+int spec_accept_ragged(const void* target_logits, const void* draft_logits, int logits_dtype,
+                       const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                       const int32_t* cu_q, const int32_t* cu_q_host, int B, int V,
+                       float temperature, float top_p, int greedy, int32_t* n_accepted,
+                       int32_t* out_tokens, int32_t* status, void* workspace,
+                       size_t workspace_bytes, sv_stream_t stream);
+
+int spec_compact_kv_ragged(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
+                           const int64_t* kv_start, void* k_cache, void* v_cache,
+                           const void* k_new, const void* v_new, int32_t* tokens_packed,
+                           int32_t* cu_tokens, const int32_t* cu_q, int B, int Hkv, int D,
+                           int dtype, int32_t* status, sv_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * sv_set_kernel_events -- timing instrumentation for the dominant kernel.

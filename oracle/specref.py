@@ -142,6 +142,88 @@ def compact_kv(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, k_new
     return packed, cu, kl, kc, vc
 
 
+# ---------------------------------------------------------------- ragged draft lengths
+#
+# "EMS-SD: Efficient Multi-sample Speculative Decoding" (abstract): samples may
+# carry different numbers of prediction tokens, without padding.  Sequences
+# are independent in every operation, so sequence b of a ragged call is the
+# uniform problem with one sequence and K = K_b on its own packed rows
+# cu_q[b] .. cu_q[b+1]-1; these wrappers apply the uniform oracle that way.
+
+def verify_attn_ragged(q, k_cache, v_cache, kv_start, kv_len, k_new, v_new, cu_q, Hq, Hkv, D,
+                       k_prefix=None, v_prefix=None, scale=0.0, lib_=None):
+    """fp64 attention with K_b + 1 queries in sequence b; returns [cu_q[B], Hq, D]."""
+    cu = np.asarray(cu_q, dtype=np.int64)
+    B = cu.shape[0] - 1
+    out = np.zeros((int(cu[B]), Hq, D), dtype=np.float64)
+    for b in range(B):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        out[r0:r1] = verify_attn(q[r0:r1], k_cache, v_cache, np.asarray(kv_start)[b:b + 1],
+                                 np.asarray(kv_len)[b:b + 1], k_new[r0:r1], v_new[r0:r1], 1,
+                                 r1 - r0 - 1, Hq, Hkv, D, k_prefix=k_prefix, v_prefix=v_prefix,
+                                 scale=scale, lib_=lib_)
+    return out
+
+
+def accept_ragged(target_logits, draft_logits, draft_tokens, u_accept, u_sample, cu_q,
+                  temperature, top_p, greedy=False, lib_=None):
+    """Modified rejection sampling with K_b drafts in sequence b.  Target rows of b
+    are cu_q[b] .. cu_q[b+1]-1; its draft rows, drafts and accept uniforms start
+    at cu_q[b] - b.  Returns n_accepted [B], out_tokens [cu_q[B]] (b's K_b + 1
+    entries from cu_q[b]), flag_pos [B], n_decisions, n_flagged."""
+    cu = np.asarray(cu_q, dtype=np.int64)
+    B = cu.shape[0] - 1
+    V = target_logits.shape[-1]
+    n = np.zeros(B, np.int32)
+    out = np.zeros(int(cu[B]), np.int32)
+    fp = np.zeros(B, np.int32)
+    nd = nf = 0
+    for b in range(B):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        k = r1 - r0 - 1
+        d0 = r0 - b
+        dl = None if (greedy and draft_logits is None) else \
+            np.asarray(draft_logits)[d0:d0 + k].reshape(1, k, V)
+        a = accept(np.asarray(target_logits)[r0:r1].reshape(1, k + 1, V), dl,
+                   np.asarray(draft_tokens)[d0:d0 + k].reshape(1, k),
+                   np.asarray(u_accept)[d0:d0 + k].reshape(1, k),
+                   np.asarray(u_sample)[b:b + 1], temperature, top_p, greedy, lib_=lib_)
+        n[b] = a["n_accepted"][0]
+        out[r0:r1] = a["out_tokens"][0]
+        fp[b] = a["flag_pos"][0]
+        nd += a["n_decisions"]
+        nf += a["n_flagged"]
+    return {"n_accepted": n, "out_tokens": out, "flag_pos": fp, "n_decisions": nd,
+            "n_flagged": nf}
+
+
+def compact_kv_ragged(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, k_new, v_new,
+                      cu_q, Hkv, D, lib_=None):
+    """Padding-free compaction with K_b drafts in sequence b: the uniform
+    compaction of each sequence on its own rows, the packed tokens placed at
+    the exclusive scan of the emitted counts.  Returns (tokens_packed,
+    cu_tokens, kv_len, k_cache, v_cache) as new arrays."""
+    cu = np.asarray(cu_q, dtype=np.int64)
+    B = cu.shape[0] - 1
+    kc = np.array(k_cache, copy=True, order="C")
+    vc = np.array(v_cache, copy=True, order="C")
+    kl = np.array(kv_len, dtype=np.int32, copy=True)
+    packed = np.full(int(cu[B]), -1, np.int32)
+    cut = np.zeros(B + 1, np.int32)
+    for b in range(B):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        k = r1 - r0 - 1
+        pk, c1, l1, kc, vc = compact_kv(np.asarray(n_accepted)[b:b + 1],
+                                        np.asarray(out_tokens)[r0:r1].reshape(1, k + 1),
+                                        kl[b:b + 1], np.asarray(kv_start)[b:b + 1], kc, vc,
+                                        k_new[r0:r1], v_new[r0:r1], k, Hkv, D, lib_=lib_)
+        e = int(c1[1])
+        packed[cut[b]:cut[b] + e] = pk[:e]
+        cut[b + 1] = cut[b] + e
+        kl[b] = l1[0]
+    return packed, cut, kl, kc, vc
+
+
 def workload_attn(w, sel_rows=None, sel_heads=None):
     """Oracle attention on a workload object from the shared input generator."""
     c = w.cfg

@@ -50,9 +50,23 @@ def lib():
                                   ctypes.c_float, i32, vp, vp, vp, vp, sz, vp]
         h.spec_compact_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                       i32, vp, vp]
+        h.spec_verify_attn_ragged_workspace_size.argtypes = [i32, i32, i32, i32, i32, vp, vp, i32,
+                                                             ctypes.POINTER(sz)]
+        h.spec_verify_attn_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                              vp, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp,
+                                              sz, vp]
+        h.spec_accept_ragged_workspace_size.argtypes = [i32, vp, i32, ctypes.POINTER(sz)]
+        h.spec_accept_ragged.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32,
+                                         ctypes.c_float, ctypes.c_float, i32, vp, vp, vp, vp, sz,
+                                         vp]
+        h.spec_compact_kv_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                             i32, i32, vp, vp]
         h.sv_set_kernel_events.argtypes = [vp, vp]
         for f in ("sv_set_kernel_events", "spec_verify_attn_workspace_size", "spec_verify_attn",
-                  "spec_accept_workspace_size", "spec_accept", "spec_compact_kv"):
+                  "spec_accept_workspace_size", "spec_accept", "spec_compact_kv",
+                  "spec_verify_attn_ragged_workspace_size", "spec_verify_attn_ragged",
+                  "spec_accept_ragged_workspace_size", "spec_accept_ragged",
+                  "spec_compact_kv_ragged"):
             getattr(h, f).restype = i32
         _lib = h
     return _lib
@@ -199,6 +213,123 @@ def spec_compact_kv(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, 
         _ptr(n_accepted), _ptr(out_tokens), _ptr(kv_len), _ptr(kv_start), _ptr(k_cache),
         _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(tokens_packed), _ptr(cu_tokens), B, K,
         Hkv, D, _kv_dtype(k_cache), _ptr(status), _stream(k_cache)))
+    return tokens_packed, cu_tokens
+
+
+# ---------------------------------------------------------------- ragged draft lengths
+
+def _cu_host(cu_q_host, B):
+    hl = [int(v) for v in (cu_q_host.tolist() if hasattr(cu_q_host, "tolist") else cu_q_host)]
+    _need(len(hl) == B + 1, "cu_q_host has B+1 entries")
+    return hl
+
+
+def spec_verify_attn_ragged_workspace_size(B, Hq, Hkv, D, dtype, kv_len_host, cu_q_host,
+                                           prefix_len=0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().spec_verify_attn_ragged_workspace_size(
+        B, Hq, Hkv, D, dtype, _host_i32(kv_len_host), _host_i32(_cu_host(cu_q_host, B)),
+        prefix_len, ctypes.byref(n)))
+    return n.value
+
+
+def spec_verify_attn_ragged(q, k_cache, v_cache, kv_start, kv_len, kv_len_host, k_new, v_new,
+                            out, cu_q, cu_q_host, k_prefix=None, v_prefix=None,
+                            softmax_scale=0.0, status=None, workspace=None):
+    """Attention of the K_b+1 verify queries of every sequence b, packed by the
+    row offsets ``cu_q`` [B+1] (device int32; ``cu_q_host`` the same on the host);
+    writes ``out`` [cu_q[B], Hq, D]."""
+    B = kv_len.shape[0]
+    hc = _cu_host(cu_q_host, B)
+    R, Hq, D = q.shape
+    _need(R == hc[B], "q rows must be cu_q[B]")
+    Hkv = k_cache.shape[1]
+    dt = _kv_dtype(q)
+    for t in (k_cache, v_cache, k_new, v_new, out):
+        _need(t.dtype == q.dtype and t.is_cuda, "KV tensors must share q's dtype and device")
+    _need(k_cache.shape[1:] == (Hkv, D) and v_cache.shape == k_cache.shape, "cache shape")
+    _need(k_new.shape == (R, Hkv, D) and v_new.shape == (R, Hkv, D), "new K/V shape")
+    _need(out.shape == q.shape, "out shape")
+    _need(cu_q.dtype == torch.int32 and cu_q.shape == (B + 1,), "cu_q [B+1] int32")
+    _need(kv_start.dtype == torch.int64 and kv_start.shape == (B,), "kv_start [B] int64")
+    _need(kv_len.dtype == torch.int32 and kv_len.shape == (B,), "kv_len [B] int32")
+    hl = [int(v) for v in (kv_len_host.tolist() if hasattr(kv_len_host, "tolist") else kv_len_host)]
+    _need(len(hl) == B, "kv_len_host has B entries")
+    P = 0
+    if k_prefix is not None:
+        P = k_prefix.shape[0]
+        _need(k_prefix.shape == (P, Hkv, D) and v_prefix.shape == (P, Hkv, D), "prefix shape")
+    need = spec_verify_attn_ragged_workspace_size(B, Hq, Hkv, D, dt, hl, hc, P)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace.numel() >= need, f"workspace needs {need} bytes")
+    _check(lib().spec_verify_attn_ragged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_start), _ptr(kv_len), _host_i32(hl),
+        _ptr(k_new), _ptr(v_new), _ptr(k_prefix), _ptr(v_prefix), P, _ptr(out), _ptr(cu_q),
+        _host_i32(hc), B, Hq, Hkv, D, dt, float(softmax_scale), _ptr(status), _ptr(workspace),
+        workspace.numel(), _stream(q)))
+    return out
+
+
+def spec_accept_ragged_workspace_size(B, cu_q_host, V) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().spec_accept_ragged_workspace_size(B, _host_i32(_cu_host(cu_q_host, B)), V,
+                                                   ctypes.byref(n)))
+    return n.value
+
+
+def spec_accept_ragged(target_logits, draft_logits, draft_tokens, u_accept, u_sample, cu_q,
+                       cu_q_host, temperature, top_p, greedy, n_accepted, out_tokens,
+                       status=None, workspace=None):
+    """Modified rejection sampling with K_b drafts in sequence b: target rows
+    cu_q[b]..cu_q[b+1]-1 of ``target_logits`` [cu_q[B], V]; draft rows, draft
+    tokens and accept uniforms of b start at cu_q[b] - b.  Writes ``n_accepted``
+    [B] and ``out_tokens`` [cu_q[B]] (b's K_b+1 entries from cu_q[b])."""
+    B = n_accepted.shape[0]
+    hc = _cu_host(cu_q_host, B)
+    NT, V = target_logits.shape
+    _need(NT == hc[B], "target rows must be cu_q[B]")
+    ND = NT - B
+    dt = _kv_dtype(target_logits)
+    if draft_logits is not None:
+        _need(draft_logits.shape == (ND, V) and draft_logits.dtype == target_logits.dtype,
+              "draft logits [cu_q[B]-B, V], same dtype as target")
+    _need(draft_tokens.shape == (ND,) and draft_tokens.dtype == torch.int32, "draft tokens")
+    if not greedy:
+        _need(draft_logits is not None, "draft logits are required unless greedy")
+        _need(u_accept.shape == (ND,) and u_accept.dtype == torch.float32, "u_accept")
+        _need(u_sample.shape == (B,) and u_sample.dtype == torch.float32, "u_sample [B]")
+    _need(cu_q.dtype == torch.int32 and cu_q.shape == (B + 1,), "cu_q [B+1] int32")
+    _need(n_accepted.dtype == torch.int32, "n_accepted [B] int32")
+    _need(out_tokens.shape == (NT,) and out_tokens.dtype == torch.int32, "out_tokens [cu_q[B]]")
+    need = spec_accept_ragged_workspace_size(B, hc, V)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=target_logits.device)
+    _need(workspace.numel() >= need, f"workspace needs {need} bytes")
+    _check(lib().spec_accept_ragged(
+        _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
+        _ptr(u_accept) if not greedy else None, _ptr(u_sample) if not greedy else None,
+        _ptr(cu_q), _host_i32(hc), B, V, float(temperature), float(top_p), int(bool(greedy)),
+        _ptr(n_accepted), _ptr(out_tokens), _ptr(status), _ptr(workspace), workspace.numel(),
+        _stream(target_logits)))
+    return n_accepted, out_tokens
+
+
+def spec_compact_kv_ragged(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, k_new,
+                           v_new, tokens_packed, cu_tokens, cu_q, status=None):
+    """Padding-free compaction with K_b drafts in sequence b (rows packed by cu_q)."""
+    B = n_accepted.shape[0]
+    _, Hkv, D = k_cache.shape
+    R = out_tokens.shape[0]
+    _need(cu_q.dtype == torch.int32 and cu_q.shape == (B + 1,), "cu_q [B+1] int32")
+    _need(kv_len.shape == (B,) and kv_len.dtype == torch.int32, "kv_len [B] int32")
+    _need(kv_start.shape == (B,) and kv_start.dtype == torch.int64, "kv_start [B] int64")
+    _need(k_new.shape == (R, Hkv, D) and v_new.shape == k_new.shape, "new K/V [cu_q[B], Hkv, D]")
+    _need(tokens_packed.numel() >= R and cu_tokens.numel() == B + 1, "outputs")
+    _check(lib().spec_compact_kv_ragged(
+        _ptr(n_accepted), _ptr(out_tokens), _ptr(kv_len), _ptr(kv_start), _ptr(k_cache),
+        _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(tokens_packed), _ptr(cu_tokens), _ptr(cu_q),
+        B, Hkv, D, _kv_dtype(k_cache), _ptr(status), _stream(k_cache)))
     return tokens_packed, cu_tokens
 
 

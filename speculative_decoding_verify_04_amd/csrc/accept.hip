@@ -93,12 +93,24 @@ struct AcceptParams {
     int* row_cnt;
     int* seq_cnt;
     int* draw_cnt;
-    int B, K, V, nseg, nrows, grid_rows;
+    const int32_t* cu_q;       // [B+1] ragged draft lengths: target rows of b start at cu_q[b]
+    int nt;                    // target rows (cu_q[B], or B*(K+1))
+    int B, K, V, nseg, nrows, grid_rows;  // K: the largest draft length
     int bf16, vec, nucleus, greedy;
     double invT;
     double top_p;
     float bscale;  // 4 / T: bin index of z is floor(z * bscale)
 };
+
+// Sequence b owns target rows q0 .. q0+K_b (q0 = cu_q[b], or b*(K+1)) and draft
+// rows nt+q0-b .. nt+q0-b+K_b-1; its drafts and accept uniforms start at
+// q0-b, its output tokens at q0.
+__device__ __forceinline__ int seq_q0(const AcceptParams& p, int b) {
+    return p.cu_q ? p.cu_q[b] : b * (p.K + 1);
+}
+__device__ __forceinline__ int seq_kb(const AcceptParams& p, int b) {
+    return p.cu_q ? min(max(p.cu_q[b + 1] - p.cu_q[b] - 1, 0), p.K) : p.K;
+}
 
 // ---------------------------------------------------------------- loads
 
@@ -140,7 +152,7 @@ __device__ __forceinline__ int seg_index(int s, int tid, int k) {
 }
 
 __device__ __forceinline__ const void* row_ptr(const AcceptParams& p, int r) {
-    const int nt = p.B * (p.K + 1);
+    const int nt = p.nt;
     const size_t es = p.bf16 ? 2 : 4;
     if (r < nt) return static_cast<const char*>(p.target) + static_cast<size_t>(r) * p.V * es;
     return static_cast<const char*>(p.draft) + static_cast<size_t>(r - nt) * p.V * es;
@@ -230,6 +242,7 @@ struct RowsLds {
     int chosen;
     int n, tok, lastpos;
     float us;                 // u_sample of the sequence
+    int rb;                   // sequence of the workgroup's row (ragged draft lengths)
 };
 
 // Exact tie-closed nucleus threshold by radix select over the whole row
@@ -532,23 +545,16 @@ __device__ __forceinline__ void list_threshold(const AcceptParams& p, double tar
 }
 
 // Merge the segments of row r and write its RowRec.
-__device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, RowsLds& L) {
+__device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b, RowsLds& L) {
     const int tid = threadIdx.x;
-    const int nt = p.B * (p.K + 1);
     const void* row = row_ptr(p, r);
     const SegHead* sr = p.seg + static_cast<size_t>(r) * p.nseg;
 
-    // drafted token of this row: target row j < K, or draft row j
-    int j = -1, b = 0;
-    const bool is_target = r < nt;
-    if (is_target) {
-        b = r / (p.K + 1);
-        j = r % (p.K + 1);
-        if (j == p.K) j = -1;
-    } else {
-        b = (r - nt) / p.K;
-        j = (r - nt) % p.K;
-    }
+    // drafted token of this row: target row j < K_b (draft index r - b), or
+    // draft row j (draft index r - nt); -1: the bonus row
+    const bool is_target = r < p.nt;
+    const int xi = is_target ? ((r + 1 < seq_q0(p, b + 1)) ? r - b : -1) : r - p.nt;
+    const int j = xi;  // >= 0 iff the row has a drafted token
 
     // one round trip: segment heads, the first kChunk segments' list slot
     // tid, and the drafted logit
@@ -568,7 +574,7 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, RowsL
     if (tid == kThreads - 1) {
         // independent loads: the drafted token, and its logit as stored by the
         // segment holding it (meaningful only for a valid token)
-        const int x = (j >= 0) ? p.draft_tokens[b * p.K + j] : -1;
+        const int x = (j >= 0) ? p.draft_tokens[xi] : -1;
         const float zv = ld_coh(p.zx + r);
         L.n = x;
         L.zx = (j >= 0 && x >= 0 && x < p.V && !p.greedy) ? zv : 0.0f;
@@ -763,10 +769,10 @@ __device__ __forceinline__ int draw_runs(const AcceptParams& p, int b, bool resi
 // holds the crossing, which E lanes of wave 0 then scan at once.  Returns -1
 // when the nucleus has more than kNuc members (the caller then draws from the
 // whole row).
-__device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int n, RowsLds& L) {
+__device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int q0, int K, int n,
+                                               RowsLds& L) {
     const int tid = threadIdx.x, lane = tid & 63;
-    const int K = p.K;
-    const int rq = b * (K + 1) + n;
+    const int rq = q0 + n;
     const bool residual = n < K;
     const DrawRows R = draw_rows(L.sq.rr[n], residual ? L.sq.rr[K + 1 + n] : L.sq.rr[n]);
     const int E0 = p.nseg;
@@ -803,7 +809,7 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
     const int E = (M + kThreads - 1) / kThreads;  // <= kNuc / kThreads
     const int m0 = tid * E;
     // second round trip: the residual needs the draft logits at those ids
-    const void* drow = row_ptr(p, p.B * (K + 1) + b * K + (residual ? n : 0));
+    const void* drow = row_ptr(p, p.nt + q0 - b + (residual ? n : 0));
     float zpv[kNuc / kThreads];
 #pragma unroll
     for (int i = 0; i < kNuc / kThreads; ++i)
@@ -869,13 +875,13 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
 // Token drawn at position n of sequence b by one pass over the whole stopping
 // row (rows whose lists do not hold the nucleus): thread t owns the
 // contiguous ids [t*per, (t+1)*per).
-__device__ __forceinline__ int draw_full_row(const AcceptParams& p, int b, int n, RowsLds& L) {
+__device__ __forceinline__ int draw_full_row(const AcceptParams& p, int b, int q0, int K, int n,
+                                             RowsLds& L) {
     const int tid = threadIdx.x;
-    const int K = p.K, nt = p.B * (K + 1);
     const bool residual = n < K;
     const DrawRows R = draw_rows(L.sq.rr[n], residual ? L.sq.rr[K + 1 + n] : L.sq.rr[n]);
-    const void* qrow = row_ptr(p, b * (K + 1) + n);
-    const void* prow = residual ? row_ptr(p, nt + b * K + n) : qrow;
+    const void* qrow = row_ptr(p, q0 + n);
+    const void* prow = residual ? row_ptr(p, p.nt + q0 - b + n) : qrow;
     const int per = (p.V + kThreads - 1) / kThreads;
     const int e0 = min(p.V, tid * per), e1 = min(p.V, e0 + per);
     const int bf16 = p.bf16;
@@ -908,12 +914,15 @@ __device__ __forceinline__ int draw_full_row(const AcceptParams& p, int b, int n
 // on (or greedy) also the emitted token.
 __device__ __forceinline__ void finalize_sequence(const AcceptParams& p, int b, RowsLds& L) {
     const int tid = threadIdx.x;
-    const int K = p.K, nt = p.B * (K + 1);
+    const int q0 = seq_q0(p, b);  // uniform
+    const int K = seq_kb(p, b);   // this sequence's draft length
+    const int d0 = q0 - b;        // its first draft token / draft row
+    const int nt = p.nt;
     const int nr = p.greedy ? K + 1 : 2 * K + 1;
     __syncthreads();  // the row merge's LDS use ends
     // one round trip: the sequence's row records, drafts and uniforms
     if (tid < nr) {
-        const int r = (tid <= K) ? b * (K + 1) + tid : nt + b * K + (tid - K - 1);
+        const int r = (tid <= K) ? q0 + tid : nt + d0 + (tid - K - 1);
         const RowRec* src = p.rows + r;
         L.sq.rr[tid].m = ld_coh(&src->m);
         L.sq.rr[tid].tau = ld_coh(&src->tau);
@@ -924,8 +933,8 @@ __device__ __forceinline__ void finalize_sequence(const AcceptParams& p, int b, 
         L.sq.rr[tid].fast = ld_coh(&src->fast);
     }
     if (tid >= 128 && tid - 128 < K) {
-        L.sq.x[tid - 128] = p.draft_tokens[b * K + tid - 128];
-        L.sq.ua[tid - 128] = p.greedy ? 0.0f : p.u_accept[b * K + tid - 128];
+        L.sq.x[tid - 128] = p.draft_tokens[d0 + tid - 128];
+        L.sq.ua[tid - 128] = p.greedy ? 0.0f : p.u_accept[d0 + tid - 128];
     }
     if (tid == kThreads - 1) L.us = p.greedy ? 0.0f : p.u_sample[b];
     __syncthreads();
@@ -952,7 +961,7 @@ __device__ __forceinline__ void finalize_sequence(const AcceptParams& p, int b, 
     __syncthreads();
     if (tid == 0) {
         const int n = L.n;
-        int32_t* out = p.out_tokens + static_cast<size_t>(b) * (K + 1);
+        int32_t* out = p.out_tokens + q0;
         for (int i = 0; i < n; ++i) out[i] = L.sq.x[i];
         for (int i = n + 1; i <= K; ++i) out[i] = -1;
         if (p.greedy) out[n] = L.sq.rr[n].argmax;
@@ -962,9 +971,9 @@ __device__ __forceinline__ void finalize_sequence(const AcceptParams& p, int b, 
     __syncthreads();
     if (p.greedy || !p.nucleus) return;  // no nucleus: draw_kernel draws
     const int n = L.n;
-    int tok = L.sq.rr[n].fast ? draw_from_lists(p, b, n, L) : -1;
-    if (tok < 0) tok = draw_full_row(p, b, n, L);
-    if (tid == 0) p.out_tokens[static_cast<size_t>(b) * (K + 1) + n] = tok;
+    int tok = L.sq.rr[n].fast ? draw_from_lists(p, b, q0, K, n, L) : -1;
+    if (tok < 0) tok = draw_full_row(p, b, q0, K, n, L);
+    if (tid == 0) p.out_tokens[q0 + n] = tok;
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void rows_kernel(AcceptParams p) {
@@ -976,17 +985,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (r >= p.nrows) return;
     const void* row = row_ptr(p, r);
 
-    // drafted token of this row (target row j < K, or draft row j): loaded
-    // with the logits; the segment holding it stores its logit for the merge
-    const int nt = p.B * (p.K + 1);
-    const int jr = (r < nt) ? r % (p.K + 1) : (r - nt) % p.K;
-    const bool has_x = (!p.greedy) & ((r >= nt) | (jr < p.K));
-    const int br = (r < nt) ? r / (p.K + 1) : (r - nt) / p.K;
-    const int xr = has_x ? p.draft_tokens[br * p.K + jr] : -1;
-
+    const int nt = p.nt;
+    if (tid == 0) L.rb = 0;
     float z[kPerThread];
     load_segment(row, p.bf16, p.vec, p.V, s, tid, z);
     fill_exp_table(L.tab);
+    // sequence of row r (ragged: the one whose target or draft rows hold it)
+    int br;
+    if (p.cu_q) {
+        const bool tgt = r < nt;
+        const int key = tgt ? r : r - nt;
+        __syncthreads();
+        for (int i = tid; i < p.B; i += kThreads) {
+            const int lo = p.cu_q[i] - (tgt ? 0 : i), hi = p.cu_q[i + 1] - (tgt ? 0 : i + 1);
+            if ((key >= lo) & (key < hi)) L.rb = i;
+        }
+        __syncthreads();
+        br = L.rb;
+    } else {
+        br = (r < nt) ? r / (p.K + 1) : (r - nt) / p.K;
+    }
+    // drafted token of this row (target row j < K_b: draft index r - b; draft
+    // row: r - nt); the segment holding it stores its logit for the merge
+    const int xi = (r < nt) ? ((r + 1 < seq_q0(p, br + 1)) ? r - br : -1) : r - nt;
+    const int xr = ((!p.greedy) & (xi >= 0)) ? p.draft_tokens[xi] : -1;
     if ((xr >= s * kSeg) & (xr < (s + 1) * kSeg) & (xr < p.V)) {
 #pragma unroll
         for (int k = 0; k < kPerThread; ++k)
@@ -1045,10 +1067,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 
     if (!arrive_last(p.row_cnt + r, p.nseg, &L.flag)) return;
-    finalize_row(p, r, L);
+    finalize_row(p, r, br, L);
 
     const int b = br;
-    const int rows_per_seq = p.greedy ? p.K + 1 : 2 * p.K + 1;
+    const int kb = seq_kb(p, b);
+    const int rows_per_seq = p.greedy ? kb + 1 : 2 * kb + 1;
     if (!arrive_last(p.seq_cnt + b, rows_per_seq, &L.flag)) return;
     finalize_sequence(p, b, L);
 }
@@ -1105,24 +1128,24 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
     const int logical = xcd_remap(blockIdx.x, total);
     const int b = logical / p.nseg, s = logical % p.nseg;
     if (b >= p.B) return;
-    const int K = p.K, nt = p.B * (K + 1);
+    const int K = seq_kb(p, b), q0 = seq_q0(p, b), nt = p.nt;
 
     if (tid == 0) L.n = min(max(p.seqs[b].n, 0), K);
     fill_exp_table(L.tab);
     __syncthreads();
     const int n = L.n;
-    if (tid == 0) L.rr[0] = p.rows[b * (K + 1) + n];
-    if (tid == 1 && n < K) L.rr[1] = p.rows[nt + b * K + n];
+    if (tid == 0) L.rr[0] = p.rows[q0 + n];
+    if (tid == 1 && n < K) L.rr[1] = p.rows[nt + q0 - b + n];
     __syncthreads();
 
     DrawCtx c;
     c.tab = L.tab;
     c.residual = n < K;
-    c.qrow = row_ptr(p, b * (K + 1) + n);
+    c.qrow = row_ptr(p, q0 + n);
     c.rq = L.rr[0];
     c.invSq = 1.0 / c.rq.S;
     if (c.residual) {
-        c.prow = row_ptr(p, nt + b * K + n);
+        c.prow = row_ptr(p, nt + q0 - b + n);
         c.rp = L.rr[1];
         c.invSp = 1.0 / c.rp.S;
     } else {
@@ -1227,17 +1250,21 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
     if (tid == 0) {
         int tok = L.tok != 0x7FFFFFFF ? L.tok : L.last_pos;
         if (tok < 0) tok = 0;
-        p.out_tokens[static_cast<size_t>(b) * (K + 1) + n] = tok;
+        p.out_tokens[q0 + n] = tok;
     }
 }
 
 }  // namespace
 
-size_t accept_workspace_bytes(int B, int K, int V) {
+size_t accept_workspace_bytes(int B, long long nt, int V) {
     const size_t nseg = (static_cast<size_t>(V) + kSeg - 1) / kSeg;
-    const size_t nrows = static_cast<size_t>(B) * (2 * K + 1);
+    const size_t nrows = static_cast<size_t>(2 * nt - B);  // target and draft rows
     size_t off = 0;
     auto take = [&](size_t bytes) { off = (off + 255) & ~static_cast<size_t>(255); off += bytes; };
+    // arrival counters first, sized for any draft lengths of B sequences
+    take(static_cast<size_t>(B) * sizeof(int));
+    take(static_cast<size_t>(B) * sizeof(int));
+    take(static_cast<size_t>(B) * kMaxRowsPerSeq * sizeof(int));
     take(nrows * nseg * sizeof(SegHead));
     take(nrows * nseg * kList * sizeof(unsigned long long));
     take(nrows * sizeof(RowRec));
@@ -1245,9 +1272,6 @@ size_t accept_workspace_bytes(int B, int K, int V) {
     take(static_cast<size_t>(B) * sizeof(SeqRec));
     take(static_cast<size_t>(B) * nseg * sizeof(double));
     take(static_cast<size_t>(B) * nseg * sizeof(double));
-    take(nrows * sizeof(int));
-    take(static_cast<size_t>(B) * sizeof(int));
-    take(static_cast<size_t>(B) * sizeof(int));
     return (off + 255) & ~static_cast<size_t>(255);
 }
 
@@ -1266,6 +1290,8 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     p.status = a.status;
     p.B = a.B;
     p.K = a.K;
+    p.cu_q = a.cu_q;
+    p.nt = a.nt;
     p.V = a.V;
     p.nseg = (a.V + kSeg - 1) / kSeg;
     p.bf16 = a.bf16;
@@ -1275,11 +1301,11 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     p.invT = 1.0 / static_cast<double>(a.temperature);
     p.top_p = static_cast<double>(a.top_p);
     p.bscale = static_cast<float>(4.0 / static_cast<double>(a.temperature));
-    p.nrows = a.greedy ? a.B * (a.K + 1) : a.B * (2 * a.K + 1);
+    p.nrows = a.greedy ? a.nt : 2 * a.nt - a.B;
     p.grid_rows = (p.nrows + 7) / 8 * 8;
 
     const size_t nseg = p.nseg;
-    const size_t nrows_max = static_cast<size_t>(a.B) * (2 * a.K + 1);
+    const size_t nrows_max = static_cast<size_t>(2 * a.nt - a.B);
     char* base = static_cast<char*>(a.workspace);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -1288,6 +1314,12 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
         off += bytes;
         return ptr;
     };
+    // arrival counters first: their place depends on B only (the rows of B
+    // sequences are at most B * kMaxRowsPerSeq), so calls with other draft
+    // lengths or vocabularies never put data over them
+    p.seq_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * sizeof(int)));
+    p.draw_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * sizeof(int)));
+    p.row_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * kMaxRowsPerSeq * sizeof(int)));
     p.seg = reinterpret_cast<SegHead*>(take(nrows_max * nseg * sizeof(SegHead)));
     p.list = reinterpret_cast<unsigned long long*>(take(nrows_max * nseg * kList * sizeof(unsigned long long)));
     p.rows = reinterpret_cast<RowRec*>(take(nrows_max * sizeof(RowRec)));
@@ -1295,9 +1327,6 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     p.seqs = reinterpret_cast<SeqRec*>(take(static_cast<size_t>(a.B) * sizeof(SeqRec)));
     p.dsum = reinterpret_cast<double*>(take(static_cast<size_t>(a.B) * nseg * sizeof(double)));
     p.qsum = reinterpret_cast<double*>(take(static_cast<size_t>(a.B) * nseg * sizeof(double)));
-    p.row_cnt = reinterpret_cast<int*>(take(nrows_max * sizeof(int)));
-    p.seq_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * sizeof(int)));
-    p.draw_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * sizeof(int)));
 
     hipLaunchKernelGGL(rows_kernel, dim3(p.grid_rows * p.nseg), dim3(kThreads), 0, stream, p);
     hipError_t err = hipGetLastError();

@@ -64,42 +64,41 @@ int check_attn_shape(int B, int K, int Hq, int Hkv, int D, int dtype, const int3
     return SV_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* sv_last_error(void) { return g_err; }
-
-int sv_version(void) { return 100; }
-
-int sv_set_kernel_events(void* start, void* stop) {
-    if (start && stop) {
-        g_ev_start = static_cast<hipEvent_t>(start);
-        g_ev_stop = static_cast<hipEvent_t>(stop);
-    } else {
-        g_ev_start = g_ev_stop = nullptr;
+// Ragged draft lengths: cu_q_host[0] = 0 and K_b = cu_q_host[b+1] - cu_q_host[b] - 1
+// >= 0; *kmax = the largest K_b.
+int check_cu_q(int B, const int32_t* cu_q_host, int* kmax) {
+    if (!cu_q_host) return fail(SV_ERR_INVALID_ARG, "cu_q_host is NULL");
+    if (B < 1) return fail(SV_ERR_INVALID_ARG, "B must be >= 1 (got %d)", B);
+    if (cu_q_host[0] != 0) return fail(SV_ERR_INVALID_ARG, "cu_q_host[0] must be 0 (got %d)", cu_q_host[0]);
+    int km = 0;
+    for (int b = 0; b < B; ++b) {
+        const long long d = static_cast<long long>(cu_q_host[b + 1]) - cu_q_host[b];
+        if (d < 1)
+            return fail(SV_ERR_INVALID_ARG, "sequence %d has %lld query rows (need K_b + 1 >= 1)", b, d);
+        if (d - 1 > km) km = static_cast<int>(d - 1 > 0x7FFFFFFF ? 0x7FFFFFFF : d - 1);
     }
-    return ok();
+    *kmax = km;
+    return SV_OK;
 }
 
-int spec_verify_attn_workspace_size(int B, int K, int Hq, int Hkv, int D, int dtype,
-                                    const int32_t* kv_len_host, int prefix_len, size_t* bytes) {
+int attn_workspace(int B, int K, int Hq, int Hkv, int D, int dtype, const int32_t* kv_len_host,
+                   const int32_t* cu_q_host, int prefix_len, size_t* bytes) {
     int rc = check_attn_shape(B, K, Hq, Hkv, D, dtype, kv_len_host, prefix_len);
     if (rc) return rc;
     if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
-    const sv::AttnPlan plan = sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, prefix_len);
+    const sv::AttnPlan plan =
+        sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, cu_q_host, prefix_len);
     if (!plan.ok) return fail(SV_ERR_UNSUPPORTED, "KV length bound too long (bf16: at most 2^25 keys per sequence, 2^30 64-key tiles in all)");
     *bytes = plan.bytes;
     return ok();
 }
 
-int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
-                     const int64_t* kv_start, const int32_t* kv_len,
-                     const int32_t* kv_len_host, const void* k_new, const void* v_new,
-                     const void* k_prefix, const void* v_prefix, int prefix_len,
-                     void* out, int B, int K, int Hq, int Hkv, int D, int dtype,
-                     float softmax_scale, int32_t* status, void* workspace,
-                     size_t workspace_bytes, sv_stream_t stream) {
+int attn_run(const void* q, const void* k_cache, const void* v_cache, const int64_t* kv_start,
+             const int32_t* kv_len, const int32_t* kv_len_host, const void* k_new,
+             const void* v_new, const void* k_prefix, const void* v_prefix, int prefix_len,
+             void* out, const int32_t* cu_q, const int32_t* cu_q_host, int rows, int B, int K,
+             int Hq, int Hkv, int D, int dtype, float softmax_scale, int32_t* status,
+             void* workspace, size_t workspace_bytes, sv_stream_t stream) {
     int rc = check_attn_shape(B, K, Hq, Hkv, D, dtype, kv_len_host, prefix_len);
     if (rc) return rc;
     if (!q || !k_cache || !v_cache || !kv_start || !kv_len || !k_new || !v_new || !out)
@@ -113,7 +112,7 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
         return fail(SV_ERR_INVALID_ARG, "tensors must be %zu-byte aligned", al);
     if (!isfinite(softmax_scale)) return fail(SV_ERR_INVALID_ARG, "softmax_scale is not finite");
     const sv::AttnPlan plan =
-        sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, prefix_len);
+        sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, cu_q_host, prefix_len);
     if (!plan.ok) return fail(SV_ERR_UNSUPPORTED, "KV length bound too long (bf16: at most 2^25 keys per sequence, 2^30 64-key tiles in all)");
     if (!workspace || workspace_bytes < plan.bytes)
         return fail(SV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.bytes,
@@ -130,6 +129,8 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
     a.v_prefix = prefix_len > 0 ? v_prefix : nullptr;
     a.out = out;
     a.status = status;
+    a.cu_q = cu_q;
+    a.rows = rows;
     a.B = B;
     a.K = K;
     a.Hq = Hq;
@@ -146,21 +147,11 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
     return ok();
 }
 
-int spec_accept_workspace_size(int B, int K, int V, size_t* bytes) {
-    if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
-    if (V > sv::accept_max_vocab())
-        return fail(SV_ERR_UNSUPPORTED, "vocabulary above %d", sv::accept_max_vocab());
-    if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = sv::accept_workspace_bytes(B, K, V);
-    return ok();
-}
-
-int spec_accept(const void* target_logits, const void* draft_logits, int logits_dtype,
-                const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
-                int B, int K, int V, float temperature, float top_p, int greedy,
-                int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
-                void* workspace, size_t workspace_bytes, sv_stream_t stream) {
-    if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
+int accept_run(const void* target_logits, const void* draft_logits, int logits_dtype,
+               const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+               const int32_t* cu_q, long long nt, int B, int K, int V, float temperature,
+               float top_p, int greedy, int32_t* n_accepted, int32_t* out_tokens,
+               int32_t* status, void* workspace, size_t workspace_bytes, sv_stream_t stream) {
     if (V > sv::accept_max_vocab())
         return fail(SV_ERR_UNSUPPORTED, "vocabulary above %d", sv::accept_max_vocab());
     if (logits_dtype != SV_F32 && logits_dtype != SV_BF16)
@@ -170,6 +161,8 @@ int spec_accept(const void* target_logits, const void* draft_logits, int logits_
     if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(SV_ERR_INVALID_ARG, "top_p must be in (0, 1]");
     if (K > sv::accept_max_drafts())
         return fail(SV_ERR_UNSUPPORTED, "K above %d", sv::accept_max_drafts());
+    if (2 * nt - B > 0x7FFFFFFF / 64)
+        return fail(SV_ERR_UNSUPPORTED, "too many logit rows (%lld)", 2 * nt - B);
     if (B == 0) return ok();
     if (!target_logits || !n_accepted || !out_tokens)
         return fail(SV_ERR_INVALID_ARG, "a required tensor pointer is NULL");
@@ -178,7 +171,7 @@ int spec_accept(const void* target_logits, const void* draft_logits, int logits_
         if (!u_sample || (K > 0 && (!u_accept || !draft_logits)))
             return fail(SV_ERR_INVALID_ARG, "draft_logits, u_accept and u_sample are required unless greedy");
     }
-    const size_t need = sv::accept_workspace_bytes(B, K, V);
+    const size_t need = sv::accept_workspace_bytes(B, nt, V);
     if (!workspace || workspace_bytes < need)
         return fail(SV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : static_cast<size_t>(0));
@@ -195,6 +188,8 @@ int spec_accept(const void* target_logits, const void* draft_logits, int logits_
     a.out_tokens = out_tokens;
     a.status = status;
     a.workspace = workspace;
+    a.cu_q = cu_q;
+    a.nt = static_cast<int>(nt);
     a.B = B;
     a.K = K;
     a.V = V;
@@ -207,13 +202,13 @@ int spec_accept(const void* target_logits, const void* draft_logits, int logits_
     return ok();
 }
 
-int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
-                    const int64_t* kv_start, void* k_cache, void* v_cache,
-                    const void* k_new, const void* v_new, int32_t* tokens_packed,
-                    int32_t* cu_tokens, int B, int K, int Hkv, int D, int dtype,
-                    int32_t* status, sv_stream_t stream) {
-    if (B < 0 || K < 0 || Hkv < 1 || D < 1)
-        return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, Hkv >= 1, D >= 1");
+int compact_run(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
+                const int64_t* kv_start, void* k_cache, void* v_cache, const void* k_new,
+                const void* v_new, int32_t* tokens_packed, int32_t* cu_tokens,
+                const int32_t* cu_q, int B, int K, int Hkv, int D, int dtype, int32_t* status,
+                sv_stream_t stream) {
+    if (B < 0 || Hkv < 1 || D < 1)
+        return fail(SV_ERR_INVALID_ARG, "need B >= 0, Hkv >= 1, D >= 1");
     if (dtype != SV_F32 && dtype != SV_BF16)
         return fail(SV_ERR_INVALID_ARG, "dtype must be SV_F32 or SV_BF16");
     const int es = dtype == SV_BF16 ? 2 : 4;
@@ -235,6 +230,7 @@ int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_
     a.tokens_packed = tokens_packed;
     a.cu_tokens = cu_tokens;
     a.status = status;
+    a.cu_q = cu_q;
     a.B = B;
     a.K = K;
     a.Hkv = Hkv;
@@ -243,6 +239,138 @@ int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_
     hipError_t e = sv::compact_launch(a, as_stream(stream));
     if (e != hipSuccess) return fail(SV_ERR_HIP, "compaction launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sv_last_error(void) { return g_err; }
+
+int sv_version(void) { return 100; }
+
+int sv_set_kernel_events(void* start, void* stop) {
+    if (start && stop) {
+        g_ev_start = static_cast<hipEvent_t>(start);
+        g_ev_stop = static_cast<hipEvent_t>(stop);
+    } else {
+        g_ev_start = g_ev_stop = nullptr;
+    }
+    return ok();
+}
+
+int spec_verify_attn_workspace_size(int B, int K, int Hq, int Hkv, int D, int dtype,
+                                    const int32_t* kv_len_host, int prefix_len, size_t* bytes) {
+    return attn_workspace(B, K, Hq, Hkv, D, dtype, kv_len_host, nullptr, prefix_len, bytes);
+}
+
+int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                     const int64_t* kv_start, const int32_t* kv_len,
+                     const int32_t* kv_len_host, const void* k_new, const void* v_new,
+                     const void* k_prefix, const void* v_prefix, int prefix_len,
+                     void* out, int B, int K, int Hq, int Hkv, int D, int dtype,
+                     float softmax_scale, int32_t* status, void* workspace,
+                     size_t workspace_bytes, sv_stream_t stream) {
+    const long long rows = static_cast<long long>(B) * (K + 1);
+    if (B >= 1 && K >= 0 && rows > 0x7FFFFFFF)
+        return fail(SV_ERR_UNSUPPORTED, "B*(K+1) above 2^31 - 1");
+    return attn_run(q, k_cache, v_cache, kv_start, kv_len, kv_len_host, k_new, v_new, k_prefix,
+                    v_prefix, prefix_len, out, nullptr, nullptr, static_cast<int>(rows), B, K, Hq,
+                    Hkv, D, dtype, softmax_scale, status, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_attn_ragged_workspace_size(int B, int Hq, int Hkv, int D, int dtype,
+                                           const int32_t* kv_len_host, const int32_t* cu_q_host,
+                                           int prefix_len, size_t* bytes) {
+    int kmax = 0;
+    int rc = check_cu_q(B, cu_q_host, &kmax);
+    if (rc) return rc;
+    return attn_workspace(B, kmax, Hq, Hkv, D, dtype, kv_len_host, cu_q_host, prefix_len, bytes);
+}
+
+int spec_verify_attn_ragged(const void* q, const void* k_cache, const void* v_cache,
+                            const int64_t* kv_start, const int32_t* kv_len,
+                            const int32_t* kv_len_host, const void* k_new, const void* v_new,
+                            const void* k_prefix, const void* v_prefix, int prefix_len,
+                            void* out, const int32_t* cu_q, const int32_t* cu_q_host, int B,
+                            int Hq, int Hkv, int D, int dtype, float softmax_scale,
+                            int32_t* status, void* workspace, size_t workspace_bytes,
+                            sv_stream_t stream) {
+    int kmax = 0;
+    int rc = check_cu_q(B, cu_q_host, &kmax);
+    if (rc) return rc;
+    if (!cu_q) return fail(SV_ERR_INVALID_ARG, "cu_q is NULL");
+    return attn_run(q, k_cache, v_cache, kv_start, kv_len, kv_len_host, k_new, v_new, k_prefix,
+                    v_prefix, prefix_len, out, cu_q, cu_q_host, cu_q_host[B], B, kmax, Hq, Hkv, D,
+                    dtype, softmax_scale, status, workspace, workspace_bytes, stream);
+}
+
+int spec_accept_workspace_size(int B, int K, int V, size_t* bytes) {
+    if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
+    if (V > sv::accept_max_vocab())
+        return fail(SV_ERR_UNSUPPORTED, "vocabulary above %d", sv::accept_max_vocab());
+    if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = sv::accept_workspace_bytes(B, static_cast<long long>(B) * (K + 1), V);
+    return ok();
+}
+
+int spec_accept(const void* target_logits, const void* draft_logits, int logits_dtype,
+                const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                int B, int K, int V, float temperature, float top_p, int greedy,
+                int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
+                void* workspace, size_t workspace_bytes, sv_stream_t stream) {
+    if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
+    return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept, u_sample,
+                      nullptr, static_cast<long long>(B) * (K + 1), B, K, V, temperature, top_p,
+                      greedy, n_accepted, out_tokens, status, workspace, workspace_bytes, stream);
+}
+
+int spec_accept_ragged_workspace_size(int B, const int32_t* cu_q_host, int V, size_t* bytes) {
+    int kmax = 0;
+    int rc = check_cu_q(B, cu_q_host, &kmax);
+    if (rc) return rc;
+    if (V < 1) return fail(SV_ERR_INVALID_ARG, "need V >= 1");
+    if (V > sv::accept_max_vocab())
+        return fail(SV_ERR_UNSUPPORTED, "vocabulary above %d", sv::accept_max_vocab());
+    if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = sv::accept_workspace_bytes(B, cu_q_host[B], V);
+    return ok();
+}
+
+int spec_accept_ragged(const void* target_logits, const void* draft_logits, int logits_dtype,
+                       const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                       const int32_t* cu_q, const int32_t* cu_q_host, int B, int V,
+                       float temperature, float top_p, int greedy, int32_t* n_accepted,
+                       int32_t* out_tokens, int32_t* status, void* workspace,
+                       size_t workspace_bytes, sv_stream_t stream) {
+    int kmax = 0;
+    int rc = check_cu_q(B, cu_q_host, &kmax);
+    if (rc) return rc;
+    if (!cu_q) return fail(SV_ERR_INVALID_ARG, "cu_q is NULL");
+    if (V < 1) return fail(SV_ERR_INVALID_ARG, "need V >= 1");
+    return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept, u_sample,
+                      cu_q, cu_q_host[B], B, kmax, V, temperature, top_p, greedy, n_accepted,
+                      out_tokens, status, workspace, workspace_bytes, stream);
+}
+
+int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
+                    const int64_t* kv_start, void* k_cache, void* v_cache,
+                    const void* k_new, const void* v_new, int32_t* tokens_packed,
+                    int32_t* cu_tokens, int B, int K, int Hkv, int D, int dtype,
+                    int32_t* status, sv_stream_t stream) {
+    if (K < 0) return fail(SV_ERR_INVALID_ARG, "need K >= 0");
+    return compact_run(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, k_new, v_new,
+                       tokens_packed, cu_tokens, nullptr, B, K, Hkv, D, dtype, status, stream);
+}
+
+int spec_compact_kv_ragged(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
+                           const int64_t* kv_start, void* k_cache, void* v_cache,
+                           const void* k_new, const void* v_new, int32_t* tokens_packed,
+                           int32_t* cu_tokens, const int32_t* cu_q, int B, int Hkv, int D,
+                           int dtype, int32_t* status, sv_stream_t stream) {
+    if (B > 0 && !cu_q) return fail(SV_ERR_INVALID_ARG, "cu_q is NULL");
+    return compact_run(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, k_new, v_new,
+                       tokens_packed, cu_tokens, cu_q, B, 0, Hkv, D, dtype, status, stream);
 }
 
 }  // extern "C"

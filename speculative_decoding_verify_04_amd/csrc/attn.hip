@@ -71,6 +71,8 @@ struct AttnParams {
     int* merge_cnt;    // [B][Hkv] arrival counters of the fused merge (bf16 path)
     float* pre_o;      // [prefix_slots][Hkv][NC][D]
     float2* pre_ml;    // [prefix_slots][Hkv][NC]
+    const int32_t* cu_q;  // [B+1] first query row of each sequence (ragged K_b), or null
+    int rows;             // query rows in all: cu_q[B], or B*(K+1)
     int B, K, Hq, Hkv, G, CPG, NC, D, chunk, prefix_chunk, prefix_len, prefix_slots, slots;
     int lambda;        // bf16 path: 16-key slices per work item at most
     int bf16;
@@ -78,6 +80,15 @@ struct AttnParams {
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Query rows of sequence b: cu_q[b] .. cu_q[b+1]-1 (K_b + 1 rows, K_b <= K), or
+// b*(K+1) .. b*(K+1)+K without cu_q.  Its new K/V rows have the same indices.
+__device__ __forceinline__ int seq_q0(const AttnParams& p, int b) {
+    return p.cu_q ? p.cu_q[b] : b * (p.K + 1);
+}
+__device__ __forceinline__ int seq_k1(const AttnParams& p, int b) {
+    return p.cu_q ? min(max(p.cu_q[b + 1] - p.cu_q[b], 1), p.K + 1) : p.K + 1;
+}
 
 // Work item x (a global chunk index) -> (sequence, chunk within it), computed by
 // wave 0 from the device lengths; writes s_b = -1 when x is past the last chunk.
@@ -93,7 +104,7 @@ __device__ void find_sequence(const AttnParams& p, int x, int g, int* s_b, int* 
                 if (x == 0 && g == 0) set_status(p.status, 3);
                 L = 0;
             }
-            n = ceil_div(L + p.K + 1, p.chunk);
+            n = ceil_div(L + seq_k1(p, b), p.chunk);
         }
         const int inc = wave_incl_scan(n, lane) + run;
         const int excl = inc - n;
@@ -167,28 +178,32 @@ struct DecLds {
     uint16_t qs[NCT * 16][D + 8];      // the work item's query columns (B operand source)
     int Q[kSkMaxB + 1];                // Q[b] = q_0 + .. + q_{b-1}
     int L;                             // kv_len of this workgroup's sequence
+    int k1;                            // its query rows (K_b + 1)
+    int q0;                            // its first query row
     long long kv0;                     // kv_start of this workgroup's sequence
     int flag;
 };
 
 // Merge every part of (sequence b, kv head g) -- the prefix chunks first, then
-// its q_b chunks in order -- and write the output rows b*(K+1)+j of heads
+// its q_b chunks in order -- and write the output rows qrow0+j (j < k1) of heads
 // g*G + hh.  Two round trips: the (m, l) of every (part, column) into LDS and
 // the per-column weights, then every o value weighted, with the loads of up
 // to 4 columns x 8 parts in flight per thread.  Fixed order: bit-reproducible.
 template <int D, typename MRG>
-__device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_slot, int qb) {
+__device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_slot, int qb,
+                          int qrow0, int k1) {
     const int tid = threadIdx.x;
     const int np = p.prefix_slots;
     const int nparts = np + qb;
-    const int CPG = p.CPG, K1 = p.K + 1;
+    const int CPG = p.CPG;
+    const int ncols = p.G * k1;  // the sequence's columns (hh * k1 + j)
     const size_t pre_col0 = static_cast<size_t>(g) * p.NC + static_cast<size_t>(b) * CPG;
     auto slot_of = [&](int j) {  // partial slot of stream part j >= np
         return static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * p.Hkv;
     };
-    const int group = max(1, min(CPG, kMergeLds / nparts));
-    for (int c0 = 0; c0 < CPG; c0 += group) {
-        const int nc = min(group, CPG - c0);
+    const int group = max(1, min(ncols, kMergeLds / nparts));
+    for (int c0 = 0; c0 < ncols; c0 += group) {
+        const int nc = min(group, ncols - c0);
         __syncthreads();
         for (int idx = tid; idx < nparts * nc; idx += kThreads) {
             const int j = idx / nc, col = c0 + idx % nc;
@@ -258,8 +273,8 @@ __device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_s
                 const int pq = q0 + u * kThreads;
                 if (pq >= npairs) continue;
                 const int cl = pq % nc, d = pq / nc, col = c0 + cl;
-                const int hh = col / K1, j = col % K1;
-                const size_t oi = ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + d;
+                const int hh = col / k1, j = col % k1;
+                const size_t oi = (static_cast<size_t>(qrow0 + j) * p.Hq + g * p.G + hh) * D + d;
                 static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(acc[u]);
             }
         }
@@ -286,21 +301,22 @@ void decode_bf16_kernel(AttnParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col16 = lane & 15, kg = lane >> 4;
-    const int K1 = p.K + 1;
     const int lambda = p.lambda;
     const int id = blockIdx.x;
 
     // ---- chunks per sequence and their prefix sum (one round trip)
-    int Lr[NPRO];
+    int Lr[NPRO], Kr[NPRO];
     long long Sr[NPRO];
 #pragma unroll
     for (int u = 0; u < NPRO; ++u) {
         const int bb = tid + u * kThreads;
         Lr[u] = 0;
         Sr[u] = 0;
+        Kr[u] = p.K + 1;
         if (bb < p.B) {
             Lr[u] = p.kv_len[bb];
             Sr[u] = p.kv_start[bb];
+            if (p.cu_q) Kr[u] = p.cu_q[bb + 1] - p.cu_q[bb];
         }
     }
 #pragma unroll
@@ -312,7 +328,11 @@ void decode_bf16_kernel(AttnParams p) {
                 Lr[u] = 0;
             }
             Lr[u] = min(Lr[u], kSkMaxKeys);
-            S.Q[bb + 1] = ceil_div(ceil_div(Lr[u] + K1, 16), lambda);
+            if (Kr[u] < 1 || Kr[u] > p.K + 1) {  // device offsets disagree with the host's
+                if (id == 0) set_status(p.status, 3);
+                Kr[u] = min(max(Kr[u], 1), p.K + 1);
+            }
+            S.Q[bb + 1] = ceil_div(ceil_div(Lr[u] + Kr[u], 16), lambda);
         }
     }
     __syncthreads();
@@ -353,12 +373,17 @@ void decode_bf16_kernel(AttnParams p) {
         if (tid + u * kThreads == b) {
             S.L = Lr[u];
             S.kv0 = Sr[u];
+            S.k1 = Kr[u];
+            S.q0 = p.cu_q ? p.cu_q[b] : b * (p.K + 1);
         }
     }
     __syncthreads();
     const int L = __builtin_amdgcn_readfirstlane(S.L);
+    const int k1 = __builtin_amdgcn_readfirstlane(S.k1);  // K_b + 1 query rows
+    const int q0 = __builtin_amdgcn_readfirstlane(S.q0);  // the first of them
+    const int ncols = p.G * k1;
     const long long kv0 = S.kv0;
-    const int T = L + K1;
+    const int T = L + k1;
     const int Sb = ceil_div(T, 16);
     const int sl_lo = static_cast<int>(static_cast<long long>(c) * Sb / qb);
     const int sl_hi = static_cast<int>(static_cast<long long>(c + 1) * Sb / qb);
@@ -375,7 +400,7 @@ void decode_bf16_kernel(AttnParams p) {
     auto row = [&](int tt, const uint16_t* cache, const uint16_t* fresh) -> const uint16_t* {
         tt = min(tt, T - 1);
         return (tt < L) ? cache + static_cast<size_t>(kv0 + tt) * rs + head
-                        : fresh + static_cast<size_t>(b * K1 + (tt - L)) * rs + head;
+                        : fresh + static_cast<size_t>(q0 + (tt - L)) * rs + head;
     };
     auto load_slice = [&](Slice<D>& sl, int k0) {
         const uint16_t* kp = row(k0 + col16, p.k_cache, p.k_new) + kg * 8;
@@ -394,10 +419,10 @@ void decode_bf16_kernel(AttnParams p) {
     for (int idx = tid; idx < NCT * 16 * VCH; idx += kThreads) {
         const int col = idx / VCH, ch = idx % VCH;
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (col < p.CPG) {
-            const int hh = col / K1, j = col % K1;
+        if (col < ncols) {
+            const int hh = col / k1, j = col % k1;
             v = *reinterpret_cast<const uint4*>(
-                p.q + ((static_cast<size_t>(b) * K1 + j) * p.Hq + g * p.G + hh) * D + ch * 8);
+                p.q + (static_cast<size_t>(q0 + j) * p.Hq + g * p.G + hh) * D + ch * 8);
         }
         uint2* dst = reinterpret_cast<uint2*>(&S.qs[col][ch * 8]);
         dst[0] = make_uint2(v.x, v.y);
@@ -407,7 +432,7 @@ void decode_bf16_kernel(AttnParams p) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         const int col = ct * 16 + col16;
-        lim[ct] = (col < p.CPG) ? L + col % K1 + 1 : 0;
+        lim[ct] = (col < ncols) ? L + col % k1 + 1 : 0;
     }
     __syncthreads();
 
@@ -438,9 +463,9 @@ void decode_bf16_kernel(AttnParams p) {
             acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const bf16x8 qb =
+                const bf16x8 qop =
                     *reinterpret_cast<const bf16x8*>(&S.qs[ct * 16 + col16][kg * 8 + 32 * kk]);
-                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl.k[kk], qb, acc[ct], 0, 0, 0);
+                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl.k[kk], qop, acc[ct], 0, 0, 0);
             }
         }
         if (si + 4 < sl_hi) load_slice(sl, k0 + 64);
@@ -514,7 +539,7 @@ void decode_bf16_kernel(AttnParams p) {
                 for (int ee = 0; ee < 4; ++ee)
                     S.red.o[w][(dt - half * (DT / 2)) * 16 + kg * 4 + ee][col16] = o[ct][dt][ee];
             __syncthreads();
-            const int ncol = min(16, p.CPG - ct * 16);
+            const int ncol = min(16, ncols - ct * 16);
             for (int idx = tid; idx < 16 * (D / 2); idx += kThreads) {
                 const int cl = idx & 15, dh = idx >> 4;
                 if (cl >= ncol) continue;
@@ -542,7 +567,7 @@ void decode_bf16_kernel(AttnParams p) {
         }
     }
     if (arrive_last(p.merge_cnt + static_cast<size_t>(b) * p.Hkv + g, qb, &S.flag))
-        dec_merge<D>(p, S.mrg, b, g, first_slot + g, qb);
+        dec_merge<D>(p, S.mrg, b, g, first_slot + g, qb, q0, k1);
 }
 
 template <int D>
@@ -562,20 +587,25 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nthreads = blockDim.x;
     const int x = blockIdx.x, g = blockIdx.y;
-    const int K1 = p.K + 1;
     const int t_begin = x * p.prefix_chunk;
     const int t_end = min(p.prefix_len, t_begin + p.prefix_chunk);
     const int col16 = lane & 15, kg = lane >> 4;
     const int tile = blockIdx.z * 16 + w;
-    const int cg = tile * 16 + col16;           // global column: b*CPG + hh*(K+1) + j
+    const int cg = tile * 16 + col16;           // global column: b*CPG + hh*(K_b+1) + j
     const bool active = tile * 16 < p.NC;
+    int k1c = 1, q0c = 0;                       // the column's sequence
+    if (cg < p.NC) {
+        k1c = seq_k1(p, cg / p.CPG);
+        q0c = seq_q0(p, cg / p.CPG);
+    }
+    const bool col_ok = (cg < p.NC) && (cg % p.CPG < p.G * k1c);
 
     bf16x8 qv[KK];
-    if (cg < p.NC) {
-        const int bb = cg / p.CPG, cl = cg % p.CPG;
-        const int hh = cl / K1, j = cl % K1;
+    if (col_ok) {
+        const int cl = cg % p.CPG;
+        const int hh = cl / k1c, j = cl % k1c;
         const uint16_t* qp =
-            p.q + ((static_cast<size_t>(bb) * K1 + j) * p.Hq + g * p.G + hh) * D + kg * 8;
+            p.q + (static_cast<size_t>(q0c + j) * p.Hq + g * p.G + hh) * D + kg * 8;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) qv[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
     } else {
@@ -682,7 +712,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p, int mo
     __shared__ int sb, scc;
     const int tid = threadIdx.x;
     const int g = blockIdx.y, x = blockIdx.x;
-    const int K1 = p.K + 1, D = p.D;
+    const int D = p.D;
     const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
     int b = 0, t_begin, t_end, ncols, L = 0;
     int64_t kv0 = 0;
@@ -695,8 +725,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p, int mo
         L = max(p.kv_len[b], 0);
         kv0 = p.kv_start[b];
         t_begin = scc * p.chunk;
-        t_end = min(L + K1, t_begin + p.chunk);
-        ncols = p.CPG;
+        t_end = min(L + seq_k1(p, b), t_begin + p.chunk);
+        ncols = p.G * seq_k1(p, b);
     } else {
         t_begin = x * p.prefix_chunk;
         t_end = min(p.prefix_len, t_begin + p.prefix_chunk);
@@ -707,13 +737,15 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p, int mo
         if (mode == 1)
             return (v ? p.vpf : p.kpf) + static_cast<size_t>(t) * row_stride + static_cast<size_t>(g) * D;
         return (t < L) ? (v ? p.vcf : p.kcf) + static_cast<size_t>(kv0 + t) * row_stride + static_cast<size_t>(g) * D
-                       : (v ? p.vnf : p.knf) + static_cast<size_t>(b * K1 + t - L) * row_stride + static_cast<size_t>(g) * D;
+                       : (v ? p.vnf : p.knf) + static_cast<size_t>(seq_q0(p, b) + t - L) * row_stride + static_cast<size_t>(g) * D;
     };
     for (int col = 0; col < ncols; ++col) {
         int bb = b, cl = col;
         if (mode == 1) { bb = col / p.CPG; cl = col % p.CPG; }
-        const int hh = cl / K1, j = cl % K1;
-        const float* qp = p.qf + ((static_cast<size_t>(bb) * K1 + j) * p.Hq + g * p.G + hh) * D;
+        const int k1 = seq_k1(p, bb);
+        if (cl >= p.G * k1) continue;  // uniform: a padding column of a shorter sequence
+        const int hh = cl / k1, j = cl % k1;
+        const float* qp = p.qf + (static_cast<size_t>(seq_q0(p, bb) + j) * p.Hq + g * p.G + hh) * D;
         const int lim = (mode == 1) ? t_end : min(t_end, L + j + 1);
         float lm = -INFINITY;
         for (int i = tid; i < nk; i += kThreads) {
@@ -763,12 +795,21 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnParams p, int mo
 // grid: one block per (row, head); threads over the head dim.
 __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
     const int r = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
-    const int K1 = p.K + 1;
-    const int b = r / K1, j = r % K1;
+    int b = r / (p.K + 1);
+    if (p.cu_q) {  // largest b with cu_q[b] <= r
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.cu_q[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+    }
+    const int k1 = seq_k1(p, b);
+    const int j = min(r - seq_q0(p, b), k1 - 1);
     const int g = h / p.G, hh = h % p.G;
-    const int col = hh * K1 + j;
+    const int col = hh * k1 + j;
     const int L = max(p.kv_len[b], 0);
-    int n = ceil_div(L + K1, p.chunk);
+    int n = ceil_div(L + k1, p.chunk);
     int base = p.seq_base[b];
     // A device length above the host bound has no work items (status 3 is set
     // by the chunk kernel); keep every read inside the partial buffers.
@@ -852,9 +893,14 @@ int sk_resident_grid(int D, int nct) {
 }  // namespace
 
 AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
-                   const int32_t* kv_len_host, int prefix_len) {
+                   const int32_t* kv_len_host, const int32_t* cu_q_host, int prefix_len) {
     AttnPlan pl{};
     const int K1 = K + 1;
+    // keys of sequence b: its cached rows and its K_b + 1 new rows
+    auto keys = [&](int b) -> long long {
+        const long long L = kv_len_host[b] > 0 ? kv_len_host[b] : 0;
+        return L + (cu_q_host ? cu_q_host[b + 1] - cu_q_host[b] : K1);
+    };
     const size_t CPG = static_cast<size_t>(Hq / Hkv) * K1;
     const size_t NC = CPG * B;
     int pchunk = env_int("SPECVERIFY_PREFIX_CHUNK", 1024);
@@ -871,18 +917,15 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
         // slices per sequence for the host bound
         int smax = 1;
         for (int b = 0; b < B; ++b) {
-            const long long L = kv_len_host[b] > 0 ? kv_len_host[b] : 0;
-            if (L + K1 > kSkMaxKeys) pl.ok = false;
-            const int sb = static_cast<int>((std::min<long long>(L, kSkMaxKeys) + K1 + 15) / 16);
+            if (keys(b) > kSkMaxKeys) pl.ok = false;
+            const int sb = static_cast<int>((std::min<long long>(keys(b), kSkMaxKeys) + 15) / 16);
             smax = sb > smax ? sb : smax;
         }
         if (B > kSkMaxB) pl.ok = false;
         auto items_for = [&](int lam) {
             long long n = 0;
-            for (int b = 0; b < B; ++b) {
-                const long long L = kv_len_host[b] > 0 ? std::min<long long>(kv_len_host[b], kSkMaxKeys) : 0;
-                n += ((L + K1 + 15) / 16 + lam - 1) / lam;
-            }
+            for (int b = 0; b < B; ++b)
+                n += ((std::min<long long>(keys(b), kSkMaxKeys) + 15) / 16 + lam - 1) / lam;
             return n * Hkv;
         };
         const int nct = static_cast<int>((CPG + 15) / 16);
@@ -912,24 +955,24 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
             chunk = 64;
             for (int c = 1024; c >= 64; c >>= 1) {
                 long long items = 0;
-                for (int b = 0; b < B; ++b)
-                    items += ((kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1 + c - 1) / c;
+                for (int b = 0; b < B; ++b) items += (keys(b) + c - 1) / c;
                 if (items * Hkv >= 1024) { chunk = c; break; }
             }
         }
         chunk = (chunk + 63) / 64 * 64;
         if (chunk > 1024) chunk = 1024;
-        for (int b = 0; b < B; ++b)
-            slots += ((kv_len_host[b] > 0 ? kv_len_host[b] : 0) + K1 + chunk - 1) / chunk;
+        for (int b = 0; b < B; ++b) slots += (keys(b) + chunk - 1) / chunk;
         if (slots > (1LL << 30)) pl.ok = false;
         slots *= Hkv;  // the fp32 partials are per (slot, kv head)
     }
+    // The arrival counters come first: their place depends on B and Hkv only,
+    // so calls with other lengths or draft counts never put data over them.
     size_t off = 0;
     auto take = [&](size_t n) { off = (off + 255) & ~static_cast<size_t>(255); off += n; };
+    take(static_cast<size_t>(B) * Hkv * 4);
+    take(static_cast<size_t>(B) * 4);
     take(static_cast<size_t>(slots) * CPG * D * 4);
     take(static_cast<size_t>(slots) * CPG * 8);
-    take(static_cast<size_t>(B) * 4);
-    take(static_cast<size_t>(B) * Hkv * 4);
     take(static_cast<size_t>(pslots) * Hkv * NC * D * 4);
     take(static_cast<size_t>(pslots) * Hkv * NC * 8);
     pl.chunk = chunk;
@@ -960,6 +1003,8 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
     p.kv_len = a.kv_len;
     p.out = a.out;
     p.status = a.status;
+    p.cu_q = a.cu_q;
+    p.rows = a.rows;
     p.B = a.B;
     p.K = a.K;
     p.Hq = a.Hq;
@@ -987,10 +1032,10 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
     };
     const size_t CPG = p.CPG, NC = p.NC;
     const size_t pslots_all = a.bf16 ? static_cast<size_t>(pl.slots) : static_cast<size_t>(pl.slots) * a.Hkv;
+    p.merge_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * a.Hkv * 4));
+    p.seq_base = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * 4));
     p.part_o = reinterpret_cast<float*>(take(pslots_all * CPG * a.D * 4));
     p.part_ml = reinterpret_cast<float2*>(take(pslots_all * CPG * 8));
-    p.seq_base = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * 4));
-    p.merge_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * a.Hkv * 4));
     p.pre_o = reinterpret_cast<float*>(take(static_cast<size_t>(pl.prefix_slots) * a.Hkv * NC * a.D * 4));
     p.pre_ml = reinterpret_cast<float2*>(take(static_cast<size_t>(pl.prefix_slots) * a.Hkv * NC * 8));
 
@@ -1053,7 +1098,7 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
     if (e != hipSuccess) return e;
     if (a.bf16) return hipSuccess;  // the chunk kernel merges in its last workgroup
     const int mthreads = a.D <= 64 ? 64 : (a.D <= 128 ? 128 : 256);
-    hipLaunchKernelGGL(merge_kernel, dim3(a.B * (a.K + 1) * a.Hq), dim3(mthreads), 0, stream, p);
+    hipLaunchKernelGGL(merge_kernel, dim3(a.rows * a.Hq), dim3(mthreads), 0, stream, p);
     return hipGetLastError();
 }
 

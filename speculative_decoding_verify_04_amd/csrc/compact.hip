@@ -5,9 +5,12 @@
 // are handled without padding tokens, so no extra memory or compute is spent.
 // With e_b = n_b + 1 tokens emitted by sequence b ("Accelerating Large Language
 // Model Decoding with Speculative Sampling", "Modified rejection sampling": at
-// least one and at most K+1 tokens per round):
-//   cu = exclusive scan of e;  packed[cu_b + i] = out_tokens[b, i];
-//   cache rows L_b .. L_b + n_b of b <- new rows 0 .. n_b;  L_b += e_b.
+// least one and at most K_b+1 tokens per round):
+//   cu = exclusive scan of e;  packed[cu_b + i] = out_tokens[q_b + i];
+//   cache rows L_b .. L_b + n_b of b <- new rows q_b .. q_b + n_b;  L_b += e_b,
+// where q_b is the first row of sequence b: cu_q[b] with ragged draft lengths
+// K_b = cu_q[b+1] - cu_q[b] - 1 (EMS-SD's samples with different numbers of
+// prediction tokens, unpadded), else b*(K+1).
 // One workgroup of 1024 threads per sequence; it computes its own scan offset,
 // so the kernel needs no cross-workgroup synchronisation.
 #include "sv_device.h"
@@ -19,6 +22,14 @@ namespace {
 constexpr int kThreads = 1024;
 
 __device__ __forceinline__ int emitted(int n, int K) { return (n >= 0 && n <= K) ? n + 1 : 0; }
+
+// First row and draft length of sequence b.
+__device__ __forceinline__ int seq_q0(const CompactArgs& a, int b) {
+    return a.cu_q ? a.cu_q[b] : b * (a.K + 1);
+}
+__device__ __forceinline__ int seq_k(const CompactArgs& a, int b) {
+    return a.cu_q ? max(a.cu_q[b + 1] - a.cu_q[b] - 1, 0) : a.K;
+}
 
 // Copy `n16` 16-byte words of K and of V with every load of a batch issued
 // before its stores: the copy takes one memory round trip per batch.  Indices
@@ -41,19 +52,20 @@ __device__ __forceinline__ void copy_rows16(const uint4* ks, const uint4* vs, ui
 __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     __shared__ int red[kThreads / 64];
     const int b = blockIdx.x, tid = threadIdx.x;
-    const int K1 = a.K + 1;
     // independent loads, issued together
     const int nb = a.n_accepted[b];
     const int L = a.kv_len[b];
     const int64_t start = a.kv_start[b];
+    const int q0 = seq_q0(a, b);
+    const int kb = seq_k(a, b);
     int part = 0;
-    for (int i = tid; i < b; i += kThreads) part += emitted(a.n_accepted[i], a.K);
-    const int e = emitted(nb, a.K);
+    for (int i = tid; i < b; i += kThreads) part += emitted(a.n_accepted[i], seq_k(a, i));
+    const int e = emitted(nb, kb);
     if (tid == 0 && e == 0) set_status(a.status, 4);
 
     const size_t row_bytes = static_cast<size_t>(a.Hkv) * a.D * a.elem_bytes;
     const size_t dst0 = static_cast<size_t>(start + L) * row_bytes;
-    const size_t src0 = static_cast<size_t>(b) * K1 * row_bytes;
+    const size_t src0 = static_cast<size_t>(q0) * row_bytes;
     const size_t nbytes = static_cast<size_t>(e) * row_bytes;
     if (row_bytes % 16 == 0) {
         copy_rows16(reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_new) + src0),
@@ -79,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
         a.kv_len[b] = L + e;
     }
     for (int i = tid; i < e; i += kThreads)
-        a.tokens_packed[cu + i] = a.out_tokens[static_cast<size_t>(b) * K1 + i];
+        a.tokens_packed[cu + i] = a.out_tokens[static_cast<size_t>(q0) + i];
 }
 
 }  // namespace

@@ -19,7 +19,9 @@ struct AttnArgs {
     const void* v_prefix;
     void* out;
     int32_t* status;
-    int B, K, Hq, Hkv, D, bf16, prefix_len;
+    const int32_t* cu_q;  // ragged draft lengths: [B+1] device query-row offsets, or null
+    int rows;             // query rows in all
+    int B, K, Hq, Hkv, D, bf16, prefix_len;  // K: the largest draft length when ragged
     float scale;
     int chunk;          // keys per split-K work item of the per-sequence part
     int prefix_chunk;   // keys per work item of the shared prefix
@@ -37,8 +39,10 @@ struct AttnPlan {
     bool ok;  // false: the sequences are too long for the merge (unsupported)
 };
 
+// cu_q_host: [B+1] host query-row offsets of ragged draft lengths (K = their
+// largest K_b), or null for K drafts in every sequence.
 AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
-                   const int32_t* kv_len_host, int prefix_len);
+                   const int32_t* kv_len_host, const int32_t* cu_q_host, int prefix_len);
 hipError_t attn_launch(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
 
 // ---------------------------------------------------------------- sampler
@@ -52,11 +56,14 @@ struct AcceptArgs {
     int32_t* out_tokens;
     int32_t* status;
     void* workspace;
-    int B, K, V, bf16, greedy;
+    const int32_t* cu_q;  // ragged draft lengths: [B+1] device target-row offsets, or null
+    int nt;               // target rows: cu_q[B], or B*(K+1)
+    int B, K, V, bf16, greedy;  // K: the largest draft length when ragged
     float temperature, top_p;
 };
 
-size_t accept_workspace_bytes(int B, int K, int V);
+// nt: target rows in all (B*(K+1) without ragged draft lengths)
+size_t accept_workspace_bytes(int B, long long nt, int V);
 int accept_max_vocab();
 int accept_max_drafts();
 hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream);
@@ -74,7 +81,8 @@ struct CompactArgs {
     int32_t* tokens_packed;
     int32_t* cu_tokens;
     int32_t* status;
-    int B, K, Hkv, D, elem_bytes;
+    const int32_t* cu_q;  // ragged draft lengths: [B+1] device row offsets, or null
+    int B, K, Hkv, D, elem_bytes;  // K: unused when ragged
 };
 
 hipError_t compact_launch(const CompactArgs& a, hipStream_t stream);

@@ -69,3 +69,43 @@ def to_device(w: W.Workload, device, logits_dtype=torch.float32) -> DeviceStep:
         cu_tokens=torch.zeros(B + 1, dtype=torch.int32, device=device),
         status=torch.zeros(1, dtype=torch.int32, device=device),
     )
+
+
+@dataclasses.dataclass
+class RaggedDeviceStep(DeviceStep):
+    cu_q: Optional[torch.Tensor] = None
+    cu_q_host: Optional[list] = None
+
+
+def ragged_to_device(rw: W.RaggedWorkload, device, logits_dtype=torch.float32) -> RaggedDeviceStep:
+    """Device tensors of a ragged-draft-length workload (rows packed by cu_q)."""
+    w = rw.base
+    B = w.cfg.B
+    NT = int(rw.cu_q[-1])
+    q = kv_tensor(rw.q, device)
+    kp = kv_tensor(w.k_prefix, device) if w.k_prefix is not None else None
+    vp = kv_tensor(w.v_prefix, device) if w.v_prefix is not None else None
+    return RaggedDeviceStep(
+        q=q,
+        k_cache=kv_tensor(w.k_cache, device),
+        v_cache=kv_tensor(w.v_cache, device),
+        kv_start=torch.from_numpy(w.kv_start).to(device),
+        kv_len=torch.from_numpy(w.kv_len).to(device),
+        k_new=kv_tensor(rw.k_new, device),
+        v_new=kv_tensor(rw.v_new, device),
+        k_prefix=kp,
+        v_prefix=vp,
+        out=torch.empty_like(q),
+        target_logits=torch.from_numpy(rw.target_logits).to(device).to(logits_dtype),
+        draft_logits=torch.from_numpy(rw.draft_logits).to(device).to(logits_dtype),
+        draft_tokens=torch.from_numpy(rw.draft_tokens).to(device),
+        u_accept=torch.from_numpy(rw.u_accept).to(device),
+        u_sample=torch.from_numpy(w.u_sample).to(device),
+        n_accepted=torch.full((B,), -7, dtype=torch.int32, device=device),
+        out_tokens=torch.full((NT,), -7, dtype=torch.int32, device=device),
+        tokens_packed=torch.full((NT,), -1, dtype=torch.int32, device=device),
+        cu_tokens=torch.zeros(B + 1, dtype=torch.int32, device=device),
+        status=torch.zeros(1, dtype=torch.int32, device=device),
+        cu_q=torch.from_numpy(rw.cu_q).to(device),
+        cu_q_host=[int(x) for x in rw.cu_q],
+    )

@@ -285,6 +285,54 @@ def make_workload(cfg: Config, sub_seed: int = 0, growth_rows: int = 0,
                     u_accept=u_accept, u_sample=u_sample)
 
 
+@dataclasses.dataclass
+class RaggedWorkload:
+    """Sequence b carries its own draft length K_b <= K: the first K_b + 1 query
+    rows, new K/V rows and target rows, and the first K_b drafts, draft rows
+    and accept uniforms of sequence b of a uniform workload, packed back to
+    back without padding (row offsets cu_q).  Caches, lengths, prefix and
+    u_sample are the base workload's."""
+    base: Workload
+    kb: np.ndarray             # [B] int32 draft length of each sequence
+    cu_q: np.ndarray           # [B+1] int32: rows of sequence b are cu_q[b] .. cu_q[b+1]-1
+    q: np.ndarray              # [cu_q[B], Hq, D]
+    k_new: np.ndarray          # [cu_q[B], Hkv, D]
+    v_new: np.ndarray
+    target_logits: np.ndarray  # [cu_q[B], V]
+    draft_logits: np.ndarray   # [cu_q[B] - B, V]
+    draft_tokens: np.ndarray   # [cu_q[B] - B]
+    u_accept: np.ndarray       # [cu_q[B] - B]
+
+    @property
+    def cfg(self) -> Config:
+        return self.base.cfg
+
+
+def ragged_draft_lengths(cfg: Config, sub_seed: int = 0) -> np.ndarray:
+    """Seeded draft lengths K_b, uniform on 0..K (their own seed stream)."""
+    rng = np.random.default_rng(np.random.SeedSequence([cfg.seed, sub_seed, 0x4B62]))
+    return rng.integers(0, cfg.K + 1, size=cfg.B).astype(np.int32)
+
+
+def make_ragged(w: Workload, kb) -> RaggedWorkload:
+    c = w.cfg
+    B, K, V = c.B, c.K, c.V
+    kb = np.asarray(kb, dtype=np.int32)
+    assert kb.shape == (B,) and np.all(kb >= 0) and np.all(kb <= K)
+    cu = np.concatenate([[0], np.cumsum(kb.astype(np.int64) + 1)]).astype(np.int32)
+    iq = np.concatenate([b * (K + 1) + np.arange(kb[b] + 1) for b in range(B)])
+    idr = np.concatenate([b * K + np.arange(kb[b]) for b in range(B)]).astype(np.int64)
+    return RaggedWorkload(
+        base=w, kb=kb, cu_q=cu,
+        q=np.ascontiguousarray(w.q[iq]) if w.q.shape[0] == B * (K + 1) else w.q,
+        k_new=np.ascontiguousarray(w.k_new[iq]) if w.k_new.shape[0] == B * (K + 1) else w.k_new,
+        v_new=np.ascontiguousarray(w.v_new[iq]) if w.v_new.shape[0] == B * (K + 1) else w.v_new,
+        target_logits=np.ascontiguousarray(w.target_logits.reshape(B * (K + 1), V)[iq]),
+        draft_logits=np.ascontiguousarray(w.draft_logits.reshape(B * K, V)[idr]),
+        draft_tokens=np.ascontiguousarray(w.draft_tokens.reshape(B * K)[idr]),
+        u_accept=np.ascontiguousarray(w.u_accept.reshape(B * K)[idr]))
+
+
 def algorithmic_bytes(cfg: Config, kv_len: np.ndarray, prefix_len: int = 0) -> dict:
     """Bytes the verify step must move at least once, by part.
 

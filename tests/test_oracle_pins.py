@@ -314,3 +314,118 @@ def test_bifurcated_prefix_equals_concatenated():
     o_cat = R.verify_attn(w.q, kc, vc, starts, caps.astype(np.int32), w.k_new, w.v_new,
                           c.B, c.K, c.Hq, c.Hkv, c.D)
     np.testing.assert_allclose(o_bif, o_cat, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- ragged draft lengths
+#
+# "EMS-SD" (abstract): samples with different numbers of prediction tokens,
+# unpadded.  The ragged oracle applies the uniform one per sequence on packed
+# rows; these pins check the packing against the uniform oracle, a numpy
+# brute force over the packed layout, and the stopping rule.
+
+RAGGED = W.small_variant(W.CONFIGS["gqa_b64k8"], B=6, K=5, Hq=4, Hkv=2, D=32, len_kind="uniform", len_lo=0,
+                         len_hi=40, V=300, prefix_len=0)
+
+
+def _ragged(kb, cfg=RAGGED, seed=3):
+    return W.make_ragged(W.make_workload(cfg, sub_seed=seed), kb)
+
+
+def test_ragged_with_equal_lengths_is_the_uniform_oracle():
+    c = RAGGED
+    w = W.make_workload(c, sub_seed=3)
+    rw = W.make_ragged(w, np.full(c.B, c.K, np.int32))
+    assert np.array_equal(rw.cu_q, np.arange(c.B + 1) * (c.K + 1))
+    a_u = R.workload_attn(w)
+    a_r = R.verify_attn_ragged(rw.q, w.k_cache, w.v_cache, w.kv_start, w.kv_len, rw.k_new,
+                               rw.v_new, rw.cu_q, c.Hq, c.Hkv, c.D)
+    assert np.array_equal(a_u, a_r)
+    s_u = R.workload_accept(w)
+    s_r = R.accept_ragged(rw.target_logits, rw.draft_logits, rw.draft_tokens, rw.u_accept,
+                          w.u_sample, rw.cu_q, c.temperature, c.top_p)
+    assert np.array_equal(s_u["n_accepted"], s_r["n_accepted"])
+    assert np.array_equal(s_u["out_tokens"].reshape(-1), s_r["out_tokens"])
+    p_u = R.compact_kv(s_u["n_accepted"], s_u["out_tokens"], w.kv_len, w.kv_start, w.k_cache,
+                       w.v_cache, w.k_new, w.v_new, c.K, c.Hkv, c.D)
+    p_r = R.compact_kv_ragged(s_r["n_accepted"], s_r["out_tokens"], w.kv_len, w.kv_start,
+                              w.k_cache, w.v_cache, rw.k_new, rw.v_new, rw.cu_q, c.Hkv, c.D)
+    for x, y in zip(p_u[1:], p_r[1:]):
+        assert np.array_equal(x, y)
+    assert np.array_equal(p_u[0][: p_u[1][-1]], p_r[0][: p_r[1][-1]])
+
+
+def test_ragged_attention_brute_force():
+    """Query j of sequence b (packed row cu_q[b] + j) against a float64 numpy
+    softmax over its cache rows and the new rows cu_q[b] .. cu_q[b] + j."""
+    c = RAGGED
+    rw = _ragged(np.array([0, 5, 2, 3, 0, 1], np.int32))
+    w = rw.base
+    o = R.verify_attn_ragged(rw.q, w.k_cache, w.v_cache, w.kv_start, w.kv_len, rw.k_new,
+                             rw.v_new, rw.cu_q, c.Hq, c.Hkv, c.D)
+    q, kc, vc = R.kv_to_f64(rw.q), R.kv_to_f64(w.k_cache), R.kv_to_f64(w.v_cache)
+    kn, vn = R.kv_to_f64(rw.k_new), R.kv_to_f64(rw.v_new)
+    G = c.Hq // c.Hkv
+    for b in range(c.B):
+        s0, L = int(w.kv_start[b]), int(w.kv_len[b])
+        for j in range(int(rw.kb[b]) + 1):
+            r = int(rw.cu_q[b]) + j
+            for h in range(c.Hq):
+                g = h // G
+                keys = np.concatenate([kc[s0:s0 + L, g], kn[rw.cu_q[b]:r + 1, g]])
+                vals = np.concatenate([vc[s0:s0 + L, g], vn[rw.cu_q[b]:r + 1, g]])
+                s = keys @ q[r, h] / np.sqrt(c.D)
+                p = np.exp(s - s.max())
+                np.testing.assert_allclose(o[r, h], p @ vals / p.sum(), rtol=1e-12, atol=1e-12)
+
+
+def test_ragged_sampler_follows_the_stopping_rule():
+    """Sequence b with its first K_b drafts of a uniform round: the scan stops at
+    min(n_b, K_b) (same rows, same uniforms); when the uniform round rejected
+    before K_b, the residual draw is the same token; K_b = 0 emits the bonus
+    token of target row 0 alone; 1 <= emitted <= K_b + 1."""
+    c = RAGGED
+    for seed in range(4):
+        w = W.make_workload(c, sub_seed=seed)
+        kb = W.ragged_draft_lengths(c, seed)
+        rw = W.make_ragged(w, kb)
+        u = R.workload_accept(w)
+        r = R.accept_ragged(rw.target_logits, rw.draft_logits, rw.draft_tokens, rw.u_accept,
+                            w.u_sample, rw.cu_q, c.temperature, c.top_p)
+        for b in range(c.B):
+            nu, nr = int(u["n_accepted"][b]), int(r["n_accepted"][b])
+            assert nr == min(nu, int(kb[b]))
+            row = r["out_tokens"][rw.cu_q[b]:rw.cu_q[b + 1]]
+            assert np.all(row[:nr] == w.draft_tokens[b, :nr])
+            assert np.all(row[nr + 1:] == -1) and row[nr] >= 0
+            if nu < kb[b]:
+                assert row[nr] == u["out_tokens"][b, nu]
+        k0 = [b for b in range(c.B) if kb[b] == 0]
+        for b in k0:
+            one = R.accept(w.target_logits[b:b + 1, :1], w.draft_logits[b:b + 1, :0],
+                           w.draft_tokens[b:b + 1, :0], w.u_accept[b:b + 1, :0],
+                           w.u_sample[b:b + 1], c.temperature, c.top_p)
+            assert r["out_tokens"][rw.cu_q[b]] == one["out_tokens"][0, 0]
+
+
+def test_ragged_compaction_definition():
+    """cu = exclusive scan of n_b + 1; packed tokens; new rows cu_q[b] .. cu_q[b] + n_b
+    appended after row L_b of sequence b; kv_len += n_b + 1."""
+    c = RAGGED
+    rw = _ragged(np.array([3, 0, 5, 1, 2, 4], np.int32), seed=5)
+    w = rw.base
+    s = R.accept_ragged(rw.target_logits, rw.draft_logits, rw.draft_tokens, rw.u_accept,
+                        w.u_sample, rw.cu_q, c.temperature, c.top_p)
+    packed, cu, kl, kc, vc = R.compact_kv_ragged(s["n_accepted"], s["out_tokens"], w.kv_len,
+                                                 w.kv_start, w.k_cache, w.v_cache, rw.k_new,
+                                                 rw.v_new, rw.cu_q, c.Hkv, c.D)
+    e = s["n_accepted"].astype(np.int64) + 1
+    assert np.array_equal(cu, np.concatenate([[0], np.cumsum(e)]))
+    assert np.array_equal(kl, w.kv_len + e)
+    ek, ev = w.k_cache.copy(), w.v_cache.copy()
+    for b in range(c.B):
+        q0, s0, L = int(rw.cu_q[b]), int(w.kv_start[b]), int(w.kv_len[b])
+        assert np.array_equal(packed[cu[b]:cu[b + 1]], s["out_tokens"][q0:q0 + e[b]])
+        ek[s0 + L:s0 + L + e[b]] = rw.k_new[q0:q0 + e[b]]
+        ev[s0 + L:s0 + L + e[b]] = rw.v_new[q0:q0 + e[b]]
+    assert np.array_equal(kc.view(np.uint16), ek.view(np.uint16))
+    assert np.array_equal(vc.view(np.uint16), ev.view(np.uint16))
