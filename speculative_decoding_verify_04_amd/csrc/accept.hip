@@ -634,12 +634,12 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
             // chains; unused slots are masked), then added.
             const int kb_top = L.kb_top;
 #pragma unroll
-            for (int c0 = 0; c0 < kChunk; c0 += 8) {
-                double wv[8];
-                int ov[8];
-                bool in[8];
+            for (int c0 = 0; c0 < kChunk; c0 += 4) {
+                double wv[4];
+                int ov[4];
+                bool in[4];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
+                for (int u = 0; u < 4; ++u) {
                     const int c = c0 + u;
                     const float zc = entry_z(e[c]);
                     ov[u] = kb_top - bin_of(zc, p.bscale);
@@ -649,7 +649,7 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
                     wv[u] = weight(zc, m, p.invT, L.tab);
                 }
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
+                for (int u = 0; u < 4; ++u)
                     if (in[u]) atomicAdd(&L.hm[ov[u]], wv[u]);
             }
         }
