@@ -202,6 +202,63 @@ __device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_s
         return static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * p.Hkv;
     };
     const int group = max(1, min(ncols, kMergeLds / nparts));
+    if (np == 0 && nparts <= 8 && ncols * D <= 4 * kThreads && group == ncols) {
+        // Common case: every partial value this thread needs fits in registers.
+        // Its loads are issued before the (m, l) loads, so both travel in the
+        // same round trip; the weights are then formed in LDS as below.
+        const int nc = ncols, npairs = nc * D;
+        float ov[8][4];
+        int off[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int pq = min(tid + u * kThreads, npairs - 1);
+            off[u] = (pq / nc) * CPG + pq % nc;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const int j = min(jj, nparts - 1);  // past the end: re-read the last part
+            const float* pb = p.part_o + slot_of(j) * D * CPG;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) ov[jj][u] = ld_coh(pb + off[u]);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nparts * nc; idx += kThreads) {
+            const int j = idx / nc, col = idx % nc;
+            const unsigned long long u =
+                ld_coh(reinterpret_cast<const unsigned long long*>(p.part_ml + slot_of(j) * CPG + col));
+            M.ml[idx] = make_float2(__uint_as_float(static_cast<unsigned>(u)),
+                                    __uint_as_float(static_cast<unsigned>(u >> 32)));
+        }
+        __syncthreads();
+        for (int cl = tid; cl < nc; cl += kThreads) {
+            float ms = -INFINITY;
+            for (int j = 0; j < nparts; ++j) ms = fmaxf(ms, M.ml[j * nc + cl].x);
+            float l = 0.0f;
+            for (int j = 0; j < nparts; ++j) {
+                const float2 v = M.ml[j * nc + cl];
+                const float f = (v.x == -INFINITY) ? 0.0f : exp2f(v.x - ms);
+                M.w[j * nc + cl] = f;
+                l += v.y * f;
+            }
+            const float inv = 1.0f / l;
+            for (int j = 0; j < nparts; ++j) M.w[j * nc + cl] *= inv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int pq = tid + u * kThreads;
+            if (pq >= npairs) continue;
+            const int cl = pq % nc, d = pq / nc;
+            float acc = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                if (jj < nparts) acc += ov[jj][u] * M.w[jj * nc + cl];
+            const int hh = cl / k1, j = cl % k1;
+            const size_t oi = (static_cast<size_t>(qrow0 + j) * p.Hq + g * p.G + hh) * D + d;
+            static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(acc);
+        }
+        return;
+    }
     for (int c0 = 0; c0 < ncols; c0 += group) {
         const int nc = min(group, ncols - c0);
         __syncthreads();
