@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--k-sweep", default=None,
                     help="comma-separated draft lengths: time the step and each entry point "
                          "per K on the workload's shape (one JSON line per K)")
+    ap.add_argument("--sampler-variants", action="store_true",
+                    help="time spec_accept alone under its filter and logit-type variants "
+                         "(one JSON line each)")
     ap.add_argument("--ragged", action="store_true",
                     help="time the step with ragged draft lengths K_b ~ U{0..K} (one JSON line)")
     ap.add_argument("--traffic-from", default=None,
@@ -162,6 +165,9 @@ def main():
         return
     if args.ragged:
         ragged_bench(args)
+        return
+    if args.sampler_variants:
+        sampler_variants(args)
         return
 
     import numpy as np
@@ -557,6 +563,69 @@ def ragged_bench(args):
         "step_hbm_frac_at_start_lengths": round((attn_b + acc_b) / (step_us * 1e-6) / 1e9
                                                 / HBM_PEAK_GBS, 4),
     }), flush=True)
+
+
+def sampler_variants(args):
+    """spec_accept alone on the workload's logits under each filter / logit-type
+    variant: graph of `steps` calls over rotating input sets; bytes = every
+    logit row read once (target rows only when greedy)."""
+    import torch
+
+    from speculative_decoding_verify_04_amd import api
+    from speculative_decoding_verify_04_amd import workloads as W
+    from speculative_decoding_verify_04_amd.devio import to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    base = W.CONFIGS[args.config]
+    steps, S = args.steps, min(args.sets, 4)
+    cap_stream = torch.cuda.Stream()
+    variants = [
+        ("fp32 logits, T, nucleus (the workload)", {}, torch.float32, 0),
+        ("bf16 logits, T, nucleus", {}, torch.bfloat16, 0),
+        ("fp32 logits, T, top-k 50", {"top_p": 1.0}, torch.float32, 50),
+        ("fp32 logits, T, top-k 50, nucleus", {}, torch.float32, 50),
+        ("fp32 logits, T, no filter", {"top_p": 1.0}, torch.float32, 0),
+        ("fp32 logits, greedy", {"greedy": True}, torch.float32, 0),
+    ]
+    for name, over, ldt, top_k in variants:
+        cfg = W.small_variant(base, **over)
+        sets = [W.make_workload(cfg, sub_seed=s, with_kv=False) for s in range(S)]
+        ds = [to_device(w, dev, logits_dtype=ldt) for w in sets]
+        wacc = torch.zeros(api.spec_accept_workspace_size(cfg.B, cfg.K, cfg.V), dtype=torch.uint8,
+                           device=dev)
+
+        def call(s):
+            t = ds[s]
+            api.spec_accept(t.target_logits, None if cfg.greedy else t.draft_logits,
+                            t.draft_tokens, t.u_accept, t.u_sample, cfg.temperature, cfg.top_p,
+                            cfg.greedy, t.n_accepted, t.out_tokens, status=t.status,
+                            workspace=wacc, top_k=top_k)
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for i in range(steps):
+                call(i % S)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        for t in ds:
+            st = int(t.status.item())
+            assert st == 0, f"{name}: device status {st}"
+        rows = cfg.B * (cfg.K + 1) + (0 if cfg.greedy else cfg.B * cfg.K)
+        nbytes = rows * cfg.V * (2 if ldt == torch.bfloat16 else 4)
+        print(json.dumps({"sampler_variant": name, "config": cfg.name, "top_k": top_k,
+                          "top_p": cfg.top_p, "greedy": cfg.greedy, "steps": steps,
+                          "accept_us": round(us, 2), "logit_bytes": nbytes,
+                          "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}), flush=True)
+        del ds, wacc
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(sets, cfg, budget_s):

@@ -240,6 +240,28 @@ int spec_accept_ragged(const void* target_logits, const void* draft_logits, int 
                        int32_t* out_tokens, int32_t* status, void* workspace,
                        size_t workspace_bytes, sv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * spec_accept_ex -- spec_accept / spec_accept_ragged with a top-k filter.
+ *
+ * [SpS] "Modified rejection sampling": standard sampling methods such as
+ * top-k and nucleus modify the probabilities before the scheme, for q and p
+ * alike.  Order: temperature, then top-k, then nucleus:
+ *   top-k (0 < top_k < V): keep the tokens whose logit is >= the top_k-th
+ *          largest logit of the row (ties at the boundary are all kept),
+ *          renormalised; the nucleus then works on that distribution.
+ * top_k = 0 (or >= V) turns it off; greedy ignores it (the argmax is kept).
+ * cu_q = cu_q_host = NULL: K drafts in every sequence, the layouts of
+ * spec_accept (workspace: spec_accept_workspace_size).  Otherwise the ragged
+ * layouts of spec_accept_ragged, K unused (workspace:
+ * spec_accept_ragged_workspace_size).  Every other argument as there.
+ * ------------------------------------------------------------------------ */
+int spec_accept_ex(const void* target_logits, const void* draft_logits, int logits_dtype,
+                   const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                   const int32_t* cu_q, const int32_t* cu_q_host, int B, int K, int V,
+                   float temperature, float top_p, int top_k, int greedy, int32_t* n_accepted,
+                   int32_t* out_tokens, int32_t* status, void* workspace,
+                   size_t workspace_bytes, sv_stream_t stream);
+
 int spec_compact_kv_ragged(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
                            const int64_t* kv_start, void* k_cache, void* v_cache,
                            const void* k_new, const void* v_new, int32_t* tokens_packed,

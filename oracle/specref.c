@@ -24,6 +24,8 @@
  *   - Grouped heads are contiguous: kv head g = h / (Hq / Hkv).
  *   - Temperature, then nucleus, are applied to both q and p before the scheme.
  *   - Nucleus keeps the smallest tie-closed top set whose mass is >= top_p.
+ *   - Top-k (when asked for) comes after temperature and before nucleus and
+ *     keeps the k most probable tokens and every tie of the k-th.
  *   - Accept iff u * p < q; if p == 0, accept iff q > 0.
  *   - The draw takes the smallest token id i with u * S < C_i (C = running sum
  *     of the weights in ascending token order, S = C_{V-1}).  If the residual
@@ -187,15 +189,19 @@ static int by_prob_desc(const void *x, const void *y) {
 
 /*
  * The distribution the scheme uses for one row of logits z[0..V):
- * temperature first, then nucleus ([SpS]: standard sampling methods modify
- * the probabilities before the rejection scheme is applied).
+ * temperature first, then top-k, then nucleus ([SpS]: standard sampling
+ * methods -- it names top-k and nucleus -- modify the probabilities before the
+ * rejection scheme is applied).
  *   d_t = z_t - max z ; x_t = d_t / T ; pi_t = exp(x_t) / sum_s exp(x_s)
+ *   top-k (0 < top_k < V): keep {t : pi_t >= the top_k-th largest pi} (ties
+ *            at the boundary kept), renormalised.
  *   nucleus: tau = the largest value among {pi_t} with sum_{pi_s >= tau} pi_s
  *            >= top_p; keep {t : pi_t >= tau}; pi'_t = pi_t / kept mass.
  * *ambiguous is set when the mass of the kept set, or of the set just above
- * its boundary tie group, is within NUCLEUS_MARGIN of top_p.
+ * its boundary tie group, is within NUCLEUS_MARGIN of top_p.  (The top-k set
+ * is decided by exact comparisons of the logits: never ambiguous.)
  */
-static int row_dist(const float *z, int V, double T, double top_p, double *pi,
+static int row_dist(const float *z, int V, double T, int top_k, double top_p, double *pi,
                     int *ambiguous) {
     double m = -INFINITY;
     for (int t = 0; t < V; ++t)
@@ -207,7 +213,8 @@ static int row_dist(const float *z, int V, double T, double top_p, double *pi,
     }
     for (int t = 0; t < V; ++t) pi[t] /= S;
     *ambiguous = 0;
-    if (!(top_p < 1.0)) return SPECREF_OK;
+    const int use_k = top_k > 0 && top_k < V;
+    if (!(top_p < 1.0) && !use_k) return SPECREF_OK;
 
     prob_id *srt = (prob_id *)malloc(sizeof(prob_id) * (size_t)V);
     if (!srt) return SPECREF_ENOMEM;
@@ -216,6 +223,20 @@ static int row_dist(const float *z, int V, double T, double top_p, double *pi,
         srt[t].id = t;
     }
     qsort(srt, (size_t)V, sizeof(prob_id), by_prob_desc);
+
+    if (use_k) {
+        /* keep the top_k largest probabilities and every tie of the last one */
+        const double tk = srt[top_k - 1].pi;
+        double mass = 0.0;
+        for (int t = 0; t < V; ++t)
+            if (pi[t] >= tk) mass += pi[t];
+        for (int t = 0; t < V; ++t) pi[t] = pi[t] >= tk ? pi[t] / mass : 0.0;
+        for (int i = 0; i < V; ++i) srt[i].pi = pi[srt[i].id];
+        if (!(top_p < 1.0)) {
+            free(srt);
+            return SPECREF_OK;
+        }
+    }
 
     /* walk tie groups from the top; stop at the first group whose inclusion
      * brings the mass to >= top_p */
@@ -289,10 +310,11 @@ static int draw(const double *w, int V, double u, int *ambiguous) {
 int specref_accept(const float *target_logits, const float *draft_logits,
                    const int32_t *draft_tokens, const float *u_accept,
                    const float *u_sample, int B, int K, int V, double temperature,
-                   double top_p, int greedy, int32_t *n_accepted, int32_t *out_tokens,
+                   double top_p, int top_k, int greedy, int32_t *n_accepted, int32_t *out_tokens,
                    double *q_tok, double *p_tok, int32_t *flag_pos,
                    int64_t *n_decisions, int64_t *n_flagged) {
-    if (B < 0 || K < 0 || V < 1 || !(temperature > 0.0) || !(top_p > 0.0) || top_p > 1.0)
+    if (B < 0 || K < 0 || V < 1 || !(temperature > 0.0) || !(top_p > 0.0) || top_p > 1.0 ||
+        top_k < 0)
         return SPECREF_EINVAL;
     for (int i = 0; i < B * K; ++i)
         if (draft_tokens[i] < 0 || draft_tokens[i] >= V) return SPECREF_EINVAL;
@@ -331,7 +353,7 @@ int specref_accept(const float *target_logits, const float *draft_logits,
         } else {
             int amb, rc;
             for (int j = 0; j <= K; ++j) {
-                rc = row_dist(zt + (size_t)j * V, V, temperature, top_p, q, &amb);
+                rc = row_dist(zt + (size_t)j * V, V, temperature, top_k, top_p, q, &amb);
                 if (rc) goto fail;
                 if (top_p < 1.0) {
                     decisions++;
@@ -344,7 +366,7 @@ int specref_accept(const float *target_logits, const float *draft_logits,
                     if (amb) { flagged++; if (first_flag < 0) first_flag = K; }
                     break;
                 }
-                rc = row_dist(zd + (size_t)j * V, V, temperature, top_p, p, &amb);
+                rc = row_dist(zd + (size_t)j * V, V, temperature, top_k, top_p, p, &amb);
                 if (rc) goto fail;
                 if (top_p < 1.0) {
                     decisions++;

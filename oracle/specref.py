@@ -85,12 +85,13 @@ def verify_attn(q, k_cache, v_cache, kv_start, kv_len, k_new, v_new, B, K, Hq, H
 
 
 def accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature,
-           top_p, greedy=False, lib_=None):
+           top_p, greedy=False, lib_=None, top_k=0):
     """One verify round of modified rejection sampling per sequence.
 
     Returns a dict with n_accepted [B], out_tokens [B, K+1], q_tok/p_tok [B, K],
     flag_pos [B], n_decisions, n_flagged.  ``temperature`` and ``top_p`` are
-    rounded to float32 first, as the GPU library receives them.
+    rounded to float32 first, as the GPU library receives them; ``top_k`` > 0
+    keeps the k most probable tokens (and ties) before the nucleus.
     """
     tl = _c(target_logits, np.float32)
     B, K1, V = tl.shape
@@ -111,7 +112,7 @@ def accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temper
     rc = lib(lib_).specref_accept(
         _p(tl), _p(dl), _p(dtok), _p(ua), _p(us), B, K, V,
         ctypes.c_double(float(np.float32(temperature))),
-        ctypes.c_double(float(np.float32(top_p))), int(bool(greedy)),
+        ctypes.c_double(float(np.float32(top_p))), int(top_k), int(bool(greedy)),
         _p(n), _p(out), _p(qt), _p(pt), _p(fp), ctypes.byref(nd), ctypes.byref(nf))
     if rc:
         raise ValueError(f"specref_accept failed: {rc}")
@@ -166,7 +167,7 @@ def verify_attn_ragged(q, k_cache, v_cache, kv_start, kv_len, k_new, v_new, cu_q
 
 
 def accept_ragged(target_logits, draft_logits, draft_tokens, u_accept, u_sample, cu_q,
-                  temperature, top_p, greedy=False, lib_=None):
+                  temperature, top_p, greedy=False, lib_=None, top_k=0):
     """Modified rejection sampling with K_b drafts in sequence b.  Target rows of b
     are cu_q[b] .. cu_q[b+1]-1; its draft rows, drafts and accept uniforms start
     at cu_q[b] - b.  Returns n_accepted [B], out_tokens [cu_q[B]] (b's K_b + 1
@@ -187,7 +188,8 @@ def accept_ragged(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
         a = accept(np.asarray(target_logits)[r0:r1].reshape(1, k + 1, V), dl,
                    np.asarray(draft_tokens)[d0:d0 + k].reshape(1, k),
                    np.asarray(u_accept)[d0:d0 + k].reshape(1, k),
-                   np.asarray(u_sample)[b:b + 1], temperature, top_p, greedy, lib_=lib_)
+                   np.asarray(u_sample)[b:b + 1], temperature, top_p, greedy, lib_=lib_,
+                   top_k=top_k)
         n[b] = a["n_accepted"][0]
         out[r0:r1] = a["out_tokens"][0]
         fp[b] = a["flag_pos"][0]

@@ -61,12 +61,15 @@ def lib():
                                          vp]
         h.spec_compact_kv_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                              i32, i32, vp, vp]
+        h.spec_accept_ex.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                     ctypes.c_float, ctypes.c_float, i32, i32, vp, vp, vp, vp, sz,
+                                     vp]
         h.sv_set_kernel_events.argtypes = [vp, vp]
         for f in ("sv_set_kernel_events", "spec_verify_attn_workspace_size", "spec_verify_attn",
                   "spec_accept_workspace_size", "spec_accept", "spec_compact_kv",
                   "spec_verify_attn_ragged_workspace_size", "spec_verify_attn_ragged",
                   "spec_accept_ragged_workspace_size", "spec_accept_ragged",
-                  "spec_compact_kv_ragged"):
+                  "spec_compact_kv_ragged", "spec_accept_ex"):
             getattr(h, f).restype = i32
         _lib = h
     return _lib
@@ -168,10 +171,11 @@ def spec_accept_workspace_size(B, K, V) -> int:
 
 
 def spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature,
-                top_p, greedy, n_accepted, out_tokens, status=None, workspace=None):
+                top_p, greedy, n_accepted, out_tokens, status=None, workspace=None, top_k=0):
     """One verify round of modified rejection sampling per sequence.
 
-    Writes ``n_accepted`` [B] and ``out_tokens`` [B, K+1] (int32)."""
+    Writes ``n_accepted`` [B] and ``out_tokens`` [B, K+1] (int32).  ``top_k`` > 0
+    keeps the k largest logits of every row (and ties) before the nucleus."""
     B, K1, V = target_logits.shape
     K = K1 - 1
     dt = _kv_dtype(target_logits)
@@ -189,6 +193,14 @@ def spec_accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, t
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=target_logits.device)
     _need(workspace.numel() >= need, f"workspace needs {need} bytes")
+    if top_k:
+        _check(lib().spec_accept_ex(
+            _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
+            _ptr(u_accept) if not greedy else None, _ptr(u_sample) if not greedy else None,
+            None, None, B, K, V, float(temperature), float(top_p), int(top_k),
+            int(bool(greedy)), _ptr(n_accepted), _ptr(out_tokens), _ptr(status),
+            _ptr(workspace), workspace.numel(), _stream(target_logits)))
+        return n_accepted, out_tokens
     _check(lib().spec_accept(
         _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
         _ptr(u_accept) if not greedy else None, _ptr(u_sample) if not greedy else None,
@@ -280,7 +292,7 @@ def spec_accept_ragged_workspace_size(B, cu_q_host, V) -> int:
 
 def spec_accept_ragged(target_logits, draft_logits, draft_tokens, u_accept, u_sample, cu_q,
                        cu_q_host, temperature, top_p, greedy, n_accepted, out_tokens,
-                       status=None, workspace=None):
+                       status=None, workspace=None, top_k=0):
     """Modified rejection sampling with K_b drafts in sequence b: target rows
     cu_q[b]..cu_q[b+1]-1 of ``target_logits`` [cu_q[B], V]; draft rows, draft
     tokens and accept uniforms of b start at cu_q[b] - b.  Writes ``n_accepted``
@@ -306,6 +318,14 @@ def spec_accept_ragged(target_logits, draft_logits, draft_tokens, u_accept, u_sa
     if workspace is None:
         workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=target_logits.device)
     _need(workspace.numel() >= need, f"workspace needs {need} bytes")
+    if top_k:
+        _check(lib().spec_accept_ex(
+            _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
+            _ptr(u_accept) if not greedy else None, _ptr(u_sample) if not greedy else None,
+            _ptr(cu_q), _host_i32(hc), B, 0, V, float(temperature), float(top_p), int(top_k),
+            int(bool(greedy)), _ptr(n_accepted), _ptr(out_tokens), _ptr(status),
+            _ptr(workspace), workspace.numel(), _stream(target_logits)))
+        return n_accepted, out_tokens
     _check(lib().spec_accept_ragged(
         _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
         _ptr(u_accept) if not greedy else None, _ptr(u_sample) if not greedy else None,

@@ -96,7 +96,8 @@ struct AcceptParams {
     const int32_t* cu_q;       // [B+1] ragged draft lengths: target rows of b start at cu_q[b]
     int nt;                    // target rows (cu_q[B], or B*(K+1))
     int B, K, V, nseg, nrows, grid_rows;  // K: the largest draft length
-    int bf16, vec, nucleus, greedy;
+    int bf16, vec, nucleus, greedy;  // nucleus: a filter is on (top_p < 1 or top_k)
+    int top_k;                       // keep the k largest logits and their ties (0: off)
     double invT;
     double top_p;
     float bscale;  // 4 / T: bin index of z is floor(z * bscale)
@@ -232,6 +233,11 @@ struct RowsLds {
     float zx;                 // logit of the drafted token of the row
     int kb_top, kb_lo;
     double hm[kBins];         // row mass per bin kb_top - og
+    int hcnt[kBins];          // row count per bin (top-k)
+    float zk;                 // top-k threshold logit (-inf: no top-k)
+    int fastk;                // the lists decided the top-k threshold
+    double Sk;                // mass of the top-k set (the full normaliser without top-k)
+    int abovec;               // radix select: count above the current digit
     int og;
     int ccount;
     int fast;
@@ -245,13 +251,16 @@ struct RowsLds {
     int rb;                   // sequence of the workgroup's row (ragged draft lengths)
 };
 
-// Exact tie-closed nucleus threshold by radix select over the whole row
-// (4 passes of 8 bits over order-preserving keys, fp64 digit masses).  Used
-// when a row's candidate lists do not hold its whole nucleus.
+// Exact tie-closed threshold by radix select over the whole row (4 passes of
+// 8 bits over order-preserving keys, fp64 digit masses and digit counts),
+// among the elements with z >= zmin.  kcount > 0: the kcount-th largest value
+// (top-k); else the nucleus boundary, the largest value whose tie-closed top
+// set reaches `target` mass.  Sets L.tau and L.kept (mass of z >= tau, z >=
+// zmin).  Used when a row's candidate lists cannot decide.
 __device__ __forceinline__ void radix_threshold(const AcceptParams& p, const void* row, float m, double target,
-                                RowsLds& L) {
+                                int kcount, float zmin, RowsLds& L) {
     const int tid = threadIdx.x;
-    if (tid == 0) { L.prefix = 0; L.mask = 0; L.above = 0.0; }
+    if (tid == 0) { L.prefix = 0; L.mask = 0; L.above = 0.0; L.abovec = 0; }
     __syncthreads();
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
@@ -266,7 +275,7 @@ __device__ __forceinline__ void radix_threshold(const AcceptParams& p, const voi
             for (int k = 0; k < 16; ++k) {
                 const int e = base + ((k >> 2) * kThreads + tid) * 4 + (k & 3);
                 const uint32_t key = fkey(z[k]);
-                if (e < p.V && (key & mask) == prefix) {
+                if (e < p.V && (key & mask) == prefix && z[k] >= zmin) {
                     const int d = (key >> shift) & 0xFF;
                     atomicAdd(&L.rad.rh_m[d], weight(z[k], m, p.invT, L.tab));
                     atomicAdd(&L.rad.rh_c[d], 1);
@@ -276,18 +285,24 @@ __device__ __forceinline__ void radix_threshold(const AcceptParams& p, const voi
         __syncthreads();
         if (tid == 0) {
             double cum = L.above;
+            int cumc = L.abovec;
             int chosen = -1, lowest = -1;
             for (int d = 255; d >= 0; --d) {
                 if (L.rad.rh_c[d] == 0) continue;
                 lowest = d;
-                if (cum + L.rad.rh_m[d] >= target) { chosen = d; break; }
+                const bool hit = kcount > 0 ? (cumc + L.rad.rh_c[d] >= kcount)
+                                            : (cum + L.rad.rh_m[d] >= target);
+                if (hit) { chosen = d; break; }
                 cum += L.rad.rh_m[d];
+                cumc += L.rad.rh_c[d];
             }
             if (chosen < 0) {  // rounding left the target unreached: keep everything
                 chosen = lowest;
                 cum -= L.rad.rh_m[lowest];
+                cumc -= L.rad.rh_c[lowest];
             }
             L.above = cum;
+            L.abovec = cumc;
             L.prefix |= static_cast<uint32_t>(chosen) << shift;
             L.mask |= 0xFFu << shift;
             L.chosen = chosen;
@@ -423,11 +438,73 @@ __device__ __forceinline__ float entry_z(unsigned long long e) {
 }
 __device__ __forceinline__ int entry_id(unsigned long long e) { return static_cast<int>(e >> 32); }
 
-// Exact tie-closed nucleus threshold of a row from its merged histogram
-// (L.hm, fp64) and the boundary bin's entries of its candidate lists, held
-// in registers (slot tid of segments 0..kChunk-1).  Sets L.fast = 0 when the
-// lists cannot decide it.
-__device__ __forceinline__ void list_threshold(const AcceptParams& p, double target,
+// Gather the listed entries of bin kb_sel with z >= zmin (held in registers:
+// slot tid of segments 0..kChunk-1) and rank them by (z desc, id asc):
+// L.cand.rz[rank] = z, L.ccount = their number.  Returns false in every thread
+// when there are none or more than kCap.
+__device__ __forceinline__ bool rank_bin(const AcceptParams& p, const unsigned long long* e, int kb_sel,
+                                         float zmin, RowsLds& L) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // per-wave counts, one barrier for the wave offsets, then positions from
+    // the ballots (no contended counter)
+    unsigned long long bal[kChunk];
+    int wcount = 0;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+        const float zc = entry_z(e[c]);
+        const bool in = static_cast<int>(c < p.nseg) & static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
+                        static_cast<int>(bin_of(zc, p.bscale) == kb_sel) & static_cast<int>(zc >= zmin);
+        bal[c] = __ballot(in);
+        wcount += __popcll(bal[c]);
+    }
+    __syncthreads();  // the caller's last reads of L.cand are done
+    if (lane == 0) L.cand.wcnt[wv] = wcount;
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int u = 0; u < kThreads / 64; ++u) base += (u < wv) ? L.cand.wcnt[u] : 0;
+    const int n = L.cand.wcnt[0] + L.cand.wcnt[1] + L.cand.wcnt[2] + L.cand.wcnt[3];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+        const unsigned long long bc = bal[c];
+        const int slot = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
+        if (((bc >> lane) & 1ull) && slot < kCap) {
+            const uint32_t id = static_cast<uint32_t>(entry_id(e[c]));
+            L.cand.ck[slot] = (static_cast<unsigned long long>(fkey(entry_z(e[c]))) << 32) | (0xFFFFFFFFu - id);
+        }
+        base += __popcll(bc);
+    }
+    if (tid == 0) L.ccount = n;
+    if (n > kCap || n == 0) {
+        __syncthreads();
+        return false;
+    }
+    // rank = number of larger keys (keys are distinct); every lane of a wave
+    // reads the same keys (LDS broadcast), 8 per batch
+    for (int i = n + tid; i < ((n + 7) & ~7); i += kThreads) L.cand.ck[i] = 0ull;  // pad: never larger
+    __syncthreads();
+    for (int i = tid; i < n; i += kThreads) {
+        const unsigned long long ki = L.cand.ck[i];
+        int rank = 0;
+        const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(L.cand.ck);
+#pragma unroll 2
+        for (int j = 0; j < n; j += 8) {
+            const ulonglong2 a0 = k2[j / 2], a1 = k2[j / 2 + 1], a2 = k2[j / 2 + 2], a3 = k2[j / 2 + 3];
+            rank += static_cast<int>(a0.x > ki) + static_cast<int>(a0.y > ki) + static_cast<int>(a1.x > ki) +
+                    static_cast<int>(a1.y > ki) + static_cast<int>(a2.x > ki) + static_cast<int>(a2.y > ki) +
+                    static_cast<int>(a3.x > ki) + static_cast<int>(a3.y > ki);
+        }
+        L.cand.rz[rank] = fkey_inv(static_cast<uint32_t>(ki >> 32));
+    }
+    __syncthreads();
+    return true;
+}
+
+// Exact tie-closed nucleus threshold of a row from its merged bin masses (L.hm,
+// fp64, entries with z >= zmin) and the boundary bin's listed entries.  Sets
+// L.fast = 0 when the lists cannot decide it.
+__device__ __forceinline__ void list_threshold(const AcceptParams& p, double target, float zmin,
                                                const unsigned long long* e, RowsLds& L) {
     const int tid = threadIdx.x;
     const float m = L.m;
@@ -454,70 +531,20 @@ __device__ __forceinline__ void list_threshold(const AcceptParams& p, double tar
             L.og = og;
             L.above = cum;
             L.fast = ok ? 1 : 0;
-            L.ccount = 0;
         }
     }
     __syncthreads();
     if (!L.fast) return;
-    const int kb_sel = kb_top - L.og;
-    const int lane = tid & 63;
-    // boundary-bin entries -> LDS keys: per-wave counts, one barrier for the
-    // wave offsets, then positions from the ballots (no contended counter)
-    const int wv = tid >> 6;
-    unsigned long long bal[kChunk];
-    int wcount = 0;
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-        const bool in = static_cast<int>(c < p.nseg) & static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
-                        static_cast<int>(bin_of(entry_z(e[c]), p.bscale) == kb_sel);
-        bal[c] = __ballot(in);
-        wcount += __popcll(bal[c]);
-    }
-    if (lane == 0) L.cand.wcnt[wv] = wcount;
-    __syncthreads();
-    int base = 0;
-#pragma unroll
-    for (int u = 0; u < kThreads / 64; ++u) base += (u < wv) ? L.cand.wcnt[u] : 0;
-    if (tid == 0) L.ccount = L.cand.wcnt[0] + L.cand.wcnt[1] + L.cand.wcnt[2] + L.cand.wcnt[3];
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-        const unsigned long long bc = bal[c];
-        const int slot = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
-        if (((bc >> lane) & 1ull) && slot < kCap) {
-            const uint32_t id = static_cast<uint32_t>(entry_id(e[c]));
-            L.cand.ck[slot] = (static_cast<unsigned long long>(fkey(entry_z(e[c]))) << 32) | (0xFFFFFFFFu - id);
-        }
-        base += __popcll(bc);
-    }
-    __syncthreads();
-    const int n = L.ccount;
-    if (n > kCap || n == 0) {
+    if (!rank_bin(p, e, kb_top - L.og, zmin, L)) {
         if (tid == 0) L.fast = 0;
         __syncthreads();
         return;
     }
-    // rank = number of larger keys (keys are distinct); every lane of a wave
-    // reads the same keys (LDS broadcast), 8 per batch
-    for (int i = n + tid; i < ((n + 7) & ~7); i += kThreads) L.cand.ck[i] = 0ull;  // pad: never larger
-    __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-        const unsigned long long ki = L.cand.ck[i];
-        int rank = 0;
-        const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(L.cand.ck);
-#pragma unroll 2
-        for (int j = 0; j < n; j += 8) {
-            const ulonglong2 a0 = k2[j / 2], a1 = k2[j / 2 + 1], a2 = k2[j / 2 + 2], a3 = k2[j / 2 + 3];
-            rank += static_cast<int>(a0.x > ki) + static_cast<int>(a0.y > ki) + static_cast<int>(a1.x > ki) +
-                    static_cast<int>(a1.y > ki) + static_cast<int>(a2.x > ki) + static_cast<int>(a2.y > ki) +
-                    static_cast<int>(a3.x > ki) + static_cast<int>(a3.y > ki);
-        }
-        const float zi = fkey_inv(static_cast<uint32_t>(ki >> 32));
-        L.cand.rz[rank] = zi;
-        L.cand.rw[rank] = weight(zi, m, p.invT, L.tab);
-    }
+    const int n = L.ccount;
+    for (int i = tid; i < n; i += kThreads) L.cand.rw[i] = weight(L.cand.rz[i], m, p.invT, L.tab);
     __syncthreads();
     if (tid < 64) {
+        const int lane = tid;
         double run = L.above;
         int istar = -1;
         for (int c0 = 0; c0 < n && istar < 0; c0 += 64) {
@@ -541,6 +568,43 @@ __device__ __forceinline__ void list_threshold(const AcceptParams& p, double tar
             L.kept = L.above + part;
         }
     }
+    __syncthreads();
+}
+
+// Top-k threshold of a row from its merged bin counts (L.hcnt) and the
+// boundary bin's listed entries: the k-th largest logit (ties kept).  Sets
+// L.zk, and L.fastk = 0 when the lists cannot decide it.
+__device__ __forceinline__ void topk_lists(const AcceptParams& p, const unsigned long long* e, RowsLds& L) {
+    const int tid = threadIdx.x;
+    const int kb_top = L.kb_top;
+    if (tid < 64) {
+        const int lane = tid;
+        const int c0 = L.hcnt[2 * lane], c1 = L.hcnt[2 * lane + 1];
+        const int inc = wave_incl_scan(c0 + c1, lane);
+        const int before = inc - (c0 + c1);
+        const unsigned long long hit = __ballot(inc >= p.top_k);
+        int og = -1, cum = 0;
+        if (hit) {
+            const int l = __ffsll(hit) - 1;
+            const int b_l = __shfl(before, l, 64), c0_l = __shfl(c0, l, 64);
+            og = (b_l + c0_l >= p.top_k) ? 2 * l : 2 * l + 1;
+            cum = (og == 2 * l) ? b_l : b_l + c0_l;
+        }
+        if (lane == 0) {
+            const bool ok = og >= 0 && kb_top - og >= L.kb_lo && p.nseg <= kChunk;
+            L.og = og;
+            L.abovec = cum;
+            L.fastk = ok ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    if (!L.fastk) return;
+    if (!rank_bin(p, e, kb_top - L.og, -INFINITY, L)) {
+        if (tid == 0) L.fastk = 0;
+        __syncthreads();
+        return;
+    }
+    if (tid == 0) L.zk = L.cand.rz[min(p.top_k - L.abovec - 1, L.ccount - 1)];
     __syncthreads();
 }
 
@@ -602,7 +666,8 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
             L.kb_lo = lo;
         }
     }
-    if (tid < kBins) L.hm[tid] = 0.0;
+    if (tid < kBins) { L.hm[tid] = 0.0; L.hcnt[tid] = 0; }
+    if (tid == 0) { L.zk = -INFINITY; L.fastk = 1; L.Sk = 0.0; }
     __syncthreads();
     const float m = L.m;
     const int x = L.n;
@@ -627,11 +692,37 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
             if (tid == 0) L.S = S;
         }
         __syncthreads();
-        if (nuc && p.nseg <= kChunk) {
-            // bin masses of the listed entries, relative to the row max: exact
-            // for every bin at or above kb_lo, which all lists hold in full.
-            // Weights of a batch are computed unconditionally (independent
-            // chains; unused slots are masked), then added.
+        // top-k first (the k largest logits and their ties), from the lists'
+        // bin counts or by radix select over the row
+        float zk = -INFINITY;
+        int fastk = 1;
+        if (nuc && p.top_k > 0) {
+            if (p.nseg <= kChunk) {
+                const int kb_top = L.kb_top;
+#pragma unroll
+                for (int c = 0; c < kChunk; ++c) {
+                    const int o = kb_top - bin_of(entry_z(e[c]), p.bscale);
+                    const bool in = static_cast<int>(c < p.nseg) &
+                                    static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
+                                    static_cast<int>(o < kBins);
+                    if (in) atomicAdd(&L.hcnt[o], 1);
+                }
+            }
+            __syncthreads();
+            topk_lists(p, e, L);
+            if (!L.fastk) {
+                radix_threshold(p, row, m, 0.0, p.top_k, -INFINITY, L);
+                if (tid == 0) { L.zk = L.tau; L.Sk = L.kept; }
+                __syncthreads();
+            }
+            zk = L.zk;
+            fastk = L.fastk;
+        }
+        if (nuc && p.nseg <= kChunk && fastk) {
+            // bin masses of the listed entries with z >= zk, relative to the
+            // row max: exact for every bin at or above kb_lo, which all lists
+            // hold in full.  Weights of a batch are computed unconditionally
+            // (independent chains; unused slots are masked), then added.
             const int kb_top = L.kb_top;
 #pragma unroll
             for (int c0 = 0; c0 < kChunk; c0 += 4) {
@@ -645,7 +736,7 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
                     ov[u] = kb_top - bin_of(zc, p.bscale);
                     in[u] = static_cast<int>(c < p.nseg) &
                             static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
-                            static_cast<int>(ov[u] < kBins);
+                            static_cast<int>(ov[u] < kBins) & static_cast<int>(zc >= zk);
                     wv[u] = weight(zc, m, p.invT, L.tab);
                 }
 #pragma unroll
@@ -654,14 +745,35 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
             }
         }
         __syncthreads();
+        if (nuc && p.top_k > 0 && fastk) {
+            // mass of the top-k set: every kept entry is listed (its bin is
+            // at or above kb_lo and within kBins of the top)
+            if (tid < 64) {
+                const double v = wave_sum(L.hm[2 * tid] + L.hm[2 * tid + 1]);
+                if (tid == 0) L.Sk = v;
+            }
+            __syncthreads();
+        }
         rec.S = L.S;
         if (nuc) {
-            const double target = p.top_p * L.S;
-            list_threshold(p, target, e, L);
-            if (!L.fast) radix_threshold(p, row, m, target, L);
-            rec.tau = L.tau;
-            rec.S = L.kept;
-            rec.fast = L.fast;
+            const double Sk = (p.top_k > 0) ? L.Sk : L.S;
+            if (p.top_p < 1.0) {
+                const double target = p.top_p * Sk;
+                if (fastk) {
+                    list_threshold(p, target, zk, e, L);
+                } else {
+                    if (tid == 0) L.fast = 0;
+                    __syncthreads();
+                }
+                if (!L.fast) radix_threshold(p, row, m, target, 0, zk, L);
+                rec.tau = L.tau;
+                rec.S = L.kept;
+                rec.fast = L.fast;
+            } else {
+                rec.tau = zk;
+                rec.S = Sk;
+                rec.fast = fastk;
+            }
         }
     }
     if (tid == 0) {
@@ -1297,7 +1409,8 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     p.bf16 = a.bf16;
     p.vec = (a.V % 4 == 0) ? 1 : 0;
     p.greedy = a.greedy;
-    p.nucleus = (!a.greedy && a.top_p < 1.0f) ? 1 : 0;
+    p.top_k = (a.top_k > 0 && a.top_k < a.V) ? a.top_k : 0;
+    p.nucleus = (!a.greedy && (a.top_p < 1.0f || p.top_k > 0)) ? 1 : 0;
     p.invT = 1.0 / static_cast<double>(a.temperature);
     p.top_p = static_cast<double>(a.top_p);
     p.bscale = static_cast<float>(4.0 / static_cast<double>(a.temperature));

@@ -150,7 +150,7 @@ int attn_run(const void* q, const void* k_cache, const void* v_cache, const int6
 int accept_run(const void* target_logits, const void* draft_logits, int logits_dtype,
                const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
                const int32_t* cu_q, long long nt, int B, int K, int V, float temperature,
-               float top_p, int greedy, int32_t* n_accepted, int32_t* out_tokens,
+               float top_p, int top_k, int greedy, int32_t* n_accepted, int32_t* out_tokens,
                int32_t* status, void* workspace, size_t workspace_bytes, sv_stream_t stream) {
     if (V > sv::accept_max_vocab())
         return fail(SV_ERR_UNSUPPORTED, "vocabulary above %d", sv::accept_max_vocab());
@@ -159,6 +159,7 @@ int accept_run(const void* target_logits, const void* draft_logits, int logits_d
     if (!(temperature > 0.0f) || !isfinite(temperature))
         return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0");
     if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(SV_ERR_INVALID_ARG, "top_p must be in (0, 1]");
+    if (top_k < 0) return fail(SV_ERR_INVALID_ARG, "top_k must be >= 0 (0: off)");
     if (K > sv::accept_max_drafts())
         return fail(SV_ERR_UNSUPPORTED, "K above %d", sv::accept_max_drafts());
     if (2 * nt - B > 0x7FFFFFFF / 64)
@@ -197,6 +198,7 @@ int accept_run(const void* target_logits, const void* draft_logits, int logits_d
     a.greedy = greedy ? 1 : 0;
     a.temperature = temperature;
     a.top_p = top_p;
+    a.top_k = top_k;
     hipError_t e = sv::accept_launch(a, as_stream(stream));
     if (e != hipSuccess) return fail(SV_ERR_HIP, "sampler launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -322,7 +324,7 @@ int spec_accept(const void* target_logits, const void* draft_logits, int logits_
     if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
     return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept, u_sample,
                       nullptr, static_cast<long long>(B) * (K + 1), B, K, V, temperature, top_p,
-                      greedy, n_accepted, out_tokens, status, workspace, workspace_bytes, stream);
+                      0, greedy, n_accepted, out_tokens, status, workspace, workspace_bytes, stream);
 }
 
 int spec_accept_ragged_workspace_size(int B, const int32_t* cu_q_host, int V, size_t* bytes) {
@@ -349,8 +351,31 @@ int spec_accept_ragged(const void* target_logits, const void* draft_logits, int 
     if (!cu_q) return fail(SV_ERR_INVALID_ARG, "cu_q is NULL");
     if (V < 1) return fail(SV_ERR_INVALID_ARG, "need V >= 1");
     return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept, u_sample,
-                      cu_q, cu_q_host[B], B, kmax, V, temperature, top_p, greedy, n_accepted,
+                      cu_q, cu_q_host[B], B, kmax, V, temperature, top_p, 0, greedy, n_accepted,
                       out_tokens, status, workspace, workspace_bytes, stream);
+}
+
+int spec_accept_ex(const void* target_logits, const void* draft_logits, int logits_dtype,
+                   const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                   const int32_t* cu_q, const int32_t* cu_q_host, int B, int K, int V,
+                   float temperature, float top_p, int top_k, int greedy, int32_t* n_accepted,
+                   int32_t* out_tokens, int32_t* status, void* workspace,
+                   size_t workspace_bytes, sv_stream_t stream) {
+    if (!cu_q && !cu_q_host) {
+        if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
+        return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept,
+                          u_sample, nullptr, static_cast<long long>(B) * (K + 1), B, K, V,
+                          temperature, top_p, top_k, greedy, n_accepted, out_tokens, status,
+                          workspace, workspace_bytes, stream);
+    }
+    int kmax = 0;
+    int rc = check_cu_q(B, cu_q_host, &kmax);
+    if (rc) return rc;
+    if (!cu_q) return fail(SV_ERR_INVALID_ARG, "cu_q is NULL");
+    if (V < 1) return fail(SV_ERR_INVALID_ARG, "need V >= 1");
+    return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept, u_sample,
+                      cu_q, cu_q_host[B], B, kmax, V, temperature, top_p, top_k, greedy,
+                      n_accepted, out_tokens, status, workspace, workspace_bytes, stream);
 }
 
 int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,

@@ -60,6 +60,7 @@ struct AcceptArgs {
     int nt;               // target rows: cu_q[B], or B*(K+1)
     int B, K, V, bf16, greedy;  // K: the largest draft length when ragged
     float temperature, top_p;
+    int top_k;            // keep the top_k largest logits (and ties) first; 0: off
 };
 
 // nt: target rows in all (B*(K+1) without ragged draft lengths)

@@ -34,7 +34,7 @@ class Case:
     re-running the method's code).
     """
 
-    def __init__(self, name, zt, zd, q_mod, p_mod, temperature=1.0, top_p=1.0):
+    def __init__(self, name, zt, zd, q_mod, p_mod, temperature=1.0, top_p=1.0, top_k=0):
         self.name = name
         self.zt = np.asarray(zt, np.float32)   # [K+1, V]
         self.zd = np.asarray(zd, np.float32)   # [K, V]
@@ -42,6 +42,7 @@ class Case:
         self.p_mod = np.asarray(p_mod, np.float64)  # [K, V]
         self.temperature = temperature
         self.top_p = top_p
+        self.top_k = top_k
 
     @property
     def K(self):
@@ -95,6 +96,26 @@ def make_cases():
     cases.append(Case("nucleus", zt, zd,
                       [[0.625, 0.375, 0.0, 0.0], [0.2, 0.2, 0.2, 0.4]],
                       [[0.0, 0.75, 0.25, 0.0]], top_p=0.79))
+    # Top-k 2 ("Accelerating ... Speculative Sampling" names top-k among the
+    # standard modifications), tie-closed at the k-th value:
+    #   target [0.4, 0.3, 0.2, 0.1] -> keep {0,1}: q' = [4/7, 3/7, 0, 0]
+    #   draft  [0.1, 0.5, 0.25, 0.15] -> keep {1,2}: p' = [0, 2/3, 1/3, 0]
+    #   bonus  [0.25, 0.25, 0.3, 0.2]: the 2nd largest value 0.25 is a tie
+    #       group of two -> keep {0,1,2}: q' = [0.25, 0.25, 0.3, 0] / 0.8
+    zt = np.log(np.array([[0.4, 0.3, 0.2, 0.1], [0.25, 0.25, 0.3, 0.2]])).astype(np.float32)
+    zd = np.log(np.array([[0.1, 0.5, 0.25, 0.15]])).astype(np.float32)
+    cases.append(Case("topk2", zt, zd, [[4 / 7, 3 / 7, 0.0, 0.0], [0.3125, 0.3125, 0.375, 0.0]],
+                      [[0.0, 2 / 3, 1 / 3, 0.0]], top_k=2))
+    # Top-k 2, then nucleus 0.9 on the renormalised top set:
+    #   target [0.5, 0.3, 0.15, 0.05] -> top-2 [0.625, 0.375] -> 0.625 < 0.9,
+    #       1.0 >= 0.9: q' = [0.625, 0.375, 0, 0]   (nucleus alone keeps {0,1,2})
+    #   draft  [0.1, 0.6, 0.2, 0.1] -> top-2 [0.75, 0.25] -> p' = [0, 0.75, 0.25, 0]
+    #   bonus  [0.2, 0.2, 0.2, 0.4] -> the 0.2 tie group enters whole: all kept,
+    #       and the nucleus needs all of them: q' = [0.2, 0.2, 0.2, 0.4]
+    zt = np.log(np.array([[0.5, 0.3, 0.15, 0.05], [0.2, 0.2, 0.2, 0.4]])).astype(np.float32)
+    zd = np.log(np.array([[0.1, 0.6, 0.2, 0.1]])).astype(np.float32)
+    cases.append(Case("topk2_nucleus", zt, zd, [[0.625, 0.375, 0.0, 0.0], [0.2, 0.2, 0.2, 0.4]],
+                      [[0.0, 0.75, 0.25, 0.0]], top_p=0.9, top_k=2))
     # Disjoint supports: logit -1e4 has exp(-1e4) == 0 in double.
     zt = np.array([[0.0, 0.0, -1e4, -1e4], [0.0, -1e4, -1e4, 0.0]], np.float32)
     zd = np.array([[-1e4, -1e4, 0.0, 0.0]], np.float32)
@@ -121,7 +142,7 @@ def make_trials(case: Case, n=N_TRIALS, seed=0):
 def run_case(sampler, case: Case, n=N_TRIALS, seed=0):
     """Run ``n`` independent verify rounds of ``case`` through ``sampler``."""
     zt, zd, tok, ua, us = make_trials(case, n, seed)
-    res = sampler(zt, zd, tok, ua, us, case.temperature, case.top_p, False)
+    res = sampler(zt, zd, tok, ua, us, case.temperature, case.top_p, False, top_k=case.top_k)
     return tok, res
 
 

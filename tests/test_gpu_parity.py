@@ -94,7 +94,7 @@ class FlagBudget:
         assert self.flagged <= 1e-4 * self.decisions, (self.flagged, self.decisions)
 
 
-def gpu_sampler(zt, zd, tok, ua, us, T, top_p, greedy):
+def gpu_sampler(zt, zd, tok, ua, us, T, top_p, greedy, top_k=0):
     B, K1, V = zt.shape
     K = K1 - 1
     dev = DEV
@@ -106,7 +106,7 @@ def gpu_sampler(zt, zd, tok, ua, us, T, top_p, greedy):
                     torch.from_numpy(np.ascontiguousarray(tok, np.int32)).to(dev),
                     torch.from_numpy(np.ascontiguousarray(ua, np.float32)).to(dev),
                     torch.from_numpy(np.ascontiguousarray(us, np.float32)).to(dev),
-                    T, top_p, greedy, n, out, status=st)
+                    T, top_p, greedy, n, out, status=st, top_k=top_k)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     return {"n_accepted": n.cpu().numpy(), "out_tokens": out.cpu().numpy()}
@@ -360,7 +360,8 @@ def test_accept_bad_token_sets_status():
     assert int(t.status.item()) == 1
 
 
-@pytest.mark.parametrize("case", ["dirichlet_v8", "nucleus", "temp_half", "disjoint"])
+@pytest.mark.parametrize("case", ["dirichlet_v8", "nucleus", "temp_half", "disjoint", "topk2",
+                                  "topk2_nucleus"])
 def test_theorem1_on_gpu(case):
     """The GPU sampler passes the same Theorem-1 pins as the oracle (10^6 trials)."""
     c = {x.name: x for x in pins.make_cases()}[case]
@@ -370,13 +371,13 @@ def test_theorem1_on_gpu(case):
     assert pins.scan_length_pvalue(res, c) > pins.ALPHA
 
 
-@pytest.mark.parametrize("case", ["dirichlet_v8", "nucleus", "disjoint"])
+@pytest.mark.parametrize("case", ["dirichlet_v8", "nucleus", "disjoint", "topk2_nucleus"])
 def test_accept_gpu_matches_oracle_many_trials(case):
     """Same 200k trials through both: bit-exact outside flagged decisions."""
     c = {x.name: x for x in pins.make_cases()}[case]
     zt, zd, tok, ua, us = pins.make_trials(c, n=200_000, seed=3)
-    res = gpu_sampler(zt, zd, tok, ua, us, c.temperature, c.top_p, False)
-    ref = R.accept(zt, zd, tok, ua, us, c.temperature, c.top_p)
+    res = gpu_sampler(zt, zd, tok, ua, us, c.temperature, c.top_p, False, top_k=c.top_k)
+    ref = R.accept(zt, zd, tok, ua, us, c.temperature, c.top_p, top_k=c.top_k)
     compare_accept(res["n_accepted"], res["out_tokens"], ref, c.K)
 
 
@@ -604,3 +605,51 @@ def test_workspace_reuse_across_lengths_and_draft_counts():
                                   cfg.top_p)
             compare_accept_ragged(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref,
                                   rw.cu_q)
+
+
+
+# ---------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("top_k,top_p", [(1, 1.0), (20, 1.0), (300, 1.0), (20, 0.95), (300, 0.9),
+                                         (5000, 1.0), (5000, 0.95), (8999, 0.95)])
+def test_accept_topk(top_k, top_p):
+    """Top-k (then nucleus) against the oracle.  k = 1 is the greedy rule; k =
+    5000 of V = 9000 is beyond the candidate lists (radix select path)."""
+    base = W.small_variant(W.CONFIGS["bass_b8k5"], B=24, K=5, V=9000, top_p=top_p)
+    budget = FlagBudget()
+    full = 0
+    for seed in range(2):
+        say(f"[accept topk] k={top_k} top_p={top_p} seed {seed}")
+        w = W.make_workload(base, sub_seed=seed, with_kv=False)
+        t = to_device(w, DEV)
+        t.status.zero_()
+        api.spec_accept(t.target_logits, t.draft_logits, t.draft_tokens, t.u_accept, t.u_sample,
+                        base.temperature, base.top_p, False, t.n_accepted, t.out_tokens,
+                        status=t.status, top_k=top_k)
+        torch.cuda.synchronize()
+        assert int(t.status.item()) == 0
+        ref = R.accept(w.target_logits, w.draft_logits, w.draft_tokens, w.u_accept, w.u_sample,
+                       base.temperature, base.top_p, top_k=top_k)
+        budget.add(ref)
+        full += compare_accept(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref,
+                               base.K)
+    budget.check()
+    assert full >= 2 * base.B - 2
+
+
+def test_accept_topk_ragged():
+    base = W.small_variant(W.CONFIGS["bass_b8k5"], B=30, K=6, V=7000, top_p=0.9)
+    for seed in range(2):
+        w = W.make_workload(base, sub_seed=40 + seed, with_kv=False)
+        rw = W.make_ragged(w, ragged_lengths(base, 40 + seed))
+        t = ragged_to_device(rw, DEV)
+        t.status.zero_()
+        api.spec_accept_ragged(t.target_logits, t.draft_logits, t.draft_tokens, t.u_accept,
+                               t.u_sample, t.cu_q, t.cu_q_host, base.temperature, base.top_p,
+                               False, t.n_accepted, t.out_tokens, status=t.status, top_k=50)
+        torch.cuda.synchronize()
+        assert int(t.status.item()) == 0
+        ref = R.accept_ragged(rw.target_logits, rw.draft_logits, rw.draft_tokens, rw.u_accept,
+                              w.u_sample, rw.cu_q, base.temperature, base.top_p, top_k=50)
+        compare_accept_ragged(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref,
+                              rw.cu_q)

@@ -28,8 +28,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def oracle_sampler(lib_=None):
-    def f(zt, zd, tok, ua, us, T, top_p, greedy):
-        return R.accept(zt, zd, tok, ua, us, T, top_p, greedy, lib_=lib_)
+    def f(zt, zd, tok, ua, us, T, top_p, greedy, top_k=0):
+        return R.accept(zt, zd, tok, ua, us, T, top_p, greedy, lib_=lib_, top_k=top_k)
     return f
 
 
@@ -429,3 +429,60 @@ def test_ragged_compaction_definition():
         ev[s0 + L:s0 + L + e[b]] = rw.v_new[q0:q0 + e[b]]
     assert np.array_equal(kc.view(np.uint16), ek.view(np.uint16))
     assert np.array_equal(vc.view(np.uint16), ev.view(np.uint16))
+
+
+# ---------------------------------------------------------------- top-k
+
+def test_topk_one_is_greedy():
+    """With k = 1 both q' and p' are the point mass at their row's argmax: a
+    draft is accepted iff it is the target argmax, and the residual (and the
+    bonus) is the target argmax -- exactly the greedy rule."""
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=32, K=5, V=500)
+    for seed in range(3):
+        w = W.make_workload(cfg, sub_seed=seed, with_kv=False)
+        a = R.accept(w.target_logits, w.draft_logits, w.draft_tokens, w.u_accept, w.u_sample,
+                     cfg.temperature, 1.0, top_k=1)
+        g = R.accept(w.target_logits, None, w.draft_tokens, w.u_accept, w.u_sample,
+                     cfg.temperature, 1.0, greedy=True)
+        assert np.array_equal(a["n_accepted"], g["n_accepted"])
+        assert np.array_equal(a["out_tokens"], g["out_tokens"])
+
+
+def test_topk_at_least_vocab_is_off():
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=8, K=4, V=300)
+    w = W.make_workload(cfg, sub_seed=1, with_kv=False)
+    base = R.workload_accept(w)
+    for k in (300, 301, 5000):
+        a = R.accept(w.target_logits, w.draft_logits, w.draft_tokens, w.u_accept, w.u_sample,
+                     cfg.temperature, cfg.top_p, top_k=k)
+        assert np.array_equal(a["out_tokens"], base["out_tokens"])
+
+
+def test_topk_kept_set_brute_force():
+    """q'(x_j) reported by the oracle equals the probability of x_j under the
+    distribution built by sorting: softmax(z/T) restricted to the k largest
+    (ties kept), renormalised, then the tie-closed nucleus, renormalised."""
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=6, K=4, V=400, temperature=0.9, top_p=0.8)
+    w = W.make_workload(cfg, sub_seed=2, with_kv=False)
+    for k in (1, 7, 40, 399):
+        a = R.accept(w.target_logits, w.draft_logits, w.draft_tokens, w.u_accept, w.u_sample,
+                     cfg.temperature, cfg.top_p, top_k=k)
+        T = float(np.float32(cfg.temperature))
+        tp = float(np.float32(cfg.top_p))
+        for b in range(cfg.B):
+            if a["flag_pos"][b] >= 0:
+                continue  # a nucleus boundary within the oracle's margin
+            for j in range(min(int(a["n_accepted"][b]) + 1, cfg.K)):  # the positions tested
+                z = w.target_logits[b, j].astype(np.float64)
+                pi = special.softmax(z / T)
+                zk = np.sort(w.target_logits[b, j])[::-1][k - 1]
+                pi = np.where(w.target_logits[b, j] >= zk, pi, 0.0)
+                pi /= pi.sum()
+                order = np.argsort(-pi, kind="stable")
+                cum = np.cumsum(pi[order])
+                i = int(np.searchsorted(cum, tp))
+                tau = pi[order[min(i, len(order) - 1)]]
+                pi = np.where(pi >= tau, pi, 0.0)
+                pi /= pi.sum()
+                x = w.draft_tokens[b, j]
+                assert abs(a["q_tok"][b, j] - pi[x]) <= 1e-12 * max(pi[x], 1e-300) + 1e-300
