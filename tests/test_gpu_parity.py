@@ -653,3 +653,39 @@ def test_accept_topk_ragged():
                               w.u_sample, rw.cu_q, base.temperature, base.top_p, top_k=50)
         compare_accept_ragged(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref,
                               rw.cu_q)
+
+
+# ---------------------------------------------------------------- maximum sizes
+
+@pytest.mark.parametrize("top_k", [0, 100])
+def test_accept_max_vocab_and_drafts(top_k):
+    """V = 2^18 (64 segments: beyond the list path, radix select and whole-row
+    draw) and K = 64 drafts (129 rows per sequence)."""
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=2, K=64, V=1 << 18, top_p=0.95)
+    say(f"[accept max] top_k={top_k}")
+    w = W.make_workload(cfg, sub_seed=9, with_kv=False)
+    t = to_device(w, DEV)
+    t.status.zero_()
+    api.spec_accept(t.target_logits, t.draft_logits, t.draft_tokens, t.u_accept, t.u_sample,
+                    cfg.temperature, cfg.top_p, False, t.n_accepted, t.out_tokens,
+                    status=t.status, top_k=top_k)
+    torch.cuda.synchronize()
+    assert int(t.status.item()) == 0
+    ref = R.accept(w.target_logits, w.draft_logits, w.draft_tokens, w.u_accept, w.u_sample,
+                   cfg.temperature, cfg.top_p, top_k=top_k)
+    compare_accept(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref, cfg.K)
+
+
+def test_attention_max_sequences_and_columns():
+    """B = 2048 sequences (the bf16 per-call limit) with short caches, and
+    (Hq/Hkv)*(K+1) = 64 query columns per kv head (K = 63, MHA)."""
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=2048, K=1, Hq=2, Hkv=2, D=64, len_lo=0,
+                          len_hi=12, V=64)
+    w = W.make_workload(cfg, sub_seed=3)
+    o = run_attn(w, to_device(w, DEV))
+    assert attn_errors(o, R.workload_attn(w)).max() <= 1e-2
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=3, K=63, Hq=2, Hkv=2, len_lo=0,
+                          len_hi=400, V=64)
+    w = W.make_workload(cfg, sub_seed=4)
+    o = run_attn(w, to_device(w, DEV))
+    assert attn_errors(o, R.workload_attn(w)).max() <= 1e-2
