@@ -145,6 +145,7 @@ __device__ void find_sequence(const AttnParams& p, int x, int g, int* s_b, int* 
 // shared-prefix partials of the prefix kernel, and writes the output rows.
 
 constexpr int kSkMaxB = 2048;        // sequences per call on the bf16 path
+constexpr int kLambdaMax = 192;      // 16-key slices per work item at most (long problems)
 constexpr int kSkMaxKeys = 1 << 25;  // keys per sequence on the bf16 path
 
 typedef short v4s_t __attribute__((__vector_size__(8)));
@@ -184,12 +185,74 @@ struct DecLds {
     int flag;
 };
 
+// Merge of the partials of (sequence, kv head g) when no prefix part is
+// involved and every value a thread needs fits in registers (UP (d, column)
+// pairs per thread, PMAX parts): the partial loads are issued before the
+// (m, l) loads, so both travel in the same round trip; the weights are formed
+// in LDS; fixed order, as in dec_merge.
+template <int D, int UP, int PMAX, typename MRG>
+__device__ __forceinline__ void merge_in_registers(const AttnParams& p, MRG& M, int g, int first_slot,
+                                                   int nparts, int nc, int qrow0, int k1) {
+    const int tid = threadIdx.x;
+    const int CPG = p.CPG, npairs = nc * D;
+    float ov[PMAX][UP];
+    int off[UP];
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+        const int pq = min(tid + u * kThreads, npairs - 1);
+        off[u] = (pq / nc) * CPG + pq % nc;
+    }
+#pragma unroll
+    for (int jj = 0; jj < PMAX; ++jj) {
+        const int j = min(jj, nparts - 1);  // past the end: re-read the last part
+        const float* pb = p.part_o + (static_cast<size_t>(first_slot) + static_cast<size_t>(j) * p.Hkv) * D * CPG;
+#pragma unroll
+        for (int u = 0; u < UP; ++u) ov[jj][u] = ld_coh(pb + off[u]);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nparts * nc; idx += kThreads) {
+        const int j = idx / nc, col = idx % nc;
+        const unsigned long long u = ld_coh(reinterpret_cast<const unsigned long long*>(
+            p.part_ml + (static_cast<size_t>(first_slot) + static_cast<size_t>(j) * p.Hkv) * CPG + col));
+        M.ml[idx] = make_float2(__uint_as_float(static_cast<unsigned>(u)),
+                                __uint_as_float(static_cast<unsigned>(u >> 32)));
+    }
+    __syncthreads();
+    for (int cl = tid; cl < nc; cl += kThreads) {
+        float ms = -INFINITY;
+        for (int j = 0; j < nparts; ++j) ms = fmaxf(ms, M.ml[j * nc + cl].x);
+        float l = 0.0f;
+        for (int j = 0; j < nparts; ++j) {
+            const float2 v = M.ml[j * nc + cl];
+            const float f = (v.x == -INFINITY) ? 0.0f : exp2f(v.x - ms);
+            M.w[j * nc + cl] = f;
+            l += v.y * f;
+        }
+        const float inv = 1.0f / l;
+        for (int j = 0; j < nparts; ++j) M.w[j * nc + cl] *= inv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+        const int pq = tid + u * kThreads;
+        if (pq >= npairs) continue;
+        const int cl = pq % nc, d = pq / nc;
+        float acc = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < PMAX; ++jj)
+            if (jj < nparts) acc += ov[jj][u] * M.w[jj * nc + cl];
+        const int hh = cl / k1, j = cl % k1;
+        const size_t oi = (static_cast<size_t>(qrow0 + j) * p.Hq + g * p.G + hh) * D + d;
+        static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(acc);
+    }
+}
+
 // Merge every part of (sequence b, kv head g) -- the prefix chunks first, then
 // its q_b chunks in order -- and write the output rows qrow0+j (j < k1) of heads
 // g*G + hh.  Two round trips: the (m, l) of every (part, column) into LDS and
 // the per-column weights, then every o value weighted, with the loads of up
 // to 4 columns x 8 parts in flight per thread.  Fixed order: bit-reproducible.
-template <int D, typename MRG>
+template <int D, int NCT, typename MRG>
 __device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_slot, int qb,
                           int qrow0, int k1) {
     const int tid = threadIdx.x;
@@ -202,62 +265,26 @@ __device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_s
         return static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * p.Hkv;
     };
     const int group = max(1, min(ncols, kMergeLds / nparts));
-    if (np == 0 && nparts <= 8 && ncols * D <= 4 * kThreads && group == ncols) {
-        // Common case: every partial value this thread needs fits in registers.
-        // Its loads are issued before the (m, l) loads, so both travel in the
-        // same round trip; the weights are then formed in LDS as below.
-        const int nc = ncols, npairs = nc * D;
-        float ov[8][4];
-        int off[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int pq = min(tid + u * kThreads, npairs - 1);
-            off[u] = (pq / nc) * CPG + pq % nc;
+    if (np == 0 && group == ncols) {
+        // every partial value a thread needs fits in registers: one round trip
+        const int npairs = ncols * D;
+        if (nparts <= 8 && npairs <= 4 * kThreads) {
+            merge_in_registers<D, 4, 8>(p, M, g, first_slot, nparts, ncols, qrow0, k1);
+            return;
         }
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int j = min(jj, nparts - 1);  // past the end: re-read the last part
-            const float* pb = p.part_o + slot_of(j) * D * CPG;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) ov[jj][u] = ld_coh(pb + off[u]);
-        }
-        __syncthreads();
-        for (int idx = tid; idx < nparts * nc; idx += kThreads) {
-            const int j = idx / nc, col = idx % nc;
-            const unsigned long long u =
-                ld_coh(reinterpret_cast<const unsigned long long*>(p.part_ml + slot_of(j) * CPG + col));
-            M.ml[idx] = make_float2(__uint_as_float(static_cast<unsigned>(u)),
-                                    __uint_as_float(static_cast<unsigned>(u >> 32)));
-        }
-        __syncthreads();
-        for (int cl = tid; cl < nc; cl += kThreads) {
-            float ms = -INFINITY;
-            for (int j = 0; j < nparts; ++j) ms = fmaxf(ms, M.ml[j * nc + cl].x);
-            float l = 0.0f;
-            for (int j = 0; j < nparts; ++j) {
-                const float2 v = M.ml[j * nc + cl];
-                const float f = (v.x == -INFINITY) ? 0.0f : exp2f(v.x - ms);
-                M.w[j * nc + cl] = f;
-                l += v.y * f;
+        // (the wider forms only where the kernel's loop already needs more
+        // registers than they do: the one-tile kernel stays at 4 workgroups
+        // per CU)
+        if constexpr (NCT > 1) {
+            if (nparts <= 4 && npairs <= 8 * kThreads) {
+                merge_in_registers<D, 8, 4>(p, M, g, first_slot, nparts, ncols, qrow0, k1);
+                return;
             }
-            const float inv = 1.0f / l;
-            for (int j = 0; j < nparts; ++j) M.w[j * nc + cl] *= inv;
+            if (nparts <= 2 && npairs <= 20 * kThreads) {
+                merge_in_registers<D, 20, 2>(p, M, g, first_slot, nparts, ncols, qrow0, k1);
+                return;
+            }
         }
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int pq = tid + u * kThreads;
-            if (pq >= npairs) continue;
-            const int cl = pq % nc, d = pq / nc;
-            float acc = 0.0f;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                if (jj < nparts) acc += ov[jj][u] * M.w[jj * nc + cl];
-            const int hh = cl / k1, j = cl % k1;
-            const size_t oi = (static_cast<size_t>(qrow0 + j) * p.Hq + g * p.G + hh) * D + d;
-            static_cast<uint16_t*>(p.out)[oi] = f32_to_bf16(acc);
-        }
-        return;
     }
     for (int c0 = 0; c0 < ncols; c0 += group) {
         const int nc = min(group, ncols - c0);
@@ -624,7 +651,7 @@ void decode_bf16_kernel(AttnParams p) {
         }
     }
     if (arrive_last(p.merge_cnt + static_cast<size_t>(b) * p.Hkv + g, qb, &S.flag))
-        dec_merge<D>(p, S.mrg, b, g, first_slot + g, qb, q0, k1);
+        dec_merge<D, NCT>(p, S.mrg, b, g, first_slot + g, qb, q0, k1);
 }
 
 template <int D>
@@ -985,8 +1012,9 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
                 n += ((std::min<long long>(keys(b), kSkMaxKeys) + 15) / 16 + lam - 1) / lam;
             return n * Hkv;
         };
-        const int nct = static_cast<int>((CPG + 15) / 16);
-        const long long cap = static_cast<long long>(sk_resident_grid(D, nct < 4 ? nct : 4)) *
+        const int nct_all = static_cast<int>((CPG + 15) / 16);
+        pl.nct = nct_all < 4 ? nct_all : 4;
+        const long long cap = static_cast<long long>(sk_resident_grid(D, pl.nct)) *
                               env_int("SPECVERIFY_SK_ROUNDS", 1);
         // smallest slice budget whose work items fit in `cap` workgroups, and
         // whose chunks per sequence fit in the merge
@@ -998,6 +1026,11 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
             const int mid = lo + (hi - lo) / 2;
             if (items_for(mid) <= cap) hi = mid; else lo = mid + 1;
         }
+        // Long problems: chunks of at most kLambdaMax slices even if that
+        // takes more workgroups than fit at once (the dispatcher then starts
+        // the next ones as earlier ones finish, which also balances them).
+        const int lam_max = std::max(env_int("SPECVERIFY_SK_LAMBDA_MAX", kLambdaMax), lam_merge);
+        if (lo > lam_max) lo = lam_max;
         const int lam_env = env_int("SPECVERIFY_SK_LAMBDA", 0);
         if (lam_env >= lo) lo = lam_env;
         const long long items = items_for(lo);
@@ -1109,7 +1142,7 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        const int nct = (p.CPG + 15) / 16;
+        const int nct = pl.nct;
         dim3 grid(pl.grid);
         // With timing events, the dispatch itself stamps them at the kernel's
         // start and end (the same timestamps a kernel trace reports).

@@ -35,6 +35,7 @@ struct AttnPlan {
     int chunk, prefix_chunk, slots, prefix_slots;
     int grid;    // bf16 path: workgroups (work items) of the decode kernel for the host bound
     int lambda;  // bf16 path: 16-key slices per work item at most
+    int nct;     // bf16 path: 16-column tiles per work item (kernel instance)
     size_t bytes;
     bool ok;  // false: the sequences are too long for the merge (unsupported)
 };
