@@ -146,6 +146,7 @@ __device__ void find_sequence(const AttnParams& p, int x, int g, int* s_b, int* 
 
 constexpr int kSkMaxB = 2048;        // sequences per call on the bf16 path
 constexpr int kLambdaMax = 192;      // 16-key slices per work item at most (long problems)
+constexpr int kLambdaMin = 12;       // 16-key slices per work item at least
 constexpr int kSkMaxKeys = 1 << 25;  // keys per sequence on the bf16 path
 
 typedef short v4s_t __attribute__((__vector_size__(8)));
@@ -1018,7 +1019,9 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
                               env_int("SPECVERIFY_SK_ROUNDS", 1);
         // smallest slice budget whose work items fit in `cap` workgroups, and
         // whose chunks per sequence fit in the merge
-        int lo = 1, hi = smax;
+        // (at least kLambdaMin slices, three per wave, so that short problems
+        // are not split into items whose fixed costs exceed their work)
+        int lo = std::min(env_int("SPECVERIFY_SK_LAMBDA_MIN", kLambdaMin), smax), hi = smax;
         const int lam_merge = (smax + (kMergeMax - pslots) - 1) / (kMergeMax - pslots);
         if (lo < lam_merge) lo = lam_merge;
         if (hi < lo) hi = lo;
