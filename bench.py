@@ -342,7 +342,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if cfg.kv_dtype == W.BF16 else "f32",
         "data": "synthetic",
         "config": {
             "workload": (f"{cfg.name}: B={B}, K={K}, {cfg.Hq}/{cfg.Hkv} heads x D{cfg.D}, "
