@@ -41,19 +41,20 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPerThread = 16;
 constexpr int kSeg = kThreads * kPerThread;  // 4096 logits per segment
-constexpr int kBins = 128;                   // quarter-unit bins of z/T below the row max
-constexpr int kCutBins = 64;                 // bins below the segment max a list may span
+constexpr int kFine = 4;                     // row bins per segment bin
+constexpr int kBins = 512;                   // 1/16-unit bins of z/T below the row max (32 units)
+constexpr int kBinsPerLane = kBins / 64;
+constexpr int kCutBins = 64;                 // quarter-unit bins below the segment max a list may span
 constexpr int kList = kThreads;              // candidate list capacity per segment
 constexpr int kCap = 1024;                   // boundary-bin entries ranked in LDS
 constexpr int kMaxSeg = 64;                  // V <= 64 * 4096
 constexpr int kChunk = 16;                   // list segments a thread loads per round trip
-constexpr int kNuc = 2048;                   // nucleus members a list draw handles
 constexpr int kMaxRowsPerSeq = 2 * 64 + 1;   // K <= 64
 
 struct SegHead {
     float m;      // segment max (greedy: max value)
-    int kb_top;   // bin of the max (greedy: index of the max)
-    int kb_cut;   // nucleus: every element with bin >= kb_cut is in the list
+    int kb_top;   // row bin of the max (greedy: index of the max)
+    int kb_cut;   // nucleus: every element with row bin >= kb_cut is in the list
     int n;        // nucleus: list length
     double S;     // sum of exp((z - m)/T) over the segment
 };
@@ -100,7 +101,8 @@ struct AcceptParams {
     int top_k;                       // keep the k largest logits and their ties (0: off)
     double invT;
     double top_p;
-    float bscale;  // 4 / T: bin index of z is floor(z * bscale)
+    float bscale;    // 16 / T: row bin of z is floor(z * bscale)
+    float bscale_c;  // 4 / T: segment bin of z is floor(z * bscale_c); row bin = 4 * segment bin + 0..3
 };
 
 // Sequence b owns target rows q0 .. q0+K_b (q0 = cu_q[b], or b*(K+1)) and draft
@@ -198,7 +200,9 @@ struct RowsLds {
             int fit;
             unsigned long long wtot[kThreads / 64];
         } seg;
-        struct {              // row merge: boundary-bin entries
+        struct {              // row merge: bin masses, boundary-bin entries
+            double hm[kBins];         // row mass per bin kb_top - og
+            int hcnt[kBins];          // row count per bin (top-k)
             unsigned long long ck[kCap + 8];  // order key: (z desc, id asc) <-> key desc
             int wcnt[kThreads / 64];
             float rz[kCap];   // z in rank order
@@ -214,9 +218,9 @@ struct RowsLds {
             int x[64];
             double scan[kThreads];
             double scan2[kThreads];
-            float mz[kNuc];   // nucleus members of the stopping row, in id order
-            int mid[kNuc];
-            float run_zp[kNuc / kThreads];
+            unsigned long long run_e[kChunk];  // the crossing run's list entries
+            int run_m[kChunk];                // and whether each is a nucleus member
+            float zpa[kChunk * kThreads];     // draft logits of every run's members
             double run0;
         } sq;
     };
@@ -232,8 +236,6 @@ struct RowsLds {
     double S;
     float zx;                 // logit of the drafted token of the row
     int kb_top, kb_lo;
-    double hm[kBins];         // row mass per bin kb_top - og
-    int hcnt[kBins];          // row count per bin (top-k)
     float zk;                 // top-k threshold logit (-inf: no top-k)
     int fastk;                // the lists decided the top-k threshold
     double Sk;                // mass of the top-k set (the full normaliser without top-k)
@@ -367,14 +369,14 @@ __device__ __forceinline__ void block_excl_scan2(double a, double b, double* sa,
 __device__ __forceinline__ void segment_list(const AcceptParams& p, int r, int s, const float* z,
                                              float ms, double Ss, RowsLds& L) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int kb_top = bin_of(ms, p.bscale);
+    const int kb_top = bin_of(ms, p.bscale_c);  // segment bins
     static_assert(4 * kCutBins == kThreads, "one counter per thread");
     (&L.seg.hc[0][0])[tid] = 0;
     __syncthreads();
     int o[kPerThread];
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
-        o[k] = (z[k] == -INFINITY) ? kCutBins : kb_top - bin_of(z[k], p.bscale);
+        o[k] = (z[k] == -INFINITY) ? kCutBins : kb_top - bin_of(z[k], p.bscale_c);
         if (o[k] < kCutBins) atomicAdd(&L.seg.hc[wv][o[k]], 1);
     }
     __syncthreads();
@@ -424,8 +426,10 @@ __device__ __forceinline__ void segment_list(const AcceptParams& p, int r, int s
     if (tid == 0) {
         SegHead* h = p.seg + static_cast<size_t>(r) * p.nseg + s;
         st_coh(&h->m, ms);
-        st_coh(&h->kb_top, kb_top);
-        st_coh(&h->kb_cut, kb_top - ocut);
+        st_coh(&h->kb_top, bin_of(ms, p.bscale));
+        // segment bin c covers row bins kFine*c .. kFine*c + kFine-1 (the scales
+        // differ by a power of two, so both floors agree)
+        st_coh(&h->kb_cut, kFine * (kb_top - ocut));
         st_coh(&h->n, run);
         st_coh(&h->S, Ss);
     }
@@ -511,19 +515,35 @@ __device__ __forceinline__ void list_threshold(const AcceptParams& p, double tar
     const int kb_top = L.kb_top;
     if (tid < 64) {
         // first bin whose cumulative mass from the top reaches the target
-        // (lane l: bins 2l and 2l+1)
+        // (lane l: bins kBinsPerLane*l .. +kBinsPerLane-1)
         const int lane = tid;
-        const double v0 = L.hm[2 * lane], v1 = L.hm[2 * lane + 1];
-        const double inc = wave_incl_scan(v0 + v1, lane);
-        const double before = inc - (v0 + v1);
+        double v[kBinsPerLane], tot = 0.0;
+#pragma unroll
+        for (int i = 0; i < kBinsPerLane; ++i) {
+            v[i] = L.cand.hm[kBinsPerLane * lane + i];
+            tot += v[i];
+        }
+        const double inc = wave_incl_scan(tot, lane);
+        const double before = inc - tot;
         const unsigned long long hit = __ballot(inc >= target);
         int og = -1;
         double cum = 0.0;
         if (hit) {
             const int l = __ffsll(hit) - 1;
-            const double b_l = __shfl(before, l, 64), v0_l = __shfl(v0, l, 64);
-            og = (b_l + v0_l >= target) ? 2 * l : 2 * l + 1;
-            cum = (og == 2 * l) ? b_l : b_l + v0_l;
+            double run = __shfl(before, l, 64);
+            // the hitting lane's bins in order, from its prefix
+            int sel = kBinsPerLane - 1;
+            double at = 0.0;
+            bool found = false;
+#pragma unroll
+            for (int i = 0; i < kBinsPerLane; ++i) {
+                const double vi = __shfl(v[i], l, 64);
+                if (!found && run + vi >= target) { sel = i; at = run; found = true; }
+                run += vi;
+            }
+            if (!found) at = run - __shfl(v[kBinsPerLane - 1], l, 64);
+            og = kBinsPerLane * l + sel;
+            cum = at;
         }
         if (lane == 0) {
             // the boundary bin must be complete in every segment's list
@@ -579,16 +599,30 @@ __device__ __forceinline__ void topk_lists(const AcceptParams& p, const unsigned
     const int kb_top = L.kb_top;
     if (tid < 64) {
         const int lane = tid;
-        const int c0 = L.hcnt[2 * lane], c1 = L.hcnt[2 * lane + 1];
-        const int inc = wave_incl_scan(c0 + c1, lane);
-        const int before = inc - (c0 + c1);
+        int cv[kBinsPerLane], tot = 0;
+#pragma unroll
+        for (int i = 0; i < kBinsPerLane; ++i) {
+            cv[i] = L.cand.hcnt[kBinsPerLane * lane + i];
+            tot += cv[i];
+        }
+        const int inc = wave_incl_scan(tot, lane);
+        const int before = inc - tot;
         const unsigned long long hit = __ballot(inc >= p.top_k);
         int og = -1, cum = 0;
         if (hit) {
             const int l = __ffsll(hit) - 1;
-            const int b_l = __shfl(before, l, 64), c0_l = __shfl(c0, l, 64);
-            og = (b_l + c0_l >= p.top_k) ? 2 * l : 2 * l + 1;
-            cum = (og == 2 * l) ? b_l : b_l + c0_l;
+            int run = __shfl(before, l, 64);
+            int sel = kBinsPerLane - 1, at = 0;
+            bool found = false;
+#pragma unroll
+            for (int i = 0; i < kBinsPerLane; ++i) {
+                const int ci = __shfl(cv[i], l, 64);
+                if (!found && run + ci >= p.top_k) { sel = i; at = run; found = true; }
+                run += ci;
+            }
+            if (!found) at = run - __shfl(cv[kBinsPerLane - 1], l, 64);
+            og = kBinsPerLane * l + sel;
+            cum = at;
         }
         if (lane == 0) {
             const bool ok = og >= 0 && kb_top - og >= L.kb_lo && p.nseg <= kChunk;
@@ -666,7 +700,7 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
             L.kb_lo = lo;
         }
     }
-    if (tid < kBins) { L.hm[tid] = 0.0; L.hcnt[tid] = 0; }
+    for (int i = tid; i < kBins; i += kThreads) { L.cand.hm[i] = 0.0; L.cand.hcnt[i] = 0; }
     if (tid == 0) { L.zk = -INFINITY; L.fastk = 1; L.Sk = 0.0; }
     __syncthreads();
     const float m = L.m;
@@ -705,7 +739,7 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
                     const bool in = static_cast<int>(c < p.nseg) &
                                     static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
                                     static_cast<int>(o < kBins);
-                    if (in) atomicAdd(&L.hcnt[o], 1);
+                    if (in) atomicAdd(&L.cand.hcnt[o], 1);
                 }
             }
             __syncthreads();
@@ -741,7 +775,7 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (in[u]) atomicAdd(&L.hm[ov[u]], wv[u]);
+                    if (in[u]) atomicAdd(&L.cand.hm[ov[u]], wv[u]);
             }
         }
         __syncthreads();
@@ -749,7 +783,10 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
             // mass of the top-k set: every kept entry is listed (its bin is
             // at or above kb_lo and within kBins of the top)
             if (tid < 64) {
-                const double v = wave_sum(L.hm[2 * tid] + L.hm[2 * tid + 1]);
+                double v = 0.0;
+#pragma unroll
+                for (int i = 0; i < kBinsPerLane; ++i) v += L.cand.hm[kBinsPerLane * tid + i];
+                v = wave_sum(v);
                 if (tid == 0) L.Sk = v;
             }
             __syncthreads();
@@ -874,20 +911,19 @@ __device__ __forceinline__ int draw_runs(const AcceptParams& p, int b, bool resi
 
 // Token drawn at position n of sequence b from the stopping row's lists.  The
 // residual (q'-p')_+ and q' vanish outside the target nucleus, so only list
-// entries with z >= tau_q take part: they are compacted in id order into LDS
-// (list slots in (segment, slot) order are in id order), the draft logits are
-// fetched at their ids, thread t takes the contiguous run [t*E, (t+1)*E) of
-// members, and one block scan of the (residual, q') pairs finds the run that
-// holds the crossing, which E lanes of wave 0 then scan at once.  Returns -1
-// when the nucleus has more than kNuc members (the caller then draws from the
-// whole row).
+// entries with z >= tau_q take part.  Thread t takes the contiguous run of
+// flat list slots [t*E, (t+1)*E) (E = segments): list slots in (segment,
+// slot) order are in id order, so the runs are too, and slots that are empty
+// or below tau_q weigh zero.  The draft logits are fetched at the members'
+// ids, one block scan of the (residual, q') run sums finds the run that holds
+// the crossing, and E lanes of wave 0 scan it.
 __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int q0, int K, int n,
                                                RowsLds& L) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int rq = q0 + n;
     const bool residual = n < K;
     const DrawRows R = draw_rows(L.sq.rr[n], residual ? L.sq.rr[K + 1 + n] : L.sq.rr[n]);
-    const int E0 = p.nseg;
+    const int E0 = p.nseg;  // <= kChunk
     const unsigned long long* lb = p.list + static_cast<size_t>(rq) * p.nseg * kList;
     // one round trip: list lengths and every slot of this thread's run
     if (tid < p.nseg) L.seg_n[tid] = ld_coh(&p.seg[static_cast<size_t>(rq) * p.nseg + tid].n);
@@ -895,46 +931,26 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) e[i] = (i < E0) ? ld_coh(lb + tid * E0 + i) : 0ull;
     __syncthreads();
-    // nucleus members in id order -> LDS
-    int cnt = 0;
+    // second round trip (residual): the draft logits at the members' ids
+    const void* drow = row_ptr(p, p.nt + q0 - b + (residual ? n : 0));
     bool mem[kChunk];
+    float zpv[kChunk];
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
         const int lin = tid * E0 + i;
-        mem[i] = static_cast<int>(i < E0) & static_cast<int>((lin % kList) < L.seg_n[min(lin / kList, kMaxSeg - 1)]) &
+        mem[i] = static_cast<int>(i < E0) &
+                 static_cast<int>((lin % kList) < L.seg_n[min(lin / kList, kMaxSeg - 1)]) &
                  static_cast<int>(entry_z(e[i]) >= R.tq);
-        cnt += mem[i] ? 1 : 0;
+        zpv[i] = (residual & mem[i]) ? load1(drow, p.bf16, entry_id(e[i])) : 0.0f;
     }
-    double unused;
-    int pos = static_cast<int>(block_excl_scan(static_cast<double>(cnt), L.sq.scan, &unused));
-    const int M = static_cast<int>(unused);
-    if (M > kNuc) return -1;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-        if (mem[i]) {
-            L.sq.mz[pos] = entry_z(e[i]);
-            L.sq.mid[pos] = entry_id(e[i]);
-            ++pos;
-        }
-    }
-    __syncthreads();
-    const int E = (M + kThreads - 1) / kThreads;  // <= kNuc / kThreads
-    const int m0 = tid * E;
-    // second round trip: the residual needs the draft logits at those ids
-    const void* drow = row_ptr(p, p.nt + q0 - b + (residual ? n : 0));
-    float zpv[kNuc / kThreads];
-#pragma unroll
-    for (int i = 0; i < kNuc / kThreads; ++i)
-        zpv[i] = (residual & (i < E) & (m0 + i < M)) ? load1(drow, p.bf16, L.sq.mid[m0 + i]) : 0.0f;
     double ds = 0.0, qs = 0.0;
 #pragma unroll
-    for (int i = 0; i < kNuc / kThreads; ++i) {
-        const bool ok = (i < E) & (m0 + i < M);
-        const float zq = L.sq.mz[min(m0 + i, kNuc - 1)];
+    for (int i = 0; i < kChunk; ++i) {
         double d, q;
-        pair_weights(R, residual, zq, zpv[i], ok, p.invT, L.tab, &d, &q);
+        pair_weights(R, residual, entry_z(e[i]), zpv[i], mem[i], p.invT, L.tab, &d, &q);
         ds += d;
         qs += q;
+        L.sq.zpa[i * kThreads + tid] = zpv[i];
     }
     double dt, qt;
     double dx, qx;
@@ -957,17 +973,20 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
     if (owner < 0) return 0;
     if (tid == owner) {
 #pragma unroll
-        for (int i = 0; i < kNuc / kThreads; ++i) L.sq.run_zp[i] = zpv[i];
+        for (int i = 0; i < kChunk; ++i) {
+            L.sq.run_e[i] = e[i];
+            L.sq.run_m[i] = mem[i] ? 1 : 0;
+        }
         L.sq.run0 = run0;
     }
     __syncthreads();
     if (tid < 64) {
-        const int mi = owner * E + lane;
-        const bool ok = (lane < E) & (mi < M);
+        const bool ok = lane < E0;
+        const unsigned long long ei = ok ? L.sq.run_e[min(lane, kChunk - 1)] : 0ull;
+        const bool is_mem = ok && L.sq.run_m[min(lane, kChunk - 1)] != 0;
         double d = 0.0, q = 0.0;
-        if (ok)
-            pair_weights(R, residual, L.sq.mz[mi], L.sq.run_zp[min(lane, kNuc / kThreads - 1)], true,
-                         p.invT, L.tab, &d, &q);
+        pair_weights(R, residual, entry_z(ei), L.sq.zpa[min(lane, kChunk - 1) * kThreads + owner],
+                     is_mem, p.invT, L.tab, &d, &q);
         const double w = useq ? q : d;
         const double run = L.sq.run0 + wave_incl_scan(w, lane);
         const bool tgt = (L.tok != 0x7FFFFFFF);
@@ -976,7 +995,7 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
         int src = -1;
         if (hit) src = __ffsll(hit) - 1;
         else if (posb) src = 63 - __clzll(posb);
-        const int id = ok ? L.sq.mid[mi] : 0;
+        const int id = entry_id(ei);
         const int tok = (src >= 0) ? __shfl(id, src, 64) : 0;
         if (lane == 0) L.n = tok;
     }
@@ -1088,7 +1107,7 @@ __device__ __forceinline__ void finalize_sequence(const AcceptParams& p, int b, 
     if (tid == 0) p.out_tokens[q0 + n] = tok;
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void rows_kernel(AcceptParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void rows_kernel(AcceptParams p) {
     __shared__ RowsLds L;
     const int tid = threadIdx.x;
     const int total = p.grid_rows * p.nseg;
@@ -1413,7 +1432,8 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     p.nucleus = (!a.greedy && (a.top_p < 1.0f || p.top_k > 0)) ? 1 : 0;
     p.invT = 1.0 / static_cast<double>(a.temperature);
     p.top_p = static_cast<double>(a.top_p);
-    p.bscale = static_cast<float>(4.0 / static_cast<double>(a.temperature));
+    p.bscale = static_cast<float>(16.0 / static_cast<double>(a.temperature));
+    p.bscale_c = static_cast<float>(4.0 / static_cast<double>(a.temperature));
     p.nrows = a.greedy ? a.nt : 2 * a.nt - a.B;
     p.grid_rows = (p.nrows + 7) / 8 * 8;
 
