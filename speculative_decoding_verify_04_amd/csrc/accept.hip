@@ -760,6 +760,7 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
             const int kb_top = L.kb_top;
 #pragma unroll
             for (int c0 = 0; c0 < kChunk; c0 += 4) {
+                if (c0 >= p.nseg) break;  // uniform
                 double wv[4];
                 int ov[4];
                 bool in[4];
@@ -946,11 +947,13 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
     double ds = 0.0, qs = 0.0;
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-        double d, q;
-        pair_weights(R, residual, entry_z(e[i]), zpv[i], mem[i], p.invT, L.tab, &d, &q);
-        ds += d;
-        qs += q;
-        L.sq.zpa[i * kThreads + tid] = zpv[i];
+        if (i < E0) {  // uniform: no work for slots past the row's segments
+            double d, q;
+            pair_weights(R, residual, entry_z(e[i]), zpv[i], mem[i], p.invT, L.tab, &d, &q);
+            ds += d;
+            qs += q;
+            L.sq.zpa[i * kThreads + tid] = zpv[i];
+        }
     }
     double dt, qt;
     double dx, qx;
@@ -1198,6 +1201,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
     }
 
     if (!arrive_last(p.row_cnt + r, p.nseg, &L.flag)) return;
+    // the merges are the critical path: their waves issue ahead of the
+    // segment work still running on the same compute unit
+    __builtin_amdgcn_s_setprio(3);
     finalize_row(p, r, br, L);
 
     const int b = br;
