@@ -531,17 +531,21 @@ __device__ __forceinline__ void list_threshold(const AcceptParams& p, double tar
         if (hit) {
             const int l = __ffsll(hit) - 1;
             double run = __shfl(before, l, 64);
-            // the hitting lane's bins in order, from its prefix
+            // the hitting lane's bins in order, from its prefix (read back
+            // from LDS: independent broadcast reads, not a chain of shuffles)
+            double vl[kBinsPerLane];
+#pragma unroll
+            for (int i = 0; i < kBinsPerLane; ++i) vl[i] = L.cand.hm[kBinsPerLane * l + i];
             int sel = kBinsPerLane - 1;
             double at = 0.0;
             bool found = false;
 #pragma unroll
             for (int i = 0; i < kBinsPerLane; ++i) {
-                const double vi = __shfl(v[i], l, 64);
+                const double vi = vl[i];
                 if (!found && run + vi >= target) { sel = i; at = run; found = true; }
                 run += vi;
             }
-            if (!found) at = run - __shfl(v[kBinsPerLane - 1], l, 64);
+            if (!found) at = run - vl[kBinsPerLane - 1];
             og = kBinsPerLane * l + sel;
             cum = at;
         }
@@ -612,15 +616,18 @@ __device__ __forceinline__ void topk_lists(const AcceptParams& p, const unsigned
         if (hit) {
             const int l = __ffsll(hit) - 1;
             int run = __shfl(before, l, 64);
+            int cl[kBinsPerLane];
+#pragma unroll
+            for (int i = 0; i < kBinsPerLane; ++i) cl[i] = L.cand.hcnt[kBinsPerLane * l + i];
             int sel = kBinsPerLane - 1, at = 0;
             bool found = false;
 #pragma unroll
             for (int i = 0; i < kBinsPerLane; ++i) {
-                const int ci = __shfl(cv[i], l, 64);
+                const int ci = cl[i];
                 if (!found && run + ci >= p.top_k) { sel = i; at = run; found = true; }
                 run += ci;
             }
-            if (!found) at = run - __shfl(cv[kBinsPerLane - 1], l, 64);
+            if (!found) at = run - cl[kBinsPerLane - 1];
             og = kBinsPerLane * l + sel;
             cum = at;
         }
@@ -684,8 +691,10 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
         float bv = (lane < p.nseg) ? L.seg_m[lane] : -INFINITY;
         int bs = (lane < p.nseg) ? lane : 0x7FFFFFFF;
         int lo = (lane < p.nseg) ? L.seg_cut[lane] : -0x40000000;
+        const int otop = (p.nseg <= 16) ? 16 : 64;  // lanes holding segments
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
+            if (o >= otop) continue;  // uniform
             const float ov = __shfl_xor(bv, o, 64);
             const int os = __shfl_xor(bs, o, 64);
             const bool take = (ov > bv) | ((ov == bv) & (os < bs));

@@ -60,6 +60,14 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
     const int kb = seq_k(a, b);
     int part = 0;
     for (int i = tid; i < b; i += kThreads) part += emitted(a.n_accepted[i], seq_k(a, i));
+    // the sequence's first 2048 output tokens (K_b + 1 of them are emitted at
+    // most), loaded with the lengths rather than after the offset scan
+    int tok[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + u * kThreads;
+        tok[u] = (i <= kb) ? a.out_tokens[static_cast<size_t>(q0) + i] : 0;
+    }
     const int e = emitted(nb, kb);
     if (tid == 0 && e == 0) set_status(a.status, 4);
 
@@ -90,7 +98,12 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs a) {
         if (b == a.B - 1) a.cu_tokens[a.B] = cu + e;
         a.kv_len[b] = L + e;
     }
-    for (int i = tid; i < e; i += kThreads)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + u * kThreads;
+        if (i < e) a.tokens_packed[cu + i] = tok[u];
+    }
+    for (int i = tid + 2 * kThreads; i < e; i += kThreads)  // draft lengths above 2047
         a.tokens_packed[cu + i] = a.out_tokens[static_cast<size_t>(q0) + i];
 }
 
