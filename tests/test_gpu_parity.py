@@ -637,6 +637,34 @@ def test_accept_topk(top_k, top_p):
     assert full >= 2 * base.B - 2
 
 
+@pytest.mark.parametrize("V,top_k,top_p", [(65536, 0, 0.95), (50001, 0, 0.95), (61441, 40, 0.95),
+                                           (57344, 300, 1.0)])
+def test_accept_list_path_segment_counts(V, top_k, top_p):
+    """The candidate-list path at 13 to 16 segments of 4096 logits per row (its
+    upper end), with a vocabulary that is not a multiple of 4 (scalar loads),
+    nucleus and top-k, on the B=8, K=5 workload's logit distributions."""
+    base = W.small_variant(W.CONFIGS["bass_b8k5"], V=V, top_p=top_p)
+    budget = FlagBudget()
+    full = 0
+    for seed in range(2):
+        say(f"[accept lists] V={V} top_k={top_k} top_p={top_p} seed {seed}")
+        w = W.make_workload(base, sub_seed=seed, with_kv=False)
+        t = to_device(w, DEV)
+        t.status.zero_()
+        api.spec_accept(t.target_logits, t.draft_logits, t.draft_tokens, t.u_accept, t.u_sample,
+                        base.temperature, base.top_p, False, t.n_accepted, t.out_tokens,
+                        status=t.status, top_k=top_k)
+        torch.cuda.synchronize()
+        assert int(t.status.item()) == 0
+        ref = R.accept(w.target_logits, w.draft_logits, w.draft_tokens, w.u_accept, w.u_sample,
+                       base.temperature, base.top_p, top_k=top_k)
+        budget.add(ref)
+        full += compare_accept(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref,
+                               base.K)
+    budget.check()
+    assert full >= 2 * base.B - 2
+
+
 def test_accept_topk_ragged():
     base = W.small_variant(W.CONFIGS["bass_b8k5"], B=30, K=6, V=7000, top_p=0.9)
     for seed in range(2):
