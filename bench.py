@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--sampler-variants", action="store_true",
                     help="time spec_accept alone under its filter and logit-type variants "
                          "(one JSON line each)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="two-stage pipeline over independent batches: the sampler and compaction "
+                         "of batch i on a second stream while batch i+1's attention runs")
     ap.add_argument("--ragged", action="store_true",
                     help="time the step with ragged draft lengths K_b ~ U{0..K} (one JSON line)")
     ap.add_argument("--traffic-from", default=None,
@@ -165,6 +168,9 @@ def main():
         return
     if args.ragged:
         ragged_bench(args)
+        return
+    if args.overlap:
+        overlap_bench(args)
         return
     if args.sampler_variants:
         sampler_variants(args)
@@ -563,6 +569,134 @@ def ragged_bench(args):
         "step_hbm_frac_at_start_lengths": round((attn_b + acc_b) / (step_us * 1e-6) / 1e9
                                                 / HBM_PEAK_GBS, 4),
     }), flush=True)
+
+
+def overlap_bench(args):
+    """The verify step as a two-stage pipeline over independent batches (the
+    rotating input sets stand for independent groups of sequences): batch i's
+    sampler and compaction wait for batch i's attention, as in a model, and
+    run on a second stream while batch i+1's attention runs on the first; a
+    batch's next attention waits for its previous compaction (which appended
+    its KV rows).  Timed against the same schedule on one stream; both are
+    captured into HIP graphs and replayed between two synchronisations."""
+    import numpy as np
+    import torch
+
+    from speculative_decoding_verify_04_amd import api
+    from speculative_decoding_verify_04_amd import workloads as W
+    from speculative_decoding_verify_04_amd.devio import to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = W.CONFIGS[args.config]
+    B, K, S = cfg.B, cfg.K, args.sets
+    steps, warmup = args.steps, args.warmup
+    uses_max = 4 * math.ceil((steps + warmup) / S) + 1  # four timed schedules below
+    growth = (K + 1) * (uses_max + 1)
+    sets = [W.make_workload(cfg, sub_seed=s, growth_rows=growth) for s in range(S)]
+    dsets = [to_device(w, dev) for w in sets]
+    bounds = [[int(x) + growth for x in w.kv_len] for w in sets]
+    P = cfg.prefix_len
+    dt = api.SV_BF16 if cfg.kv_dtype == W.BF16 else api.SV_F32
+    wa = torch.zeros(max(api.spec_verify_attn_workspace_size(B, K, cfg.Hq, cfg.Hkv, cfg.D, dt, bnd, P)
+                         for bnd in bounds), dtype=torch.uint8, device=dev)
+    wacc = torch.zeros(api.spec_accept_workspace_size(B, K, cfg.V), dtype=torch.uint8, device=dev)
+
+    def attn(s):
+        t = dsets[s]
+        api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, bounds[s], t.k_new,
+                             t.v_new, t.out, K, k_prefix=t.k_prefix, v_prefix=t.v_prefix,
+                             status=t.status, workspace=wa)
+
+    def accept_compact(s):
+        t = dsets[s]
+        api.spec_accept(t.target_logits, None if cfg.greedy else t.draft_logits, t.draft_tokens,
+                        t.u_accept, t.u_sample, cfg.temperature, cfg.top_p, cfg.greedy,
+                        t.n_accepted, t.out_tokens, status=t.status, workspace=wacc)
+        api.spec_compact_kv(t.n_accepted, t.out_tokens, t.kv_len, t.kv_start, t.k_cache,
+                            t.v_cache, t.k_new, t.v_new, t.tokens_packed, t.cu_tokens,
+                            status=t.status)
+
+    # reference tokens of every set (the sampler does not read the KV state)
+    ref_n, ref_tok = [], []
+    for s in range(S):
+        t = dsets[s]
+        api.spec_accept(t.target_logits, None if cfg.greedy else t.draft_logits, t.draft_tokens,
+                        t.u_accept, t.u_sample, cfg.temperature, cfg.top_p, cfg.greedy,
+                        t.n_accepted, t.out_tokens, status=t.status, workspace=wacc)
+        torch.cuda.synchronize()
+        ref_n.append(t.n_accepted.cpu().numpy().copy())
+        ref_tok.append(t.out_tokens.cpu().numpy().copy())
+    emitted = [int((n + 1).sum()) for n in ref_n]
+    kv0 = [t.kv_len.cpu().numpy().copy() for t in dsets]
+
+    sA = torch.cuda.Stream()
+    sB = torch.cuda.Stream()
+
+    def capture(first, n, two_streams):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=sA):
+            if not two_streams:
+                for i in range(first, first + n):
+                    attn(i % S)
+                    accept_compact(i % S)
+                return g
+            sB.wait_stream(sA)
+            done = [None] * S
+            for i in range(first, first + n):
+                s = i % S
+                if done[s] is not None:
+                    sA.wait_event(done[s])  # the batch's previous compaction
+                attn(s)
+                ea = torch.cuda.Event()
+                ea.record(sA)
+                with torch.cuda.stream(sB):
+                    sB.wait_event(ea)
+                    accept_compact(s)
+                    ed = torch.cuda.Event()
+                    ed.record(sB)
+                done[s] = ed
+            sA.wait_stream(sB)
+        return g
+
+    res = {}
+    for mode in ("one_stream", "two_streams", "one_stream", "two_streams"):
+        gw = capture(0, warmup, mode == "two_streams") if warmup else None
+        gt = capture(warmup, steps, mode == "two_streams")
+        torch.cuda.synchronize()
+        if gw is not None:
+            gw.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()  # replay() launches on the current stream
+        gt.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        tokens = sum(emitted[(warmup + i) % S] for i in range(steps))
+        res.setdefault(mode, []).append((ms, tokens))
+        for s in range(S):
+            t = dsets[s]
+            st = int(t.status.item())
+            assert st == 0, f"{mode} set {s}: device status {st}"
+            assert np.array_equal(t.n_accepted.cpu().numpy(), ref_n[s]), f"{mode} set {s}: n_accepted"
+            assert np.array_equal(t.out_tokens.cpu().numpy(), ref_tok[s]), f"{mode} set {s}: tokens"
+        del gw, gt
+    # every compaction ran once per use: the lengths advanced by (n + 1) per use
+    for s in range(S):
+        uses_s = 0
+        for _ in range(4):
+            uses_s += sum(1 for i in range(warmup + steps) if i % S == s)
+        want = kv0[s] + uses_s * (ref_n[s].astype(np.int64) + 1)
+        assert np.array_equal(dsets[s].kv_len.cpu().numpy(), want), f"set {s}: kv_len"
+    out = {"overlap": True, "config": cfg.name, "B": B, "K": K, "steps": steps, "sets": S}
+    for mode, v in res.items():
+        ms = min(x[0] for x in v)
+        tokens = v[0][1]
+        out[mode] = {"us_per_step": round(1e3 * ms / steps, 2),
+                     "verified_tokens_per_s": round(tokens / (ms * 1e-3), 1)}
+    out["speedup"] = round(out["one_stream"]["us_per_step"] / out["two_streams"]["us_per_step"], 3)
+    print(json.dumps(out), flush=True)
 
 
 def sampler_variants(args):

@@ -412,6 +412,89 @@ def test_compaction_matches_oracle(name):
     assert np.array_equal(got_v.view(view), vc.view(view))
 
 
+def test_two_stream_pipeline_matches_one_stream():
+    """The pipelined schedule of the benchmark's overlap mode (batch i's sampler
+    and compaction on a second stream while batch i+1's attention runs, a
+    batch's next attention after its previous compaction), captured into a HIP
+    graph, gives bit-identical attention outputs, tokens, packed tokens, KV
+    lengths and caches to the same steps on one stream."""
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=6, Hq=8, Hkv=8, len_lo=20, len_hi=700,
+                          V=8192, K=4)
+    S, steps = 3, 9
+    growth = (cfg.K + 1) * (steps // S + 2)
+    works = [W.make_workload(cfg, sub_seed=20 + s, growth_rows=growth) for s in range(S)]
+    bounds = [[int(x) + growth for x in w.kv_len] for w in works]
+
+    def run(two_streams):
+        ds = [to_device(w, DEV) for w in works]
+        wa = torch.zeros(max(api.spec_verify_attn_workspace_size(cfg.B, cfg.K, cfg.Hq, cfg.Hkv, cfg.D,
+                                                                 api.SV_BF16, bnd, 0)
+                             for bnd in bounds), dtype=torch.uint8, device=DEV)
+        wacc = torch.zeros(api.spec_accept_workspace_size(cfg.B, cfg.K, cfg.V), dtype=torch.uint8,
+                           device=DEV)
+        outs = torch.zeros((steps,) + tuple(ds[0].out.shape), dtype=ds[0].out.dtype, device=DEV)
+        sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+
+        def attn(i):
+            t = ds[i % S]
+            api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, bounds[i % S],
+                                 t.k_new, t.v_new, t.out, cfg.K, status=t.status, workspace=wa)
+            outs[i].copy_(t.out)
+
+        def rest(i):
+            t = ds[i % S]
+            api.spec_accept(t.target_logits, t.draft_logits, t.draft_tokens, t.u_accept, t.u_sample,
+                            cfg.temperature, cfg.top_p, False, t.n_accepted, t.out_tokens,
+                            status=t.status, workspace=wacc)
+            api.spec_compact_kv(t.n_accepted, t.out_tokens, t.kv_len, t.kv_start, t.k_cache,
+                                t.v_cache, t.k_new, t.v_new, t.tokens_packed, t.cu_tokens,
+                                status=t.status)
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=sA):
+            if two_streams:
+                sB.wait_stream(sA)
+                done = [None] * S
+                for i in range(steps):
+                    if done[i % S] is not None:
+                        sA.wait_event(done[i % S])
+                    attn(i)
+                    ea = torch.cuda.Event()
+                    ea.record(sA)
+                    with torch.cuda.stream(sB):
+                        sB.wait_event(ea)
+                        rest(i)
+                        ed = torch.cuda.Event()
+                        ed.record(sB)
+                    done[i % S] = ed
+                sA.wait_stream(sB)
+            else:
+                for i in range(steps):
+                    attn(i)
+                    rest(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t in ds:
+            assert int(t.status.item()) == 0
+        return outs.cpu(), [(t.n_accepted.cpu(), t.out_tokens.cpu(), t.tokens_packed.cpu(),
+                             t.cu_tokens.cpu(), t.kv_len.cpu(), t.k_cache.cpu(), t.v_cache.cpu())
+                            for t in ds]
+
+    o1, r1 = run(False)
+    o2, r2 = run(True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    for a, b in zip(r1, r2):
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+    # each batch advanced by its emitted tokens once per use
+    for s, w in enumerate(works):
+        uses = sum(1 for i in range(steps) if i % S == s)
+        n = r1[s][0].numpy().astype(np.int64)
+        assert np.array_equal(r1[s][4].numpy(), w.kv_len + uses * (n + 1))
+
+
 def test_compaction_rejects_bad_count():
     cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=3, Hq=2, Hkv=2, len_lo=5, len_hi=30, V=512)
     w = W.make_workload(cfg, sub_seed=1)
