@@ -218,10 +218,7 @@ struct RowsLds {
             int x[64];
             double scan[kThreads];
             double scan2[kThreads];
-            unsigned long long run_e[kChunk];  // the crossing run's list entries
-            int run_m[kChunk];                // and whether each is a nucleus member
             float zpa[kChunk * kThreads];     // draft logits of every run's members
-            double run0;
         } sq;
     };
     // row merge
@@ -926,7 +923,8 @@ __device__ __forceinline__ int draw_runs(const AcceptParams& p, int b, bool resi
 // slot) order are in id order, so the runs are too, and slots that are empty
 // or below tau_q weigh zero.  The draft logits are fetched at the members'
 // ids, one block scan of the (residual, q') run sums finds the run that holds
-// the crossing, and E lanes of wave 0 scan it.
+// the crossing, and E lanes of the owning thread's wave scan it (its entries
+// read from that thread's registers with lane reads).
 __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int q0, int K, int n,
                                                RowsLds& L) {
     const int tid = threadIdx.x, lane = tid & 63;
@@ -966,6 +964,7 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
     }
     double dt, qt;
     double dx, qx;
+    if (tid == 0) { L.tok = 0x7FFFFFFF; L.lastpos = -1; }  // ordered by the scan's barriers
     block_excl_scan2(ds, qs, L.sq.scan, L.sq.scan2, &dx, &qx, &dt, &qt);
     const bool useq = residual && !(dt > 0.0);  // zero residual mass: fall back to q'
     const double tot = useq ? qt : dt;
@@ -974,34 +973,41 @@ __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int
     const double target = static_cast<double>(u) * tot;
     const double run0 = useq ? qx : dx;
     const double mine = useq ? qs : ds;
-    if (tid == 0) { L.tok = 0x7FFFFFFF; L.lastpos = -1; }
+    // the last run with positive mass (one atomic per wave), and the run that
+    // holds the crossing (one thread at most)
+    const unsigned long long posm = __ballot(mine > 0.0);
+    if (posm && lane == 63 - __clzll(posm)) atomicMax(&L.lastpos, tid);
+    if ((mine > 0.0) & (run0 <= target) & (target < run0 + mine)) L.tok = tid;
     __syncthreads();
-    if (mine > 0.0) {
-        atomicMax(&L.lastpos, tid);
-        if ((run0 <= target) & (target < run0 + mine)) L.tok = tid;  // one run holds it
-    }
-    __syncthreads();
-    const int owner = (L.tok != 0x7FFFFFFF) ? L.tok : L.lastpos;  // rounding: last positive run
-    if (owner < 0) return 0;
-    if (tid == owner) {
+    const bool tgt = (L.tok != 0x7FFFFFFF);
+    const int owner = tgt ? L.tok : L.lastpos;  // rounding: last positive run
+    if (owner < 0) return 0;  // uniform: no mass at all
+    if ((tid >> 6) == (owner >> 6)) {
+        // the owner's wave scans its run: lane i takes entry i, read from the
+        // owner lane's registers
+        const int ol = __builtin_amdgcn_readfirstlane(owner & 63);
+        unsigned mm = 0;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) mm |= mem[i] ? (1u << i) : 0u;
+        mm = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(mm), ol));
+        const long long rb = __double_as_longlong(run0);
+        const unsigned rlo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(rb), ol));
+        const unsigned rhi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(rb >> 32), ol));
+        const double r0 = __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(rhi) << 32) | rlo));
+        unsigned long long ei = 0ull;
 #pragma unroll
         for (int i = 0; i < kChunk; ++i) {
-            L.sq.run_e[i] = e[i];
-            L.sq.run_m[i] = mem[i] ? 1 : 0;
+            const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(e[i]), ol));
+            const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(e[i] >> 32), ol));
+            if (lane == i) ei = (static_cast<unsigned long long>(hi) << 32) | lo;
         }
-        L.sq.run0 = run0;
-    }
-    __syncthreads();
-    if (tid < 64) {
         const bool ok = lane < E0;
-        const unsigned long long ei = ok ? L.sq.run_e[min(lane, kChunk - 1)] : 0ull;
-        const bool is_mem = ok && L.sq.run_m[min(lane, kChunk - 1)] != 0;
+        const bool is_mem = ok && ((mm >> min(lane, 31)) & 1u);
         double d = 0.0, q = 0.0;
         pair_weights(R, residual, entry_z(ei), L.sq.zpa[min(lane, kChunk - 1) * kThreads + owner],
                      is_mem, p.invT, L.tab, &d, &q);
         const double w = useq ? q : d;
-        const double run = L.sq.run0 + wave_incl_scan(w, lane);
-        const bool tgt = (L.tok != 0x7FFFFFFF);
+        const double run = r0 + wave_incl_scan(w, lane);
         const unsigned long long hit = __ballot((w > 0.0) & (target < run) & tgt);
         const unsigned long long posb = __ballot(w > 0.0);
         int src = -1;
