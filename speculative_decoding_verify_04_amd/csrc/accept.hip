@@ -441,10 +441,11 @@ __device__ __forceinline__ int entry_id(unsigned long long e) { return static_ca
 
 // Gather the listed entries of bin kb_sel with z >= zmin (held in registers:
 // slot tid of segments 0..kChunk-1) and rank them by (z desc, id asc):
-// L.cand.rz[rank] = z, L.ccount = their number.  Returns false in every thread
+// L.cand.rz[rank] = z, L.cand.rw[rank] = its fp64 weight relative to the row
+// max m, L.ccount = their number.  Returns false in every thread
 // when there are none or more than kCap.
 __device__ __forceinline__ bool rank_bin(const AcceptParams& p, const unsigned long long* e, int kb_sel,
-                                         float zmin, RowsLds& L) {
+                                         float zmin, float m, RowsLds& L) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // per-wave counts, one barrier for the wave offsets, then positions from
     // the ballots (no contended counter)
@@ -458,7 +459,8 @@ __device__ __forceinline__ bool rank_bin(const AcceptParams& p, const unsigned l
         bal[c] = __ballot(in);
         wcount += __popcll(bal[c]);
     }
-    __syncthreads();  // the caller's last reads of L.cand are done
+    // (earlier reads of wcnt, ccount, ck, rz and rw all end before barriers of
+    // the caller)
     if (lane == 0) L.cand.wcnt[wv] = wcount;
     __syncthreads();
     int base = 0;
@@ -496,7 +498,9 @@ __device__ __forceinline__ bool rank_bin(const AcceptParams& p, const unsigned l
                     static_cast<int>(a1.y > ki) + static_cast<int>(a2.x > ki) + static_cast<int>(a2.y > ki) +
                     static_cast<int>(a3.x > ki) + static_cast<int>(a3.y > ki);
         }
-        L.cand.rz[rank] = fkey_inv(static_cast<uint32_t>(ki >> 32));
+        const float zi = fkey_inv(static_cast<uint32_t>(ki >> 32));
+        L.cand.rz[rank] = zi;
+        L.cand.rw[rank] = weight(zi, m, p.invT, L.tab);  // relative to the row max
     }
     __syncthreads();
     return true;
@@ -556,14 +560,12 @@ __device__ __forceinline__ void list_threshold(const AcceptParams& p, double tar
     }
     __syncthreads();
     if (!L.fast) return;
-    if (!rank_bin(p, e, kb_top - L.og, zmin, L)) {
+    if (!rank_bin(p, e, kb_top - L.og, zmin, m, L)) {
         if (tid == 0) L.fast = 0;
         __syncthreads();
         return;
     }
     const int n = L.ccount;
-    for (int i = tid; i < n; i += kThreads) L.cand.rw[i] = weight(L.cand.rz[i], m, p.invT, L.tab);
-    __syncthreads();
     if (tid < 64) {
         const int lane = tid;
         double run = L.above;
@@ -637,7 +639,7 @@ __device__ __forceinline__ void topk_lists(const AcceptParams& p, const unsigned
     }
     __syncthreads();
     if (!L.fastk) return;
-    if (!rank_bin(p, e, kb_top - L.og, -INFINITY, L)) {
+    if (!rank_bin(p, e, kb_top - L.og, -INFINITY, L.m, L)) {
         if (tid == 0) L.fastk = 0;
         __syncthreads();
         return;
@@ -705,6 +707,16 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
             L.kb_top = bin_of(bv, p.bscale);
             L.kb_lo = lo;
         }
+        if (!p.greedy) {
+            // normaliser relative to the row max (lane 0 holds it), in the same
+            // wave: no barrier between the two
+            const float mrow = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bv)));
+            const float ms = (lane < p.nseg) ? L.seg_m[lane] : -INFINITY;
+            const double sc = (ms == -INFINITY) ? 0.0 : weight(ms, mrow, p.invT, L.tab);
+            if (lane < p.nseg) L.sc[lane] = sc;
+            const double S = wave_sum((lane < p.nseg) ? L.seg_S[lane] * sc : 0.0);
+            if (lane == 0) L.S = S;
+        }
     }
     for (int i = tid; i < kBins; i += kThreads) { L.cand.hm[i] = 0.0; L.cand.hcnt[i] = 0; }
     if (tid == 0) { L.zk = -INFINITY; L.fastk = 1; L.Sk = 0.0; }
@@ -724,14 +736,6 @@ __device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b
     rec.pad = 0;
 
     if (!p.greedy) {
-        if (tid < 64) {
-            const float ms = (tid < p.nseg) ? L.seg_m[tid] : -INFINITY;
-            const double sc = (ms == -INFINITY) ? 0.0 : weight(ms, m, p.invT, L.tab);
-            if (tid < p.nseg) L.sc[tid] = sc;
-            const double S = wave_sum((tid < p.nseg) ? L.seg_S[tid] * sc : 0.0);
-            if (tid == 0) L.S = S;
-        }
-        __syncthreads();
         // top-k first (the k largest logits and their ties), from the lists'
         // bin counts or by radix select over the row
         float zk = -INFINITY;
