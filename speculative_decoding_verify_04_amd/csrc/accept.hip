@@ -1400,8 +1400,13 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
         run += w[k];
         mine = ((mine == 0x7FFFFFFF) & (w[k] > 0.0) & (target < run)) ? e0 + k : mine;
     }
-    if (mine != 0x7FFFFFFF) atomicMin(&L.tok, mine);
-    if (lastpos >= 0) atomicMax(&L.last_pos, lastpos);
+    // ids increase with the thread: the wave's smallest candidate is its first
+    // lane's with one, its largest positive id its last lane's (one LDS
+    // atomic per wave instead of one per thread)
+    const unsigned long long hasm = __ballot(mine != 0x7FFFFFFF);
+    const unsigned long long hasl = __ballot(lastpos >= 0);
+    if (hasm && lane == __ffsll(hasm) - 1) atomicMin(&L.tok, mine);
+    if (hasl && lane == 63 - __clzll(hasl)) atomicMax(&L.last_pos, lastpos);
     __syncthreads();
     if (tid == 0) {
         int tok = L.tok != 0x7FFFFFFF ? L.tok : L.last_pos;
