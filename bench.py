@@ -94,6 +94,28 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def measured_copy_gbs(mib=1024, reps=5):
+    """Bytes moved per second (read + write) by a plain elementwise copy of
+    `mib` MiB on this GPU: the streaming rate an HBM-bound kernel can expect,
+    reported beside the 8 TB/s specification."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.add(src, 0, out=dst)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        torch.add(src, 0, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
 def copy_calibration(mib):
     """A plain elementwise copy kernel of `mib` MiB (reads and writes n bytes once)."""
     import torch
@@ -325,6 +347,9 @@ def main():
     kern_ok = all(m is not None and m > 0 for m in kern_ms)
     kern_avg_us = 1e3 * sum(kern_ms) / steps if kern_ok else None
     achieved = (sum(kern_bytes) / (1e-3 * sum(kern_ms))) / 1e9 if kern_ok else None
+    kern_pct = ([round(1e3 * float(v), 2) for v in np.percentile(kern_ms, [10, 50, 90])]
+                if kern_ok else None)
+    copy_gbs = measured_copy_gbs()
 
     # HBM counter summary (if one was taken for the current kernel source)
     traffic = None
@@ -372,6 +397,10 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch_avg": int(sum(kern_bytes) / steps),
             "avg_launch_us": round(kern_avg_us, 3) if kern_avg_us else None,
+            "launch_us_p10_p50_p90": kern_pct,
+            "measured_copy_GBs": copy_gbs,
+            "frac_of_measured_copy": (round(achieved / copy_gbs, 4)
+                                      if achieved and copy_gbs else None),
         },
     }
 
