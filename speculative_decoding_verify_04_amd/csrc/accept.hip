@@ -11,19 +11,21 @@
 //   segment  read the segment once: max, fp64 mass relative to it, and
 //            (nucleus) the segment's candidate list: every element of the
 //            highest quarter-unit bins of z/T, as many bins as fit in 256
-//            entries, stored in id order.  Near-threshold tokens of a nucleus
-//            are few per segment, so the lists hold the whole nucleus.
-//   row      the last segment of a row merges it: max, normaliser, and the
-//            exact tie-closed nucleus threshold from the lists alone (bin
-//            masses, then the boundary bin's few entries ranked exactly);
-//            for target rows it also fetches the draft logits at the list
-//            ids (the residual of that position only needs those).  When a
-//            list misses part of the nucleus the row falls back to a radix
-//            select over the whole row.
+//            entries, stored in id order.  A nucleus of top_p < 1 keeps the
+//            upper part of the distribution, so the lists normally hold it
+//            whole.
+//   row      the last segment of a row merges it: max, normaliser, fp64
+//            masses of the listed entries over 1/16-unit bins, and the exact
+//            tie-closed nucleus threshold (the boundary bin from the bin
+//            masses, then its few entries ranked exactly).  When a list
+//            misses part of the nucleus the row falls back to a radix select
+//            over the whole row.
 //   sequence the last row of a sequence runs the accept scan and draws the
-//            emitted token from the stopping row's list: the residual
-//            (q' - p')_+ and q' vanish outside the target nucleus.  A row
-//            without a complete list is drawn by a pass over the whole row.
+//            emitted token from the stopping row's lists: the residual
+//            (q' - p')_+ and q' vanish outside the target nucleus, so the
+//            draft logits are read at the target nucleus members' ids only.
+//            A row without a complete list is drawn by a pass over the
+//            whole row.
 // draw_kernel  (no nucleus) grid = sequences x segments: fp64 residual or
 //   bonus weights of the stopping row, per-segment sums; the last segment
 //   picks the crossing segment and scans it exactly.
