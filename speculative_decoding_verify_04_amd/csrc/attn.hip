@@ -706,21 +706,59 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
     float mrun = -INFINITY, lrun = 0.0f;
     const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
 
+    // One 64-key K and V tile is 2*64*VCH 16-byte words.  With at least
+    // 2*64*VCH/kPL threads every thread holds its words of the next tile in
+    // registers: they are issued before the current tile's products and
+    // written to LDS after them, so the loads overlap the MFMA work.
+    constexpr int kPL = 4;
+    constexpr int kWords = 2 * 64 * VCH;
+    const bool staged = kWords <= kPL * nthreads;
+    auto word_src = [&](int qi, int tb) -> const uint4* {
+        const int isv = qi >= 64 * VCH;
+        const int r = (qi % (64 * VCH)) / VCH, dc = qi % VCH;
+        const int t = min(tb + r, p.prefix_len - 1);
+        return reinterpret_cast<const uint4*>((isv ? p.v_prefix : p.k_prefix) +
+                                              static_cast<size_t>(t) * row_stride +
+                                              static_cast<size_t>(g) * D + dc * 8);
+    };
+    auto word_put = [&](int qi, uint4 v) {
+        const int isv = qi >= 64 * VCH;
+        const int r = (qi % (64 * VCH)) / VCH, dc = qi % VCH;
+        uint16_t* dst = isv ? &S.vs[r][dc * 8] : &S.ks[r][dc * 8];
+        reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
+        reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+    };
+    uint4 nx[kPL];
+    auto issue = [&](int tb) {
+#pragma unroll
+        for (int u = 0; u < kPL; ++u) {
+            const int qi = tid + u * nthreads;
+            if (qi < kWords) nx[u] = *word_src(qi, tb);
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int u = 0; u < kPL; ++u) {
+            const int qi = tid + u * nthreads;
+            if (qi < kWords) word_put(qi, nx[u]);
+        }
+    };
+    // transposed-read address of this lane in a 16-key sub-tile of V (as in
+    // the decode kernel): row kg*4 + col16/4, column 4*(col16%4)
+    const uint16_t* vt_lane = &S.vs[kg * 4 + (col16 >> 2)][(col16 & 3) * 4];
+
+    if (staged && t_begin < t_end) {
+        issue(t_begin);
+        stash();
+    }
     for (int tb = t_begin; tb < t_end; tb += 64) {
-        // cooperative load of the 64-key K and V tiles
-        for (int qi = tid; qi < 2 * 64 * VCH; qi += nthreads) {
-            const int isv = qi >= 64 * VCH;
-            const int r = (qi % (64 * VCH)) / VCH, dc = qi % VCH;
-            const int t = min(tb + r, p.prefix_len - 1);
-            const uint16_t* src = (isv ? p.v_prefix : p.k_prefix) +
-                                  static_cast<size_t>(t) * row_stride + static_cast<size_t>(g) * D +
-                                  dc * 8;
-            uint4 v = *reinterpret_cast<const uint4*>(src);
-            uint16_t* dst = isv ? &S.vs[r][dc * 8] : &S.ks[r][dc * 8];
-            reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
-            reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+        if (!staged) {
+            // cooperative load of the 64-key K and V tiles
+            for (int qi = tid; qi < kWords; qi += nthreads) word_put(qi, *word_src(qi, tb));
         }
         __syncthreads();
+        const bool more = staged && (tb + 64 < t_end);
+        if (more) issue(tb + 64);  // in flight during this tile's products
         if (active) {
             floatx4 acc[4];
             float mt = -INFINITY;
@@ -765,15 +803,14 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
             for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    shortx4 va;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        va[e] = static_cast<short>(S.vs[kt * 16 + kg * 4 + e][dt * 16 + col16]);
+                    // V^T operand: lane (d = dt*16 + col16) gets keys kt*16 + kg*4 .. +3
+                    const shortx4 va = lds_read_tr16(vt_lane + kt * 16 * PrefixLds<D>::VP + dt * 16);
                     o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kt], o[dt], 0, 0, 0);
                 }
             }
         }
-        __syncthreads();
+        __syncthreads();  // every wave is done with the tile
+        if (more) stash();
     }
     lrun += __shfl_xor(lrun, 16, 64);
     lrun += __shfl_xor(lrun, 32, 64);
