@@ -659,12 +659,14 @@ template <int D>
 struct PrefixLds {
     static constexpr int KP = D + 8;  // K tile pitch (bf16)
     static constexpr int VP = D + 4;  // V tile pitch (bf16)
-    uint16_t ks[64][KP];
-    uint16_t vs[64][VP];
+    static constexpr int kTile = 128; // keys per tile (two halves of 64 for the products)
+    uint16_t ks[kTile][KP];
+    uint16_t vs[kTile][VP];
 };
 
 // grid: x = prefix chunk, y = kv head, z = column group (16 tiles of 16 columns);
-// block: one wave per column tile of the group.
+// block: 16 waves, one per column tile of the group (waves past the group's
+// tiles only help load the K/V tiles).
 template <int D>
 __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
     constexpr int KK = D / 32, DT = D / 16, VCH = D / 8;
@@ -706,24 +708,25 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
     float mrun = -INFINITY, lrun = 0.0f;
     const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
 
-    // One 64-key K and V tile is 2*64*VCH 16-byte words.  With at least
-    // 2*64*VCH/kPL threads every thread holds its words of the next tile in
-    // registers: they are issued before the current tile's products and
-    // written to LDS after them, so the loads overlap the MFMA work.
+    // One K and V tile of kTile keys is 2*kTile*VCH 16-byte words.  With at
+    // least 2*kTile*VCH/kPL threads every thread holds its words of the next
+    // tile in registers: they are issued before the current tile's products
+    // and written to LDS after them, so the loads overlap the MFMA work.
+    constexpr int kTile = PrefixLds<D>::kTile;
     constexpr int kPL = 4;
-    constexpr int kWords = 2 * 64 * VCH;
+    constexpr int kWords = 2 * kTile * VCH;
     const bool staged = kWords <= kPL * nthreads;
     auto word_src = [&](int qi, int tb) -> const uint4* {
-        const int isv = qi >= 64 * VCH;
-        const int r = (qi % (64 * VCH)) / VCH, dc = qi % VCH;
+        const int isv = qi >= kTile * VCH;
+        const int r = (qi % (kTile * VCH)) / VCH, dc = qi % VCH;
         const int t = min(tb + r, p.prefix_len - 1);
         return reinterpret_cast<const uint4*>((isv ? p.v_prefix : p.k_prefix) +
                                               static_cast<size_t>(t) * row_stride +
                                               static_cast<size_t>(g) * D + dc * 8);
     };
     auto word_put = [&](int qi, uint4 v) {
-        const int isv = qi >= 64 * VCH;
-        const int r = (qi % (64 * VCH)) / VCH, dc = qi % VCH;
+        const int isv = qi >= kTile * VCH;
+        const int r = (qi % (kTile * VCH)) / VCH, dc = qi % VCH;
         uint16_t* dst = isv ? &S.vs[r][dc * 8] : &S.ks[r][dc * 8];
         reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
         reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
@@ -751,15 +754,18 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
         issue(t_begin);
         stash();
     }
-    for (int tb = t_begin; tb < t_end; tb += 64) {
+    for (int tb = t_begin; tb < t_end; tb += kTile) {
         if (!staged) {
-            // cooperative load of the 64-key K and V tiles
+            // cooperative load of the K and V tiles
             for (int qi = tid; qi < kWords; qi += nthreads) word_put(qi, *word_src(qi, tb));
         }
         __syncthreads();
-        const bool more = staged && (tb + 64 < t_end);
-        if (more) issue(tb + 64);  // in flight during this tile's products
-        if (active) {
+        const bool more = staged && (tb + kTile < t_end);
+        if (more) issue(tb + kTile);  // in flight during this tile's products
+#pragma unroll 1
+        for (int half = 0; half < kTile / 64; ++half) {
+        const int hb = tb + half * 64;   // first key of the half
+        if (active && hb < t_end) {
             floatx4 acc[4];
             float mt = -INFINITY;
 #pragma unroll
@@ -768,7 +774,7 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) {
                     const uint2* src =
-                        reinterpret_cast<const uint2*>(&S.ks[kt * 16 + col16][kg * 8 + 32 * kk]);
+                        reinterpret_cast<const uint2*>(&S.ks[half * 64 + kt * 16 + col16][kg * 8 + 32 * kk]);
                     uint2 lo = src[0], hi = src[1];
                     uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
                     bf16x8 ka = *reinterpret_cast<bf16x8*>(&u);
@@ -776,14 +782,14 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = tb + kt * 16 + kg * 4 + e;
+                    const int t = hb + kt * 16 + kg * 4 + e;
                     acc[kt][e] = (t < t_end) ? acc[kt][e] * p.scale_log2 : -INFINITY;
                     mt = fmaxf(mt, acc[kt][e]);
                 }
             }
             mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float mnew = fmaxf(mrun, mt);   // finite: every tile has a valid key
+            const float mnew = fmaxf(mrun, mt);   // finite: every half computed has a valid key
             const float alpha = exp2f(mrun - mnew);
             float ps = 0.0f;
             shortx4 pb[4];
@@ -804,11 +810,13 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     // V^T operand: lane (d = dt*16 + col16) gets keys kt*16 + kg*4 .. +3
-                    const shortx4 va = lds_read_tr16(vt_lane + kt * 16 * PrefixLds<D>::VP + dt * 16);
+                    const shortx4 va =
+                        lds_read_tr16(vt_lane + (half * 64 + kt * 16) * PrefixLds<D>::VP + dt * 16);
                     o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kt], o[dt], 0, 0, 0);
                 }
             }
         }
+        }  // half
         __syncthreads();  // every wave is done with the tile
         if (more) stash();
     }
@@ -1173,12 +1181,11 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
         if (pl.prefix_slots > 0) {
             const int tiles = (p.NC + 15) / 16;
             const int groups = (tiles + 15) / 16;
-            const int waves = tiles < 16 ? tiles : 16;
-            dim3 grid(pl.prefix_slots, a.Hkv, groups);
+            dim3 grid(pl.prefix_slots, a.Hkv, groups);  // 16 waves: all load, the group's tiles compute
             if (a.D == 128)
-                hipLaunchKernelGGL(prefix_bf16_kernel<128>, grid, dim3(waves * 64), 0, stream, p);
+                hipLaunchKernelGGL(prefix_bf16_kernel<128>, grid, dim3(1024), 0, stream, p);
             else
-                hipLaunchKernelGGL(prefix_bf16_kernel<64>, grid, dim3(waves * 64), 0, stream, p);
+                hipLaunchKernelGGL(prefix_bf16_kernel<64>, grid, dim3(1024), 0, stream, p);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
