@@ -660,7 +660,7 @@ struct PrefixLds {
     static constexpr int KP = D + 8;  // K tile pitch (bf16)
     static constexpr int VP = D + 4;  // V tile pitch (bf16)
     static constexpr int kTile = 128; // keys per tile (two halves of 64 for the products)
-    uint16_t ks[kTile][KP];
+    alignas(16) uint16_t ks[kTile][KP];  // rows of KP*2 = 16*(D/8+1) bytes: 16-byte reads
     uint16_t vs[kTile][VP];
 };
 
@@ -727,9 +727,13 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
     auto word_put = [&](int qi, uint4 v) {
         const int isv = qi >= kTile * VCH;
         const int r = (qi % (kTile * VCH)) / VCH, dc = qi % VCH;
-        uint16_t* dst = isv ? &S.vs[r][dc * 8] : &S.ks[r][dc * 8];
-        reinterpret_cast<uint2*>(dst)[0] = make_uint2(v.x, v.y);
-        reinterpret_cast<uint2*>(dst)[1] = make_uint2(v.z, v.w);
+        if (isv) {
+            uint2* dst = reinterpret_cast<uint2*>(&S.vs[r][dc * 8]);  // V rows are 8-byte aligned
+            dst[0] = make_uint2(v.x, v.y);
+            dst[1] = make_uint2(v.z, v.w);
+        } else {
+            *reinterpret_cast<uint4*>(&S.ks[r][dc * 8]) = v;
+        }
     };
     uint4 nx[kPL];
     auto issue = [&](int tb) {
@@ -769,17 +773,26 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
             floatx4 acc[4];
             float mt = -INFINITY;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                acc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < 4; ++kt) acc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            // one slice of D at a time: two 16-key operands are read together,
+            // then feed two independent products
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const uint2* src =
-                        reinterpret_cast<const uint2*>(&S.ks[half * 64 + kt * 16 + col16][kg * 8 + 32 * kk]);
-                    uint2 lo = src[0], hi = src[1];
-                    uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    bf16x8 ka = *reinterpret_cast<bf16x8*>(&u);
-                    acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv[kk], acc[kt], 0, 0, 0);
+            for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+                for (int k0 = 0; k0 < 4; k0 += 2) {
+                    bf16x8 ka[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        ka[u] = *reinterpret_cast<const bf16x8*>(
+                            &S.ks[half * 64 + (k0 + u) * 16 + col16][kg * 8 + 32 * kk]);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        acc[k0 + u] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u], qv[kk], acc[k0 + u], 0, 0, 0);
                 }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = hb + kt * 16 + kg * 4 + e;
@@ -807,12 +820,18 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
             for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
+                // V^T operands of 16 keys: lane (d = dt*16 + col16) gets keys
+                // kt*16 + kg*4 .. +3; four reads issue before their products
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    // V^T operand: lane (d = dt*16 + col16) gets keys kt*16 + kg*4 .. +3
-                    const shortx4 va =
-                        lds_read_tr16(vt_lane + (half * 64 + kt * 16) * PrefixLds<D>::VP + dt * 16);
-                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kt], o[dt], 0, 0, 0);
+                for (int d0 = 0; d0 < DT; d0 += 4) {
+                    shortx4 va[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        va[u] = lds_read_tr16(vt_lane + (half * 64 + kt * 16) * PrefixLds<D>::VP +
+                                              (d0 + u) * 16);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        o[d0 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[u], pb[kt], o[d0 + u], 0, 0, 0);
                 }
             }
         }
