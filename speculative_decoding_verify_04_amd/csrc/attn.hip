@@ -851,6 +851,185 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
     }
 }
 
+// D = 128 form of the prefix kernel whose K/V tiles reach LDS through the
+// direct global-to-LDS load (global_load_lds_dwordx4): two tile buffers, one
+// barrier per tile and no staging registers.  Each wave-wide load writes
+// 64 x 16 contiguous bytes of LDS, so rows are stored unpadded (256 bytes);
+// the 16-byte chunk c of row r is stored at position c ^ swz(r), which puts
+// the 16-byte K reads of 16 consecutive rows and the transposed 8-byte V reads
+// of 16 rows x 2 chunks on distinct LDS banks.
+// One tile buffer; the kernel holds two as separate LDS objects, so the
+// compiler can tell reads of one from direct loads still landing in the other.
+struct PrefixDmaBuf {
+    static constexpr int kTile = 128;   // keys per tile
+    static constexpr int kChunks = 16;  // 16-byte chunks per 128-wide bf16 row
+    uint4 k[kTile * kChunks];
+    uint4 v[kTile * kChunks];
+};
+
+__device__ __forceinline__ int prefix_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+// grid and block as for prefix_bf16_kernel; blockDim.x is a multiple of 64.
+__global__ __launch_bounds__(1024) void prefix_dma_kernel(AttnParams p) {
+    constexpr int D = 128, KK = D / 32, DT = D / 16;
+    constexpr int kTile = PrefixDmaBuf::kTile, kCh = PrefixDmaBuf::kChunks;
+    constexpr int kBlocks = 2 * kTile * kCh / 64;  // 1 KB blocks of K and V per tile
+    __shared__ PrefixDmaBuf SA, SB;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int x = blockIdx.x, g = blockIdx.y;
+    const int t_begin = x * p.prefix_chunk;
+    const int t_end = min(p.prefix_len, t_begin + p.prefix_chunk);
+    const int col16 = lane & 15, kg = lane >> 4;
+    const int tile = blockIdx.z * 16 + w;
+    const int cg = tile * 16 + col16;           // global column: b*CPG + hh*(K_b+1) + j
+    const bool active = tile * 16 < p.NC;
+    int k1c = 1, q0c = 0;                       // the column's sequence
+    if (cg < p.NC) {
+        k1c = seq_k1(p, cg / p.CPG);
+        q0c = seq_q0(p, cg / p.CPG);
+    }
+    const bool col_ok = (cg < p.NC) && (cg % p.CPG < p.G * k1c);
+
+    bf16x8 qv[KK];
+    if (col_ok) {
+        const int cl = cg % p.CPG;
+        const int hh = cl / k1c, j = cl % k1c;
+        const uint16_t* qp =
+            p.q + (static_cast<size_t>(q0c + j) * p.Hq + g * p.G + hh) * D + kg * 8;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qv[kk] = *reinterpret_cast<const bf16x8*>(qp + 32 * kk);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[kk][e] = static_cast<__bf16>(0.0f);
+    }
+
+    floatx4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.0f;
+    const size_t row_stride = static_cast<size_t>(p.Hkv) * D;
+
+    // block b of a tile: K rows 4b..4b+3 (b < kBlocks/2), else V rows of
+    // b - kBlocks/2; lane l fills row 4*(b mod kBlocks/2) + l/16, position l%16
+    const int lrow = lane >> 4, lpos = lane & 15;
+    auto issue = [&](int tb, PrefixDmaBuf& B) {
+        for (int b = w; b < kBlocks; b += nwaves) {
+            const int isv = b >= kBlocks / 2;
+            const int bb = isv ? b - kBlocks / 2 : b;
+            const int r = bb * 4 + lrow;
+            const int c = lpos ^ prefix_swz(r);
+            const int t = min(tb + r, p.prefix_len - 1);
+            const uint16_t* src = (isv ? p.v_prefix : p.k_prefix) + static_cast<size_t>(t) * row_stride +
+                                  static_cast<size_t>(g) * D + c * 8;
+            uint4* dst = (isv ? B.v : B.k) + bb * 64;
+            __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+        }
+    };
+    // K operand: row half*64 + kt*16 + col16 (row mod 16 = col16), logical
+    // chunk kg + 4*kk, stored at (kg ^ (sk & 3)) + 4*(kk ^ (sk >> 2))
+    const int sk = prefix_swz(col16);
+    const int kcol = col16 * kCh + (kg ^ (sk & 3));
+    const int sk2 = sk >> 2;
+    // V^T operand: row half*64 + kt*16 + rv with rv = kg*4 + col16/4, logical
+    // chunk 2*dt + h (h = (col16 & 3) >> 1), 8-byte half (col16 & 1); stored
+    // at chunk 2*(dt ^ (sv >> 1)) + (h ^ (sv & 1))
+    const int rv = kg * 4 + (col16 >> 2);
+    const int sv = prefix_swz(rv);
+    const int sv1 = sv >> 1;
+    const int vcol = rv * D + 8 * (((col16 & 3) >> 1) ^ (sv & 1)) + 4 * (col16 & 1);  // bf16 elements
+
+    // products of the tile at tb held in C, while the next tile loads into N
+    auto step = [&](int tb, const PrefixDmaBuf& C, PrefixDmaBuf& N) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile are in LDS
+        __syncthreads();                // ... and every wave's; N is no longer read
+        if (tb + kTile < t_end) issue(tb + kTile, N);  // in flight during the products
+        const uint4* kb = C.k;
+        const uint16_t* vb = reinterpret_cast<const uint16_t*>(C.v);
+#pragma unroll 1
+        for (int half = 0; half < kTile / 64; ++half) {
+            const int hb = tb + half * 64;
+            if (!(active && hb < t_end)) continue;
+            floatx4 acc[4];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) acc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const uint4* kr = kb + (half * 64) * kCh + kcol + 4 * (kk ^ sk2);
+#pragma unroll
+                for (int k0 = 0; k0 < 4; k0 += 2) {
+                    bf16x8 ka[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        ka[u] = *reinterpret_cast<const bf16x8*>(kr + (k0 + u) * 16 * kCh);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        acc[k0 + u] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u], qv[kk], acc[k0 + u], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = hb + kt * 16 + kg * 4 + e;
+                    acc[kt][e] = (t < t_end) ? acc[kt][e] * p.scale_log2 : -INFINITY;
+                    mt = fmaxf(mt, acc[kt][e]);
+                }
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float mnew = fmaxf(mrun, mt);   // finite: every half computed has a valid key
+            const float alpha = exp2f(mrun - mnew);
+            float ps = 0.0f;
+            shortx4 pb[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pe = exp2f(acc[kt][e] - mnew);
+                    ps += pe;
+                    pb[kt][e] = static_cast<short>(f32_to_bf16(pe));
+                }
+            lrun = lrun * alpha + ps;
+            mrun = mnew;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                const uint16_t* vr = vb + (half * 64 + kt * 16) * D + vcol;
+#pragma unroll
+                for (int d0 = 0; d0 < DT; d0 += 4) {
+                    shortx4 va[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) va[u] = lds_read_tr16(vr + 16 * ((d0 + u) ^ sv1));
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        o[d0 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[u], pb[kt], o[d0 + u], 0, 0, 0);
+                }
+            }
+        }
+    };
+    if (t_begin < t_end) issue(t_begin, SA);
+    for (int tb = t_begin; tb < t_end; tb += 2 * kTile) {
+        step(tb, SA, SB);
+        if (tb + kTile < t_end) step(tb + kTile, SB, SA);
+    }
+    lrun += __shfl_xor(lrun, 16, 64);
+    lrun += __shfl_xor(lrun, 32, 64);
+    if (cg < p.NC) {
+        const size_t base = (static_cast<size_t>(x) * p.Hkv + g) * p.NC + cg;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p.pre_o[base * D + dt * 16 + kg * 4 + e] = o[dt][e];
+        if (kg == 0) p.pre_ml[base] = make_float2(mrun, lrun);
+    }
+}
+
 // ---------------------------------------------------------------- fp32 path
 
 // mode 0: per-sequence chunks (grid.x = slot); mode 1: prefix chunks (grid.x = chunk).
@@ -1202,7 +1381,7 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
             const int groups = (tiles + 15) / 16;
             dim3 grid(pl.prefix_slots, a.Hkv, groups);  // 16 waves: all load, the group's tiles compute
             if (a.D == 128)
-                hipLaunchKernelGGL(prefix_bf16_kernel<128>, grid, dim3(1024), 0, stream, p);
+                hipLaunchKernelGGL(prefix_dma_kernel, grid, dim3(1024), 0, stream, p);
             else
                 hipLaunchKernelGGL(prefix_bf16_kernel<64>, grid, dim3(1024), 0, stream, p);
             hipError_t e = hipGetLastError();
