@@ -23,9 +23,11 @@
 //       merges all partials (log-sum-exp) and writes the output rows; the
 //       hand-off uses coherent stores/loads and an arrival counter, no cache
 //       flush.
-//   prefix_bf16_kernel  one workgroup per (prefix chunk, kv head, column
-//       group): every query column of every sequence against one 64-key LDS
-//       tile at a time, so the shared prefix is read from HBM once.
+//   prefix_dma_kernel (D = 128) / prefix_bf16_kernel (D = 64)  one
+//       workgroup per (prefix chunk, kv head, column group): every query
+//       column of every sequence against one 128-key LDS tile at a time, so
+//       the shared prefix is read from HBM once; the D = 128 form fills its
+//       two tile buffers with direct global-to-LDS loads.
 //   attn_f32_kernel  fp32 VALU path (small head dims, fp32 inputs).
 //   merge_kernel  log-sum-exp merge of the fp32 path's partials.
 // Scores are kept in the log2 domain (scale * log2(e) folded into S).
