@@ -131,6 +131,17 @@ SMALL_ATTN = {
     "bf16_prefix_gqa_many_cols": W.small_variant(W.CONFIGS["prefix_b32k4"], B=60, K=4, Hq=8,
                                                  Hkv=2, prefix_len=1100, len_lo=0, len_hi=20,
                                                  V=64),
+    # prefix kernel edge cases: head dim 64 (register-staged tiles), a prefix
+    # shorter than one 64-key half, a second chunk ending inside the second
+    # half of its only tile, and prefix chunks filled exactly
+    "bf16_prefix_d64": W.small_variant(W.CONFIGS["prefix_b32k4"], B=5, Hq=4, Hkv=2, D=64,
+                                       prefix_len=333, len_lo=0, len_hi=50, V=64),
+    "bf16_prefix_tiny": W.small_variant(W.CONFIGS["prefix_b32k4"], B=3, Hq=2, Hkv=2,
+                                        prefix_len=5, len_lo=0, len_hi=30, V=64),
+    "bf16_prefix_half_tail": W.small_variant(W.CONFIGS["prefix_b32k4"], B=4, Hq=4, Hkv=4,
+                                             prefix_len=1124, len_lo=0, len_hi=30, V=64),
+    "bf16_prefix_exact_chunks": W.small_variant(W.CONFIGS["prefix_b32k4"], B=2, Hq=2, Hkv=2,
+                                                prefix_len=2048, len_lo=0, len_hi=10, V=64),
     "bf16_k0_single_query": W.small_variant(W.CONFIGS["bass_b8k5"], K=0, B=3, Hq=2, Hkv=2,
                                             len_lo=0, len_hi=200, V=64),
     "bf16_all_empty_cache": W.small_variant(W.CONFIGS["bass_b8k5"], B=4, Hq=2, Hkv=2, len_lo=0,
