@@ -163,6 +163,24 @@ __device__ __forceinline__ shortx4 lds_read_tr16(const uint16_t* p) {
     return shortx4{r[0], r[1], r[2], r[3]};
 }
 
+// Max and sum over the lanes {l, l^16, l^32, l^48} (the four key groups of one
+// query column) with the gfx950 lane swaps: v_permlane16_swap exchanges rows 0
+// and 1, 2 and 3 (16 lanes each) between its two operands, v_permlane32_swap
+// the two halves of the wave; with both operands equal to x, the two results
+// hold x and its partner's value on every lane.  VALU only, no LDS traffic.
+__device__ __forceinline__ float colmax4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float colsum4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int D, int NCT>
 struct DecLds {
     static constexpr int VP = D + 4;   // V slice pitch (bf16)
@@ -574,8 +592,7 @@ void decode_bf16_kernel(AttnParams p) {
                 s[ee] = (full || tt < lim[ct]) ? acc[ct][ee] * p.scale_log2 : -INFINITY;
                 mt = fmaxf(mt, s[ee]);
             }
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            mt = colmax4(mt);
             const float mnew = fmaxf(mrun[ct], mt);
             float alpha = 1.0f;
             shortx4 pb;
@@ -604,8 +621,7 @@ void decode_bf16_kernel(AttnParams p) {
 
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-        lrun[ct] += __shfl_xor(lrun[ct], 16, 64);
-        lrun[ct] += __shfl_xor(lrun[ct], 32, 64);
+        lrun[ct] = colsum4(lrun[ct]);
     }
 
     // combine the 4 waves (fixed order) in two halves of the head dim; the
@@ -802,8 +818,7 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
                     mt = fmaxf(mt, acc[kt][e]);
                 }
             }
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            mt = colmax4(mt);
             const float mnew = fmaxf(mrun, mt);   // finite: every half computed has a valid key
             const float alpha = exp2f(mrun - mnew);
             float ps = 0.0f;
@@ -841,8 +856,7 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
         __syncthreads();  // every wave is done with the tile
         if (more) stash();
     }
-    lrun += __shfl_xor(lrun, 16, 64);
-    lrun += __shfl_xor(lrun, 32, 64);
+    lrun = colsum4(lrun);
     if (cg < p.NC) {
         const size_t base = (static_cast<size_t>(x) * p.Hkv + g) * p.NC + cg;
 #pragma unroll
@@ -982,8 +996,7 @@ __global__ __launch_bounds__(1024) void prefix_dma_kernel(AttnParams p) {
                     mt = fmaxf(mt, acc[kt][e]);
                 }
             }
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            mt = colmax4(mt);
             const float mnew = fmaxf(mrun, mt);   // finite: every half computed has a valid key
             const float alpha = exp2f(mrun - mnew);
             float ps = 0.0f;
@@ -1020,8 +1033,7 @@ __global__ __launch_bounds__(1024) void prefix_dma_kernel(AttnParams p) {
         step(tb, SA, SB);
         if (tb + kTile < t_end) step(tb + kTile, SB, SA);
     }
-    lrun += __shfl_xor(lrun, 16, 64);
-    lrun += __shfl_xor(lrun, 32, 64);
+    lrun = colsum4(lrun);
     if (cg < p.NC) {
         const size_t base = (static_cast<size_t>(x) * p.Hkv + g) * p.NC + cg;
 #pragma unroll
