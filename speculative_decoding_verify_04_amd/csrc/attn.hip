@@ -897,15 +897,25 @@ __global__ __launch_bounds__(1024) void prefix_dma_kernel(AttnParams p) {
     const int t_begin = x * p.prefix_chunk;
     const int t_end = min(p.prefix_len, t_begin + p.prefix_chunk);
     const int col16 = lane & 15, kg = lane >> 4;
-    const int tile = blockIdx.z * 16 + w;
+    // Waves to column tiles: with more than 8 tiles in the group, 16 - ntiles
+    // of them are split so that two waves take one 64-key half of every K/V
+    // tile each (10 tiles: 4 whole + 12 half waves, five half-tile units on
+    // each SIMD instead of 3/3/2/2 whole tiles); with at most 8, all are
+    // split.  A split pair merges its two softmax states at the end.
+    const int ntiles = min(16, (p.NC + 15) / 16 - static_cast<int>(blockIdx.z) * 16);
+    const int nsplit = ntiles <= 8 ? ntiles : 16 - ntiles;
+    const int nwhole = ntiles - nsplit;
+    const int tile_l = w < nwhole ? w : nwhole + (w - nwhole) / 2;
+    const int myhalf = w < nwhole ? -1 : (w - nwhole) & 1;  // -1: both halves
+    const int tile = blockIdx.z * 16 + tile_l;
     const int cg = tile * 16 + col16;           // global column: b*CPG + hh*(K_b+1) + j
-    const bool active = tile * 16 < p.NC;
+    const bool active = tile_l < ntiles;
     int k1c = 1, q0c = 0;                       // the column's sequence
-    if (cg < p.NC) {
+    if (active && cg < p.NC) {
         k1c = seq_k1(p, cg / p.CPG);
         q0c = seq_q0(p, cg / p.CPG);
     }
-    const bool col_ok = (cg < p.NC) && (cg % p.CPG < p.G * k1c);
+    const bool col_ok = active && (cg < p.NC) && (cg % p.CPG < p.G * k1c);
 
     bf16x8 qv[KK];
     if (col_ok) {
@@ -967,7 +977,7 @@ __global__ __launch_bounds__(1024) void prefix_dma_kernel(AttnParams p) {
 #pragma unroll 1
         for (int half = 0; half < kTile / 64; ++half) {
             const int hb = tb + half * 64;
-            if (!(active && hb < t_end)) continue;
+            if (!(active && hb < t_end && (myhalf < 0 || myhalf == half))) continue;
             floatx4 acc[4];
             float mt = -INFINITY;
 #pragma unroll
@@ -1034,7 +1044,34 @@ __global__ __launch_bounds__(1024) void prefix_dma_kernel(AttnParams p) {
         if (tb + kTile < t_end) step(tb + kTile, SB, SA);
     }
     lrun = colsum4(lrun);
-    if (cg < p.NC) {
+    // split pairs: the second-half wave hands (O, m, l) to the first-half wave
+    // through the tile buffers, which no wave reads any more
+    constexpr int kXf = DT * 4 + 2;  // floats per lane
+    __syncthreads();
+    const int sidx = max(tile_l - nwhole, 0);  // index of the split tile (when myhalf >= 0)
+    float* xo = reinterpret_cast<float*>(sidx < 4 ? &SA : &SB) + ((sidx & 3) * 64 + lane) * kXf;
+    if (active && myhalf == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xo[dt * 4 + e] = o[dt][e];
+        xo[DT * 4] = mrun;
+        xo[DT * 4 + 1] = lrun;
+    }
+    __syncthreads();
+    if (active && myhalf == 0) {
+        const float m1 = xo[DT * 4], l1 = xo[DT * 4 + 1];
+        const float mm = fmaxf(mrun, m1);
+        const float f0 = (mrun == -INFINITY) ? 0.0f : exp2f(mrun - mm);
+        const float f1 = (m1 == -INFINITY) ? 0.0f : exp2f(m1 - mm);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[dt][e] = o[dt][e] * f0 + xo[dt * 4 + e] * f1;
+        lrun = lrun * f0 + l1 * f1;
+        mrun = mm;
+    }
+    if (active && myhalf != 1 && cg < p.NC) {
         const size_t base = (static_cast<size_t>(x) * p.Hkv + g) * p.NC + cg;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
