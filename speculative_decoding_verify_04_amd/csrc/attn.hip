@@ -997,14 +997,23 @@ __global__ __launch_bounds__(1024) void prefix_dma_kernel(AttnParams p) {
                             __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u], qv[kk], acc[k0 + u], 0, 0, 0);
                 }
             }
+            if (hb + 64 <= t_end) {  // every key of the half is in the chunk
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = hb + kt * 16 + kg * 4 + e;
-                    acc[kt][e] = (t < t_end) ? acc[kt][e] * p.scale_log2 : -INFINITY;
-                    mt = fmaxf(mt, acc[kt][e]);
-                }
+                    for (int e = 0; e < 4; ++e) {
+                        acc[kt][e] *= p.scale_log2;
+                        mt = fmaxf(mt, acc[kt][e]);
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = hb + kt * 16 + kg * 4 + e;
+                        acc[kt][e] = (t < t_end) ? acc[kt][e] * p.scale_log2 : -INFINITY;
+                        mt = fmaxf(mt, acc[kt][e]);
+                    }
             }
             mt = colmax4(mt);
             const float mnew = fmaxf(mrun, mt);   // finite: every half computed has a valid key
