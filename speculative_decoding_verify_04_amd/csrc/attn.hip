@@ -885,7 +885,8 @@ struct PrefixDmaBuf {
 
 __device__ __forceinline__ int prefix_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
-// grid and block as for prefix_bf16_kernel; blockDim.x is a multiple of 64.
+// grid as for prefix_bf16_kernel; block: 1024 threads (16 waves), which the
+// mapping of waves to column tiles below assumes.
 __global__ __launch_bounds__(1024) void prefix_dma_kernel(AttnParams p) {
     constexpr int D = 128, KK = D / 32, DT = D / 16;
     constexpr int kTile = PrefixDmaBuf::kTile, kCh = PrefixDmaBuf::kChunks;
