@@ -264,6 +264,22 @@ static int row_dist(const float *z, int V, double T, int top_k, double top_p, do
     return SPECREF_OK;
 }
 
+/*
+ * The modified distribution of one row of logits (temperature, then top-k,
+ * then nucleus, as row_dist states), exported so that a check can test
+ * whether a token has positive probability under q' or (q' - p')_+.
+ * pi [V] out; *ambiguous as in row_dist.
+ */
+int specref_row_dist(const float *z, int V, double temperature, int top_k, double top_p,
+                     double *pi, int32_t *ambiguous) {
+    if (V < 1 || !(temperature > 0.0) || !(top_p > 0.0) || top_p > 1.0 || top_k < 0)
+        return SPECREF_EINVAL;
+    int amb = 0;
+    int rc = row_dist(z, V, temperature, top_k, top_p, pi, &amb);
+    if (ambiguous) *ambiguous = amb;
+    return rc;
+}
+
 static int argmax_row(const float *z, int V) {
     int best = 0;
     for (int t = 1; t < V; ++t)

@@ -25,6 +25,7 @@ def load(path: str):
     h.specref_verify_attn.restype = ctypes.c_int
     h.specref_accept.restype = ctypes.c_int
     h.specref_compact_kv.restype = ctypes.c_int
+    h.specref_row_dist.restype = ctypes.c_int
     return h
 
 
@@ -118,6 +119,22 @@ def accept(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temper
         raise ValueError(f"specref_accept failed: {rc}")
     return {"n_accepted": n, "out_tokens": out, "q_tok": qt, "p_tok": pt, "flag_pos": fp,
             "n_decisions": int(nd.value), "n_flagged": int(nf.value)}
+
+
+def row_dist(z, temperature, top_p, top_k=0, lib_=None):
+    """The modified distribution pi' of one row of logits z [V] (temperature,
+    top-k, nucleus), in float64; ``temperature`` and ``top_p`` are rounded to
+    float32 first, as the GPU library receives them."""
+    zz = _c(z, np.float32).reshape(-1)
+    V = int(zz.shape[0])
+    pi = np.zeros(V, np.float64)
+    amb = ctypes.c_int32(0)
+    rc = lib(lib_).specref_row_dist(
+        _p(zz), V, ctypes.c_double(float(np.float32(temperature))), int(top_k),
+        ctypes.c_double(float(np.float32(top_p))), _p(pi), ctypes.byref(amb))
+    if rc:
+        raise ValueError(f"specref_row_dist failed: {rc}")
+    return pi
 
 
 def compact_kv(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, k_new, v_new,

@@ -217,3 +217,37 @@ def check_counts(res, draft_tokens, K, V):
         assert np.array_equal(out[b, : n[b]], draft_tokens[b, : n[b]])
         assert 0 <= out[b, n[b]] < V
         assert np.all(out[b, e:] == -1)
+
+
+# ---------------------------------------------------------------- fixed-value draw cases
+
+def load_draw_cases(golden_dir):
+    """Hand-derived verify rounds (tests/golden/draw_zero_weight_cases.json)
+    whose emitted token is fixed by the inverse-CDF convention: ids of zero
+    weight are never drawn, even at u = 0."""
+    import json
+    import os
+    with open(os.path.join(golden_dir, "draw_zero_weight_cases.json")) as f:
+        gold = json.load(f)
+    out = []
+    for c in gold["cases"]:
+        zt = np.asarray(c["target_logits"], np.float32)
+        K = zt.shape[0] - 1
+        V = zt.shape[1]
+        zd = np.asarray(c["draft_logits"], np.float32).reshape(K, V)
+        out.append(dict(name=c["name"], zt=zt[None], zd=zd[None],
+                        tok=np.asarray(c["draft_tokens"], np.int32).reshape(1, K),
+                        ua=np.asarray(c["u_accept"], np.float32).reshape(1, K),
+                        us=np.asarray([c["u_sample"]], np.float32),
+                        T=c["temperature"], top_p=c["top_p"],
+                        n=c["n_accepted"], out=np.asarray(c["out_tokens"], np.int32)))
+    return out
+
+
+def check_draw_cases(sampler, golden_dir):
+    """Every case's n_accepted and out_tokens equal the hand-derived values."""
+    for c in load_draw_cases(golden_dir):
+        res = sampler(c["zt"], c["zd"], c["tok"], c["ua"], c["us"], c["T"], c["top_p"], False)
+        assert int(res["n_accepted"][0]) == c["n"], (c["name"], res["n_accepted"])
+        assert np.array_equal(np.asarray(res["out_tokens"][0]), c["out"]), \
+            (c["name"], res["out_tokens"][0], c["out"])

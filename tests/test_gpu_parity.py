@@ -9,6 +9,8 @@ Bars:
     flagged decisions must stay below 0.01% of all decisions.
   * compaction: bit-exact.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -65,8 +67,44 @@ def run_accept(w, t, greedy=None):
     return t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy()
 
 
-def compare_accept(n, toks, ref, K):
-    """Bit-exact outside flagged decisions.  Returns (#sequences compared fully)."""
+def check_flagged_valid(n_b, toks_b, zt_b, zd_b, drafts_b, T, top_p, top_k=0):
+    """A sequence released from the bit-exact comparison by a flagged decision
+    must still be a valid round: its first n_b tokens are the drafts, the token
+    at n_b has positive weight under the distribution it is drawn from --
+    (q'_n - p'_n)_+ after a rejection (q'_n when that has no mass), q'_K for the
+    bonus -- and the rest is -1.  ("Modified rejection sampling": an id of
+    weight zero has probability zero.)"""
+    K = drafts_b.shape[0]
+    assert 0 <= n_b <= K
+    assert np.array_equal(toks_b[:n_b], drafts_b[:n_b])
+    assert np.all(toks_b[n_b + 1:] == -1)
+    tok = int(toks_b[n_b])
+    V = zt_b.shape[-1]
+    assert 0 <= tok < V
+    q = R.row_dist(zt_b[n_b], T, top_p, top_k)
+    if n_b == K:
+        assert q[tok] > 0.0, ("bonus token of zero weight", tok)
+        return
+    p = R.row_dist(zd_b[n_b], T, top_p, top_k)
+    w = np.maximum(q - p, 0.0)
+    if w.sum() > 0.0:
+        assert w[tok] > 0.0, ("residual token of zero weight", n_b, tok)
+    else:
+        assert q[tok] > 0.0, ("fallback token of zero weight", n_b, tok)
+
+
+def rows_of(w, top_k=0):
+    """The inputs check_flagged_valid needs, from a workload."""
+    c = w.cfg
+    return (w.target_logits, None if c.greedy else w.draft_logits, w.draft_tokens,
+            c.temperature, c.top_p, top_k)
+
+
+def compare_accept(n, toks, ref, K, rows=None):
+    """Bit-exact outside flagged decisions; a flagged sequence must agree before
+    its flag and, given its inputs ``rows`` = (target logits, draft logits,
+    drafts, T, top_p, top_k), be a valid round (check_flagged_valid).
+    Returns (#sequences compared fully)."""
     full = 0
     for b in range(n.shape[0]):
         f, nr = int(ref["flag_pos"][b]), int(ref["n_accepted"][b])
@@ -77,6 +115,10 @@ def compare_accept(n, toks, ref, K):
         else:
             assert n[b] >= f, (b, n[b], f)
             assert np.array_equal(toks[b, :f], ref["out_tokens"][b, :f])
+            if rows is not None:
+                zt, zd, dr, T, tp, tk = rows
+                check_flagged_valid(int(n[b]), toks[b], zt[b], None if zd is None else zd[b],
+                                    dr[b], T, tp, tk)
     return full
 
 
@@ -255,8 +297,31 @@ def test_attention_bifurcated_equals_concatenated_gpu():
 FULL = ["bass_b8k5", "chinchilla_b1k4", "gqa_b64k8", "prefix_b32k4"]
 
 
+def oracle_attn_threaded(w, pairs):
+    """Oracle attention of the listed (row, head) pairs, split over host threads
+    (each thread calls the single-threaded oracle on its share; the foreign call
+    releases the interpreter lock).  Returns [len(pairs), D] float64."""
+    import concurrent.futures as cf
+    import os as _os
+    rows = np.asarray([r for r, _ in pairs], np.int32)
+    heads = np.asarray([h for _, h in pairs], np.int32)
+    n = rows.shape[0]
+    nthr = max(1, min(16, _os.cpu_count() or 1))
+    step = max(1, (n + 4 * nthr - 1) // (4 * nthr))
+    parts = [(i, min(n, i + step)) for i in range(0, n, step)]
+    out = np.zeros((n, w.cfg.D), np.float64)
+    with cf.ThreadPoolExecutor(nthr) as ex:
+        futs = {ex.submit(R.workload_attn, w, rows[a:b], heads[a:b]): (a, b) for a, b in parts}
+        for fu in cf.as_completed(futs):
+            a, b = futs[fu]
+            out[a:b] = fu.result()
+    return out
+
+
 @pytest.mark.parametrize("name", FULL)
-def test_attention_full_size_sampled(name):
+def test_attention_full_size_all_rows(name):
+    """Every output (row, head) of the full-size workload against the oracle,
+    in the launch configuration the benchmark times."""
     cfg = W.CONFIGS[name]
     say(f"[attn full] {name}: generating")
     w = W.make_workload(cfg, sub_seed=0)
@@ -264,17 +329,13 @@ def test_attention_full_size_sampled(name):
     say(f"[attn full] {name}: running B={cfg.B} K={cfg.K} Hq={cfg.Hq} Hkv={cfg.Hkv}")
     o = run_attn(w, t)
     assert np.isfinite(o).all()
-    rng = np.random.default_rng(5)
     R_ = cfg.rows
-    # the longest sequence's rows, the first and last rows, and random rows
-    bmax = int(np.argmax(w.kv_len))
-    rows = [0, R_ - 1, bmax * (cfg.K + 1), bmax * (cfg.K + 1) + cfg.K]
-    rows += list(rng.integers(0, R_, size=28))
-    heads = [0, cfg.Hq - 1] + list(rng.integers(0, cfg.Hq, size=len(rows) - 2))
-    ref = R.workload_attn(w, sel_rows=rows, sel_heads=heads)
-    got = o[rows, heads]
-    err = attn_errors(got, ref)
-    assert err.max() <= 1e-2, (name, float(err.max()))
+    pairs = [(r, h) for r in range(R_) for h in range(cfg.Hq)]
+    say(f"[attn full] {name}: oracle over {len(pairs)} (row, head) pairs")
+    ref = oracle_attn_threaded(w, pairs).reshape(R_, cfg.Hq, cfg.D)
+    err = attn_errors(o, ref)
+    say(f"[attn full] {name}: max row error {float(err.max()):.3e}")
+    assert err.max() <= 1e-2, (name, float(err.max()), np.unravel_index(np.argmax(err), err.shape))
 
 
 # ---------------------------------------------------------------- sampler
@@ -295,7 +356,7 @@ def test_accept_full_size(name):
         n, toks = run_accept(w, t)
         ref = R.workload_accept(w)
         budget.add(ref)
-        compare_accept(n, toks, ref, cfg.K)
+        compare_accept(n, toks, ref, cfg.K, rows_of(w))
         pins.check_counts({"n_accepted": n, "out_tokens": toks}, w.draft_tokens, cfg.K, cfg.V)
     budget.check()
 
@@ -312,7 +373,15 @@ def test_accept_many_sequences_small_vocab(logits):
     t = to_device(w, DEV, logits_dtype=torch.bfloat16 if logits == "bf16" else torch.float32)
     n, toks = run_accept(w, t)
     ref = R.workload_accept(w)
-    compare_accept(n, toks, ref, cfg.K)
+    compare_accept(n, toks, ref, cfg.K, rows_of(w))
+
+
+def test_accept_draw_zero_weight_cases():
+    """The hand-derived rounds of the oracle's draw pin, on the GPU: ids of zero
+    weight are never drawn (u = 0 included)."""
+    def sampler(zt, zd, tok, ua, us, T, top_p, greedy, top_k=0):
+        return gpu_sampler(zt, zd, tok, ua, us, T, top_p, greedy, top_k)
+    pins.check_draw_cases(sampler, os.path.join(os.path.dirname(__file__), "golden"))
 
 
 def test_accept_k0_bonus_only():
@@ -321,7 +390,7 @@ def test_accept_k0_bonus_only():
     t = to_device(w, DEV)
     n, toks = run_accept(w, t)
     ref = R.workload_accept(w)
-    compare_accept(n, toks, ref, 0)
+    compare_accept(n, toks, ref, 0, rows_of(w))
     assert np.all(n == 0)
 
 
@@ -333,7 +402,7 @@ def test_accept_p_equals_q_accepts_all():
     t = to_device(w, DEV)
     n, toks = run_accept(w, t)
     assert np.all(n == cfg.K)
-    compare_accept(n, toks, R.workload_accept(w), cfg.K)
+    compare_accept(n, toks, R.workload_accept(w), cfg.K, rows_of(w))
 
 
 def test_accept_flat_rows_use_exact_fallback():
@@ -346,7 +415,7 @@ def test_accept_flat_rows_use_exact_fallback():
     w.draft_tokens[:] = np.arange(cfg.B * cfg.K, dtype=np.int32).reshape(cfg.B, cfg.K) * 7
     t = to_device(w, DEV)
     n, toks = run_accept(w, t)
-    compare_accept(n, toks, R.workload_accept(w), cfg.K)
+    compare_accept(n, toks, R.workload_accept(w), cfg.K, rows_of(w))
 
 
 def test_accept_wide_rows_deep_threshold():
@@ -356,7 +425,7 @@ def test_accept_wide_rows_deep_threshold():
     w = W.make_workload(cfg, sub_seed=6, with_kv=False)
     t = to_device(w, DEV)
     n, toks = run_accept(w, t)
-    compare_accept(n, toks, R.workload_accept(w), cfg.K)
+    compare_accept(n, toks, R.workload_accept(w), cfg.K, rows_of(w))
 
 
 def test_accept_bad_token_sets_status():
@@ -389,7 +458,8 @@ def test_accept_gpu_matches_oracle_many_trials(case):
     zt, zd, tok, ua, us = pins.make_trials(c, n=200_000, seed=3)
     res = gpu_sampler(zt, zd, tok, ua, us, c.temperature, c.top_p, False, top_k=c.top_k)
     ref = R.accept(zt, zd, tok, ua, us, c.temperature, c.top_p, top_k=c.top_k)
-    compare_accept(res["n_accepted"], res["out_tokens"], ref, c.K)
+    compare_accept(res["n_accepted"], res["out_tokens"], ref, c.K,
+                   (zt, zd, tok, c.temperature, c.top_p, c.top_k))
 
 
 # ---------------------------------------------------------------- compaction
@@ -593,8 +663,10 @@ def run_accept_ragged(rw, t, greedy):
     return t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy()
 
 
-def compare_accept_ragged(n, toks, ref, cu):
-    """compare_accept for outputs packed by cu_q (b's tokens at cu[b] .. cu[b+1]-1)."""
+def compare_accept_ragged(n, toks, ref, cu, rows=None):
+    """compare_accept for outputs packed by cu_q (b's tokens at cu[b] .. cu[b+1]-1);
+    ``rows`` = (packed target logits, packed draft logits, packed drafts, T,
+    top_p, top_k) enables the validity check of flagged sequences."""
     full = 0
     for b in range(n.shape[0]):
         f, nr = int(ref["flag_pos"][b]), int(ref["n_accepted"][b])
@@ -605,6 +677,13 @@ def compare_accept_ragged(n, toks, ref, cu):
             full += 1
         else:
             assert n[b] >= f and np.array_equal(got[:f], exp[:f])
+            if rows is not None:
+                zt, zd, dr, T, tp, tk = rows
+                k = int(cu[b + 1] - cu[b]) - 1
+                d0 = int(cu[b]) - b
+                check_flagged_valid(int(n[b]), got, zt[cu[b]:cu[b + 1]],
+                                    None if zd is None else zd[d0:d0 + k], dr[d0:d0 + k], T,
+                                    tp, tk)
     return full
 
 
@@ -631,7 +710,10 @@ def test_accept_ragged(case):
                               rw.draft_tokens, rw.u_accept, w.u_sample, rw.cu_q,
                               base.temperature, base.top_p, base.greedy)
         budget.add(ref)
-        full += compare_accept_ragged(n, toks, ref, rw.cu_q)
+        full += compare_accept_ragged(
+            n, toks, ref, rw.cu_q,
+            (rw.target_logits, None if base.greedy else rw.draft_logits, rw.draft_tokens,
+             base.temperature, base.top_p, 0))
         assert np.all(n >= 0) and np.all(n <= rw.kb)
     budget.check()
     assert full >= 3 * base.B - 2
@@ -698,7 +780,8 @@ def test_workspace_reuse_across_lengths_and_draft_counts():
                                   rw.u_accept, rw.base.u_sample, rw.cu_q, cfg.temperature,
                                   cfg.top_p)
             compare_accept_ragged(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref,
-                                  rw.cu_q)
+                                  rw.cu_q, (rw.target_logits, rw.draft_logits, rw.draft_tokens,
+                                            cfg.temperature, cfg.top_p, 0))
 
 
 
@@ -726,7 +809,7 @@ def test_accept_topk(top_k, top_p):
                        base.temperature, base.top_p, top_k=top_k)
         budget.add(ref)
         full += compare_accept(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref,
-                               base.K)
+                               base.K, rows_of(w, top_k))
     budget.check()
     assert full >= 2 * base.B - 2
 
@@ -754,7 +837,7 @@ def test_accept_list_path_segment_counts(V, top_k, top_p):
                        base.temperature, base.top_p, top_k=top_k)
         budget.add(ref)
         full += compare_accept(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref,
-                               base.K)
+                               base.K, rows_of(w, top_k))
     budget.check()
     assert full >= 2 * base.B - 2
 
@@ -774,7 +857,8 @@ def test_accept_topk_ragged():
         ref = R.accept_ragged(rw.target_logits, rw.draft_logits, rw.draft_tokens, rw.u_accept,
                               w.u_sample, rw.cu_q, base.temperature, base.top_p, top_k=50)
         compare_accept_ragged(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref,
-                              rw.cu_q)
+                              rw.cu_q, (rw.target_logits, rw.draft_logits, rw.draft_tokens,
+                                        base.temperature, base.top_p, 50))
 
 
 # ---------------------------------------------------------------- maximum sizes
@@ -795,7 +879,8 @@ def test_accept_max_vocab_and_drafts(top_k):
     assert int(t.status.item()) == 0
     ref = R.accept(w.target_logits, w.draft_logits, w.draft_tokens, w.u_accept, w.u_sample,
                    cfg.temperature, cfg.top_p, top_k=top_k)
-    compare_accept(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref, cfg.K)
+    compare_accept(t.n_accepted.cpu().numpy(), t.out_tokens.cpu().numpy(), ref, cfg.K,
+                   rows_of(w, top_k))
 
 
 def test_attention_max_sequences_and_columns():

@@ -87,6 +87,15 @@ def _compaction(lib_):
     return True
 
 
+def _draw_cases(lib_):
+    try:
+        pins.check_draw_cases(oracle_sampler(lib_), os.path.join(os.path.dirname(__file__),
+                                                                 "golden"))
+    except AssertionError:
+        return False
+    return True
+
+
 MUTANTS = {
     "resample_from_q": (
         "tok = draw(mass > 0.0 ? w : q, V, (double)u_sample[b], &amb);",
@@ -104,6 +113,10 @@ MUTANTS = {
         "                    tok = draw(q, V, (double)u_sample[b], &amb);",
         "                    tok = draw(p, V, (double)u_sample[b], &amb);",
         _theorem1(["dirichlet_v4", "dirichlet_v8"])),
+    "draw_le": (
+        "        if (target < C) {",
+        "        if (target <= C) {",
+        _draw_cases),
     "temperature_multiplied": (
         "pi[t] = exp(((double)z[t] - m) / T);",
         "pi[t] = exp(((double)z[t] - m) * T);",

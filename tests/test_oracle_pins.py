@@ -159,6 +159,12 @@ def test_residual_closed_form_v2():
     assert abs(np.minimum(p, q).sum() - gold["accept_rate"]) < 1e-12
 
 
+def test_draw_never_picks_zero_weight_ids():
+    """Hand-derived rounds: the inverse-CDF draw skips ids of zero weight (they
+    have probability zero under q' and (q' - p')_+), also at u = 0."""
+    pins.check_draw_cases(oracle_sampler(), GOLDEN)
+
+
 def test_ambiguity_accounting():
     """A uniform exactly at q/p is flagged; a clear one is not."""
     z = np.log(np.array([0.5, 0.5]))[None, None].astype(np.float32)            # [1, 1, 2]
