@@ -126,6 +126,31 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      size_t workspace_bytes, sv_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * spec_verify_attn_noalloc -- spec_verify_attn without a workspace argument
+ * and without any device allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * operation, arguments (minus the workspace), kernels and results as
+ * spec_verify_attn; its arrival counters and split-K partial results live in
+ * a fixed 32 MiB device array of the library, one per GPU, held until the
+ * process ends.  The first call on a device looks the array up and enqueues a
+ * clear of its counters on `stream`; every completed call leaves them at zero.
+ * Limits: B * Hkv <= 65536, and the partial results of the call (the
+ * workspace spec_verify_attn_workspace_size reports, less its counter
+ * region) within 32 MiB - 256 KiB; larger problems return SV_ERR_UNSUPPORTED
+ * before anything is enqueued.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race.
+ * ------------------------------------------------------------------------ */
+int spec_verify_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                             const int64_t* kv_start, const int32_t* kv_len,
+                             const int32_t* kv_len_host, const void* k_new, const void* v_new,
+                             const void* k_prefix, const void* v_prefix, int prefix_len,
+                             void* out, int B, int K, int Hq, int Hkv, int D, int dtype,
+                             float softmax_scale, int32_t* status, sv_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * spec_accept -- modified rejection sampling, one verify round per sequence.
  *
  * [SpS] "Modified rejection sampling": with q the target and p the draft

@@ -45,6 +45,9 @@ def lib():
                                                       ctypes.POINTER(sz)]
         h.spec_verify_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32,
                                        i32, i32, i32, i32, ctypes.c_float, vp, vp, sz, vp]
+        h.spec_verify_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                               i32, i32, i32, i32, i32, i32, ctypes.c_float, vp,
+                                               vp]
         h.spec_accept_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(sz)]
         h.spec_accept.argtypes = [vp, vp, i32, vp, vp, vp, i32, i32, i32, ctypes.c_float,
                                   ctypes.c_float, i32, vp, vp, vp, vp, sz, vp]
@@ -66,6 +69,7 @@ def lib():
                                      vp]
         h.sv_set_kernel_events.argtypes = [vp, vp]
         for f in ("sv_set_kernel_events", "spec_verify_attn_workspace_size", "spec_verify_attn",
+                  "spec_verify_attn_noalloc",
                   "spec_accept_workspace_size", "spec_accept", "spec_compact_kv",
                   "spec_verify_attn_ragged_workspace_size", "spec_verify_attn_ragged",
                   "spec_accept_ragged_workspace_size", "spec_accept_ragged",
@@ -161,6 +165,37 @@ def spec_verify_attn(q, k_cache, v_cache, kv_start, kv_len, kv_len_host, k_new, 
         _ptr(k_new), _ptr(v_new), _ptr(k_prefix), _ptr(v_prefix), P, _ptr(out), B, K, Hq, Hkv,
         D, dt, float(softmax_scale), _ptr(status), _ptr(workspace), workspace.numel(),
         _stream(q)))
+    return out
+
+
+def spec_verify_attn_noalloc(q, k_cache, v_cache, kv_start, kv_len, kv_len_host, k_new, v_new,
+                             out, K, k_prefix=None, v_prefix=None, softmax_scale=0.0,
+                             status=None):
+    """spec_verify_attn without a workspace: the library's fixed per-GPU scratch
+    holds the counters and partial results (no device allocation here or in
+    the library).  Calls that overlap on one GPU race on that scratch."""
+    R, Hq, D = q.shape
+    _need(R % (K + 1) == 0, "q rows must be B*(K+1)")
+    B = R // (K + 1)
+    Hkv = k_cache.shape[1]
+    dt = _kv_dtype(q)
+    for t in (k_cache, v_cache, k_new, v_new, out):
+        _need(t.dtype == q.dtype and t.is_cuda, "KV tensors must share q's dtype and device")
+    _need(k_cache.shape[1:] == (Hkv, D) and v_cache.shape == k_cache.shape, "cache shape")
+    _need(k_new.shape == (R, Hkv, D) and v_new.shape == (R, Hkv, D), "new K/V shape")
+    _need(out.shape == q.shape, "out shape")
+    _need(kv_start.dtype == torch.int64 and kv_start.shape == (B,), "kv_start [B] int64")
+    _need(kv_len.dtype == torch.int32 and kv_len.shape == (B,), "kv_len [B] int32")
+    hl = [int(v) for v in (kv_len_host.tolist() if hasattr(kv_len_host, "tolist") else kv_len_host)]
+    _need(len(hl) == B, "kv_len_host has B entries")
+    P = 0
+    if k_prefix is not None:
+        P = k_prefix.shape[0]
+        _need(k_prefix.shape == (P, Hkv, D) and v_prefix.shape == (P, Hkv, D), "prefix shape")
+    _check(lib().spec_verify_attn_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_start), _ptr(kv_len), _host_i32(hl),
+        _ptr(k_new), _ptr(v_new), _ptr(k_prefix), _ptr(v_prefix), P, _ptr(out), B, K, Hq, Hkv,
+        D, dt, float(softmax_scale), _ptr(status), _stream(q)))
     return out
 
 

@@ -98,7 +98,7 @@ int attn_run(const void* q, const void* k_cache, const void* v_cache, const int6
              const void* v_new, const void* k_prefix, const void* v_prefix, int prefix_len,
              void* out, const int32_t* cu_q, const int32_t* cu_q_host, int rows, int B, int K,
              int Hq, int Hkv, int D, int dtype, float softmax_scale, int32_t* status,
-             void* workspace, size_t workspace_bytes, sv_stream_t stream) {
+             void* workspace, size_t workspace_bytes, sv_stream_t stream, bool noalloc = false) {
     int rc = check_attn_shape(B, K, Hq, Hkv, D, dtype, kv_len_host, prefix_len);
     if (rc) return rc;
     if (!q || !k_cache || !v_cache || !kv_start || !kv_len || !k_new || !v_new || !out)
@@ -114,9 +114,27 @@ int attn_run(const void* q, const void* k_cache, const void* v_cache, const int6
     const sv::AttnPlan plan =
         sv::attn_plan(B, K, Hq, Hkv, D, dtype == SV_BF16, kv_len_host, cu_q_host, prefix_len);
     if (!plan.ok) return fail(SV_ERR_UNSUPPORTED, "KV length bound too long (bf16: at most 2^25 keys per sequence, 2^30 64-key tiles in all)");
-    if (!workspace || workspace_bytes < plan.bytes)
+    void* counters = nullptr;
+    if (noalloc) {
+        // the library's fixed scratch: counters in its counter region, the
+        // partial results in its data region (sizes checked before any launch)
+        size_t cbytes = 0, dbytes = 0;
+        sv::noalloc_limits(&cbytes, &dbytes);
+        if (plan.counter_bytes > cbytes)
+            return fail(SV_ERR_UNSUPPORTED, "B*Hkv = %lld arrival counters exceed the %zu of the "
+                        "fixed scratch", static_cast<long long>(B) * Hkv, cbytes / 4);
+        if (plan.bytes - plan.counter_bytes > dbytes)
+            return fail(SV_ERR_UNSUPPORTED, "%zu bytes of partial results exceed the %zu-byte "
+                        "fixed scratch (use spec_verify_attn with a workspace)",
+                        plan.bytes - plan.counter_bytes, dbytes);
+        hipError_t e = sv::noalloc_scratch(as_stream(stream), &counters, &cbytes, &workspace,
+                                           &workspace_bytes);
+        if (e != hipSuccess)
+            return fail(SV_ERR_HIP, "scratch set-up failed: %s", hipGetErrorString(e));
+    } else if (!workspace || workspace_bytes < plan.bytes) {
         return fail(SV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.bytes,
                     workspace ? workspace_bytes : static_cast<size_t>(0));
+    }
     sv::AttnArgs a{};
     a.q = q;
     a.k_cache = k_cache;
@@ -140,6 +158,7 @@ int attn_run(const void* q, const void* k_cache, const void* v_cache, const int6
     a.prefix_len = prefix_len;
     a.scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
     a.workspace = workspace;
+    a.counters = counters;
     a.ev_start = g_ev_start;
     a.ev_stop = g_ev_stop;
     hipError_t e = sv::attn_launch(a, plan, as_stream(stream));
@@ -279,6 +298,20 @@ int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
     return attn_run(q, k_cache, v_cache, kv_start, kv_len, kv_len_host, k_new, v_new, k_prefix,
                     v_prefix, prefix_len, out, nullptr, nullptr, static_cast<int>(rows), B, K, Hq,
                     Hkv, D, dtype, softmax_scale, status, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                             const int64_t* kv_start, const int32_t* kv_len,
+                             const int32_t* kv_len_host, const void* k_new, const void* v_new,
+                             const void* k_prefix, const void* v_prefix, int prefix_len,
+                             void* out, int B, int K, int Hq, int Hkv, int D, int dtype,
+                             float softmax_scale, int32_t* status, sv_stream_t stream) {
+    const long long rows = static_cast<long long>(B) * (K + 1);
+    if (B >= 1 && K >= 0 && rows > 0x7FFFFFFF)
+        return fail(SV_ERR_UNSUPPORTED, "B*(K+1) above 2^31 - 1");
+    return attn_run(q, k_cache, v_cache, kv_start, kv_len, kv_len_host, k_new, v_new, k_prefix,
+                    v_prefix, prefix_len, out, nullptr, nullptr, static_cast<int>(rows), B, K, Hq,
+                    Hkv, D, dtype, softmax_scale, status, nullptr, 0, stream, true);
 }
 
 int spec_verify_attn_ragged_workspace_size(int B, int Hq, int Hkv, int D, int dtype,

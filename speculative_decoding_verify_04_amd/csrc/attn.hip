@@ -1364,9 +1364,9 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
     }
     // The arrival counters come first: their place depends on B and Hkv only,
     // so calls with other lengths or draft counts never put data over them.
-    size_t off = 0;
+    pl.counter_bytes = (static_cast<size_t>(B) * Hkv * 4 + 255) & ~static_cast<size_t>(255);
+    size_t off = pl.counter_bytes;
     auto take = [&](size_t n) { off = (off + 255) & ~static_cast<size_t>(255); off += n; };
-    take(static_cast<size_t>(B) * Hkv * 4);
     take(static_cast<size_t>(B) * 4);
     take(static_cast<size_t>(slots) * CPG * D * 4);
     take(static_cast<size_t>(slots) * CPG * 8);
@@ -1419,7 +1419,14 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
     p.bf16 = a.bf16;
     p.scale_log2 = a.scale * kLog2e;
 
+    // counters, then the data region (its layout as in attn_plan)
     char* base = static_cast<char*>(a.workspace);
+    if (a.counters) {
+        p.merge_cnt = static_cast<int*>(a.counters);
+    } else {
+        p.merge_cnt = reinterpret_cast<int*>(base);
+        base += pl.counter_bytes;
+    }
     size_t off = 0;
     auto take = [&](size_t n) {
         off = (off + 255) & ~static_cast<size_t>(255);
@@ -1429,7 +1436,6 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
     };
     const size_t CPG = p.CPG, NC = p.NC;
     const size_t pslots_all = a.bf16 ? static_cast<size_t>(pl.slots) : static_cast<size_t>(pl.slots) * a.Hkv;
-    p.merge_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * a.Hkv * 4));
     p.seq_base = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * 4));
     p.part_o = reinterpret_cast<float*>(take(pslots_all * CPG * a.D * 4));
     p.part_ml = reinterpret_cast<float2*>(take(pslots_all * CPG * 8));

@@ -26,7 +26,9 @@ struct AttnArgs {
     int chunk;          // keys per split-K work item of the per-sequence part
     int prefix_chunk;   // keys per work item of the shared prefix
     int slots;          // split-K work items per kv head (host upper bound)
-    void* workspace;
+    void* workspace;      // partial results (the data region of the plan)
+    void* counters;       // arrival counters, zero on entry and left zero (null: at the
+                          // start of `workspace`, which then holds the whole plan)
     hipEvent_t ev_start, ev_stop;  // optional records around the chunk kernel
 };
 
@@ -36,7 +38,8 @@ struct AttnPlan {
     int grid;    // bf16 path: workgroups (work items) of the decode kernel for the host bound
     int lambda;  // bf16 path: 16-key slices per work item at most
     int nct;     // bf16 path: 16-column tiles per work item (kernel instance)
-    size_t bytes;
+    size_t bytes;          // whole workspace: counter region, then data region
+    size_t counter_bytes;  // the counter region (B * Hkv arrival counters, 256-byte rounded)
     bool ok;  // false: the sequences are too long for the merge (unsupported)
 };
 
@@ -45,6 +48,15 @@ struct AttnPlan {
 AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
                    const int32_t* kv_len_host, const int32_t* cu_q_host, int prefix_len);
 hipError_t attn_launch(const AttnArgs& a, const AttnPlan& plan, hipStream_t stream);
+
+// The library's fixed scratch array on the current device (allocation-free
+// entry point): its counter region (zero between calls) and its data region.
+// The first call on a device looks the array up and enqueues a clear of the
+// counter region on `stream`.
+hipError_t noalloc_scratch(hipStream_t stream, void** counters, size_t* counter_bytes,
+                           void** data, size_t* data_bytes);
+// The sizes of those two regions (no device call).
+void noalloc_limits(size_t* counter_bytes, size_t* data_bytes);
 
 // ---------------------------------------------------------------- sampler
 struct AcceptArgs {
