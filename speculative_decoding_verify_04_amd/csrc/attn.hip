@@ -78,7 +78,19 @@ struct AttnParams {
     int B, K, Hq, Hkv, G, CPG, NC, D, chunk, prefix_chunk, prefix_len, prefix_slots, slots;
     int lambda;        // bf16 path: 16-key slices per work item at most
     int bf16;
+    int xcd;           // decode kernel: deal contiguous work items to each XCD
     float scale_log2;
+};
+
+// The decode kernel's work plan for up to kPlanB sequences, made on the host
+// from the host length bound and passed in the kernel arguments: a workgroup
+// finds its (sequence, chunk, kv head) without reading device memory.
+constexpr int kPlanB = kAttnPlanB;
+struct DecPlan {
+    int nb;                    // B when the plan is valid; 0: find the plan on the device
+    int q[kPlanB + 1];         // q[b] = first chunk of sequence b; q[nb] = chunks in all
+    int s[kPlanB];             // 16-key slices of sequence b for its host bound
+    int row0[kPlanB + 1];      // first query row of sequence b; row0[nb] = query rows
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -395,7 +407,7 @@ struct Slice {
 
 template <int D, int NCT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? SV_NCT1_WAVES : 1)))
-void decode_bf16_kernel(AttnParams p) {
+void decode_bf16_kernel(AttnParams p, DecPlan plan) {
     constexpr int KK = D / 32;   // 16x16x32 steps over the head dim
     constexpr int DT = D / 16;   // 16-wide head-dim tiles of the PV product
     constexpr int VCH = D / 8;   // 16-byte chunks per K/V row
@@ -407,89 +419,133 @@ void decode_bf16_kernel(AttnParams p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col16 = lane & 15, kg = lane >> 4;
     const int lambda = p.lambda;
-    const int id = blockIdx.x;
+    // with p.xcd the grid is a multiple of 8 and XCD x (which runs workgroups
+    // x, x+8, ...) gets the contiguous work items [x*n/8, (x+1)*n/8)
+    const int id = p.xcd ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
 
-    // ---- chunks per sequence and their prefix sum (one round trip)
-    int Lr[NPRO], Kr[NPRO];
-    long long Sr[NPRO];
-#pragma unroll
-    for (int u = 0; u < NPRO; ++u) {
-        const int bb = tid + u * kThreads;
-        Lr[u] = 0;
-        Sr[u] = 0;
-        Kr[u] = p.K + 1;
-        if (bb < p.B) {
-            Lr[u] = p.kv_len[bb];
-            Sr[u] = p.kv_start[bb];
-            if (p.cu_q) Kr[u] = p.cu_q[bb + 1] - p.cu_q[bb];
+    int b, qb, c, g, first_slot, L, k1, q0, Sb;
+    long long kv0;
+    if (plan.nb > 0) {
+        // ---- host plan: b = the number of sequences whose chunks all precede
+        // this workgroup's chunk (a ballot over the sequences)
+        const int cidx = id / p.Hkv;
+        int cnt = 0;
+        for (int b0 = 0; b0 < plan.nb; b0 += 64) {
+            const int bb = b0 + lane;
+            cnt += __popcll(__ballot((bb < plan.nb) && (plan.q[bb + 1] <= cidx)));
         }
-    }
+        b = __builtin_amdgcn_readfirstlane(cnt);
+        if (b >= plan.nb) return;  // past the last work item
+        const int qlo = plan.q[b];
+        qb = plan.q[b + 1] - qlo;
+        c = cidx - qlo;
+        g = id - cidx * p.Hkv;
+        first_slot = p.Hkv * qlo;
+        Sb = plan.s[b];
+        q0 = plan.row0[b];
+        k1 = plan.row0[b + 1] - q0;
+        // the sequence's device data, one round trip; every workgroup of a
+        // sequence takes the same decision, so a bad sequence arrives nowhere
+        L = p.kv_len[b];
+        kv0 = p.kv_start[b];
+        bool bad = (L < 0) || (static_cast<long long>(L) + k1 > 16LL * Sb);
+        if (p.cu_q) bad = bad || (p.cu_q[b] != q0) || (p.cu_q[b + 1] != q0 + k1);
+        if (bad) {
+            if (c == 0 && g == 0 && tid == 0) set_status(p.status, 3);
+            return;
+        }
+    } else {
+        // ---- chunks per sequence from the device lengths and their prefix
+        // sum (one round trip), then a binary search
+        int Lr[NPRO], Kr[NPRO];
+        long long Sr[NPRO];
 #pragma unroll
-    for (int u = 0; u < NPRO; ++u) {
-        const int bb = tid + u * kThreads;
-        if (bb < p.B) {
-            if (Lr[u] < 0) {
-                if (id == 0) set_status(p.status, 3);
-                Lr[u] = 0;
+        for (int u = 0; u < NPRO; ++u) {
+            const int bb = tid + u * kThreads;
+            Lr[u] = 0;
+            Sr[u] = 0;
+            Kr[u] = p.K + 1;
+            if (bb < p.B) {
+                Lr[u] = p.kv_len[bb];
+                Sr[u] = p.kv_start[bb];
+                if (p.cu_q) Kr[u] = p.cu_q[bb + 1] - p.cu_q[bb];
             }
-            Lr[u] = min(Lr[u], kSkMaxKeys);
-            if (Kr[u] < 1 || Kr[u] > p.K + 1) {  // device offsets disagree with the host's
-                if (id == 0) set_status(p.status, 3);
-                Kr[u] = min(max(Kr[u], 1), p.K + 1);
-            }
-            S.Q[bb + 1] = ceil_div(ceil_div(Lr[u] + Kr[u], 16), lambda);
         }
-    }
-    __syncthreads();
-    if (w == 0) {
-        int run = 0;
-        for (int b0 = 0; b0 < p.B; b0 += 64) {
-            const int v = (b0 + lane < p.B) ? S.Q[b0 + lane + 1] : 0;
-            const int inc = wave_incl_scan(v, lane) + run;
-            if (b0 + lane < p.B) S.Q[b0 + lane + 1] = inc;
-            run = __shfl(inc, 63, 64);
-        }
-        if (lane == 0) S.Q[0] = 0;
-    }
-    __syncthreads();
-    // Device lengths above the host bound would need more work items than the
-    // launch has: every workgroup sees the same total and leaves.
-    const long long items = static_cast<long long>(p.Hkv) * S.Q[p.B];
-    if (items > static_cast<long long>(gridDim.x)) {
-        if (id == 0 && tid == 0) set_status(p.status, 3);
-        return;
-    }
-    if (id >= items) return;
-    int b;
-    {
-        int lo = 0, hi = p.B - 1;  // largest b with Hkv * Q[b] <= id
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.Hkv * S.Q[mid] <= id) lo = mid; else hi = mid - 1;
-        }
-        b = __builtin_amdgcn_readfirstlane(lo);
-    }
-    const int first_slot = p.Hkv * S.Q[b];
-    const int qb = S.Q[b + 1] - S.Q[b];
-    const int c = (id - first_slot) / p.Hkv;
-    const int g = (id - first_slot) % p.Hkv;
 #pragma unroll
-    for (int u = 0; u < NPRO; ++u) {
-        if (tid + u * kThreads == b) {
-            S.L = Lr[u];
-            S.kv0 = Sr[u];
-            S.k1 = Kr[u];
-            S.q0 = p.cu_q ? p.cu_q[b] : b * (p.K + 1);
+        for (int u = 0; u < NPRO; ++u) {
+            const int bb = tid + u * kThreads;
+            if (bb < p.B) {
+                if (Lr[u] < 0) {
+                    if (id == 0) set_status(p.status, 3);
+                    Lr[u] = 0;
+                }
+                Lr[u] = min(Lr[u], kSkMaxKeys);
+                if (Kr[u] < 1 || Kr[u] > p.K + 1) {  // device offsets disagree with the host's
+                    if (id == 0) set_status(p.status, 3);
+                    Kr[u] = min(max(Kr[u], 1), p.K + 1);
+                }
+                S.Q[bb + 1] = ceil_div(ceil_div(Lr[u] + Kr[u], 16), lambda);
+            }
         }
+        __syncthreads();
+        if (w == 0) {
+            int run = 0, qmax = 0;
+            for (int b0 = 0; b0 < p.B; b0 += 64) {
+                const int v = (b0 + lane < p.B) ? S.Q[b0 + lane + 1] : 0;
+                qmax = max(qmax, v);
+                const int inc = wave_incl_scan(v, lane) + run;
+                if (b0 + lane < p.B) S.Q[b0 + lane + 1] = inc;
+                run = __shfl(inc, 63, 64);
+            }
+            qmax = static_cast<int>(wave_max(static_cast<float>(qmax)));  // exact below 2^24
+            if (lane == 0) {
+                S.Q[0] = 0;
+                S.flag = qmax;
+            }
+        }
+        __syncthreads();
+        // Device lengths above the host bound would need more work items than
+        // the launch has, or more chunks of one sequence than the merge takes:
+        // every workgroup sees the same totals and leaves.
+        const long long items = static_cast<long long>(p.Hkv) * S.Q[p.B];
+        if (items > static_cast<long long>(gridDim.x) || S.flag + p.prefix_slots > kMergeMax) {
+            if (id == 0 && tid == 0) set_status(p.status, 3);
+            return;
+        }
+        if (id >= items) return;
+        {
+            int lo = 0, hi = p.B - 1;  // largest b with Hkv * Q[b] <= id
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (p.Hkv * S.Q[mid] <= id) lo = mid; else hi = mid - 1;
+            }
+            b = __builtin_amdgcn_readfirstlane(lo);
+        }
+        first_slot = p.Hkv * S.Q[b];
+        qb = S.Q[b + 1] - S.Q[b];
+        c = (id - first_slot) / p.Hkv;
+        g = (id - first_slot) % p.Hkv;
+        __syncthreads();  // S.flag is reused by the merge hand-off
+#pragma unroll
+        for (int u = 0; u < NPRO; ++u) {
+            if (tid + u * kThreads == b) {
+                S.L = Lr[u];
+                S.kv0 = Sr[u];
+                S.k1 = Kr[u];
+                S.q0 = p.cu_q ? p.cu_q[b] : b * (p.K + 1);
+            }
+        }
+        __syncthreads();
+        L = __builtin_amdgcn_readfirstlane(S.L);
+        k1 = __builtin_amdgcn_readfirstlane(S.k1);  // K_b + 1 query rows
+        q0 = __builtin_amdgcn_readfirstlane(S.q0);  // the first of them
+        kv0 = S.kv0;
     }
-    __syncthreads();
-    const int L = __builtin_amdgcn_readfirstlane(S.L);
-    const int k1 = __builtin_amdgcn_readfirstlane(S.k1);  // K_b + 1 query rows
-    const int q0 = __builtin_amdgcn_readfirstlane(S.q0);  // the first of them
+    // the qb chunks of the sequence share its slices for the device length
+    // (a host bound above it leaves no masked slices, at most empty chunks)
+    Sb = ceil_div(L + k1, 16);
     const int ncols = p.G * k1;
-    const long long kv0 = S.kv0;
-    const int T = L + k1;
-    const int Sb = ceil_div(T, 16);
+    const int T = L + k1;       // keys of the sequence (on the device)
     const int sl_lo = static_cast<int>(static_cast<long long>(c) * Sb / qb);
     const int sl_hi = static_cast<int>(static_cast<long long>(c + 1) * Sb / qb);
 
@@ -1345,6 +1401,21 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
         pl.lambda = lo;
         pl.grid = pl.ok ? static_cast<int>(items) : 0;
         slots = pl.ok ? items : 0;
+        // the per-sequence plan for the kernel arguments
+        pl.plan_nb = 0;
+        if (pl.ok && B <= kAttnPlanB) {
+            int qrun = 0;
+            for (int b = 0; b < B; ++b) {
+                const int sb = static_cast<int>((std::min<long long>(keys(b), kSkMaxKeys) + 15) / 16);
+                pl.plan_q[b] = qrun;
+                pl.plan_s[b] = sb;
+                pl.plan_row0[b] = cu_q_host ? cu_q_host[b] : b * K1;
+                qrun += (sb + lo - 1) / lo;
+            }
+            pl.plan_q[B] = qrun;
+            pl.plan_row0[B] = cu_q_host ? cu_q_host[B] : B * K1;
+            pl.plan_nb = B;
+        }
     } else {
         chunk = env_int("SPECVERIFY_ATTN_CHUNK", 0);
         if (chunk <= 0) {
@@ -1417,6 +1488,7 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
     p.slots = pl.slots;
     p.lambda = pl.lambda;
     p.bf16 = a.bf16;
+    p.xcd = env_int("SPECVERIFY_ATTN_XCD", 0) > 0 ? 1 : 0;
     p.scale_log2 = a.scale * kLog2e;
 
     // counters, then the data region (its layout as in attn_plan)
@@ -1455,16 +1527,26 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
             if (e != hipSuccess) return e;
         }
         const int nct = pl.nct;
-        dim3 grid(pl.grid);
+        DecPlan dp;
+        dp.nb = pl.plan_nb;
+        for (int b = 0; b <= pl.plan_nb && pl.plan_nb > 0; ++b) {
+            dp.q[b] = pl.plan_q[b];
+            dp.row0[b] = pl.plan_row0[b];
+            if (b < pl.plan_nb) dp.s[b] = pl.plan_s[b];
+        }
+        // XCD-contiguous items need a grid that is a multiple of 8 (the extra
+        // workgroups find no item and leave)
+        dim3 grid(p.xcd ? (pl.grid + 7) / 8 * 8 : pl.grid);
         // With timing events, the dispatch itself stamps them at the kernel's
         // start and end (the same timestamps a kernel trace reports).
 #define SV_DECODE(DD, NN)                                                                          \
     do {                                                                                           \
         if (a.ev_start && a.ev_stop)                                                               \
             hipExtLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream,  \
-                                  a.ev_start, a.ev_stop, 0, p);                                    \
+                                  a.ev_start, a.ev_stop, 0, p, dp);                                \
         else                                                                                       \
-            hipLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream, p);  \
+            hipLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream, p,  \
+                               dp);                                                                \
     } while (0)
         if (a.D == 128) {
             switch (nct) {

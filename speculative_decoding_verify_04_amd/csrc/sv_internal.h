@@ -32,12 +32,21 @@ struct AttnArgs {
     hipEvent_t ev_start, ev_stop;  // optional records around the chunk kernel
 };
 
+// Sequences whose decode work plan travels in the kernel arguments.
+constexpr int kAttnPlanB = 128;
+
 // Chunking decisions made on the host from the host length bound.
 struct AttnPlan {
     int chunk, prefix_chunk, slots, prefix_slots;
     int grid;    // bf16 path: workgroups (work items) of the decode kernel for the host bound
     int lambda;  // bf16 path: 16-key slices per work item at most
     int nct;     // bf16 path: 16-column tiles per work item (kernel instance)
+    // bf16 path, B <= kAttnPlanB: chunk prefix sums, slices and first query
+    // rows per sequence (plan_nb = B), else plan_nb = 0
+    int plan_nb;
+    int plan_q[kAttnPlanB + 1];
+    int plan_s[kAttnPlanB];
+    int plan_row0[kAttnPlanB + 1];
     size_t bytes;          // whole workspace: counter region, then data region
     size_t counter_bytes;  // the counter region (B * Hkv arrival counters, 256-byte rounded)
     bool ok;  // false: the sequences are too long for the merge (unsupported)

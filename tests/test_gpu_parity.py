@@ -261,6 +261,37 @@ def test_attention_timing_events(name):
     assert np.array_equal(o1, o2)
 
 
+def test_attention_device_lengths_against_host_bound():
+    """kv_len_host only bounds the device lengths: a device length above its
+    sequence's bound (others unchanged) or a negative one sets status 3 and
+    leaves that sequence unread; a device length below the bound gives the
+    oracle's result for the device length."""
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=4, Hq=2, Hkv=2, len_lo=100, len_hi=300, V=64)
+    w = W.make_workload(cfg, sub_seed=12)
+    t = to_device(w, DEV)
+    for bad in (int(w.kv_len[1]) + 40, -1):
+        kl = t.kv_len.clone()
+        kl[1] = bad
+        t.status.zero_()
+        api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, kl, w.kv_len, t.k_new,
+                             t.v_new, t.out, cfg.K, status=t.status)
+        torch.cuda.synchronize()
+        assert int(t.status.item()) == 3, bad
+    short = w.kv_len.copy()
+    short[2] = max(0, int(short[2]) - 37)
+    short[0] = 0
+    t.status.zero_()
+    api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start,
+                         torch.from_numpy(short).to(DEV), w.kv_len, t.k_new, t.v_new, t.out,
+                         cfg.K, status=t.status)
+    torch.cuda.synchronize()
+    assert int(t.status.item()) == 0
+    o = t.out.float().cpu().numpy().astype(np.float64)
+    ref = R.verify_attn(w.q, w.k_cache, w.v_cache, w.kv_start, short, w.k_new, w.v_new, cfg.B,
+                        cfg.K, cfg.Hq, cfg.Hkv, cfg.D)
+    assert attn_errors(o, ref).max() <= 1e-2
+
+
 def test_attention_bifurcated_equals_concatenated_gpu():
     """Prefix read once == the same prefix copied into every sequence's cache."""
     cfg = SMALL_ATTN["bf16_prefix"]
