@@ -4,35 +4,47 @@
 // Sampling", section "Modified rejection sampling" and Theorem 1: accept draft
 // x_j with probability min(1, q(x_j)/p(x_j)) left to right, resample the first
 // rejected position from (q - p)_+, draw a bonus token from the last target
-// row when all K drafts pass; temperature and nucleus modify q and p first.
+// row when all K drafts pass; temperature and the top-k / nucleus filters
+// modify q and p first.
 //
-// rows_kernel  grid = rows x segments of 4096 logits; one kernel for the whole
-//   round when the nucleus is on (or greedy), chained by last-arriver counters:
-//   segment  read the segment once: max, fp64 mass relative to it, and
-//            (nucleus) the segment's candidate list: every element of the
-//            highest quarter-unit bins of z/T, as many bins as fit in 256
-//            entries, stored in id order.  A nucleus of top_p < 1 keeps the
-//            upper part of the distribution, so the lists normally hold it
-//            whole.
-//   row      the last segment of a row merges it: max, normaliser, fp64
-//            masses of the listed entries over 1/16-unit bins, and the exact
-//            tie-closed nucleus threshold (the boundary bin from the bin
-//            masses, then its few entries ranked exactly).  When a list
-//            misses part of the nucleus the row falls back to a radix select
-//            over the whole row.
-//   sequence the last row of a sequence runs the accept scan and draws the
-//            emitted token from the stopping row's lists: the residual
-//            (q' - p')_+ and q' vanish outside the target nucleus, so the
-//            draft logits are read at the target nucleus members' ids only.
-//            A row without a complete list is drawn by a pass over the
-//            whole row.
-// draw_kernel  (no nucleus) grid = sequences x segments: fp64 residual or
-//   bonus weights of the stopping row, per-segment sums; the last segment
-//   picks the crossing segment and scans it exactly.
+// verify_kernel<EPT>  grid = units x segments of 256*EPT logits.  A unit is a
+//   target row r of sequence b at position j: for j < K_b it pairs with draft
+//   row j of b (the drafted token x_j is tested on the pair), for j = K_b it
+//   is the bonus row.
+//   segment_kernel (256 threads per unit segment)
+//            one workgroup reads the same segment (the same token ids) of
+//            the unit's target and draft rows: per row the max, the fp64
+//            mass relative to it and, with a filter on, the candidate list
+//            (every element of the highest quarter-unit bins of z/T that fit
+//            in the list, in id order; target entries also carry the draft
+//            logit of their id) and the fp64 mass and count of each listed
+//            bin.  A nucleus keeps the upper part of the distribution, so
+//            the lists normally hold it whole.
+//   merge_kernel (1024 threads per unit; after the segment kernel)
+//            merges both rows of the unit at once, one half of the
+//            workgroup per row: max, normaliser, the exact tie-closed
+//            filter threshold (bin masses summed over the segments, then the
+//            boundary bin's listed entries ranked), the accept test of x_j
+//            and -- only after a rejection, or for the bonus row -- the drawn
+//            token: (q' - p')_+ and q' vanish outside the target's kept set,
+//            and every target list entry carries its draft logit, so the draw
+//            walks the target lists in id order with no further load.  A row
+//            whose lists do not hold its kept set falls back to a radix
+//            select and a draw over the whole row.
+//            The units of a sequence then count themselves in one 64-bit
+//            word that also gathers one rejection bit per position; the last
+//            one stops at the first rejection and writes the emitted tokens.
+//   Two launches instead of a last-arriver hand-off inside one: the merges
+//   are chains of dependent steps, and a workgroup of their own (16 waves,
+//   eight per row, coalesced list loads) runs them several times faster than
+//   the last segment workgroup could, while the segment kernel keeps the
+//   registers and occupancy of a streaming pass.
+// draw_kernel  (no filter) grid = sequences x segments: the draw needs every
+//   token of the stopping row, so it runs after the units: fp64 residual or
+//   bonus weights per segment; the last segment picks the crossing segment
+//   and scans it exactly.
 // Every quantity that decides a token is fp64; the exp of the logits is the
-// table-driven fp64 exp of sv_math.h (table of 2^(j/64) built per workgroup).
-// A chain of dependent global accesses costs about a microsecond per link
-// under load, so every merge issues its loads together.
+// table-driven fp64 exp of sv_math.h (table of 2^(j/256) built per workgroup).
 #include "sv_device.h"
 #include "sv_internal.h"
 #include "sv_math.h"
@@ -40,35 +52,37 @@
 namespace sv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kPerThread = 16;
-constexpr int kSeg = kThreads * kPerThread;  // 4096 logits per segment
-constexpr int kFine = 4;                     // row bins per segment bin
-constexpr int kBins = 512;                   // 1/16-unit bins of z/T below the row max (32 units)
-constexpr int kBinsPerLane = kBins / 64;
-constexpr int kCutBins = 64;                 // quarter-unit bins below the segment max a list may span
-constexpr int kList = kThreads;              // candidate list capacity per segment
-constexpr int kCap = 1024;                   // boundary-bin entries ranked in LDS
-constexpr int kMaxSeg = 64;                  // V <= 64 * 4096
-constexpr int kChunk = 16;                   // list segments a thread loads per round trip
-constexpr int kMaxRowsPerSeq = 2 * 64 + 1;   // K <= 64
+constexpr int kThreads = 256;        // segment kernel workgroup
+constexpr int kMThreads = 1024;      // merge kernel workgroup: one unit, two rows
+constexpr int kHalf = kMThreads / 2; // threads per row in a unit merge
+constexpr int kRW = kHalf / 64;      // waves per row
+constexpr int kQB = 64;              // quarter-unit bins of z/T below a top bin (16 units)
+constexpr int kSlots = 8;            // list slots per merging thread (list path: nseg*klist <= 4096)
+constexpr int kCap = 512;            // boundary-bin entries ranked per row
+constexpr int kSub = 64;             // sub-bins of a boundary quarter bin (1/256 unit of z/T each)
+constexpr int kListSegMax = 21;      // segments the list path merges (3072-logit segments)
+constexpr int kMaxSeg = 88;          // V <= 262144 with 3072-logit segments
+constexpr int kMaxDrafts = 64;
+constexpr int kMaskBits = 56;        // rejection bits in the sequence arrival word
+constexpr int kListCap = 256;        // list capacity of a segment (16 * EPT)
+constexpr unsigned long long kArrive = 1ull << kMaskBits;
 
 struct SegHead {
     float m;      // segment max (greedy: max value)
-    int kb_top;   // row bin of the max (greedy: index of the max)
-    int kb_cut;   // nucleus: every element with row bin >= kb_cut is in the list
-    int n;        // nucleus: list length
-    double S;     // sum of exp((z - m)/T) over the segment
+    int top;      // quarter bin floor(m * 4/T) (greedy: lowest index of the max)
+    int ocut;     // quarter bins top .. top - ocut are listed completely (-1: none)
+    int n;        // list length
+    double S;     // fp64 sum of exp((z - m)/T) over the segment
 };
 
 struct RowRec {
     float m;      // row max
-    float tau;    // nucleus threshold logit (-inf: no nucleus)
-    double S;     // kept mass relative to m (= full normaliser without nucleus)
-    double wx;    // exp((z[x] - m)/T) for the drafted token x of this row
-    int kept;     // drafted token inside the nucleus
+    float tau;    // filter threshold logit (-inf: no filter)
+    double S;     // kept mass relative to m (the full normaliser without filter)
+    double wx;    // exp((z[x] - m)/T) for the drafted token x of the unit
+    int kept;     // drafted token inside the kept set
     int argmax;   // lowest id of the row maximum (greedy)
-    int fast;     // the row's lists hold its whole nucleus
+    int fast;     // the row's lists hold its kept set
     int pad;
 };
 
@@ -86,29 +100,32 @@ struct AcceptParams {
     int32_t* n_accepted;
     int32_t* out_tokens;
     int32_t* status;
-    SegHead* seg;
-    unsigned long long* list;  // [nrows][nseg][kList]: (id << 32) | bits of z, ids ascending
-    RowRec* rows;
-    float* zx;                 // [nrows]: logit of the row's drafted token (segment that holds it)
-    SeqRec* seqs;
-    double* dsum;
+    SegHead* seg;              // [nrows][nseg]
+    unsigned long long* list;  // [nrows][nseg][klist]: (id << 32) | bits of z, ids ascending
+    float* lzp;                // [nt][nseg][klist]: draft logit at each target entry's id
+    double* bmass;             // [nrows][nseg][kQB]: mass of listed quarter bin top - o (rel. to the segment max)
+    int* bcnt;                 // [nrows][nseg][kQB]: its element count
+    RowRec* rows;              // [nrows]
+    float* zx;                 // [nrows]: logit of the unit's drafted token
+    int* utok;                 // [nt]: token drawn by a unit (after a rejection, or the bonus)
+    SeqRec* seqs;              // [B]
+    double* dsum;              // [B][nseg] draw_kernel segment sums
     double* qsum;
-    int* row_cnt;
-    int* seq_cnt;
-    int* draw_cnt;
+    unsigned long long* seq_word;  // [B]: arrivals (top bits) and rejection bits
+    unsigned long long* seq_mask;  // [B]: rejection bits of sequences with K_b > kMaskBits
+    int* draw_cnt;             // [B]
     const int32_t* cu_q;       // [B+1] ragged draft lengths: target rows of b start at cu_q[b]
-    int nt;                    // target rows (cu_q[B], or B*(K+1))
-    int B, K, V, nseg, nrows, grid_rows;  // K: the largest draft length
-    int bf16, vec, nucleus, greedy;  // nucleus: a filter is on (top_p < 1 or top_k)
-    int top_k;                       // keep the k largest logits and their ties (0: off)
-    double invT;
+    int nt;                    // target rows (cu_q[B], or B*(K+1)); draft row d is row nt + d
+    int B, K, V, nseg, klist, grid_units;
+    int bf16, vec, filter, greedy;  // filter: top_p < 1 or top-k on
+    int top_k;                 // keep the k largest logits and their ties (0: off)
+    double yscale;             // 256 / (T ln 2): exp((z - m)/T) = 2^((z - m) * yscale / 256)
     double top_p;
-    float bscale;    // 16 / T: row bin of z is floor(z * bscale)
-    float bscale_c;  // 4 / T: segment bin of z is floor(z * bscale_c); row bin = 4 * segment bin + 0..3
+    float qscale;              // 4 / T: the quarter bin of z is floor(z * qscale)
 };
 
-// Sequence b owns target rows q0 .. q0+K_b (q0 = cu_q[b], or b*(K+1)) and draft
-// rows nt+q0-b .. nt+q0-b+K_b-1; its drafts and accept uniforms start at
+// Sequence b owns target rows q0 .. q0+K_b (q0 = cu_q[b], or b*(K+1)) and
+// draft rows nt+q0-b .. nt+q0-b+K_b-1; its drafts and accept uniforms start at
 // q0-b, its output tokens at q0.
 __device__ __forceinline__ int seq_q0(const AcceptParams& p, int b) {
     return p.cu_q ? p.cu_q[b] : b * (p.K + 1);
@@ -144,39 +161,75 @@ __device__ __forceinline__ void load4(const void* row, int bf16, int vec, int V,
     for (int k = 0; k < 4; ++k) z[k] = (e + k < V) ? load1(row, bf16, e + k) : -INFINITY;
 }
 
-// Segment element k of thread tid: index seg*4096 + (k/4)*1024 + tid*4 + k%4.
-__device__ __forceinline__ void load_segment(const void* row, int bf16, int vec, int V,
-                                             int s, int tid, float* z) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        load4(row, bf16, vec, V, s * kSeg + i * 1024 + tid * 4, z + 4 * i);
+// Segment element k of thread tid (segments of 256*EPT logits): id
+// s*256*EPT + (k/4)*1024 + tid*4 + k%4.
+template <int EPT>
+__device__ __forceinline__ int seg_index(int s, int tid, int k) {
+    return s * (kThreads * EPT) + (k >> 2) * 1024 + tid * 4 + (k & 3);
 }
 
-__device__ __forceinline__ int seg_index(int s, int tid, int k) {
-    return s * kSeg + (k >> 2) * 1024 + tid * 4 + (k & 3);
+template <int EPT>
+__device__ __forceinline__ void load_segment(const void* row, int bf16, int vec, int V, int s,
+                                             int tid, float* z) {
+    const int e0 = s * (kThreads * EPT);
+    if (vec && e0 + kThreads * EPT <= V) {  // uniform: the whole segment lies in the row
+        if (bf16) {
+            const uint2* r2 = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(row) + e0) + tid;
+            uint2 w[EPT / 4];
+#pragma unroll
+            for (int g = 0; g < EPT / 4; ++g) w[g] = r2[g * kThreads];
+#pragma unroll
+            for (int g = 0; g < EPT / 4; ++g) {
+                z[4 * g + 0] = __uint_as_float(w[g].x << 16);
+                z[4 * g + 1] = __uint_as_float(w[g].x & 0xFFFF0000u);
+                z[4 * g + 2] = __uint_as_float(w[g].y << 16);
+                z[4 * g + 3] = __uint_as_float(w[g].y & 0xFFFF0000u);
+            }
+        } else {
+            const float4* r4 = reinterpret_cast<const float4*>(static_cast<const float*>(row) + e0) + tid;
+            float4 w[EPT / 4];
+#pragma unroll
+            for (int g = 0; g < EPT / 4; ++g) w[g] = r4[g * kThreads];
+#pragma unroll
+            for (int g = 0; g < EPT / 4; ++g) {
+                z[4 * g + 0] = w[g].x;
+                z[4 * g + 1] = w[g].y;
+                z[4 * g + 2] = w[g].z;
+                z[4 * g + 3] = w[g].w;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int g = 0; g < EPT / 4; ++g)
+        load4(row, bf16, vec, V, e0 + g * 1024 + tid * 4, z + 4 * g);
 }
 
 __device__ __forceinline__ const void* row_ptr(const AcceptParams& p, int r) {
-    const int nt = p.nt;
     const size_t es = p.bf16 ? 2 : 4;
-    if (r < nt) return static_cast<const char*>(p.target) + static_cast<size_t>(r) * p.V * es;
-    return static_cast<const char*>(p.draft) + static_cast<size_t>(r - nt) * p.V * es;
+    if (r < p.nt) return static_cast<const char*>(p.target) + static_cast<size_t>(r) * p.V * es;
+    return static_cast<const char*>(p.draft) + static_cast<size_t>(r - p.nt) * p.V * es;
 }
 
-__device__ __forceinline__ int bin_of(float z, float bscale) {
-    float y = fminf(fmaxf(z * bscale, -1.0e9f), 1.0e9f);
-    return static_cast<int>(floorf(y));
+// Quarter-unit bin of z/T: floor(z * 4/T), the product clamped far outside
+// any logit range (one med3) and floored and converted by one instruction.
+__device__ __forceinline__ int qbin(float z, float qscale) {
+    const float y = __builtin_amdgcn_fmed3f(z * qscale, -1.0e9f, 1.0e9f);
+    int b;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(b) : "v"(y));
+    return b;
 }
 
-// fp64 weight of logit z relative to the max m (both exact in double).
-__device__ __forceinline__ double weight(float z, float m, double invT, const double* tab) {
-    return exp_nonpos((static_cast<double>(z) - static_cast<double>(m)) * invT, tab);
+// fp64 weight exp((z - m)/T) of logit z relative to the max m (z - m exact in
+// double; ys = 256 / (T ln 2)).
+__device__ __forceinline__ double weight(float z, float m, double ys, const double* tab) {
+    return exp2_256((static_cast<double>(z) - static_cast<double>(m)) * ys, tab);
 }
 
-// Fill the 64-entry table 2^(j/64) of exp_nonpos (threads 0..63); the caller
-// synchronises before use.
+// Fill the 256-entry table 2^(j/256) of exp2_256 (workgroups of at least 256
+// threads); the caller synchronises before use.
 __device__ __forceinline__ void fill_exp_table(double* tab) {
-    if (threadIdx.x < 64) tab[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) * (1.0 / 64.0));
+    if (threadIdx.x < 256) tab[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) * (1.0 / 256.0));
 }
 
 // Order-preserving 32-bit key of a float (larger float -> larger key); -0 == +0.
@@ -188,97 +241,252 @@ __device__ __forceinline__ float fkey_inv(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+__device__ __forceinline__ float entry_z(unsigned long long e) {
+    return __uint_as_float(static_cast<unsigned>(e));
+}
+__device__ __forceinline__ int entry_id(unsigned long long e) { return static_cast<int>(e >> 32); }
+
+__device__ __forceinline__ double lane_read_d(double v, int src) {
+    const long long bits = __double_as_longlong(v);
+    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(bits), src));
+    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(bits >> 32), src));
+    return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
 // ---------------------------------------------------------------- LDS layout
 
-struct RowsLds {
-    double tab[64];           // 2^(j/64) for exp_nonpos
-    double red_d[kThreads / 64];
-    double red_d2[kThreads / 64];
-    float red_f[kThreads / 64];
-    int flag;
-    union alignas(16) {
-        struct {              // segment: per-wave counts of bins kb_top - o
-            int hc[4][kCutBins];
-            int fit;
-            unsigned long long wtot[kThreads / 64];
-        } seg;
-        struct {              // row merge: bin masses, boundary-bin entries
-            double hm[kBins];         // row mass per bin kb_top - og
-            int hcnt[kBins];          // row count per bin (top-k)
-            unsigned long long ck[kCap + 8];  // order key: (z desc, id asc) <-> key desc
-            int wcnt[kThreads / 64];
-            float rz[kCap];   // z in rank order
-            double rw[kCap];  // weight in rank order
-        } cand;
-        struct {              // radix select fallback
-            double rh_m[256];
-            int rh_c[256];
-        } rad;
-        struct {              // sequence
-            RowRec rr[kMaxRowsPerSeq];
-            float ua[64];
-            int x[64];
-            double scan[kThreads];
-            double scan2[kThreads];
-            float zpa[kChunk * kThreads];     // draft logits of every run's members
-        } sq;
-    };
-    // row merge
+struct SegLds {                     // segment kernel: rows 0 (target) and 1 (draft)
+    double tab[256];                // 2^(j/256) for exp2_256
+    float red_f[2][4];
+    double red_d[2][4];
+    int hc[2][4][kQB + 64];         // per-wave counts of quarter bins top - o (+ a dummy per lane)
+    int fit[2];                     // bins top .. top - fit + 1 fit in the list
+    unsigned long long wtot[2][4];  // per-wave packed list counts
+    double hm[2][kQB];              // fp64 masses of the listed bins
+    unsigned long long stage[2][kListCap];  // list entries in id order
+    float stzp[kListCap];           // the draft logits of the target entries
+    float gv[4];                    // greedy: per-wave max and its lowest index
+    int gi[4];
+};
+
+struct RowPart {                    // one row of a unit merge
     float seg_m[kMaxSeg];
-    int seg_kb[kMaxSeg];
-    int seg_cut[kMaxSeg];
+    int seg_top[kMaxSeg];
+    int seg_ocut[kMaxSeg];
     int seg_n[kMaxSeg];
     double seg_S[kMaxSeg];
-    double sc[kMaxSeg];       // per-segment rescale exp((m_s - m)/T)
-    float m;
-    int argmax;
-    double S;
-    float zx;                 // logit of the drafted token of the row
-    int kb_top, kb_lo;
-    float zk;                 // top-k threshold logit (-inf: no top-k)
-    int fastk;                // the lists decided the top-k threshold
-    double Sk;                // mass of the top-k set (the full normaliser without top-k)
-    int abovec;               // radix select: count above the current digit
-    int og;
-    int ccount;
-    int fast;
+    double bm[kListSegMax][kQB];    // listed bin masses of every segment
+    union {
+        int bc[kListSegMax][kQB];   // their counts (top-k)
+        struct {
+            unsigned long long ck[kCap + 8];  // (z desc, id asc) order keys of the boundary bin
+            float rz[kCap];                   // z in rank order
+            double rw[kCap];                  // weight relative to the row max, in rank order
+        } rk;
+    };
+    double part[kRW][kQB];          // per-wave partial bin masses
+    int cpart[kRW][kQB];            // and counts
+    double mass[kQB];               // row bin masses (bins top - o)
+    double sbm[kSub];               // sub-bins of the boundary bin: masses,
+    uint32_t sbk[2][kSub];          // and the smallest and largest order key of z
+    int wcnt[kRW];
+    float m;                        // row max
+    int top;                        // its quarter bin
+    int ocmax;                      // row bins top - o with o <= ocmax are listed in every segment
+    double S;                       // normaliser relative to m
+    float zx;                       // logit of the drafted token
+    int fast;                       // the lists decided the kept set
+    int og;                         // boundary bin (offset from top)
+    double above;                   // mass of the bins above it
+    int ccount;                     // ranked (gathered) entries
+    int needsub;                    // the nucleus boundary is to be found in bin og
+    float zmin;                     // only entries with z >= zmin take part (top-k floor)
+    double target;                  // the nucleus mass to reach (from the row max)
+    float zk;                       // top-k threshold logit (-inf: off)
+    int abovec;                     // top-k: count above the boundary bin
+    double Sk;                      // mass of the top-k set
+    float tau;                      // kept set: z >= tau
+    double kept;                    // its mass relative to m
+};
+
+struct MergeLds {
+    double tab[256];
+    union {
+        RowPart r[2];
+        double wdraw[kHalf * kSlots];  // draw: the chosen weight of every list slot, id order
+    };
+    struct {                        // radix select over a whole row
+        double rh_m[256];
+        int rh_c[256];
+    } rad;
+    double ta[kMThreads / 64];      // per-wave scan totals
+    double tb[kMThreads / 64];
+    uint32_t prefix, mask;
+    int chosen, abovec;
     double above;
     float tau;
     double kept;
-    uint32_t prefix, mask;
-    int chosen;
-    int n, tok, lastpos;
-    float us;                 // u_sample of the sequence
-    int rb;                   // sequence of the workgroup's row (ragged draft lengths)
+    int tok, lastpos, fstar;
+    int seqn;                       // accepted drafts of the sequence (-1: not the last unit)
+    int acc;                        // the unit's draft was accepted
+    float us;                       // u_sample of the sequence
+    float ua;                       // u_accept of the unit
 };
 
-// Exact tie-closed threshold by radix select over the whole row (4 passes of
-// 8 bits over order-preserving keys, fp64 digit masses and digit counts),
-// among the elements with z >= zmin.  kcount > 0: the kcount-th largest value
-// (top-k); else the nucleus boundary, the largest value whose tie-closed top
-// set reaches `target` mass.  Sets L.tau and L.kept (mass of z >= tau, z >=
-// zmin).  Used when a row's candidate lists cannot decide.
-__device__ __forceinline__ void radix_threshold(const AcceptParams& p, const void* row, float m, double target,
-                                int kcount, float zmin, RowsLds& L) {
+// ---------------------------------------------------------------- segment pass
+
+// Bin offset o = top - (quarter bin of z), capped at kQB (below the window).
+__device__ __forceinline__ unsigned bin_off(float z, int top, float qscale) {
+    return min(static_cast<unsigned>(top - qbin(z, qscale)), static_cast<unsigned>(kQB));
+}
+
+// Candidate lists of both rows of a unit segment (row 1 only if has_d), after
+// the per-wave counts of the quarter bins top - o (o < kQB) are complete:
+// the highest bins that fit in the list, the listed elements in id order
+// ((id << 32) | bits of z; target entries also store the draft logit of
+// their id), and the fp64 masses and counts of the listed bins.  ow holds the
+// bin offsets of the thread's elements, four per word (kQB and above: below
+// the window).  The elements are
+// staged in LDS at their list positions, then stored with coalesced writes;
+// the masses are taken over the staged entries, one per thread.
+template <int EPT>
+__device__ __forceinline__ void segment_lists(const AcceptParams& p, int s, int row0, int row1, bool has_d,
+                                              const float (&z)[2][EPT], const unsigned (&ow)[2][EPT / 4],
+                                              const int (&top)[2], const float* ms, SegLds& L) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nr = has_d ? 2 : 1;
+    if (tid < 64 * nr) {
+        // cumulative counts from the top bin down: bins 0 .. fit-1 fit (the
+        // counts are nondecreasing in o)
+        const int r = tid >> 6;
+        const int rowr = r ? row1 : row0;
+        const int c = (L.hc[r][0][lane] + L.hc[r][1][lane]) + (L.hc[r][2][lane] + L.hc[r][3][lane]);
+        const int cum = wave_incl_scan(c, lane);
+        const unsigned long long bal = __ballot(cum <= p.klist);
+        if (lane == 0) L.fit[r] = __popcll(bal);
+        if (p.top_k > 0) p.bcnt[(static_cast<size_t>(rowr) * p.nseg + s) * kQB + lane] = c;
+    }
+    __syncthreads();
+    int ocut[2];
+    unsigned long long packed[2] = {0ull, 0ull};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        ocut[r] = (r < nr) ? L.fit[r] - 1 : -1;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int o = static_cast<int>((ow[r][k >> 2] >> (8 * (k & 3))) & 0xFFu);
+            packed[r] += (o <= ocut[r]) ? (1ull << (16 * (k >> 2))) : 0ull;
+        }
+    }
+    // list positions in id order: 64-bit words of four 16-bit counters (one
+    // per 1024-id group); no carry crosses a field
+    unsigned long long inc[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        inc[r] = wave_incl_scan(packed[r], lane);
+        if (lane == 63) L.wtot[r][wv] = inc[r];
+    }
+    __syncthreads();
+    int nlist[2] = {0, 0};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (r >= nr) continue;  // uniform
+        unsigned long long off = 0, tot = 0;
+#pragma unroll
+        for (int u = 0; u < kThreads / 64; ++u) {
+            if (u < wv) off += L.wtot[r][u];
+            tot += L.wtot[r][u];
+        }
+        const unsigned long long excl = off + inc[r] - packed[r];
+        int gofs[EPT / 4];
+        int run = 0;
+#pragma unroll
+        for (int g = 0; g < EPT / 4; ++g) {
+            gofs[g] = run + static_cast<int>((excl >> (16 * g)) & 0xFFFF);
+            run += static_cast<int>((tot >> (16 * g)) & 0xFFFF);
+        }
+        nlist[r] = run;
+        const unsigned id0 = static_cast<unsigned>(seg_index<EPT>(s, tid, 0));
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int o = static_cast<int>((ow[r][k >> 2] >> (8 * (k & 3))) & 0xFFu);
+            const int g = k >> 2;
+            if (o <= ocut[r]) {
+                const unsigned id = id0 + static_cast<unsigned>((k >> 2) * 1024 + (k & 3));
+                L.stage[r][gofs[g]] = (static_cast<unsigned long long>(id) << 32) | __float_as_uint(z[r][k]);
+                if (r == 0) L.stzp[gofs[g]] = z[1][k];
+                ++gofs[g];
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (r >= nr) continue;  // uniform
+        const size_t lbase = (static_cast<size_t>(r ? row1 : row0) * p.nseg + s) * p.klist;
+        for (int t = tid; t < nlist[r]; t += kThreads) {
+            const unsigned long long en = L.stage[r][t];
+            p.list[lbase + t] = en;
+            if (r == 0 && has_d) p.lzp[lbase + t] = L.stzp[t];
+            const float ze = entry_z(en);
+            atomicAdd(&L.hm[r][bin_off(ze, top[r], p.qscale)], weight(ze, ms[r], p.yscale, L.tab));
+        }
+    }
+    __syncthreads();
+    if (tid < 64 * nr) {
+        // the listed bins only (the merge reads no bin below a segment's cut)
+        const int r = tid >> 6;
+        const int oc = r ? ocut[1] : ocut[0];
+        if (lane <= oc) p.bmass[(static_cast<size_t>(r ? row1 : row0) * p.nseg + s) * kQB + lane] = L.hm[r][lane];
+    }
+    if (tid < nr) {
+        const int r = tid;
+        SegHead* h = p.seg + static_cast<size_t>(r ? row1 : row0) * p.nseg + s;
+        h->m = r ? ms[1] : ms[0];
+        h->top = r ? top[1] : top[0];
+        h->ocut = r ? ocut[1] : ocut[0];
+        h->n = r ? nlist[1] : nlist[0];
+    }
+}
+
+// ---------------------------------------------------------------- radix select
+
+// Exact tie-closed threshold of one row by radix select over the whole row
+// (4 passes of 8 bits over order-preserving keys, fp64 digit masses and digit
+// counts), among the elements with z >= zmin.  kcount > 0: the kcount-th
+// largest value (top-k); else the filter boundary, the largest value whose
+// tie-closed top set reaches `target` mass.  Sets L.tau and L.kept (mass of
+// z >= tau, z >= zmin, relative to m).  All threads of the merge call it; the
+// row arrives by value (an out-of-line call must not take the address of the
+// kernel arguments).
+struct RadixRow {
+    const void* row;
+    int V, bf16, vec;
+    double ys;
+};
+
+__device__ __noinline__ void radix_threshold(RadixRow p, float m, double target, int kcount, float zmin,
+                                             MergeLds& L) {
+    const void* row = p.row;
     const int tid = threadIdx.x;
     if (tid == 0) { L.prefix = 0; L.mask = 0; L.above = 0.0; L.abovec = 0; }
     __syncthreads();
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        for (int d = tid; d < 256; d += kThreads) { L.rad.rh_m[d] = 0.0; L.rad.rh_c[d] = 0; }
+        for (int d = tid; d < 256; d += kMThreads) { L.rad.rh_m[d] = 0.0; L.rad.rh_c[d] = 0; }
         __syncthreads();
         const uint32_t prefix = L.prefix, mask = L.mask;
-        for (int base = 0; base < p.V; base += kThreads * 16) {
+        for (int base = 0; base < p.V; base += kMThreads * 16) {
             float z[16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) load4(row, p.bf16, p.vec, p.V, base + (i * kThreads + tid) * 4, z + 4 * i);
+            for (int i = 0; i < 4; ++i) load4(row, p.bf16, p.vec, p.V, base + (i * kMThreads + tid) * 4, z + 4 * i);
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-                const int e = base + ((k >> 2) * kThreads + tid) * 4 + (k & 3);
+                const int e = base + ((k >> 2) * kMThreads + tid) * 4 + (k & 3);
                 const uint32_t key = fkey(z[k]);
                 if (e < p.V && (key & mask) == prefix && z[k] >= zmin) {
                     const int d = (key >> shift) & 0xFF;
-                    atomicAdd(&L.rad.rh_m[d], weight(z[k], m, p.invT, L.tab));
+                    atomicAdd(&L.rad.rh_m[d], weight(z[k], m, p.ys, L.tab));
                     atomicAdd(&L.rad.rh_c[d], 1);
                 }
             }
@@ -317,39 +525,307 @@ __device__ __forceinline__ void radix_threshold(const AcceptParams& p, const voi
     __syncthreads();
 }
 
-// Block-wide exclusive scan of one double per thread in thread order; returns
-// the exclusive prefix and writes the total to *total.  Fixed order.
-__device__ __forceinline__ double block_excl_scan(double v, double* scan, double* total) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const double inc = wave_incl_scan(v, lane);
-    __syncthreads();
-    scan[tid] = inc;
-    __syncthreads();
-    double off = 0.0, tot = 0.0;
-#pragma unroll
-    for (int u = 0; u < kThreads / 64; ++u) {
-        const double t = scan[u * 64 + 63];
-        if (u < wv) off += t;
-        tot += t;
-    }
-    *total = tot;
-    return off + inc - v;
+// ---------------------------------------------------------------- unit merge
+
+// Int wave minimum with DPP row shifts and broadcasts (every lane gets it).
+__device__ __forceinline__ int wave_min_i(int v) {
+    const int big = 0x7FFFFFFF;
+    int r = min(v, dpp_i<0x111, 0xF, 0xF>(v, big));
+    r = min(r, dpp_i<0x112, 0xF, 0xF>(v, big));
+    r = min(r, dpp_i<0x113, 0xF, 0xF>(v, big));
+    r = min(r, dpp_i<0x114, 0xF, 0xE>(r, big));
+    r = min(r, dpp_i<0x118, 0xF, 0xC>(r, big));
+    r = min(r, dpp_i<0x142, 0xA, 0xF>(r, big));
+    r = min(r, dpp_i<0x143, 0xC, 0xF>(r, big));
+    return __builtin_amdgcn_readlane(r, 63);
 }
 
-// Two block-wide exclusive scans at once (thread order, fixed order).
+// Segment and slot of flat list slot f (klist is 192 or 256).
+__device__ __forceinline__ void slot_pos(int f, int klist, int* sg, int* o) {
+    const int s = (klist == 256) ? (f >> 8) : ((f >> 6) / 3);
+    *sg = s;
+    *o = f - s * klist;
+}
+
+// Gather the listed entries of quarter bin R.top - R.og with z >= R.zmin from
+// the slots of each row whose list path is on (want), and rank them by
+// (z desc, id asc): R.rk.rz[rank] = z, R.rk.rw[rank] = fp64 weight relative to
+// the row max, R.ccount = their number.  Clears R.fast when there are none or
+// more than kCap.  All threads call it; each half works on its row (slot i of
+// this thread is valid iff bit i of vmask).
+__device__ __forceinline__ void rank_bin(const AcceptParams& p, const unsigned long long (&e)[kSlots],
+                                         unsigned vmask, bool want, MergeLds& L) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int rr = tid / kHalf, rt = tid & (kHalf - 1), rw = rt >> 6;
+    RowPart& R = L.r[rr];
+    const bool go = want && R.fast;
+    const int sel = R.top - R.og;
+    const float zmin = R.zmin;
+    unsigned long long bal[kSlots];
+    int wcount = 0;
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+        const float zi = entry_z(e[i]);
+        const bool in = go && ((vmask >> i) & 1u) && qbin(zi, p.qscale) == sel && zi >= zmin;
+        bal[i] = __ballot(in);
+        wcount += __popcll(bal[i]);
+    }
+    if (lane == 0) R.wcnt[rw] = wcount;
+    __syncthreads();
+    int base = 0, n = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kRW; ++w2) {
+        const int c = R.wcnt[w2];
+        base += (w2 < rw) ? c : 0;
+        n += c;
+    }
+    const bool ok = go && n > 0 && n <= kCap;
+    if (ok) {
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const unsigned long long bc = bal[i];
+            const int slot = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
+            if ((bc >> lane) & 1ull) {
+                const uint32_t id = static_cast<uint32_t>(entry_id(e[i]));
+                R.rk.ck[slot] = (static_cast<unsigned long long>(fkey(entry_z(e[i]))) << 32) | (0xFFFFFFFFu - id);
+            }
+            base += __popcll(bc);
+        }
+        for (int i = n + rt; i < ((n + 7) & ~7); i += kHalf) R.rk.ck[i] = 0ull;  // pad: never larger
+    }
+    if (rt == 0 && go) {
+        R.ccount = n;
+        if (!ok) R.fast = 0;
+    }
+    __syncthreads();
+    if (ok) {
+        // rank = number of larger keys (keys are distinct): each thread ranks
+        // entries rt and rt + kHalf in one pass over the keys, which the
+        // row's threads read together (LDS broadcast), 8 per batch
+        const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(R.rk.ck);
+        const bool h0 = rt < n, h1 = rt + kHalf < n;
+        const unsigned long long c0 = h0 ? R.rk.ck[rt] : ~0ull;
+        const unsigned long long c1 = h1 ? R.rk.ck[rt + kHalf] : ~0ull;
+        int r0 = 0, r1 = 0;
+#pragma unroll 4
+        for (int jj = 0; jj < n; jj += 8) {
+            const ulonglong2 a0 = k2[jj / 2], a1 = k2[jj / 2 + 1], a2 = k2[jj / 2 + 2], a3 = k2[jj / 2 + 3];
+            r0 += static_cast<int>(a0.x > c0) + static_cast<int>(a0.y > c0) + static_cast<int>(a1.x > c0) +
+                  static_cast<int>(a1.y > c0) + static_cast<int>(a2.x > c0) + static_cast<int>(a2.y > c0) +
+                  static_cast<int>(a3.x > c0) + static_cast<int>(a3.y > c0);
+            r1 += static_cast<int>(a0.x > c1) + static_cast<int>(a0.y > c1) + static_cast<int>(a1.x > c1) +
+                  static_cast<int>(a1.y > c1) + static_cast<int>(a2.x > c1) + static_cast<int>(a2.y > c1) +
+                  static_cast<int>(a3.x > c1) + static_cast<int>(a3.y > c1);
+        }
+        if (h0) {
+            const float zi = fkey_inv(static_cast<uint32_t>(c0 >> 32));
+            R.rk.rz[r0] = zi;
+            R.rk.rw[r0] = weight(zi, R.m, p.yscale, L.tab);
+        }
+        if (h1) {
+            const float zi = fkey_inv(static_cast<uint32_t>(c1 >> 32));
+            R.rk.rz[r1] = zi;
+            R.rk.rw[r1] = weight(zi, R.m, p.yscale, L.tab);
+        }
+    }
+    __syncthreads();
+}
+
+// Sub-bin of z inside its quarter bin sel: 64 equal parts of the bin's width,
+// in increasing z (y is the clamped z * 4/T of qbin; y - sel is exact below
+// 2^24 and 0 above, where every z of a bin is one value).
+__device__ __forceinline__ int sub_bin(float y, int sel) {
+    return min(static_cast<int>((y - static_cast<float>(sel)) * static_cast<float>(kSub)), kSub - 1);
+}
+
+// Nucleus threshold inside quarter bin og of each row with R.needsub: the
+// largest z whose tie-inclusive mass from the top (R.above, the bins above og,
+// plus the entries of og with z >= that value and z >= R.zmin) reaches
+// R.target; sets R.tau and R.kept.  The bin's listed entries are gathered
+// (z, then their fp64 weights, one or two per thread) and spread over kSub
+// sub-bins (mass, smallest and largest z); the first sub-bin from the top
+// whose cumulative mass reaches the target holds the threshold.  When that
+// sub-bin holds one value (bf16 logits nearly always), it is the threshold;
+// otherwise each of its entries' tie-inclusive mass is summed exactly.  All
+// threads call it; each half works on its row (slot i of this thread is valid
+// iff bit i of vmask).  The sub-bin arrays start cleared.
+__device__ __forceinline__ void subbin_threshold(const AcceptParams& p, const unsigned long long (&e)[kSlots],
+                                                 unsigned vmask, MergeLds& L) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int rr = tid / kHalf, rt = tid & (kHalf - 1), rw = rt >> 6;
+    RowPart& R = L.r[rr];
+    const bool go = R.needsub != 0;
+    const int sel = R.top - R.og;
+    const float zfloor = R.zmin;
+    // ---- gather the bin's entries
+    unsigned long long bal[kSlots];
+    int wcount = 0;
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+        const float zi = entry_z(e[i]);
+        const bool in = go && ((vmask >> i) & 1u) && qbin(zi, p.qscale) == sel && zi >= zfloor;
+        bal[i] = __ballot(in);
+        wcount += __popcll(bal[i]);
+    }
+    if (lane == 0) R.wcnt[rw] = wcount;
+    __syncthreads();
+    int base = 0, n = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kRW; ++w2) {
+        const int c = R.wcnt[w2];
+        base += (w2 < rw) ? c : 0;
+        n += c;
+    }
+    const bool ok = go && n <= kCap;
+    if (ok) {
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const unsigned long long bc = bal[i];
+            const int slot = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
+            if ((bc >> lane) & 1ull) R.rk.rz[slot] = entry_z(e[i]);
+            base += __popcll(bc);
+        }
+    }
+    if (rt == 0 && go) {
+        R.ccount = n;
+        if (!ok) R.fast = 0;  // more than the gather holds: whole-row select
+    }
+    __syncthreads();
+    // ---- weights and sub-bins
+    if (ok) {
+        for (int t = rt; t < n; t += kHalf) {
+            const float zi = R.rk.rz[t];
+            const float y = __builtin_amdgcn_fmed3f(zi * p.qscale, -1.0e9f, 1.0e9f);
+            const int sb = sub_bin(y, sel);
+            const uint32_t k = fkey(zi);
+            const double w = weight(zi, R.m, p.yscale, L.tab);
+            R.rk.rw[t] = w;
+            atomicAdd(&R.sbm[sb], w);
+            atomicMin(&R.sbk[0][sb], k);
+            atomicMax(&R.sbk[1][sb], k);
+        }
+    }
+    __syncthreads();
+    if (ok && rw == 0) {
+        const int sb = kSub - 1 - lane;  // lane 0: the highest sub-bin
+        const double v = R.sbm[sb];
+        const uint32_t kmin = R.sbk[0][sb], kmax = R.sbk[1][sb];
+        const double target = R.target;
+        const double cum = R.above + wave_incl_scan(v, lane);
+        const unsigned long long hit = __ballot(kmax != 0u && cum >= target);
+        const unsigned long long any = __ballot(kmax != 0u);
+        // no sub-bin reaches the target (rounding between the bin and entry
+        // sums): keep every entry, down to the lowest value
+        const int star = hit ? __ffsll(hit) - 1 : (any ? 63 - __clzll(any) : 0);
+        const double before = star > 0 ? __shfl(cum, star - 1, 64) : R.above;
+        const double at = __shfl(cum, star, 64);
+        const uint32_t smin = __shfl(kmin, star, 64), smax = __shfl(kmax, star, 64);
+        if (!hit || smin == smax) {  // uniform: one value, or everything kept
+            if (lane == 0) {
+                R.tau = fkey_inv(smin);
+                R.kept = at;
+            }
+        } else {
+            // several values in the crossing sub-bin: this wave gathers its
+            // entries (indices into rk) and sums each one's tie-inclusive mass
+            const int starsb = kSub - 1 - star;
+            int m = 0;
+            for (int c0 = 0; c0 < n; c0 += 64) {
+                const int i = c0 + lane;
+                bool in = false;
+                if (i < n) {
+                    const float zi = R.rk.rz[i];
+                    in = sub_bin(__builtin_amdgcn_fmed3f(zi * p.qscale, -1.0e9f, 1.0e9f), sel) == starsb;
+                }
+                const unsigned long long bc = __ballot(in);
+                if (in) {
+                    const int at2 = m + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
+                    R.rk.ck[at2] = static_cast<unsigned long long>(i);
+                }
+                m += __popcll(bc);
+            }
+            // the indices written by other lanes of this wave are read next
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float best = -INFINITY, lowest = INFINITY;
+            for (int c0 = 0; c0 < m; c0 += 64) {
+                const int a2 = c0 + lane;
+                const float zi = a2 < m ? R.rk.rz[static_cast<int>(R.rk.ck[a2])] : INFINITY;
+                double g = 0.0;
+                for (int jj = 0; jj < m; ++jj) {
+                    const int ij = static_cast<int>(R.rk.ck[jj]);
+                    g += (R.rk.rz[ij] >= zi) ? R.rk.rw[ij] : 0.0;
+                }
+                if (a2 < m) {
+                    lowest = fminf(lowest, zi);
+                    if (before + g >= target) best = fmaxf(best, zi);
+                }
+            }
+            best = wave_max(best);
+            lowest = -wave_max(-lowest);
+            const float tau = (best != -INFINITY) ? best : lowest;
+            double part = 0.0;
+            for (int c0 = 0; c0 < m; c0 += 64) {
+                const int a2 = c0 + lane;
+                if (a2 < m) {
+                    const int ia = static_cast<int>(R.rk.ck[a2]);
+                    part += (R.rk.rz[ia] >= tau) ? R.rk.rw[ia] : 0.0;
+                }
+            }
+            part = wave_sum(part);
+            if (lane == 0) {
+                R.tau = tau;
+                R.kept = before + part;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// The stopping row's parameters a draw needs (target q', draft p').
+struct DrawRows {
+    float mq, tq, mp, tp;  // row maxima and filter thresholds
+    double Sq, Sp;         // kept masses
+};
+
+// Draw weights of one element, each up to a positive factor common to the
+// whole row (the inverse-CDF draw is invariant to it): q' ~ w_q, and the
+// residual (q' - p')_+ = (w_q/S_q - w_p/S_p)_+ ~ (w_q*S_p - w_p*S_q)_+.  Both
+// exps are computed unconditionally, so the calls of an unrolled loop are
+// independent chains.
+__device__ __forceinline__ void pair_weights(const DrawRows& R, bool residual, float zq, float zpv,
+                                             bool valid, double ys, const double* tab, double* d,
+                                             double* q) {
+    const double wq = weight(zq, R.mq, ys, tab);
+    const double wp = weight(zpv, R.mp, ys, tab);
+    const double qv = (valid & (zq >= R.tq)) ? wq : 0.0;
+    const double pv = (valid & residual & (zpv >= R.tp)) ? wp : 0.0;
+    *q = qv;
+    const double dd = fma(qv, R.Sp, -(pv * R.Sq));
+    *d = residual ? (dd > 0.0 ? dd : 0.0) : qv;
+}
+
+// Block-wide exclusive scan of one or two doubles per thread in thread order
+// (fixed order); sa, sb hold the per-wave totals.
 __device__ __forceinline__ void block_excl_scan2(double a, double b, double* sa, double* sb,
                                                  double* ea, double* eb, double* ta, double* tb) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const double ia = wave_incl_scan(a, lane);
     const double ib = wave_incl_scan(b, lane);
     __syncthreads();
-    sa[tid] = ia;
-    sb[tid] = ib;
+    if (lane == 63) {
+        sa[wv] = ia;
+        sb[wv] = ib;
+    }
     __syncthreads();
     double oa = 0.0, ob = 0.0, xa = 0.0, xb = 0.0;
 #pragma unroll
-    for (int u = 0; u < kThreads / 64; ++u) {
-        const double va = sa[u * 64 + 63], vb = sb[u * 64 + 63];
+    for (int u = 0; u < kMThreads / 64; ++u) {
+        const double va = sa[u], vb = sb[u];
         if (u < wv) { oa += va; ob += vb; }
         xa += va;
         xb += vb;
@@ -360,551 +836,139 @@ __device__ __forceinline__ void block_excl_scan2(double a, double b, double* sa,
     *eb = ob + ib - b;
 }
 
-// ---------------------------------------------------------------- segment
-
-// Counts of bins kb_top - o, o in [0, kCutBins), and the candidate list: all
-// elements of the highest bins that fit in kList entries, in id order; then
-// the segment head.  The row merge takes bin masses from the lists.
-__device__ __forceinline__ void segment_list(const AcceptParams& p, int r, int s, const float* z,
-                                             float ms, double Ss, RowsLds& L) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int kb_top = bin_of(ms, p.bscale_c);  // segment bins
-    static_assert(4 * kCutBins == kThreads, "one counter per thread");
-    (&L.seg.hc[0][0])[tid] = 0;
-    __syncthreads();
-    int o[kPerThread];
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        o[k] = (z[k] == -INFINITY) ? kCutBins : kb_top - bin_of(z[k], p.bscale_c);
-        if (o[k] < kCutBins) atomicAdd(&L.seg.hc[wv][o[k]], 1);
-    }
-    __syncthreads();
-    if (tid < kCutBins) {
-        // cumulative counts from the top bin down; bins 0 .. fit-1 fit in the list
-        const int c = (L.seg.hc[0][tid] + L.seg.hc[1][tid]) + (L.seg.hc[2][tid] + L.seg.hc[3][tid]);
-        const int cum = wave_incl_scan(c, lane);
-        const unsigned long long bal = __ballot(cum <= kList);
-        if (lane == 0) L.seg.fit = __popcll(bal);
-    }
-    __syncthreads();
-    // bins 0 .. ocut fit (cum is nondecreasing); -1: the top bin alone overflows
-    const int ocut = L.seg.fit - 1;
-    // positions in id order: group g = k/4 holds ids s*4096 + g*1024 + 4*tid + k%4
-    unsigned long long packed = 0;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k)
-        if (o[k] <= ocut) packed += 1ull << (16 * (k >> 2));
-    // 64-bit words holding four 16-bit counters: no carry crosses a field
-    const unsigned long long inc = wave_incl_scan(packed, lane);
-    if (lane == 63) L.seg.wtot[wv] = inc;
-    __syncthreads();
-    unsigned long long off = 0, tot = 0;
-#pragma unroll
-    for (int u = 0; u < kThreads / 64; ++u) {
-        if (u < wv) off += L.seg.wtot[u];
-        tot += L.seg.wtot[u];
-    }
-    const unsigned long long excl = off + inc - packed;
-    int gofs[4];
-    int run = 0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        gofs[g] = run + static_cast<int>((excl >> (16 * g)) & 0xFFFF);
-        run += static_cast<int>((tot >> (16 * g)) & 0xFFFF);
-    }
-    unsigned long long* dst = p.list + (static_cast<size_t>(r) * p.nseg + s) * kList;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        if (o[k] <= ocut) {
-            const int g = k >> 2;
-            const unsigned id = static_cast<unsigned>(seg_index(s, tid, k));
-            st_coh(dst + gofs[g], (static_cast<unsigned long long>(id) << 32) | __float_as_uint(z[k]));
-            ++gofs[g];
-        }
-    }
+// Token drawn by a unit from its target row's lists (every thread returns it;
+// -1 when the residual has no mass).
+// The target half's thread rt holds flat slots rt + kHalf*i (coalesced
+// loads); members are valid slots with z >= tau_q, each with its draft logit
+// in zpv.  The draw weights -- (q' - p')_+, or q' when that has no mass -- go
+// to LDS in flat slot order, which is id order; runs of consecutive slots are
+// summed and scanned over the threads, the run holding the crossing is
+// walked, and the slot's owner supplies its id.
+__device__ __forceinline__ int draw_from_lists(const AcceptParams& p, const DrawRows& R, bool residual,
+                                               float us, const unsigned long long (&e)[kSlots],
+                                               const float (&zpv)[kSlots], unsigned vmask, int nslots,
+                                               MergeLds& L) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const bool tg = tid < kHalf;
     if (tid == 0) {
-        SegHead* h = p.seg + static_cast<size_t>(r) * p.nseg + s;
-        st_coh(&h->m, ms);
-        st_coh(&h->kb_top, bin_of(ms, p.bscale));
-        // segment bin c covers row bins kFine*c .. kFine*c + kFine-1 (the scales
-        // differ by a power of two, so both floors agree)
-        st_coh(&h->kb_cut, kFine * (kb_top - ocut));
-        st_coh(&h->n, run);
-        st_coh(&h->S, Ss);
+        L.fstar = 0x7FFFFFFF;
+        L.lastpos = -1;
+        if (!(us >= 0.0f && us < 1.0f)) set_status(p.status, 2);
     }
+    // every thread holds its row parameters in R: the weights may overwrite
+    // the row records (they share LDS)
+    __syncthreads();
+    int anyd = 0;
+    if (tg) {
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const int f = tid + kHalf * i;
+            const bool mem = ((vmask >> i) & 1u) && entry_z(e[i]) >= R.tq;
+            double d, q;
+            pair_weights(R, residual, entry_z(e[i]), zpv[i], mem, p.yscale, L.tab, &d, &q);
+            anyd |= (d > 0.0) ? 1 : 0;
+            if (f < nslots) L.wdraw[f] = d;
+        }
+    }
+    // the residual has mass (it can lack it through rounding only: then the
+    // caller draws from q' over the whole row)
+    if (residual && !__syncthreads_or(anyd)) return -1;  // uniform
+    __syncthreads();
+    // runs of E2 consecutive slots per target thread, summed in slot order
+    const int E2 = (nslots + kHalf - 1) / kHalf;
+    const int f0 = tg ? min(tid * E2, nslots) : nslots;
+    const int f1 = tg ? min(f0 + E2, nslots) : nslots;
+    double mine = 0.0;
+    int lastf = -1;
+    for (int f = f0; f < f1; ++f) {
+        const double w = L.wdraw[f];
+        mine += w;
+        if (w > 0.0) lastf = f;
+    }
+    double rx, zx, tot, tz;
+    block_excl_scan2(mine, 0.0, L.ta, L.tb, &rx, &zx, &tot, &tz);
+    const double target = static_cast<double>(us) * tot;
+    if ((mine > 0.0) & (rx <= target) & (target < rx + mine)) {
+        double run = rx;
+        int hit = -1;
+        for (int f = f0; f < f1 && hit < 0; ++f) {
+            const double w = L.wdraw[f];
+            if (w > 0.0) {
+                run += w;
+                if (target < run) hit = f;
+            }
+        }
+        if (hit >= 0) L.fstar = hit;
+    }
+    // the last slot of positive weight (rounding left the target past every
+    // prefix); slots grow with the thread, so one atomic per wave
+    const unsigned long long hasl = __ballot(lastf >= 0);
+    if (hasl && lane == 63 - __clzll(hasl)) atomicMax(&L.lastpos, lastf);
+    __syncthreads();
+    const int fs = (L.fstar != 0x7FFFFFFF) ? L.fstar : L.lastpos;
+    if (fs < 0) return 0;  // uniform: no mass at all
+    if (tid == (fs & (kHalf - 1))) {
+        const int ii = fs / kHalf;
+        int id = 0;
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i)
+            if (i == ii) id = entry_id(e[i]);
+        L.tok = id;
+    }
+    __syncthreads();
+    return L.tok;
 }
 
-// ---------------------------------------------------------------- row merge
-
-__device__ __forceinline__ float entry_z(unsigned long long e) {
-    return __uint_as_float(static_cast<unsigned>(e));
-}
-__device__ __forceinline__ int entry_id(unsigned long long e) { return static_cast<int>(e >> 32); }
-
-// Gather the listed entries of bin kb_sel with z >= zmin (held in registers:
-// slot tid of segments 0..kChunk-1) and rank them by (z desc, id asc):
-// L.cand.rz[rank] = z, L.cand.rw[rank] = its fp64 weight relative to the row
-// max m, L.ccount = their number.  Returns false in every thread
-// when there are none or more than kCap.
-__device__ __forceinline__ bool rank_bin(const AcceptParams& p, const unsigned long long* e, int kb_sel,
-                                         float zmin, float m, RowsLds& L) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    // per-wave counts, one barrier for the wave offsets, then positions from
-    // the ballots (no contended counter)
-    unsigned long long bal[kChunk];
-    int wcount = 0;
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-        const float zc = entry_z(e[c]);
-        const bool in = static_cast<int>(c < p.nseg) & static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
-                        static_cast<int>(bin_of(zc, p.bscale) == kb_sel) & static_cast<int>(zc >= zmin);
-        bal[c] = __ballot(in);
-        wcount += __popcll(bal[c]);
-    }
-    // (earlier reads of wcnt, ccount, ck, rz and rw all end before barriers of
-    // the caller)
-    if (lane == 0) L.cand.wcnt[wv] = wcount;
-    __syncthreads();
-    int base = 0;
-#pragma unroll
-    for (int u = 0; u < kThreads / 64; ++u) base += (u < wv) ? L.cand.wcnt[u] : 0;
-    const int n = L.cand.wcnt[0] + L.cand.wcnt[1] + L.cand.wcnt[2] + L.cand.wcnt[3];
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-        const unsigned long long bc = bal[c];
-        const int slot = base + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
-        if (((bc >> lane) & 1ull) && slot < kCap) {
-            const uint32_t id = static_cast<uint32_t>(entry_id(e[c]));
-            L.cand.ck[slot] = (static_cast<unsigned long long>(fkey(entry_z(e[c]))) << 32) | (0xFFFFFFFFu - id);
-        }
-        base += __popcll(bc);
-    }
-    if (tid == 0) L.ccount = n;
-    if (n > kCap || n == 0) {
-        __syncthreads();
-        return false;
-    }
-    // rank = number of larger keys (keys are distinct); every lane of a wave
-    // reads the same keys (LDS broadcast), 8 per batch
-    for (int i = n + tid; i < ((n + 7) & ~7); i += kThreads) L.cand.ck[i] = 0ull;  // pad: never larger
-    __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-        const unsigned long long ki = L.cand.ck[i];
-        int rank = 0;
-        const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(L.cand.ck);
-#pragma unroll 2
-        for (int j = 0; j < n; j += 8) {
-            const ulonglong2 a0 = k2[j / 2], a1 = k2[j / 2 + 1], a2 = k2[j / 2 + 2], a3 = k2[j / 2 + 3];
-            rank += static_cast<int>(a0.x > ki) + static_cast<int>(a0.y > ki) + static_cast<int>(a1.x > ki) +
-                    static_cast<int>(a1.y > ki) + static_cast<int>(a2.x > ki) + static_cast<int>(a2.y > ki) +
-                    static_cast<int>(a3.x > ki) + static_cast<int>(a3.y > ki);
-        }
-        const float zi = fkey_inv(static_cast<uint32_t>(ki >> 32));
-        L.cand.rz[rank] = zi;
-        L.cand.rw[rank] = weight(zi, m, p.invT, L.tab);  // relative to the row max
-    }
-    __syncthreads();
-    return true;
-}
-
-// Exact tie-closed nucleus threshold of a row from its merged bin masses (L.hm,
-// fp64, entries with z >= zmin) and the boundary bin's listed entries.  Sets
-// L.fast = 0 when the lists cannot decide it.
-__device__ __forceinline__ void list_threshold(const AcceptParams& p, double target, float zmin,
-                                               const unsigned long long* e, RowsLds& L) {
-    const int tid = threadIdx.x;
-    const float m = L.m;
-    const int kb_top = L.kb_top;
-    if (tid < 64) {
-        // first bin whose cumulative mass from the top reaches the target
-        // (lane l: bins kBinsPerLane*l .. +kBinsPerLane-1)
-        const int lane = tid;
-        double v[kBinsPerLane], tot = 0.0;
-#pragma unroll
-        for (int i = 0; i < kBinsPerLane; ++i) {
-            v[i] = L.cand.hm[kBinsPerLane * lane + i];
-            tot += v[i];
-        }
-        const double inc = wave_incl_scan(tot, lane);
-        const double before = inc - tot;
-        const unsigned long long hit = __ballot(inc >= target);
-        int og = -1;
-        double cum = 0.0;
-        if (hit) {
-            const int l = __ffsll(hit) - 1;
-            double run = __shfl(before, l, 64);
-            // the hitting lane's bins in order, from its prefix (read back
-            // from LDS: independent broadcast reads, not a chain of shuffles)
-            double vl[kBinsPerLane];
-#pragma unroll
-            for (int i = 0; i < kBinsPerLane; ++i) vl[i] = L.cand.hm[kBinsPerLane * l + i];
-            int sel = kBinsPerLane - 1;
-            double at = 0.0;
-            bool found = false;
-#pragma unroll
-            for (int i = 0; i < kBinsPerLane; ++i) {
-                const double vi = vl[i];
-                if (!found && run + vi >= target) { sel = i; at = run; found = true; }
-                run += vi;
-            }
-            if (!found) at = run - vl[kBinsPerLane - 1];
-            og = kBinsPerLane * l + sel;
-            cum = at;
-        }
-        if (lane == 0) {
-            // the boundary bin must be complete in every segment's list
-            const bool ok = og >= 0 && kb_top - og >= L.kb_lo && p.nseg <= kChunk;
-            L.og = og;
-            L.above = cum;
-            L.fast = ok ? 1 : 0;
-        }
-    }
-    __syncthreads();
-    if (!L.fast) return;
-    if (!rank_bin(p, e, kb_top - L.og, zmin, m, L)) {
-        if (tid == 0) L.fast = 0;
-        __syncthreads();
-        return;
-    }
-    const int n = L.ccount;
-    if (tid < 64) {
-        const int lane = tid;
-        double run = L.above;
-        int istar = -1;
-        for (int c0 = 0; c0 < n && istar < 0; c0 += 64) {
-            const double v = (c0 + lane < n) ? L.cand.rw[c0 + lane] : 0.0;
-            const double inc = run + wave_incl_scan(v, lane);
-            const unsigned long long hit = __ballot(c0 + lane < n && inc >= target);
-            if (hit) istar = c0 + __ffsll(hit) - 1;
-            run = __shfl(inc, 63, 64);
-        }
-        if (istar < 0) istar = n - 1;
-        const float tau = L.cand.rz[istar];
-        // kept mass: everything above the bin plus the entries >= tau (ties kept)
-        double part = 0.0;
-        for (int c0 = 0; c0 < n; c0 += 64) {
-            const int i = c0 + lane;
-            part += (i < n && L.cand.rz[i] >= tau) ? L.cand.rw[i] : 0.0;
-        }
-        part = wave_sum(part);
-        if (lane == 0) {
-            L.tau = tau;
-            L.kept = L.above + part;
-        }
-    }
-    __syncthreads();
-}
-
-// Top-k threshold of a row from its merged bin counts (L.hcnt) and the
-// boundary bin's listed entries: the k-th largest logit (ties kept).  Sets
-// L.zk, and L.fastk = 0 when the lists cannot decide it.
-__device__ __forceinline__ void topk_lists(const AcceptParams& p, const unsigned long long* e, RowsLds& L) {
-    const int tid = threadIdx.x;
-    const int kb_top = L.kb_top;
-    if (tid < 64) {
-        const int lane = tid;
-        int cv[kBinsPerLane], tot = 0;
-#pragma unroll
-        for (int i = 0; i < kBinsPerLane; ++i) {
-            cv[i] = L.cand.hcnt[kBinsPerLane * lane + i];
-            tot += cv[i];
-        }
-        const int inc = wave_incl_scan(tot, lane);
-        const int before = inc - tot;
-        const unsigned long long hit = __ballot(inc >= p.top_k);
-        int og = -1, cum = 0;
-        if (hit) {
-            const int l = __ffsll(hit) - 1;
-            int run = __shfl(before, l, 64);
-            int cl[kBinsPerLane];
-#pragma unroll
-            for (int i = 0; i < kBinsPerLane; ++i) cl[i] = L.cand.hcnt[kBinsPerLane * l + i];
-            int sel = kBinsPerLane - 1, at = 0;
-            bool found = false;
-#pragma unroll
-            for (int i = 0; i < kBinsPerLane; ++i) {
-                const int ci = cl[i];
-                if (!found && run + ci >= p.top_k) { sel = i; at = run; found = true; }
-                run += ci;
-            }
-            if (!found) at = run - cl[kBinsPerLane - 1];
-            og = kBinsPerLane * l + sel;
-            cum = at;
-        }
-        if (lane == 0) {
-            const bool ok = og >= 0 && kb_top - og >= L.kb_lo && p.nseg <= kChunk;
-            L.og = og;
-            L.abovec = cum;
-            L.fastk = ok ? 1 : 0;
-        }
-    }
-    __syncthreads();
-    if (!L.fastk) return;
-    if (!rank_bin(p, e, kb_top - L.og, -INFINITY, L.m, L)) {
-        if (tid == 0) L.fastk = 0;
-        __syncthreads();
-        return;
-    }
-    if (tid == 0) L.zk = L.cand.rz[min(p.top_k - L.abovec - 1, L.ccount - 1)];
-    __syncthreads();
-}
-
-// Merge the segments of row r and write its RowRec.
-__device__ __forceinline__ void finalize_row(const AcceptParams& p, int r, int b, RowsLds& L) {
-    const int tid = threadIdx.x;
-    const void* row = row_ptr(p, r);
-    const SegHead* sr = p.seg + static_cast<size_t>(r) * p.nseg;
-
-    // drafted token of this row: target row j < K_b (draft index r - b), or
-    // draft row j (draft index r - nt); -1: the bonus row
-    const bool is_target = r < p.nt;
-    const int xi = is_target ? ((r + 1 < seq_q0(p, b + 1)) ? r - b : -1) : r - p.nt;
-    const int j = xi;  // >= 0 iff the row has a drafted token
-
-    // one round trip: segment heads, the first kChunk segments' list slot
-    // tid, and the drafted logit
-    if (tid < p.nseg) {
-        L.seg_m[tid] = ld_coh(&sr[tid].m);
-        L.seg_kb[tid] = ld_coh(&sr[tid].kb_top);
-        L.seg_cut[tid] = ld_coh(&sr[tid].kb_cut);
-        L.seg_n[tid] = ld_coh(&sr[tid].n);
-        L.seg_S[tid] = ld_coh(&sr[tid].S);
-    }
-    const bool nuc = p.nucleus != 0;
-    unsigned long long e[kChunk];
-    const unsigned long long* lb = p.list + static_cast<size_t>(r) * p.nseg * kList;
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c)
-        e[c] = (nuc && c < p.nseg) ? ld_coh(lb + static_cast<size_t>(c) * kList + tid) : 0ull;
-    if (tid == kThreads - 1) {
-        // independent loads: the drafted token, and its logit as stored by the
-        // segment holding it (meaningful only for a valid token)
-        const int x = (j >= 0) ? p.draft_tokens[xi] : -1;
-        const float zv = ld_coh(p.zx + r);
-        L.n = x;
-        L.zx = (j >= 0 && x >= 0 && x < p.V && !p.greedy) ? zv : 0.0f;
-    }
-    __syncthreads();
-    if (tid < 64) {
-        // row max (first segment holding it: lowest ids), deepest complete bin
-        const int lane = tid;
-        float bv = (lane < p.nseg) ? L.seg_m[lane] : -INFINITY;
-        int bs = (lane < p.nseg) ? lane : 0x7FFFFFFF;
-        int lo = (lane < p.nseg) ? L.seg_cut[lane] : -0x40000000;
-        const int otop = (p.nseg <= 16) ? 16 : 64;  // lanes holding segments
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            if (o >= otop) continue;  // uniform
-            const float ov = __shfl_xor(bv, o, 64);
-            const int os = __shfl_xor(bs, o, 64);
-            const bool take = (ov > bv) | ((ov == bv) & (os < bs));
-            bv = take ? ov : bv;
-            bs = take ? os : bs;
-            lo = max(lo, __shfl_xor(lo, o, 64));
-        }
-        if (lane == 0) {
-            L.m = bv;
-            L.argmax = (bs < p.nseg) ? L.seg_kb[bs] : 0;
-            L.kb_top = bin_of(bv, p.bscale);
-            L.kb_lo = lo;
-        }
-        if (!p.greedy) {
-            // normaliser relative to the row max (lane 0 holds it), in the same
-            // wave: no barrier between the two
-            const float mrow = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bv)));
-            const float ms = (lane < p.nseg) ? L.seg_m[lane] : -INFINITY;
-            const double sc = (ms == -INFINITY) ? 0.0 : weight(ms, mrow, p.invT, L.tab);
-            if (lane < p.nseg) L.sc[lane] = sc;
-            const double S = wave_sum((lane < p.nseg) ? L.seg_S[lane] * sc : 0.0);
-            if (lane == 0) L.S = S;
-        }
-    }
-    for (int i = tid; i < kBins; i += kThreads) { L.cand.hm[i] = 0.0; L.cand.hcnt[i] = 0; }
-    if (tid == 0) { L.zk = -INFINITY; L.fastk = 1; L.Sk = 0.0; }
-    __syncthreads();
-    const float m = L.m;
-    const int x = L.n;
-    const bool x_ok = (x >= 0 && x < p.V);
-
-    RowRec rec;
-    rec.m = m;
-    rec.tau = -INFINITY;
-    rec.argmax = L.argmax;
-    rec.kept = 1;
-    rec.wx = 0.0;
-    rec.S = 0.0;
-    rec.fast = 0;
-    rec.pad = 0;
-
-    if (!p.greedy) {
-        // top-k first (the k largest logits and their ties), from the lists'
-        // bin counts or by radix select over the row
-        float zk = -INFINITY;
-        int fastk = 1;
-        if (nuc && p.top_k > 0) {
-            if (p.nseg <= kChunk) {
-                const int kb_top = L.kb_top;
-#pragma unroll
-                for (int c = 0; c < kChunk; ++c) {
-                    const int o = kb_top - bin_of(entry_z(e[c]), p.bscale);
-                    const bool in = static_cast<int>(c < p.nseg) &
-                                    static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
-                                    static_cast<int>(o < kBins);
-                    if (in) atomicAdd(&L.cand.hcnt[o], 1);
-                }
-            }
-            __syncthreads();
-            topk_lists(p, e, L);
-            if (!L.fastk) {
-                radix_threshold(p, row, m, 0.0, p.top_k, -INFINITY, L);
-                if (tid == 0) { L.zk = L.tau; L.Sk = L.kept; }
-                __syncthreads();
-            }
-            zk = L.zk;
-            fastk = L.fastk;
-        }
-        if (nuc && p.nseg <= kChunk && fastk) {
-            // bin masses of the listed entries with z >= zk, relative to the
-            // row max: exact for every bin at or above kb_lo, which all lists
-            // hold in full.  Weights of a batch are computed unconditionally
-            // (independent chains; unused slots are masked), then added.
-            const int kb_top = L.kb_top;
-#pragma unroll
-            for (int c0 = 0; c0 < kChunk; c0 += 4) {
-                if (c0 >= p.nseg) break;  // uniform
-                double wv[4];
-                int ov[4];
-                bool in[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int c = c0 + u;
-                    const float zc = entry_z(e[c]);
-                    ov[u] = kb_top - bin_of(zc, p.bscale);
-                    in[u] = static_cast<int>(c < p.nseg) &
-                            static_cast<int>(tid < L.seg_n[min(c, p.nseg - 1)]) &
-                            static_cast<int>(ov[u] < kBins) & static_cast<int>(zc >= zk);
-                    wv[u] = weight(zc, m, p.invT, L.tab);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (in[u]) atomicAdd(&L.cand.hm[ov[u]], wv[u]);
-            }
-        }
-        __syncthreads();
-        if (nuc && p.top_k > 0 && fastk) {
-            // mass of the top-k set: every kept entry is listed (its bin is
-            // at or above kb_lo and within kBins of the top)
-            if (tid < 64) {
-                double v = 0.0;
-#pragma unroll
-                for (int i = 0; i < kBinsPerLane; ++i) v += L.cand.hm[kBinsPerLane * tid + i];
-                v = wave_sum(v);
-                if (tid == 0) L.Sk = v;
-            }
-            __syncthreads();
-        }
-        rec.S = L.S;
-        if (nuc) {
-            const double Sk = (p.top_k > 0) ? L.Sk : L.S;
-            if (p.top_p < 1.0) {
-                const double target = p.top_p * Sk;
-                if (fastk) {
-                    list_threshold(p, target, zk, e, L);
-                } else {
-                    if (tid == 0) L.fast = 0;
-                    __syncthreads();
-                }
-                if (!L.fast) radix_threshold(p, row, m, target, 0, zk, L);
-                rec.tau = L.tau;
-                rec.S = L.kept;
-                rec.fast = L.fast;
-            } else {
-                rec.tau = zk;
-                rec.S = Sk;
-                rec.fast = fastk;
-            }
-        }
-    }
-    if (tid == 0) {
-        if (j >= 0) {
-            if (!x_ok) {
-                set_status(p.status, 1);
-                rec.kept = 0;
-            } else if (!p.greedy) {
-                rec.kept = (L.zx >= rec.tau) ? 1 : 0;
-                rec.wx = weight(L.zx, m, p.invT, L.tab);
-            }
-        }
-        RowRec* dst = p.rows + r;
-        st_coh(&dst->m, rec.m);
-        st_coh(&dst->tau, rec.tau);
-        st_coh(&dst->S, rec.S);
-        st_coh(&dst->wx, rec.wx);
-        st_coh(&dst->kept, rec.kept);
-        st_coh(&dst->argmax, rec.argmax);
-        st_coh(&dst->fast, rec.fast);
-    }
-}
-
-// ---------------------------------------------------------------- sequence
-
-// The stopping row's parameters a draw needs (target q', draft p').
-struct DrawRows {
-    float mq, tq, mp, tp;  // row maxima and nucleus thresholds
-    double Sq, Sp;         // kept masses
+// Token drawn from the unit's target row by one pass over the whole row
+// (rows whose lists do not hold the kept set, or rows beyond the list path):
+// thread t owns the contiguous ids [t*per, (t+1)*per).
+struct FullRow {
+    const void* qrow;
+    const void* prow;
+    int32_t* status;
+    int V, bf16;
+    double ys;
 };
 
-__device__ __forceinline__ DrawRows draw_rows(const RowRec& rq, const RowRec& rp) {
-    return DrawRows{rq.m, rq.tau, rp.m, rp.tau, rq.S, rp.S};
-}
-
-// Draw weights of one element of the stopping row: residual (q'-p')_+ and q'.
-// Branch-free: the weights are computed unconditionally and selected.
-// Draw weights of one element, each up to a positive factor common to the
-// whole row (the inverse-CDF draw is invariant to it): q' ~ w_q, and the
-// residual (q' - p')_+ = (w_q/S_q - w_p/S_p)_+ ~ (w_q*S_p - w_p*S_q)_+.
-// Both exps are computed unconditionally, so the calls of an unrolled loop
-// are independent chains.
-__device__ __forceinline__ void pair_weights(const DrawRows& R, bool residual, float zq, float zpv,
-                                             bool valid, double invT, const double* tab, double* d,
-                                             double* q) {
-    const double wq = weight(zq, R.mq, invT, tab);
-    const double wp = weight(zpv, R.mp, invT, tab);
-    const double qv = (valid & (zq >= R.tq)) ? wq : 0.0;
-    const double pv = (valid & residual & (zpv >= R.tp)) ? wp : 0.0;
-    *q = qv;
-    const double dd = fma(qv, R.Sp, -(pv * R.Sq));
-    *d = residual ? (dd > 0.0 ? dd : 0.0) : qv;
-}
-
-// The draw over per-thread runs of elements in id order (thread t's run
-// precedes thread t+1's).  Given this thread's sums `ds` (residual) and `qs`
-// (q'), finds the crossing run with two block scans and returns, in every
-// thread, the drawn id; `rescan(run, target, useq, &hit, &last)` walks this
-// thread's run from the prefix `run`.  The residual falls back to q' when it
-// has no mass.
-template <typename RS>
-__device__ __forceinline__ int draw_runs(const AcceptParams& p, int b, bool residual, double ds,
-                                         double qs, RS rescan, RowsLds& L) {
+__device__ __noinline__ int draw_full_row(FullRow p, DrawRows R, bool residual, float us, MergeLds& L) {
+    const void* qrow = p.qrow;
+    const void* prow = p.prow;
     const int tid = threadIdx.x;
-    double dt, qt;
-    const double dx = block_excl_scan(ds, L.sq.scan, &dt);
-    const double qx = block_excl_scan(qs, L.sq.scan, &qt);
+    const int per = (p.V + kMThreads - 1) / kMThreads;
+    const int e0 = min(p.V, tid * per), e1 = min(p.V, e0 + per);
+    const int bf16 = p.bf16;
+    const double ys = p.ys;
+    double ds = 0.0, qs = 0.0;
+    for (int e = e0; e < e1; ++e) {
+        double d, q;
+        pair_weights(R, residual, load1(qrow, bf16, e), residual ? load1(prow, bf16, e) : 0.0f, true,
+                     ys, L.tab, &d, &q);
+        ds += d;
+        qs += q;
+    }
+    if (tid == 0) { L.tok = 0x7FFFFFFF; L.lastpos = -1; }
+    double dx, qx, dt, qt;
+    block_excl_scan2(ds, qs, L.ta, L.tb, &dx, &qx, &dt, &qt);
     const bool useq = residual && !(dt > 0.0);
     const double tot = useq ? qt : dt;
-    const float u = L.us;
-    if (tid == 0 && !(u >= 0.0f && u < 1.0f)) set_status(p.status, 2);
-    const double target = static_cast<double>(u) * tot;
-    const double run0 = useq ? qx : dx;
+    if (tid == 0 && !(us >= 0.0f && us < 1.0f)) set_status(p.status, 2);
+    const double target = static_cast<double>(us) * tot;
     const double mine = useq ? qs : ds;
-    if (tid == 0) { L.tok = 0x7FFFFFFF; L.lastpos = -1; }
-    __syncthreads();
+    double run = useq ? qx : dx;
     if (mine > 0.0) {
         atomicMax(&L.lastpos, tid);
-        if (run0 <= target && target < run0 + mine) {
-            int hit = 0x7FFFFFFF, last = -1;
-            rescan(run0, target, useq, &hit, &last);
+        if (run <= target && target < run + mine) {
+            int hit = 0x7FFFFFFF;
+            for (int e = e0; e < e1; ++e) {
+                double d, q;
+                pair_weights(R, residual, load1(qrow, bf16, e), residual ? load1(prow, bf16, e) : 0.0f,
+                             true, ys, L.tab, &d, &q);
+                const double w = useq ? q : d;
+                if (w > 0.0) {
+                    run += w;
+                    if (hit == 0x7FFFFFFF && target < run) hit = e;
+                }
+            }
             if (hit != 0x7FFFFFFF) atomicMin(&L.tok, hit);
         }
     }
@@ -912,332 +976,639 @@ __device__ __forceinline__ int draw_runs(const AcceptParams& p, int b, bool resi
     if (L.tok == 0x7FFFFFFF) {
         // rounding left the target past every prefix: the last positive id
         if (tid == L.lastpos) {
-            int hit = 0x7FFFFFFF, last = -1;
-            rescan(run0, INFINITY, useq, &hit, &last);
+            int last = -1;
+            for (int e = e0; e < e1; ++e) {
+                double d, q;
+                pair_weights(R, residual, load1(qrow, bf16, e), residual ? load1(prow, bf16, e) : 0.0f,
+                             true, ys, L.tab, &d, &q);
+                if ((useq ? q : d) > 0.0) last = e;
+            }
             L.tok = last >= 0 ? last : 0;
         }
         __syncthreads();
         if (L.tok == 0x7FFFFFFF) return 0;
     }
-    return L.tok;
+    const int tok = L.tok;
+    __syncthreads();
+    return tok;
 }
 
-// Token drawn at position n of sequence b from the stopping row's lists.  The
-// residual (q'-p')_+ and q' vanish outside the target nucleus, so only list
-// entries with z >= tau_q take part.  Thread t takes the contiguous run of
-// flat list slots [t*E, (t+1)*E) (E = segments): list slots in (segment,
-// slot) order are in id order, so the runs are too, and slots that are empty
-// or below tau_q weigh zero.  The draft logits are fetched at the members'
-// ids, one block scan of the (residual, q') run sums finds the run that holds
-// the crossing, and E lanes of the owning thread's wave scan it (its entries
-// read from that thread's registers with lane reads).
-__device__ __forceinline__ int draw_from_lists(const AcceptParams& p, int b, int q0, int K, int n,
-                                               RowsLds& L) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int rq = q0 + n;
-    const bool residual = n < K;
-    const DrawRows R = draw_rows(L.sq.rr[n], residual ? L.sq.rr[K + 1 + n] : L.sq.rr[n]);
-    const int E0 = p.nseg;  // <= kChunk
-    const unsigned long long* lb = p.list + static_cast<size_t>(rq) * p.nseg * kList;
-    // one round trip: list lengths and every slot of this thread's run
-    if (tid < p.nseg) L.seg_n[tid] = ld_coh(&p.seg[static_cast<size_t>(rq) * p.nseg + tid].n);
-    unsigned long long e[kChunk];
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) e[i] = (i < E0) ? ld_coh(lb + tid * E0 + i) : 0ull;
-    __syncthreads();
-    // second round trip (residual): the draft logits at the members' ids
-    const void* drow = row_ptr(p, p.nt + q0 - b + (residual ? n : 0));
-    bool mem[kChunk];
-    float zpv[kChunk];
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-        const int lin = tid * E0 + i;
-        mem[i] = static_cast<int>(i < E0) &
-                 static_cast<int>((lin % kList) < L.seg_n[min(lin / kList, kMaxSeg - 1)]) &
-                 static_cast<int>(entry_z(e[i]) >= R.tq);
-        zpv[i] = (residual & mem[i]) ? load1(drow, p.bf16, entry_id(e[i])) : 0.0f;
-    }
-    double ds = 0.0, qs = 0.0;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-        if (i < E0) {  // uniform: no work for slots past the row's segments
-            double d, q;
-            pair_weights(R, residual, entry_z(e[i]), zpv[i], mem[i], p.invT, L.tab, &d, &q);
-            ds += d;
-            qs += q;
-            L.sq.zpa[i * kThreads + tid] = zpv[i];
-        }
-    }
-    double dt, qt;
-    double dx, qx;
-    if (tid == 0) { L.tok = 0x7FFFFFFF; L.lastpos = -1; }  // ordered by the scan's barriers
-    block_excl_scan2(ds, qs, L.sq.scan, L.sq.scan2, &dx, &qx, &dt, &qt);
-    const bool useq = residual && !(dt > 0.0);  // zero residual mass: fall back to q'
-    const double tot = useq ? qt : dt;
-    const float u = L.us;
-    if (tid == 0 && !(u >= 0.0f && u < 1.0f)) set_status(p.status, 2);
-    const double target = static_cast<double>(u) * tot;
-    const double run0 = useq ? qx : dx;
-    const double mine = useq ? qs : ds;
-    // the last run with positive mass (one atomic per wave), and the run that
-    // holds the crossing (one thread at most)
-    const unsigned long long posm = __ballot(mine > 0.0);
-    if (posm && lane == 63 - __clzll(posm)) atomicMax(&L.lastpos, tid);
-    if ((mine > 0.0) & (run0 <= target) & (target < run0 + mine)) L.tok = tid;
-    __syncthreads();
-    const bool tgt = (L.tok != 0x7FFFFFFF);
-    const int owner = tgt ? L.tok : L.lastpos;  // rounding: last positive run
-    if (owner < 0) return 0;  // uniform: no mass at all
-    if ((tid >> 6) == (owner >> 6)) {
-        // the owner's wave scans its run: lane i takes entry i, read from the
-        // owner lane's registers
-        const int ol = __builtin_amdgcn_readfirstlane(owner & 63);
-        unsigned mm = 0;
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) mm |= mem[i] ? (1u << i) : 0u;
-        mm = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(mm), ol));
-        const long long rb = __double_as_longlong(run0);
-        const unsigned rlo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(rb), ol));
-        const unsigned rhi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(rb >> 32), ol));
-        const double r0 = __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(rhi) << 32) | rlo));
-        unsigned long long ei = 0ull;
-#pragma unroll
-        for (int i = 0; i < kChunk; ++i) {
-            const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(e[i]), ol));
-            const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(e[i] >> 32), ol));
-            if (lane == i) ei = (static_cast<unsigned long long>(hi) << 32) | lo;
-        }
-        const bool ok = lane < E0;
-        const bool is_mem = ok && ((mm >> min(lane, 31)) & 1u);
-        double d = 0.0, q = 0.0;
-        pair_weights(R, residual, entry_z(ei), L.sq.zpa[min(lane, kChunk - 1) * kThreads + owner],
-                     is_mem, p.invT, L.tab, &d, &q);
-        const double w = useq ? q : d;
-        const double run = r0 + wave_incl_scan(w, lane);
-        const unsigned long long hit = __ballot((w > 0.0) & (target < run) & tgt);
-        const unsigned long long posb = __ballot(w > 0.0);
-        int src = -1;
-        if (hit) src = __ffsll(hit) - 1;
-        else if (posb) src = 63 - __clzll(posb);
-        const int id = entry_id(ei);
-        const int tok = (src >= 0) ? __shfl(id, src, 64) : 0;
-        if (lane == 0) L.n = tok;
-    }
-    __syncthreads();
-    return L.n;
-}
+// ---------------------------------------------------------------- sequence
 
-// Token drawn at position n of sequence b by one pass over the whole stopping
-// row (rows whose lists do not hold the nucleus): thread t owns the
-// contiguous ids [t*per, (t+1)*per).
-__device__ __forceinline__ int draw_full_row(const AcceptParams& p, int b, int q0, int K, int n,
-                                             RowsLds& L) {
+// Arrival of unit j of sequence b (all threads call it).  The units count
+// themselves in seq_word[b] (top bits) and set bit j there when x_j was
+// rejected; the last one to arrive stops at the first rejection n (K_b if
+// none) and writes out_tokens (drafts before n, the token drawn at n, -1
+// after it) and n_accepted.  A unit that drew a token stores it in utok first,
+// and its store completes before its arrival.  Draft lengths above kMaskBits
+// gather their rejection bits in seq_mask[b] instead.  has_tok: the token at
+// n is known here (with no filter the draw kernel writes it).
+__device__ __forceinline__ void sequence_arrival(const AcceptParams& p, int u, int b, int q0, int kb, int j,
+                                                 bool rej, bool drew, int token, bool has_tok, MergeLds& L) {
     const int tid = threadIdx.x;
-    const bool residual = n < K;
-    const DrawRows R = draw_rows(L.sq.rr[n], residual ? L.sq.rr[K + 1 + n] : L.sq.rr[n]);
-    const void* qrow = row_ptr(p, q0 + n);
-    const void* prow = residual ? row_ptr(p, p.nt + q0 - b + n) : qrow;
-    const int per = (p.V + kThreads - 1) / kThreads;
-    const int e0 = min(p.V, tid * per), e1 = min(p.V, e0 + per);
-    const int bf16 = p.bf16;
-    const double invT = p.invT;
-    double ds = 0.0, qs = 0.0;
-    for (int e = e0; e < e1; ++e) {
-        double d, q;
-        pair_weights(R, residual, load1(qrow, bf16, e), residual ? load1(prow, bf16, e) : 0.0f,
-                     true, invT, L.tab, &d, &q);
-        ds += d;
-        qs += q;
-    }
-    auto rescan = [&](double run, double target, bool useq, int* hit, int* last) {
-        for (int e = e0; e < e1; ++e) {
-            double d, q;
-            pair_weights(R, residual, load1(qrow, bf16, e), residual ? load1(prow, bf16, e) : 0.0f,
-                         true, invT, L.tab, &d, &q);
-            const double w = useq ? q : d;
-            if (w > 0.0) {
-                *last = e;
-                run += w;
-                if (*hit == 0x7FFFFFFF && target < run) *hit = e;
-            }
-        }
-    };
-    return draw_runs(p, b, residual, ds, qs, rescan, L);
-}
-
-// Accept scan of sequence b once all of its rows are final; with the nucleus
-// on (or greedy) also the emitted token.
-__device__ __forceinline__ void finalize_sequence(const AcceptParams& p, int b, RowsLds& L) {
-    const int tid = threadIdx.x;
-    const int q0 = seq_q0(p, b);  // uniform
-    const int K = seq_kb(p, b);   // this sequence's draft length
-    const int d0 = q0 - b;        // its first draft token / draft row
-    const int nt = p.nt;
-    const int nr = p.greedy ? K + 1 : 2 * K + 1;
-    __syncthreads();  // the row merge's LDS use ends
-    // one round trip: the sequence's row records, drafts and uniforms
-    if (tid < nr) {
-        const int r = (tid <= K) ? q0 + tid : nt + d0 + (tid - K - 1);
-        const RowRec* src = p.rows + r;
-        L.sq.rr[tid].m = ld_coh(&src->m);
-        L.sq.rr[tid].tau = ld_coh(&src->tau);
-        L.sq.rr[tid].S = ld_coh(&src->S);
-        L.sq.rr[tid].wx = ld_coh(&src->wx);
-        L.sq.rr[tid].kept = ld_coh(&src->kept);
-        L.sq.rr[tid].argmax = ld_coh(&src->argmax);
-        L.sq.rr[tid].fast = ld_coh(&src->fast);
-    }
-    if (tid >= 128 && tid - 128 < K) {
-        L.sq.x[tid - 128] = p.draft_tokens[d0 + tid - 128];
-        L.sq.ua[tid - 128] = p.greedy ? 0.0f : p.u_accept[d0 + tid - 128];
-    }
-    if (tid == kThreads - 1) L.us = p.greedy ? 0.0f : p.u_sample[b];
-    __syncthreads();
-    if (tid < 64) {
-        // every position's test at once (lane jj); n = first rejection
-        const int jj = tid;
-        bool acc = true;
-        if (jj < K) {
-            const RowRec& tr = L.sq.rr[jj];
-            if (p.greedy) {
-                acc = (L.sq.x[jj] == tr.argmax);
-            } else {
-                const RowRec& dr = L.sq.rr[K + 1 + jj];
-                const double q = tr.kept ? tr.wx / tr.S : 0.0;
-                const double pp = dr.kept ? dr.wx / dr.S : 0.0;
-                const float u = L.sq.ua[jj];
-                if (!(u >= 0.0f && u < 1.0f)) set_status(p.status, 2);
-                acc = (pp > 0.0) ? (static_cast<double>(u) * pp < q) : (q > 0.0);
-            }
-        }
-        const unsigned long long rej = __ballot(jj < K && !acc);
-        if (jj == 0) L.n = rej ? __ffsll(rej) - 1 : K;
-    }
-    __syncthreads();
     if (tid == 0) {
-        const int n = L.n;
-        int32_t* out = p.out_tokens + q0;
-        for (int i = 0; i < n; ++i) out[i] = L.sq.x[i];
-        for (int i = n + 1; i <= K; ++i) out[i] = -1;
-        if (p.greedy) out[n] = L.sq.rr[n].argmax;
-        p.n_accepted[b] = n;
-        p.seqs[b].n = n;
+        if (drew) st_coh(p.utok + u, token);
+        unsigned long long bits = 0ull;
+        bool last;
+        if (kb <= kMaskBits) {
+            const unsigned long long add = kArrive | (rej ? (1ull << j) : 0ull);
+            __builtin_amdgcn_s_waitcnt(0);
+            const unsigned long long old =
+                __hip_atomic_fetch_add(p.seq_word + b, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = (old >> kMaskBits) == static_cast<unsigned long long>(kb);
+            bits = (old + add) & (kArrive - 1);
+        } else {
+            if (rej) __hip_atomic_fetch_or(p.seq_mask + b, 1ull << j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0);
+            const unsigned long long old =
+                __hip_atomic_fetch_add(p.seq_word + b, kArrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = (old >> kMaskBits) == static_cast<unsigned long long>(kb);
+            if (last) bits = ld_coh(p.seq_mask + b);
+        }
+        int n = -1;
+        if (last) {
+            n = bits ? __ffsll(bits) - 1 : kb;
+            st_coh(p.seq_word + b, 0ull);
+            if (kb > kMaskBits) st_coh(p.seq_mask + b, 0ull);
+        }
+        L.seqn = n;
     }
     __syncthreads();
-    if (p.greedy || !p.nucleus) return;  // no nucleus: draw_kernel draws
-    const int n = L.n;
-    int tok = L.sq.rr[n].fast ? draw_from_lists(p, b, q0, K, n, L) : -1;
-    if (tok < 0) tok = draw_full_row(p, b, q0, K, n, L);
-    if (tid == 0) p.out_tokens[q0 + n] = tok;
+    const int n = L.seqn;
+    if (n < 0) return;
+    if (tid <= kb) {
+        if (tid < n) {
+            p.out_tokens[q0 + tid] = p.draft_tokens[q0 - b + tid];
+        } else if (tid > n) {
+            p.out_tokens[q0 + tid] = -1;
+        } else if (has_tok) {
+            p.out_tokens[q0 + tid] = (n == j) ? token : ld_coh(p.utok + q0 + n);
+        }
+    }
+    if (tid == 0) {
+        p.n_accepted[b] = n;
+        st_coh(&p.seqs[b].n, n);
+    }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void rows_kernel(AcceptParams p) {
-    __shared__ RowsLds L;
-    const int tid = threadIdx.x;
-    const int total = p.grid_rows * p.nseg;
-    const int logical = xcd_remap(blockIdx.x, total);
-    const int r = logical / p.nseg, s = logical % p.nseg;
-    if (r >= p.nrows) return;
-    const void* row = row_ptr(p, r);
-
-    const int nt = p.nt;
-    if (tid == 0) L.rb = 0;
-    float z[kPerThread];
-    load_segment(row, p.bf16, p.vec, p.V, s, tid, z);
-    fill_exp_table(L.tab);
-    // sequence of row r (ragged: the one whose target or draft rows hold it)
-    int br;
-    if (p.cu_q) {
-        const bool tgt = r < nt;
-        const int key = tgt ? r : r - nt;
-        __syncthreads();
-        for (int i = tid; i < p.B; i += kThreads) {
-            const int lo = p.cu_q[i] - (tgt ? 0 : i), hi = p.cu_q[i + 1] - (tgt ? 0 : i + 1);
-            if ((key >= lo) & (key < hi)) L.rb = i;
+// Row records of the unit's rows and the accept test of x_j (thread 0; every
+// thread returns the decision): q'_j(x) = w_x / kept mass if x is kept, else 0;
+// accept iff u * p' < q' (p' = 0: iff q' > 0).
+__device__ __forceinline__ bool accept_test(const AcceptParams& p, int u, int dr, int j, int kb, bool x_ok,
+                                            MergeLds& L) {
+    const RowPart& T = L.r[0];
+    const RowPart& D = L.r[1];
+    if (threadIdx.x == 0) {
+        bool acc = true;
+        const bool tk = x_ok && j < kb && T.zx >= T.tau;
+        const double wxq = (x_ok && j < kb) ? weight(T.zx, T.m, p.yscale, L.tab) : 0.0;
+        RowRec* tr = p.rows + u;
+        st_coh(&tr->m, T.m);
+        st_coh(&tr->tau, T.tau);
+        st_coh(&tr->S, T.kept);
+        st_coh(&tr->wx, wxq);
+        st_coh(&tr->kept, tk ? 1 : 0);
+        st_coh(&tr->fast, T.fast);
+        if (j < kb) {
+            const bool dk = x_ok && D.zx >= D.tau;
+            const double wxp = x_ok ? weight(D.zx, D.m, p.yscale, L.tab) : 0.0;
+            RowRec* drr = p.rows + dr;
+            st_coh(&drr->m, D.m);
+            st_coh(&drr->tau, D.tau);
+            st_coh(&drr->S, D.kept);
+            st_coh(&drr->wx, wxp);
+            st_coh(&drr->kept, dk ? 1 : 0);
+            st_coh(&drr->fast, D.fast);
+            if (!x_ok) set_status(p.status, 1);
+            const double q = tk ? wxq / T.kept : 0.0;
+            const double pp = dk ? wxp / D.kept : 0.0;
+            const float ua = L.ua;
+            if (!(ua >= 0.0f && ua < 1.0f)) set_status(p.status, 2);
+            acc = (pp > 0.0) ? (static_cast<double>(ua) * pp < q) : (q > 0.0);
         }
-        __syncthreads();
-        br = L.rb;
-    } else {
-        br = (r < nt) ? r / (p.K + 1) : (r - nt) / p.K;
-    }
-    // drafted token of this row (target row j < K_b: draft index r - b; draft
-    // row: r - nt); the segment holding it stores its logit for the merge
-    const int xi = (r < nt) ? ((r + 1 < seq_q0(p, br + 1)) ? r - br : -1) : r - nt;
-    const int xr = ((!p.greedy) & (xi >= 0)) ? p.draft_tokens[xi] : -1;
-    if ((xr >= s * kSeg) & (xr < (s + 1) * kSeg) & (xr < p.V)) {
-#pragma unroll
-        for (int k = 0; k < kPerThread; ++k)
-            if (seg_index(s, tid, k) == xr) st_coh(p.zx + r, z[k]);
+        L.acc = acc ? 1 : 0;
     }
     __syncthreads();
+    return L.acc != 0;
+}
+
+__device__ __forceinline__ DrawRows draw_rows(const MergeLds& L, bool residual) {
+    const RowPart& T = L.r[0];
+    const RowPart& D = L.r[1];
+    DrawRows Rw;
+    Rw.mq = T.m;
+    Rw.tq = T.tau;
+    Rw.Sq = T.kept;
+    Rw.mp = residual ? D.m : T.m;
+    Rw.tp = residual ? D.tau : T.tau;
+    Rw.Sp = residual ? D.kept : T.kept;
+    return Rw;
+}
+
+// ---------------------------------------------------------------- merge kernel
+
+// One workgroup per unit u: the target row (first half of the workgroup) and,
+// for j < K_b, the draft row (second half); then the accept test of x_j, the
+// draw after a rejection or for the bonus row, and the unit's arrival at its
+// sequence.
+__global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
+    __shared__ MergeLds L;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int u = blockIdx.x;
+    if (u >= p.nt) return;
+    // sequence of unit u: the number of sequences whose rows all precede it
+    int b;
+    if (p.cu_q) {
+        int cnt = 0;
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            const int i = b0 + lane;
+            cnt += __popcll(__ballot(i < p.B && p.cu_q[i + 1] <= u));
+        }
+        b = min(__builtin_amdgcn_readfirstlane(cnt), p.B - 1);
+    } else {
+        b = u / (p.K + 1);
+    }
+    const int q0 = seq_q0(p, b), kb = seq_kb(p, b), j = u - q0;
+    const bool has_d = !p.greedy && j < kb;
+    const int dr = p.nt + u - b;
+    const int x = (j < kb) ? p.draft_tokens[u - b] : -1;
+    const bool x_ok = x >= 0 && x < p.V;
+
+    if (p.greedy) {
+        fill_exp_table(L.tab);
+        // argmax of the target row: the segment maxima, lowest index on ties
+        if (tid < 64) {
+            float bv = -INFINITY;
+            int bi = 0x7FFFFFFF;
+            for (int s = lane; s < p.nseg; s += 64) {
+                const SegHead* h = p.seg + static_cast<size_t>(u) * p.nseg + s;
+                const float v = h->m;
+                const int i = h->top;
+                const bool take = (v > bv) | ((v == bv) & (i < bi));
+                bv = take ? v : bv;
+                bi = take ? i : bi;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
+                bv = take ? ov : bv;
+                bi = take ? oi : bi;
+            }
+            if (lane == 0) L.tok = bi;
+        }
+        __syncthreads();
+        const int am = L.tok;
+        bool acc = true;
+        if (j < kb) {
+            if (tid == 0 && !x_ok) set_status(p.status, 1);
+            acc = x_ok && x == am;
+        }
+        if (tid == 0) p.rows[u].argmax = am;
+        const bool drew = (j == kb) || !acc;
+        sequence_arrival(p, u, b, q0, kb, j, (j < kb) && !acc, drew, am, true, L);
+        return;
+    }
+
+    const int rr = tid / kHalf, rt = tid & (kHalf - 1), rw = rt >> 6;
+    RowPart& R = L.r[rr];
+    const bool act = (rr == 0) || has_d;
+    const int row = rr ? dr : u;
+    const int nslots = p.nseg * p.klist;
+    const bool lists = p.filter && p.nseg <= kListSegMax && nslots <= kHalf * kSlots;
+    unsigned long long e[kSlots];
+    float zpv[kSlots];
+
+    // ---- one round trip: the list slots of this thread (coalesced: slot
+    // rt + kHalf*i), segment heads, listed bin masses and counts, the drafted
+    // logit, the uniforms.  The segment kernel wrote them; this launch reads
+    // them with plain loads.  Every load is issued before the first LDS store.
+    constexpr int kBmIter = (kListSegMax * kQB + kHalf - 1) / kHalf;
+    static_assert(kMaxSeg <= kHalf, "one segment head per thread");
+    {
+        const unsigned long long* lb = p.list + static_cast<size_t>(row) * nslots;
+        const float* zb = p.lzp + static_cast<size_t>(u) * nslots;
+        const bool ldz = lists && rr == 0 && has_d;
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const int f = rt + kHalf * i;
+            const bool in = lists && act && f < nslots;
+            e[i] = in ? lb[f] : 0ull;
+            zpv[i] = (in && ldz) ? zb[f] : 0.0f;
+        }
+    }
+    SegHead h{};
+    double bmv[kBmIter];
+    int bcv[kBmIter];
+    const int nb = (lists && act) ? p.nseg * kQB : 0;
+    {
+        const SegHead* hs = p.seg + static_cast<size_t>(row) * p.nseg;
+        if (act && rt < p.nseg) h = hs[rt];
+        const double* bmr = p.bmass + static_cast<size_t>(row) * p.nseg * kQB;
+        const int* bcr = p.bcnt + static_cast<size_t>(row) * p.nseg * kQB;
+#pragma unroll
+        for (int it = 0; it < kBmIter; ++it) {
+            const int i = rt + kHalf * it;
+            bmv[it] = (i < nb) ? bmr[i] : 0.0;
+            bcv[it] = (i < nb && p.top_k > 0) ? bcr[i] : 0;
+        }
+    }
+    const float zxv = act ? p.zx[row] : 0.0f;
+    const float uav = (tid == kMThreads - 1 && j < kb) ? p.u_accept[u - b] : 0.0f;
+    const float usv = (tid == kMThreads - 1) ? p.u_sample[b] : 0.0f;
+    if (act) {
+        if (rt < p.nseg) {
+            R.seg_m[rt] = h.m;
+            R.seg_top[rt] = h.top;
+            R.seg_ocut[rt] = h.ocut;
+            R.seg_n[rt] = h.n;
+            R.seg_S[rt] = h.S;
+        }
+#pragma unroll
+        for (int it = 0; it < kBmIter; ++it) {
+            const int i = rt + kHalf * it;
+            if (i < nb) {
+                (&R.bm[0][0])[i] = bmv[it];
+                if (p.top_k > 0) (&R.bc[0][0])[i] = bcv[it];
+            }
+        }
+        if (rt == 0) R.zx = (x_ok && j < kb) ? zxv : 0.0f;
+    }
+    if (tid == kMThreads - 1) {
+        L.ua = uav;
+        L.us = usv;
+    }
+    fill_exp_table(L.tab);
+    __syncthreads();
+
+    // valid slots of this thread: slot < its segment's list length
+    unsigned vmask = 0u;
+    if (lists && act) {
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const int f = rt + kHalf * i;
+            int sg, o;
+            slot_pos(f, p.klist, &sg, &o);
+            if (f < nslots && o < R.seg_n[min(sg, kMaxSeg - 1)]) vmask |= 1u << i;
+        }
+    }
+
+    // ---- row max, normaliser and bin masses in one step: every wave of a row
+    // finds the row max and the segment scales exp((m_s - m)/T) itself (lane
+    // l holds segments l and l + 64) and sums its share of the segments' listed
+    // bin masses (every kRW-th segment; lane = row bin); the first wave also
+    // the normaliser and the bins listed in every segment
+    static_assert(kMaxSeg <= 128, "two segments per lane");
+    if (act) {
+        const bool s0 = lane < p.nseg, s1 = lane + 64 < p.nseg;
+        const float v0 = s0 ? R.seg_m[lane] : -INFINITY;
+        const float v1 = s1 ? R.seg_m[lane + 64] : -INFINITY;
+        const float m = wave_max(fmaxf(v0, v1));
+        const int top = qbin(m, p.qscale);
+        const double sc0 = (v0 == -INFINITY) ? 0.0 : weight(v0, m, p.yscale, L.tab);
+        const double sc1 = (v1 == -INFINITY) ? 0.0 : weight(v1, m, p.yscale, L.tab);
+        if (rw == 0) {
+            double Sacc = (s0 ? R.seg_S[lane] * sc0 : 0.0) + (s1 ? R.seg_S[lane + 64] * sc1 : 0.0);
+            int oc = 0x7FFFFFFF;
+            if (v0 != -INFINITY) oc = R.seg_ocut[lane] + (top - R.seg_top[lane]);
+            if (v1 != -INFINITY) oc = min(oc, R.seg_ocut[lane + 64] + (top - R.seg_top[lane + 64]));
+            Sacc = wave_sum(Sacc);
+            oc = wave_min_i(oc);
+            if (lane == 0) {
+                R.m = m;
+                R.top = top;
+                R.S = Sacc;
+                R.ocmax = oc;
+                R.fast = lists ? 1 : 0;
+                R.tau = -INFINITY;
+                R.kept = Sacc;
+                R.zk = -INFINITY;
+                R.Sk = Sacc;
+                R.zmin = -INFINITY;
+                R.ccount = 0;
+                R.needsub = 0;
+                R.above = 0.0;
+                R.abovec = 0;
+            }
+        }
+        if (lists) {
+            const int o = lane;
+            double pm = 0.0;
+            int pc = 0;
+            for (int s = rw; s < p.nseg; s += kRW) {  // s is uniform
+                const double scs = (s < 64) ? lane_read_d(sc0, s) : lane_read_d(sc1, s - 64);
+                const int os = o - (top - R.seg_top[s]);
+                if (R.seg_m[s] != -INFINITY && os >= 0 && os <= R.seg_ocut[s]) {
+                    pm += R.bm[s][os] * scs;
+                    if (p.top_k > 0) pc += R.bc[s][os];
+                }
+            }
+            R.part[rw][o] = pm;
+            R.cpart[rw][o] = pc;
+        }
+    }
+    if (rw == 1) {  // the sub-bins start cleared
+        R.sbm[lane] = 0.0;
+        R.sbk[0][lane] = 0xFFFFFFFFu;
+        R.sbk[1][lane] = 0u;
+    }
+    __syncthreads();
+
+    if (lists) {
+        // ---- the first wave of a row adds the partial bin masses in a fixed
+        // order and finds the first boundary bin (the top-k count boundary, or
+        // the nucleus mass boundary)
+        if (act && rw == 0) {
+            const int o = lane;
+            double mass = 0.0;
+            int cnt = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < kRW; ++w2) {
+                mass += R.part[w2][o];
+                cnt += R.cpart[w2][o];
+            }
+            R.mass[o] = mass;
+            int og;
+            if (p.top_k > 0) {
+                const int cum = wave_incl_scan(cnt, lane);
+                const unsigned long long hit = __ballot(cum >= p.top_k);
+                og = hit ? __ffsll(hit) - 1 : -1;
+                const int before = __shfl(cum, max(og - 1, 0), 64);
+                if (lane == 0) R.abovec = og > 0 ? before : 0;
+            } else {
+                const double target = p.top_p * R.S;
+                const double cum = wave_incl_scan(mass, lane);
+                const unsigned long long hit = __ballot(cum >= target);
+                og = hit ? __ffsll(hit) - 1 : -1;
+                const double before = __shfl(cum, max(og - 1, 0), 64);
+                if (lane == 0) R.above = og > 0 ? before : 0.0;
+            }
+            if (lane == 0) {
+                R.og = og;
+                if (!(og >= 0 && og <= R.ocmax)) R.fast = 0;
+                if (p.top_k == 0 && R.fast) {
+                    R.target = p.top_p * R.S;
+                    R.needsub = 1;
+                }
+            }
+        }
+        __syncthreads();
+        // ---- top-k: rank the count boundary bin; the k-th largest z, the
+        // mass of the top-k set, and where its nucleus boundary lies
+        if (p.top_k > 0) {  // uniform
+            rank_bin(p, e, vmask, act, L);
+            if (act && rw == 0 && R.fast) {
+                const int n = R.ccount;
+                const float zk = R.rk.rz[min(max(p.top_k - R.abovec - 1, 0), n - 1)];
+                const double mv = (lane < R.og) ? R.mass[lane] : 0.0;
+                const double cum = wave_incl_scan(mv, lane);
+                const double above = __shfl(cum, 63, 64);  // the complete bins above og
+                double part = 0.0;
+                for (int c0 = 0; c0 < n; c0 += 64) {
+                    const int i = c0 + lane;
+                    part += (i < n && R.rk.rz[i] >= zk) ? R.rk.rw[i] : 0.0;
+                }
+                part = wave_sum(part);
+                const double Sk = above + part;
+                if (p.top_p < 1.0) {
+                    const double target = p.top_p * Sk;
+                    const unsigned long long hit = __ballot(lane < R.og && cum >= target);
+                    const int on = hit ? __ffsll(hit) - 1 : 0;
+                    const double before = __shfl(cum, max(on - 1, 0), 64);
+                    if (lane == 0) {
+                        if (hit) {  // in a bin above og: all of it lies above zk
+                            R.og = on;
+                            R.above = on > 0 ? before : 0.0;
+                        } else {    // in og itself, among the entries with z >= zk
+                            R.above = above;
+                            R.zmin = zk;
+                        }
+                        R.target = target;
+                        R.needsub = 1;
+                    }
+                } else if (lane == 0) {
+                    R.tau = zk;
+                    R.kept = Sk;
+                }
+            }
+            __syncthreads();
+        }
+        subbin_threshold(p, e, vmask, L);
+    }
+
+    // ---- rows whose lists cannot decide: radix select over the whole row;
+    // such a unit draws from the whole target row (the slot registers are
+    // dead from here on that path)
+    if (p.filter && (!L.r[0].fast || (has_d && !L.r[1].fast))) {  // uniform
+        for (int r2 = 0; r2 < 2; ++r2) {
+            RowPart& Q = L.r[r2];
+            if (r2 == 1 && !has_d) break;
+            if (Q.fast) continue;  // uniform
+            const RadixRow rrow{row_ptr(p, r2 ? dr : u), p.V, p.bf16, p.vec, p.yscale};
+            const float m = Q.m;
+            float zk = -INFINITY;
+            double Sk = Q.S;
+            if (p.top_k > 0) {
+                radix_threshold(rrow, m, 0.0, p.top_k, -INFINITY, L);
+                zk = L.tau;
+                Sk = L.kept;
+            }
+            if (p.top_p < 1.0) radix_threshold(rrow, m, p.top_p * Sk, 0, zk, L);
+            if (tid == 0) {
+                Q.tau = (p.top_p < 1.0) ? L.tau : zk;
+                Q.kept = (p.top_p < 1.0) ? L.kept : Sk;
+            }
+            __syncthreads();
+        }
+        const bool acc = accept_test(p, u, dr, j, kb, x_ok, L);
+        const bool need = (j == kb) || !acc;
+        int token = -1;
+        if (need) {  // uniform
+            const bool residual = j < kb;
+            const FullRow fr{row_ptr(p, u), row_ptr(p, residual ? dr : u), p.status, p.V, p.bf16, p.yscale};
+            token = draw_full_row(fr, draw_rows(L, residual), residual, L.us, L);
+        }
+        sequence_arrival(p, u, b, q0, kb, j, (j < kb) && !acc, need, token, true, L);
+        return;
+    }
+    const bool acc = accept_test(p, u, dr, j, kb, x_ok, L);
+    const bool need = (j == kb) || !acc;
+    int token = -1;
+    if (p.filter && need) {  // uniform
+        const bool residual = j < kb;
+        const DrawRows Rw = draw_rows(L, residual);
+        token = lists ? draw_from_lists(p, Rw, residual, L.us, e, zpv, vmask, nslots, L) : -1;
+        if (token < 0) {  // uniform: beyond the list path, or no residual mass
+            const FullRow fr{row_ptr(p, u), row_ptr(p, residual ? dr : u), p.status, p.V, p.bf16, p.yscale};
+            token = draw_full_row(fr, Rw, residual, L.us, L);
+        }
+    }
+    sequence_arrival(p, u, b, q0, kb, j, (j < kb) && !acc, p.filter && need, token, p.filter != 0, L);
+}
+
+// ---------------------------------------------------------------- segment kernel
+
+template <int EPT>
+__global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
+    __shared__ SegLds L;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int total = p.grid_units * p.nseg;
+    const int logical = xcd_remap(blockIdx.x, total);
+    const int u = logical / p.nseg, s = logical % p.nseg;
+    if (u >= p.nt) return;
+    // sequence of unit u: the number of sequences whose rows all precede it
+    int b;
+    if (p.cu_q) {
+        int cnt = 0;
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            const int i = b0 + lane;
+            cnt += __popcll(__ballot(i < p.B && p.cu_q[i + 1] <= u));
+        }
+        b = min(__builtin_amdgcn_readfirstlane(cnt), p.B - 1);
+    } else {
+        b = u / (p.K + 1);
+    }
+    const int q0 = seq_q0(p, b), kb = seq_kb(p, b), j = u - q0;
+    const bool has_d = !p.greedy && j < kb;
+    const int dr = p.nt + u - b;
+    float z[2][EPT];
+    load_segment<EPT>(row_ptr(p, u), p.bf16, p.vec, p.V, s, tid, z[0]);
+    if (has_d) {
+        load_segment<EPT>(row_ptr(p, dr), p.bf16, p.vec, p.V, s, tid, z[1]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) z[1][k] = -INFINITY;
+    }
+    fill_exp_table(L.tab);
+    // the segment counters start at zero (ordered before use by the first barrier)
+    for (int i = tid; i < 2 * 4 * (kQB + 64); i += kThreads) (&L.hc[0][0][0])[i] = 0;
+    for (int i = tid; i < 2 * kQB; i += kThreads) (&L.hm[0][0])[i] = 0.0;
+    // the drafted token's logits, stored by the thread that holds them
+    // (element k of thread t has id seg_lo + (k/4)*1024 + 4*t + k%4)
+    const int x = (j < kb) ? p.draft_tokens[u - b] : -1;
+    const int seg_lo = s * kThreads * EPT;
+    if (!p.greedy && x >= seg_lo && x < seg_lo + kThreads * EPT && x < p.V) {
+        const int off = x - seg_lo;
+        const int kx = ((off >> 10) << 2) | (off & 3);
+        if (tid == ((off & 1023) >> 2)) {
+            float zq = 0.0f, zp = 0.0f;
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                zq = (k == kx) ? z[0][k] : zq;
+                zp = (k == kx) ? z[1][k] : zp;
+            }
+            p.zx[u] = zq;
+            if (has_d) p.zx[dr] = zp;
+        }
+    }
 
     if (p.greedy) {
         float bv = -INFINITY;
         int bi = 0x7FFFFFFF;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
-            int e = seg_index(s, tid, k);
-            const bool take = (e < p.V) & ((z[k] > bv) | ((z[k] == bv) & (e < bi)));
-            bv = take ? z[k] : bv;
+        for (int k = 0; k < EPT; ++k) {
+            const int e = seg_index<EPT>(s, tid, k);
+            const bool take = (e < p.V) & ((z[0][k] > bv) | ((z[0][k] == bv) & (e < bi)));
+            bv = take ? z[0][k] : bv;
             bi = take ? e : bi;
         }
-        // (value desc, index asc) reduction
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
-            float ov = __shfl_xor(bv, o, 64);
-            int oi = __shfl_xor(bi, o, 64);
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
             const bool take = (ov > bv) | ((ov == bv) & (oi < bi));
             bv = take ? ov : bv;
             bi = take ? oi : bi;
         }
-        __shared__ float gv[kThreads / 64];
-        __shared__ int gi[kThreads / 64];
-        if ((tid & 63) == 0) { gv[tid >> 6] = bv; gi[tid >> 6] = bi; }
+        if (lane == 0) {
+            L.gv[wv] = bv;
+            L.gi[wv] = bi;
+        }
         __syncthreads();
         if (tid == 0) {
-            for (int w = 1; w < kThreads / 64; ++w)
-                if (gv[w] > bv || (gv[w] == bv && gi[w] < bi)) { bv = gv[w]; bi = gi[w]; }
-            SegHead* dst = p.seg + static_cast<size_t>(r) * p.nseg + s;
-            st_coh(&dst->m, bv);
-            st_coh(&dst->kb_top, bi);
+            for (int w2 = 1; w2 < kThreads / 64; ++w2)
+                if (L.gv[w2] > bv || (L.gv[w2] == bv && L.gi[w2] < bi)) {
+                    bv = L.gv[w2];
+                    bi = L.gi[w2];
+                }
+            SegHead* h = p.seg + static_cast<size_t>(u) * p.nseg + s;
+            h->m = bv;
+            h->top = bi;
         }
     } else {
-        float lm = -INFINITY;
+        float lm[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) lm = fmaxf(lm, z[k]);
-        const float ms = block_max<kThreads>(lm, L.red_f);
-        double acc = 0.0;
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k)
-            acc += (ms == -INFINITY) ? 0.0 : weight(z[k], ms, p.invT, L.tab);
-        const double Ss = block_sum<kThreads>(acc, L.red_d);
-        if (p.nucleus) {
-            segment_list(p, r, s, z, ms, Ss, L);
-        } else if (tid == 0) {
-            SegHead* dst = p.seg + static_cast<size_t>(r) * p.nseg + s;
-            st_coh(&dst->m, ms);
-            st_coh(&dst->kb_top, bin_of(ms, p.bscale));
-            st_coh(&dst->S, Ss);
+            for (int k = 0; k < EPT; ++k) lm[r] = fmaxf(lm[r], z[r][k]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            lm[r] = wave_max(lm[r]);
+            if (lane == 0) L.red_f[r][wv] = lm[r];
+        }
+        __syncthreads();
+        float ms[2];
+        int top[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            ms[r] = fmaxf(fmaxf(L.red_f[r][0], L.red_f[r][1]), fmaxf(L.red_f[r][2], L.red_f[r][3]));
+            top[r] = qbin(ms[r], p.qscale);
+        }
+        // one pass per element: the fp64 weight (a row max of -inf gives NaN
+        // arguments, which exp2_256 maps to 0) and, with a filter on, the bin
+        // offset (kept) and its count
+        double acc[2] = {0.0, 0.0};
+        unsigned ow[2][EPT / 4];  // bin offsets (0..kQB-1 in the window, kQB.. below it), four per word
+        const unsigned past = static_cast<unsigned>(kQB + lane);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+#pragma unroll
+            for (int g = 0; g < EPT / 4; ++g) ow[r][g] = 0u;  // row 1 without a draft: never listed (ocut -1)
+            if (r == 1 && !has_d) continue;  // uniform
+            const double mr = static_cast<double>(ms[r]);
+            if (p.filter) {  // uniform
+#pragma unroll
+                for (int k = 0; k < EPT; ++k) {
+                    acc[r] += exp2_256((static_cast<double>(z[r][k]) - mr) * p.yscale, L.tab);
+                    // the bin offset; below the window a counter past the bins
+                    // (at most the lane's own: no branch, few conflicts)
+                    const unsigned o = min(static_cast<unsigned>(top[r] - qbin(z[r][k], p.qscale)), past);
+                    ow[r][k >> 2] |= o << (8 * (k & 3));
+                    atomicAdd(&L.hc[r][wv][o], 1);
+                    // four elements at a time: the exps of a whole row in
+                    // flight at once would cost occupancy
+                    if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < EPT; ++k) {
+                    acc[r] += exp2_256((static_cast<double>(z[r][k]) - mr) * p.yscale, L.tab);
+                    if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            acc[r] = wave_sum(acc[r]);
+            if (lane == 0) L.red_d[r][wv] = acc[r];
+        }
+        __syncthreads();
+        if (p.filter) segment_lists<EPT>(p, s, u, dr, has_d, z, ow, top, ms, L);
+        if (tid < (has_d ? 2 : 1)) {
+            const int r = tid;
+            SegHead* h = p.seg + static_cast<size_t>(r ? dr : u) * p.nseg + s;
+            h->S = (L.red_d[r][0] + L.red_d[r][1]) + (L.red_d[r][2] + L.red_d[r][3]);
+            if (!p.filter) h->m = r ? ms[1] : ms[0];
         }
     }
-
-    if (!arrive_last(p.row_cnt + r, p.nseg, &L.flag)) return;
-    // the merges are the critical path: their waves issue ahead of the
-    // segment work still running on the same compute unit
-    __builtin_amdgcn_s_setprio(3);
-    finalize_row(p, r, br, L);
-
-    const int b = br;
-    const int kb = seq_kb(p, b);
-    const int rows_per_seq = p.greedy ? kb + 1 : 2 * kb + 1;
-    if (!arrive_last(p.seq_cnt + b, rows_per_seq, &L.flag)) return;
-    finalize_sequence(p, b, L);
 }
 
-// ---------------------------------------------------------------- draw
+
+// ---------------------------------------------------------------- draw (no filter)
 
 struct DrawLds {
-    double tab[64];
+    double tab[256];
     double red_d[kThreads / 64];
     double red_d2[kThreads / 64];
     int flag;
@@ -1266,11 +1637,11 @@ struct DrawCtx {
 
 __device__ __forceinline__ void draw_weights(const DrawCtx& c, const AcceptParams& p, float zq,
                                              float zp, bool valid, double* w, double* qv) {
-    const double wq = weight(zq, c.rq.m, p.invT, c.tab) * c.invSq;
+    const double wq = weight(zq, c.rq.m, p.yscale, c.tab) * c.invSq;
     const double q = (valid & (zq >= c.rq.tau)) ? wq : 0.0;
     *qv = q;
     if (c.residual) {
-        const double wp = weight(zp, c.rp.m, p.invT, c.tab) * c.invSp;
+        const double wp = weight(zp, c.rp.m, p.yscale, c.tab) * c.invSp;
         const double pv = (valid & (zp >= c.rp.tau)) ? wp : 0.0;
         const double d = q - pv;
         *w = d > 0.0 ? d : 0.0;
@@ -1279,6 +1650,7 @@ __device__ __forceinline__ void draw_weights(const DrawCtx& c, const AcceptParam
     }
 }
 
+template <int EPT>
 __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid_seqs) {
     __shared__ DrawLds L;
     const int tid = threadIdx.x;
@@ -1312,14 +1684,14 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
         c.invSp = 0.0;
     }
 
-    float zq[kPerThread], zp[kPerThread];
-    load_segment(c.qrow, p.bf16, p.vec, p.V, s, tid, zq);
-    if (c.residual) load_segment(c.prow, p.bf16, p.vec, p.V, s, tid, zp);
+    float zq[EPT], zp[EPT];
+    load_segment<EPT>(c.qrow, p.bf16, p.vec, p.V, s, tid, zq);
+    if (c.residual) load_segment<EPT>(c.prow, p.bf16, p.vec, p.V, s, tid, zp);
     double ws = 0.0, qs = 0.0;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
+    for (int k = 0; k < EPT; ++k) {
         double w, qv;
-        const bool valid = seg_index(s, tid, k) < p.V;
+        const bool valid = seg_index<EPT>(s, tid, k) < p.V;
         draw_weights(c, p, zq[k], c.residual ? zp[k] : 0.0f, valid, &w, &qv);
         ws += w;
         qs += qv;
@@ -1333,9 +1705,9 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
     if (!arrive_last(p.draw_cnt + b, p.nseg, &L.flag)) return;
 
     // ---- last segment of sequence b: every segment sum in one round trip
-    if (tid < p.nseg) {
-        L.ds[tid] = ld_coh(p.dsum + static_cast<size_t>(b) * p.nseg + tid);
-        L.qs[tid] = ld_coh(p.qsum + static_cast<size_t>(b) * p.nseg + tid);
+    for (int t = tid; t < p.nseg; t += kThreads) {
+        L.ds[t] = ld_coh(p.dsum + static_cast<size_t>(b) * p.nseg + t);
+        L.qs[t] = ld_coh(p.qsum + static_cast<size_t>(b) * p.nseg + t);
     }
     __syncthreads();
     if (tid == 0) {
@@ -1369,18 +1741,18 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
     __syncthreads();
     const int ss = L.sstar;
     const double target = L.target;
-    // contiguous layout for the exact in-order scan: thread t owns 16 ids
-    const int e0 = ss * kSeg + tid * kPerThread;
-    float q4[16], p4[16];
+    // contiguous layout for the exact in-order scan: thread t owns EPT ids
+    const int e0 = ss * (kThreads * EPT) + tid * EPT;
+    float q4[EPT], p4[EPT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < EPT / 4; ++i) {
         load4(c.qrow, p.bf16, p.vec, p.V, e0 + 4 * i, q4 + 4 * i);
         if (c.residual) load4(c.prow, p.bf16, p.vec, p.V, e0 + 4 * i, p4 + 4 * i);
     }
-    double w[kPerThread];
+    double w[EPT];
     double loc = 0.0;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
+    for (int k = 0; k < EPT; ++k) {
         double ww, qv;
         const bool valid = e0 + k < p.V;
         draw_weights(c, p, q4[k], c.residual ? p4[k] : 0.0f, valid, &ww, &qv);
@@ -1397,7 +1769,7 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
     double run = off + inc - loc;
     int mine = 0x7FFFFFFF, lastpos = -1;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
+    for (int k = 0; k < EPT; ++k) {
         if (w[k] > 0.0) lastpos = e0 + k;
         run += w[k];
         mine = ((mine == 0x7FFFFFFF) & (w[k] > 0.0) & (target < run)) ? e0 + k : mine;
@@ -1417,29 +1789,109 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
     }
 }
 
-}  // namespace
+// ---------------------------------------------------------------- host
 
-size_t accept_workspace_bytes(int B, long long nt, int V) {
-    const size_t nseg = (static_cast<size_t>(V) + kSeg - 1) / kSeg;
-    const size_t nrows = static_cast<size_t>(2 * nt - B);  // target and draft rows
-    size_t off = 0;
-    auto take = [&](size_t bytes) { off = (off + 255) & ~static_cast<size_t>(255); off += bytes; };
-    // arrival counters first, sized for any draft lengths of B sequences
-    take(static_cast<size_t>(B) * sizeof(int));
-    take(static_cast<size_t>(B) * sizeof(int));
-    take(static_cast<size_t>(B) * kMaxRowsPerSeq * sizeof(int));
-    take(nrows * nseg * sizeof(SegHead));
-    take(nrows * nseg * kList * sizeof(unsigned long long));
-    take(nrows * sizeof(RowRec));
-    take(nrows * sizeof(float));
-    take(static_cast<size_t>(B) * sizeof(SeqRec));
-    take(static_cast<size_t>(B) * nseg * sizeof(double));
-    take(static_cast<size_t>(B) * nseg * sizeof(double));
-    return (off + 255) & ~static_cast<size_t>(255);
+struct Layout {
+    int nseg, klist;
+};
+
+Layout layout_for(int ept, int V) {
+    const int seg = kThreads * ept;
+    return Layout{(V + seg - 1) / seg, 16 * ept};
 }
 
-int accept_max_vocab() { return kMaxSeg * kSeg; }
-int accept_max_drafts() { return 64; }
+// Workgroups of one launch per compute unit, cached per device.
+int device_cus() {
+    static int cache[16];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    cache[dev] = cus;
+    return cus;
+}
+
+// Segments of 4096 (EPT 16) or 3072 (EPT 12) logits: the list path needs
+// nseg*klist <= 4096 slots and nseg <= kListSegMax; among the sizes that
+// allow it (when a filter is on), the one whose grid fills the last round of
+// workgroups on the compute units best (three resident per unit).
+int choose_ept(long long units, int V, bool filter) {
+    const int cus = device_cus();
+    int best = 16;
+    double best_fill = -1.0;
+    for (int ept : {16, 12}) {
+        const Layout l = layout_for(ept, V);
+        const bool lists = l.nseg <= kListSegMax && l.nseg * l.klist <= kHalf * kSlots;
+        if (filter && !lists && best_fill >= 0.0) continue;
+        const long long wgs = units * l.nseg;
+        const long long slots = 3LL * cus;
+        const long long rounds = (wgs + slots - 1) / slots;
+        const double fill = static_cast<double>(wgs) / static_cast<double>(rounds * slots);
+        const bool better = best_fill < 0.0 || fill > best_fill + 1e-9;
+        const Layout bl = layout_for(best, V);
+        const bool best_lists = bl.nseg <= kListSegMax && bl.nseg * bl.klist <= kHalf * kSlots;
+        if (better || (filter && lists && !best_lists)) {
+            best = ept;
+            best_fill = fill;
+        }
+    }
+    return best;
+}
+
+// Offsets of the workspace parts (counters first: their place depends on B only).
+struct WsParts {
+    size_t seq_word, seq_mask, draw_cnt, seg, list, lzp, bmass, bcnt, rows, zx, utok, seqs,
+        dsum, qsum, end;
+};
+
+WsParts ws_parts(int B, long long nt, int V) {
+    size_t nseg = 0, slots = 0;
+    for (int ept : {16, 12}) {
+        const Layout l = layout_for(ept, V);
+        nseg = nseg > static_cast<size_t>(l.nseg) ? nseg : static_cast<size_t>(l.nseg);
+        const size_t sl = static_cast<size_t>(l.nseg) * l.klist;
+        slots = slots > sl ? slots : sl;
+    }
+    const size_t nrows = static_cast<size_t>(2 * nt - B);  // target and draft rows
+    WsParts w{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        off = (off + 255) & ~static_cast<size_t>(255);
+        const size_t at = off;
+        off += bytes;
+        return at;
+    };
+    w.seq_word = take(static_cast<size_t>(B) * sizeof(unsigned long long));
+    w.seq_mask = take(static_cast<size_t>(B) * sizeof(unsigned long long));
+    w.draw_cnt = take(static_cast<size_t>(B) * sizeof(int));
+    w.seg = take(nrows * nseg * sizeof(SegHead));
+    w.list = take(nrows * slots * sizeof(unsigned long long));
+    w.lzp = take(static_cast<size_t>(nt) * slots * sizeof(float));
+    w.bmass = take(nrows * nseg * kQB * sizeof(double));
+    w.bcnt = take(nrows * nseg * kQB * sizeof(int));
+    w.rows = take(nrows * sizeof(RowRec));
+    w.zx = take(nrows * sizeof(float));
+    w.utok = take(static_cast<size_t>(nt) * sizeof(int));
+    w.seqs = take(static_cast<size_t>(B) * sizeof(SeqRec));
+    w.dsum = take(static_cast<size_t>(B) * nseg * sizeof(double));
+    w.qsum = take(static_cast<size_t>(B) * nseg * sizeof(double));
+    w.end = (off + 255) & ~static_cast<size_t>(255);
+    return w;
+}
+
+}  // namespace
+
+size_t accept_workspace_bytes(int B, long long nt, int V) { return ws_parts(B, nt, V).end; }
+
+int accept_max_vocab() { return 262144; }
+int accept_max_drafts() { return kMaxDrafts; }
 
 hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     AcceptParams p{};
@@ -1456,49 +1908,52 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     p.cu_q = a.cu_q;
     p.nt = a.nt;
     p.V = a.V;
-    p.nseg = (a.V + kSeg - 1) / kSeg;
     p.bf16 = a.bf16;
     p.vec = (a.V % 4 == 0) ? 1 : 0;
     p.greedy = a.greedy;
-    p.top_k = (a.top_k > 0 && a.top_k < a.V) ? a.top_k : 0;
-    p.nucleus = (!a.greedy && (a.top_p < 1.0f || p.top_k > 0)) ? 1 : 0;
-    p.invT = 1.0 / static_cast<double>(a.temperature);
+    p.top_k = (!a.greedy && a.top_k > 0 && a.top_k < a.V) ? a.top_k : 0;
+    p.filter = (!a.greedy && (a.top_p < 1.0f || p.top_k > 0)) ? 1 : 0;
+    p.yscale = (1.0 / static_cast<double>(a.temperature)) * kY256PerLn2;
     p.top_p = static_cast<double>(a.top_p);
-    p.bscale = static_cast<float>(16.0 / static_cast<double>(a.temperature));
-    p.bscale_c = static_cast<float>(4.0 / static_cast<double>(a.temperature));
-    p.nrows = a.greedy ? a.nt : 2 * a.nt - a.B;
-    p.grid_rows = (p.nrows + 7) / 8 * 8;
+    p.qscale = static_cast<float>(4.0 / static_cast<double>(a.temperature));
+    const int ept = choose_ept(a.nt, a.V, p.filter != 0);
+    const Layout lay = layout_for(ept, a.V);
+    p.nseg = lay.nseg;
+    p.klist = lay.klist;
+    p.grid_units = (a.nt + 7) / 8 * 8;
 
-    const size_t nseg = p.nseg;
-    const size_t nrows_max = static_cast<size_t>(2 * a.nt - a.B);
+    const WsParts w = ws_parts(a.B, a.nt, a.V);
     char* base = static_cast<char*>(a.workspace);
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        off = (off + 255) & ~static_cast<size_t>(255);
-        char* ptr = base + off;
-        off += bytes;
-        return ptr;
-    };
-    // arrival counters first: their place depends on B only (the rows of B
-    // sequences are at most B * kMaxRowsPerSeq), so calls with other draft
-    // lengths or vocabularies never put data over them
-    p.seq_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * sizeof(int)));
-    p.draw_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * sizeof(int)));
-    p.row_cnt = reinterpret_cast<int*>(take(static_cast<size_t>(a.B) * kMaxRowsPerSeq * sizeof(int)));
-    p.seg = reinterpret_cast<SegHead*>(take(nrows_max * nseg * sizeof(SegHead)));
-    p.list = reinterpret_cast<unsigned long long*>(take(nrows_max * nseg * kList * sizeof(unsigned long long)));
-    p.rows = reinterpret_cast<RowRec*>(take(nrows_max * sizeof(RowRec)));
-    p.zx = reinterpret_cast<float*>(take(nrows_max * sizeof(float)));
-    p.seqs = reinterpret_cast<SeqRec*>(take(static_cast<size_t>(a.B) * sizeof(SeqRec)));
-    p.dsum = reinterpret_cast<double*>(take(static_cast<size_t>(a.B) * nseg * sizeof(double)));
-    p.qsum = reinterpret_cast<double*>(take(static_cast<size_t>(a.B) * nseg * sizeof(double)));
+    p.seq_word = reinterpret_cast<unsigned long long*>(base + w.seq_word);
+    p.seq_mask = reinterpret_cast<unsigned long long*>(base + w.seq_mask);
+    p.draw_cnt = reinterpret_cast<int*>(base + w.draw_cnt);
+    p.seg = reinterpret_cast<SegHead*>(base + w.seg);
+    p.list = reinterpret_cast<unsigned long long*>(base + w.list);
+    p.lzp = reinterpret_cast<float*>(base + w.lzp);
+    p.bmass = reinterpret_cast<double*>(base + w.bmass);
+    p.bcnt = reinterpret_cast<int*>(base + w.bcnt);
+    p.rows = reinterpret_cast<RowRec*>(base + w.rows);
+    p.zx = reinterpret_cast<float*>(base + w.zx);
+    p.utok = reinterpret_cast<int*>(base + w.utok);
+    p.seqs = reinterpret_cast<SeqRec*>(base + w.seqs);
+    p.dsum = reinterpret_cast<double*>(base + w.dsum);
+    p.qsum = reinterpret_cast<double*>(base + w.qsum);
 
-    hipLaunchKernelGGL(rows_kernel, dim3(p.grid_rows * p.nseg), dim3(kThreads), 0, stream, p);
+    const dim3 grid(p.grid_units * p.nseg);
+    if (ept == 16)
+        hipLaunchKernelGGL(segment_kernel<16>, grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(segment_kernel<12>, grid, dim3(kThreads), 0, stream, p);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || a.greedy || p.nucleus) return err;
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(merge_kernel, dim3(a.nt), dim3(kMThreads), 0, stream, p);
+    err = hipGetLastError();
+    if (err != hipSuccess || a.greedy || p.filter) return err;
     const int grid_seqs = (a.B + 7) / 8 * 8;
-    hipLaunchKernelGGL(draw_kernel, dim3(grid_seqs * p.nseg), dim3(kThreads), 0, stream, p,
-                       grid_seqs);
+    if (ept == 16)
+        hipLaunchKernelGGL(draw_kernel<16>, dim3(grid_seqs * p.nseg), dim3(kThreads), 0, stream, p, grid_seqs);
+    else
+        hipLaunchKernelGGL(draw_kernel<12>, dim3(grid_seqs * p.nseg), dim3(kThreads), 0, stream, p, grid_seqs);
     return hipGetLastError();
 }
 

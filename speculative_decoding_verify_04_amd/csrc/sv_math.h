@@ -2,14 +2,17 @@
 //
 // Table-driven method of P. T. P. Tang, "Table-driven implementation of the
 // exponential function in IEEE floating-point arithmetic", ACM TOMS 15(2),
-// 1989: write x = (64 k + j) ln2/64 + r with |r| <= ln2/128, then
-//   exp(x) = 2^k * 2^(j/64) * exp(r),
-// with exp(r) from its degree-5 Taylor polynomial (truncation below 4e-17 for
-// |r| <= ln2/128) and the 64 values 2^(j/64) from a table the caller fills
-// with exp2(j/64).  The reduction uses ln2/64 split into a 32-bit head (exact
-// products for |k| < 2^20) and a tail.  Relative error stays below ~1e-15,
-// far inside the 1e-12 decision margins of the sampler; about 14 vector
-// instructions instead of ~40 for the library's general exp.
+// 1989, in base 2 with a 256-entry table: the caller forms
+//   y = (z - m) * (256 / (T ln 2))        (one rounding of a double product)
+// and exp2_256(y) = 2^(y/256) splits y = 256 k + j + t (k, j integers,
+// 0 <= j < 256, |t| <= 1/2, t exact by Sterbenz's lemma):
+//   2^(y/256) = 2^k * 2^(j/256) * exp(t ln2 / 256),
+// with exp(r) - 1 from its degree-4 Taylor polynomial (|r| <= ln2/512, so the
+// truncation stays below 4e-17) and 2^(j/256) from a table the caller fills
+// with exp2(j/256).  Relative error of exp2_256 for an exact y stays below
+// ~3e-16; the rounding of y adds |y| ln2/256 * 2^-53, about 1.1e-16 per unit
+// of |(z - m)/T| -- the same order as forming (z - m)/T in double at all.
+// Both are far inside the 1e-12 decision margins of the sampler.
 //
 // The header compiles for the device (hipcc) and for host-side accuracy tests.
 #pragma once
@@ -23,30 +26,29 @@
 
 namespace sv {
 
-constexpr double kInvLn2x64 = 92.33248261689366;        // 64 / ln 2
-constexpr double kLn2d64Hi = 0.01083042469326756;       // ln2/64, 32 significant bits
-constexpr double kLn2d64Lo = 2.9815858269852933e-12;    // ln2/64 - kLn2d64Hi
+constexpr double kY256PerLn2 = 369.3299304675746;       // 256 / ln 2
+// Taylor coefficients of exp(t * ln2/256) - 1 in powers of t: (ln2/256)^i / i!
+constexpr double kE1 = 2.7076061740622863e-03;
+constexpr double kE2 = 3.6655655969101062e-06;
+constexpr double kE3 = 3.3083026805413713e-09;
+constexpr double kE4 = 2.2393951908751570e-12;
+// Below this y every result rounds to +0 (2^(y/256) < 2^-1075).
+constexpr double kYMin = -1076.0 * 256.0;
 
-// exp(x) for x <= 0 (including -inf); `tab[j]` = 2^(j/64), j = 0..63.
-// Branch-free: arguments at or below -745 (exp underflows), -inf and NaN give 0
-// through a final select, so vector code runs it without divergent branches.
-SV_HD double exp_nonpos(double x_in, const double* tab) {
-    const bool live = x_in > -745.0;
-    const double x = live ? x_in : -745.0;
-    const double kd = rint(x * kInvLn2x64);
-    double r = fma(-kd, kLn2d64Hi, x);
-    r = fma(-kd, kLn2d64Lo, r);
+// 2^(y/256) for y <= 0 (including -inf; NaN gives 0 as well); `tab[j]` =
+// 2^(j/256), j = 0..255.  Branch-free: the clamp at kYMin makes every
+// argument at or below it (and NaN, which fmax drops) come out as +0.
+SV_HD double exp2_256(double y_in, const double* tab) {
+    const double y = fmax(y_in, kYMin);
+    const double kd = rint(y);
+    const double t = y - kd;
+    double p = fma(t, kE4, kE3);
+    p = fma(t, p, kE2);
+    p = fma(t, p, kE1);
+    p = p * t;  // exp(t ln2/256) - 1
     const int k = static_cast<int>(kd);
-    const int j = k & 63;
-    const int e = k >> 6;  // arithmetic shift: floor(k / 64)
-    double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
-    p = fma(r, p, 1.0 / 6.0);
-    p = fma(r, p, 0.5);
-    p = fma(r, p, 1.0);
-    p = p * r;  // exp(r) - 1
-    const double t = tab[j];
-    const double r_ = ldexp(fma(t, p, t), e);
-    return live ? r_ : 0.0;
+    const double b = tab[k & 255];
+    return ldexp(fma(b, p, b), k >> 8);  // arithmetic shift: floor(k / 256)
 }
 
 }  // namespace sv

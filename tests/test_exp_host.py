@@ -2,8 +2,12 @@
 
 The same header the gfx950 kernels include is compiled for the host with g++
 and compared against the C library's long-double expl over the whole argument
-range the sampler uses (x <= 0).  The sampler's decision margins are 1e-12
-relative; the bound checked here is 2e-15.
+range the sampler uses (exponents <= 0), and the composite weight
+exp((z - m)/T) as the kernels form it from fp32 logits against the exact
+quotient.  The sampler's decision margins are 1e-12 relative; the bounds
+checked here are 1e-15 for exact arguments and 1e-15 + 3.5e-16 |x| for the
+composite (x = (z - m)/T with |z - m| <= 60 and 0.05 <= T <= 2.05; the
+|x| term is the rounding of the scaled argument).
 """
 import os
 import subprocess
@@ -17,35 +21,54 @@ PROG = r"""
 #include <cstdlib>
 #include "sv_math.h"
 int main() {
-    double tab[64];
-    for (int j = 0; j < 64; ++j) tab[j] = std::exp2(j / 64.0);
-    double worst = 0.0, worst_x = 0.0;
+    double tab[256];
+    for (int j = 0; j < 256; ++j) tab[j] = std::exp2(j / 256.0);
+    double worst = 0.0, worst_y = 0.0, worst_c = 0.0, worst_x = 0.0;
     unsigned long long s = 88172645463325252ull;
-    for (long i = 0; i < 4000000; ++i) {
+    auto next = [&]() {
         s ^= s << 13; s ^= s >> 7; s ^= s << 17;
-        double u = (s >> 11) * (1.0 / 9007199254740992.0);
-        double x = (i & 1) ? -745.0 * u : -40.0 * u * u;   // dense near 0 too
-        long double ref = expl((long double)x);
-        double got = sv::exp_nonpos(x, tab);
-        if (ref == 0.0L) { if (got != 0.0) { printf("FAIL nonzero %g\n", x); return 1; } continue; }
-        if (ref < 2.2250738585072014e-308L) continue;            // subnormal results
-        double rel = (double)fabsl(((long double)got - ref) / ref);
-        if (rel > worst) { worst = rel; worst_x = x; }
+        return (s >> 11) * (1.0 / 9007199254740992.0);
+    };
+    // exp2_256 for exact arguments over the whole range the sampler uses
+    for (long i = 0; i < 4000000; ++i) {
+        const double u = next();
+        const double y = (i & 1) ? -745.0 * sv::kY256PerLn2 * u : -40.0 * sv::kY256PerLn2 * u * u;
+        const long double ref = exp2l((long double)y / 256.0L);
+        const double got = sv::exp2_256(y, tab);
+        if (ref < 2.2250738585072014e-308L) continue;            // subnormal or zero results
+        const double rel = (double)fabsl(((long double)got - ref) / ref);
+        if (rel > worst) { worst = rel; worst_y = y; }
     }
-    if (sv::exp_nonpos(0.0, tab) != 1.0) { printf("FAIL exp(0)\n"); return 1; }
-    if (sv::exp_nonpos(-INFINITY, tab) != 0.0) { printf("FAIL exp(-inf)\n"); return 1; }
-    if (sv::exp_nonpos(-800.0, tab) != 0.0) { printf("FAIL underflow\n"); return 1; }
-    printf("%.3e %.17g\n", worst, worst_x);
+    // the composite weight exp((z - m)/T) from fp32 logits, as the kernels form it
+    for (long i = 0; i < 2000000; ++i) {
+        const float m = (float)(40.0 * next() - 20.0);
+        const float z = (float)(m - 60.0 * next());
+        const double T = 0.05 + 2.0 * next();
+        const double c = (1.0 / T) * sv::kY256PerLn2;
+        const double got = sv::exp2_256(((double)z - (double)m) * c, tab);
+        const long double x = ((long double)z - (long double)m) / (long double)T;
+        const long double ref = expl(x);
+        if (ref < 2.2250738585072014e-308L) continue;
+        const double rel = (double)fabsl(((long double)got - ref) / ref);
+        const double bound = 1e-15 + 3.5e-16 * (double)fabsl(x);
+        if (rel / bound > worst_c) { worst_c = rel / bound; worst_x = (double)x; }
+    }
+    if (sv::exp2_256(0.0, tab) != 1.0) { printf("FAIL exp(0)\n"); return 1; }
+    if (sv::exp2_256(-INFINITY, tab) != 0.0) { printf("FAIL exp(-inf)\n"); return 1; }
+    if (sv::exp2_256(NAN, tab) != 0.0) { printf("FAIL nan\n"); return 1; }
+    if (sv::exp2_256(-800.0 * sv::kY256PerLn2, tab) != 0.0) { printf("FAIL underflow\n"); return 1; }
+    printf("%.3e %.17g %.3e %.6g\n", worst, worst_y, worst_c, worst_x);
     return 0;
 }
 """
 
 
-def test_exp_nonpos_accuracy(tmp_path):
+def test_exp2_256_accuracy(tmp_path):
     src = tmp_path / "t.cpp"
     src.write_text(PROG)
     exe = tmp_path / "t"
     subprocess.check_call(["g++", "-O2", "-std=c++17", f"-I{HDR}", str(src), "-o", str(exe)])
     out = subprocess.check_output([str(exe)], text=True).split()
-    worst = float(out[0])
-    assert worst < 2e-15, out
+    worst, worst_composite = float(out[0]), float(out[2])
+    assert worst < 1e-15, out
+    assert worst_composite < 1.0, out
