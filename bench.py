@@ -5,14 +5,19 @@ One step = spec_verify_attn + spec_accept + spec_compact_kv over one batch of
 the workload (default: B=8 sequences, K=5 drafts, 32 heads x D128, ragged KV
 lengths U{512..2048}, V=49152, bf16 KV, fp32 logits, T=0.8, nucleus 0.95).
 
-Inputs are synthetic and seeded; `--sets` input sets (default 6, ~1.1 GB) are
-resident in HBM before timing and the steps rotate through them, so the 256 MB
-Infinity Cache cannot serve a step from the previous use of its inputs.  The
-timed steps are captured into one HIP graph (the per-step host work of the
+Inputs are synthetic and seeded; `--sets` input sets (default 16, ~4.5 GB on
+the default workload) are resident in HBM before timing and the steps rotate
+through them, so the 256 MB Infinity Cache cannot serve a step from the
+previous use of its inputs.  The `--warmup` steps and the `--steps` timed
+steps are each captured into one HIP graph (the per-step host work of the
 ctypes binding would otherwise exceed the GPU time); the timed region is one
-replay between two device synchronisations.  The dominant kernel's duration is
-then measured with HIP events stamped by its own dispatch, over the same
-rotation of sets.
+replay between two device synchronisations.  The distribution of one step's
+time (median, p10, p90) comes from `--steps` further steps launched eagerly
+with an event after each (a graph per step would add ~10 us of launch per
+step; the eager launches stay ahead of the GPU).  Each entry point alone is
+timed both ways: one graph of `--steps` calls (mean) and eager calls with
+events (distribution).  The dominant kernel's duration is then measured with
+HIP events stamped by its own dispatch, over the same rotation of sets.
 
 Compaction appends each set's accepted KV rows, so a set's KV grows by its
 emitted tokens on every use, as in real decoding; the byte counts follow the
@@ -39,10 +44,10 @@ METRIC = "verified tokens/sec per verify step (B=8,K=5 ragged); % of HBM peak GB
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=60)
-    ap.add_argument("--warmup", type=int, default=12)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="bass_b8k5")
-    ap.add_argument("--sets", type=int, default=6, help="rotating input sets resident in HBM")
+    ap.add_argument("--sets", type=int, default=16, help="rotating input sets resident in HBM")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0: skip)")
     ap.add_argument("--traffic-json", default=None,
@@ -199,27 +204,34 @@ def main():
         return
 
     import numpy as np
-    import torch
 
-    from speculative_decoding_verify_04_amd import api
     from speculative_decoding_verify_04_amd import workloads as W
-    from speculative_decoding_verify_04_amd.devio import to_device
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
     cfg = W.CONFIGS[args.config]
     B, K = cfg.B, cfg.K
     S = args.sets
     steps, warmup = args.steps, args.warmup
-    uses_max = math.ceil((steps + warmup) / S) + 1
+    # uses of a set by compacting calls: warm-up, timed and eager steps, and
+    # 2 S compactions alone in each of the two timings
+    n_comp = 2 * S
+    uses_max = math.ceil((warmup + 2 * steps) / S) + 2 * math.ceil(n_comp / S) + 1
     growth = (K + 1) * (uses_max + 1)
 
+    # the sets are generated before anything touches the GPU, in worker processes
     t_gen = time.perf_counter()
-    sets = [W.make_workload(cfg, sub_seed=s, growth_rows=growth) for s in range(S)]
+    sets = generate_sets(cfg, S, growth)
+    print(f"# generated {S} input sets in {time.perf_counter() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+
+    import torch
+
+    from speculative_decoding_verify_04_amd import api
+    from speculative_decoding_verify_04_amd.devio import to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
     dsets = [to_device(w, dev) for w in sets]
     bounds = [[int(x) + growth for x in w.kv_len] for w in sets]
-    print(f"# generated and uploaded {S} input sets in {time.perf_counter() - t_gen:.1f}s",
-          file=sys.stderr, flush=True)
 
     P = cfg.prefix_len
     ws_attn = max(api.spec_verify_attn_workspace_size(B, K, cfg.Hq, cfg.Hkv, cfg.D,
@@ -230,43 +242,51 @@ def main():
     wa = torch.zeros(ws_attn, dtype=torch.uint8, device=dev)
     wacc = torch.zeros(ws_acc, dtype=torch.uint8, device=dev)
 
-    def step(s):
+    def attn(s):
         t = dsets[s]
         api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, bounds[s], t.k_new,
                              t.v_new, t.out, K, k_prefix=t.k_prefix, v_prefix=t.v_prefix,
                              status=t.status, workspace=wa)
-        api.spec_accept(t.target_logits, None if cfg.greedy else t.draft_logits, t.draft_tokens,
-                        t.u_accept, t.u_sample, cfg.temperature, cfg.top_p, cfg.greedy,
-                        t.n_accepted, t.out_tokens, status=t.status, workspace=wacc)
-        api.spec_compact_kv(t.n_accepted, t.out_tokens, t.kv_len, t.kv_start, t.k_cache,
-                            t.v_cache, t.k_new, t.v_new, t.tokens_packed, t.cu_tokens,
-                            status=t.status)
 
-    # Reference tokens of every set (the sampler does not depend on the KV state).
-    ref_n, ref_tok = [], []
-    for s in range(S):
+    def accept(s):
         t = dsets[s]
         api.spec_accept(t.target_logits, None if cfg.greedy else t.draft_logits, t.draft_tokens,
                         t.u_accept, t.u_sample, cfg.temperature, cfg.top_p, cfg.greedy,
                         t.n_accepted, t.out_tokens, status=t.status, workspace=wacc)
+
+    def compact(s):
+        t = dsets[s]
+        api.spec_compact_kv(t.n_accepted, t.out_tokens, t.kv_len, t.kv_start, t.k_cache,
+                            t.v_cache, t.k_new, t.v_new, t.tokens_packed, t.cu_tokens,
+                            status=t.status)
+
+    def step(s):
+        attn(s)
+        accept(s)
+        compact(s)
+
+    # Reference tokens of every set (the sampler does not depend on the KV state).
+    ref_n, ref_tok = [], []
+    for s in range(S):
+        accept(s)
         torch.cuda.synchronize()
-        ref_n.append(t.n_accepted.cpu().numpy().copy())
-        ref_tok.append(t.out_tokens.cpu().numpy().copy())
+        ref_n.append(dsets[s].n_accepted.cpu().numpy().copy())
+        ref_tok.append(dsets[s].out_tokens.cpu().numpy().copy())
     emitted = [int((n + 1).sum()) for n in ref_n]
 
-    # The warm-up steps and the timed steps are each captured into one HIP graph
+    # The warm-up steps and the timed steps are each captured into one graph
     # (step i uses input set i % S); one replay runs them back to back.
     cap_stream = torch.cuda.Stream()
 
-    def capture(n, first):
+    def capture(fn, first, n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap_stream):
             for i in range(first, first + n):
-                step(i % S)
+                fn(i % S)
         return g
 
-    g_warm = capture(warmup, 0) if warmup else None
-    g_timed = capture(steps, warmup)
+    g_warm = capture(step, 0, warmup) if warmup else None
+    g_timed = capture(step, warmup, steps)
     torch.cuda.synchronize()
     uses = [0] * S
     if g_warm is not None:
@@ -286,6 +306,17 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_stop)
     timed_sets = [(warmup + i) % S for i in range(steps)]
+    for s in timed_sets:
+        uses[s] += 1
+    del g_warm, g_timed
+
+    # Check every set's last outputs against its reference (graph replays vs eager).
+    for s in range(S):
+        t = dsets[s]
+        st = int(t.status.item())
+        assert st == 0, f"set {s}: device status {st} ({api.device_error_name(st)})"
+        assert np.array_equal(t.n_accepted.cpu().numpy(), ref_n[s]), f"set {s}: n_accepted"
+        assert np.array_equal(t.out_tokens.cpu().numpy(), ref_tok[s]), f"set {s}: out_tokens"
 
     # Dominant kernel: the split-K chunk kernel of spec_verify_attn, timed with
     # HIP events that its own dispatch stamps at kernel start and end (eager
@@ -296,11 +327,8 @@ def main():
     kern_bytes = []
     for i in range(steps):
         s = timed_sets[i]
-        t = dsets[s]
         api.sv_set_kernel_events(*evs[i])
-        api.spec_verify_attn(t.q, t.k_cache, t.v_cache, t.kv_start, t.kv_len, bounds[s], t.k_new,
-                             t.v_new, t.out, K, k_prefix=t.k_prefix, v_prefix=t.v_prefix,
-                             status=t.status, workspace=wa)
+        attn(s)
     api.sv_set_kernel_events(None, None)
     torch.cuda.synchronize()
 
@@ -317,13 +345,32 @@ def main():
         assert torch.equal(prev, t.out), f"set {s}: attention output differs on a fresh workspace"
         del fresh
 
-    # Check every set's last outputs against its reference (graph replays vs eager).
-    for s in range(S):
-        t = dsets[s]
-        st = int(t.status.item())
-        assert st == 0, f"set {s}: device status {st} ({api.device_error_name(st)})"
-        assert np.array_equal(t.n_accepted.cpu().numpy(), ref_n[s]), f"set {s}: n_accepted"
-        assert np.array_equal(t.out_tokens.cpu().numpy(), ref_tok[s]), f"set {s}: out_tokens"
+    # Each entry point alone over the same rotation, then the per-step
+    # distribution.  Attention and the sampler do not change the KV state;
+    # compaction appends, so the steps and compactions run last, and their
+    # extra uses stay inside the sets' spare rows.
+    rot = [(warmup + i) % S for i in range(steps)]
+    uses_after_timed = list(uses)
+    alone = {}
+    for name, fn, sel in (("spec_verify_attn", attn, rot), ("spec_accept", accept, rot),
+                          ("spec_compact_kv", compact, list(range(n_comp)))):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for s in sel:
+                fn(s % S)
+        torch.cuda.synchronize()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        g.replay()
+        b_.record()
+        torch.cuda.synchronize()
+        graph_us = a_.elapsed_time(b_) * 1e3 / len(sel)
+        del g
+        _, per = eager_timed(fn, [x % S for x in sel])
+        alone[name] = dict(pct(per), graph_mean=round(graph_us, 2))
+    _, per_step = eager_timed(step, rot)
+    for s in rot:
+        uses[s] += 1
 
     # Bytes and tokens of every timed step from the realised lengths.
     es = 2 if cfg.kv_dtype == W.BF16 else 4
@@ -331,6 +378,7 @@ def main():
     R = cfg.rows
     tokens = 0
     step_bytes = 0
+    acc_bytes = 0
     uses = list(use_at_start)
     for i in range(steps):
         s = timed_sets[i]
@@ -338,11 +386,14 @@ def main():
         uses[s] += 1
         b = W.algorithmic_bytes(cfg, L, P)
         step_bytes += b["attn"] + b["accept"]
+        acc_bytes += b["accept"]
         tokens += emitted[s]
-    for i in range(steps):  # the kernel-timing loop ran on the lengths after the timed steps
+    attn_alone_bytes = 0
+    for i in range(steps):  # the kernel timing and the attention alone ran on these lengths
         s = timed_sets[i]
-        L = sets[s].kv_len.astype(np.int64) + uses[s] * (ref_n[s].astype(np.int64) + 1)
+        L = sets[s].kv_len.astype(np.int64) + uses_after_timed[s] * (ref_n[s].astype(np.int64) + 1)
         kern_bytes.append(int(L.sum()) * row_kv + R * row_kv + R * cfg.Hq * cfg.D * es)
+        attn_alone_bytes += W.algorithmic_bytes(cfg, L, P)["attn"]
     kern_ms = [hip.elapsed_ms(*evs[i]) for i in range(steps)]
     kern_ok = all(m is not None and m > 0 for m in kern_ms)
     kern_avg_us = 1e3 * sum(kern_ms) / steps if kern_ok else None
@@ -362,6 +413,8 @@ def main():
 
     ms_step = ms_total / steps
     value = tokens / (ms_total * 1e-3)
+    med_attn = alone["spec_verify_attn"]["graph_mean"] * 1e-6
+    med_acc = alone["spec_accept"]["graph_mean"] * 1e-6
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -383,7 +436,11 @@ def main():
                          + (", greedy" if cfg.greedy else "")),
             "B": B, "K": K, "rotating_input_sets": S,
         },
+        "step_us_eager": pct(per_step),
+        "alone_us": alone,
         "hbm_frac_step": round(step_bytes / (ms_total * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_frac_attn_plus_accept_alone": round(
+            (attn_alone_bytes + acc_bytes) / steps / (med_attn + med_acc) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes_avg": int(step_bytes / steps),
         "verified_tokens_per_step_avg": round(tokens / steps, 3),
         "wall_s_timed": round(wall, 4),
@@ -407,6 +464,52 @@ def main():
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(sets, cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def _make_set(cfg_name, sub_seed, growth):
+    from speculative_decoding_verify_04_amd import workloads as W
+    return W.make_workload(W.CONFIGS[cfg_name], sub_seed=sub_seed, growth_rows=growth)
+
+
+def generate_sets(cfg, n, growth):
+    """The n seeded input sets of a workload, built in worker processes that
+    never touch the GPU (at most 8 at a time)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    workers = max(1, min(8, n, os.cpu_count() or 1))
+    if workers == 1:
+        return [_make_set(cfg.name, s, growth) for s in range(n)]
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        return list(ex.map(_make_set, [cfg.name] * n, range(n), [growth] * n))
+
+
+def eager_timed(fn, sel):
+    """Call fn(s) for s in sel back to back on the current stream with an event
+    after each; returns (first-to-last ms, per-call ms).  A short spin kernel
+    first lets the host queue the calls ahead of the GPU, so the events time
+    GPU work, not launch latency."""
+    import torch
+    n = len(sel)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(2_000_000)
+    evs[0].record()
+    for i, s in enumerate(sel):
+        fn(s)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+    return evs[0].elapsed_time(evs[n]), per
+
+
+def pct(ms_list):
+    """p10 / median / p90 in microseconds of a list of milliseconds."""
+    import numpy as np
+    if not ms_list:
+        return None
+    v = np.percentile(np.asarray(ms_list) * 1e3, [10, 50, 90])
+    return {"p10": round(float(v[0]), 2), "median": round(float(v[1]), 2),
+            "p90": round(float(v[2]), 2), "n": len(ms_list)}
 
 
 def k_sweep(args, ks):
