@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the batched speculative-sampling verify step on one MI355X.
 
-One step = spec_verify_attn + spec_accept + spec_compact_kv over one batch of
-the workload (default: B=8 sequences, K=5 drafts, 32 heads x D128, ragged KV
+One step = spec_verify_attn + spec_accept_compact (the sampler with the
+padding-free compaction in its own kernels) over one batch of the workload (default: B=8 sequences, K=5 drafts, 32 heads x D128, ragged KV
 lengths U{512..2048}, V=49152, bf16 KV, fp32 logits, T=0.8, nucleus 0.95).
 
 Inputs are synthetic and seeded; `--sets` input sets (default 16, ~4.5 GB on
@@ -212,9 +212,9 @@ def main():
     S = args.sets
     steps, warmup = args.steps, args.warmup
     # uses of a set by compacting calls: warm-up, timed and eager steps, and
-    # 2 S compactions alone in each of the two timings
+    # 2 S calls alone of each compacting entry point in each of the two timings
     n_comp = 2 * S
-    uses_max = math.ceil((warmup + 2 * steps) / S) + 2 * math.ceil(n_comp / S) + 1
+    uses_max = math.ceil((warmup + 2 * steps) / S) + 4 * math.ceil(n_comp / S) + 1
     growth = (K + 1) * (uses_max + 1)
 
     # the sets are generated before anything touches the GPU, in worker processes
@@ -260,10 +260,17 @@ def main():
                             t.v_cache, t.k_new, t.v_new, t.tokens_packed, t.cu_tokens,
                             status=t.status)
 
+    def accept_compact(s):
+        t = dsets[s]
+        api.spec_accept_compact(t.target_logits, None if cfg.greedy else t.draft_logits,
+                                t.draft_tokens, t.u_accept, t.u_sample, cfg.temperature,
+                                cfg.top_p, cfg.greedy, t.n_accepted, t.out_tokens, t.kv_len,
+                                t.kv_start, t.k_cache, t.v_cache, t.k_new, t.v_new,
+                                t.tokens_packed, t.cu_tokens, status=t.status, workspace=wacc)
+
     def step(s):
         attn(s)
-        accept(s)
-        compact(s)
+        accept_compact(s)
 
     # Reference tokens of every set (the sampler does not depend on the KV state).
     ref_n, ref_tok = [], []
@@ -353,7 +360,8 @@ def main():
     uses_after_timed = list(uses)
     alone = {}
     for name, fn, sel in (("spec_verify_attn", attn, rot), ("spec_accept", accept, rot),
-                          ("spec_compact_kv", compact, list(range(n_comp)))):
+                          ("spec_compact_kv", compact, list(range(n_comp))),
+                          ("spec_accept_compact", accept_compact, list(range(n_comp)))):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap_stream):
             for s in sel:

@@ -287,6 +287,34 @@ int spec_accept_ex(const void* target_logits, const void* draft_logits, int logi
                    int32_t* out_tokens, int32_t* status, void* workspace,
                    size_t workspace_bytes, sv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * spec_accept_compact -- spec_accept_ex and spec_compact_kv in one call.
+ *
+ * [SpS] "Modified rejection sampling" followed by [EMS]'s padding-free
+ * compaction, with the compaction done by the sampler's own kernels: the
+ * workgroup that makes a sequence's tokens final appends its accepted KV rows
+ * and advances its kv_len, and the last sequence to finish writes cu_tokens
+ * and tokens_packed.  No compaction launch, no round trip through n_accepted.
+ * Every output equals that of spec_accept_ex followed by spec_compact_kv
+ * (uniform: cu_q = cu_q_host = NULL) or spec_compact_kv_ragged (ragged) on the
+ * same arguments; the sampler arguments and the workspace are those of
+ * spec_accept_ex (its workspace size functions cover this call), the
+ * compaction arguments those of spec_compact_kv with kv_dtype its dtype.  The
+ * sampler's tokens are always valid counts, so status never takes
+ * SV_DEV_BAD_COUNT here.  The workspace's counters are zero on entry (a
+ * zero-filled workspace before the first call) and every completed call leaves
+ * them at zero.
+ * ------------------------------------------------------------------------ */
+int spec_accept_compact(const void* target_logits, const void* draft_logits, int logits_dtype,
+                        const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                        const int32_t* cu_q, const int32_t* cu_q_host, int B, int K, int V,
+                        float temperature, float top_p, int top_k, int greedy,
+                        int32_t* n_accepted, int32_t* out_tokens, int32_t* kv_len,
+                        const int64_t* kv_start, void* k_cache, void* v_cache, const void* k_new,
+                        const void* v_new, int Hkv, int D, int kv_dtype, int32_t* tokens_packed,
+                        int32_t* cu_tokens, int32_t* status, void* workspace,
+                        size_t workspace_bytes, sv_stream_t stream);
+
 int spec_compact_kv_ragged(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
                            const int64_t* kv_start, void* k_cache, void* v_cache,
                            const void* k_new, const void* v_new, int32_t* tokens_packed,

@@ -67,13 +67,16 @@ def lib():
         h.spec_accept_ex.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32,
                                      ctypes.c_float, ctypes.c_float, i32, i32, vp, vp, vp, vp, sz,
                                      vp]
+        h.spec_accept_compact.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                          ctypes.c_float, ctypes.c_float, i32, i32, vp, vp, vp, vp,
+                                          vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         h.sv_set_kernel_events.argtypes = [vp, vp]
         for f in ("sv_set_kernel_events", "spec_verify_attn_workspace_size", "spec_verify_attn",
                   "spec_verify_attn_noalloc",
                   "spec_accept_workspace_size", "spec_accept", "spec_compact_kv",
                   "spec_verify_attn_ragged_workspace_size", "spec_verify_attn_ragged",
                   "spec_accept_ragged_workspace_size", "spec_accept_ragged",
-                  "spec_compact_kv_ragged", "spec_accept_ex"):
+                  "spec_compact_kv_ragged", "spec_accept_ex", "spec_accept_compact"):
             getattr(h, f).restype = i32
         _lib = h
     return _lib
@@ -386,6 +389,56 @@ def spec_compact_kv_ragged(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_
         _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(tokens_packed), _ptr(cu_tokens), _ptr(cu_q),
         B, Hkv, D, _kv_dtype(k_cache), _ptr(status), _stream(k_cache)))
     return tokens_packed, cu_tokens
+
+
+def spec_accept_compact(target_logits, draft_logits, draft_tokens, u_accept, u_sample, temperature,
+                        top_p, greedy, n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache,
+                        k_new, v_new, tokens_packed, cu_tokens, status=None, workspace=None,
+                        top_k=0, cu_q=None, cu_q_host=None):
+    """spec_accept (or spec_accept_ragged with ``cu_q``/``cu_q_host``) and
+    spec_compact_kv in one call: the sampler's kernels also append the accepted
+    KV rows, advance ``kv_len`` and write ``tokens_packed`` and ``cu_tokens``.
+    The tensors and their layouts are those of the two separate calls."""
+    ragged = cu_q is not None
+    B = n_accepted.shape[0]
+    _, Hkv, D = k_cache.shape
+    dt = _kv_dtype(target_logits)
+    if ragged:
+        hc = _cu_host(cu_q_host, B)
+        NT, V = target_logits.shape
+        _need(NT == hc[B], "target rows must be cu_q[B]")
+        _need(cu_q.dtype == torch.int32 and cu_q.shape == (B + 1,), "cu_q [B+1] int32")
+        _need(out_tokens.shape == (NT,) and out_tokens.dtype == torch.int32, "out_tokens [cu_q[B]]")
+        K = 0
+        R = NT
+        need = spec_accept_ragged_workspace_size(B, hc, V)
+        cu_dev, cu_host = _ptr(cu_q), _host_i32(hc)
+    else:
+        _, K1, V = target_logits.shape
+        K = K1 - 1
+        R = B * K1
+        _need(out_tokens.shape == (B, K1) and out_tokens.dtype == torch.int32, "out_tokens")
+        need = spec_accept_workspace_size(B, K, V)
+        cu_dev, cu_host = None, None
+    if not greedy:
+        _need(draft_logits is not None, "draft logits are required unless greedy")
+    _need(n_accepted.shape == (B,) and n_accepted.dtype == torch.int32, "n_accepted [B] int32")
+    _need(kv_len.shape == (B,) and kv_len.dtype == torch.int32, "kv_len [B] int32")
+    _need(kv_start.shape == (B,) and kv_start.dtype == torch.int64, "kv_start [B] int64")
+    _need(k_new.shape == (R, Hkv, D) and v_new.shape == k_new.shape, "new K/V rows")
+    _need(tokens_packed.numel() >= R and cu_tokens.numel() == B + 1, "outputs")
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=target_logits.device)
+    _need(workspace.numel() >= need, f"workspace needs {need} bytes")
+    _check(lib().spec_accept_compact(
+        _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
+        _ptr(u_accept) if not greedy else None, _ptr(u_sample) if not greedy else None,
+        cu_dev, cu_host, B, K, V, float(temperature), float(top_p), int(top_k),
+        int(bool(greedy)), _ptr(n_accepted), _ptr(out_tokens), _ptr(kv_len), _ptr(kv_start),
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), Hkv, D, _kv_dtype(k_cache),
+        _ptr(tokens_packed), _ptr(cu_tokens), _ptr(status), _ptr(workspace), workspace.numel(),
+        _stream(target_logits)))
+    return n_accepted, out_tokens
 
 
 def sv_set_kernel_events(start: Optional[int], stop: Optional[int]) -> None:

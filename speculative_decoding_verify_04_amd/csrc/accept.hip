@@ -114,6 +114,19 @@ struct AcceptParams {
     unsigned long long* seq_word;  // [B]: arrivals (top bits) and rejection bits
     unsigned long long* seq_mask;  // [B]: rejection bits of sequences with K_b > kMaskBits
     int* draw_cnt;             // [B]
+    // compaction fused into the call (spec_accept_compact; compact = 0: off)
+    int32_t* kv_len;           // [B] in/out
+    const int64_t* kv_start;   // [B]
+    char* k_cache;             // [rows][row_bytes] in/out
+    char* v_cache;
+    const char* k_new;         // [nt][row_bytes]
+    const char* v_new;
+    int32_t* tokens_packed;    // [nt]
+    int32_t* cu_tokens;        // [B+1]
+    int* cmp_e;                // [B] workspace: tokens emitted per sequence
+    int* cmp_cnt;              // workspace: sequences compacted so far (zero between calls)
+    long long row_bytes;       // one KV row (Hkv * D * element size)
+    int compact;
     const int32_t* cu_q;       // [B+1] ragged draft lengths: target rows of b start at cu_q[b]
     int nt;                    // target rows (cu_q[B], or B*(K+1)); draft row d is row nt + d
     int B, K, V, nseg, klist, grid_units;
@@ -328,6 +341,8 @@ struct MergeLds {
     double kept;
     int tok, lastpos, fstar;
     int seqn;                       // accepted drafts of the sequence (-1: not the last unit)
+    int cflag;                      // compaction: this sequence arrived last
+    int cscan[kMThreads / 64];      // compaction: per-wave scan totals
     int acc;                        // the unit's draft was accepted
     float us;                       // u_sample of the sequence
     float ua;                       // u_accept of the unit
@@ -995,6 +1010,88 @@ __device__ __noinline__ int draw_full_row(FullRow p, DrawRows R, bool residual, 
 
 // ---------------------------------------------------------------- sequence
 
+// Padding-free compaction fused into the sampler ("EMS-SD: Efficient
+// Multi-sample Speculative Decoding", abstract: samples that accept different
+// numbers of tokens are handled without padding).  Called by every thread of
+// the workgroup that has just made sequence b's tokens final (n accepted
+// drafts, out_tokens written with coherent stores): it appends the new KV rows
+// q0 .. q0+n after the sequence's cache rows, advances kv_len[b] by e = n + 1
+// and counts the sequence in; the last sequence to arrive writes cu_tokens
+// (exclusive scan of e) and packs every sequence's e emitted tokens.  The same
+// results as spec_compact_kv after the sampler.
+template <int NT>
+__device__ void compact_sequence(const AcceptParams& p, int b, int q0, int n, int* flag, int* scan) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int e = n + 1;
+    const int L = p.kv_len[b];
+    const long long start = p.kv_start[b];
+    __syncthreads();  // every thread has read kv_len[b]
+    if (tid == 0) {
+        p.kv_len[b] = L + e;
+        st_coh(p.cmp_e + b, e);
+    }
+    // arrive before the row copy: the packing needs the tokens and counts of
+    // every sequence, not the copied rows (those are read by later launches)
+    const bool last = arrive_last(p.cmp_cnt, p.B, flag);
+    const size_t rb = static_cast<size_t>(p.row_bytes);
+    const size_t dst0 = static_cast<size_t>(start + L) * rb, src0 = static_cast<size_t>(q0) * rb;
+    const size_t nbytes = static_cast<size_t>(e) * rb;
+    if (rb % 16 == 0) {
+        const uint4* ks = reinterpret_cast<const uint4*>(p.k_new + src0);
+        const uint4* vs = reinterpret_cast<const uint4*>(p.v_new + src0);
+        uint4* kd = reinterpret_cast<uint4*>(p.k_cache + dst0);
+        uint4* vd = reinterpret_cast<uint4*>(p.v_cache + dst0);
+        for (size_t i = tid; i < nbytes / 16; i += NT) {
+            const uint4 kv = ks[i], vv = vs[i];
+            kd[i] = kv;
+            vd[i] = vv;
+        }
+    } else {
+        const uint32_t* ks = reinterpret_cast<const uint32_t*>(p.k_new + src0);
+        const uint32_t* vs = reinterpret_cast<const uint32_t*>(p.v_new + src0);
+        uint32_t* kd = reinterpret_cast<uint32_t*>(p.k_cache + dst0);
+        uint32_t* vd = reinterpret_cast<uint32_t*>(p.v_cache + dst0);
+        for (size_t i = tid; i < nbytes / 4; i += NT) {
+            const uint32_t kv = ks[i], vv = vs[i];
+            kd[i] = kv;
+            vd[i] = vv;
+        }
+    }
+    if (!last) return;
+    // ---- the last sequence: thread t takes the sequences [t per, (t+1) per)
+    const int per = (p.B + NT - 1) / NT;
+    const int b0 = min(p.B, tid * per), b1 = min(p.B, b0 + per);
+    int mine = 0;
+    for (int bb = b0; bb < b1; ++bb) mine += ld_coh(p.cmp_e + bb);
+    const int inc = wave_incl_scan(mine, lane);
+    if (lane == 63) scan[wv] = inc;
+    __syncthreads();
+    int cu = 0, total = 0;
+#pragma unroll
+    for (int u = 0; u < NT / 64; ++u) {
+        const int t = scan[u];
+        cu += (u < wv) ? t : 0;
+        total += t;
+    }
+    cu += inc - mine;
+    for (int bb = b0; bb < b1; ++bb) {
+        const int eb = ld_coh(p.cmp_e + bb);
+        const int qb = seq_q0(p, bb);
+        p.cu_tokens[bb] = cu;
+        // the tokens eight at a time, their loads issued together
+        for (int i0 = 0; i0 < eb; i0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = (i0 + u < eb) ? ld_coh(p.out_tokens + qb + i0 + u) : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (i0 + u < eb) p.tokens_packed[cu + i0 + u] = v[u];
+        }
+        cu += eb;
+    }
+    if (tid == 0) p.cu_tokens[p.B] = total;
+}
+
 // Arrival of unit j of sequence b (all threads call it).  The units count
 // themselves in seq_word[b] (top bits) and set bit j there when x_j was
 // rejected; the last one to arrive stops at the first rejection n (K_b if
@@ -1037,18 +1134,23 @@ __device__ __forceinline__ void sequence_arrival(const AcceptParams& p, int u, i
     const int n = L.seqn;
     if (n < 0) return;
     if (tid <= kb) {
+        // coherent stores: with the compaction on, another workgroup packs them
+        int v = -1;
+        bool st = true;
         if (tid < n) {
-            p.out_tokens[q0 + tid] = p.draft_tokens[q0 - b + tid];
-        } else if (tid > n) {
-            p.out_tokens[q0 + tid] = -1;
-        } else if (has_tok) {
-            p.out_tokens[q0 + tid] = (n == j) ? token : ld_coh(p.utok + q0 + n);
+            v = p.draft_tokens[q0 - b + tid];
+        } else if (tid == n) {
+            st = has_tok;
+            if (has_tok) v = (n == j) ? token : ld_coh(p.utok + q0 + n);
         }
+        if (st) st_coh(p.out_tokens + q0 + tid, v);
     }
     if (tid == 0) {
         p.n_accepted[b] = n;
         st_coh(&p.seqs[b].n, n);
     }
+    // the draw kernel writes the token at n without a filter: it compacts then
+    if (p.compact && has_tok) compact_sequence<kMThreads>(p, b, q0, n, &L.cflag, L.cscan);
 }
 
 // Row records of the unit's rows and the accept test of x_j (thread 0; every
@@ -1612,6 +1714,8 @@ struct DrawLds {
     double red_d[kThreads / 64];
     double red_d2[kThreads / 64];
     int flag;
+    int cflag;                      // compaction: this sequence arrived last
+    int cscan[kThreads / 64];       // compaction: per-wave scan totals
     RowRec rr[2];
     int n;
     double ds[kMaxSeg];
@@ -1785,8 +1889,9 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
     if (tid == 0) {
         int tok = L.tok != 0x7FFFFFFF ? L.tok : L.last_pos;
         if (tok < 0) tok = 0;
-        p.out_tokens[q0 + n] = tok;
+        st_coh(p.out_tokens + q0 + n, tok);
     }
+    if (p.compact) compact_sequence<kThreads>(p, b, q0, n, &L.cflag, L.cscan);
 }
 
 // ---------------------------------------------------------------- host
@@ -1847,7 +1952,7 @@ int choose_ept(long long units, int V, bool filter) {
 
 // Offsets of the workspace parts (counters first: their place depends on B only).
 struct WsParts {
-    size_t seq_word, seq_mask, draw_cnt, seg, list, lzp, bmass, bcnt, rows, zx, utok, seqs,
+    size_t seq_word, seq_mask, draw_cnt, cmp_cnt, cmp_e, seg, list, lzp, bmass, bcnt, rows, zx, utok, seqs,
         dsum, qsum, end;
 };
 
@@ -1871,6 +1976,8 @@ WsParts ws_parts(int B, long long nt, int V) {
     w.seq_word = take(static_cast<size_t>(B) * sizeof(unsigned long long));
     w.seq_mask = take(static_cast<size_t>(B) * sizeof(unsigned long long));
     w.draw_cnt = take(static_cast<size_t>(B) * sizeof(int));
+    w.cmp_cnt = take(sizeof(int));
+    w.cmp_e = take(static_cast<size_t>(B) * sizeof(int));
     w.seg = take(nrows * nseg * sizeof(SegHead));
     w.list = take(nrows * slots * sizeof(unsigned long long));
     w.lzp = take(static_cast<size_t>(nt) * slots * sizeof(float));
@@ -1927,6 +2034,18 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     p.seq_word = reinterpret_cast<unsigned long long*>(base + w.seq_word);
     p.seq_mask = reinterpret_cast<unsigned long long*>(base + w.seq_mask);
     p.draw_cnt = reinterpret_cast<int*>(base + w.draw_cnt);
+    p.cmp_cnt = reinterpret_cast<int*>(base + w.cmp_cnt);
+    p.cmp_e = reinterpret_cast<int*>(base + w.cmp_e);
+    p.compact = a.kv_len ? 1 : 0;
+    p.kv_len = a.kv_len;
+    p.kv_start = a.kv_start;
+    p.k_cache = static_cast<char*>(a.k_cache);
+    p.v_cache = static_cast<char*>(a.v_cache);
+    p.k_new = static_cast<const char*>(a.k_new);
+    p.v_new = static_cast<const char*>(a.v_new);
+    p.tokens_packed = a.tokens_packed;
+    p.cu_tokens = a.cu_tokens;
+    p.row_bytes = static_cast<long long>(a.row_bytes);
     p.seg = reinterpret_cast<SegHead*>(base + w.seg);
     p.list = reinterpret_cast<unsigned long long*>(base + w.list);
     p.lzp = reinterpret_cast<float*>(base + w.lzp);

@@ -170,7 +170,8 @@ int accept_run(const void* target_logits, const void* draft_logits, int logits_d
                const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
                const int32_t* cu_q, long long nt, int B, int K, int V, float temperature,
                float top_p, int top_k, int greedy, int32_t* n_accepted, int32_t* out_tokens,
-               int32_t* status, void* workspace, size_t workspace_bytes, sv_stream_t stream) {
+               int32_t* status, void* workspace, size_t workspace_bytes, sv_stream_t stream,
+               const sv::AcceptArgs* fused = nullptr) {
     if (V > sv::accept_max_vocab())
         return fail(SV_ERR_UNSUPPORTED, "vocabulary above %d", sv::accept_max_vocab());
     if (logits_dtype != SV_F32 && logits_dtype != SV_BF16)
@@ -218,6 +219,17 @@ int accept_run(const void* target_logits, const void* draft_logits, int logits_d
     a.temperature = temperature;
     a.top_p = top_p;
     a.top_k = top_k;
+    if (fused) {
+        a.kv_len = fused->kv_len;
+        a.kv_start = fused->kv_start;
+        a.k_cache = fused->k_cache;
+        a.v_cache = fused->v_cache;
+        a.k_new = fused->k_new;
+        a.v_new = fused->v_new;
+        a.tokens_packed = fused->tokens_packed;
+        a.cu_tokens = fused->cu_tokens;
+        a.row_bytes = fused->row_bytes;
+    }
     hipError_t e = sv::accept_launch(a, as_stream(stream));
     if (e != hipSuccess) return fail(SV_ERR_HIP, "sampler launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -419,6 +431,51 @@ int spec_compact_kv(const int32_t* n_accepted, const int32_t* out_tokens, int32_
     if (K < 0) return fail(SV_ERR_INVALID_ARG, "need K >= 0");
     return compact_run(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, k_new, v_new,
                        tokens_packed, cu_tokens, nullptr, B, K, Hkv, D, dtype, status, stream);
+}
+
+int spec_accept_compact(const void* target_logits, const void* draft_logits, int logits_dtype,
+                        const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                        const int32_t* cu_q, const int32_t* cu_q_host, int B, int K, int V,
+                        float temperature, float top_p, int top_k, int greedy,
+                        int32_t* n_accepted, int32_t* out_tokens, int32_t* kv_len,
+                        const int64_t* kv_start, void* k_cache, void* v_cache, const void* k_new,
+                        const void* v_new, int Hkv, int D, int kv_dtype, int32_t* tokens_packed,
+                        int32_t* cu_tokens, int32_t* status, void* workspace,
+                        size_t workspace_bytes, sv_stream_t stream) {
+    if (Hkv < 1 || D < 1) return fail(SV_ERR_INVALID_ARG, "need Hkv >= 1, D >= 1");
+    if (kv_dtype != SV_F32 && kv_dtype != SV_BF16)
+        return fail(SV_ERR_INVALID_ARG, "kv_dtype must be SV_F32 or SV_BF16");
+    const int es = kv_dtype == SV_BF16 ? 2 : 4;
+    if ((static_cast<size_t>(Hkv) * D * es) % 4 != 0)
+        return fail(SV_ERR_UNSUPPORTED, "a KV row must be a multiple of 4 bytes");
+    if (B > 0 && (!kv_len || !kv_start || !k_cache || !v_cache || !k_new || !v_new ||
+                  !tokens_packed || !cu_tokens))
+        return fail(SV_ERR_INVALID_ARG, "a required compaction pointer is NULL");
+    sv::AcceptArgs f{};
+    f.kv_len = kv_len;
+    f.kv_start = kv_start;
+    f.k_cache = k_cache;
+    f.v_cache = v_cache;
+    f.k_new = k_new;
+    f.v_new = v_new;
+    f.tokens_packed = tokens_packed;
+    f.cu_tokens = cu_tokens;
+    f.row_bytes = static_cast<size_t>(Hkv) * D * es;
+    if (!cu_q && !cu_q_host) {
+        if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
+        return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept,
+                          u_sample, nullptr, static_cast<long long>(B) * (K + 1), B, K, V,
+                          temperature, top_p, top_k, greedy, n_accepted, out_tokens, status,
+                          workspace, workspace_bytes, stream, &f);
+    }
+    int kmax = 0;
+    int rc = check_cu_q(B, cu_q_host, &kmax);
+    if (rc) return rc;
+    if (!cu_q) return fail(SV_ERR_INVALID_ARG, "cu_q is NULL");
+    if (V < 1) return fail(SV_ERR_INVALID_ARG, "need V >= 1");
+    return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept, u_sample,
+                      cu_q, cu_q_host[B], B, kmax, V, temperature, top_p, top_k, greedy,
+                      n_accepted, out_tokens, status, workspace, workspace_bytes, stream, &f);
 }
 
 int spec_compact_kv_ragged(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,

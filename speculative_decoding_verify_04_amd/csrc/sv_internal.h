@@ -83,6 +83,16 @@ struct AcceptArgs {
     int B, K, V, bf16, greedy;  // K: the largest draft length when ragged
     float temperature, top_p;
     int top_k;            // keep the top_k largest logits (and ties) first; 0: off
+    // the compaction fused into the call (spec_accept_compact); kv_len null: off
+    int32_t* kv_len;
+    const int64_t* kv_start;
+    void* k_cache;
+    void* v_cache;
+    const void* k_new;
+    const void* v_new;
+    int32_t* tokens_packed;
+    int32_t* cu_tokens;
+    size_t row_bytes;     // Hkv * D * element size (a multiple of 4)
 };
 
 // nt: target rows in all (B*(K+1) without ragged draft lengths)

@@ -927,3 +927,112 @@ def test_attention_max_sequences_and_columns():
     w = W.make_workload(cfg, sub_seed=4)
     o = run_attn(w, to_device(w, DEV))
     assert attn_errors(o, R.workload_attn(w)).max() <= 1e-2
+
+
+# ---------------------------------------------------------------- fused compaction
+
+def _fused_case(case):
+    over = dict(B=8, Hq=4, Hkv=4, len_lo=5, len_hi=300, V=4096, K=5)
+    top_k = 0
+    if case == "greedy":
+        over["greedy"] = True
+    elif case == "no_filter":
+        over["top_p"] = 1.0
+    elif case == "k0":
+        over["K"] = 0
+    elif case == "topk":
+        top_k = 20
+    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], **over)
+    return cfg, top_k
+
+
+@pytest.mark.parametrize("case", ["nucleus", "greedy", "no_filter", "topk", "k0", "ragged"])
+def test_accept_compact_matches_two_calls_and_oracle(case):
+    """spec_accept_compact equals spec_accept_ex followed by spec_compact_kv on
+    the same inputs, bit for bit (tokens, counts, KV lengths, caches, packed
+    tokens, offsets), over two rounds on one workspace (its counters must come
+    back to zero); its tokens agree with the oracle and its compaction with the
+    oracle's compaction of those tokens."""
+    cfg, top_k = _fused_case("nucleus" if case == "ragged" else case)
+    growth = 2 * (cfg.K + 1)
+    w = W.make_workload(cfg, sub_seed=40, growth_rows=growth)
+    ragged = case == "ragged"
+    rw = W.make_ragged(w, ragged_lengths(cfg, 40)) if ragged else None
+    say(f"[accept_compact] {case}")
+
+    def dev():
+        return ragged_to_device(rw, DEV) if ragged else to_device(w, DEV)
+
+    g = cfg.greedy
+    ta, tb = dev(), dev()
+    if ragged:
+        wsz = api.spec_accept_ragged_workspace_size(cfg.B, rw.cu_q, cfg.V)
+    else:
+        wsz = api.spec_accept_workspace_size(cfg.B, cfg.K, cfg.V)
+    wa = torch.zeros(wsz, dtype=torch.uint8, device=DEV)
+    wb = torch.zeros(wsz, dtype=torch.uint8, device=DEV)
+    rounds = []
+    for rnd in range(2):
+        for t in (ta, tb):
+            t.status.zero_()
+        # two calls
+        if ragged:
+            api.spec_accept_ragged(ta.target_logits, None if g else ta.draft_logits, ta.draft_tokens,
+                                   ta.u_accept, ta.u_sample, ta.cu_q, ta.cu_q_host, cfg.temperature,
+                                   cfg.top_p, g, ta.n_accepted, ta.out_tokens, status=ta.status,
+                                   workspace=wa, top_k=top_k)
+            api.spec_compact_kv_ragged(ta.n_accepted, ta.out_tokens, ta.kv_len, ta.kv_start,
+                                       ta.k_cache, ta.v_cache, ta.k_new, ta.v_new,
+                                       ta.tokens_packed, ta.cu_tokens, ta.cu_q, status=ta.status)
+        else:
+            api.spec_accept(ta.target_logits, None if g else ta.draft_logits, ta.draft_tokens,
+                            ta.u_accept, ta.u_sample, cfg.temperature, cfg.top_p, g,
+                            ta.n_accepted, ta.out_tokens, status=ta.status, workspace=wa,
+                            top_k=top_k)
+            api.spec_compact_kv(ta.n_accepted, ta.out_tokens, ta.kv_len, ta.kv_start, ta.k_cache,
+                                ta.v_cache, ta.k_new, ta.v_new, ta.tokens_packed, ta.cu_tokens,
+                                status=ta.status)
+        # one call
+        api.spec_accept_compact(tb.target_logits, None if g else tb.draft_logits, tb.draft_tokens,
+                                tb.u_accept, tb.u_sample, cfg.temperature, cfg.top_p, g,
+                                tb.n_accepted, tb.out_tokens, tb.kv_len, tb.kv_start, tb.k_cache,
+                                tb.v_cache, tb.k_new, tb.v_new, tb.tokens_packed, tb.cu_tokens,
+                                status=tb.status, workspace=wb, top_k=top_k,
+                                cu_q=tb.cu_q if ragged else None,
+                                cu_q_host=tb.cu_q_host if ragged else None)
+        torch.cuda.synchronize()
+        assert int(ta.status.item()) == 0 and int(tb.status.item()) == 0
+        for name in ("n_accepted", "out_tokens", "kv_len", "cu_tokens"):
+            assert torch.equal(getattr(ta, name), getattr(tb, name)), (case, rnd, name)
+        cu_end = int(tb.cu_tokens[-1].item())
+        assert torch.equal(ta.tokens_packed[:cu_end], tb.tokens_packed[:cu_end]), (case, rnd)
+        bits = torch.int16 if ta.k_cache.dtype == torch.bfloat16 else torch.int32  # spare rows hold NaN
+        assert torch.equal(ta.k_cache.view(bits), tb.k_cache.view(bits)), (case, rnd)
+        assert torch.equal(ta.v_cache.view(bits), tb.v_cache.view(bits)), (case, rnd)
+        rounds.append((tb.n_accepted.cpu().numpy().copy(), tb.out_tokens.cpu().numpy().copy(),
+                       tb.tokens_packed.cpu().numpy().copy(), tb.cu_tokens.cpu().numpy().copy(),
+                       tb.kv_len.cpu().numpy().copy()))
+    # the oracle: tokens (the same inputs both rounds) and the first round's compaction
+    n, toks = rounds[0][0], rounds[0][1]
+    if ragged:
+        ref = R.accept_ragged(rw.target_logits, None if g else rw.draft_logits, rw.draft_tokens,
+                              rw.u_accept, w.u_sample, rw.cu_q, cfg.temperature, cfg.top_p, g,
+                              top_k=top_k)
+        compare_accept_ragged(n, toks, ref, rw.cu_q,
+                              (rw.target_logits, None if g else rw.draft_logits, rw.draft_tokens,
+                               cfg.temperature, cfg.top_p, top_k))
+        packed, cu, kl, _, _ = R.compact_kv_ragged(n, toks, w.kv_len, w.kv_start, w.k_cache,
+                                                   w.v_cache, rw.k_new, rw.v_new, rw.cu_q,
+                                                   cfg.Hkv, cfg.D)
+    else:
+        ref = R.accept(w.target_logits, None if g else w.draft_logits, w.draft_tokens, w.u_accept,
+                       w.u_sample, cfg.temperature, cfg.top_p, g, top_k=top_k)
+        compare_accept(n, toks, ref, cfg.K, rows_of(w, top_k))
+        packed, cu, kl, _, _ = R.compact_kv(n, toks, w.kv_len, w.kv_start, w.k_cache, w.v_cache,
+                                            w.k_new, w.v_new, cfg.K, cfg.Hkv, cfg.D)
+    assert np.array_equal(rounds[0][3], cu)
+    assert np.array_equal(rounds[0][2][: cu[-1]], packed[: cu[-1]])
+    assert np.array_equal(rounds[0][4], kl)
+    # the second round appended the same tokens' rows again
+    e = (n.astype(np.int64) + 1)
+    assert np.array_equal(rounds[1][4], kl + e)
