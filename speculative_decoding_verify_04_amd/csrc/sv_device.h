@@ -186,6 +186,20 @@ __device__ __forceinline__ T ld_coh(const T* p) {
     return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The relaxed hand-off below relies on gfx950's behaviour of sc1 accesses:
+// coherent stores complete to the device-coherent level before s_waitcnt
+// returns, and coherent loads do not hit stale lines in the reader's L2.  The
+// HIP memory model alone would ask for a release on the counter and an
+// acquire in the last arriver (SV_ARRIVE_RELEASE=1 builds that form; its
+// measured cost is recorded with the design notes).  Other targets are
+// refused at compile time rather than trusted.
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
+#error "arrive_last's relaxed hand-off is argued for gfx950 only"
+#endif
+#ifndef SV_ARRIVE_RELEASE
+#define SV_ARRIVE_RELEASE 0
+#endif
+
 // Called by all threads of a workgroup after its st_coh stores.  Waits until
 // those stores have completed, counts the workgroup in *cnt, and returns true
 // in the workgroup that arrives n-th (which also resets *cnt to 0 for the next
@@ -195,7 +209,11 @@ __device__ __forceinline__ bool arrive_last(int* cnt, int n, int* flag_lds) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
+#if SV_ARRIVE_RELEASE
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+#else
         const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#endif
         const int last = (old == n - 1) ? 1 : 0;
         if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *flag_lds = last;

@@ -529,7 +529,8 @@ def test_two_stream_pipeline_matches_one_stream():
     and compaction on a second stream while batch i+1's attention runs, a
     batch's next attention after its previous compaction), captured into a HIP
     graph, gives bit-identical attention outputs, tokens, packed tokens, KV
-    lengths and caches to the same steps on one stream."""
+    lengths and caches to the same steps on one stream, and both agree with
+    the oracle run through the same schedule."""
     cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=6, Hq=8, Hkv=8, len_lo=20, len_hi=700,
                           V=8192, K=4)
     S, steps = 3, 9
@@ -605,6 +606,37 @@ def test_two_stream_pipeline_matches_one_stream():
         uses = sum(1 for i in range(steps) if i % S == s)
         n = r1[s][0].numpy().astype(np.int64)
         assert np.array_equal(r1[s][4].numpy(), w.kv_len + uses * (n + 1))
+    # The oracle runs the same schedule on the host: every step's attention
+    # over the cache state its batch has reached, the sampler's tokens, and the
+    # compaction of the GPU's tokens into that state; the pipelined run's final
+    # states (bit-identical to the one-stream run above) must equal it.
+    state = [(w.kv_len.copy(), w.k_cache.copy(), w.v_cache.copy()) for w in works]
+    last = [None] * S
+    for i in range(steps):
+        s = i % S
+        w = works[s]
+        kl, kc, vc = state[s]
+        say(f"[two streams] oracle step {i} (batch {s})")
+        ref_o = R.verify_attn(w.q, kc, vc, w.kv_start, kl, w.k_new, w.v_new, cfg.B, cfg.K, cfg.Hq,
+                              cfg.Hkv, cfg.D)
+        got_o = o2[i].float().numpy().astype(np.float64)
+        assert attn_errors(got_o, ref_o).max() <= attn_tol(cfg), (i, s)
+        n_gpu, toks_gpu = r2[s][0].numpy(), r2[s][1].numpy()
+        ref = R.accept(w.target_logits, w.draft_logits, w.draft_tokens, w.u_accept, w.u_sample,
+                       cfg.temperature, cfg.top_p)
+        compare_accept(n_gpu, toks_gpu, ref, cfg.K, rows_of(w))
+        packed, cu, kl2, kc2, vc2 = R.compact_kv(n_gpu, toks_gpu, kl, w.kv_start, kc, vc, w.k_new,
+                                                 w.v_new, cfg.K, cfg.Hkv, cfg.D)
+        state[s] = (kl2, kc2, vc2)
+        last[s] = (packed, cu)
+    for s in range(S):
+        kl, kc, vc = state[s]
+        packed, cu = last[s]
+        assert np.array_equal(r2[s][4].numpy(), kl)
+        assert np.array_equal(r2[s][3].numpy(), cu)
+        assert np.array_equal(r2[s][2].numpy()[: cu[-1]], packed[: cu[-1]])
+        assert np.array_equal(r2[s][5].view(torch.int16).numpy().view(np.uint16), kc.view(np.uint16))
+        assert np.array_equal(r2[s][6].view(torch.int16).numpy().view(np.uint16), vc.view(np.uint16))
 
 
 def test_compaction_rejects_bad_count():
