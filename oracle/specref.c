@@ -463,3 +463,39 @@ int specref_compact_kv(const int32_t *n_accepted, const int32_t *out_tokens,
     }
     return SPECREF_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* LM head and the softmax statistics of its rows ([SpS] "Conditional       */
+/* scoring": the target model scores the K drafts and one more position in   */
+/* one call; its last linear layer turns each row's final hidden state into  */
+/* logits over the vocabulary, and the sampler's first need from every row   */
+/* is its maximum and its normaliser).                                       */
+/*   z[r][v] = sum_h hidden[r][h] * W[v][h]   (W stored [V][H], no bias)     */
+/*   m = max_v z[v],   S = sum_v exp((z[v] - m) / T)                         */
+/* ------------------------------------------------------------------------ */
+
+int specref_lm_head(const void *hidden, const void *weight, int dtype, int rows, int H, int V,
+                    double *logits) {
+    if (rows < 0 || H < 1 || V < 1 || !hidden || !weight || !logits) return 1;
+    for (int r = 0; r < rows; ++r)
+        for (int v = 0; v < V; ++v) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += elem(hidden, dtype, (size_t)r * H + h) * elem(weight, dtype, (size_t)v * H + h);
+            logits[(size_t)r * V + v] = acc;
+        }
+    return 0;
+}
+
+/* Statistics of one row of (fp32) logits: m = max z, S = sum exp((z - m)/T). */
+int specref_row_stats(const float *z, int V, double temperature, double *m, double *S) {
+    if (V < 1 || !z || !m || !S || !(temperature > 0.0)) return 1;
+    double mx = -INFINITY;
+    for (int v = 0; v < V; ++v)
+        if ((double)z[v] > mx) mx = (double)z[v];
+    double sum = 0.0;
+    for (int v = 0; v < V; ++v) sum += exp(((double)z[v] - mx) / temperature);
+    *m = mx;
+    *S = sum;
+    return 0;
+}

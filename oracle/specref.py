@@ -26,6 +26,8 @@ def load(path: str):
     h.specref_accept.restype = ctypes.c_int
     h.specref_compact_kv.restype = ctypes.c_int
     h.specref_row_dist.restype = ctypes.c_int
+    h.specref_lm_head.restype = ctypes.c_int
+    h.specref_row_stats.restype = ctypes.c_int
     return h
 
 
@@ -135,6 +137,40 @@ def row_dist(z, temperature, top_p, top_k=0, lib_=None):
     if rc:
         raise ValueError(f"specref_row_dist failed: {rc}")
     return pi
+
+
+def lm_head(hidden, weight, lib_=None):
+    """LM head: z[r][v] = sum_h hidden[r][h] * weight[v][h] in fp64, from bf16
+    (uint16 bits) or float32 inputs of the same type.  Returns [rows, V] float64."""
+    dt = _kv_dtype(hidden)
+    store = np.uint16 if dt == BF16 else np.float32
+    hd, wt = _c(hidden, store), _c(weight, store)
+    rows, H = hd.shape
+    V, H2 = wt.shape
+    if H2 != H:
+        raise ValueError("hidden [rows, H] and weight [V, H]")
+    out = np.zeros((rows, V), np.float64)
+    rc = lib(lib_).specref_lm_head(_p(hd), _p(wt), dt, rows, H, V, _p(out))
+    if rc:
+        raise ValueError(f"specref_lm_head failed: {rc}")
+    return out
+
+
+def row_stats(z, temperature, lib_=None):
+    """Per row of fp32 logits z [rows, V]: (m, S) with m = max z and
+    S = sum exp((z - m) / T), both float64 [rows]."""
+    zz = _c(z, np.float32)
+    rows, V = zz.shape
+    m = np.zeros(rows, np.float64)
+    S = np.zeros(rows, np.float64)
+    for r in range(rows):
+        mr, sr = ctypes.c_double(0.0), ctypes.c_double(0.0)
+        rc = lib(lib_).specref_row_stats(_p(zz[r]), V, ctypes.c_double(float(temperature)),
+                                         ctypes.byref(mr), ctypes.byref(sr))
+        if rc:
+            raise ValueError(f"specref_row_stats failed: {rc}")
+        m[r], S[r] = mr.value, sr.value
+    return m, S
 
 
 def compact_kv(n_accepted, out_tokens, kv_len, kv_start, k_cache, v_cache, k_new, v_new,

@@ -96,6 +96,23 @@ def _draw_cases(lib_):
     return True
 
 
+def _lm_head(lib_):
+    from test_oracle_pins import lm_head_pin_inputs
+    h, w = lm_head_pin_inputs()
+    ref = h.astype(np.float64) @ w.astype(np.float64).T
+    return np.allclose(R.lm_head(h, w, lib_=lib_), ref, rtol=1e-13, atol=1e-13)
+
+
+def _row_stats(lib_):
+    from scipy import special
+    rng = np.random.default_rng(3)
+    z = (3.0 * rng.standard_normal((2, 800))).astype(np.float32)
+    m, S = R.row_stats(z, 0.5, lib_=lib_)
+    zd = z.astype(np.float64)
+    ref = np.exp(special.logsumexp(zd / 0.5, axis=1) - zd.max(axis=1) / 0.5)
+    return np.allclose(S, ref, rtol=1e-13, atol=0)
+
+
 MUTANTS = {
     "resample_from_q": (
         "tok = draw(mass > 0.0 ? w : q, V, (double)u_sample[b], &amb);",
@@ -135,6 +152,14 @@ MUTANTS = {
         "if (above + group >= top_p || e == V) {",
         "if (above + group > top_p + 0.05 || e == V) {",
         _nucleus_closed_forms),
+    "lm_head_transposed_weight": (
+        "elem(weight, dtype, (size_t)v * H + h);",
+        "elem(weight, dtype, (size_t)h * V + v);",
+        _lm_head),
+    "row_stats_without_temperature": (
+        "for (int v = 0; v < V; ++v) sum += exp(((double)z[v] - mx) / temperature);",
+        "for (int v = 0; v < V; ++v) sum += exp((double)z[v] - mx);",
+        _row_stats),
     "causal_window_short": (
         "int n_keys = a->prefix_len + a->kv_len[b] + j + 1;",
         "int n_keys = a->prefix_len + a->kv_len[b] + (j > 0 ? j : 1);",

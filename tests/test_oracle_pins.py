@@ -492,3 +492,66 @@ def test_topk_kept_set_brute_force():
                 pi /= pi.sum()
                 x = w.draft_tokens[b, j]
                 assert abs(a["q_tok"][b, j] - pi[x]) <= 1e-12 * max(pi[x], 1e-300) + 1e-300
+
+
+# ---------------------------------------------------------------- LM head and row statistics
+#
+# "Accelerating Large Language Model Decoding with Speculative Sampling",
+# "Conditional scoring": the target call's last linear layer turns each
+# row's hidden state into logits; the sampler's first need is every row's
+# maximum and normaliser.
+
+def lm_head_pin_inputs(seed=0, rows=5, H=96, V=37):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((rows, H)).astype(np.float32)
+    w = (0.1 * rng.standard_normal((V, H))).astype(np.float32)
+    return h, w
+
+
+def test_lm_head_against_numpy_matmul():
+    """The oracle's loops against numpy's float64 product of the exactly
+    converted inputs (bf16 bits and float32), on a shape where rows, H and V
+    all differ, so a transposed or swapped operand cannot pass."""
+    h, w = lm_head_pin_inputs()
+    ref = h.astype(np.float64) @ w.astype(np.float64).T
+    assert np.allclose(R.lm_head(h, w), ref, rtol=1e-13, atol=1e-13)
+    hb, wb = W.f32_to_bf16_bits(h), W.f32_to_bf16_bits(w)
+    refb = W.bf16_bits_to_f32(hb).astype(np.float64) @ W.bf16_bits_to_f32(wb).astype(np.float64).T
+    assert np.allclose(R.lm_head(hb, wb), refb, rtol=1e-13, atol=1e-13)
+
+
+def test_lm_head_unit_vectors():
+    """hidden = e_h reads column h of W (every vocabulary row's weight h);
+    a weight matrix of unit rows e_h reads hidden component h."""
+    H, V = 12, 7
+    w = np.arange(V * H, dtype=np.float32).reshape(V, H) / 16.0
+    eye = np.eye(H, dtype=np.float32)
+    z = R.lm_head(eye, w)
+    assert np.array_equal(z, w.T.astype(np.float64))
+    hid = np.arange(3 * H, dtype=np.float32).reshape(3, H) - 5.0
+    sel = np.zeros((V, H), np.float32)
+    for v in range(V):
+        sel[v, (3 * v) % H] = 1.0
+    z = R.lm_head(hid, sel)
+    for v in range(V):
+        assert np.array_equal(z[:, v], hid[:, (3 * v) % H].astype(np.float64))
+
+
+def test_row_stats_against_logsumexp():
+    """m = max z and S = exp(logsumexp(z/T) - m/T) (SciPy) at several
+    temperatures; a constant row gives S = V; one logit far above the rest
+    gives S = 1 to double precision."""
+    rng = np.random.default_rng(3)
+    z = (3.0 * rng.standard_normal((4, 5000))).astype(np.float32)
+    for T in (0.5, 1.0, 2.0):
+        m, S = R.row_stats(z, T)
+        zd = z.astype(np.float64)
+        assert np.array_equal(m, zd.max(axis=1))
+        ref = np.exp(special.logsumexp(zd / T, axis=1) - zd.max(axis=1) / T)
+        assert np.allclose(S, ref, rtol=1e-13, atol=0)
+    m, S = R.row_stats(np.full((1, 321), 2.5, np.float32), 0.8)
+    assert m[0] == 2.5 and S[0] == 321.0
+    spike = np.full((1, 100), -1000.0, np.float32)
+    spike[0, 17] = 40.0
+    m, S = R.row_stats(spike, 1.0)
+    assert m[0] == 40.0 and S[0] == 1.0
