@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--overlap", action="store_true",
                     help="two-stage pipeline over independent batches: the sampler and compaction "
                          "of batch i on a second stream while batch i+1's attention runs")
+    ap.add_argument("--lm-head", action="store_true",
+                    help="the target LM head with row statistics (spec_lm_head_stats) and the "
+                         "sampler that takes them (spec_accept_prestats), against the sampler "
+                         "alone (one JSON line per shape)")
     ap.add_argument("--ragged", action="store_true",
                     help="time the step with ragged draft lengths K_b ~ U{0..K} (one JSON line)")
     ap.add_argument("--traffic-from", default=None,
@@ -201,6 +205,9 @@ def main():
         return
     if args.sampler_variants:
         sampler_variants(args)
+        return
+    if args.lm_head:
+        lm_head_bench(args)
         return
 
     import numpy as np
@@ -899,6 +906,150 @@ def sampler_variants(args):
                           "accept_us": round(us, 2), "logit_bytes": nbytes,
                           "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}), flush=True)
         del ds, wacc
+        torch.cuda.empty_cache()
+
+
+def lm_head_bench(args):
+    """Target LM head (hidden [rows, H] x weight [V, H]^T, bf16 in, fp32 logits)
+    with per-part row statistics, then the sampler without a filter, either
+    from the logits alone (spec_accept: a statistics pass over every row, then
+    the merge and draws) or with the LM head's statistics (spec_accept_prestats:
+    no statistics pass).  Synthetic weights of std sigma/sqrt(H) give target
+    logits of std sigma; the draft rows use weight a*W + W_noise (the workload's
+    draft = a*target + N(0, s^2)) on the same hidden states; draft tokens are
+    drawn from the draft softmax.  Shapes: the B=8, K=5 workload (H = 32*128,
+    V = 49152, here without its nucleus) and the B=64, K=8 GQA workload
+    (V = 128256, no filter).  Each entry point: a graph of `steps` calls over
+    two rotating weight/input sets; hipBLASLt's bf16 GEMM of the same shape
+    (bf16 output) is timed beside the LM head for context."""
+    import torch
+
+    from speculative_decoding_verify_04_amd import api
+    from speculative_decoding_verify_04_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    steps, S = args.steps, 2
+    cap_stream = torch.cuda.Stream()
+    for cname in ("bass_b8k5", "gqa_b64k8"):
+        cfg = W.CONFIGS[cname]
+        B, K, V, T = cfg.B, cfg.K, cfg.V, cfg.temperature
+        H = cfg.Hq * cfg.D
+        nt, nd = B * (K + 1), B * K
+        P = api.spec_lm_head_parts(V)
+        g = torch.Generator(device=dev)
+        g.manual_seed(cfg.seed)
+        sets = []
+        for s in range(S):
+            hid = torch.randn((nt, H), generator=g, device=dev).to(torch.bfloat16)
+            wt = (torch.randn((V, H), generator=g, device=dev) * (cfg.target_sigma / math.sqrt(H)))
+            wd = (cfg.draft_a * wt + torch.randn((V, H), generator=g, device=dev)
+                  * (cfg.draft_sigma / math.sqrt(H))).to(torch.bfloat16)
+            wt = wt.to(torch.bfloat16)
+            hd = hid.view(B, K + 1, H)[:, :K].reshape(nd, H).contiguous()
+            d = {"hid": hid, "wt": wt,
+                 "zt": torch.empty((nt, V), dtype=torch.float32, device=dev),
+                 "pmt": torch.empty((nt, P), dtype=torch.float32, device=dev),
+                 "pst": torch.empty((nt, P), dtype=torch.float64, device=dev),
+                 "zd": torch.empty((nd, V), dtype=torch.float32, device=dev),
+                 "pmd": torch.empty((nd, P), dtype=torch.float32, device=dev),
+                 "psd": torch.empty((nd, P), dtype=torch.float64, device=dev),
+                 "zb": torch.empty((nt, V), dtype=torch.bfloat16, device=dev),
+                 "ua": (torch.randint(0, 1 << 24, (B, K), generator=g, device=dev)
+                        .to(torch.float32) * 2.0 ** -24),
+                 "us": (torch.randint(0, 1 << 24, (B,), generator=g, device=dev)
+                        .to(torch.float32) * 2.0 ** -24),
+                 "n": torch.zeros(B, dtype=torch.int32, device=dev),
+                 "toks": torch.zeros((B, K + 1), dtype=torch.int32, device=dev),
+                 "status": torch.zeros(1, dtype=torch.int32, device=dev)}
+            # draft rows: the draft model's logits and statistics (computed
+            # before the verify step; not timed)
+            api.spec_lm_head_stats(hd, wd, T, d["zd"], d["pmd"], d["psd"])
+            gum = -torch.log(-torch.log(torch.rand((nd, V), generator=g, device=dev)
+                                        .clamp_(1e-30, 1.0 - 1e-7)))
+            d["drafts"] = torch.argmax(d["zd"] / T + gum, dim=-1).to(torch.int32).view(B, K)
+            del wd, gum
+            api.spec_lm_head_stats(hid, wt, T, d["zt"], d["pmt"], d["pst"])
+            sets.append(d)
+        torch.cuda.synchronize()
+        wacc = torch.zeros(api.spec_accept_workspace_size(B, K, V), dtype=torch.uint8, device=dev)
+
+        def lm(s):
+            d = sets[s]
+            api.spec_lm_head_stats(d["hid"], d["wt"], T, d["zt"], d["pmt"], d["pst"])
+
+        def blas(s):
+            d = sets[s]
+            torch.mm(d["hid"], d["wt"].t(), out=d["zb"])
+
+        def acc(s):
+            d = sets[s]
+            api.spec_accept(d["zt"].view(B, K + 1, V), d["zd"].view(B, K, V), d["drafts"], d["ua"],
+                            d["us"], T, 1.0, False, d["n"], d["toks"], status=d["status"],
+                            workspace=wacc)
+
+        def accp(s):
+            d = sets[s]
+            api.spec_accept_prestats(d["zt"].view(B, K + 1, V), d["zd"].view(B, K, V),
+                                     d["drafts"], d["ua"], d["us"], T, 1.0, False, d["n"],
+                                     d["toks"], d["pmt"], d["pst"], d["pmd"], d["psd"],
+                                     status=d["status"], workspace=wacc)
+
+        def graph_us(fn):
+            fn(0)  # library handles and workspaces are created outside the capture
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=cap_stream):
+                for i in range(steps):
+                    fn(i % S)
+            torch.cuda.synchronize()
+            gr.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            del gr
+            return a.elapsed_time(b) * 1e3 / steps
+
+        # parity of the two sampler forms on these inputs (the same tokens
+        # except where a decision is within rounding: none expected here)
+        acc(0)
+        n0, t0 = sets[0]["n"].clone(), sets[0]["toks"].clone()
+        accp(0)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(n0, sets[0]["n"]) and torch.equal(t0, sets[0]["toks"]))
+        lm_us = graph_us(lm)
+        blas_us = graph_us(blas)
+        acc_us = graph_us(acc)
+        accp_us = graph_us(accp)
+        step_us = graph_us(lambda s: (lm(s), acc(s)))
+        stepp_us = graph_us(lambda s: (lm(s), accp(s)))
+        for d in sets:
+            st = int(d["status"].item())
+            assert st == 0, f"{cname}: device status {st}"
+        lm_bytes = V * H * 2 + nt * H * 2 + nt * V * 4 + nt * P * 12
+        lm_flops = 2.0 * nt * H * V
+        logit_bytes = (nt + nd) * V * 4
+        print(json.dumps({
+            "lm_head": cname, "rows": nt, "H": H, "V": V, "parts": P, "temperature": T,
+            "top_p": 1.0, "steps": steps,
+            "lm_head_us": round(lm_us, 2),
+            "lm_head_roofline": {
+                "algorithmic_bytes": lm_bytes, "flops": lm_flops,
+                "GBs": round(lm_bytes / (lm_us * 1e-6) / 1e9, 1),
+                "hbm_frac": round(lm_bytes / (lm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+                "TFLOPs": round(lm_flops / (lm_us * 1e-6) / 1e12, 1),
+                "mfma_frac": round(lm_flops / (lm_us * 1e-6) / 1e12 / 2500.0, 3),
+                "bound": "hbm" if lm_flops / lm_bytes < 2500.0 / 8.0 else "mfma"},
+            "hipblaslt_bf16_gemm_us": round(blas_us, 2),
+            "accept_us": round(acc_us, 2), "accept_prestats_us": round(accp_us, 2),
+            "sampler_logit_bytes": logit_bytes,
+            "step_lm_head_accept_us": round(step_us, 2),
+            "step_lm_head_accept_prestats_us": round(stepp_us, 2),
+            "same_tokens": same}), flush=True)
+        del sets, wacc
         torch.cuda.empty_cache()
 
 

@@ -315,6 +315,59 @@ int spec_accept_compact(const void* target_logits, const void* draft_logits, int
                         int32_t* cu_tokens, int32_t* status, void* workspace,
                         size_t workspace_bytes, sv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * spec_lm_head_stats -- the target's LM head with the sampler's row
+ * statistics in its epilogue.
+ *
+ * [SpS] "Conditional scoring": one target call scores the K drafts plus one
+ * position; its last linear layer turns each row's final hidden state into
+ * logits, and the sampler's first need from every row ("Modified rejection
+ * sampling": tempered softmax distributions) is its maximum and normaliser.
+ *   logits[r][v] = sum_h hidden[r][h] * weight[v][h]   (fp32 accumulation)
+ * and, per row r and part i of 64 consecutive ids [64 i, 64 i + 64) of the
+ * vocabulary (the last part shorter when V % 64 != 0):
+ *   part_max[r][i] = max z,  part_sum[r][i] = sum exp((z - part_max[r][i]) / T)
+ * with fp64 sums, so that m_r = max_i part_max and
+ * S_r = sum_i part_sum exp((part_max - m_r) / T).
+ *
+ * hidden   [rows, H] bf16, weight [V, H] bf16 (no bias), both 16-byte aligned
+ * logits   [rows, V] fp32 out (16-byte aligned)
+ * part_max [rows, parts] fp32 out, part_sum [rows, parts] fp64 out, with
+ *          parts = spec_lm_head_parts(V) = ceil(V / 64)
+ * H must be a multiple of 32 (SV_ERR_UNSUPPORTED otherwise).  One launch on
+ * `stream`; the library allocates nothing.  Errors: negative SV_ERR_* codes
+ * before any launch (bad sizes, NULL or misaligned pointers, temperature not
+ * finite and > 0).
+ * ------------------------------------------------------------------------ */
+int spec_lm_head_parts(int V);
+int spec_lm_head_stats(const void* hidden, const void* weight, int rows, int H, int V,
+                       float temperature, float* logits, float* part_max, double* part_sum,
+                       sv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * spec_accept_prestats -- spec_accept_ex with the rows' statistics from
+ * spec_lm_head_stats.
+ *
+ * For stochastic calls without a filter (top_p = 1, top_k off, not greedy)
+ * the sampler takes every row's max and normaliser from the parts instead of
+ * its own pass over the logits (one launch and one read of every logit row
+ * fewer); with a filter, or greedy, the statistics are not needed and the
+ * call is spec_accept_ex.  target_part_* are [nt, parts] for the target
+ * rows, draft_part_* [nt - B, parts] for the draft rows (row order of the
+ * logits; NULL allowed when there is no draft row), both made at the same
+ * temperature as this call.  Every other argument and the workspace as in
+ * spec_accept_ex; results agree with it on the same logits up to the fp64
+ * rounding of the normalisers (the oracle's decision margins cover it).
+ * ------------------------------------------------------------------------ */
+int spec_accept_prestats(const void* target_logits, const void* draft_logits, int logits_dtype,
+                         const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                         const int32_t* cu_q, const int32_t* cu_q_host, int B, int K, int V,
+                         float temperature, float top_p, int top_k, int greedy,
+                         const float* target_part_max, const double* target_part_sum,
+                         const float* draft_part_max, const double* draft_part_sum, int parts,
+                         int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
+                         void* workspace, size_t workspace_bytes, sv_stream_t stream);
+
 int spec_compact_kv_ragged(const int32_t* n_accepted, const int32_t* out_tokens, int32_t* kv_len,
                            const int64_t* kv_start, void* k_cache, void* v_cache,
                            const void* k_new, const void* v_new, int32_t* tokens_packed,

@@ -70,13 +70,19 @@ def lib():
         h.spec_accept_compact.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32,
                                           ctypes.c_float, ctypes.c_float, i32, i32, vp, vp, vp, vp,
                                           vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        h.spec_lm_head_parts.argtypes = [i32]
+        h.spec_lm_head_stats.argtypes = [vp, vp, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp]
+        h.spec_accept_prestats.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                           ctypes.c_float, ctypes.c_float, i32, i32, vp, vp, vp,
+                                           vp, i32, vp, vp, vp, vp, sz, vp]
         h.sv_set_kernel_events.argtypes = [vp, vp]
         for f in ("sv_set_kernel_events", "spec_verify_attn_workspace_size", "spec_verify_attn",
                   "spec_verify_attn_noalloc",
                   "spec_accept_workspace_size", "spec_accept", "spec_compact_kv",
                   "spec_verify_attn_ragged_workspace_size", "spec_verify_attn_ragged",
                   "spec_accept_ragged_workspace_size", "spec_accept_ragged",
-                  "spec_compact_kv_ragged", "spec_accept_ex", "spec_accept_compact"):
+                  "spec_compact_kv_ragged", "spec_accept_ex", "spec_accept_compact",
+                  "spec_lm_head_parts", "spec_lm_head_stats", "spec_accept_prestats"):
             getattr(h, f).restype = i32
         _lib = h
     return _lib
@@ -437,6 +443,60 @@ def spec_accept_compact(target_logits, draft_logits, draft_tokens, u_accept, u_s
         int(bool(greedy)), _ptr(n_accepted), _ptr(out_tokens), _ptr(kv_len), _ptr(kv_start),
         _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), Hkv, D, _kv_dtype(k_cache),
         _ptr(tokens_packed), _ptr(cu_tokens), _ptr(status), _ptr(workspace), workspace.numel(),
+        _stream(target_logits)))
+    return n_accepted, out_tokens
+
+
+def spec_lm_head_parts(V) -> int:
+    n = lib().spec_lm_head_parts(int(V))
+    if n < 0:
+        _check(n)
+    return n
+
+
+def spec_lm_head_stats(hidden, weight, temperature, logits, part_max, part_sum):
+    """LM head (logits = hidden @ weight^T, bf16 in, fp32 out) with every
+    row's max and fp64 sum of exp((z - max)/T) over each part of 64 ids."""
+    rows, H = hidden.shape
+    V, H2 = weight.shape
+    _need(H2 == H, "hidden [rows, H] and weight [V, H]")
+    _need(hidden.dtype == torch.bfloat16 and weight.dtype == torch.bfloat16, "bf16 inputs")
+    P = spec_lm_head_parts(V)
+    _need(logits.shape == (rows, V) and logits.dtype == torch.float32, "logits [rows, V] fp32")
+    _need(part_max.shape == (rows, P) and part_max.dtype == torch.float32, "part_max [rows, parts]")
+    _need(part_sum.shape == (rows, P) and part_sum.dtype == torch.float64, "part_sum [rows, parts]")
+    _check(lib().spec_lm_head_stats(_ptr(hidden), _ptr(weight), rows, H, V, float(temperature),
+                                    _ptr(logits), _ptr(part_max), _ptr(part_sum),
+                                    _stream(hidden)))
+    return logits, part_max, part_sum
+
+
+def spec_accept_prestats(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+                         temperature, top_p, greedy, n_accepted, out_tokens, target_part_max,
+                         target_part_sum, draft_part_max, draft_part_sum, status=None,
+                         workspace=None, top_k=0):
+    """spec_accept with the rows' statistics from spec_lm_head_stats (used by
+    stochastic calls without a filter; the segment pass is skipped)."""
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dt = _kv_dtype(target_logits)
+    P = target_part_max.shape[-1]
+    _need(target_part_max.shape == (B * K1, P) and target_part_sum.shape == (B * K1, P),
+          "target statistics [B*(K+1), parts]")
+    if draft_part_max is not None:
+        _need(draft_part_max.shape == (B * K, P) and draft_part_sum.shape == (B * K, P),
+              "draft statistics [B*K, parts]")
+    _need(n_accepted.shape == (B,) and out_tokens.shape == (B, K1), "outputs")
+    need = spec_accept_workspace_size(B, K, V)
+    if workspace is None:
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=target_logits.device)
+    _need(workspace.numel() >= need, f"workspace needs {need} bytes")
+    _check(lib().spec_accept_prestats(
+        _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
+        _ptr(u_accept) if not greedy else None, _ptr(u_sample) if not greedy else None,
+        None, None, B, K, V, float(temperature), float(top_p), int(top_k), int(bool(greedy)),
+        _ptr(target_part_max), _ptr(target_part_sum), _ptr(draft_part_max), _ptr(draft_part_sum),
+        P, _ptr(n_accepted), _ptr(out_tokens), _ptr(status), _ptr(workspace), workspace.numel(),
         _stream(target_logits)))
     return n_accepted, out_tokens
 

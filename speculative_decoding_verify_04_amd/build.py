@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["api.cpp", "accept.hip", "attn.hip", "compact.hip", "noalloc.hip"]
+SOURCES = ["api.cpp", "accept.hip", "attn.hip", "compact.hip", "noalloc.hip", "lmhead.hip"]
 ARCH = os.environ.get("SPECVERIFY_ARCH", "gfx950")
 
 

@@ -127,6 +127,13 @@ struct AcceptParams {
     int* cmp_cnt;              // workspace: sequences compacted so far (zero between calls)
     long long row_bytes;       // one KV row (Hkv * D * element size)
     int compact;
+    // row statistics from the LM head (spec_accept_prestats): per row, parts
+    // of its ids with their max and fp64 sum relative to it; [0] target rows
+    // [nt][pre_parts], [1] draft rows; used by stochastic rows without a filter
+    const float* pre_m[2];
+    const double* pre_s[2];
+    int pre_parts;
+    int prestats;
     const int32_t* cu_q;       // [B+1] ragged draft lengths: target rows of b start at cu_q[b]
     int nt;                    // target rows (cu_q[B], or B*(K+1)); draft row d is row nt + d
     int B, K, V, nseg, klist, grid_units;
@@ -1306,7 +1313,7 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
     const int nb = (lists && act) ? p.nseg * kQB : 0;
     {
         const SegHead* hs = p.seg + static_cast<size_t>(row) * p.nseg;
-        if (act && rt < p.nseg) h = hs[rt];
+        if (act && rt < p.nseg && !p.prestats) h = hs[rt];
         const double* bmr = p.bmass + static_cast<size_t>(row) * p.nseg * kQB;
         const int* bcr = p.bcnt + static_cast<size_t>(row) * p.nseg * kQB;
 #pragma unroll
@@ -1316,7 +1323,11 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
             bcv[it] = (i < nb && p.top_k > 0) ? bcr[i] : 0;
         }
     }
-    const float zxv = act ? p.zx[row] : 0.0f;
+    // the drafted token's logit (with LM-head statistics there is no segment
+    // pass to pick it up: read it from the row)
+    const float zxv = !act ? 0.0f
+                           : (p.prestats ? (x_ok && j < kb ? load1(row_ptr(p, row), p.bf16, x) : 0.0f)
+                                         : p.zx[row]);
     const float uav = (tid == kMThreads - 1 && j < kb) ? p.u_accept[u - b] : 0.0f;
     const float usv = (tid == kMThreads - 1) ? p.u_sample[b] : 0.0f;
     if (act) {
@@ -1362,7 +1373,38 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
     // bin masses (every kRW-th segment; lane = row bin); the first wave also
     // the normaliser and the bins listed in every segment
     static_assert(kMaxSeg <= 128, "two segments per lane");
-    if (act) {
+    if (act && p.prestats) {
+        // no filter: the row's max and normaliser from the LM head's parts.
+        // Every wave of the row finds the max over all parts; each adds the
+        // rescaled sums of every kRW-th stretch of 64 parts (the waves'
+        // shares are added in wave order after the barrier below).
+        const size_t pr = rr ? static_cast<size_t>(dr - p.nt) : static_cast<size_t>(u);
+        const float* pm = p.pre_m[rr] + pr * p.pre_parts;
+        const double* ps = p.pre_s[rr] + pr * p.pre_parts;
+        float m = -INFINITY;
+        for (int i = lane; i < p.pre_parts; i += 64) m = fmaxf(m, pm[i]);
+        m = wave_max(m);
+        double Sacc = 0.0;
+        for (int i = rt; i < p.pre_parts; i += kHalf) {
+            const float mi = pm[i];
+            if (mi != -INFINITY) Sacc += ps[i] * weight(mi, m, p.yscale, L.tab);
+        }
+        Sacc = wave_sum(Sacc);
+        if (lane == 0) R.part[rw][0] = Sacc;
+        if (rw == 0 && lane == 0) {
+            R.m = m;
+            R.top = qbin(m, p.qscale);
+            R.ocmax = -1;
+            R.fast = 0;
+            R.tau = -INFINITY;
+            R.zk = -INFINITY;
+            R.zmin = -INFINITY;
+            R.ccount = 0;
+            R.needsub = 0;
+            R.above = 0.0;
+            R.abovec = 0;
+        }
+    } else if (act) {
         const bool s0 = lane < p.nseg, s1 = lane + 64 < p.nseg;
         const float v0 = s0 ? R.seg_m[lane] : -INFINITY;
         const float v1 = s1 ? R.seg_m[lane + 64] : -INFINITY;
@@ -1416,6 +1458,17 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
         R.sbk[1][lane] = 0u;
     }
     __syncthreads();
+    if (p.prestats) {  // uniform: the normaliser from the waves' shares
+        if (act && rw == 0 && lane == 0) {
+            double Sr = 0.0;
+#pragma unroll
+            for (int w2 = 0; w2 < kRW; ++w2) Sr += R.part[w2][0];
+            R.S = Sr;
+            R.kept = Sr;
+            R.Sk = Sr;
+        }
+        __syncthreads();
+    }
 
     if (lists) {
         // ---- the first wave of a row adds the partial bin masses in a fixed
@@ -2058,13 +2111,22 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     p.dsum = reinterpret_cast<double*>(base + w.dsum);
     p.qsum = reinterpret_cast<double*>(base + w.qsum);
 
-    const dim3 grid(p.grid_units * p.nseg);
-    if (ept == 16)
-        hipLaunchKernelGGL(segment_kernel<16>, grid, dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(segment_kernel<12>, grid, dim3(kThreads), 0, stream, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    p.prestats = (a.pre_m[0] && !p.filter && !p.greedy) ? 1 : 0;
+    p.pre_m[0] = a.pre_m[0];
+    p.pre_m[1] = a.pre_m[1];
+    p.pre_s[0] = a.pre_s[0];
+    p.pre_s[1] = a.pre_s[1];
+    p.pre_parts = a.pre_parts;
+    hipError_t err = hipSuccess;
+    if (!p.prestats) {  // the LM head's statistics replace the segment pass
+        const dim3 grid(p.grid_units * p.nseg);
+        if (ept == 16)
+            hipLaunchKernelGGL(segment_kernel<16>, grid, dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL(segment_kernel<12>, grid, dim3(kThreads), 0, stream, p);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     hipLaunchKernelGGL(merge_kernel, dim3(a.nt), dim3(kMThreads), 0, stream, p);
     err = hipGetLastError();
     if (err != hipSuccess || a.greedy || p.filter) return err;

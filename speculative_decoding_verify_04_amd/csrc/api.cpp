@@ -229,6 +229,11 @@ int accept_run(const void* target_logits, const void* draft_logits, int logits_d
         a.tokens_packed = fused->tokens_packed;
         a.cu_tokens = fused->cu_tokens;
         a.row_bytes = fused->row_bytes;
+        a.pre_m[0] = fused->pre_m[0];
+        a.pre_m[1] = fused->pre_m[1];
+        a.pre_s[0] = fused->pre_s[0];
+        a.pre_s[1] = fused->pre_s[1];
+        a.pre_parts = fused->pre_parts;
     }
     hipError_t e = sv::accept_launch(a, as_stream(stream));
     if (e != hipSuccess) return fail(SV_ERR_HIP, "sampler launch failed: %s", hipGetErrorString(e));
@@ -461,6 +466,77 @@ int spec_accept_compact(const void* target_logits, const void* draft_logits, int
     f.tokens_packed = tokens_packed;
     f.cu_tokens = cu_tokens;
     f.row_bytes = static_cast<size_t>(Hkv) * D * es;
+    if (!cu_q && !cu_q_host) {
+        if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
+        return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept,
+                          u_sample, nullptr, static_cast<long long>(B) * (K + 1), B, K, V,
+                          temperature, top_p, top_k, greedy, n_accepted, out_tokens, status,
+                          workspace, workspace_bytes, stream, &f);
+    }
+    int kmax = 0;
+    int rc = check_cu_q(B, cu_q_host, &kmax);
+    if (rc) return rc;
+    if (!cu_q) return fail(SV_ERR_INVALID_ARG, "cu_q is NULL");
+    if (V < 1) return fail(SV_ERR_INVALID_ARG, "need V >= 1");
+    return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept, u_sample,
+                      cu_q, cu_q_host[B], B, kmax, V, temperature, top_p, top_k, greedy,
+                      n_accepted, out_tokens, status, workspace, workspace_bytes, stream, &f);
+}
+
+int spec_lm_head_parts(int V) {
+    if (V < 1) return fail(SV_ERR_INVALID_ARG, "need V >= 1");
+    ok();
+    return sv::lm_head_parts(V);
+}
+
+int spec_lm_head_stats(const void* hidden, const void* weight, int rows, int H, int V,
+                       float temperature, float* logits, float* part_max, double* part_sum,
+                       sv_stream_t stream) {
+    if (rows < 0 || H < 1 || V < 1) return fail(SV_ERR_INVALID_ARG, "need rows >= 0, H >= 1, V >= 1");
+    if (H % 32 != 0) return fail(SV_ERR_UNSUPPORTED, "H must be a multiple of 32");
+    if (!(temperature > 0.0f) || !isfinite(temperature))
+        return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0");
+    if (static_cast<long long>(rows) * V > 0x7FFFFFFFLL * 4)
+        return fail(SV_ERR_UNSUPPORTED, "rows * V too large");
+    if (rows == 0) return ok();
+    if (!hidden || !weight || !logits || !part_max || !part_sum)
+        return fail(SV_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+    if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(logits, 16))
+        return fail(SV_ERR_INVALID_ARG, "hidden, weight and logits must be 16-byte aligned");
+    sv::LmArgs a{};
+    a.hidden = hidden;
+    a.weight = weight;
+    a.rows = rows;
+    a.H = H;
+    a.V = V;
+    a.temperature = temperature;
+    a.logits = logits;
+    a.part_max = part_max;
+    a.part_sum = part_sum;
+    hipError_t e = sv::lm_head_launch(a, as_stream(stream));
+    if (e != hipSuccess) return fail(SV_ERR_HIP, "LM head launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int spec_accept_prestats(const void* target_logits, const void* draft_logits, int logits_dtype,
+                         const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                         const int32_t* cu_q, const int32_t* cu_q_host, int B, int K, int V,
+                         float temperature, float top_p, int top_k, int greedy,
+                         const float* target_part_max, const double* target_part_sum,
+                         const float* draft_part_max, const double* draft_part_sum, int parts,
+                         int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
+                         void* workspace, size_t workspace_bytes, sv_stream_t stream) {
+    if (parts < 1) return fail(SV_ERR_INVALID_ARG, "need parts >= 1");
+    if (B > 0 && (!target_part_max || !target_part_sum))
+        return fail(SV_ERR_INVALID_ARG, "target row statistics are NULL");
+    if (B > 0 && !greedy && (K > 0 || cu_q_host) && (!draft_part_max || !draft_part_sum))
+        return fail(SV_ERR_INVALID_ARG, "draft row statistics are NULL");
+    sv::AcceptArgs f{};
+    f.pre_m[0] = target_part_max;
+    f.pre_s[0] = target_part_sum;
+    f.pre_m[1] = draft_part_max;
+    f.pre_s[1] = draft_part_sum;
+    f.pre_parts = parts;
     if (!cu_q && !cu_q_host) {
         if (B < 0 || K < 0 || V < 1) return fail(SV_ERR_INVALID_ARG, "need B >= 0, K >= 0, V >= 1");
         return accept_run(target_logits, draft_logits, logits_dtype, draft_tokens, u_accept,

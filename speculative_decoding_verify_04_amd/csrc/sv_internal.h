@@ -93,6 +93,10 @@ struct AcceptArgs {
     int32_t* tokens_packed;
     int32_t* cu_tokens;
     size_t row_bytes;     // Hkv * D * element size (a multiple of 4)
+    // row statistics from the LM head (spec_accept_prestats); pre_m[0] null: none
+    const float* pre_m[2];   // [0] target rows [nt][pre_parts], [1] draft rows
+    const double* pre_s[2];
+    int pre_parts;
 };
 
 // nt: target rows in all (B*(K+1) without ragged draft lengths)
@@ -100,6 +104,20 @@ size_t accept_workspace_bytes(int B, long long nt, int V);
 int accept_max_vocab();
 int accept_max_drafts();
 hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- LM head
+struct LmArgs {
+    const void* hidden;   // [rows][H] bf16
+    const void* weight;   // [V][H] bf16
+    int rows, H, V;       // H a multiple of 32
+    float temperature;
+    float* logits;        // [rows][V] fp32
+    float* part_max;      // [rows][lm_head_parts(V)]
+    double* part_sum;
+};
+int lm_head_parts(int V);
+int lm_head_part_len();
+hipError_t lm_head_launch(const LmArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- compaction
 struct CompactArgs {
