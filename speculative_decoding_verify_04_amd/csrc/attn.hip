@@ -34,6 +34,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include <hip/hip_ext.h>
 
@@ -218,6 +219,27 @@ struct DecLds {
     int flag;
 };
 
+// LDS of the column-wave form: the query tiles (read into registers at the
+// start), the device plan's prefix sums (prologue) and the merge's weights
+// (end) are never live at once.
+template <int D, int NCT>
+struct DecLdsCol {
+    static constexpr int VP = D + 4;
+    union {
+        uint16_t qs[NCT * 16][D + 8];
+        int Q[kSkMaxB + 1];
+        struct {
+            float2 ml[kMergeLds];
+            float w[kMergeLds];
+        } mrg;
+    };
+    int L;
+    int k1;
+    int q0;
+    long long kv0;
+    int flag;
+};
+
 // Merge of the partials of (sequence, kv head g) when no prefix part is
 // involved and every value a thread needs fits in registers (UP (d, column)
 // pairs per thread, PMAX parts): the partial loads are issued before the
@@ -398,6 +420,21 @@ __device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_s
     }
 }
 
+// Position of the 16-byte chunk c of a 128-wide bf16 row r in LDS: c ^ swz(r).
+// The 16-byte K reads of 16 consecutive rows and the transposed 8-byte V reads
+// of 16 rows x 2 chunks then fall on distinct LDS banks.
+__device__ __forceinline__ int prefix_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+// One 16-key slice of K and V for the whole workgroup (column-wave form),
+// filled by direct global-to-LDS loads (D = 128: rows of 16 chunks, chunk c
+// of row r at c ^ prefix_swz(r)).  The kernel holds six as separate LDS
+// objects, so the compiler can tell reads of one from direct loads still
+// landing in the others.
+struct DecColSlot {
+    uint4 k[16 * 16];
+    uint4 v[16 * 16];
+};
+
 // K and V of one 16-key slice held in registers.
 template <int D>
 struct Slice {
@@ -405,16 +442,26 @@ struct Slice {
     uint4 v[16 * (D / 8) / 64];
 };
 
-template <int D, int NCT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(NCT == 1 ? SV_NCT1_WAVES : 1)))
+// MODE 0: each wave takes every 4th slice of the item for all NCT column
+// tiles and keeps its next slice in registers.  MODE 2 (D = 128, NCT 2..4):
+// column waves -- wave w < NCT takes column tile w over every slice of the
+// item, so it holds one tile's accumulators instead of NCT (the multi-tile
+// form of mode 0 runs one wave per SIMD); the slices pass through a six-slot
+// LDS ring that all four waves fill with direct loads, one barrier per
+// slice, and no wave combine is needed.
+template <int D, int NCT, int MODE>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(NCT == 1 ? SV_NCT1_WAVES : (MODE == 2 ? 2 : 1))))
 void decode_bf16_kernel(AttnParams p, DecPlan plan) {
+    static_assert(MODE == 0 || (MODE == 2 && D == 128), "the ring layout is for 128-wide heads");
     constexpr int KK = D / 32;   // 16x16x32 steps over the head dim
     constexpr int DT = D / 16;   // 16-wide head-dim tiles of the PV product
     constexpr int VCH = D / 8;   // 16-byte chunks per K/V row
     constexpr int VLD = 16 * VCH / 64;  // 16-byte V loads per lane per slice
     constexpr int VP = DecLds<D, NCT>::VP;
     constexpr int NPRO = kSkMaxB / kThreads;
-    __shared__ DecLds<D, NCT> S;
+    using LdsT = typename std::conditional<MODE == 2, DecLdsCol<D, NCT>, DecLds<D, NCT>>::type;
+    __shared__ LdsT S;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col16 = lane & 15, kg = lane >> 4;
@@ -551,19 +598,16 @@ void decode_bf16_kernel(AttnParams p, DecPlan plan) {
 
     const int rs = p.Hkv * D;  // elements per cache row
     const size_t head = static_cast<size_t>(g) * D;
-    uint16_t(*vs)[VP] = S.vs[w];
-    // transposed-read address of this lane: row kg*4 + col16/4, column 4*(col16%4)
-    const uint16_t* vt_base = &vs[kg * 4 + (col16 >> 2)][(col16 & 3) * 4];
 
     // Slice of keys [k0, k0+16) into registers.  Every lane addresses its own
     // row: cache rows for keys < L, new rows after them; keys past the last
     // one are clamped to it (and masked).
-    auto row = [&](int tt, const uint16_t* cache, const uint16_t* fresh) -> const uint16_t* {
+    auto row = [&](int tt, const uint16_t* cache, const uint16_t* fresh) __attribute__((always_inline)) -> const uint16_t* {
         tt = min(tt, T - 1);
         return (tt < L) ? cache + static_cast<size_t>(kv0 + tt) * rs + head
                         : fresh + static_cast<size_t>(q0 + (tt - L)) * rs + head;
     };
-    auto load_slice = [&](Slice<D>& sl, int k0) {
+    auto load_slice = [&](Slice<D>& sl, int k0) __attribute__((always_inline)) {
         const uint16_t* kp = row(k0 + col16, p.k_cache, p.k_new) + kg * 8;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) sl.k[kk] = *reinterpret_cast<const bf16x8*>(kp + 32 * kk);
@@ -574,7 +618,61 @@ void decode_bf16_kernel(AttnParams p, DecPlan plan) {
     };
 
     Slice<D> sl;
-    if (sl_lo + w < sl_hi) load_slice(sl, (sl_lo + w) * 16);
+    if constexpr (MODE == 0) {
+        if (sl_lo + w < sl_hi) load_slice(sl, (sl_lo + w) * 16);
+    }
+    // (the sequence's length and first cache row as wave-uniform scalars, and
+    // the row chosen by selects: the direct loads then wait for nothing)
+    const int Lu = __builtin_amdgcn_readfirstlane(L);
+    const long long kv0u = static_cast<long long>(
+        (static_cast<unsigned long long>(static_cast<unsigned>(__builtin_amdgcn_readfirstlane(
+             static_cast<int>(kv0 >> 32))))
+         << 32) |
+        static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(kv0))));
+    const uint16_t* const kc = p.k_cache;  // (kernel arguments as scalars, not loads)
+    const uint16_t* const vc = p.v_cache;
+    const uint16_t* const kn = p.k_new;
+    const uint16_t* const vn = p.v_new;
+    auto row_sel = [&](int tt, const uint16_t* cache, const uint16_t* fresh) __attribute__((always_inline)) -> const uint16_t* {
+        tt = min(tt, T - 1);
+        const bool in_cache = tt < Lu;
+        const long long ri = in_cache ? kv0u + tt : static_cast<long long>(q0 + (tt - Lu));
+        return (in_cache ? cache : fresh) + static_cast<size_t>(ri) * rs + head;
+    };
+    // column waves: every slice of the item; wave w loads blocks 2w, 2w+1
+    // (waves 0, 1: K rows 0-7, 8-15; waves 2, 3: the same V rows)
+    const int nslc = sl_hi - sl_lo;
+    const bool cisv = w >= 2;
+    const int cbb0 = 2 * (w & 1);
+    // row within the slice and element offset of this lane's 16 bytes, per block
+    const int cr0 = cbb0 * 4 + (lane >> 4), cr1 = cr0 + 4;
+    const int cp0 = (lane & 15) ^ prefix_swz(cr0), cp1 = (lane & 15) ^ prefix_swz(cr1);
+    const int coff0 = cr0 * rs + static_cast<int>(head) + cp0 * 8;
+    const int coff1 = cr1 * rs + static_cast<int>(head) + cp1 * 8;
+    auto issue_c = [&](int j, DecColSlot& R) __attribute__((always_inline)) {
+        const int k0 = (sl_lo + j) * 16;
+        if (k0 + 15 < Lu) {  // uniform: every row of the slice is a cache row
+            const size_t base = static_cast<size_t>(kv0u + k0) * rs;
+            const uint16_t* src0 = (cisv ? vc : kc) + base + coff0;
+            const uint16_t* src1 = (cisv ? vc : kc) + base + coff1;
+            __builtin_amdgcn_global_load_lds(src0, (cisv ? R.v : R.k) + cbb0 * 64, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src1, (cisv ? R.v : R.k) + cbb0 * 64 + 64, 16, 0, 0);
+        } else {
+            const uint16_t* src0 = row_sel(k0 + cr0, cisv ? vc : kc, cisv ? vn : kn) + cp0 * 8;
+            const uint16_t* src1 = row_sel(k0 + cr1, cisv ? vc : kc, cisv ? vn : kn) + cp1 * 8;
+            __builtin_amdgcn_global_load_lds(src0, (cisv ? R.v : R.k) + cbb0 * 64, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(src1, (cisv ? R.v : R.k) + cbb0 * 64 + 64, 16, 0, 0);
+        }
+    };
+    // six slots: slice j in slot j mod 6, five slices in flight
+    __shared__ DecColSlot C0, C1, C2, C3, C4, C5;  // referenced only when MODE == 2
+    if constexpr (MODE == 2) {
+        if (nslc > 0) issue_c(0, C0);
+        if (nslc > 1) issue_c(1, C1);
+        if (nslc > 2) issue_c(2, C2);
+        if (nslc > 3) issue_c(3, C3);
+        if (nslc > 4) issue_c(4, C4);
+    }
 
     // the work item's query columns -> LDS (zero rows for padding columns)
     for (int idx = tid; idx < NCT * 16 * VCH; idx += kThreads) {
@@ -607,72 +705,151 @@ void decode_bf16_kernel(AttnParams p, DecPlan plan) {
         for (int dt = 0; dt < DT; ++dt) o[ct][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Per slice: stage V in LDS, S^T = K Q^T, then reissue the slice
-    // registers for the wave's next slice (in flight during the softmax and
-    // the PV product).
-    for (int si = sl_lo + w; si < sl_hi; si += 4) {
-        const int k0 = si * 16;
+    // Online softmax of one column tile's scores on one slice (S^T tile
+    // `acc`, keys k0 + kg*4 + ee) and O^T += V^T P^T with the slice's V^T
+    // operands.
+    auto tile_update = [&](int k0, bool full, int limt, const floatx4& acc, const shortx4 (&va)[DT],
+                           float& mr, float& lr, floatx4 (&ot)[DT]) __attribute__((always_inline)) {
+        float s[4];
+        float mt = -INFINITY;
 #pragma unroll
-        for (int q = 0; q < VLD; ++q) {
-            uint2* dst = reinterpret_cast<uint2*>(&vs[(q * 64 + lane) / VCH][((q * 64 + lane) % VCH) * 8]);
-            dst[0] = make_uint2(sl.v[q].x, sl.v[q].y);
-            dst[1] = make_uint2(sl.v[q].z, sl.v[q].w);
+        for (int ee = 0; ee < 4; ++ee) {
+            const int tt = k0 + kg * 4 + ee;
+            s[ee] = (full || tt < limt) ? acc[ee] * p.scale_log2 : -INFINITY;
+            mt = fmaxf(mt, s[ee]);
         }
-        floatx4 acc[NCT];
+        mt = colmax4(mt);
+        const float mnew = fmaxf(mr, mt);
+        // the running max of no column of the tile grew: alpha would be
+        // exactly 1 on every lane, so the rescale of O is skipped (most
+        // slices after the first few)
+        const bool grew = __ballot(mt > mr) != 0;
+        float alpha = 1.0f;
+        shortx4 pb;
+        if (mnew == -INFINITY) {
+            pb = shortx4{0, 0, 0, 0};
+        } else {
+            if (grew) alpha = __builtin_amdgcn_exp2f(mr - mnew);
+            float pe[4];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int ee = 0; ee < 4; ++ee) pe[ee] = __builtin_amdgcn_exp2f(s[ee] - mnew);
+            lr = lr * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
+            mr = mnew;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const bf16x8 qop =
-                    *reinterpret_cast<const bf16x8*>(&S.qs[ct * 16 + col16][kg * 8 + 32 * kk]);
-                acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl.k[kk], qop, acc[ct], 0, 0, 0);
-            }
+            for (int ee = 0; ee < 4; ++ee) pb[ee] = static_cast<short>(f32_to_bf16(pe[ee]));
         }
-        if (si + 4 < sl_hi) load_slice(sl, k0 + 64);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // V^T operands: lane (d = dt*16 + col16) gets keys kg*4 .. kg*4+3
-        shortx4 va[DT];
+        if (grew) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) va[dt] = lds_read_tr16(vt_base + dt * 16);
+            for (int dt = 0; dt < DT; ++dt) ot[dt] *= alpha;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            ot[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, ot[dt], 0, 0, 0);
+    };
+    auto softmax_pv = [&](int k0, const floatx4 (&acc)[NCT], const shortx4 (&va)[DT]) __attribute__((always_inline)) {
         const bool full = k0 + 15 < L;  // no key of the slice is masked for any column
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            float s[4];
-            float mt = -INFINITY;
+        for (int ct = 0; ct < NCT; ++ct) tile_update(k0, full, lim[ct], acc[ct], va, mrun[ct], lrun[ct], o[ct]);
+    };
+
+    // K operand of a ring slot: row col16, logical chunk kg + 4 kk, stored at
+    // (kg ^ (sk & 3)) + 4 (kk ^ (sk >> 2)); V^T operand: row rv = kg*4 +
+    // col16/4, logical chunk 2 dt + h (h = (col16 & 3) >> 1), 8-byte half
+    // col16 & 1, stored at chunk 2 (dt ^ (sv >> 1)) + (h ^ (sv & 1))
+    const int csk = prefix_swz(col16);
+    const int ckcol = col16 * 16 + (kg ^ (csk & 3));
+    const int csk2 = csk >> 2;
+    const int crv = kg * 4 + (col16 >> 2);
+    const int csv = prefix_swz(crv);
+    const int csv1 = csv >> 1;
+    const int cvcol = crv * D + 8 * (((col16 & 3) >> 1) ^ (csv & 1)) + 4 * (col16 & 1);
+    // column waves: this wave's tile and its state
+    float mcw = -INFINITY, lcw = 0.0f;
+    floatx4 ocw[DT];
 #pragma unroll
-            for (int ee = 0; ee < 4; ++ee) {
-                const int tt = k0 + kg * 4 + ee;
-                s[ee] = (full || tt < lim[ct]) ? acc[ct][ee] * p.scale_log2 : -INFINITY;
-                mt = fmaxf(mt, s[ee]);
+    for (int dt = 0; dt < DT; ++dt) ocw[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (MODE == 2) {
+        const bool cw = w < NCT;  // uniform: this wave computes tile w
+        const int colw = w * 16 + col16;
+        const int limw = (cw && colw < ncols) ? L + colw % k1 + 1 : 0;
+        bf16x8 qv[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qv[kk] = *reinterpret_cast<const bf16x8*>(&S.qs[(cw ? w : 0) * 16 + col16][kg * 8 + 32 * kk]);
+        auto step_c = [&](int j, DecColSlot& R, DecColSlot& Rn) __attribute__((always_inline)) {
+            // this wave's blocks of slice j are in when at most those of the
+            // slices issued after it (j+1 .. j+4, two each) are in flight
+            switch (min(4, nslc - 1 - j)) {
+                case 4: __builtin_amdgcn_s_waitcnt(0x0F78); break;  // vmcnt(8)
+                case 3: __builtin_amdgcn_s_waitcnt(0x0F76); break;  // vmcnt(6)
+                case 2: __builtin_amdgcn_s_waitcnt(0x0F74); break;  // vmcnt(4)
+                case 1: __builtin_amdgcn_s_waitcnt(0x0F72); break;  // vmcnt(2)
+                default: __builtin_amdgcn_s_waitcnt(0x0F70); break; // vmcnt(0)
             }
-            mt = colmax4(mt);
-            const float mnew = fmaxf(mrun[ct], mt);
-            float alpha = 1.0f;
-            shortx4 pb;
-            if (mnew == -INFINITY) {
-                pb = shortx4{0, 0, 0, 0};
-            } else {
-                alpha = exp2f(mrun[ct] - mnew);
-                float pe[4];
+            __syncthreads();  // every block of slice j is in R; slice j-1 (in Rn) is read
+            if (j + 5 < nslc) issue_c(j + 5, Rn);
+            if (cw) {
+                const int k0 = (sl_lo + j) * 16;
+                floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ee = 0; ee < 4; ++ee) pe[ee] = exp2f(s[ee] - mnew);
-                lrun[ct] = lrun[ct] * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-                mrun[ct] = mnew;
+                for (int kk = 0; kk < KK; ++kk) {
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(R.k + ckcol + 4 * (kk ^ csk2));
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qv[kk], acc, 0, 0, 0);
+                }
+                const uint16_t* vb = reinterpret_cast<const uint16_t*>(R.v);
+                shortx4 va[DT];
 #pragma unroll
-                for (int ee = 0; ee < 4; ++ee) pb[ee] = static_cast<short>(f32_to_bf16(pe[ee]));
+                for (int dt = 0; dt < DT; ++dt) va[dt] = lds_read_tr16(vb + cvcol + 16 * (dt ^ csv1));
+                tile_update(k0, k0 + 15 < L, limw, acc, va, mcw, lcw, ocw);
             }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                o[ct][dt] *= alpha;
-                o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, o[ct][dt], 0, 0, 0);
-            }
+        };
+        for (int j = 0; j < nslc; j += 6) {
+            step_c(j, C0, C5);
+            if (j + 1 < nslc) step_c(j + 1, C1, C0);
+            if (j + 2 < nslc) step_c(j + 2, C2, C1);
+            if (j + 3 < nslc) step_c(j + 3, C3, C2);
+            if (j + 4 < nslc) step_c(j + 4, C4, C3);
+            if (j + 5 < nslc) step_c(j + 5, C5, C4);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        uint16_t(*vs)[VP] = S.vs[w];
+        // transposed-read address of this lane: row kg*4 + col16/4, column 4*(col16%4)
+        const uint16_t* vt_base = &vs[kg * 4 + (col16 >> 2)][(col16 & 3) * 4];
+        // Per slice: stage V in LDS, S^T = K Q^T, then reissue the slice
+        // registers for the wave's next slice (in flight during the softmax
+        // and the PV product).
+        for (int si = sl_lo + w; si < sl_hi; si += 4) {
+            const int k0 = si * 16;
+#pragma unroll
+            for (int q = 0; q < VLD; ++q) {
+                uint2* dst = reinterpret_cast<uint2*>(&vs[(q * 64 + lane) / VCH][((q * 64 + lane) % VCH) * 8]);
+                dst[0] = make_uint2(sl.v[q].x, sl.v[q].y);
+                dst[1] = make_uint2(sl.v[q].z, sl.v[q].w);
+            }
+            floatx4 acc[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    const bf16x8 qop =
+                        *reinterpret_cast<const bf16x8*>(&S.qs[ct * 16 + col16][kg * 8 + 32 * kk]);
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl.k[kk], qop, acc[ct], 0, 0, 0);
+                }
+            }
+            if (si + 4 < sl_hi) load_slice(sl, k0 + 64);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // V^T operands: lane (d = dt*16 + col16) gets keys kg*4 .. kg*4+3
+            shortx4 va[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) va[dt] = lds_read_tr16(vt_base + dt * 16);
+            softmax_pv(k0, acc, va);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
     }
 
 #pragma unroll
@@ -683,6 +860,24 @@ void decode_bf16_kernel(AttnParams p, DecPlan plan) {
     // combine the 4 waves (fixed order) in two halves of the head dim; the
     // partial of work item `id` is stored at slot id, laid out [d][column]
     const size_t slot = static_cast<size_t>(id);
+    if constexpr (MODE == 2) {
+        // column waves hold their tile's whole partial: store it as it is
+        lcw = colsum4(lcw);
+        const int colw = w * 16 + col16;
+        if (w < NCT && colw < ncols) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee)
+                    st_coh(p.part_o + (slot * D + dt * 16 + kg * 4 + ee) * p.CPG + colw, ocw[dt][ee]);
+            if (kg == 0) {
+                const unsigned long long v =
+                    (static_cast<unsigned long long>(__float_as_uint(lcw)) << 32) | __float_as_uint(mcw);
+                st_coh(reinterpret_cast<unsigned long long*>(p.part_ml + slot * p.CPG + colw), v);
+            }
+        }
+    }
+    if constexpr (MODE != 2) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
@@ -724,6 +919,7 @@ void decode_bf16_kernel(AttnParams p, DecPlan plan) {
                 }
             }
         }
+    }
     }
     if (arrive_last(p.merge_cnt + static_cast<size_t>(b) * p.Hkv + g, qb, &S.flag))
         dec_merge<D, NCT>(p, S.mrg, b, g, first_slot + g, qb, q0, k1);
@@ -939,7 +1135,6 @@ struct PrefixDmaBuf {
     uint4 v[kTile * kChunks];
 };
 
-__device__ __forceinline__ int prefix_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 // grid as for prefix_bf16_kernel; block: 1024 threads (16 waves), which the
 // mapping of waves to column tiles below assumes.
@@ -1300,6 +1495,14 @@ int env_int(const char* name, int dflt) {
     return v > 0 ? v : dflt;
 }
 
+// Decode kernel form: the multi-tile forms with 128-wide heads run column
+// waves (mode 2); SPECVERIFY_ATTN_MODE=0 selects the register form for them.
+int sk_mode(int D, int nct) {
+    static const int env = env_int("SPECVERIFY_ATTN_MODE", 2);
+    if (D != 128 || nct < 2) return 0;
+    return env == 0 ? 0 : 2;
+}
+
 // Workgroups of the decode kernel that the GPU holds at once (CUs x
 // resident workgroups per CU), cached per device and kernel variant.
 int sk_resident_grid(int D, int nct) {
@@ -1314,13 +1517,17 @@ int sk_resident_grid(int D, int nct) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
     const void* fn = nullptr;
-#define SV_FN(DD, NN) fn = reinterpret_cast<const void*>(&decode_bf16_kernel<DD, NN>)
-    if (D == 128) {
-        switch (nct) { case 1: SV_FN(128, 1); break; case 2: SV_FN(128, 2); break;
-                       case 3: SV_FN(128, 3); break; default: SV_FN(128, 4); break; }
+#define SV_FN(DD, NN, MM) fn = reinterpret_cast<const void*>(&decode_bf16_kernel<DD, NN, MM>)
+    const int mode = sk_mode(D, nct);
+    if (D == 128 && mode == 2) {
+        switch (nct) { case 2: SV_FN(128, 2, 2); break;
+                       case 3: SV_FN(128, 3, 2); break; default: SV_FN(128, 4, 2); break; }
+    } else if (D == 128) {
+        switch (nct) { case 1: SV_FN(128, 1, 0); break; case 2: SV_FN(128, 2, 0); break;
+                       case 3: SV_FN(128, 3, 0); break; default: SV_FN(128, 4, 0); break; }
     } else {
-        switch (nct) { case 1: SV_FN(64, 1); break; case 2: SV_FN(64, 2); break;
-                       case 3: SV_FN(64, 3); break; default: SV_FN(64, 4); break; }
+        switch (nct) { case 1: SV_FN(64, 1, 0); break; case 2: SV_FN(64, 2, 0); break;
+                       case 3: SV_FN(64, 3, 0); break; default: SV_FN(64, 4, 0); break; }
     }
 #undef SV_FN
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess) per_cu = 0;
@@ -1539,28 +1746,35 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
         dim3 grid(p.xcd ? (pl.grid + 7) / 8 * 8 : pl.grid);
         // With timing events, the dispatch itself stamps them at the kernel's
         // start and end (the same timestamps a kernel trace reports).
-#define SV_DECODE(DD, NN)                                                                          \
+#define SV_DECODE(DD, NN, RR)                                                                      \
     do {                                                                                           \
         if (a.ev_start && a.ev_stop)                                                               \
-            hipExtLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream,  \
-                                  a.ev_start, a.ev_stop, 0, p, dp);                                \
+            hipExtLaunchKernelGGL((decode_bf16_kernel<DD, NN, RR>), grid, dim3(kThreads), 0,      \
+                                  stream, a.ev_start, a.ev_stop, 0, p, dp);                        \
         else                                                                                       \
-            hipLaunchKernelGGL((decode_bf16_kernel<DD, NN>), grid, dim3(kThreads), 0, stream, p,  \
-                               dp);                                                                \
+            hipLaunchKernelGGL((decode_bf16_kernel<DD, NN, RR>), grid, dim3(kThreads), 0, stream, \
+                               p, dp);                                                             \
     } while (0)
-        if (a.D == 128) {
+        const int mode = sk_mode(a.D, nct);
+        if (a.D == 128 && mode == 2) {
             switch (nct) {
-                case 1: SV_DECODE(128, 1); break;
-                case 2: SV_DECODE(128, 2); break;
-                case 3: SV_DECODE(128, 3); break;
-                default: SV_DECODE(128, 4); break;
+                case 2: SV_DECODE(128, 2, 2); break;
+                case 3: SV_DECODE(128, 3, 2); break;
+                default: SV_DECODE(128, 4, 2); break;
+            }
+        } else if (a.D == 128) {
+            switch (nct) {
+                case 1: SV_DECODE(128, 1, 0); break;
+                case 2: SV_DECODE(128, 2, 0); break;
+                case 3: SV_DECODE(128, 3, 0); break;
+                default: SV_DECODE(128, 4, 0); break;
             }
         } else {
             switch (nct) {
-                case 1: SV_DECODE(64, 1); break;
-                case 2: SV_DECODE(64, 2); break;
-                case 3: SV_DECODE(64, 3); break;
-                default: SV_DECODE(64, 4); break;
+                case 1: SV_DECODE(64, 1, 0); break;
+                case 2: SV_DECODE(64, 2, 0); break;
+                case 3: SV_DECODE(64, 3, 0); break;
+                default: SV_DECODE(64, 4, 0); break;
             }
         }
 #undef SV_DECODE
