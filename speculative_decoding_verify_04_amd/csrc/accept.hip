@@ -1821,18 +1821,25 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
     fill_exp_table(L.tab);
     __syncthreads();
     const int n = L.n;
+    // the stopping rows' logits and their records in one round trip
+    const bool residual = n < K;
+    const void* qrow = row_ptr(p, q0 + n);
+    const void* prow = residual ? row_ptr(p, nt + q0 - b + n) : nullptr;
+    float zq[EPT], zp[EPT];
+    load_segment<EPT>(qrow, p.bf16, p.vec, p.V, s, tid, zq);
+    if (residual) load_segment<EPT>(prow, p.bf16, p.vec, p.V, s, tid, zp);
     if (tid == 0) L.rr[0] = p.rows[q0 + n];
-    if (tid == 1 && n < K) L.rr[1] = p.rows[nt + q0 - b + n];
+    if (tid == 1 && residual) L.rr[1] = p.rows[nt + q0 - b + n];
     __syncthreads();
 
     DrawCtx c;
     c.tab = L.tab;
-    c.residual = n < K;
-    c.qrow = row_ptr(p, q0 + n);
+    c.residual = residual;
+    c.qrow = qrow;
     c.rq = L.rr[0];
     c.invSq = 1.0 / c.rq.S;
-    if (c.residual) {
-        c.prow = row_ptr(p, nt + q0 - b + n);
+    if (residual) {
+        c.prow = prow;
         c.rp = L.rr[1];
         c.invSp = 1.0 / c.rp.S;
     } else {
@@ -1840,10 +1847,6 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(AcceptParams p, int grid
         c.rp = c.rq;
         c.invSp = 0.0;
     }
-
-    float zq[EPT], zp[EPT];
-    load_segment<EPT>(c.qrow, p.bf16, p.vec, p.V, s, tid, zq);
-    if (c.residual) load_segment<EPT>(c.prow, p.bf16, p.vec, p.V, s, tid, zp);
     double ws = 0.0, qs = 0.0;
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {

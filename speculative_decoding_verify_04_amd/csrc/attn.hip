@@ -1072,21 +1072,26 @@ __global__ __launch_bounds__(1024) void prefix_bf16_kernel(AttnParams p) {
             }
             mt = colmax4(mt);
             const float mnew = fmaxf(mrun, mt);   // finite: every half computed has a valid key
-            const float alpha = exp2f(mrun - mnew);
+            // no column of the tile raised its running max: alpha is exactly 1
+            // on every lane and the rescale of O is skipped
+            const bool grew = __ballot(mt > mrun) != 0;
+            const float alpha = grew ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
             float ps = 0.0f;
             shortx4 pb[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float pe = exp2f(acc[kt][e] - mnew);
+                    const float pe = __builtin_amdgcn_exp2f(acc[kt][e] - mnew);
                     ps += pe;
                     pb[kt][e] = static_cast<short>(f32_to_bf16(pe));
                 }
             lrun = lrun * alpha + ps;
             mrun = mnew;
+            if (grew) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+                for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+            }
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
                 // V^T operands of 16 keys: lane (d = dt*16 + col16) gets keys
@@ -1269,32 +1274,49 @@ __global__ __launch_bounds__(1024) void prefix_dma_kernel(AttnParams p) {
             }
             mt = colmax4(mt);
             const float mnew = fmaxf(mrun, mt);   // finite: every half computed has a valid key
-            const float alpha = exp2f(mrun - mnew);
+            // no column of the tile raised its running max: alpha is exactly 1
+            // on every lane and the rescale of O is skipped
+            const bool grew = __ballot(mt > mrun) != 0;
+            const float alpha = grew ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.0f;
             float ps = 0.0f;
             shortx4 pb[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float pe = exp2f(acc[kt][e] - mnew);
+                    const float pe = __builtin_amdgcn_exp2f(acc[kt][e] - mnew);
                     ps += pe;
                     pb[kt][e] = static_cast<short>(f32_to_bf16(pe));
                 }
             lrun = lrun * alpha + ps;
             mrun = mnew;
+            if (grew) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+                for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+            }
+            // O^T += V^T P^T over 32 keys per product (v_mfma_f32_16x16x32_bf16):
+            // key tiles kt and kt+1 form the K dimension, lane group kg
+            // supplying keys kt*16 + kg*4 + 0..3 then (kt+1)*16 + kg*4 + 0..3 on
+            // both operands (the same order, so every key is summed once)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                const uint16_t* vr = vb + (half * 64 + kt * 16) * D + vcol;
+            for (int kt = 0; kt < 4; kt += 2) {
+                const uint16_t* vr0 = vb + (half * 64 + kt * 16) * D + vcol;
+                const uint16_t* vr1 = vr0 + 16 * D;
+                const bf16x8 pk = __builtin_bit_cast(
+                    bf16x8, (shortx8{pb[kt][0], pb[kt][1], pb[kt][2], pb[kt][3], pb[kt + 1][0], pb[kt + 1][1],
+                                     pb[kt + 1][2], pb[kt + 1][3]}));
 #pragma unroll
                 for (int d0 = 0; d0 < DT; d0 += 4) {
-                    shortx4 va[4];
+                    bf16x8 va[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) va[u] = lds_read_tr16(vr + 16 * ((d0 + u) ^ sv1));
+                    for (int u = 0; u < 4; ++u) {
+                        const shortx4 a0 = lds_read_tr16(vr0 + 16 * ((d0 + u) ^ sv1));
+                        const shortx4 a1 = lds_read_tr16(vr1 + 16 * ((d0 + u) ^ sv1));
+                        va[u] = __builtin_bit_cast(bf16x8, (shortx8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}));
+                    }
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        o[d0 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[u], pb[kt], o[d0 + u], 0, 0, 0);
+                        o[d0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], pk, o[d0 + u], 0, 0, 0);
                 }
             }
         }
