@@ -225,6 +225,23 @@ __device__ __forceinline__ void load_segment(const void* row, int bf16, int vec,
         load4(row, bf16, vec, V, e0 + g * 1024 + tid * 4, z + 4 * g);
 }
 
+// A whole fp32 segment with vector loads and no branch: the loads of both
+// rows of a unit are then in flight together, and the first row's use waits
+// for its own loads only (for rows whose vocabulary is a whole number of
+// segments).
+template <int EPT>
+__device__ __forceinline__ void seg_load_f32(const void* row, int s, int tid, float* z) {
+    const float4* r4 = reinterpret_cast<const float4*>(static_cast<const float*>(row) + s * (kThreads * EPT)) + tid;
+#pragma unroll
+    for (int g = 0; g < EPT / 4; ++g) {
+        const float4 f = r4[g * kThreads];
+        z[4 * g + 0] = f.x;
+        z[4 * g + 1] = f.y;
+        z[4 * g + 2] = f.z;
+        z[4 * g + 3] = f.w;
+    }
+}
+
 __device__ __forceinline__ const void* row_ptr(const AcceptParams& p, int r) {
     const size_t es = p.bf16 ? 2 : 4;
     if (r < p.nt) return static_cast<const char*>(p.target) + static_cast<size_t>(r) * p.V * es;
@@ -333,13 +350,18 @@ struct MergeLds {
     double tab[256];
     union {
         RowPart r[2];
-        double wdraw[kHalf * kSlots];  // draw: the chosen weight of every list slot, id order
+        struct {                       // draw: the kept target entries in id order
+            float z[kHalf * kSlots];   // target logit
+            float zp[kHalf * kSlots];  // draft logit at the same id
+            int id[kHalf * kSlots];
+        } dk;
     };
     struct {                        // radix select over a whole row
         double rh_m[256];
         int rh_c[256];
     } rad;
     double ta[kMThreads / 64];      // per-wave scan totals
+    int dcnt[kSlots][kRW];          // draw: kept entries per (slot index, target wave)
     double tb[kMThreads / 64];
     uint32_t prefix, mask;
     int chosen, abovec;
@@ -750,37 +772,65 @@ __device__ __forceinline__ void subbin_threshold(const AcceptParams& p, const un
                 R.kept = at;
             }
         } else {
-            // several values in the crossing sub-bin: this wave gathers its
-            // entries (indices into rk) and sums each one's tie-inclusive mass
+            // several values in the crossing sub-bin: this wave compacts its
+            // entries (z and weight, in gather order) to the front of rz/rw
+            // -- a slot is written only after the read of every slot up to
+            // it -- and sums each one's tie-inclusive mass
             const int starsb = kSub - 1 - star;
             int m = 0;
-            for (int c0 = 0; c0 < n; c0 += 64) {
-                const int i = c0 + lane;
-                bool in = false;
-                if (i < n) {
-                    const float zi = R.rk.rz[i];
-                    in = sub_bin(__builtin_amdgcn_fmed3f(zi * p.qscale, -1.0e9f, 1.0e9f), sel) == starsb;
+            for (int c0 = 0; c0 < n; c0 += 256) {
+                float zq[4];
+                double wq[4];
+#pragma unroll
+                for (int h2 = 0; h2 < 4; ++h2) {  // the reads of four chunks at once (clamped ids)
+                    const int i = min(c0 + 64 * h2 + lane, kCap - 1);
+                    zq[h2] = R.rk.rz[i];
+                    wq[h2] = R.rk.rw[i];
                 }
-                const unsigned long long bc = __ballot(in);
-                if (in) {
-                    const int at2 = m + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
-                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
-                    R.rk.ck[at2] = static_cast<unsigned long long>(i);
+#pragma unroll
+                for (int h2 = 0; h2 < 4; ++h2) {
+                    const int i = c0 + 64 * h2 + lane;
+                    const bool in = i < n &&
+                                    sub_bin(__builtin_amdgcn_fmed3f(zq[h2] * p.qscale, -1.0e9f, 1.0e9f), sel) ==
+                                        starsb;
+                    const unsigned long long bc = __ballot(in);
+                    if (in) {
+                        const int at2 = m + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
+                        R.rk.rz[at2] = zq[h2];
+                        R.rk.rw[at2] = wq[h2];
+                    }
+                    m += __popcll(bc);
                 }
-                m += __popcll(bc);
             }
-            // the indices written by other lanes of this wave are read next
+            // the entries written by other lanes of this wave are read next
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // each lane's tie-inclusive mass sums the entries in gather order;
+            // they are held 64 at a time in registers and broadcast lane by
+            // lane (no LDS round trip per term)
             float best = -INFINITY, lowest = INFINITY;
+            float zown = -INFINITY;  // this lane's entry when m <= 64
+            double wown = 0.0;
             for (int c0 = 0; c0 < m; c0 += 64) {
                 const int a2 = c0 + lane;
-                const float zi = a2 < m ? R.rk.rz[static_cast<int>(R.rk.ck[a2])] : INFINITY;
+                const float zi = a2 < m ? R.rk.rz[a2] : INFINITY;
                 double g = 0.0;
-                for (int jj = 0; jj < m; ++jj) {
-                    const int ij = static_cast<int>(R.rk.ck[jj]);
-                    g += (R.rk.rz[ij] >= zi) ? R.rk.rw[ij] : 0.0;
+                for (int c1 = 0; c1 < m; c1 += 64) {
+                    const int b2 = c1 + lane;
+                    const float zb = b2 < m ? R.rk.rz[b2] : -INFINITY;
+                    const double wb = b2 < m ? R.rk.rw[b2] : 0.0;
+                    if (c0 == 0 && c1 == 0) {
+                        zown = zb;
+                        wown = wb;
+                    }
+                    const int nn = min(64, m - c1);
+                    for (int jj = 0; jj < nn; ++jj) {
+                        const float zj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zb), jj));
+                        const double wj = lane_read_d(wb, jj);
+                        g += (zj >= zi) ? wj : 0.0;
+                    }
                 }
                 if (a2 < m) {
                     lowest = fminf(lowest, zi);
@@ -791,11 +841,12 @@ __device__ __forceinline__ void subbin_threshold(const AcceptParams& p, const un
             lowest = -wave_max(-lowest);
             const float tau = (best != -INFINITY) ? best : lowest;
             double part = 0.0;
-            for (int c0 = 0; c0 < m; c0 += 64) {
-                const int a2 = c0 + lane;
-                if (a2 < m) {
-                    const int ia = static_cast<int>(R.rk.ck[a2]);
-                    part += (R.rk.rz[ia] >= tau) ? R.rk.rw[ia] : 0.0;
+            if (m <= 64) {  // uniform
+                part = (zown >= tau) ? wown : 0.0;
+            } else {
+                for (int c0 = 0; c0 < m; c0 += 64) {
+                    const int a2 = c0 + lane;
+                    if (a2 < m) part += (R.rk.rz[a2] >= tau) ? R.rk.rw[a2] : 0.0;
                 }
             }
             part = wave_sum(part);
@@ -858,87 +909,184 @@ __device__ __forceinline__ void block_excl_scan2(double a, double b, double* sa,
     *eb = ob + ib - b;
 }
 
+// The accept test's inputs: the unit's row records, read by one thread into
+// registers (the draw reuses their LDS).
+struct AcceptIn {
+    float zq, mq, tq;   // target row: drafted logit, max, filter threshold
+    float zp, mp, tp;   // draft row
+    double Sq, Sp;      // kept masses relative to the maxima
+    int fq, fp;         // the lists decided the kept sets
+    float ua;           // u_accept of the unit
+};
+
+__device__ __forceinline__ AcceptIn accept_in(const MergeLds& L) {
+    const RowPart& T = L.r[0];
+    const RowPart& D = L.r[1];
+    return AcceptIn{T.zx, T.m, T.tau, D.zx, D.m, D.tau, T.kept, D.kept, T.fast, D.fast, L.ua};
+}
+
+// The accept test of x_j (one thread): q'_j(x) = w_x / kept mass if x is
+// kept, else 0; accept iff u * p' < q' (p' = 0: iff q' > 0).  Also stores
+// the unit's row records.
+__device__ __forceinline__ bool accept_decide(const AcceptParams& p, const AcceptIn& a, int u, int dr, int j,
+                                              int kb, bool x_ok, const double* tab) {
+    bool acc = true;
+    const bool tk = x_ok && j < kb && a.zq >= a.tq;
+    const double wxq = (x_ok && j < kb) ? weight(a.zq, a.mq, p.yscale, tab) : 0.0;
+    RowRec* tr = p.rows + u;
+    st_coh(&tr->m, a.mq);
+    st_coh(&tr->tau, a.tq);
+    st_coh(&tr->S, a.Sq);
+    st_coh(&tr->wx, wxq);
+    st_coh(&tr->kept, tk ? 1 : 0);
+    st_coh(&tr->fast, a.fq);
+    if (j < kb) {
+        const bool dk = x_ok && a.zp >= a.tp;
+        const double wxp = x_ok ? weight(a.zp, a.mp, p.yscale, tab) : 0.0;
+        RowRec* drr = p.rows + dr;
+        st_coh(&drr->m, a.mp);
+        st_coh(&drr->tau, a.tp);
+        st_coh(&drr->S, a.Sp);
+        st_coh(&drr->wx, wxp);
+        st_coh(&drr->kept, dk ? 1 : 0);
+        st_coh(&drr->fast, a.fp);
+        if (!x_ok) set_status(p.status, 1);
+        const double q = tk ? wxq / a.Sq : 0.0;
+        const double pp = dk ? wxp / a.Sp : 0.0;
+        if (!(a.ua >= 0.0f && a.ua < 1.0f)) set_status(p.status, 2);
+        acc = (pp > 0.0) ? (static_cast<double>(a.ua) * pp < q) : (q > 0.0);
+    }
+    return acc;
+}
+
+// The accept test on thread 0; every thread returns the decision.
+__device__ __forceinline__ bool accept_test(const AcceptParams& p, int u, int dr, int j, int kb, bool x_ok,
+                                            MergeLds& L) {
+    if (threadIdx.x == 0) L.acc = accept_decide(p, accept_in(L), u, dr, j, kb, x_ok, L.tab) ? 1 : 0;
+    __syncthreads();
+    return L.acc != 0;
+}
+
+// Block-wide exclusive scan of one double per thread in thread order (fixed
+// order); sa holds the per-wave totals.  The caller has passed a barrier since
+// sa was last read.
+__device__ __forceinline__ void block_excl_scan1(double a, double* sa, double* ea, double* ta) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const double ia = wave_incl_scan(a, lane);
+    if (lane == 63) sa[wv] = ia;
+    __syncthreads();
+    double oa = 0.0, xa = 0.0;
+#pragma unroll
+    for (int u = 0; u < kMThreads / 64; ++u) {
+        const double va = sa[u];
+        if (u < wv) oa += va;
+        xa += va;
+    }
+    *ta = xa;
+    *ea = oa + ia - a;
+}
+
 // Token drawn by a unit from its target row's lists (every thread returns it;
 // -1 when the residual has no mass).
 // The target half's thread rt holds flat slots rt + kHalf*i (coalesced
-// loads); members are valid slots with z >= tau_q, each with its draft logit
-// in zpv.  The draw weights -- (q' - p')_+, or q' when that has no mass -- go
-// to LDS in flat slot order, which is id order; runs of consecutive slots are
-// summed and scanned over the threads, the run holding the crossing is
-// walked, and the slot's owner supplies its id.
+// loads), so the order (i, wave, lane) is id order.  The kept entries (valid
+// slots with z >= tau_q: q' and (q' - p')_+ vanish elsewhere) are compacted
+// in that order with their draft logits; the whole workgroup then takes runs
+// of consecutive entries, computes the draw weights -- (q' - p')_+, or q'
+// for the bonus row -- sums and scans the runs, and the run holding the
+// crossing is walked.  The accept test of the unit's draft runs inside, on
+// the last thread (ai holds its inputs there), and leaves its decision in
+// L.acc; the draw is made whatever the decision.
 __device__ __forceinline__ int draw_from_lists(const AcceptParams& p, const DrawRows& R, bool residual,
                                                float us, const unsigned long long (&e)[kSlots],
-                                               const float (&zpv)[kSlots], unsigned vmask, int nslots,
-                                               MergeLds& L) {
-    const int tid = threadIdx.x, lane = tid & 63;
+                                               const float (&zpv)[kSlots], unsigned vmask, const AcceptIn& ai,
+                                               int u, int dr, int j, int kb, bool x_ok, MergeLds& L) {
+    static_assert(kHalf * kSlots <= 4 * kMThreads, "at most four kept entries per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const bool tg = tid < kHalf;
+    unsigned long long bal[kSlots];
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i)
+        bal[i] = __ballot(tg && ((vmask >> i) & 1u) && entry_z(e[i]) >= R.tq);
+    if (tg && lane == 0) {
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) L.dcnt[i][wv] = __popcll(bal[i]);
+    }
     if (tid == 0) {
         L.fstar = 0x7FFFFFFF;
         L.lastpos = -1;
         if (!(us >= 0.0f && us < 1.0f)) set_status(p.status, 2);
     }
-    // every thread holds its row parameters in R: the weights may overwrite
-    // the row records (they share LDS)
+    // every thread holds its row parameters (R, ai) in registers: the kept
+    // entries overwrite the row records (they share LDS)
     __syncthreads();
-    int anyd = 0;
+    // offsets of the kept entries: one wave scan over the counts in (slot
+    // index, wave) order, each wave reads its own eight
+    static_assert(kSlots * kRW == 64, "one count per lane");
+    const int cnt = (&L.dcnt[0][0])[lane];
+    const int inc = wave_incl_scan(cnt, lane);
+    const int n = __builtin_amdgcn_readlane(inc, 63);
+    const int exc = inc - cnt;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    int base[kSlots];
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) base[i] = __builtin_amdgcn_readlane(exc, i * kRW + (wvu & (kRW - 1)));
     if (tg) {
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
-            const int f = tid + kHalf * i;
-            const bool mem = ((vmask >> i) & 1u) && entry_z(e[i]) >= R.tq;
-            double d, q;
-            pair_weights(R, residual, entry_z(e[i]), zpv[i], mem, p.yscale, L.tab, &d, &q);
-            anyd |= (d > 0.0) ? 1 : 0;
-            if (f < nslots) L.wdraw[f] = d;
+            const unsigned long long bc = bal[i];
+            if ((bc >> lane) & 1ull) {
+                const int c = base[i] + __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(bc >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(bc), 0));
+                L.dk.z[c] = entry_z(e[i]);
+                L.dk.zp[c] = zpv[i];
+                L.dk.id[c] = entry_id(e[i]);
+            }
         }
     }
+    __syncthreads();
+    // runs of E consecutive kept entries (E <= 4), weights summed in id order
+    const int E = (n + kMThreads - 1) / kMThreads;
+    const int c0 = min(tid * E, n), c1 = min(c0 + E, n);
+    double w[4];
+    double mine = 0.0;
+    int lastc = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = c0 + k;
+        double d = 0.0, q;
+        if (c < c1) pair_weights(R, residual, L.dk.z[c], L.dk.zp[c], true, p.yscale, L.tab, &d, &q);
+        w[k] = d;
+        mine += d;
+        if (d > 0.0) lastc = c;
+    }
+    if (tid == kMThreads - 1) L.acc = accept_decide(p, ai, u, dr, j, kb, x_ok, L.tab) ? 1 : 0;
+    double rx, tot;
+    block_excl_scan1(mine, L.ta, &rx, &tot);
     // the residual has mass (it can lack it through rounding only: then the
     // caller draws from q' over the whole row)
-    if (residual && !__syncthreads_or(anyd)) return -1;  // uniform
-    __syncthreads();
-    // runs of E2 consecutive slots per target thread, summed in slot order
-    const int E2 = (nslots + kHalf - 1) / kHalf;
-    const int f0 = tg ? min(tid * E2, nslots) : nslots;
-    const int f1 = tg ? min(f0 + E2, nslots) : nslots;
-    double mine = 0.0;
-    int lastf = -1;
-    for (int f = f0; f < f1; ++f) {
-        const double w = L.wdraw[f];
-        mine += w;
-        if (w > 0.0) lastf = f;
-    }
-    double rx, zx, tot, tz;
-    block_excl_scan2(mine, 0.0, L.ta, L.tb, &rx, &zx, &tot, &tz);
+    if (residual && !(tot > 0.0)) return -1;  // uniform
     const double target = static_cast<double>(us) * tot;
     if ((mine > 0.0) & (rx <= target) & (target < rx + mine)) {
         double run = rx;
         int hit = -1;
-        for (int f = f0; f < f1 && hit < 0; ++f) {
-            const double w = L.wdraw[f];
-            if (w > 0.0) {
-                run += w;
-                if (target < run) hit = f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (hit < 0 && w[k] > 0.0) {
+                run += w[k];
+                if (target < run) hit = c0 + k;
             }
         }
         if (hit >= 0) L.fstar = hit;
     }
-    // the last slot of positive weight (rounding left the target past every
-    // prefix); slots grow with the thread, so one atomic per wave
-    const unsigned long long hasl = __ballot(lastf >= 0);
-    if (hasl && lane == 63 - __clzll(hasl)) atomicMax(&L.lastpos, lastf);
+    // the last entry of positive weight (rounding left the target past every
+    // prefix); entries grow with the thread, so one atomic per wave
+    const unsigned long long hasl = __ballot(lastc >= 0);
+    if (hasl && lane == 63 - __clzll(hasl)) atomicMax(&L.lastpos, lastc);
     __syncthreads();
     const int fs = (L.fstar != 0x7FFFFFFF) ? L.fstar : L.lastpos;
     if (fs < 0) return 0;  // uniform: no mass at all
-    if (tid == (fs & (kHalf - 1))) {
-        const int ii = fs / kHalf;
-        int id = 0;
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i)
-            if (i == ii) id = entry_id(e[i]);
-        L.tok = id;
-    }
-    __syncthreads();
-    return L.tok;
+    return L.dk.id[fs];
 }
 
 // Token drawn from the unit's target row by one pass over the whole row
@@ -1160,47 +1308,6 @@ __device__ __forceinline__ void sequence_arrival(const AcceptParams& p, int u, i
     if (p.compact && has_tok) compact_sequence<kMThreads>(p, b, q0, n, &L.cflag, L.cscan);
 }
 
-// Row records of the unit's rows and the accept test of x_j (thread 0; every
-// thread returns the decision): q'_j(x) = w_x / kept mass if x is kept, else 0;
-// accept iff u * p' < q' (p' = 0: iff q' > 0).
-__device__ __forceinline__ bool accept_test(const AcceptParams& p, int u, int dr, int j, int kb, bool x_ok,
-                                            MergeLds& L) {
-    const RowPart& T = L.r[0];
-    const RowPart& D = L.r[1];
-    if (threadIdx.x == 0) {
-        bool acc = true;
-        const bool tk = x_ok && j < kb && T.zx >= T.tau;
-        const double wxq = (x_ok && j < kb) ? weight(T.zx, T.m, p.yscale, L.tab) : 0.0;
-        RowRec* tr = p.rows + u;
-        st_coh(&tr->m, T.m);
-        st_coh(&tr->tau, T.tau);
-        st_coh(&tr->S, T.kept);
-        st_coh(&tr->wx, wxq);
-        st_coh(&tr->kept, tk ? 1 : 0);
-        st_coh(&tr->fast, T.fast);
-        if (j < kb) {
-            const bool dk = x_ok && D.zx >= D.tau;
-            const double wxp = x_ok ? weight(D.zx, D.m, p.yscale, L.tab) : 0.0;
-            RowRec* drr = p.rows + dr;
-            st_coh(&drr->m, D.m);
-            st_coh(&drr->tau, D.tau);
-            st_coh(&drr->S, D.kept);
-            st_coh(&drr->wx, wxp);
-            st_coh(&drr->kept, dk ? 1 : 0);
-            st_coh(&drr->fast, D.fast);
-            if (!x_ok) set_status(p.status, 1);
-            const double q = tk ? wxq / T.kept : 0.0;
-            const double pp = dk ? wxp / D.kept : 0.0;
-            const float ua = L.ua;
-            if (!(ua >= 0.0f && ua < 1.0f)) set_status(p.status, 2);
-            acc = (pp > 0.0) ? (static_cast<double>(ua) * pp < q) : (q > 0.0);
-        }
-        L.acc = acc ? 1 : 0;
-    }
-    __syncthreads();
-    return L.acc != 0;
-}
-
 __device__ __forceinline__ DrawRows draw_rows(const MergeLds& L, bool residual) {
     const RowPart& T = L.r[0];
     const RowPart& D = L.r[1];
@@ -1289,24 +1396,14 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
     unsigned long long e[kSlots];
     float zpv[kSlots];
 
-    // ---- one round trip: the list slots of this thread (coalesced: slot
-    // rt + kHalf*i), segment heads, listed bin masses and counts, the drafted
-    // logit, the uniforms.  The segment kernel wrote them; this launch reads
-    // them with plain loads.  Every load is issued before the first LDS store.
+    // ---- one round trip: segment heads, listed bin masses and counts, the
+    // drafted logit, the uniforms, then the list slots of this thread
+    // (coalesced: slot rt + kHalf*i).  The segment kernel wrote them; this
+    // launch reads them with plain loads.  Every load is issued before the
+    // first LDS store; the list slots, issued last and first used by the
+    // boundary-bin gather, arrive while the row statistics are formed.
     constexpr int kBmIter = (kListSegMax * kQB + kHalf - 1) / kHalf;
     static_assert(kMaxSeg <= kHalf, "one segment head per thread");
-    {
-        const unsigned long long* lb = p.list + static_cast<size_t>(row) * nslots;
-        const float* zb = p.lzp + static_cast<size_t>(u) * nslots;
-        const bool ldz = lists && rr == 0 && has_d;
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
-            const int f = rt + kHalf * i;
-            const bool in = lists && act && f < nslots;
-            e[i] = in ? lb[f] : 0ull;
-            zpv[i] = (in && ldz) ? zb[f] : 0.0f;
-        }
-    }
     SegHead h{};
     double bmv[kBmIter];
     int bcv[kBmIter];
@@ -1330,6 +1427,18 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
                                          : p.zx[row]);
     const float uav = (tid == kMThreads - 1 && j < kb) ? p.u_accept[u - b] : 0.0f;
     const float usv = (tid == kMThreads - 1) ? p.u_sample[b] : 0.0f;
+    {
+        const unsigned long long* lb = p.list + static_cast<size_t>(row) * nslots;
+        const float* zb = p.lzp + static_cast<size_t>(u) * nslots;
+        const bool ldz = lists && rr == 0 && has_d;
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const int f = rt + kHalf * i;
+            const bool in = lists && act && f < nslots;
+            e[i] = in ? lb[f] : 0ull;
+            zpv[i] = (in && ldz) ? zb[f] : 0.0f;
+        }
+    }
     if (act) {
         if (rt < p.nseg) {
             R.seg_m[rt] = h.m;
@@ -1354,18 +1463,6 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
     }
     fill_exp_table(L.tab);
     __syncthreads();
-
-    // valid slots of this thread: slot < its segment's list length
-    unsigned vmask = 0u;
-    if (lists && act) {
-#pragma unroll
-        for (int i = 0; i < kSlots; ++i) {
-            const int f = rt + kHalf * i;
-            int sg, o;
-            slot_pos(f, p.klist, &sg, &o);
-            if (f < nslots && o < R.seg_n[min(sg, kMaxSeg - 1)]) vmask |= 1u << i;
-        }
-    }
 
     // ---- row max, normaliser and bin masses in one step: every wave of a row
     // finds the row max and the segment scales exp((m_s - m)/T) itself (lane
@@ -1470,6 +1567,17 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
         __syncthreads();
     }
 
+    // valid slots of this thread: slot < its segment's list length
+    unsigned vmask = 0u;
+    if (lists && act) {
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const int f = rt + kHalf * i;
+            int sg, o;
+            slot_pos(f, p.klist, &sg, &o);
+            if (f < nslots && o < R.seg_n[min(sg, kMaxSeg - 1)]) vmask |= 1u << i;
+        }
+    }
     if (lists) {
         // ---- the first wave of a row adds the partial bin masses in a fixed
         // order and finds the first boundary bin (the top-k count boundary, or
@@ -1587,24 +1695,37 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
         sequence_arrival(p, u, b, q0, kb, j, (j < kb) && !acc, need, token, true, L);
         return;
     }
-    const bool acc = accept_test(p, u, dr, j, kb, x_ok, L);
-    const bool need = (j == kb) || !acc;
-    int token = -1;
-    if (p.filter && need) {  // uniform
+    if (lists) {  // uniform: the lists hold both rows' kept sets
+        // the draw -- needed after a rejection, or for the bonus row -- is
+        // made together with the accept test instead of after it
         const bool residual = j < kb;
         const DrawRows Rw = draw_rows(L, residual);
-        token = lists ? draw_from_lists(p, Rw, residual, L.us, e, zpv, vmask, nslots, L) : -1;
-        if (token < 0) {  // uniform: beyond the list path, or no residual mass
+        AcceptIn ai{};
+        if (tid == kMThreads - 1) ai = accept_in(L);
+        int token = draw_from_lists(p, Rw, residual, L.us, e, zpv, vmask, ai, u, dr, j, kb, x_ok, L);
+        const bool acc = L.acc != 0;
+        const bool need = (j == kb) || !acc;
+        if (need && token < 0) {  // uniform: no residual mass
             const FullRow fr{row_ptr(p, u), row_ptr(p, residual ? dr : u), p.status, p.V, p.bf16, p.yscale};
             token = draw_full_row(fr, Rw, residual, L.us, L);
         }
+        sequence_arrival(p, u, b, q0, kb, j, (j < kb) && !acc, need, token, true, L);
+        return;
+    }
+    const bool acc = accept_test(p, u, dr, j, kb, x_ok, L);
+    const bool need = (j == kb) || !acc;
+    int token = -1;
+    if (p.filter && need) {  // uniform: beyond the list path
+        const bool residual = j < kb;
+        const FullRow fr{row_ptr(p, u), row_ptr(p, residual ? dr : u), p.status, p.V, p.bf16, p.yscale};
+        token = draw_full_row(fr, draw_rows(L, residual), residual, L.us, L);
     }
     sequence_arrival(p, u, b, q0, kb, j, (j < kb) && !acc, p.filter && need, token, p.filter != 0, L);
 }
 
 // ---------------------------------------------------------------- segment kernel
 
-template <int EPT>
+template <int EPT, bool FAST>
 __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
     __shared__ SegLds L;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -1627,36 +1748,23 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
     const int q0 = seq_q0(p, b), kb = seq_kb(p, b), j = u - q0;
     const bool has_d = !p.greedy && j < kb;
     const int dr = p.nt + u - b;
+    // both rows' loads at once (a bonus unit reads its target segment twice,
+    // the second time from cache); with FAST the target row is used while the
+    // draft row's loads are still in flight
     float z[2][EPT];
-    load_segment<EPT>(row_ptr(p, u), p.bf16, p.vec, p.V, s, tid, z[0]);
-    if (has_d) {
-        load_segment<EPT>(row_ptr(p, dr), p.bf16, p.vec, p.V, s, tid, z[1]);
+    if constexpr (FAST) {
+        seg_load_f32<EPT>(row_ptr(p, u), s, tid, z[0]);
+        seg_load_f32<EPT>(row_ptr(p, has_d ? dr : u), s, tid, z[1]);
     } else {
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) z[1][k] = -INFINITY;
+        load_segment<EPT>(row_ptr(p, u), p.bf16, p.vec, p.V, s, tid, z[0]);
+        load_segment<EPT>(row_ptr(p, has_d ? dr : u), p.bf16, p.vec, p.V, s, tid, z[1]);
     }
     fill_exp_table(L.tab);
     // the segment counters start at zero (ordered before use by the first barrier)
     for (int i = tid; i < 2 * 4 * (kQB + 64); i += kThreads) (&L.hc[0][0][0])[i] = 0;
     for (int i = tid; i < 2 * kQB; i += kThreads) (&L.hm[0][0])[i] = 0.0;
-    // the drafted token's logits, stored by the thread that holds them
-    // (element k of thread t has id seg_lo + (k/4)*1024 + 4*t + k%4)
     const int x = (j < kb) ? p.draft_tokens[u - b] : -1;
     const int seg_lo = s * kThreads * EPT;
-    if (!p.greedy && x >= seg_lo && x < seg_lo + kThreads * EPT && x < p.V) {
-        const int off = x - seg_lo;
-        const int kx = ((off >> 10) << 2) | (off & 3);
-        if (tid == ((off & 1023) >> 2)) {
-            float zq = 0.0f, zp = 0.0f;
-#pragma unroll
-            for (int k = 0; k < EPT; ++k) {
-                zq = (k == kx) ? z[0][k] : zq;
-                zp = (k == kx) ? z[1][k] : zp;
-            }
-            p.zx[u] = zq;
-            if (has_d) p.zx[dr] = zp;
-        }
-    }
 
     if (p.greedy) {
         float bv = -INFINITY;
@@ -1692,27 +1800,12 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
             h->top = bi;
         }
     } else {
-        float lm[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int k = 0; k < EPT; ++k) lm[r] = fmaxf(lm[r], z[r][k]);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            lm[r] = wave_max(lm[r]);
-            if (lane == 0) L.red_f[r][wv] = lm[r];
-        }
-        __syncthreads();
-        float ms[2];
+        // row by row: the segment max, then one pass per element: the fp64
+        // weight (a row max of -inf gives NaN arguments, which exp2_256 maps
+        // to 0) and, with a filter on, the bin offset (kept) and its count.
+        // The target row is done while the draft row's loads are in flight.
+        float ms[2] = {-INFINITY, -INFINITY};
         int top[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            ms[r] = fmaxf(fmaxf(L.red_f[r][0], L.red_f[r][1]), fmaxf(L.red_f[r][2], L.red_f[r][3]));
-            top[r] = qbin(ms[r], p.qscale);
-        }
-        // one pass per element: the fp64 weight (a row max of -inf gives NaN
-        // arguments, which exp2_256 maps to 0) and, with a filter on, the bin
-        // offset (kept) and its count
         double acc[2] = {0.0, 0.0};
         unsigned ow[2][EPT / 4];  // bin offsets (0..kQB-1 in the window, kQB.. below it), four per word
         const unsigned past = static_cast<unsigned>(kQB + lane);
@@ -1720,7 +1813,20 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
         for (int r = 0; r < 2; ++r) {
 #pragma unroll
             for (int g = 0; g < EPT / 4; ++g) ow[r][g] = 0u;  // row 1 without a draft: never listed (ocut -1)
+            top[r] = qbin(ms[r], p.qscale);
+            if (r == 1) {
+#pragma unroll
+                for (int k = 0; k < EPT; ++k) z[1][k] = has_d ? z[1][k] : -INFINITY;
+            }
             if (r == 1 && !has_d) continue;  // uniform
+            float lm = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) lm = fmaxf(lm, z[r][k]);
+            lm = wave_max(lm);
+            if (lane == 0) L.red_f[r][wv] = lm;
+            __syncthreads();
+            ms[r] = fmaxf(fmaxf(L.red_f[r][0], L.red_f[r][1]), fmaxf(L.red_f[r][2], L.red_f[r][3]));
+            top[r] = qbin(ms[r], p.qscale);
             const double mr = static_cast<double>(ms[r]);
             if (p.filter) {  // uniform
 #pragma unroll
@@ -1741,6 +1847,22 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
                     acc[r] += exp2_256((static_cast<double>(z[r][k]) - mr) * p.yscale, L.tab);
                     if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
                 }
+            }
+        }
+        // the drafted token's logits, stored by the thread that holds them
+        // (element k of thread t has id seg_lo + (k/4)*1024 + 4*t + k%4)
+        if (x >= seg_lo && x < seg_lo + kThreads * EPT && x < p.V) {
+            const int off = x - seg_lo;
+            const int kx = ((off >> 10) << 2) | (off & 3);
+            if (tid == ((off & 1023) >> 2)) {
+                float zq = 0.0f, zp = 0.0f;
+#pragma unroll
+                for (int k = 0; k < EPT; ++k) {
+                    zq = (k == kx) ? z[0][k] : zq;
+                    zp = (k == kx) ? z[1][k] : zp;
+                }
+                p.zx[u] = zq;
+                if (has_d) p.zx[dr] = zp;
             }
         }
 #pragma unroll
@@ -2123,10 +2245,11 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     hipError_t err = hipSuccess;
     if (!p.prestats) {  // the LM head's statistics replace the segment pass
         const dim3 grid(p.grid_units * p.nseg);
-        if (ept == 16)
-            hipLaunchKernelGGL(segment_kernel<16>, grid, dim3(kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL(segment_kernel<12>, grid, dim3(kThreads), 0, stream, p);
+        // every segment whole, fp32, vector loads: the branch-free load form
+        const bool fast = !p.bf16 && p.vec && a.V % (kThreads * ept) == 0;
+        void (*kern)(AcceptParams) = (ept == 16) ? (fast ? segment_kernel<16, true> : segment_kernel<16, false>)
+                                                 : (fast ? segment_kernel<12, true> : segment_kernel<12, false>);
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, p);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
