@@ -30,6 +30,18 @@
 //   consecutive on one XCD, so the part's weight slice is fetched from HBM
 //   once and served to the other row blocks from that XCD's L2.  The weight
 //   matrix is streamed once; the hidden rows stay in L2.
+//   This form suits decode-sized row counts (the weight stream bounds it).
+//
+// lm_gemm_kernel: more rows, where the products bound the call.  One
+//   workgroup (4 waves) per (block of 192 rows, tile of 128 ids = two
+//   statistics parts); both operands pass through LDS in 32-wide steps of the
+//   hidden dimension, three stages deep (direct 16-byte global-to-LDS loads,
+//   one barrier per step), so each weight and hidden element read from L2 or
+//   HBM feeds 128 or 192 products instead of 64.  Wave (wr, wn) computes rows
+//   96 wr .. +96 and ids 64 wn .. +64 of the tile: 24 products
+//   v_mfma_f32_16x16x32_bf16 per step, the weight tile as A, the hidden rows
+//   as B, as above.  Each wave then holds whole statistics parts of its rows,
+//   so the epilogue needs no exchange between waves.
 #include "sv_device.h"
 #include "sv_internal.h"
 #include "sv_math.h"
@@ -227,6 +239,163 @@ void launch_nr(const LmParams& p, int blocks, hipStream_t stream) {
     hipLaunchKernelGGL((lm_head_kernel<NR, KU>), dim3(blocks), dim3(kThreads), 0, stream, p);
 }
 
+constexpr int kGM = 192;       // rows per workgroup tile
+constexpr int kGN = 128;       // ids per workgroup tile (two statistics parts)
+constexpr int kGK = 32;        // hidden-dimension step: one 16x16x32 product
+constexpr int kSmallRows = 64; // up to this many rows: lm_head_kernel
+
+// One stage of both operand tiles: rows of 32 bf16 (four 16-byte chunks);
+// chunk c of row r is stored at c ^ ((r >> 2) & 3), so that the 16-byte
+// operand reads of 16 consecutive rows fall on distinct banks.
+struct GemmStage {
+    uint4 h[kGM * kGK / 8];  // hidden rows of the block (12 KiB)
+    uint4 w[kGN * kGK / 8];  // weight rows of the tile (8 KiB)
+};
+
+__global__ __launch_bounds__(kThreads, 2) void lm_gemm_kernel(LmParams p, int ntiles) {
+    // three separate LDS objects: the compiler's wait for one stage's direct
+    // loads then does not cover the others
+    __shared__ GemmStage G0, G1, G2;
+    __shared__ double tab[256];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col16 = lane & 15, kg = lane >> 4;
+    const int wr = w >> 1, wn = w & 1;
+    // XCD-aware order: the row blocks of an id tile are consecutive on one XCD
+    const int L = blockIdx.x;
+    const int xcd = L % kXcd, i = L / kXcd;
+    const int tile = (i / p.nrb) * kXcd + xcd;
+    const int rb = i % p.nrb;
+    if (tile >= ntiles) return;  // uniform: the whole workgroup leaves
+    const int id0 = tile * kGN;
+    const int row0 = rb * kGM;
+    tab[tid] = exp2(static_cast<double>(tid) * (1.0 / 256.0));
+    __syncthreads();  // the table, before any load is in flight
+
+    // this wave's loads of a stage: hidden chunks (w*3 + j)*64 + lane,
+    // weight chunks (w*2 + j)*64 + lane; chunk q is row q/4 at stored
+    // position q%4, i.e. logical chunk (q%4) ^ ((row >> 2) & 3).  Rows past
+    // `rows` and ids past V are clamped (their products are never stored).
+    const uint16_t* hp[3];
+    const uint16_t* wp[2];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int r = ((w * 3 + j) * 64 + lane) >> 2;
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        hp[j] = p.hidden + static_cast<size_t>(min(row0 + r, p.rows - 1)) * p.H + c * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = ((w * 2 + j) * 64 + lane) >> 2;
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        wp[j] = p.weight + static_cast<size_t>(min(id0 + r, p.V - 1)) * p.H + c * 8;
+    }
+    const int nk = p.H / kGK;
+    // steps past the last re-read the last one into a stage no longer read,
+    // so that every step issues the same five loads (the compiler's waits
+    // then follow the explicit counts below)
+    auto issue = [&](int k, GemmStage& G) __attribute__((always_inline)) {
+        const int k0 = min(k, nk - 1) * kGK;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) __builtin_amdgcn_global_load_lds(hp[j] + k0, G.h + (w * 3 + j) * 64, 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) __builtin_amdgcn_global_load_lds(wp[j] + k0, G.w + (w * 2 + j) * 64, 16, 0, 0);
+    };
+
+    floatx4 acc[4][6];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int rt = 0; rt < 6; ++rt) acc[it][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // operand reads: row base + col16, logical chunk kg (stored at kg ^ sw)
+    const int loff = col16 * 4 + (kg ^ ((col16 >> 2) & 3));
+    auto compute = [&](const GemmStage& G) __attribute__((always_inline)) {
+        bf16x8 wa[4], hb[6];
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            wa[it] = *reinterpret_cast<const bf16x8*>(&G.w[(wn * 64 + it * 16) * 4 + loff]);
+#pragma unroll
+        for (int rt = 0; rt < 6; ++rt)
+            hb[rt] = *reinterpret_cast<const bf16x8*>(&G.h[(wr * 96 + rt * 16) * 4 + loff]);
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int rt = 0; rt < 6; ++rt)
+                acc[it][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[it], hb[rt], acc[it][rt], 0, 0, 0);
+    };
+    // step k: this wave's loads of step k are in when at most those of step
+    // k + 1 (five) are in flight; the barrier makes every wave's loads of
+    // step k visible and frees the stage of step k - 1 for step k + 2 (every
+    // wave's reads of it fed its products before it arrived).  A plain
+    // barrier: the workgroup release of __syncthreads would also wait for
+    // the loads of step k + 1; the LDS-only acquire keeps the reads after it.
+    auto step = [&](int k, const GemmStage& G, GemmStage& Gn) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        issue(k + 2, Gn);
+        compute(G);
+    };
+    issue(0, G0);
+    issue(1, G1);
+    int k = 0;
+    for (; k + 3 <= nk; k += 3) {
+        step(k, G0, G2);
+        step(k + 1, G1, G0);
+        step(k + 2, G2, G1);
+    }
+    if (k < nk) step(k, G0, G2);
+    if (k + 1 < nk) step(k + 1, G1, G0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the loop
+
+    // ---- epilogue: acc[it][rt][e] is row row0 + 96 wr + 16 rt + col16, id
+    // id0 + 64 wn + 16 it + 4 kg + e; this wave holds part 2 tile + wn of its
+    // 96 rows whole
+    const int part = tile * 2 + wn;
+    const int vw = id0 + wn * 64 + kg * 4;
+    const bool vec = (p.V & 3) == 0;
+#pragma unroll
+    for (int rt = 0; rt < 6; ++rt) {
+        const int r = row0 + wr * 96 + rt * 16 + col16;
+        if (r < p.rows) {
+            float* dst = p.logits + static_cast<size_t>(r) * p.V;
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int vb = vw + it * 16;
+                if (vec && vb + 3 < p.V) {
+                    *reinterpret_cast<float4*>(dst + vb) =
+                        make_float4(acc[it][rt][0], acc[it][rt][1], acc[it][rt][2], acc[it][rt][3]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (vb + e < p.V) dst[vb + e] = acc[it][rt][e];
+                }
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (vw + it * 16 + e < p.V) mx = fmaxf(mx, acc[it][rt][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        double sum = 0.0;
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (vw + it * 16 + e < p.V)
+                    sum += exp2_256((static_cast<double>(acc[it][rt][e]) - static_cast<double>(mx)) * p.ys, tab);
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        if (kg == 0 && r < p.rows && part < p.nparts) {
+            const size_t o = static_cast<size_t>(r) * p.nparts + part;
+            p.part_m[o] = mx;
+            p.part_s[o] = sum;
+        }
+    }
+}
+
 }  // namespace
 
 int lm_head_parts(int V) { return (V + kPart - 1) / kPart; }
@@ -245,6 +414,15 @@ hipError_t lm_head_launch(const LmArgs& a, hipStream_t stream) {
     p.V = a.V;
     p.nparts = lm_head_parts(a.V);
     p.ys = (1.0 / static_cast<double>(a.temperature)) * kY256PerLn2;
+    if (a.rows > kSmallRows) {
+        // row blocks of 192, id tiles of 128; every XCD gets ceil(ntiles / 8)
+        // tiles' worth of workgroups, those past the end leave at once
+        const int ntiles = (a.V + kGN - 1) / kGN;
+        p.nrb = (a.rows + kGM - 1) / kGM;
+        const int blocks = ((ntiles + kXcd - 1) / kXcd) * kXcd * p.nrb;
+        hipLaunchKernelGGL(lm_gemm_kernel, dim3(blocks), dim3(kThreads), 0, stream, p, ntiles);
+        return hipGetLastError();
+    }
     const int tiles = (a.rows + 15) / 16;
     const int nr = tiles < 4 ? tiles : 4;
     p.nrb = (tiles + nr - 1) / nr;
