@@ -33,15 +33,15 @@
 //   This form suits decode-sized row counts (the weight stream bounds it).
 //
 // lm_gemm_kernel: more rows, where the products bound the call.  One
-//   workgroup (4 waves) per (block of 192 rows, tile of 128 ids = two
+//   workgroup (8 waves) per (block of 192 rows, tile of 256 ids = four
 //   statistics parts); both operands pass through LDS in 32-wide steps of the
-//   hidden dimension, three stages deep (direct 16-byte global-to-LDS loads,
+//   hidden dimension, five stages deep (direct 16-byte global-to-LDS loads,
 //   one barrier per step), so each weight and hidden element read from L2 or
-//   HBM feeds 128 or 192 products instead of 64.  Wave (wr, wn) computes rows
+//   HBM feeds 256 or 192 products instead of 64.  Wave (wr, wn) computes rows
 //   96 wr .. +96 and ids 64 wn .. +64 of the tile: 24 products
 //   v_mfma_f32_16x16x32_bf16 per step, the weight tile as A, the hidden rows
-//   as B, as above.  Each wave then holds whole statistics parts of its rows,
-//   so the epilogue needs no exchange between waves.
+//   as B, as above.  Each wave then holds a whole statistics part of its
+//   rows, so the epilogue needs no exchange between waves.
 #include "sv_device.h"
 #include "sv_internal.h"
 #include "sv_math.h"
@@ -240,65 +240,99 @@ void launch_nr(const LmParams& p, int blocks, hipStream_t stream) {
 }
 
 constexpr int kGM = 192;       // rows per workgroup tile
-constexpr int kGN = 128;       // ids per workgroup tile (two statistics parts)
+constexpr int kGN = 256;       // ids per workgroup tile (four statistics parts)
+constexpr int kGThreads = 512; // 8 waves: 2 along the rows x 4 along the ids
 constexpr int kGK = 32;        // hidden-dimension step: one 16x16x32 product
 constexpr int kSmallRows = 64; // up to this many rows: lm_head_kernel
 
 // One stage of both operand tiles: rows of 32 bf16 (four 16-byte chunks);
-// chunk c of row r is stored at c ^ ((r >> 2) & 3), so that the 16-byte
-// operand reads of 16 consecutive rows fall on distinct banks.
+// chunk c of row r is stored at c ^ gemm_swz(r), so that the 16-byte operand
+// reads of 16 consecutive rows (one chunk each) fall on distinct banks: any
+// 8 consecutive rows cover all eight 16-byte bank groups of 128 bytes, and
+// rows r, r+4, r+8, r+12 all four positions of their 64-byte group.
+__device__ __forceinline__ int gemm_swz(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
+template <int GN>
 struct GemmStage {
     uint4 h[kGM * kGK / 8];  // hidden rows of the block (12 KiB)
-    uint4 w[kGN * kGK / 8];  // weight rows of the tile (8 KiB)
+    uint4 w[GN * kGK / 8];   // weight rows of the tile (GN / 16 KiB)
 };
 
-__global__ __launch_bounds__(kThreads, 2) void lm_gemm_kernel(LmParams p, int ntiles) {
-    // three separate LDS objects: the compiler's wait for one stage's direct
-    // loads then does not cover the others
-    __shared__ GemmStage G0, G1, G2;
+// NWN waves along the ids (tile of GN = 64 NWN ids), two along the rows, NST
+// stages.  (The body is a device function called by a plain kernel: as a
+// kernel template it would not get its host-side launch stub, because the
+// direct LDS load builtin does not instantiate in the host pass.)
+template <int NWN, int NST>
+__device__ __forceinline__ void lm_gemm_body(const LmParams& p, int ntiles) {
+    constexpr int GN = 64 * NWN;
+    constexpr int NW = 2 * NWN;                 // waves
+    constexpr int HPW = (12 + NW - 1) / NW;     // hidden-tile loads per wave and stage (12 in all)
+    constexpr int LPW = HPW + 2;                // all loads per wave and stage (2 of the weight tile)
+    static_assert(NST >= 3 && NST <= 5 && (NST - 2) * LPW < 16, "stages and the wait count");
+    // NST separate LDS objects (the unused ones are not allocated): the
+    // compiler's wait for one stage's direct loads then does not cover the
+    // others
+    __shared__ GemmStage<GN> G0, G1, G2, G3, G4;
     __shared__ double tab[256];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col16 = lane & 15, kg = lane >> 4;
-    const int wr = w >> 1, wn = w & 1;
+    const int wr = w / NWN, wn = w % NWN;
     // XCD-aware order: the row blocks of an id tile are consecutive on one XCD
     const int L = blockIdx.x;
     const int xcd = L % kXcd, i = L / kXcd;
     const int tile = (i / p.nrb) * kXcd + xcd;
     const int rb = i % p.nrb;
     if (tile >= ntiles) return;  // uniform: the whole workgroup leaves
-    const int id0 = tile * kGN;
+    const int id0 = tile * GN;
     const int row0 = rb * kGM;
-    tab[tid] = exp2(static_cast<double>(tid) * (1.0 / 256.0));
+    if (tid < 256) tab[tid] = exp2(static_cast<double>(tid) * (1.0 / 256.0));
     __syncthreads();  // the table, before any load is in flight
 
-    // this wave's loads of a stage: hidden chunks (w*3 + j)*64 + lane,
-    // weight chunks (w*2 + j)*64 + lane; chunk q is row q/4 at stored
-    // position q%4, i.e. logical chunk (q%4) ^ ((row >> 2) & 3).  Rows past
-    // `rows` and ids past V are clamped (their products are never stored).
-    const uint16_t* hp[3];
+    // this wave's loads of a stage: hidden chunks ((w*HPW + j) mod 12)*64 +
+    // lane (with 8 waves the last two repeat loads of the first ones, same
+    // data to the same place, so that every wave issues as many), weight
+    // chunks (w*2 + j)*64 + lane; chunk q is row q/4 at stored position q%4,
+    // i.e. logical chunk (q%4) ^ ((row >> 2) & 3).  Rows past `rows` and ids
+    // past V are clamped (their products are never stored).
+    const uint16_t* hp[HPW];
     const uint16_t* wp[2];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int r = ((w * 3 + j) * 64 + lane) >> 2;
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
+    for (int j = 0; j < HPW; ++j) {
+        const int r = (((w * HPW + j) % 12) * 64 + lane) >> 2;
+        const int c = (lane & 3) ^ gemm_swz(r);
         hp[j] = p.hidden + static_cast<size_t>(min(row0 + r, p.rows - 1)) * p.H + c * 8;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int r = ((w * 2 + j) * 64 + lane) >> 2;
-        const int c = (lane & 3) ^ ((r >> 2) & 3);
+        const int c = (lane & 3) ^ gemm_swz(r);
         wp[j] = p.weight + static_cast<size_t>(min(id0 + r, p.V - 1)) * p.H + c * 8;
     }
     const int nk = p.H / kGK;
     // steps past the last re-read the last one into a stage no longer read,
-    // so that every step issues the same five loads (the compiler's waits
-    // then follow the explicit counts below)
-    auto issue = [&](int k, GemmStage& G) __attribute__((always_inline)) {
+    // so that every step issues the same loads (the compiler's waits then
+    // follow the explicit counts below)
+    // (the stage objects are named directly, so the direct-load builtin sees
+    // LDS addresses; st folds to a constant in every use)
+    auto dma_h = [&](const uint16_t* src, int d, int st) __attribute__((always_inline)) {
+        if (st == 0) __builtin_amdgcn_global_load_lds(src, G0.h + d, 16, 0, 0);
+        else if (st == 1) __builtin_amdgcn_global_load_lds(src, G1.h + d, 16, 0, 0);
+        else if (st == 2) __builtin_amdgcn_global_load_lds(src, G2.h + d, 16, 0, 0);
+        else if (st == 3) __builtin_amdgcn_global_load_lds(src, G3.h + d, 16, 0, 0);
+        else __builtin_amdgcn_global_load_lds(src, G4.h + d, 16, 0, 0);
+    };
+    auto dma_w = [&](const uint16_t* src, int d, int st) __attribute__((always_inline)) {
+        if (st == 0) __builtin_amdgcn_global_load_lds(src, G0.w + d, 16, 0, 0);
+        else if (st == 1) __builtin_amdgcn_global_load_lds(src, G1.w + d, 16, 0, 0);
+        else if (st == 2) __builtin_amdgcn_global_load_lds(src, G2.w + d, 16, 0, 0);
+        else if (st == 3) __builtin_amdgcn_global_load_lds(src, G3.w + d, 16, 0, 0);
+        else __builtin_amdgcn_global_load_lds(src, G4.w + d, 16, 0, 0);
+    };
+    auto issue = [&](int k, int st) __attribute__((always_inline)) {
         const int k0 = min(k, nk - 1) * kGK;
 #pragma unroll
-        for (int j = 0; j < 3; ++j) __builtin_amdgcn_global_load_lds(hp[j] + k0, G.h + (w * 3 + j) * 64, 16, 0, 0);
+        for (int j = 0; j < HPW; ++j) dma_h(hp[j] + k0, ((w * HPW + j) % 12) * 64, st);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) __builtin_amdgcn_global_load_lds(wp[j] + k0, G.w + (w * 2 + j) * 64, 16, 0, 0);
+        for (int j = 0; j < 2; ++j) dma_w(wp[j] + k0, (w * 2 + j) * 64, st);
     };
 
     floatx4 acc[4][6];
@@ -306,9 +340,10 @@ __global__ __launch_bounds__(kThreads, 2) void lm_gemm_kernel(LmParams p, int nt
     for (int it = 0; it < 4; ++it)
 #pragma unroll
         for (int rt = 0; rt < 6; ++rt) acc[it][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // operand reads: row base + col16, logical chunk kg (stored at kg ^ sw)
-    const int loff = col16 * 4 + (kg ^ ((col16 >> 2) & 3));
-    auto compute = [&](const GemmStage& G) __attribute__((always_inline)) {
+    // operand reads: row base + col16, logical chunk kg (stored at
+    // kg ^ gemm_swz(col16): the bases are multiples of 16)
+    const int loff = col16 * 4 + (kg ^ gemm_swz(col16));
+    auto compute = [&](const GemmStage<GN>& G) __attribute__((always_inline)) {
         bf16x8 wa[4], hb[6];
 #pragma unroll
         for (int it = 0; it < 4; ++it)
@@ -322,35 +357,40 @@ __global__ __launch_bounds__(kThreads, 2) void lm_gemm_kernel(LmParams p, int nt
             for (int rt = 0; rt < 6; ++rt)
                 acc[it][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[it], hb[rt], acc[it][rt], 0, 0, 0);
     };
-    // step k: this wave's loads of step k are in when at most those of step
-    // k + 1 (five) are in flight; the barrier makes every wave's loads of
-    // step k visible and frees the stage of step k - 1 for step k + 2 (every
-    // wave's reads of it fed its products before it arrived).  A plain
-    // barrier: the workgroup release of __syncthreads would also wait for
-    // the loads of step k + 1; the LDS-only acquire keeps the reads after it.
-    auto step = [&](int k, const GemmStage& G, GemmStage& Gn) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+    // step k (in stage st = k mod NST): this wave's loads of step k are in
+    // when at most those of steps k+1 .. k+NST-2 are in flight; the barrier
+    // makes every wave's loads of step k visible and frees the stage of step
+    // k - 1 for step k + NST - 1 (every wave's reads of it fed its products
+    // before it arrived).  A plain barrier: the workgroup release of
+    // __syncthreads would also wait for the later steps' loads; the LDS-only
+    // acquire keeps the reads after it.
+    auto step = [&](int k, int st) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | ((NST - 2) * LPW));  // vmcnt((NST-2) LPW)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        issue(k + 2, Gn);
-        compute(G);
+        issue(k + NST - 1, (st + NST - 1) % NST);
+        if (st == 0) compute(G0);
+        else if (st == 1) compute(G1);
+        else if (st == 2) compute(G2);
+        else if (st == 3) compute(G3);
+        else compute(G4);
     };
-    issue(0, G0);
-    issue(1, G1);
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s) issue(s, s);
     int k = 0;
-    for (; k + 3 <= nk; k += 3) {
-        step(k, G0, G2);
-        step(k + 1, G1, G0);
-        step(k + 2, G2, G1);
+    for (; k + NST <= nk; k += NST) {
+#pragma unroll
+        for (int s = 0; s < NST; ++s) step(k + s, s);
     }
-    if (k < nk) step(k, G0, G2);
-    if (k + 1 < nk) step(k + 1, G1, G0);
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (k + s < nk) step(k + s, s);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the loop
 
     // ---- epilogue: acc[it][rt][e] is row row0 + 96 wr + 16 rt + col16, id
     // id0 + 64 wn + 16 it + 4 kg + e; this wave holds part 2 tile + wn of its
     // 96 rows whole
-    const int part = tile * 2 + wn;
+    const int part = tile * NWN + wn;
     const int vw = id0 + wn * 64 + kg * 4;
     const bool vec = (p.V & 3) == 0;
 #pragma unroll
@@ -396,6 +436,8 @@ __global__ __launch_bounds__(kThreads, 2) void lm_gemm_kernel(LmParams p, int nt
     }
 }
 
+__global__ __launch_bounds__(512, 1) void lm_gemm_kernel(LmParams p, int ntiles) { lm_gemm_body<4, 5>(p, ntiles); }
+
 }  // namespace
 
 int lm_head_parts(int V) { return (V + kPart - 1) / kPart; }
@@ -415,12 +457,12 @@ hipError_t lm_head_launch(const LmArgs& a, hipStream_t stream) {
     p.nparts = lm_head_parts(a.V);
     p.ys = (1.0 / static_cast<double>(a.temperature)) * kY256PerLn2;
     if (a.rows > kSmallRows) {
-        // row blocks of 192, id tiles of 128; every XCD gets ceil(ntiles / 8)
+        // row blocks of 192, id tiles of 256; every XCD gets ceil(ntiles / 8)
         // tiles' worth of workgroups, those past the end leave at once
         const int ntiles = (a.V + kGN - 1) / kGN;
         p.nrb = (a.rows + kGM - 1) / kGM;
         const int blocks = ((ntiles + kXcd - 1) / kXcd) * kXcd * p.nrb;
-        hipLaunchKernelGGL(lm_gemm_kernel, dim3(blocks), dim3(kThreads), 0, stream, p, ntiles);
+        hipLaunchKernelGGL(lm_gemm_kernel, dim3(blocks), dim3(kGThreads), 0, stream, p, ntiles);
         return hipGetLastError();
     }
     const int tiles = (a.rows + 15) / 16;

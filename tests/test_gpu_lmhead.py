@@ -51,9 +51,9 @@ def combine_parts(pm, ps, T):
 
 @pytest.mark.parametrize("rows,H,V", [(48, 512, 12288), (5, 96, 1000), (130, 64, 302),
                                       (16, 2048, 4096), (1, 32, 129),
-                                      # more than 64 rows: the LDS-staged tiles (192 rows x 128
+                                      # more than 64 rows: the LDS-staged tiles (192 rows x 256
                                       # ids): several row blocks, partial id tiles, every count
-                                      # of 32-wide steps modulo the three stages, one step
+                                      # of 32-wide steps modulo the five stages, one step
                                       (200, 256, 2000), (576, 128, 1030), (65, 32, 129),
                                       (384, 160, 4096)])
 def test_lm_head_logits_and_part_statistics(rows, H, V):
