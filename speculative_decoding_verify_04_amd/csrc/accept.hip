@@ -225,23 +225,6 @@ __device__ __forceinline__ void load_segment(const void* row, int bf16, int vec,
         load4(row, bf16, vec, V, e0 + g * 1024 + tid * 4, z + 4 * g);
 }
 
-// A whole fp32 segment with vector loads and no branch: the loads of both
-// rows of a unit are then in flight together, and the first row's use waits
-// for its own loads only (for rows whose vocabulary is a whole number of
-// segments).
-template <int EPT>
-__device__ __forceinline__ void seg_load_f32(const void* row, int s, int tid, float* z) {
-    const float4* r4 = reinterpret_cast<const float4*>(static_cast<const float*>(row) + s * (kThreads * EPT)) + tid;
-#pragma unroll
-    for (int g = 0; g < EPT / 4; ++g) {
-        const float4 f = r4[g * kThreads];
-        z[4 * g + 0] = f.x;
-        z[4 * g + 1] = f.y;
-        z[4 * g + 2] = f.z;
-        z[4 * g + 3] = f.w;
-    }
-}
-
 __device__ __forceinline__ const void* row_ptr(const AcceptParams& p, int r) {
     const size_t es = p.bf16 ? 2 : 4;
     if (r < p.nt) return static_cast<const char*>(p.target) + static_cast<size_t>(r) * p.V * es;
@@ -1725,7 +1708,7 @@ __global__ __launch_bounds__(kMThreads) void merge_kernel(AcceptParams p) {
 
 // ---------------------------------------------------------------- segment kernel
 
-template <int EPT, bool FAST>
+template <int EPT>
 __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
     __shared__ SegLds L;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -1748,23 +1731,36 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
     const int q0 = seq_q0(p, b), kb = seq_kb(p, b), j = u - q0;
     const bool has_d = !p.greedy && j < kb;
     const int dr = p.nt + u - b;
-    // both rows' loads at once (a bonus unit reads its target segment twice,
-    // the second time from cache); with FAST the target row is used while the
-    // draft row's loads are still in flight
     float z[2][EPT];
-    if constexpr (FAST) {
-        seg_load_f32<EPT>(row_ptr(p, u), s, tid, z[0]);
-        seg_load_f32<EPT>(row_ptr(p, has_d ? dr : u), s, tid, z[1]);
+    load_segment<EPT>(row_ptr(p, u), p.bf16, p.vec, p.V, s, tid, z[0]);
+    if (has_d) {
+        load_segment<EPT>(row_ptr(p, dr), p.bf16, p.vec, p.V, s, tid, z[1]);
     } else {
-        load_segment<EPT>(row_ptr(p, u), p.bf16, p.vec, p.V, s, tid, z[0]);
-        load_segment<EPT>(row_ptr(p, has_d ? dr : u), p.bf16, p.vec, p.V, s, tid, z[1]);
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) z[1][k] = -INFINITY;
     }
     fill_exp_table(L.tab);
     // the segment counters start at zero (ordered before use by the first barrier)
     for (int i = tid; i < 2 * 4 * (kQB + 64); i += kThreads) (&L.hc[0][0][0])[i] = 0;
     for (int i = tid; i < 2 * kQB; i += kThreads) (&L.hm[0][0])[i] = 0.0;
+    // the drafted token's logits, stored by the thread that holds them
+    // (element k of thread t has id seg_lo + (k/4)*1024 + 4*t + k%4)
     const int x = (j < kb) ? p.draft_tokens[u - b] : -1;
     const int seg_lo = s * kThreads * EPT;
+    if (!p.greedy && x >= seg_lo && x < seg_lo + kThreads * EPT && x < p.V) {
+        const int off = x - seg_lo;
+        const int kx = ((off >> 10) << 2) | (off & 3);
+        if (tid == ((off & 1023) >> 2)) {
+            float zq = 0.0f, zp = 0.0f;
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) {
+                zq = (k == kx) ? z[0][k] : zq;
+                zp = (k == kx) ? z[1][k] : zp;
+            }
+            p.zx[u] = zq;
+            if (has_d) p.zx[dr] = zp;
+        }
+    }
 
     if (p.greedy) {
         float bv = -INFINITY;
@@ -1800,12 +1796,27 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
             h->top = bi;
         }
     } else {
-        // row by row: the segment max, then one pass per element: the fp64
-        // weight (a row max of -inf gives NaN arguments, which exp2_256 maps
-        // to 0) and, with a filter on, the bin offset (kept) and its count.
-        // The target row is done while the draft row's loads are in flight.
-        float ms[2] = {-INFINITY, -INFINITY};
+        float lm[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) lm[r] = fmaxf(lm[r], z[r][k]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            lm[r] = wave_max(lm[r]);
+            if (lane == 0) L.red_f[r][wv] = lm[r];
+        }
+        __syncthreads();
+        float ms[2];
         int top[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            ms[r] = fmaxf(fmaxf(L.red_f[r][0], L.red_f[r][1]), fmaxf(L.red_f[r][2], L.red_f[r][3]));
+            top[r] = qbin(ms[r], p.qscale);
+        }
+        // one pass per element: the fp64 weight (a row max of -inf gives NaN
+        // arguments, which exp2_256 maps to 0) and, with a filter on, the bin
+        // offset (kept) and its count
         double acc[2] = {0.0, 0.0};
         unsigned ow[2][EPT / 4];  // bin offsets (0..kQB-1 in the window, kQB.. below it), four per word
         const unsigned past = static_cast<unsigned>(kQB + lane);
@@ -1813,20 +1824,7 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
         for (int r = 0; r < 2; ++r) {
 #pragma unroll
             for (int g = 0; g < EPT / 4; ++g) ow[r][g] = 0u;  // row 1 without a draft: never listed (ocut -1)
-            top[r] = qbin(ms[r], p.qscale);
-            if (r == 1) {
-#pragma unroll
-                for (int k = 0; k < EPT; ++k) z[1][k] = has_d ? z[1][k] : -INFINITY;
-            }
             if (r == 1 && !has_d) continue;  // uniform
-            float lm = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < EPT; ++k) lm = fmaxf(lm, z[r][k]);
-            lm = wave_max(lm);
-            if (lane == 0) L.red_f[r][wv] = lm;
-            __syncthreads();
-            ms[r] = fmaxf(fmaxf(L.red_f[r][0], L.red_f[r][1]), fmaxf(L.red_f[r][2], L.red_f[r][3]));
-            top[r] = qbin(ms[r], p.qscale);
             const double mr = static_cast<double>(ms[r]);
             if (p.filter) {  // uniform
 #pragma unroll
@@ -1847,22 +1845,6 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
                     acc[r] += exp2_256((static_cast<double>(z[r][k]) - mr) * p.yscale, L.tab);
                     if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-        }
-        // the drafted token's logits, stored by the thread that holds them
-        // (element k of thread t has id seg_lo + (k/4)*1024 + 4*t + k%4)
-        if (x >= seg_lo && x < seg_lo + kThreads * EPT && x < p.V) {
-            const int off = x - seg_lo;
-            const int kx = ((off >> 10) << 2) | (off & 3);
-            if (tid == ((off & 1023) >> 2)) {
-                float zq = 0.0f, zp = 0.0f;
-#pragma unroll
-                for (int k = 0; k < EPT; ++k) {
-                    zq = (k == kx) ? z[0][k] : zq;
-                    zp = (k == kx) ? z[1][k] : zp;
-                }
-                p.zx[u] = zq;
-                if (has_d) p.zx[dr] = zp;
             }
         }
 #pragma unroll
@@ -2245,11 +2227,10 @@ hipError_t accept_launch(const AcceptArgs& a, hipStream_t stream) {
     hipError_t err = hipSuccess;
     if (!p.prestats) {  // the LM head's statistics replace the segment pass
         const dim3 grid(p.grid_units * p.nseg);
-        // every segment whole, fp32, vector loads: the branch-free load form
-        const bool fast = !p.bf16 && p.vec && a.V % (kThreads * ept) == 0;
-        void (*kern)(AcceptParams) = (ept == 16) ? (fast ? segment_kernel<16, true> : segment_kernel<16, false>)
-                                                 : (fast ? segment_kernel<12, true> : segment_kernel<12, false>);
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, p);
+        if (ept == 16)
+            hipLaunchKernelGGL(segment_kernel<16>, grid, dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL(segment_kernel<12>, grid, dim3(kThreads), 0, stream, p);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
