@@ -30,7 +30,13 @@
 //   consecutive on one XCD, so the part's weight slice is fetched from HBM
 //   once and served to the other row blocks from that XCD's L2.  The weight
 //   matrix is streamed once; the hidden rows stay in L2.
-//   This form suits decode-sized row counts (the weight stream bounds it).
+//   Used for up to 16 rows (one row tile; the weight stream bounds it).
+//
+// lm_gemm_rows_kernel<RT>: 17 to 64 rows, still bound by the weight stream.
+//   One workgroup (3 waves) per tile of 192 ids; both the block of 16 RT
+//   rows and the weight tile pass through LDS as below, so each hidden
+//   element loaded feeds 192 products; each wave holds one statistics part
+//   of all the rows.
 //
 // lm_gemm_kernel: more rows, where the products bound the call.  One
 //   workgroup (8 waves) per (block of 192 rows, tile of 256 ids = four
@@ -234,16 +240,9 @@ __global__ __launch_bounds__(kThreads) void lm_head_kernel(LmParams p) {
     }
 }
 
-template <int NR, int KU>
-void launch_nr(const LmParams& p, int blocks, hipStream_t stream) {
-    hipLaunchKernelGGL((lm_head_kernel<NR, KU>), dim3(blocks), dim3(kThreads), 0, stream, p);
-}
-
-constexpr int kGM = 192;       // rows per workgroup tile
-constexpr int kGN = 256;       // ids per workgroup tile (four statistics parts)
-constexpr int kGThreads = 512; // 8 waves: 2 along the rows x 4 along the ids
 constexpr int kGK = 32;        // hidden-dimension step: one 16x16x32 product
-constexpr int kSmallRows = 64; // up to this many rows: lm_head_kernel
+constexpr int kStreamRows = 16; // up to this many rows: lm_head_kernel
+constexpr int kSmallRows = 64;  // up to this many rows: lm_gemm_rows_kernel
 
 // One stage of both operand tiles: rows of 32 bf16 (four 16-byte chunks);
 // chunk c of row r is stored at c ^ gemm_swz(r), so that the 16-byte operand
@@ -251,31 +250,38 @@ constexpr int kSmallRows = 64; // up to this many rows: lm_head_kernel
 // 8 consecutive rows cover all eight 16-byte bank groups of 128 bytes, and
 // rows r, r+4, r+8, r+12 all four positions of their 64-byte group.
 __device__ __forceinline__ int gemm_swz(int r) { return ((r >> 1) ^ ((r >> 3) & 1)) & 3; }
-template <int GN>
+
+template <int GM, int GN>
 struct GemmStage {
-    uint4 h[kGM * kGK / 8];  // hidden rows of the block (12 KiB)
+    uint4 h[GM * kGK / 8];   // hidden rows of the block (GM / 16 KiB)
     uint4 w[GN * kGK / 8];   // weight rows of the tile (GN / 16 KiB)
 };
 
-// NWN waves along the ids (tile of GN = 64 NWN ids), two along the rows, NST
-// stages.  (The body is a device function called by a plain kernel: as a
-// kernel template it would not get its host-side launch stub, because the
-// direct LDS load builtin does not instantiate in the host pass.)
-template <int NWN, int NST>
+// s_waitcnt immediate for vmcnt(n), n < 64 (the other counters left alone)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Tile of GM = WR RT 16 rows x GN = WN 64 ids, WR x WN waves, each wave RT
+// row tiles x 4 id tiles (one statistics part), NST stages.  (The body is a
+// device function called by plain kernels: as a kernel template it would not
+// get its host-side launch stub, because the direct LDS load builtin does
+// not instantiate in the host pass.)
+template <int WR, int RT, int WN, int NST>
 __device__ __forceinline__ void lm_gemm_body(const LmParams& p, int ntiles) {
-    constexpr int GN = 64 * NWN;
-    constexpr int NW = 2 * NWN;                 // waves
-    constexpr int HPW = (12 + NW - 1) / NW;     // hidden-tile loads per wave and stage (12 in all)
-    constexpr int LPW = HPW + 2;                // all loads per wave and stage (2 of the weight tile)
-    static_assert(NST >= 3 && NST <= 5 && (NST - 2) * LPW < 16, "stages and the wait count");
+    constexpr int GM = WR * RT * 16;
+    constexpr int GN = WN * 64;
+    constexpr int NW = WR * WN;                 // waves
+    constexpr int TH = GM / 16, TW = GN / 16;   // loads of 64 x 16 bytes per stage: hidden, weight
+    constexpr int TI = TH + TW;
+    constexpr int LPW = (TI + NW - 1) / NW;     // loads per wave and stage (the excess repeats loads)
+    static_assert(NST >= 3 && NST <= 6 && (NST - 2) * LPW < 64, "stages and the wait count");
     // NST separate LDS objects (the unused ones are not allocated): the
     // compiler's wait for one stage's direct loads then does not cover the
     // others
-    __shared__ GemmStage<GN> G0, G1, G2, G3, G4;
+    __shared__ GemmStage<GM, GN> G0, G1, G2, G3, G4, G5;
     __shared__ double tab[256];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col16 = lane & 15, kg = lane >> 4;
-    const int wr = w / NWN, wn = w % NWN;
+    const int wr = w / WN, wn = w % WN;
     // XCD-aware order: the row blocks of an id tile are consecutive on one XCD
     const int L = blockIdx.x;
     const int xcd = L % kXcd, i = L / kXcd;
@@ -283,78 +289,80 @@ __device__ __forceinline__ void lm_gemm_body(const LmParams& p, int ntiles) {
     const int rb = i % p.nrb;
     if (tile >= ntiles) return;  // uniform: the whole workgroup leaves
     const int id0 = tile * GN;
-    const int row0 = rb * kGM;
-    if (tid < 256) tab[tid] = exp2(static_cast<double>(tid) * (1.0 / 256.0));
+    const int row0 = rb * GM;
+    for (int t = tid; t < 256; t += NW * 64) tab[t] = exp2(static_cast<double>(t) * (1.0 / 256.0));
     __syncthreads();  // the table, before any load is in flight
 
-    // this wave's loads of a stage: hidden chunks ((w*HPW + j) mod 12)*64 +
-    // lane (with 8 waves the last two repeat loads of the first ones, same
-    // data to the same place, so that every wave issues as many), weight
-    // chunks (w*2 + j)*64 + lane; chunk q is row q/4 at stored position q%4,
-    // i.e. logical chunk (q%4) ^ ((row >> 2) & 3).  Rows past `rows` and ids
-    // past V are clamped (their products are never stored).
-    const uint16_t* hp[HPW];
-    const uint16_t* wp[2];
+    // this wave's loads of a stage: load q = (w LPW + j) mod TI (the last
+    // waves may repeat loads of the first ones: same data to the same place,
+    // so that every wave issues as many); loads q < TH carry hidden chunks
+    // q*64 + lane, the others weight chunks (q - TH)*64 + lane; chunk c is
+    // row c/4 at stored position c%4, i.e. logical chunk (c%4) ^ gemm_swz(row).
+    // Rows past `rows` and ids past V are clamped (their products are never
+    // stored).
+    const uint16_t* src[LPW];
+    int dst[LPW];
+    bool ish[LPW];
 #pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-        const int r = (((w * HPW + j) % 12) * 64 + lane) >> 2;
+    for (int j = 0; j < LPW; ++j) {
+        const int q = (w * LPW + j) % TI;
+        ish[j] = q < TH;
+        const int qq = ish[j] ? q : q - TH;
+        const int r = (qq * 64 + lane) >> 2;
         const int c = (lane & 3) ^ gemm_swz(r);
-        hp[j] = p.hidden + static_cast<size_t>(min(row0 + r, p.rows - 1)) * p.H + c * 8;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int r = ((w * 2 + j) * 64 + lane) >> 2;
-        const int c = (lane & 3) ^ gemm_swz(r);
-        wp[j] = p.weight + static_cast<size_t>(min(id0 + r, p.V - 1)) * p.H + c * 8;
+        src[j] = ish[j] ? p.hidden + static_cast<size_t>(min(row0 + r, p.rows - 1)) * p.H + c * 8
+                        : p.weight + static_cast<size_t>(min(id0 + r, p.V - 1)) * p.H + c * 8;
+        dst[j] = qq * 64;
     }
     const int nk = p.H / kGK;
     // steps past the last re-read the last one into a stage no longer read,
     // so that every step issues the same loads (the compiler's waits then
-    // follow the explicit counts below)
-    // (the stage objects are named directly, so the direct-load builtin sees
-    // LDS addresses; st folds to a constant in every use)
-    auto dma_h = [&](const uint16_t* src, int d, int st) __attribute__((always_inline)) {
-        if (st == 0) __builtin_amdgcn_global_load_lds(src, G0.h + d, 16, 0, 0);
-        else if (st == 1) __builtin_amdgcn_global_load_lds(src, G1.h + d, 16, 0, 0);
-        else if (st == 2) __builtin_amdgcn_global_load_lds(src, G2.h + d, 16, 0, 0);
-        else if (st == 3) __builtin_amdgcn_global_load_lds(src, G3.h + d, 16, 0, 0);
-        else __builtin_amdgcn_global_load_lds(src, G4.h + d, 16, 0, 0);
-    };
-    auto dma_w = [&](const uint16_t* src, int d, int st) __attribute__((always_inline)) {
-        if (st == 0) __builtin_amdgcn_global_load_lds(src, G0.w + d, 16, 0, 0);
-        else if (st == 1) __builtin_amdgcn_global_load_lds(src, G1.w + d, 16, 0, 0);
-        else if (st == 2) __builtin_amdgcn_global_load_lds(src, G2.w + d, 16, 0, 0);
-        else if (st == 3) __builtin_amdgcn_global_load_lds(src, G3.w + d, 16, 0, 0);
-        else __builtin_amdgcn_global_load_lds(src, G4.w + d, 16, 0, 0);
+    // follow the explicit counts below).  The stage objects are named
+    // directly, so the direct-load builtin sees LDS addresses; st folds to a
+    // constant in every use.
+    auto dma = [&](const uint16_t* g, bool h, int d, int st) __attribute__((always_inline)) {
+        if (h) {
+            if (st == 0) __builtin_amdgcn_global_load_lds(g, G0.h + d, 16, 0, 0);
+            else if (st == 1) __builtin_amdgcn_global_load_lds(g, G1.h + d, 16, 0, 0);
+            else if (st == 2) __builtin_amdgcn_global_load_lds(g, G2.h + d, 16, 0, 0);
+            else if (st == 3) __builtin_amdgcn_global_load_lds(g, G3.h + d, 16, 0, 0);
+            else if (st == 4) __builtin_amdgcn_global_load_lds(g, G4.h + d, 16, 0, 0);
+            else __builtin_amdgcn_global_load_lds(g, G5.h + d, 16, 0, 0);
+        } else {
+            if (st == 0) __builtin_amdgcn_global_load_lds(g, G0.w + d, 16, 0, 0);
+            else if (st == 1) __builtin_amdgcn_global_load_lds(g, G1.w + d, 16, 0, 0);
+            else if (st == 2) __builtin_amdgcn_global_load_lds(g, G2.w + d, 16, 0, 0);
+            else if (st == 3) __builtin_amdgcn_global_load_lds(g, G3.w + d, 16, 0, 0);
+            else if (st == 4) __builtin_amdgcn_global_load_lds(g, G4.w + d, 16, 0, 0);
+            else __builtin_amdgcn_global_load_lds(g, G5.w + d, 16, 0, 0);
+        }
     };
     auto issue = [&](int k, int st) __attribute__((always_inline)) {
         const int k0 = min(k, nk - 1) * kGK;
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) dma_h(hp[j] + k0, ((w * HPW + j) % 12) * 64, st);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dma_w(wp[j] + k0, (w * 2 + j) * 64, st);
+        for (int j = 0; j < LPW; ++j) dma(src[j] + k0, ish[j], dst[j], st);
     };
 
-    floatx4 acc[4][6];
+    floatx4 acc[4][RT];
 #pragma unroll
     for (int it = 0; it < 4; ++it)
 #pragma unroll
-        for (int rt = 0; rt < 6; ++rt) acc[it][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RT; ++rt) acc[it][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
     // operand reads: row base + col16, logical chunk kg (stored at
     // kg ^ gemm_swz(col16): the bases are multiples of 16)
     const int loff = col16 * 4 + (kg ^ gemm_swz(col16));
-    auto compute = [&](const GemmStage<GN>& G) __attribute__((always_inline)) {
-        bf16x8 wa[4], hb[6];
+    auto compute = [&](const GemmStage<GM, GN>& G) __attribute__((always_inline)) {
+        bf16x8 wa[4], hb[RT];
 #pragma unroll
         for (int it = 0; it < 4; ++it)
             wa[it] = *reinterpret_cast<const bf16x8*>(&G.w[(wn * 64 + it * 16) * 4 + loff]);
 #pragma unroll
-        for (int rt = 0; rt < 6; ++rt)
-            hb[rt] = *reinterpret_cast<const bf16x8*>(&G.h[(wr * 96 + rt * 16) * 4 + loff]);
+        for (int rt = 0; rt < RT; ++rt)
+            hb[rt] = *reinterpret_cast<const bf16x8*>(&G.h[((wr * RT + rt) * 16) * 4 + loff]);
 #pragma unroll
         for (int it = 0; it < 4; ++it)
 #pragma unroll
-            for (int rt = 0; rt < 6; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
                 acc[it][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[it], hb[rt], acc[it][rt], 0, 0, 0);
     };
     // step k (in stage st = k mod NST): this wave's loads of step k are in
@@ -365,7 +373,7 @@ __device__ __forceinline__ void lm_gemm_body(const LmParams& p, int ntiles) {
     // __syncthreads would also wait for the later steps' loads; the LDS-only
     // acquire keeps the reads after it.
     auto step = [&](int k, int st) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | ((NST - 2) * LPW));  // vmcnt((NST-2) LPW)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NST - 2) * LPW));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         issue(k + NST - 1, (st + NST - 1) % NST);
@@ -373,7 +381,8 @@ __device__ __forceinline__ void lm_gemm_body(const LmParams& p, int ntiles) {
         else if (st == 1) compute(G1);
         else if (st == 2) compute(G2);
         else if (st == 3) compute(G3);
-        else compute(G4);
+        else if (st == 4) compute(G4);
+        else compute(G5);
     };
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s) issue(s, s);
@@ -385,29 +394,29 @@ __device__ __forceinline__ void lm_gemm_body(const LmParams& p, int ntiles) {
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
         if (k + s < nk) step(k + s, s);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the loop
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load outlives the loop
 
-    // ---- epilogue: acc[it][rt][e] is row row0 + 96 wr + 16 rt + col16, id
-    // id0 + 64 wn + 16 it + 4 kg + e; this wave holds part 2 tile + wn of its
-    // 96 rows whole
-    const int part = tile * NWN + wn;
+    // ---- epilogue: acc[it][rt][e] is row row0 + 16 (RT wr + rt) + col16, id
+    // id0 + 64 wn + 16 it + 4 kg + e; this wave holds part WN tile + wn of its
+    // rows whole
+    const int part = tile * WN + wn;
     const int vw = id0 + wn * 64 + kg * 4;
     const bool vec = (p.V & 3) == 0;
 #pragma unroll
-    for (int rt = 0; rt < 6; ++rt) {
-        const int r = row0 + wr * 96 + rt * 16 + col16;
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = row0 + (wr * RT + rt) * 16 + col16;
         if (r < p.rows) {
-            float* dst = p.logits + static_cast<size_t>(r) * p.V;
+            float* dstp = p.logits + static_cast<size_t>(r) * p.V;
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int vb = vw + it * 16;
                 if (vec && vb + 3 < p.V) {
-                    *reinterpret_cast<float4*>(dst + vb) =
+                    *reinterpret_cast<float4*>(dstp + vb) =
                         make_float4(acc[it][rt][0], acc[it][rt][1], acc[it][rt][2], acc[it][rt][3]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (vb + e < p.V) dst[vb + e] = acc[it][rt][e];
+                        if (vb + e < p.V) dstp[vb + e] = acc[it][rt][e];
                 }
             }
         }
@@ -436,7 +445,21 @@ __device__ __forceinline__ void lm_gemm_body(const LmParams& p, int ntiles) {
     }
 }
 
-__global__ __launch_bounds__(512, 1) void lm_gemm_kernel(LmParams p, int ntiles) { lm_gemm_body<4, 5>(p, ntiles); }
+// Decode row counts (weight-stream bound): 16 RT rows x 192 ids, 3 waves of
+// RT row tiles x 64 ids, six stages (one workgroup per CU; with V = 49152 the
+// 256 tiles are one per CU).  The hidden rows are a small share of each
+// workgroup's loads next to its 192 weight rows.
+constexpr int kRowsGN = 192, kRowsThreads = 192;
+template <int RT>
+__global__ __launch_bounds__(192, 1) void lm_gemm_rows_kernel(LmParams p, int ntiles) {
+    lm_gemm_body<1, RT, 3, 6>(p, ntiles);
+}
+// More rows (product bound): 192 rows x 256 ids, 8 waves of 96 rows x 64 ids,
+// five stages (140 KiB, one workgroup per CU).
+constexpr int kGM = 192, kGN = 256, kGThreads = 512;
+__global__ __launch_bounds__(512, 1) void lm_gemm_kernel(LmParams p, int ntiles) {
+    lm_gemm_body<2, 6, 4, 5>(p, ntiles);
+}
 
 }  // namespace
 
@@ -456,27 +479,31 @@ hipError_t lm_head_launch(const LmArgs& a, hipStream_t stream) {
     p.V = a.V;
     p.nparts = lm_head_parts(a.V);
     p.ys = (1.0 / static_cast<double>(a.temperature)) * kY256PerLn2;
-    if (a.rows > kSmallRows) {
-        // row blocks of 192, id tiles of 256; every XCD gets ceil(ntiles / 8)
-        // tiles' worth of workgroups, those past the end leave at once
-        const int ntiles = (a.V + kGN - 1) / kGN;
-        p.nrb = (a.rows + kGM - 1) / kGM;
-        const int blocks = ((ntiles + kXcd - 1) / kXcd) * kXcd * p.nrb;
-        hipLaunchKernelGGL(lm_gemm_kernel, dim3(blocks), dim3(kGThreads), 0, stream, p, ntiles);
+    if (a.rows <= kStreamRows) {
+        // one row tile: 64-id parts, the weight streamed by 4 waves
+        p.nrb = 1;
+        // every XCD gets ceil(nparts / 8) parts' worth of workgroups; those of
+        // parts past the end leave at once
+        const int blocks = ((p.nparts + kXcd - 1) / kXcd) * kXcd;
+        hipLaunchKernelGGL((lm_head_kernel<1, 2>), dim3(blocks), dim3(kThreads), 0, stream, p);
         return hipGetLastError();
     }
-    const int tiles = (a.rows + 15) / 16;
-    const int nr = tiles < 4 ? tiles : 4;
-    p.nrb = (tiles + nr - 1) / nr;
-    // every XCD gets ceil(nparts / 8) parts' worth of workgroups; those of
-    // parts past the end leave at once
-    const int blocks = ((p.nparts + kXcd - 1) / kXcd) * kXcd * p.nrb;
-    switch (nr) {
-        case 1: launch_nr<1, 2>(p, blocks, stream); break;
-        case 2: launch_nr<2, 2>(p, blocks, stream); break;
-        case 3: launch_nr<3, 2>(p, blocks, stream); break;
-        default: launch_nr<4, 2>(p, blocks, stream); break;
-    }
+    // row blocks x id tiles; every XCD gets ceil(ntiles / 8) tiles' worth of
+    // workgroups, those past the end leave at once
+    const bool big = a.rows > kSmallRows;
+    const int rt = (a.rows + 15) / 16;  // up to 64 rows: one row block of rt row tiles
+    const int gm = big ? kGM : 16 * rt, gn = big ? kGN : kRowsGN;
+    const int ntiles = (a.V + gn - 1) / gn;
+    p.nrb = (a.rows + gm - 1) / gm;
+    const int blocks = ((ntiles + kXcd - 1) / kXcd) * kXcd * p.nrb;
+    if (big)
+        hipLaunchKernelGGL(lm_gemm_kernel, dim3(blocks), dim3(kGThreads), 0, stream, p, ntiles);
+    else if (rt == 2)
+        hipLaunchKernelGGL(lm_gemm_rows_kernel<2>, dim3(blocks), dim3(kRowsThreads), 0, stream, p, ntiles);
+    else if (rt == 3)
+        hipLaunchKernelGGL(lm_gemm_rows_kernel<3>, dim3(blocks), dim3(kRowsThreads), 0, stream, p, ntiles);
+    else
+        hipLaunchKernelGGL(lm_gemm_rows_kernel<4>, dim3(blocks), dim3(kRowsThreads), 0, stream, p, ntiles);
     return hipGetLastError();
 }
 

@@ -51,6 +51,8 @@ def combine_parts(pm, ps, T):
 
 @pytest.mark.parametrize("rows,H,V", [(48, 512, 12288), (5, 96, 1000), (130, 64, 302),
                                       (16, 2048, 4096), (1, 32, 129),
+                                      # 17 to 64 rows: 192-id tiles of 2, 3 or 4 row tiles
+                                      (17, 96, 500), (40, 224, 2000), (64, 32, 193),
                                       # more than 64 rows: the LDS-staged tiles (192 rows x 256
                                       # ids): several row blocks, partial id tiles, every count
                                       # of 32-wide steps modulo the five stages, one step
