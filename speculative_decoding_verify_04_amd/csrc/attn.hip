@@ -34,6 +34,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <vector>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -90,8 +91,11 @@ constexpr int kPlanB = kAttnPlanB;
 struct DecPlan {
     int nb;                    // B when the plan is valid; 0: find the plan on the device
     int q[kPlanB + 1];         // q[b] = first chunk of sequence b; q[nb] = chunks in all
+                               // (even split: q[b] = slices of the sequences before b)
     int s[kPlanB];             // 16-key slices of sequence b for its host bound
     int row0[kPlanB + 1];      // first query row of sequence b; row0[nb] = query rows
+    int W;                     // even split: slice ranges per kv head (0: per-sequence chunks)
+    long long N;               // even split: slices of all sequences (one kv head)
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -240,6 +244,50 @@ struct DecLdsCol {
     int flag;
 };
 
+// Online softmax of one 16-column tile's scores on one 16-key slice (S^T tile
+// `acc`: keys k0 + kg*4 + ee of column col16; keys at or past `limt` masked
+// unless `full`) and O^T += V^T P^T with the slice's V^T operands `va`.
+template <int DT>
+__device__ __forceinline__ void col_tile_update(int kg, float scale_log2, int k0, bool full, int limt,
+                                                const floatx4& acc, const shortx4 (&va)[DT], float& mr,
+                                                float& lr, floatx4 (&ot)[DT]) {
+    float s[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int ee = 0; ee < 4; ++ee) {
+        const int tt = k0 + kg * 4 + ee;
+        s[ee] = (full || tt < limt) ? acc[ee] * scale_log2 : -INFINITY;
+        mt = fmaxf(mt, s[ee]);
+    }
+    mt = colmax4(mt);
+    const float mnew = fmaxf(mr, mt);
+    // the running max of no column of the tile grew: alpha would be exactly 1
+    // on every lane, so the rescale of O is skipped (most slices after the
+    // first few)
+    const bool grew = __ballot(mt > mr) != 0;
+    float alpha = 1.0f;
+    shortx4 pb;
+    if (mnew == -INFINITY) {
+        pb = shortx4{0, 0, 0, 0};
+    } else {
+        if (grew) alpha = __builtin_amdgcn_exp2f(mr - mnew);
+        float pe[4];
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) pe[ee] = __builtin_amdgcn_exp2f(s[ee] - mnew);
+        lr = lr * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
+        mr = mnew;
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) pb[ee] = static_cast<short>(f32_to_bf16(pe[ee]));
+    }
+    if (grew) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) ot[dt] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        ot[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, ot[dt], 0, 0, 0);
+}
+
 // Merge of the partials of (sequence, kv head g) when no prefix part is
 // involved and every value a thread needs fits in registers (UP (d, column)
 // pairs per thread, PMAX parts): the partial loads are issued before the
@@ -247,7 +295,7 @@ struct DecLdsCol {
 // in LDS; fixed order, as in dec_merge.
 template <int D, int UP, int PMAX, typename MRG>
 __device__ __forceinline__ void merge_in_registers(const AttnParams& p, MRG& M, int g, int first_slot,
-                                                   int nparts, int nc, int qrow0, int k1) {
+                                                   int stride, int nparts, int nc, int qrow0, int k1) {
     const int tid = threadIdx.x;
     const int CPG = p.CPG, npairs = nc * D;
     float ov[PMAX][UP];
@@ -260,7 +308,7 @@ __device__ __forceinline__ void merge_in_registers(const AttnParams& p, MRG& M, 
 #pragma unroll
     for (int jj = 0; jj < PMAX; ++jj) {
         const int j = min(jj, nparts - 1);  // past the end: re-read the last part
-        const float* pb = p.part_o + (static_cast<size_t>(first_slot) + static_cast<size_t>(j) * p.Hkv) * D * CPG;
+        const float* pb = p.part_o + (static_cast<size_t>(first_slot) + static_cast<size_t>(j) * stride) * D * CPG;
 #pragma unroll
         for (int u = 0; u < UP; ++u) ov[jj][u] = ld_coh(pb + off[u]);
     }
@@ -268,7 +316,7 @@ __device__ __forceinline__ void merge_in_registers(const AttnParams& p, MRG& M, 
     for (int idx = tid; idx < nparts * nc; idx += kThreads) {
         const int j = idx / nc, col = idx % nc;
         const unsigned long long u = ld_coh(reinterpret_cast<const unsigned long long*>(
-            p.part_ml + (static_cast<size_t>(first_slot) + static_cast<size_t>(j) * p.Hkv) * CPG + col));
+            p.part_ml + (static_cast<size_t>(first_slot) + static_cast<size_t>(j) * stride) * CPG + col));
         M.ml[idx] = make_float2(__uint_as_float(static_cast<unsigned>(u)),
                                 __uint_as_float(static_cast<unsigned>(u >> 32)));
     }
@@ -303,12 +351,12 @@ __device__ __forceinline__ void merge_in_registers(const AttnParams& p, MRG& M, 
 }
 
 // Merge every part of (sequence b, kv head g) -- the prefix chunks first, then
-// its q_b chunks in order -- and write the output rows qrow0+j (j < k1) of heads
-// g*G + hh.  Two round trips: the (m, l) of every (part, column) into LDS and
+// its q_b chunks in order, at partial slots first_slot + j*stride -- and write
+// the output rows qrow0+j (j < k1) of heads g*G + hh.  Two round trips: the (m, l) of every (part, column) into LDS and
 // the per-column weights, then every o value weighted, with the loads of up
 // to 4 columns x 8 parts in flight per thread.  Fixed order: bit-reproducible.
 template <int D, int NCT, typename MRG>
-__device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_slot, int qb,
+__device__ __forceinline__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_slot, int stride, int qb,
                           int qrow0, int k1) {
     const int tid = threadIdx.x;
     const int np = p.prefix_slots;
@@ -317,14 +365,15 @@ __device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_s
     const int ncols = p.G * k1;  // the sequence's columns (hh * k1 + j)
     const size_t pre_col0 = static_cast<size_t>(g) * p.NC + static_cast<size_t>(b) * CPG;
     auto slot_of = [&](int j) {  // partial slot of stream part j >= np
-        return static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * p.Hkv;
+        return static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * stride;
     };
-    const int group = max(1, min(ncols, kMergeLds / nparts));
+    constexpr int cap = static_cast<int>(sizeof(M.w) / sizeof(M.w[0]));  // (part, column) pairs in LDS
+    const int group = max(1, min(ncols, cap / nparts));
     if (np == 0 && group == ncols) {
         // every partial value a thread needs fits in registers: one round trip
         const int npairs = ncols * D;
         if (nparts <= 8 && npairs <= 4 * kThreads) {
-            merge_in_registers<D, 4, 8>(p, M, g, first_slot, nparts, ncols, qrow0, k1);
+            merge_in_registers<D, 4, 8>(p, M, g, first_slot, stride, nparts, ncols, qrow0, k1);
             return;
         }
         // (the wider forms only where the kernel's loop already needs more
@@ -332,11 +381,11 @@ __device__ void dec_merge(const AttnParams& p, MRG& M, int b, int g, int first_s
         // per CU)
         if constexpr (NCT > 1) {
             if (nparts <= 4 && npairs <= 8 * kThreads) {
-                merge_in_registers<D, 8, 4>(p, M, g, first_slot, nparts, ncols, qrow0, k1);
+                merge_in_registers<D, 8, 4>(p, M, g, first_slot, stride, nparts, ncols, qrow0, k1);
                 return;
             }
             if (nparts <= 2 && npairs <= 20 * kThreads) {
-                merge_in_registers<D, 20, 2>(p, M, g, first_slot, nparts, ncols, qrow0, k1);
+                merge_in_registers<D, 20, 2>(p, M, g, first_slot, stride, nparts, ncols, qrow0, k1);
                 return;
             }
         }
@@ -705,46 +754,9 @@ void decode_bf16_kernel(AttnParams p, DecPlan plan) {
         for (int dt = 0; dt < DT; ++dt) o[ct][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Online softmax of one column tile's scores on one slice (S^T tile
-    // `acc`, keys k0 + kg*4 + ee) and O^T += V^T P^T with the slice's V^T
-    // operands.
     auto tile_update = [&](int k0, bool full, int limt, const floatx4& acc, const shortx4 (&va)[DT],
                            float& mr, float& lr, floatx4 (&ot)[DT]) __attribute__((always_inline)) {
-        float s[4];
-        float mt = -INFINITY;
-#pragma unroll
-        for (int ee = 0; ee < 4; ++ee) {
-            const int tt = k0 + kg * 4 + ee;
-            s[ee] = (full || tt < limt) ? acc[ee] * p.scale_log2 : -INFINITY;
-            mt = fmaxf(mt, s[ee]);
-        }
-        mt = colmax4(mt);
-        const float mnew = fmaxf(mr, mt);
-        // the running max of no column of the tile grew: alpha would be
-        // exactly 1 on every lane, so the rescale of O is skipped (most
-        // slices after the first few)
-        const bool grew = __ballot(mt > mr) != 0;
-        float alpha = 1.0f;
-        shortx4 pb;
-        if (mnew == -INFINITY) {
-            pb = shortx4{0, 0, 0, 0};
-        } else {
-            if (grew) alpha = __builtin_amdgcn_exp2f(mr - mnew);
-            float pe[4];
-#pragma unroll
-            for (int ee = 0; ee < 4; ++ee) pe[ee] = __builtin_amdgcn_exp2f(s[ee] - mnew);
-            lr = lr * alpha + ((pe[0] + pe[1]) + (pe[2] + pe[3]));
-            mr = mnew;
-#pragma unroll
-            for (int ee = 0; ee < 4; ++ee) pb[ee] = static_cast<short>(f32_to_bf16(pe[ee]));
-        }
-        if (grew) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) ot[dt] *= alpha;
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            ot[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[dt], pb, ot[dt], 0, 0, 0);
+        col_tile_update<DT>(kg, p.scale_log2, k0, full, limt, acc, va, mr, lr, ot);
     };
     auto softmax_pv = [&](int k0, const floatx4 (&acc)[NCT], const shortx4 (&va)[DT]) __attribute__((always_inline)) {
         const bool full = k0 + 15 < L;  // no key of the slice is masked for any column
@@ -922,7 +934,457 @@ void decode_bf16_kernel(AttnParams p, DecPlan plan) {
     }
     }
     if (arrive_last(p.merge_cnt + static_cast<size_t>(b) * p.Hkv + g, qb, &S.flag))
-        dec_merge<D, NCT>(p, S.mrg, b, g, first_slot + g, qb, q0, k1);
+        dec_merge<D, NCT>(p, S.mrg, b, g, first_slot + g, p.Hkv, qb, q0, k1);
+}
+
+// ---- Column waves over an even split of the slices (grouped heads, D = 128).
+//
+// The 16-key slices of all sequences are laid end to end (N in all, one kv
+// head's worth) and cut into W equal ranges; workgroup r * Hkv + g takes range
+// r of kv head g, so every resident workgroup gets the same work in one round
+// and the Hkv workgroups of a range, dispatched together, read the same cache
+// rows at the same time.  (Per-sequence chunks of at most 192 slices need
+// about 1.6 rounds on the B=64, K=8 workload, and each workgroup streams at
+// the same rate whether the round is full or not, so the partly filled second
+// round took as long as a full one.)  A range meets one or more sequences;
+// its part of sequence b is a piece with its own partial at slot (r + b) *
+// Hkv + g, so the pieces of a (sequence, kv head) sit Hkv slots apart and no
+// two pieces share a slot.  The pieces pass through a seven-slot ring (six
+// items in flight) as one stream of items: for each piece its query tiles (two tiles per item, in the
+// K and V halves of a slot), then its slices.  Each wave counts the vector
+// memory operations it issues (ring loads and partial stores; they complete
+// in issue order), so the wait for an item is exact even when a piece's
+// partial stores sit between it and the later items.  A piece that is all of
+// its sequence writes the output itself; for the others, at its end the
+// workgroup counts itself in the arrival counter of their (sequence, kv head)
+// pairs, and the last arriver merges that pair's pieces.
+constexpr int kPieceMax = 8;
+constexpr int kStreamMerge = 512;  // (part, column) pairs a merge stages in LDS at a time
+constexpr int kStreamSlots = 7;    // ring slots: six items in flight
+
+struct StreamPiece {
+    int b, g;      // sequence, kv head
+    int lo, n;     // first slice of the piece; slices with keys on the device (-1: bad sequence)
+    int L, q0, k1; // device cache length, first query row, query rows
+    int whole;     // the piece is all of the sequence: its result is the output
+    long long kv0; // first cache row of the sequence
+};
+
+struct DecLdsStream {
+    struct {
+        float2 ml[kStreamMerge];
+        float w[kStreamMerge];
+    } mrg;
+    StreamPiece pc[kPieceMax];
+    int np;
+    int last[kPieceMax];
+};
+
+// A position in a workgroup's item stream: piece k, item i of its `items`
+// (the query items, then the piece's slices), and the piece's parameters as
+// wave-uniform values.
+struct StreamCursor {
+    int k, i, items;
+    int b, g, lo, n, L, q0, k1, whole;
+    long long kv0;
+};
+
+__device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uniform_i64(long long v) {
+    return static_cast<long long>(
+        (static_cast<unsigned long long>(static_cast<unsigned>(uniform_i32(static_cast<int>(v >> 32))))
+         << 32) |
+        static_cast<unsigned>(uniform_i32(static_cast<int>(v))));
+}
+
+// Piece k's parameters into the cursor (item 0).
+template <int NQI>
+__device__ __forceinline__ void stream_at(StreamCursor& c, const DecLdsStream& S, int k) {
+    const StreamPiece& P = S.pc[k];
+    c.k = k;
+    c.i = 0;
+    c.b = uniform_i32(P.b);
+    c.g = uniform_i32(P.g);
+    c.lo = uniform_i32(P.lo);
+    c.n = uniform_i32(P.n);
+    c.L = uniform_i32(P.L);
+    c.q0 = uniform_i32(P.q0);
+    c.k1 = uniform_i32(P.k1);
+    c.whole = uniform_i32(P.whole);
+    c.kv0 = uniform_i64(P.kv0);
+    c.items = c.n > 0 ? NQI + c.n : 0;
+}
+
+// Where this wave's two 16-byte loads of an item go: rows r0, r1 of the K half
+// (waves 0, 1) or the V half (waves 2, 3) of a slot, from 16-byte chunks
+// c0, c1 of their source rows (the row swizzle applied on the load side);
+// off0, off1: their element offsets from a slice's first cache row.
+struct StreamLoadLanes {
+    bool vhalf;
+    int dst, r0, r1, c0, c1, off0, off1;
+};
+
+// Issue this wave's loads of the cursor's current item into slot R.
+template <int NQI>
+__device__ __forceinline__ void stream_issue(const AttnParams& p, DecColSlot& R, const StreamCursor& c,
+                                             const StreamLoadLanes& ln) {
+    constexpr int D = 128;
+    const uint16_t* src0;
+    const uint16_t* src1;
+    if (c.i < NQI) {
+        // query tiles 2i (K half) and 2i + 1 (V half); padding columns repeat
+        // the last column (finite, never stored)
+        const int ncl = p.G * c.k1;
+        const int col0 = min(32 * c.i + (ln.vhalf ? 16 : 0) + ln.r0, ncl - 1);
+        const int col1 = min(32 * c.i + (ln.vhalf ? 16 : 0) + ln.r1, ncl - 1);
+        src0 = p.q + (static_cast<size_t>(c.q0 + col0 % c.k1) * p.Hq + c.g * p.G + col0 / c.k1) * D + ln.c0 * 8;
+        src1 = p.q + (static_cast<size_t>(c.q0 + col1 % c.k1) * p.Hq + c.g * p.G + col1 / c.k1) * D + ln.c1 * 8;
+    } else if ((c.lo + c.i - NQI) * 16 + 15 < c.L) {
+        // every row of the slice is a cache row: a uniform base
+        const size_t base = static_cast<size_t>(c.kv0 + (c.lo + c.i - NQI) * 16) * p.Hkv * D;
+        const uint16_t* cache = (ln.vhalf ? p.v_cache : p.k_cache) + base;
+        src0 = cache + ln.off0;
+        src1 = cache + ln.off1;
+    } else {
+        // keys < L are cache rows, the next k1 the new rows; keys past the
+        // last one are clamped to it (and masked)
+        const int k0 = (c.lo + c.i - NQI) * 16;
+        const int T = c.L + c.k1;
+        const int t0 = min(k0 + ln.r0, T - 1), t1 = min(k0 + ln.r1, T - 1);
+        const size_t rs = static_cast<size_t>(p.Hkv) * D, head = static_cast<size_t>(c.g) * D;
+        const uint16_t* cache = ln.vhalf ? p.v_cache : p.k_cache;
+        const uint16_t* fresh = ln.vhalf ? p.v_new : p.k_new;
+        src0 = ((t0 < c.L) ? cache + static_cast<size_t>(c.kv0 + t0) * rs
+                           : fresh + static_cast<size_t>(c.q0 + (t0 - c.L)) * rs) + head + ln.c0 * 8;
+        src1 = ((t1 < c.L) ? cache + static_cast<size_t>(c.kv0 + t1) * rs
+                           : fresh + static_cast<size_t>(c.q0 + (t1 - c.L)) * rs) + head + ln.c1 * 8;
+    }
+    __builtin_amdgcn_global_load_lds(src0, (ln.vhalf ? R.v : R.k) + ln.dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src1, (ln.vhalf ? R.v : R.k) + ln.dst + 64, 16, 0, 0);
+}
+
+// Running state of a column wave's tile over the current piece.
+template <int KK, int DT>
+struct StreamTile {
+    float m, l;
+    floatx4 o[DT];
+    bf16x8 qv[KK];
+};
+
+// Store the compute wave's tile partial at `slot` -- or, for a piece that is
+// all of its sequence (`whole`), the normalised output rows q0 + j of heads
+// g*G + hh -- and reset the state.  Returns the vector memory operations
+// issued, counted low: the (m, l) store, issued only where kg == 0, is left
+// out.
+template <int KK, int DT>
+__device__ __forceinline__ int stream_store(const AttnParams& p, StreamTile<KK, DT>& t, bool cw, int w,
+                                            int colw, int kg, size_t slot, int ncl, bool whole, int q0,
+                                            int k1, int g) {
+    constexpr int D = 128;
+    int ops = 0;
+    t.l = colsum4(t.l);
+    // (opaque copies of the lane's column and key group: the store addresses
+    // are formed here, not hoisted out of the item loop where they would hold
+    // registers)
+    asm volatile("" : "+v"(colw), "+v"(kg));
+    if (whole) {
+        // a single part: the merge would weight it by exactly 1 / l
+        if (cw && w * 16 < ncl) {
+            if (colw < ncl) {
+                const float inv = 1.0f / t.l;
+                const int hh = colw / k1, j = colw - hh * k1;
+                uint16_t* orow = static_cast<uint16_t*>(p.out) +
+                                 (static_cast<size_t>(q0 + j) * p.Hq + g * p.G + hh) * D + kg * 4;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const unsigned lo = f32_to_bf16(t.o[dt][0] * inv) | (f32_to_bf16(t.o[dt][1] * inv) << 16);
+                    const unsigned hi = f32_to_bf16(t.o[dt][2] * inv) | (f32_to_bf16(t.o[dt][3] * inv) << 16);
+                    *reinterpret_cast<uint2*>(orow + dt * 16) = make_uint2(lo, hi);
+                }
+            }
+            ops = DT;
+        }
+    } else if (cw && w * 16 < ncl) {
+        if (colw < ncl) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee)
+                    st_coh(p.part_o + (slot * D + dt * 16 + kg * 4 + ee) * p.CPG + colw, t.o[dt][ee]);
+            if (kg == 0) {
+                const unsigned long long v =
+                    (static_cast<unsigned long long>(__float_as_uint(t.l)) << 32) | __float_as_uint(t.m);
+                st_coh(reinterpret_cast<unsigned long long*>(p.part_ml + slot * p.CPG + colw), v);
+            }
+        }
+        ops = DT * 4;
+    }
+    t.m = -INFINITY;
+    t.l = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) t.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    return ops;
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n computed at run time (n > 63: 63).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define SV_VMC(c) case c: __builtin_amdgcn_s_waitcnt(0x0F70 | ((c) & 15) | (((c) >> 4) << 14)); break;
+#define SV_VMC8(c) SV_VMC(c) SV_VMC(c + 1) SV_VMC(c + 2) SV_VMC(c + 3) SV_VMC(c + 4) SV_VMC(c + 5) \
+    SV_VMC(c + 6) SV_VMC(c + 7)
+    switch (n) {
+        SV_VMC8(0) SV_VMC8(8) SV_VMC8(16) SV_VMC8(24) SV_VMC8(32) SV_VMC8(40) SV_VMC8(48)
+        SV_VMC(56) SV_VMC(57) SV_VMC(58) SV_VMC(59) SV_VMC(60) SV_VMC(61) SV_VMC(62)
+        default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15 | (3 << 14)); break;
+    }
+#undef SV_VMC8
+#undef SV_VMC
+}
+
+// The range that holds slice x of the even split.
+__device__ __forceinline__ int stream_owner(long long x, int W, long long N) {
+    return static_cast<int>(((x + 1) * W - 1) / N);
+}
+
+template <int NCT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_stream_kernel(AttnParams p, DecPlan plan) {
+    constexpr int D = 128;
+    constexpr int KK = D / 32, DT = D / 16;
+    constexpr int NQI = (NCT + 1) / 2;  // ring items holding a piece's query tiles
+    __shared__ DecLdsStream S;
+    __shared__ DecColSlot C0, C1, C2, C3, C4, C5, C6;  // kStreamSlots slots
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col16 = lane & 15, kg = lane >> 4;
+    const int Hkv = p.Hkv, W = plan.W;
+    const int wg = blockIdx.x, rg = wg / Hkv, hg = wg - rg * Hkv;  // range, kv head
+    const long long N = plan.N;
+    const long long x0 = static_cast<long long>(rg) * N / W;
+    const long long x1 = static_cast<long long>(rg + 1) * N / W;
+
+    // ---- the pieces of [x0, x1): wave 0, lane k records piece k
+    if (w == 0) {
+        int pb = 0, plo = 0, phi = 0, np = 0;
+        long long x = x0;
+        while (x < x1 && np < kPieceMax) {
+            int cnt = 0;  // sequence of slice x: the sequences whose slices all precede it
+            for (int b0 = 0; b0 < plan.nb; b0 += 64) {
+                const int bb = b0 + lane;
+                cnt += __popcll(__ballot((bb < plan.nb) && plan.q[bb + 1] <= x));
+            }
+            const int b = uniform_i32(cnt);
+            const int lo = static_cast<int>(x - plan.q[b]);
+            const int len = static_cast<int>(min(static_cast<long long>(plan.s[b] - lo), x1 - x));
+            if (lane == np) {
+                pb = b;
+                plo = lo;
+                phi = lo + len;
+            }
+            ++np;
+            x += len;
+        }
+        if (x < x1 && lane == 0) set_status(p.status, 3);  // more pieces than the host plan allows
+        if (lane < np) {
+            // the sequence's device data: every workgroup of a sequence takes
+            // the same decision, so a bad sequence arrives nowhere
+            const int q0 = plan.row0[pb], k1 = plan.row0[pb + 1] - q0;
+            const int L = p.kv_len[pb];
+            const long long kv0 = p.kv_start[pb];
+            bool bad = (L < 0) || (static_cast<long long>(L) + k1 > 16LL * plan.s[pb]);
+            if (p.cu_q) bad = bad || (p.cu_q[pb] != q0) || (p.cu_q[pb + 1] != q0 + k1);
+            if (bad) set_status(p.status, 3);
+            const int n = bad ? -1 : max(0, min(phi, ceil_div(L + k1, 16)) - plo);
+            const int whole = (plo == 0 && phi == plan.s[pb]) ? 1 : 0;
+            S.pc[lane] = StreamPiece{pb, hg, plo, n, L, q0, k1, whole, kv0};
+        }
+        if (lane == 0) S.np = np;
+    }
+    __syncthreads();
+    const int np = S.np;
+    int nitems = 0;
+    for (int k = 0; k < np; ++k) {
+        const int n = S.pc[k].n;
+        nitems += n > 0 ? NQI + n : 0;
+    }
+
+    // loads: wave w fills blocks 2(w&1), 2(w&1)+1 of the K half (waves 0, 1)
+    // or the V half (waves 2, 3) of a slot
+    StreamLoadLanes ln;
+    ln.vhalf = w >= 2;
+    ln.dst = 2 * (w & 1) * 64;
+    ln.r0 = 2 * (w & 1) * 4 + (lane >> 4);
+    ln.r1 = ln.r0 + 4;
+    ln.c0 = (lane & 15) ^ prefix_swz(ln.r0);
+    ln.c1 = (lane & 15) ^ prefix_swz(ln.r1);
+    ln.off0 = ln.r0 * Hkv * D + hg * D + ln.c0 * 8;
+    ln.off1 = ln.r1 * Hkv * D + hg * D + ln.c1 * 8;
+    // the loader's cursor: at the first piece with items
+    StreamCursor lc{};
+    lc.k = -1;
+    for (int k = 0; k < np && lc.k < 0; ++k)
+        if (S.pc[k].n > 0) stream_at<NQI>(lc, S, k);
+    auto lnext = [&]() __attribute__((always_inline)) {
+        if (++lc.i == lc.items) {
+            int k = lc.k + 1;
+            while (k < np && S.pc[k].n <= 0) ++k;
+            if (k < np) stream_at<NQI>(lc, S, k);
+        }
+    };
+
+    // compute: wave w < NCT holds column tile w of the current piece
+    const bool cw = w < NCT;
+    const int colw = w * 16 + col16;
+    // K operand of a slot: row col16, logical chunk kg + 4 kk, at (kg ^ (sk &
+    // 3)) + 4 (kk ^ (sk >> 2)); V^T operand: row kg*4 + col16/4 (as the
+    // grouped-head ring of decode_bf16_kernel)
+    const int csk = prefix_swz(col16);
+    const int ckcol = col16 * 16 + (kg ^ (csk & 3));
+    const int csk2 = csk >> 2;
+    const int crv = kg * 4 + (col16 >> 2);
+    const int csv = prefix_swz(crv);
+    const int csv1 = csv >> 1;
+    const int cvcol = crv * D + 8 * (((col16 & 3) >> 1) ^ (csv & 1)) + 4 * (col16 & 1);
+    StreamTile<KK, DT> t;
+    t.m = -INFINITY;
+    t.l = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) t.o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) t.qv[kk] = bf16x8{};
+    int iss = 0;  // vector memory operations this wave has issued (counted low)
+    // the compute cursor: pieces of no slice on the device before the first
+    // piece with items store an empty partial (their segment counts them),
+    // bad sequences nothing
+    StreamCursor cc{};
+    cc.k = -1;
+    int climw = 0;  // causal limit of this lane's column in the current piece
+    for (int k = 0; k < np && cc.k < 0; ++k) {
+        const int n = S.pc[k].n;
+        if (n > 0) {
+            stream_at<NQI>(cc, S, k);
+            climw = (cw && colw < p.G * cc.k1) ? cc.L + colw % cc.k1 + 1 : 0;
+        } else if (n == 0) {
+            iss += stream_store<KK, DT>(p, t, cw, w, colw, kg, static_cast<size_t>(rg + S.pc[k].b) * Hkv + hg,
+                                        p.G * S.pc[k].k1, false, 0, 1, hg);
+        }
+    }
+    auto cnext = [&]() __attribute__((always_inline)) {
+        if (++cc.i == cc.items) {
+            // the piece is done: its partial, then those of the empty pieces
+            // up to the next one with items
+            iss += stream_store<KK, DT>(p, t, cw, w, colw, kg, static_cast<size_t>(rg + cc.b) * Hkv + hg,
+                                        p.G * cc.k1, cc.whole != 0, cc.q0, cc.k1, hg);
+            int k = cc.k + 1;
+            for (; k < np && S.pc[k].n <= 0; ++k)
+                if (S.pc[k].n == 0)
+                    iss += stream_store<KK, DT>(p, t, cw, w, colw, kg,
+                                                static_cast<size_t>(rg + S.pc[k].b) * Hkv + hg,
+                                                p.G * S.pc[k].k1, false, 0, 1, hg);
+            if (k < np) {
+                stream_at<NQI>(cc, S, k);
+                climw = (cw && colw < p.G * cc.k1) ? cc.L + colw % cc.k1 + 1 : 0;
+            }
+        }
+    };
+    // item in slot R: the query tiles into registers, or one slice's products
+    auto compute = [&](DecColSlot& R) __attribute__((always_inline)) {
+        if (cc.i < NQI) {
+            if (cw && (w >> 1) == cc.i) {
+                const uint4* src = (w & 1) ? R.v : R.k;
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    t.qv[kk] = *reinterpret_cast<const bf16x8*>(src + ckcol + 4 * (kk ^ csk2));
+            }
+        } else if (cw) {
+            const int k0 = (cc.lo + cc.i - NQI) * 16;
+            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(R.k + ckcol + 4 * (kk ^ csk2));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, t.qv[kk], acc, 0, 0, 0);
+            }
+            const uint16_t* vb = reinterpret_cast<const uint16_t*>(R.v);
+            shortx4 va[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) va[dt] = lds_read_tr16(vb + cvcol + 16 * (dt ^ csv1));
+            col_tile_update<DT>(kg, p.scale_log2, k0, k0 + 15 < cc.L, climw, acc, va, t.m, t.l, t.o);
+        }
+    };
+
+    constexpr int AHEAD = kStreamSlots - 1;  // items in flight
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0, a4 = 0, a5 = 0, a6 = 0;  // iss after each slot's loads
+#define SV_ISSUE(R, A)                     \
+    do {                                   \
+        stream_issue<NQI>(p, R, lc, ln);   \
+        lnext();                           \
+        iss += 2;                          \
+        A = iss;                           \
+    } while (0)
+    // one ring step: item j is in once this wave's loads of it are done and
+    // every wave passed the barrier; slot Rn (item j-1) is then free for
+    // item j + AHEAD
+#define SV_STEP(J, R, Rn, A, An)                                      \
+    do {                                                              \
+        {                                                             \
+            const int vm_ = uniform_i32(iss - (A));                   \
+            if (vm_ == 2 * (AHEAD - 1)) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (AHEAD - 1))); \
+            else wait_vmcnt(vm_);                                     \
+        }                                                             \
+        __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): LDS reads done */ \
+        __builtin_amdgcn_s_barrier();                                 \
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local"); \
+        if ((J) + AHEAD < nitems) SV_ISSUE(Rn, An);                   \
+        compute(R);                                                   \
+        cnext();                                                      \
+    } while (0)
+    static_assert(kStreamSlots == 7 && 2 * (AHEAD - 1) < 16, "the ring below has seven slots");
+    if (nitems > 0) SV_ISSUE(C0, a0);
+    if (nitems > 1) SV_ISSUE(C1, a1);
+    if (nitems > 2) SV_ISSUE(C2, a2);
+    if (nitems > 3) SV_ISSUE(C3, a3);
+    if (nitems > 4) SV_ISSUE(C4, a4);
+    if (nitems > 5) SV_ISSUE(C5, a5);
+    for (int j = 0; j < nitems; j += 7) {
+        SV_STEP(j, C0, C6, a0, a6);
+        if (j + 1 < nitems) SV_STEP(j + 1, C1, C0, a1, a0);
+        if (j + 2 < nitems) SV_STEP(j + 2, C2, C1, a2, a1);
+        if (j + 3 < nitems) SV_STEP(j + 3, C3, C2, a3, a2);
+        if (j + 4 < nitems) SV_STEP(j + 4, C4, C3, a4, a3);
+        if (j + 5 < nitems) SV_STEP(j + 5, C5, C4, a5, a4);
+        if (j + 6 < nitems) SV_STEP(j + 6, C6, C5, a6, a5);
+    }
+#undef SV_STEP
+#undef SV_ISSUE
+
+    // ---- arrivals: every partial of this workgroup is stored; count it in
+    // the (sequence, kv head) of each piece that is not the whole sequence
+    // (nor of a bad one); the last arriver merges that pair's pieces
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        for (int k = 0; k < np; ++k) {
+            const StreamPiece& P = S.pc[k];
+            int last = 0;
+            if (P.n >= 0 && !P.whole) {
+                const long long st = plan.q[P.b];
+                const int parts = stream_owner(st + plan.s[P.b] - 1, W, N) - stream_owner(st, W, N) + 1;
+                int* cnt = p.merge_cnt + static_cast<size_t>(P.b) * Hkv + P.g;
+                const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = (old == parts - 1) ? 1 : 0;
+                if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            S.last[k] = last;
+        }
+    }
+    __syncthreads();
+    for (int k = 0; k < np; ++k) {
+        if (!S.last[k]) continue;
+        const int b = S.pc[k].b;
+        const long long st = plan.q[b];
+        const int r_lo = stream_owner(st, W, N);
+        const int parts = stream_owner(st + plan.s[b] - 1, W, N) - r_lo + 1;
+        dec_merge<D, NCT>(p, S.mrg, b, hg, (r_lo + b) * Hkv + hg, Hkv, parts, S.pc[k].q0, S.pc[k].k1);
+    }
 }
 
 template <int D>
@@ -1564,6 +2026,28 @@ int sk_resident_grid(int D, int nct) {
     return c;
 }
 
+// Workgroups of the even-split grouped-head kernel that the GPU holds at once.
+int sk_stream_resident(int nct) {
+    static int cache[16][4];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) {
+        (void)hipGetLastError();
+        return 512;  // no device: any value sizes a workspace that is never launched
+    }
+    int& c = cache[dev][nct - 1];
+    if (c > 0) return c;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    const void* fn = nct == 2 ? reinterpret_cast<const void*>(&decode_stream_kernel<2>)
+                   : nct == 3 ? reinterpret_cast<const void*>(&decode_stream_kernel<3>)
+                              : reinterpret_cast<const void*>(&decode_stream_kernel<4>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess) per_cu = 0;
+    (void)hipGetLastError();
+    if (cus <= 0 || per_cu <= 0) return 512;
+    c = cus * per_cu;
+    return c;
+}
+
 }  // namespace
 
 AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
@@ -1644,6 +2128,42 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
             pl.plan_q[B] = qrun;
             pl.plan_row0[B] = cu_q_host ? cu_q_host[B] : B * K1;
             pl.plan_nb = B;
+        }
+        // Column waves: the even split over one round of workgroups when
+        // every workgroup meets at most kPieceMax segments and every segment
+        // fits in the merge (else, or with SPECVERIFY_SK_CHUNKS=1, the
+        // per-sequence chunks above).
+        pl.plan_W = 0;
+        pl.plan_N = 0;
+        if (pl.plan_nb > 0 && sk_mode(D, pl.nct) == 2 && env_int("SPECVERIFY_SK_CHUNKS", 0) == 0) {
+            long long N = 0;  // slices of all sequences, one kv head
+            for (int b = 0; b < B; ++b) N += pl.plan_s[b];
+            const long long Wl = std::min<long long>(sk_stream_resident(pl.nct) / Hkv,
+                                                     std::max<long long>(1, N / kLambdaMin));
+            const int W = static_cast<int>(std::max<long long>(1, Wl));  // slice ranges
+            auto owner = [&](long long x) { return static_cast<int>(((x + 1) * W - 1) / N); };
+            std::vector<int> pieces(W, 0);
+            bool fits = N > 0;
+            long long st = 0;
+            for (int b = 0; b < B && fits; ++b) {
+                const int r0 = owner(st), r1 = owner(st + pl.plan_s[b] - 1);
+                if (r1 - r0 + 1 + pslots > kStreamMerge) fits = false;
+                for (int r = r0; r <= r1 && fits; ++r)
+                    if (++pieces[r] > kPieceMax) fits = false;
+                st += pl.plan_s[b];
+            }
+            if (fits) {
+                long long run = 0;
+                for (int b = 0; b < B; ++b) {
+                    pl.plan_q[b] = static_cast<int>(run);
+                    run += pl.plan_s[b];
+                }
+                pl.plan_q[B] = static_cast<int>(run);
+                pl.plan_W = W;
+                pl.plan_N = N;
+                pl.grid = W * Hkv;
+                slots = (static_cast<long long>(W) + B) * Hkv;
+            }
         }
     } else {
         chunk = env_int("SPECVERIFY_ATTN_CHUNK", 0);
@@ -1758,6 +2278,8 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
         const int nct = pl.nct;
         DecPlan dp;
         dp.nb = pl.plan_nb;
+        dp.W = pl.plan_W;
+        dp.N = pl.plan_N;
         for (int b = 0; b <= pl.plan_nb && pl.plan_nb > 0; ++b) {
             dp.q[b] = pl.plan_q[b];
             dp.row0[b] = pl.plan_row0[b];
@@ -1778,7 +2300,23 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream
                                p, dp);                                                             \
     } while (0)
         const int mode = sk_mode(a.D, nct);
-        if (a.D == 128 && mode == 2) {
+        if (pl.plan_W > 0) {
+            dim3 sgrid(pl.plan_W * a.Hkv);
+#define SV_STREAM(NN)                                                                              \
+    do {                                                                                           \
+        if (a.ev_start && a.ev_stop)                                                               \
+            hipExtLaunchKernelGGL((decode_stream_kernel<NN>), sgrid, dim3(kThreads), 0, stream,    \
+                                  a.ev_start, a.ev_stop, 0, p, dp);                                \
+        else                                                                                       \
+            hipLaunchKernelGGL((decode_stream_kernel<NN>), sgrid, dim3(kThreads), 0, stream, p, dp); \
+    } while (0)
+            switch (nct) {
+                case 2: SV_STREAM(2); break;
+                case 3: SV_STREAM(3); break;
+                default: SV_STREAM(4); break;
+            }
+#undef SV_STREAM
+        } else if (a.D == 128 && mode == 2) {
             switch (nct) {
                 case 2: SV_DECODE(128, 2, 2); break;
                 case 3: SV_DECODE(128, 3, 2); break;

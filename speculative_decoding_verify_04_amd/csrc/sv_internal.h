@@ -47,6 +47,12 @@ struct AttnPlan {
     int plan_q[kAttnPlanB + 1];
     int plan_s[kAttnPlanB];
     int plan_row0[kAttnPlanB + 1];
+    // grouped heads (column waves): the slices of all sequences cut into
+    // plan_W equal ranges, each taken by Hkv workgroups, one per kv head
+    // (plan_W = 0: per-sequence chunks); plan_q then holds slice prefix sums,
+    // plan_N all slices
+    int plan_W;
+    long long plan_N;
     size_t bytes;          // whole workspace: counter region, then data region
     size_t counter_bytes;  // the counter region (B * Hkv arrival counters, 256-byte rounded)
     bool ok;  // false: the sequences are too long for the merge (unsupported)

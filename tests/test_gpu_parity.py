@@ -194,6 +194,9 @@ SMALL_ATTN = {
                                        len_hi=2500, V=64),
     "bf16_gqa_many_items": W.small_variant(W.CONFIGS["gqa_b64k8"], B=24, K=5, Hq=8, Hkv=2,
                                            len_lo=700, len_hi=3000, V=64),
+    # grouped heads over the even split of the slices, with a shared prefix
+    "bf16_prefix_gqa_even": W.small_variant(W.CONFIGS["prefix_b32k4"], B=6, K=4, Hq=8, Hkv=2,
+                                            prefix_len=700, len_lo=100, len_hi=600, V=64),
     # more work items than workgroups resident at once (one chunk each)
     "bf16_more_items_than_resident": W.small_variant(W.CONFIGS["bass_b8k5"], B=600, K=3, Hq=2,
                                                      Hkv=2, len_lo=0, len_hi=80, V=64),
@@ -215,6 +218,26 @@ def test_attention_small(name):
     err = attn_errors(o, ref)
     assert np.isfinite(o).all()
     assert err.max() <= attn_tol(cfg), (name, float(err.max()))
+
+
+# shapes that run the grouped-head kernel (D = 128, more than 16 query columns
+# per kv head); by default over the even split of the slices
+GQA_RING = ["bf16_gqa_k8", "bf16_gqa_many_items", "bf16_prefix_gqa_even",
+            "bf16_prefix_gqa_many_cols"]
+
+
+@pytest.mark.parametrize("name", GQA_RING)
+def test_attention_gqa_per_sequence_chunks(name, monkeypatch):
+    """The grouped-head kernel over per-sequence chunks (SPECVERIFY_SK_CHUNKS=1)
+    instead of the even split of the slices: the same oracle bar."""
+    cfg = SMALL_ATTN[name]
+    w = W.make_workload(cfg, sub_seed=21)
+    t = to_device(w, DEV)
+    monkeypatch.setenv("SPECVERIFY_SK_CHUNKS", "1")
+    o = run_attn(w, t)
+    ref = R.workload_attn(w)
+    assert np.isfinite(o).all()
+    assert attn_errors(o, ref).max() <= attn_tol(cfg), name
 
 
 def test_attention_custom_scale_and_determinism():
@@ -261,12 +284,18 @@ def test_attention_timing_events(name):
     assert np.array_equal(o1, o2)
 
 
-def test_attention_device_lengths_against_host_bound():
+@pytest.mark.parametrize("heads", [(2, 2), (8, 2)])
+def test_attention_device_lengths_against_host_bound(heads):
     """kv_len_host only bounds the device lengths: a device length above its
     sequence's bound (others unchanged) or a negative one sets status 3 and
     leaves that sequence unread; a device length below the bound gives the
-    oracle's result for the device length."""
-    cfg = W.small_variant(W.CONFIGS["bass_b8k5"], B=4, Hq=2, Hkv=2, len_lo=100, len_hi=300, V=64)
+    oracle's result for the device length.  With 8/2 heads and K = 8 the
+    grouped-head kernel runs, whose even split then meets pieces with no key
+    on the device."""
+    Hq, Hkv = heads
+    base = W.CONFIGS["bass_b8k5"] if Hq == Hkv else W.CONFIGS["gqa_b64k8"]
+    cfg = W.small_variant(base, len_kind="uniform", B=4, Hq=Hq, Hkv=Hkv, len_lo=100, len_hi=300,
+                          V=64)
     w = W.make_workload(cfg, sub_seed=12)
     t = to_device(w, DEV)
     for bad in (int(w.kv_len[1]) + 40, -1):
