@@ -91,11 +91,12 @@ constexpr int kPlanB = kAttnPlanB;
 struct DecPlan {
     int nb;                    // B when the plan is valid; 0: find the plan on the device
     int q[kPlanB + 1];         // q[b] = first chunk of sequence b; q[nb] = chunks in all
-                               // (even split: q[b] = slices of the sequences before b)
-    int s[kPlanB];             // 16-key slices of sequence b for its host bound
+                               // (even split: q[b] = items of the sequences before b)
+    int s[kPlanB];             // 16-key slices (even split: 32-key items) of sequence b
+                               // for its host bound
     int row0[kPlanB + 1];      // first query row of sequence b; row0[nb] = query rows
-    int W;                     // even split: slice ranges per kv head (0: per-sequence chunks)
-    long long N;               // even split: slices of all sequences (one kv head)
+    int W;                     // even split: item ranges per kv head (0: per-sequence chunks)
+    long long N;               // even split: 32-key items of all sequences (one kv head)
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -937,36 +938,48 @@ void decode_bf16_kernel(AttnParams p, DecPlan plan) {
         dec_merge<D, NCT>(p, S.mrg, b, g, first_slot + g, p.Hkv, qb, q0, k1);
 }
 
-// ---- Column waves over an even split of the slices (grouped heads, D = 128).
+// ---- Column waves over an even split of the keys (grouped heads, D = 128).
 //
-// The 16-key slices of all sequences are laid end to end (N in all, one kv
+// The 32-key items of all sequences are laid end to end (N in all, one kv
 // head's worth) and cut into W equal ranges; workgroup r * Hkv + g takes range
 // r of kv head g, so every resident workgroup gets the same work in one round
 // and the Hkv workgroups of a range, dispatched together, read the same cache
-// rows at the same time.  (Per-sequence chunks of at most 192 slices need
-// about 1.6 rounds on the B=64, K=8 workload, and each workgroup streams at
-// the same rate whether the round is full or not, so the partly filled second
-// round took as long as a full one.)  A range meets one or more sequences;
-// its part of sequence b is a piece with its own partial at slot (r + b) *
-// Hkv + g, so the pieces of a (sequence, kv head) sit Hkv slots apart and no
-// two pieces share a slot.  The pieces pass through a seven-slot ring (six
-// items in flight) as one stream of items: for each piece its query tiles (two tiles per item, in the
-// K and V halves of a slot), then its slices.  Each wave counts the vector
-// memory operations it issues (ring loads and partial stores; they complete
-// in issue order), so the wait for an item is exact even when a piece's
-// partial stores sit between it and the later items.  A piece that is all of
-// its sequence writes the output itself; for the others, at its end the
-// workgroup counts itself in the arrival counter of their (sequence, kv head)
-// pairs, and the last arriver merges that pair's pieces.
+// rows at the same time.  (Per-sequence chunks of at most 192 16-key slices
+// need about 1.6 rounds on the B=64, K=8 workload, and each workgroup streams
+// at the same rate whether the round is full or not, so the partly filled
+// second round took as long as a full one.)  A range meets one or more
+// sequences; its part of sequence b is a piece with its own partial at slot
+// (r + b) * Hkv + g, so the pieces of a (sequence, kv head) sit Hkv slots
+// apart and no two pieces share a slot.  The pieces pass through a four-slot
+// ring (three items in flight, 16 KB each) as one stream of items: for each
+// piece its query item (all its column tiles), then its key items.  Each
+// compute wave takes a whole 32-key item per step: two independent 16-key
+// score chains, one online softmax step and 32-key PV products, which halves
+// the dependent steps and barriers per key of a 16-key step.  Each wave counts
+// the vector memory operations it issues (ring loads and partial stores; they
+// complete in issue order), so the wait for an item is exact even when a
+// piece's partial stores sit between it and the later items.  A piece that is
+// all of its sequence (no shared prefix) writes the output itself; for the
+// others, at its end the workgroup counts itself in the arrival counter of
+// their (sequence, kv head) pairs, and the last arriver merges that pair's
+// pieces.
 constexpr int kPieceMax = 8;
 constexpr int kStreamMerge = 512;  // (part, column) pairs a merge stages in LDS at a time
-constexpr int kStreamSlots = 7;    // ring slots: six items in flight
+constexpr int kStreamSlots = 4;    // ring slots: three 32-key items in flight
+
+// One ring slot of the even-split kernel: 32 K rows and the same 32 V rows
+// (16-byte chunk c of row r at c ^ prefix_swz(r)), or 64 query rows.
+struct StreamSlot {
+    uint4 k[32 * 16];
+    uint4 v[32 * 16];
+};
 
 struct StreamPiece {
     int b, g;      // sequence, kv head
-    int lo, n;     // first slice of the piece; slices with keys on the device (-1: bad sequence)
+    int lo, n;     // first 32-key item of the piece; its items with keys on the device (-1: bad sequence)
     int L, q0, k1; // device cache length, first query row, query rows
-    int whole;     // the piece is all of the sequence: its result is the output
+    int whole;     // the piece is all of the sequence and there is no shared prefix:
+                   // its result is the output
     long long kv0; // first cache row of the sequence
 };
 
@@ -981,7 +994,7 @@ struct DecLdsStream {
 };
 
 // A position in a workgroup's item stream: piece k, item i of its `items`
-// (the query items, then the piece's slices), and the piece's parameters as
+// (the query item, then the piece's key items), and the piece's parameters as
 // wave-uniform values.
 struct StreamCursor {
     int k, i, items;
@@ -998,7 +1011,6 @@ __device__ __forceinline__ long long uniform_i64(long long v) {
 }
 
 // Piece k's parameters into the cursor (item 0).
-template <int NQI>
 __device__ __forceinline__ void stream_at(StreamCursor& c, const DecLdsStream& S, int k) {
     const StreamPiece& P = S.pc[k];
     c.k = k;
@@ -1012,55 +1024,65 @@ __device__ __forceinline__ void stream_at(StreamCursor& c, const DecLdsStream& S
     c.k1 = uniform_i32(P.k1);
     c.whole = uniform_i32(P.whole);
     c.kv0 = uniform_i64(P.kv0);
-    c.items = c.n > 0 ? NQI + c.n : 0;
+    c.items = c.n > 0 ? 1 + c.n : 0;
 }
 
-// Where this wave's two 16-byte loads of an item go: rows r0, r1 of the K half
-// (waves 0, 1) or the V half (waves 2, 3) of a slot, from 16-byte chunks
-// c0, c1 of their source rows (the row swizzle applied on the load side);
-// off0, off1: their element offsets from a slice's first cache row.
+// This wave's four 16-byte loads of an item: rows r0 = 8w + lane/16 and
+// r1 = r0 + 4 of both halves of a slot, from 16-byte chunks c0, c1 of their
+// source rows (the row swizzle applied on the load side); off0, off1: their
+// element offsets from an item's first cache row.
 struct StreamLoadLanes {
-    bool vhalf;
     int dst, r0, r1, c0, c1, off0, off1;
 };
 
-// Issue this wave's loads of the cursor's current item into slot R.
-template <int NQI>
-__device__ __forceinline__ void stream_issue(const AttnParams& p, DecColSlot& R, const StreamCursor& c,
+// Issue this wave's loads of the cursor's current item into slot R: the
+// query item (columns 0-31 in the K half, 32-63 in the V half; padding
+// columns repeat the last column, finite and never stored), or 32 keys.
+__device__ __forceinline__ void stream_issue(const AttnParams& p, StreamSlot& R, const StreamCursor& c,
                                              const StreamLoadLanes& ln) {
     constexpr int D = 128;
-    const uint16_t* src0;
-    const uint16_t* src1;
-    if (c.i < NQI) {
-        // query tiles 2i (K half) and 2i + 1 (V half); padding columns repeat
-        // the last column (finite, never stored)
+    const uint16_t *k0p, *k1p, *v0p, *v1p;
+    if (c.i == 0) {
         const int ncl = p.G * c.k1;
-        const int col0 = min(32 * c.i + (ln.vhalf ? 16 : 0) + ln.r0, ncl - 1);
-        const int col1 = min(32 * c.i + (ln.vhalf ? 16 : 0) + ln.r1, ncl - 1);
-        src0 = p.q + (static_cast<size_t>(c.q0 + col0 % c.k1) * p.Hq + c.g * p.G + col0 / c.k1) * D + ln.c0 * 8;
-        src1 = p.q + (static_cast<size_t>(c.q0 + col1 % c.k1) * p.Hq + c.g * p.G + col1 / c.k1) * D + ln.c1 * 8;
-    } else if ((c.lo + c.i - NQI) * 16 + 15 < c.L) {
-        // every row of the slice is a cache row: a uniform base
-        const size_t base = static_cast<size_t>(c.kv0 + (c.lo + c.i - NQI) * 16) * p.Hkv * D;
-        const uint16_t* cache = (ln.vhalf ? p.v_cache : p.k_cache) + base;
-        src0 = cache + ln.off0;
-        src1 = cache + ln.off1;
+        int col[4] = {ln.r0, ln.r1, 32 + ln.r0, 32 + ln.r1};
+        const uint16_t* src[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int cl = min(col[u], ncl - 1);
+            src[u] = p.q + (static_cast<size_t>(c.q0 + cl % c.k1) * p.Hq + c.g * p.G + cl / c.k1) * D +
+                     ((u & 1) ? ln.c1 : ln.c0) * 8;
+        }
+        k0p = src[0];
+        k1p = src[1];
+        v0p = src[2];
+        v1p = src[3];
+    } else if ((c.lo + c.i - 1) * 32 + 31 < c.L) {
+        // every row of the item is a cache row: a uniform base
+        const size_t base = static_cast<size_t>(c.kv0 + (c.lo + c.i - 1) * 32) * p.Hkv * D;
+        k0p = p.k_cache + base + ln.off0;
+        k1p = p.k_cache + base + ln.off1;
+        v0p = p.v_cache + base + ln.off0;
+        v1p = p.v_cache + base + ln.off1;
     } else {
         // keys < L are cache rows, the next k1 the new rows; keys past the
         // last one are clamped to it (and masked)
-        const int k0 = (c.lo + c.i - NQI) * 16;
+        const int k0 = (c.lo + c.i - 1) * 32;
         const int T = c.L + c.k1;
         const int t0 = min(k0 + ln.r0, T - 1), t1 = min(k0 + ln.r1, T - 1);
         const size_t rs = static_cast<size_t>(p.Hkv) * D, head = static_cast<size_t>(c.g) * D;
-        const uint16_t* cache = ln.vhalf ? p.v_cache : p.k_cache;
-        const uint16_t* fresh = ln.vhalf ? p.v_new : p.k_new;
-        src0 = ((t0 < c.L) ? cache + static_cast<size_t>(c.kv0 + t0) * rs
-                           : fresh + static_cast<size_t>(c.q0 + (t0 - c.L)) * rs) + head + ln.c0 * 8;
-        src1 = ((t1 < c.L) ? cache + static_cast<size_t>(c.kv0 + t1) * rs
-                           : fresh + static_cast<size_t>(c.q0 + (t1 - c.L)) * rs) + head + ln.c1 * 8;
+        const size_t o0 = ((t0 < c.L) ? static_cast<size_t>(c.kv0 + t0) : 0) * rs + head + ln.c0 * 8;
+        const size_t n0 = static_cast<size_t>(c.q0 + (t0 - c.L)) * rs + head + ln.c0 * 8;
+        const size_t o1 = ((t1 < c.L) ? static_cast<size_t>(c.kv0 + t1) : 0) * rs + head + ln.c1 * 8;
+        const size_t n1 = static_cast<size_t>(c.q0 + (t1 - c.L)) * rs + head + ln.c1 * 8;
+        k0p = (t0 < c.L) ? p.k_cache + o0 : p.k_new + n0;
+        v0p = (t0 < c.L) ? p.v_cache + o0 : p.v_new + n0;
+        k1p = (t1 < c.L) ? p.k_cache + o1 : p.k_new + n1;
+        v1p = (t1 < c.L) ? p.v_cache + o1 : p.v_new + n1;
     }
-    __builtin_amdgcn_global_load_lds(src0, (ln.vhalf ? R.v : R.k) + ln.dst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(src1, (ln.vhalf ? R.v : R.k) + ln.dst + 64, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(k0p, R.k + ln.dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(k1p, R.k + ln.dst + 64, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(v0p, R.v + ln.dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(v1p, R.v + ln.dst + 64, 16, 0, 0);
 }
 
 // Running state of a column wave's tile over the current piece.
@@ -1150,9 +1172,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_stream_kernel(AttnParams p, DecPlan plan) {
     constexpr int D = 128;
     constexpr int KK = D / 32, DT = D / 16;
-    constexpr int NQI = (NCT + 1) / 2;  // ring items holding a piece's query tiles
     __shared__ DecLdsStream S;
-    __shared__ DecColSlot C0, C1, C2, C3, C4, C5, C6;  // kStreamSlots slots
+    __shared__ StreamSlot C0, C1, C2, C3;  // kStreamSlots slots
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col16 = lane & 15, kg = lane >> 4;
@@ -1167,7 +1188,7 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
         int pb = 0, plo = 0, phi = 0, np = 0;
         long long x = x0;
         while (x < x1 && np < kPieceMax) {
-            int cnt = 0;  // sequence of slice x: the sequences whose slices all precede it
+            int cnt = 0;  // sequence of item x: the sequences whose items all precede it
             for (int b0 = 0; b0 < plan.nb; b0 += 64) {
                 const int bb = b0 + lane;
                 cnt += __popcll(__ballot((bb < plan.nb) && plan.q[bb + 1] <= x));
@@ -1190,11 +1211,12 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
             const int q0 = plan.row0[pb], k1 = plan.row0[pb + 1] - q0;
             const int L = p.kv_len[pb];
             const long long kv0 = p.kv_start[pb];
-            bool bad = (L < 0) || (static_cast<long long>(L) + k1 > 16LL * plan.s[pb]);
+            bool bad = (L < 0) || (static_cast<long long>(L) + k1 > 32LL * plan.s[pb]);
             if (p.cu_q) bad = bad || (p.cu_q[pb] != q0) || (p.cu_q[pb + 1] != q0 + k1);
             if (bad) set_status(p.status, 3);
-            const int n = bad ? -1 : max(0, min(phi, ceil_div(L + k1, 16)) - plo);
-            const int whole = (plo == 0 && phi == plan.s[pb]) ? 1 : 0;
+            const int n = bad ? -1 : max(0, min(phi, ceil_div(L + k1, 32)) - plo);
+            // (with a shared prefix every piece is merged with the prefix parts)
+            const int whole = (p.prefix_slots == 0 && plo == 0 && phi == plan.s[pb]) ? 1 : 0;
             S.pc[lane] = StreamPiece{pb, hg, plo, n, L, q0, k1, whole, kv0};
         }
         if (lane == 0) S.np = np;
@@ -1204,15 +1226,13 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
     int nitems = 0;
     for (int k = 0; k < np; ++k) {
         const int n = S.pc[k].n;
-        nitems += n > 0 ? NQI + n : 0;
+        nitems += n > 0 ? 1 + n : 0;
     }
 
-    // loads: wave w fills blocks 2(w&1), 2(w&1)+1 of the K half (waves 0, 1)
-    // or the V half (waves 2, 3) of a slot
+    // loads: wave w fills rows 8w .. 8w+7 of both halves of a slot
     StreamLoadLanes ln;
-    ln.vhalf = w >= 2;
-    ln.dst = 2 * (w & 1) * 64;
-    ln.r0 = 2 * (w & 1) * 4 + (lane >> 4);
+    ln.dst = 2 * w * 64;
+    ln.r0 = 8 * w + (lane >> 4);
     ln.r1 = ln.r0 + 4;
     ln.c0 = (lane & 15) ^ prefix_swz(ln.r0);
     ln.c1 = (lane & 15) ^ prefix_swz(ln.r1);
@@ -1222,12 +1242,12 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
     StreamCursor lc{};
     lc.k = -1;
     for (int k = 0; k < np && lc.k < 0; ++k)
-        if (S.pc[k].n > 0) stream_at<NQI>(lc, S, k);
+        if (S.pc[k].n > 0) stream_at(lc, S, k);
     auto lnext = [&]() __attribute__((always_inline)) {
         if (++lc.i == lc.items) {
             int k = lc.k + 1;
             while (k < np && S.pc[k].n <= 0) ++k;
-            if (k < np) stream_at<NQI>(lc, S, k);
+            if (k < np) stream_at(lc, S, k);
         }
     };
 
@@ -1261,7 +1281,7 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
     for (int k = 0; k < np && cc.k < 0; ++k) {
         const int n = S.pc[k].n;
         if (n > 0) {
-            stream_at<NQI>(cc, S, k);
+            stream_at(cc, S, k);
             climw = (cw && colw < p.G * cc.k1) ? cc.L + colw % cc.k1 + 1 : 0;
         } else if (n == 0) {
             iss += stream_store<KK, DT>(p, t, cw, w, colw, kg, static_cast<size_t>(rg + S.pc[k].b) * Hkv + hg,
@@ -1281,43 +1301,99 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
                                                 static_cast<size_t>(rg + S.pc[k].b) * Hkv + hg,
                                                 p.G * S.pc[k].k1, false, 0, 1, hg);
             if (k < np) {
-                stream_at<NQI>(cc, S, k);
+                stream_at(cc, S, k);
                 climw = (cw && colw < p.G * cc.k1) ? cc.L + colw % cc.k1 + 1 : 0;
             }
         }
     };
-    // item in slot R: the query tiles into registers, or one slice's products
-    auto compute = [&](DecColSlot& R) __attribute__((always_inline)) {
-        if (cc.i < NQI) {
-            if (cw && (w >> 1) == cc.i) {
-                const uint4* src = (w & 1) ? R.v : R.k;
+    // item in slot R: the query tiles into registers, or 32 keys' products:
+    // S^T of the two 16-key halves (two independent chains), one online
+    // softmax step over all 32, and O^T += V^T P^T with 32 keys per product,
+    // lane group kg supplying keys kg*4 + 0..3 of the first half, then of the
+    // second, on both operands (the same order, so every key is summed once)
+    auto compute = [&](StreamSlot& R) __attribute__((always_inline)) {
+        if (cc.i == 0) {
+            if (cw) {
+                const uint4* src = (w < 2 ? R.k : R.v) + (w & 1) * 256;
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
                     t.qv[kk] = *reinterpret_cast<const bf16x8*>(src + ckcol + 4 * (kk ^ csk2));
             }
         } else if (cw) {
-            const int k0 = (cc.lo + cc.i - NQI) * 16;
-            floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+            const int k0 = (cc.lo + cc.i - 1) * 32;
+            floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(R.k + ckcol + 4 * (kk ^ csk2));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, t.qv[kk], acc, 0, 0, 0);
-            }
-            const uint16_t* vb = reinterpret_cast<const uint16_t*>(R.v);
-            shortx4 va[DT];
+                bf16x8 ka[2];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) va[dt] = lds_read_tr16(vb + cvcol + 16 * (dt ^ csv1));
-            col_tile_update<DT>(kg, p.scale_log2, k0, k0 + 15 < cc.L, climw, acc, va, t.m, t.l, t.o);
+                for (int h = 0; h < 2; ++h)
+                    ka[h] = *reinterpret_cast<const bf16x8*>(R.k + h * 256 + ckcol + 4 * (kk ^ csk2));
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h], t.qv[kk], acc[h], 0, 0, 0);
+            }
+            const bool full = k0 + 31 < cc.L;  // no key of the item is masked for any column
+            float mt = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tt = k0 + h * 16 + kg * 4 + e;
+                    acc[h][e] = (full || tt < climw) ? acc[h][e] * p.scale_log2 : -INFINITY;
+                    mt = fmaxf(mt, acc[h][e]);
+                }
+            mt = colmax4(mt);
+            const float mnew = fmaxf(t.m, mt);
+            // no column of the tile raised its running max: alpha is exactly 1
+            // on every lane and the rescale of O is skipped
+            const bool grew = __ballot(mt > t.m) != 0;
+            shortx4 pb[2] = {shortx4{0, 0, 0, 0}, shortx4{0, 0, 0, 0}};
+            float alpha = 1.0f;
+            if (mnew != -INFINITY) {  // (a padding column has no key)
+                if (grew) alpha = __builtin_amdgcn_exp2f(t.m - mnew);
+                float ps = 0.0f;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float pe = __builtin_amdgcn_exp2f(acc[h][e] - mnew);
+                        ps += pe;
+                        pb[h][e] = static_cast<short>(f32_to_bf16(pe));
+                    }
+                t.l = t.l * alpha + ps;
+                t.m = mnew;
+            }
+            if (grew) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) t.o[dt] *= alpha;
+            }
+            const bf16x8 pk = __builtin_bit_cast(
+                bf16x8, (shortx8{pb[0][0], pb[0][1], pb[0][2], pb[0][3], pb[1][0], pb[1][1], pb[1][2], pb[1][3]}));
+            const uint16_t* vb = reinterpret_cast<const uint16_t*>(R.v);
+#pragma unroll
+            for (int d0 = 0; d0 < DT; d0 += 4) {
+                bf16x8 va[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const shortx4 a0 = lds_read_tr16(vb + cvcol + 16 * ((d0 + u) ^ csv1));
+                    const shortx4 a1 = lds_read_tr16(vb + 16 * D + cvcol + 16 * ((d0 + u) ^ csv1));
+                    va[u] = __builtin_bit_cast(bf16x8, (shortx8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}));
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    t.o[d0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], pk, t.o[d0 + u], 0, 0, 0);
+            }
         }
     };
 
     constexpr int AHEAD = kStreamSlots - 1;  // items in flight
-    int a0 = 0, a1 = 0, a2 = 0, a3 = 0, a4 = 0, a5 = 0, a6 = 0;  // iss after each slot's loads
+    constexpr int kOps = 4;                  // loads per wave per item
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;      // iss after each slot's loads
 #define SV_ISSUE(R, A)                     \
     do {                                   \
-        stream_issue<NQI>(p, R, lc, ln);   \
+        stream_issue(p, R, lc, ln);        \
         lnext();                           \
-        iss += 2;                          \
+        iss += kOps;                       \
         A = iss;                           \
     } while (0)
     // one ring step: item j is in once this wave's loads of it are done and
@@ -1327,7 +1403,7 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
     do {                                                              \
         {                                                             \
             const int vm_ = uniform_i32(iss - (A));                   \
-            if (vm_ == 2 * (AHEAD - 1)) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (AHEAD - 1))); \
+            if (vm_ == kOps * (AHEAD - 1)) __builtin_amdgcn_s_waitcnt(0x0F70 | (kOps * (AHEAD - 1))); \
             else wait_vmcnt(vm_);                                     \
         }                                                             \
         __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): LDS reads done */ \
@@ -1337,21 +1413,15 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
         compute(R);                                                   \
         cnext();                                                      \
     } while (0)
-    static_assert(kStreamSlots == 7 && 2 * (AHEAD - 1) < 16, "the ring below has seven slots");
+    static_assert(kStreamSlots == 4 && kOps * (AHEAD - 1) < 16, "the ring below has four slots");
     if (nitems > 0) SV_ISSUE(C0, a0);
     if (nitems > 1) SV_ISSUE(C1, a1);
     if (nitems > 2) SV_ISSUE(C2, a2);
-    if (nitems > 3) SV_ISSUE(C3, a3);
-    if (nitems > 4) SV_ISSUE(C4, a4);
-    if (nitems > 5) SV_ISSUE(C5, a5);
-    for (int j = 0; j < nitems; j += 7) {
-        SV_STEP(j, C0, C6, a0, a6);
+    for (int j = 0; j < nitems; j += 4) {
+        SV_STEP(j, C0, C3, a0, a3);
         if (j + 1 < nitems) SV_STEP(j + 1, C1, C0, a1, a0);
         if (j + 2 < nitems) SV_STEP(j + 2, C2, C1, a2, a1);
         if (j + 3 < nitems) SV_STEP(j + 3, C3, C2, a3, a2);
-        if (j + 4 < nitems) SV_STEP(j + 4, C4, C3, a4, a3);
-        if (j + 5 < nitems) SV_STEP(j + 5, C5, C4, a5, a4);
-        if (j + 6 < nitems) SV_STEP(j + 6, C6, C5, a6, a5);
     }
 #undef SV_STEP
 #undef SV_ISSUE
@@ -1361,20 +1431,18 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
     // (nor of a bad one); the last arriver merges that pair's pieces
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) {
-        for (int k = 0; k < np; ++k) {
-            const StreamPiece& P = S.pc[k];
-            int last = 0;
-            if (P.n >= 0 && !P.whole) {
-                const long long st = plan.q[P.b];
-                const int parts = stream_owner(st + plan.s[P.b] - 1, W, N) - stream_owner(st, W, N) + 1;
-                int* cnt = p.merge_cnt + static_cast<size_t>(P.b) * Hkv + P.g;
-                const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                last = (old == parts - 1) ? 1 : 0;
-                if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            S.last[k] = last;
+    if (tid < np) {  // lane k of wave 0: piece k (the counts in one round trip)
+        const StreamPiece& P = S.pc[tid];
+        int last = 0;
+        if (P.n >= 0 && !P.whole) {
+            const long long st = plan.q[P.b];
+            const int parts = stream_owner(st + plan.s[P.b] - 1, W, N) - stream_owner(st, W, N) + 1;
+            int* cnt = p.merge_cnt + static_cast<size_t>(P.b) * Hkv + P.g;
+            const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = (old == parts - 1) ? 1 : 0;
+            if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        S.last[tid] = last;
     }
     __syncthreads();
     for (int k = 0; k < np; ++k) {
@@ -2136,27 +2204,33 @@ AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int bf16,
         pl.plan_W = 0;
         pl.plan_N = 0;
         if (pl.plan_nb > 0 && sk_mode(D, pl.nct) == 2 && env_int("SPECVERIFY_SK_CHUNKS", 0) == 0) {
-            long long N = 0;  // slices of all sequences, one kv head
-            for (int b = 0; b < B; ++b) N += pl.plan_s[b];
+            // 32-key items per sequence for the host bound
+            std::vector<int> s32(B);
+            long long N = 0;  // items of all sequences, one kv head
+            for (int b = 0; b < B; ++b) {
+                s32[b] = static_cast<int>((std::min<long long>(keys(b), kSkMaxKeys) + 31) / 32);
+                N += s32[b];
+            }
             const long long Wl = std::min<long long>(sk_stream_resident(pl.nct) / Hkv,
-                                                     std::max<long long>(1, N / kLambdaMin));
+                                                     std::max<long long>(1, N / (kLambdaMin / 2)));
             const int W = static_cast<int>(std::max<long long>(1, Wl));  // slice ranges
             auto owner = [&](long long x) { return static_cast<int>(((x + 1) * W - 1) / N); };
             std::vector<int> pieces(W, 0);
             bool fits = N > 0;
             long long st = 0;
             for (int b = 0; b < B && fits; ++b) {
-                const int r0 = owner(st), r1 = owner(st + pl.plan_s[b] - 1);
+                const int r0 = owner(st), r1 = owner(st + s32[b] - 1);
                 if (r1 - r0 + 1 + pslots > kStreamMerge) fits = false;
                 for (int r = r0; r <= r1 && fits; ++r)
                     if (++pieces[r] > kPieceMax) fits = false;
-                st += pl.plan_s[b];
+                st += s32[b];
             }
             if (fits) {
                 long long run = 0;
                 for (int b = 0; b < B; ++b) {
                     pl.plan_q[b] = static_cast<int>(run);
-                    run += pl.plan_s[b];
+                    pl.plan_s[b] = s32[b];
+                    run += s32[b];
                 }
                 pl.plan_q[B] = static_cast<int>(run);
                 pl.plan_W = W;

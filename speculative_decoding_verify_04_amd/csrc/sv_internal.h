@@ -47,10 +47,10 @@ struct AttnPlan {
     int plan_q[kAttnPlanB + 1];
     int plan_s[kAttnPlanB];
     int plan_row0[kAttnPlanB + 1];
-    // grouped heads (column waves): the slices of all sequences cut into
+    // grouped heads (column waves): the 32-key items of all sequences cut into
     // plan_W equal ranges, each taken by Hkv workgroups, one per kv head
-    // (plan_W = 0: per-sequence chunks); plan_q then holds slice prefix sums,
-    // plan_N all slices
+    // (plan_W = 0: per-sequence chunks); plan_s then counts 32-key items,
+    // plan_q holds their prefix sums and plan_N all items
     int plan_W;
     long long plan_N;
     size_t bytes;          // whole workspace: counter region, then data region
