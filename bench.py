@@ -460,7 +460,10 @@ def main():
         "verified_tokens_per_step_avg": round(tokens / steps, 3),
         "wall_s_timed": round(wall, 4),
         "roofline": {
-            "kernel": "decode_bf16_kernel (split-K verify attention)",
+            "kernel": ("decode_stream_kernel (split-K verify attention, grouped heads)"
+                       if cfg.D == 128 and (cfg.Hq // cfg.Hkv) * (cfg.K + 1) > 16 and cfg.B <= 128
+                       else "decode_bf16_kernel (split-K verify attention)") if cfg.kv_dtype == 1
+                      else "attn_f32_kernel (split-K verify attention, fp32)",
             "bound": "hbm",
             "achieved": round(achieved, 1) if achieved else None,
             "peak": HBM_PEAK_GBS,
