@@ -1288,12 +1288,26 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
                                         p.G * S.pc[k].k1, false, 0, 1, hg);
         }
     }
+    // The first piece that ends before the stream does and is not a whole
+    // sequence is counted in its arrival counter early, once the loads of a
+    // later item have been waited for (its partial stores, issued before
+    // them, are then complete in every wave): the workgroup of the range
+    // before this one, whose last piece shares the pair and ends later, is
+    // then the one that merges it, and no workgroup merges two pairs at its
+    // end.  (0: none yet, 1: stores issued, 2: counted; `early_old` holds the
+    // count before it in lane early_k of wave 0.)
+    int early_state = 0, early_k = 0, early_iss = 0, early_old = 0;
     auto cnext = [&]() __attribute__((always_inline)) {
         if (++cc.i == cc.items) {
             // the piece is done: its partial, then those of the empty pieces
             // up to the next one with items
             iss += stream_store<KK, DT>(p, t, cw, w, colw, kg, static_cast<size_t>(rg + cc.b) * Hkv + hg,
                                         p.G * cc.k1, cc.whole != 0, cc.q0, cc.k1, hg);
+            if (early_state == 0 && cc.whole == 0) {
+                early_state = 1;
+                early_k = cc.k;
+                early_iss = iss;
+            }
             int k = cc.k + 1;
             for (; k < np && S.pc[k].n <= 0; ++k)
                 if (S.pc[k].n == 0)
@@ -1409,6 +1423,13 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
         __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): LDS reads done */ \
         __builtin_amdgcn_s_barrier();                                 \
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local"); \
+        if (early_state == 1 && (A) > early_iss) {                    \
+            early_state = 2;                                          \
+            if (tid == early_k)                                       \
+                early_old = __hip_atomic_fetch_add(                   \
+                    p.merge_cnt + static_cast<size_t>(S.pc[early_k].b) * Hkv + S.pc[early_k].g, 1, \
+                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);      \
+        }                                                             \
         if ((J) + AHEAD < nitems) SV_ISSUE(Rn, An);                   \
         compute(R);                                                   \
         cnext();                                                      \
@@ -1438,7 +1459,9 @@ void decode_stream_kernel(AttnParams p, DecPlan plan) {
             const long long st = plan.q[P.b];
             const int parts = stream_owner(st + plan.s[P.b] - 1, W, N) - stream_owner(st, W, N) + 1;
             int* cnt = p.merge_cnt + static_cast<size_t>(P.b) * Hkv + P.g;
-            const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int old = (early_state == 2 && tid == early_k)
+                                ? early_old
+                                : __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             last = (old == parts - 1) ? 1 : 0;
             if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
