@@ -294,32 +294,49 @@ __device__ __forceinline__ void col_tile_update(int kg, float scale_log2, int k0
 // pairs per thread, PMAX parts): the partial loads are issued before the
 // (m, l) loads, so both travel in the same round trip; the weights are formed
 // in LDS; fixed order, as in dec_merge.
+// With np > 0 the first np parts are the shared prefix's chunk partials of
+// sequence b (written by the prefix kernel), the rest at first_slot + (j -
+// np)*stride.
 template <int D, int UP, int PMAX, typename MRG>
-__device__ __forceinline__ void merge_in_registers(const AttnParams& p, MRG& M, int g, int first_slot,
-                                                   int stride, int nparts, int nc, int qrow0, int k1) {
+__device__ __forceinline__ void merge_in_registers(const AttnParams& p, MRG& M, int b, int g, int first_slot,
+                                                   int stride, int np, int nparts, int nc, int qrow0,
+                                                   int k1) {
     const int tid = threadIdx.x;
     const int CPG = p.CPG, npairs = nc * D;
+    const size_t pre_col0 = static_cast<size_t>(g) * p.NC + static_cast<size_t>(b) * CPG;
     float ov[PMAX][UP];
-    int off[UP];
+    int off[UP], poff[UP];
 #pragma unroll
     for (int u = 0; u < UP; ++u) {
         const int pq = min(tid + u * kThreads, npairs - 1);
         off[u] = (pq / nc) * CPG + pq % nc;
+        poff[u] = (pq % nc) * D + pq / nc;  // prefix partials: [chunk][Hkv][NC][D]
     }
 #pragma unroll
     for (int jj = 0; jj < PMAX; ++jj) {
         const int j = min(jj, nparts - 1);  // past the end: re-read the last part
-        const float* pb = p.part_o + (static_cast<size_t>(first_slot) + static_cast<size_t>(j) * stride) * D * CPG;
+        if (j < np) {
+            const float* pb = p.pre_o + (static_cast<size_t>(j) * p.Hkv * p.NC + pre_col0) * D;
 #pragma unroll
-        for (int u = 0; u < UP; ++u) ov[jj][u] = ld_coh(pb + off[u]);
+            for (int u = 0; u < UP; ++u) ov[jj][u] = pb[poff[u]];
+        } else {
+            const float* pb =
+                p.part_o + (static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * stride) * D * CPG;
+#pragma unroll
+            for (int u = 0; u < UP; ++u) ov[jj][u] = ld_coh(pb + off[u]);
+        }
     }
     __syncthreads();
     for (int idx = tid; idx < nparts * nc; idx += kThreads) {
         const int j = idx / nc, col = idx % nc;
-        const unsigned long long u = ld_coh(reinterpret_cast<const unsigned long long*>(
-            p.part_ml + (static_cast<size_t>(first_slot) + static_cast<size_t>(j) * stride) * CPG + col));
-        M.ml[idx] = make_float2(__uint_as_float(static_cast<unsigned>(u)),
-                                __uint_as_float(static_cast<unsigned>(u >> 32)));
+        if (j < np) {
+            M.ml[idx] = p.pre_ml[static_cast<size_t>(j) * p.Hkv * p.NC + pre_col0 + col];
+        } else {
+            const unsigned long long u = ld_coh(reinterpret_cast<const unsigned long long*>(
+                p.part_ml + (static_cast<size_t>(first_slot) + static_cast<size_t>(j - np) * stride) * CPG + col));
+            M.ml[idx] = make_float2(__uint_as_float(static_cast<unsigned>(u)),
+                                    __uint_as_float(static_cast<unsigned>(u >> 32)));
+        }
     }
     __syncthreads();
     for (int cl = tid; cl < nc; cl += kThreads) {
@@ -353,7 +370,9 @@ __device__ __forceinline__ void merge_in_registers(const AttnParams& p, MRG& M, 
 
 // Merge every part of (sequence b, kv head g) -- the prefix chunks first, then
 // its q_b chunks in order, at partial slots first_slot + j*stride -- and write
-// the output rows qrow0+j (j < k1) of heads g*G + hh.  Two round trips: the (m, l) of every (part, column) into LDS and
+// the output rows qrow0+j (j < k1) of heads g*G + hh.  When every value a
+// thread needs fits in registers, one round trip (merge_in_registers); else
+// two: the (m, l) of every (part, column) into LDS and
 // the per-column weights, then every o value weighted, with the loads of up
 // to 4 columns x 8 parts in flight per thread.  Fixed order: bit-reproducible.
 template <int D, int NCT, typename MRG>
@@ -370,23 +389,28 @@ __device__ __forceinline__ void dec_merge(const AttnParams& p, MRG& M, int b, in
     };
     constexpr int cap = static_cast<int>(sizeof(M.w) / sizeof(M.w[0]));  // (part, column) pairs in LDS
     const int group = max(1, min(ncols, cap / nparts));
-    if (np == 0 && group == ncols) {
+    if (group == ncols) {
         // every partial value a thread needs fits in registers: one round trip
         const int npairs = ncols * D;
-        if (nparts <= 8 && npairs <= 4 * kThreads) {
-            merge_in_registers<D, 4, 8>(p, M, g, first_slot, stride, nparts, ncols, qrow0, k1);
+        if (np == 0 && nparts <= 8 && npairs <= 4 * kThreads) {
+            merge_in_registers<D, 4, 8>(p, M, b, g, first_slot, stride, 0, nparts, ncols, qrow0, k1);
+            return;
+        }
+        // with a shared prefix (its chunks, then the sequence's own parts)
+        if (np > 0 && nparts <= 12 && npairs <= 3 * kThreads) {
+            merge_in_registers<D, 3, 12>(p, M, b, g, first_slot, stride, np, nparts, ncols, qrow0, k1);
             return;
         }
         // (the wider forms only where the kernel's loop already needs more
         // registers than they do: the one-tile kernel stays at 4 workgroups
         // per CU)
         if constexpr (NCT > 1) {
-            if (nparts <= 4 && npairs <= 8 * kThreads) {
-                merge_in_registers<D, 8, 4>(p, M, g, first_slot, stride, nparts, ncols, qrow0, k1);
+            if (np == 0 && nparts <= 4 && npairs <= 8 * kThreads) {
+                merge_in_registers<D, 8, 4>(p, M, b, g, first_slot, stride, 0, nparts, ncols, qrow0, k1);
                 return;
             }
-            if (nparts <= 2 && npairs <= 20 * kThreads) {
-                merge_in_registers<D, 20, 2>(p, M, g, first_slot, stride, nparts, ncols, qrow0, k1);
+            if (np == 0 && nparts <= 2 && npairs <= 20 * kThreads) {
+                merge_in_registers<D, 20, 2>(p, M, b, g, first_slot, stride, 0, nparts, ncols, qrow0, k1);
                 return;
             }
         }
