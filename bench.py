@@ -164,7 +164,7 @@ def traffic_summary(d, config, mib):
         calib = [v for k, _, v in _counter_rows(os.path.join(d, "calib_" + sub), counter)
                  if "add" in k.lower() and "random" not in k.lower()]
         kern = [v for k, _, v in _counter_rows(os.path.join(d, sub), counter)
-                if "decode_bf16_kernel" in k]
+                if "decode_bf16_kernel" in k or "decode_stream_kernel" in k]
         if not calib or not kern:
             raise SystemExit(f"no {counter} rows for the copy or the attention kernel under {d}")
         c_kib = sum(calib) / len(calib)
