@@ -1843,7 +1843,7 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(AcceptParams p) {
 #pragma unroll
                 for (int k = 0; k < EPT; ++k) {
                     acc[r] += exp2_256((static_cast<double>(z[r][k]) - mr) * p.yscale, L.tab);
-                    if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                    if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }
