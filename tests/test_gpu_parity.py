@@ -197,6 +197,10 @@ SMALL_ATTN = {
     # grouped heads over the even split of the slices, with a shared prefix
     "bf16_prefix_gqa_even": W.small_variant(W.CONFIGS["prefix_b32k4"], B=6, K=4, Hq=8, Hkv=2,
                                             prefix_len=700, len_lo=100, len_hi=600, V=64),
+    # 64 query columns per kv head: four column tiles, the fourth read from
+    # the query item's second half; short and long sequences side by side
+    "bf16_gqa_four_tiles": W.small_variant(W.CONFIGS["gqa_b64k8"], len_kind="uniform", B=11, K=7,
+                                           Hq=16, Hkv=2, len_lo=0, len_hi=1500, V=64),
     # more work items than workgroups resident at once (one chunk each)
     "bf16_more_items_than_resident": W.small_variant(W.CONFIGS["bass_b8k5"], B=600, K=3, Hq=2,
                                                      Hkv=2, len_lo=0, len_hi=80, V=64),
@@ -223,7 +227,7 @@ def test_attention_small(name):
 # shapes that run the grouped-head kernel (D = 128, more than 16 query columns
 # per kv head); by default over the even split of the slices
 GQA_RING = ["bf16_gqa_k8", "bf16_gqa_many_items", "bf16_prefix_gqa_even",
-            "bf16_prefix_gqa_many_cols"]
+            "bf16_prefix_gqa_many_cols", "bf16_gqa_four_tiles"]
 
 
 @pytest.mark.parametrize("name", GQA_RING)
